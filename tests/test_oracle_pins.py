@@ -1,0 +1,395 @@
+"""Pins for the CPU oracle: each test ties an oracle function to something other than itself --
+values the pages print (tests/golden/), closed forms, exact special cases, library routines or
+brute force on tiny shapes.  A plausible slip in the oracle (dropped term, wrong fill, fused vs
+unfused rounding, a transposed index, accumulating in f32) fails at least one of them.
+
+Sources: Phobos docs "@aligned" and "Slicing, bounds and masking"; Mojo GPU puzzle 35 "Aligned Load
+& Store"; teenygrad "Memory Coalescing and Tensor Layout".
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from edge_masking_vector_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bits(a):
+    return np.ascontiguousarray(a, np.float32).view(np.uint32)
+
+
+# ---- loop remainder split ------------------------------------------------------------------------
+
+def test_split_worked_example():
+    """'Slicing, bounds and masking', 'Loops over a dynamic extent': K=1000, TILE_K=16 -> 62 + 8."""
+    g = _golden("split_loop.json")
+    assert oracle.split(g["K"], g["TILE_K"]) == (g["whole_tiles"], g["remainder_cols"])
+
+
+def test_split_masked_rowmax_shape():
+    """The same rule on the score walk: Nk=1000 in BC=64 tiles -> 15 whole tiles + 40 columns."""
+    assert oracle.split(1000, 64) == (15, 40)
+
+
+def test_split_closed_form_exhaustive():
+    """nfull*T + rem == K with 0 <= rem < T, for every small K and T."""
+    for K in range(0, 300):
+        for T in range(1, 40):
+            nf, rm = oracle.split(K, T)
+            assert nf * T + rm == K and 0 <= rm < T, (K, T, nf, rm)
+
+
+# ---- edge tiles ----------------------------------------------------------------------------------
+
+def test_edge_tile_worked_example():
+    g = _golden("edge_tile.json")
+    M, N = g["derived_shape"]["M"], g["derived_shape"]["N"]
+    pm, pn = g["block"]
+    live = oracle.tile_live(M, N, g["TM"], g["TN"], pm, pn)
+    assert live == g["live"]
+    assert g["TM"] * g["TN"] - live == g["masked"]
+
+
+def test_edge_tile_shape_is_unique():
+    """Among extents that are multiples of 4 (the pages' assumption) and that leave tile (2, 3) of
+    an 8 x 8 tiling partly inside the tensor, only M=20, N=28 gives 16 live elements."""
+    hits = []
+    for M in range(4, 33, 4):
+        for N in range(4, 41, 4):
+            live = oracle.tile_live(M, N, 8, 8, 2, 3)
+            if live == 16:
+                hits.append((M, N))
+    assert hits == [(20, 28)]
+
+
+def test_edge_tile_brute_force_counts():
+    """Brute force over tiny shapes: live count equals the overlap of row and column ranges."""
+    for M in range(0, 14):
+        for N in range(0, 14):
+            for TM in (1, 2, 3, 4, 8):
+                for TN in (1, 2, 4, 5, 8):
+                    for pm in range(0, 4):
+                        for pn in range(0, 4):
+                            rows = len([i for i in range(pm * TM, pm * TM + TM) if i < M])
+                            cols = len([j for j in range(pn * TN, pn * TN + TN) if j < N])
+                            assert oracle.tile_live(M, N, TM, TN, pm, pn) == rows * cols
+
+
+def test_edge_tile_stores_land_only_inside():
+    """The masked tiled map on the worked example writes exactly the 16 live elements of tile
+    (2, 3) and nothing outside the 20 x 28 tensor (48 masked stores skipped)."""
+    M, N, ld = 20, 28, 32
+    rows_alloc = 24
+    x = np.arange(rows_alloc * ld, dtype=np.float32)
+    sentinel = np.float32(3.25e38)
+    y = np.full(rows_alloc * ld, sentinel, np.float32)
+    oracle.map_affine_tiled(x, ld, y, ld, M, N, 2.0, 1.0, 8, 8)
+    y2 = y.reshape(rows_alloc, ld)
+    written = y2 != sentinel
+    assert written[:M, :N].all()
+    assert not written[M:, :].any() and not written[:, N:].any()
+    tile = written[16:24, 24:32]
+    assert tile.sum() == 16 and (~tile).sum() == 48
+
+
+# ---- the affine map ------------------------------------------------------------------------------
+
+def test_map_1d_closed_form():
+    """'Aligned Load & Store': out = a*2 + 1 over the 1M-element buffer.  With a = (k - 2**23) *
+    2**-23 (k a 24-bit integer), out = (k - 2**22) * 2**-22 exactly -- computed from integers."""
+    n = 1 << 20
+    a = inputs.map1d_input(n)
+    k = inputs.u24(1, n)
+    assert np.array_equal(a.astype(np.float64), (k - 2 ** 23) * 2.0 ** -23)
+    want = ((k - 2 ** 22) * 2.0 ** -22).astype(np.float32)
+    y = np.empty(n, np.float32)
+    oracle.map_affine(a, n, y, n, 1, n, 2.0, 1.0)
+    assert np.array_equal(_bits(y), _bits(want))
+
+
+@pytest.mark.parametrize("alpha,beta,gen", [
+    (0.75, -0.25, lambda: inputs.ragged_input(64, 1000)),
+    (2.0, 1.0, lambda: inputs.map1d_input(1 << 16)),
+])
+def test_map_single_rounding(alpha, beta, gen):
+    """fmaf is one rounding of the exact a*x + b.  For these inputs the double expression is exact
+    (under 53 significant bits), so rounding it once to f32 is the correctly rounded result."""
+    x = gen()
+    exact = x.astype(np.float64) * alpha + beta
+    # exactness of the double expression, checked with rationals on a sample
+    for v in x[:200]:
+        assert Fraction(float(v)) * Fraction(alpha) + Fraction(beta) == Fraction(float(v) * alpha + beta)
+    want = exact.astype(np.float32)
+    y = np.empty_like(x)
+    oracle.map_affine(x, x.size, y, x.size, 1, x.size, alpha, beta)
+    assert np.array_equal(_bits(y), _bits(want))
+
+
+def test_map_fused_differs_from_unfused():
+    """Negative control for the pin above: on the ragged workload's data, multiply-then-add in f32
+    (two roundings) differs from the fused result for some elements, so the pin tells them apart."""
+    x = inputs.ragged_input(64, 1000)
+    unfused = (x * np.float32(0.75)) + np.float32(-0.25)
+    y = np.empty_like(x)
+    oracle.map_affine(x, x.size, y, x.size, 1, x.size, 0.75, -0.25)
+    assert (_bits(unfused) != _bits(y)).sum() > 0
+
+
+def test_map_respects_strides():
+    """Row strides are the passed ones ('The alignment constraint'): padding is never read or
+    written, and swapping ldx/ldy misplaces data."""
+    M, N, ldx, ldy = 5, 7, 9, 11
+    x = np.arange(M * ldx, dtype=np.float32)
+    y = np.full(M * ldy, -7.0, np.float32)
+    oracle.map_affine(x, ldx, y, ldy, M, N, 2.0, 1.0)
+    for i in range(M):
+        for j in range(ldy):
+            if j < N:
+                assert y[i * ldy + j] == 2.0 * x[i * ldx + j] + 1.0
+            else:
+                assert y[i * ldy + j] == -7.0
+
+
+# ---- scale and copy ------------------------------------------------------------------------------
+
+def test_scale_is_ieee_multiply():
+    """Y = alpha*X is one IEEE f32 multiply: numpy's f32 multiply is that operation.  Signed zeros
+    survive (1.5 * -0 = -0), which a fused alpha*x + 0 would turn into +0."""
+    x = inputs.scale_input(64, 512)
+    x[:4] = [-0.0, 0.0, 1e-40, -1e-40]   # signed zeros and subnormals
+    y = np.empty_like(x)
+    oracle.scale2d(x, 512, y, 512, 64, 512, 1.5)
+    want = np.float32(1.5) * x
+    assert np.array_equal(_bits(y), _bits(want))
+    assert _bits(y)[0] == 0x80000000
+
+
+def test_scale_exact_in_double():
+    """For alpha = 1.5 the product of an f32 with 1.5 is exact in double; rounding once to f32
+    reproduces the f32 multiply."""
+    x = inputs.scale_input(128, 1024)
+    y = np.empty_like(x)
+    oracle.scale2d(x, 1024, y, 1024, 128, 1024, 1.5)
+    assert np.array_equal(_bits(y), _bits((x.astype(np.float64) * 1.5).astype(np.float32)))
+
+
+def test_copy_is_bitwise():
+    specials = np.array([0x7FC00001, 0xFFC12345, 0x80000000, 0x00000001, 0x7F800000,
+                         0xFF800000, 0x7FA00000], np.uint32)
+    x = np.concatenate([specials, inputs.u32(9, 57)]).view(np.float32).copy()
+    y = np.zeros(64 * 2, np.float32)
+    oracle.copy2d(x, 64, y, 128, 1, 64)
+    assert np.array_equal(_bits(y[:64]), _bits(x))
+    assert not _bits(y[64:]).any()
+
+
+# ---- tiled walks vs plain definitions: brute force on tiny shapes --------------------------------
+
+def _tiny_cases():
+    for M in range(0, 18):
+        for N in range(0, 18):
+            for ld in sorted({max(N, 1), N + 3, max(4 * ((N + 3) // 4), 1)}):
+                yield M, N, ld
+
+
+def test_tiled_map_equals_plain_brute_force():
+    """'Masking': masked reads give 0, masked stores are skipped.  For every tiny shape and tile
+    the tiled walk writes exactly the plain map's values, and never touches padding or the
+    rows past M (sentinels)."""
+    sentinel = np.float32(3.0e38)
+    for M, N, ld in _tiny_cases():
+        x = inputs.uniform(M * 131 + N * 7 + ld, (M + 1) * ld + 1, -4.0, 4.0)
+        ref = np.full(x.size, sentinel, np.float32)
+        oracle.map_affine(x, ld, ref, ld, M, N, 0.75, -0.25)
+        for TM in (1, 2, 4, 8, 16):
+            for TN in (1, 2, 4, 8, 16):
+                y = np.full(x.size, sentinel, np.float32)
+                oracle.map_affine_tiled(x, ld, y, ld, M, N, 0.75, -0.25, TM, TN)
+                assert np.array_equal(_bits(y), _bits(ref)), (M, N, ld, TM, TN)
+
+
+def test_tiled_rowsum_equals_plain_brute_force():
+    """Whole tiles + one zero-filled remainder give the plain fp64 row sum bit for bit."""
+    for M, N, ld in _tiny_cases():
+        if M == 0:
+            continue
+        x = inputs.uniform(M * 17 + N + 5 * ld, M * ld, -3.0, 3.0)
+        ref = oracle.rowsum_f64(x, ld, M, N)
+        for T in (1, 2, 4, 8, 16):
+            got = oracle.rowsum_tiled_f64(x, ld, M, N, T)
+            assert np.array_equal(got, ref), (M, N, ld, T)
+
+
+def test_tiled_rowmax_equals_plain_brute_force():
+    """With the -1e30 fill the masked remainder never wins, so the tiled walk equals the plain max."""
+    for M, N, ld in _tiny_cases():
+        if M == 0:
+            continue
+        s = inputs.uniform(M * 29 + N + 3 * ld, M * ld, -10.0, -1.0)
+        ref = oracle.rowmax(s, ld, M, N)
+        for BC in (1, 2, 4, 8, 16):
+            got = oracle.rowmax_tiled(s, ld, M, N, BC)
+            assert np.array_equal(_bits(got), _bits(ref)), (M, N, ld, BC)
+
+
+# ---- reductions ----------------------------------------------------------------------------------
+
+def test_rowmax_fill_value_bits():
+    """-1.0e30 in f32 is the nearest float, 0xF149F2CA."""
+    assert int(np.array([oracle.MAX_FILL], np.float32).view(np.uint32)[0]) == 0xF149F2CA
+    s = np.zeros(4, np.float32)
+    out = oracle.rowmax(s, 1, 3, 0)        # empty rows
+    assert (_bits(out) == 0xF149F2CA).all()
+
+
+def test_rowmax_all_negative_never_zero():
+    """'Reductions over a ragged tile': a ragged row of negative scores keeps its true (negative)
+    maximum under the -1e30 fill ..."""
+    M, N, BC = 64, 1000, 64
+    s = inputs.scores_input(M, N)
+    got = oracle.rowmax_tiled(s, N, M, N, BC)
+    assert (got < 0).all()
+    assert np.array_equal(got, s.reshape(M, N).max(axis=1))
+
+
+def test_rowmax_zero_fill_negative_control():
+    """... and the same walk with a 0 fill reports 0, the wrong answer the pages warn about."""
+    M, N, BC = 64, 1000, 64
+    s = inputs.scores_input(M, N)
+    got = oracle.rowmax_tiled(s, N, M, N, BC, fill=0.0)
+    assert (got == 0).all()
+
+
+def test_rowmax_matches_numpy_full_shape():
+    """Max is exact and order-free: the masked-rowmax workload (8192 x 1000) against numpy's max."""
+    M, N = 8192, 1000
+    s = inputs.scores_input(M, N)
+    got = oracle.rowmax(s, N, M, N)
+    assert np.array_equal(_bits(got), _bits(s.reshape(M, N).max(axis=1)))
+
+
+def test_rowmax_nan_never_wins():
+    s = np.array([-3.0, np.nan, -2.0, -5.0], np.float32)
+    assert oracle.rowmax(s, 4, 1, 4)[0] == np.float32(-2.0)
+
+
+def test_sums_integer_inputs_exact():
+    """Integer inputs in [0, 16): every sum is an exact integer; compare with Python integers."""
+    M, N = 96, 200
+    x = inputs.integers(11, M * N, 0, 16)
+    xi = x.astype(np.int64).reshape(M, N)
+    assert np.array_equal(oracle.rowsum_f64(x, N, M, N), xi.sum(axis=1).astype(np.float64))
+    assert np.array_equal(oracle.colsum_f64(x, N, M, N), xi.sum(axis=0).astype(np.float64))
+
+
+def test_sums_constant_closed_form():
+    M, N, c = 300, 700, 0.125
+    x = np.full(M * N, c, np.float32)
+    assert (oracle.rowsum_f64(x, N, M, N) == N * c).all()
+    assert (oracle.colsum_f64(x, N, M, N) == M * c).all()
+
+
+def test_sums_accumulate_in_double():
+    """A large term followed by many tiny ones: an f32 accumulator would drop the tiny terms, the
+    fp64 one keeps them.  Compared with math.fsum (exactly rounded)."""
+    N = 4096
+    row = np.full(N, 2.0 ** -30, np.float32)
+    row[0] = 1.0
+    got = oracle.rowsum_f64(row, N, 1, N)[0]
+    assert got == math.fsum(float(v) for v in row)
+    assert got > 1.0 + 1e-6
+
+
+def test_sums_against_fsum():
+    """Row and column sums of the 4096 x 4096 U[0,1) workload against math.fsum on sampled lines
+    (fp64 left-to-right accumulation of 4096 terms is within 4096 * 2**-53 relative)."""
+    M = N = 4096
+    x = inputs.colrow_input(M, N)
+    rs = oracle.rowsum_f64(x, N, M, N)
+    cs = oracle.colsum_f64(x, N, M, N)
+    X = x.reshape(M, N)
+    for i in (0, 1, 777, 2048, 4095):
+        ref = math.fsum(X[i, :].astype(np.float64))
+        assert abs(rs[i] - ref) <= 1e-12 * ref
+        ref = math.fsum(X[:, i].astype(np.float64))
+        assert abs(cs[i] - ref) <= 1e-12 * ref
+
+
+def test_colsum_is_rowsum_of_transpose():
+    """Column sums of X equal row sums of X^T, bit for bit (same terms, same order)."""
+    M, N = 123, 77
+    x = inputs.uniform(21, M * N, -1.0, 1.0)
+    xt = np.ascontiguousarray(x.reshape(M, N).T).reshape(-1)
+    assert np.array_equal(oracle.colsum_f64(x, N, M, N), oracle.rowsum_f64(xt, M, N, M))
+
+
+def test_sums_respect_stride_padding():
+    M, N, ld = 33, 10, 13
+    x = np.full(M * ld, 1000.0, np.float32)
+    x.reshape(M, ld)[:, :N] = 1.0
+    assert (oracle.rowsum_f64(x, ld, M, N) == N).all()
+    assert (oracle.colsum_f64(x, ld, M, N) == M).all()
+
+
+# ---- the alignment promise -----------------------------------------------------------------------
+
+def test_promise_worked_shapes():
+    """The scale kernel's shape (4096 x 4096, 32 x 128 tiles) keeps the promise; the ragged shape
+    (4100 x 1000 under 64 x 64 tiles: 4100 % 64 = 4, 1000 % 64 = 40) breaks it."""
+    assert oracle.promise_holds(4096, 4096, 4096, 4096, 32, 128, 0x10000, 0x20000)
+    assert not oracle.promise_holds(4100, 1000, 1000, 1000, 64, 64, 0x10000, 0x20000)
+    assert not oracle.promise_holds(4096, 1000, 1000, 1000, 64, 64, 0x10000, 0x20000)
+    assert not oracle.promise_holds(4100, 1024, 1024, 1024, 64, 64, 0x10000, 0x20000)
+    assert oracle.promise_holds(4096, 1024, 1024, 1024, 64, 64, 0x10000, 0x20000)
+
+
+def test_promise_needs_16_byte_rows():
+    """Whole tiles are not enough: rows must start on 16-byte boundaries ('@aligned' licenses
+    16-byte vectors; 'The alignment constraint' asks for 16-byte rows)."""
+    ok = dict(M=64, N=64, ld_in=64, ld_out=64, TM=8, TN=8, in_addr=0x1000, out_addr=0x2000)
+    assert oracle.promise_holds(**ok)
+    for k, v in [("ld_in", 66), ("ld_out", 65), ("in_addr", 0x1004), ("out_addr", 0x2008)]:
+        bad = dict(ok, **{k: v})
+        assert not oracle.promise_holds(**bad), k
+    assert not oracle.promise_holds(**dict(ok, N=2 * 2, TN=2))      # 8-byte tile rows
+    # reductions have no 2-D output: only the input side counts
+    assert oracle.promise_holds(**dict(ok, ld_out=3, out_addr=0))
+
+
+def test_coalescing_table_byte_accounting():
+    """'What it actually costs': the printed bandwidths are the 64 MiB read over the printed
+    times in decimal GB/s (to the printed rounding)."""
+    g = _golden("coalescing_table.json")
+    M, N = g["matrix"]
+    assert M * N * 4 == g["bytes_read"]
+    for walk in ("rows", "columns"):
+        gbs = g["bytes_read"] / (g[walk]["time_us"] * 1e-6) / 1e9
+        assert abs(gbs - g[walk]["gbs"]) < 0.3
+    assert round(g["columns"]["time_us"] / g["rows"]["time_us"], 1) == g["slowdown"]
+
+
+def test_promise_whole_tiles_brute_force():
+    """'A dimension is a whole number of tiles' restated through the edge-tile count: with 16-byte
+    rows and bases, the promise holds exactly when every tile of the ceil(M/TM) x ceil(N/TN) grid
+    is full (no element of any tile masked)."""
+    for M in range(1, 25):
+        for N in range(4, 41, 4):
+            for TM in (1, 2, 4, 8, 16):
+                for TN in (4, 8, 16, 32):
+                    tiles_m, tiles_n = -(-M // TM), -(-N // TN)
+                    full = all(oracle.tile_live(M, N, TM, TN, pm, pn) == TM * TN
+                               for pm in range(tiles_m) for pn in range(tiles_n))
+                    got = oracle.promise_holds(M, N, N + (-N % 4), 4 * ((N + 7) // 4), TM, TN,
+                                               0x4000, 0x8000)
+                    assert got == full, (M, N, TM, TN)
