@@ -48,18 +48,19 @@ int orc_promise_holds(int64_t M, int64_t N, int64_t ld_in, int64_t ld_out, int64
         return 0;
     if (N % TN != 0)
         return 0;
-    /* ... and its rows may be moved as 16-byte vectors, which needs 16-byte rows
-     * ([LAYOUT] "The alignment constraint": four f32 elements) at 16-byte aligned bases. */
+    /* ... and its rows may be moved as 16-byte vectors, which needs every row to start on a
+     * 16-byte boundary ([LAYOUT] "The alignment constraint": four f32 elements): a 16-byte base
+     * and, when there is more than one row, a row stride that is a multiple of 4 elements. */
     if (TN % 4 != 0)
-        return 0;
-    if (ld_in % 4 != 0)
         return 0;
     if (in_addr % 16 != 0)
         return 0;
+    if (M > 1 && ld_in % 4 != 0)
+        return 0;
     if (out_addr != 0) {
-        if (ld_out % 4 != 0)
-            return 0;
         if (out_addr % 16 != 0)
+            return 0;
+        if (M > 1 && ld_out % 4 != 0)
             return 0;
     }
     return 1;

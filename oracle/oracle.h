@@ -50,9 +50,10 @@ int64_t orc_tile_live(int64_t M, int64_t N, int64_t TM, int64_t TN, int64_t pm, 
 /* ---- the alignment promise ([ALIGNED] "What it changes", "When the promise is broken";
  * [LAYOUT] "The alignment constraint") ------------------------------------------------------------
  * Returns 1 when an M x N tensor pair keeps the whole-tile promise for TM x TN tiles and its rows
- * may move as 16-byte vectors: M % TM == 0, N % TN == 0, TN % 4 == 0, both row strides % 4 == 0
- * and both base addresses % 16 == 0.  `out_addr == 0` means there is no 2-D output (reductions);
- * ld_out is then ignored.  Returns 0 otherwise.  Requires TM, TN > 0. */
+ * may move as 16-byte vectors: M % TM == 0, N % TN == 0, TN % 4 == 0, and every row of both
+ * tensors starts on a 16-byte boundary (base % 16 == 0 and, when M > 1, row stride % 4 == 0).
+ * `out_addr == 0` means there is no 2-D output (reductions); ld_out is then ignored.  Returns 0
+ * otherwise.  Requires TM, TN > 0. */
 int orc_promise_holds(int64_t M, int64_t N, int64_t ld_in, int64_t ld_out, int64_t TM, int64_t TN,
                       uint64_t in_addr, uint64_t out_addr);
 

@@ -365,6 +365,10 @@ def test_promise_needs_16_byte_rows():
     assert not oracle.promise_holds(**dict(ok, N=2 * 2, TN=2))      # 8-byte tile rows
     # reductions have no 2-D output: only the input side counts
     assert oracle.promise_holds(**dict(ok, ld_out=3, out_addr=0))
+    # a single row starts at the base: its stride plays no part
+    one = dict(ok, M=1, TM=1)
+    assert oracle.promise_holds(**dict(one, ld_in=65, ld_out=67))
+    assert not oracle.promise_holds(**dict(one, in_addr=0x1004))
 
 
 def test_coalescing_table_byte_accounting():
