@@ -1,0 +1,239 @@
+// colred.hip -- column sums for gfx950 over row-major f32: the naive strided walk and the
+// LDS-staged coalesced walk, both followed by a fixed-order pass over per-slab partials.
+//
+// Sources (web pages): teenygrad "Memory Coalescing and Tensor Layout" ("What it actually costs":
+// the row and column walks of one 4096 x 4096 matrix, 65536 programs of 256 elements, column index
+// varying fastest across programs; "Seeing it in a real kernel" and "A checklist": stage a tile in
+// fast memory, then read it in any order); Phobos docs "Slicing, bounds and masking" ("Masking":
+// out-of-range elements read as 0).
+//
+// Both walks cut the rows into slabs of TM rows and write one partial per (slab, column) into the
+// caller's workspace ws[slab * N + column]; colsum_finish then adds each column's partials in slab
+// order.  Nothing uses atomics, so results are deterministic.
+//
+// Naive walk: one workgroup per (slab, column), column fastest; lane t reads row slab*TM + t of
+// that column.  The lane-varying term of the address is row * ld: every lane touches its own
+// cache line.
+//
+// LDS walk: one workgroup per (slab, strip of TW columns), strip fastest.  LPR = TW / W lanes
+// cover one row of the strip with consecutive 16-byte chunks (W = 4; W = 1 on the scalar path), so
+// the 256 threads read RP = 256 / LPR rows at a time, fully coalesced, and each thread keeps
+// running column partials in registers while walking down the slab.  The RP x TW partials are then
+// staged in LDS row by row and read back column by column: thread c adds the RP values of column c
+// in fixed order.  Writes into LDS are consecutive 16-byte chunks and reads are consecutive dwords,
+// so neither side has bank conflicts and no padding is needed.
+#include "device.hpp"
+#include "launch.h"
+
+namespace tmk {
+namespace {
+
+struct ColArgs {
+    const float *x;
+    float *ws;
+    int64_t ld, M, N;
+    int log_tm;
+    uint32_t strips;  // LDS walk: strips of TW columns; naive walk: N
+    uint32_t slabs;
+};
+
+// ---- naive walk ------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void col_naive(ColArgs a) {
+    __shared__ float wave_sum[kBlock / 64];
+    const int t = threadIdx.x;
+    const int nwaves = blockDim.x / 64;
+    const int64_t tm = int64_t(1) << a.log_tm;
+    const uint64_t nwork = uint64_t(a.slabs) * uint64_t(a.N);
+    for (uint64_t w = blockIdx.x; w < nwork; w += gridDim.x) {
+        const uint64_t slab = w / uint64_t(a.N);
+        const int64_t c = int64_t(w - slab * uint64_t(a.N));
+        const int64_t row = int64_t(slab) * tm + t;
+        float v = 0.0f;  // rows past the slab or past M read as 0
+        if (t < tm && row < a.M)
+            v = a.x[row * a.ld + c];
+        v = group_reduce<SumOp, 64>(v);
+        if ((t & 63) == 0)
+            wave_sum[t >> 6] = v;
+        __syncthreads();
+        if (t == 0) {
+            float s = wave_sum[0];
+            for (int i = 1; i < nwaves; ++i)
+                s += wave_sum[i];
+            a.ws[int64_t(slab) * a.N + c] = s;
+        }
+        __syncthreads();
+    }
+}
+
+// ---- LDS-staged walk -------------------------------------------------------------------------
+
+constexpr int kRowsInFlight = 8;  // rows each thread loads before adding
+
+template <bool VEC>
+__device__ __forceinline__ auto chunk_or_zero(const float *p, int64_t live) {
+    if constexpr (VEC) {
+        if (live >= 4)
+            return ld16(p);
+        f4 r = f4(0.0f);
+        if (live > 0)
+            r.x = p[0];
+        if (live > 1)
+            r.y = p[1];
+        if (live > 2)
+            r.z = p[2];
+        return r;
+    } else {
+        return live > 0 ? *p : 0.0f;
+    }
+}
+
+template <bool VEC, bool ALIGNED, int LPR>
+__global__ __launch_bounds__(kBlock) void col_lds(ColArgs a) {
+    using T = typename std::conditional<VEC, f4, float>::type;
+    constexpr int W = VEC ? 4 : 1;
+    constexpr int RP = kBlock / LPR;  // rows read per step
+    constexpr int TW = LPR * W;       // strip width in columns
+    __shared__ float part[RP * TW];   // kBlock * W floats
+
+    const int t = threadIdx.x;
+    const int g = t % LPR;
+    const int q = t / LPR;
+    const int64_t tm = int64_t(1) << a.log_tm;
+    const uint64_t nwork = uint64_t(a.slabs) * a.strips;
+
+    for (uint64_t w = blockIdx.x; w < nwork; w += gridDim.x) {
+        const uint64_t slab = w / a.strips;
+        const int64_t strip = int64_t(w - slab * a.strips);
+        const int64_t col0 = strip * TW;
+        const int64_t row0 = int64_t(slab) << a.log_tm;
+        const int64_t c = col0 + g * W;
+        const int64_t live = a.N - c;  // elements of this thread's chunk inside the tensor
+        const float *p = a.x + row0 * a.ld + c;
+        const int64_t rows = ALIGNED ? tm : (a.M - row0 < tm ? a.M - row0 : tm);
+
+        T acc[kRowsInFlight];
+#pragma unroll
+        for (int u = 0; u < kRowsInFlight; ++u)
+            acc[u] = T(0.0f);
+        for (int64_t r = q; r < rows; r += int64_t(RP) * kRowsInFlight) {
+            T v[kRowsInFlight];
+#pragma unroll
+            for (int u = 0; u < kRowsInFlight; ++u) {
+                const int64_t rr = r + int64_t(u) * RP;
+                v[u] = T(0.0f);
+                if (rr < rows) {
+                    if constexpr (ALIGNED)
+                        v[u] = ld16(p + rr * a.ld);
+                    else
+                        v[u] = chunk_or_zero<VEC>(p + rr * a.ld, live);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kRowsInFlight; ++u)
+                acc[u] += v[u];
+        }
+        // Fixed-order fold of the row accumulators.
+        T s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+
+        // Stage: row q of the partials, columns g*W .. g*W+W-1.
+        if constexpr (VEC)
+            *reinterpret_cast<f4 *>(&part[q * TW + g * W]) = s;
+        else
+            part[q * TW + g] = s;
+        __syncthreads();
+        // Read back by column: thread cl adds the RP partials of column cl in order.
+        for (int cl = t; cl < TW; cl += kBlock) {
+            float colsum = 0.0f;
+            for (int k = 0; k < RP; ++k)
+                colsum += part[k * TW + cl];
+            if (col0 + cl < a.N)
+                a.ws[int64_t(slab) * a.N + col0 + cl] = colsum;
+        }
+        __syncthreads();
+    }
+}
+
+// ---- pass 2: fixed-order sum of the slab partials ---------------------------------------------
+
+constexpr uint32_t kFinishBlock = 32;  // partials added before joining the running total
+
+__global__ __launch_bounds__(kBlock) void colsum_finish(const float *ws, float *out, int64_t N,
+                                                      uint32_t slabs) {
+    for (int64_t j = int64_t(blockIdx.x) * kBlock + threadIdx.x; j < N;
+         j += int64_t(gridDim.x) * kBlock) {
+        float total = 0.0f;
+        for (uint32_t s0 = 0; s0 < slabs; s0 += kFinishBlock) {
+            const uint32_t s1 = s0 + kFinishBlock < slabs ? s0 + kFinishBlock : slabs;
+            float blk = 0.0f;
+            for (uint32_t s = s0; s < s1; ++s)
+                blk += ws[int64_t(s) * N + j];
+            total += blk;
+        }
+        out[j] = total;
+    }
+}
+
+template <bool VEC, bool AL>
+const void *pick_lpr(int lpr) {
+    switch (lpr) {
+    case 1: return reinterpret_cast<const void *>(&col_lds<VEC, AL, 1>);
+    case 2: return reinterpret_cast<const void *>(&col_lds<VEC, AL, 2>);
+    case 4: return reinterpret_cast<const void *>(&col_lds<VEC, AL, 4>);
+    case 8: return reinterpret_cast<const void *>(&col_lds<VEC, AL, 8>);
+    case 16: return reinterpret_cast<const void *>(&col_lds<VEC, AL, 16>);
+    case 32: return reinterpret_cast<const void *>(&col_lds<VEC, AL, 32>);
+    case 64: return reinterpret_cast<const void *>(&col_lds<VEC, AL, 64>);
+    case 128: return reinterpret_cast<const void *>(&col_lds<VEC, AL, 128>);
+    default: return reinterpret_cast<const void *>(&col_lds<VEC, AL, 256>);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_cols(const tmp::ColPlan &p, hipStream_t stream) {
+    constexpr uint32_t kGridCap = 1u << 20;
+    if (p.launch) {
+        ColArgs a;
+        a.x = p.x;
+        a.ws = p.ws;
+        a.ld = p.ld;
+        a.M = p.M;
+        a.N = p.N;
+        a.log_tm = p.log_tm;
+        a.strips = p.strips;
+        a.slabs = p.slabs;
+        void *args[] = {&a};
+        const uint64_t nwork = uint64_t(p.slabs) * p.strips;
+        const uint32_t grid = static_cast<uint32_t>(nwork < kGridCap ? nwork : kGridCap);
+        hipError_t err;
+        if (p.walk == TM_COL_LDS) {
+            const int W = p.vec ? 4 : 1;
+            const int lpr = p.tw / W;
+            // 16-byte chunks are only used when the host checked 16-byte rows; the unmasked body
+            // only when it also checked whole tiles.
+            const void *fn = p.vec ? (p.aligned ? pick_lpr<true, true>(lpr) : pick_lpr<true, false>(lpr))
+                                   : pick_lpr<false, false>(lpr);
+            err = hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, stream);
+        } else {
+            err = hipLaunchKernel(reinterpret_cast<const void *>(&col_naive), dim3(grid),
+                                  dim3(p.naive_block), args, 0, stream);
+        }
+        if (err != hipSuccess)
+            return err;
+    }
+    if (p.finish) {
+        const int64_t blocks = (p.N + kBlock - 1) / kBlock;
+        const uint32_t grid = static_cast<uint32_t>(blocks < kGridCap ? blocks : kGridCap);
+        const float *ws = p.ws;
+        float *out = p.out;
+        int64_t N = p.N;
+        uint32_t slabs = p.launch ? p.slabs : 0u;
+        void *args[] = {&ws, &out, &N, &slabs};
+        return hipLaunchKernel(reinterpret_cast<const void *>(&colsum_finish), dim3(grid),
+                               dim3(kBlock), args, 0, stream);
+    }
+    return hipSuccess;
+}
+
+}  // namespace tmk

@@ -1,0 +1,67 @@
+// device.hpp -- gfx950 device helpers shared by the tilemap kernels: 16-byte vector access,
+// masked loads, and wavefront reductions built from DPP, ds_swizzle and readlane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace tmk {
+
+constexpr int kBlock = 256;  // threads per workgroup: four wave64s
+constexpr float kMaxFill = -1.0e30f;  // masked-max fill, f32 bits 0xF149F2CA
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load / store (global_load_dwordx4 / global_store_dwordx4); p must be 16-byte aligned.
+__device__ __forceinline__ f4 ld16(const float *p) { return *reinterpret_cast<const f4 *>(p); }
+__device__ __forceinline__ void st16(float *p, f4 v) { *reinterpret_cast<f4 *>(p) = v; }
+
+// ---- reduction operators ------------------------------------------------------------------
+struct SumOp {
+    static constexpr float kFill = 0.0f;  // masked elements read as 0
+    __device__ __forceinline__ static float f(float a, float b) { return a + b; }
+};
+struct MaxOp {
+    static constexpr float kFill = kMaxFill;  // a value no real score reaches
+    __device__ __forceinline__ static float f(float a, float b) { return __builtin_fmaxf(a, b); }
+};
+
+// ---- cross-lane moves ---------------------------------------------------------------------
+// DPP controls (GFX9 encoding): quad_perm [1,0,3,2] swaps lane pairs, [2,3,0,1] swaps pairs of
+// pairs, row_half_mirror reverses each 8-lane half-row, row_mirror reverses each 16-lane row.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+// ds_swizzle bit-mask mode: and_mask 0x1F, or_mask 0, xor_mask 0x10 -> lane ^ 16 within 32 lanes.
+constexpr int kSwizzleXor16 = 0x401F;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float swizzle_xor16(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16));
+}
+
+// Combine `v` over aligned groups of LPR consecutive lanes (LPR a power of two <= 64).  Every lane
+// of a group ends with the same bits: each step combines two equal-sized halves whose values are
+// uniform, and the operators are commutative.  All 64 lanes of the wave must be active.
+template <class Op, int LPR>
+__device__ __forceinline__ float group_reduce(float v) {
+    if constexpr (LPR >= 2) v = Op::f(v, dpp<kDppXor1>(v));
+    if constexpr (LPR >= 4) v = Op::f(v, dpp<kDppXor2>(v));
+    if constexpr (LPR >= 8) v = Op::f(v, dpp<kDppHalfMirror>(v));
+    if constexpr (LPR >= 16) v = Op::f(v, dpp<kDppMirror>(v));
+    if constexpr (LPR >= 32) v = Op::f(v, swizzle_xor16(v));
+    if constexpr (LPR >= 64) {
+        const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+        const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+        v = Op::f(lo, hi);
+    }
+    return v;
+}
+
+}  // namespace tmk

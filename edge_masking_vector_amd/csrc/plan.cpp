@@ -1,0 +1,316 @@
+// plan.cpp -- argument checks, the alignment-promise checker, the loop remainder split and the
+// tile scheduler of libtilemap.  Pure host C++17 (no HIP), run before anything is enqueued.
+//
+// Sources (web pages): Phobos docs "@aligned" ("What it changes", "When the promise is broken");
+// Phobos docs "Slicing, bounds and masking" ("Masking", "Loops over a dynamic extent");
+// teenygrad "Memory Coalescing and Tensor Layout" ("The alignment constraint").
+#include "plan.h"
+
+#include <algorithm>
+#include <climits>
+
+namespace tmp {
+
+namespace {
+
+// Workgroups launched at most per kernel; larger jobs loop over their work inside the grid.
+// 2^20 workgroups of 256 threads stays far inside the 2^32 work-item limit of one dispatch.
+constexpr uint32_t kGridCap = 1u << 20;
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+bool aligned_to(const void *p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// One M x N view with row stride ld.  `work`: the call will touch it (M > 0 and N > 0).
+int check_view(const void *p, int64_t M, int64_t N, int64_t ld, bool work) {
+    if (M < 0 || N < 0 || ld < 0 || ld < N)
+        return TM_E_INVAL;
+    if (!work)
+        return TM_OK;
+    if (p == nullptr || !aligned_to(p, 4))
+        return TM_E_INVAL;
+    // (M - 1) * ld + N elements must be addressable with int64 byte offsets.
+    const int64_t lim = (INT64_MAX / 4) - N;
+    if (ld > 0 && (M - 1) > lim / ld)
+        return TM_E_INVAL;
+    return TM_OK;
+}
+
+// A contiguous vector of n floats (reduction outputs, workspaces).
+int check_vector(const void *p, int64_t n) {
+    if (n == 0)
+        return TM_OK;
+    if (p == nullptr || !aligned_to(p, 4))
+        return TM_E_INVAL;
+    return TM_OK;
+}
+
+// Every row of an M-row view with stride ld starts on a 16-byte boundary: a 16-byte base and,
+// when there is more than one row, a stride of whole 16-byte units.
+bool rows16(const void *p, int64_t M, int64_t ld) {
+    return aligned_to(p, 16) && (M <= 1 || ld % 4 == 0);
+}
+
+// Whole tiles and 16-byte rows ([ALIGNED] "What it changes"; [LAYOUT] "The alignment constraint").
+bool promise_holds(int64_t M, int64_t N, int64_t ld_in, int64_t ld_out, int TM, int TN,
+                   const void *in, const void *out) {
+    if (M % TM != 0 || N % TN != 0)
+        return false;
+    if (TN % 4 != 0 || !rows16(in, M, ld_in))
+        return false;
+    if (out != nullptr && !rows16(out, M, ld_out))
+        return false;
+    return true;
+}
+
+uint32_t cap_grid(int64_t work_items) {
+    return static_cast<uint32_t>(std::min<int64_t>(work_items, kGridCap));
+}
+
+}  // namespace
+
+int ilog2(int64_t v) {
+    int l = 0;
+    while ((int64_t{1} << l) < v)
+        ++l;
+    return l;
+}
+
+int split(int64_t K, int64_t T, int64_t *nfull, int64_t *rem) {
+    // [SLICING] "Loops over a dynamic extent": whole tiles need no mask; what is left over (if
+    // anything) is one masked tile.
+    if (K < 0 || T <= 0 || nfull == nullptr || rem == nullptr)
+        return TM_E_INVAL;
+    *nfull = K / T;
+    *rem = K - *nfull * T;
+    return TM_OK;
+}
+
+int check_tile(int TM, int TN) {
+    if (TM <= 0 || TN <= 0)
+        return TM_E_INVAL;  // a divisor must be positive ([ALIGNED] "When the promise is broken")
+    if (!is_pow2(TM) || TM > kMaxTM || !is_pow2(TN) || TN > kMaxTN)
+        return TM_E_UNSUPPORTED;  // not a tile the kernels were built for
+    return TM_OK;
+}
+
+int check_promise(int64_t M, int64_t N, int64_t ld_in, int64_t ld_out, int TM, int TN,
+                  const void *in, const void *out) {
+    if (M < 0 || N < 0 || ld_in < N || (out != nullptr && ld_out < N) || TM <= 0 || TN <= 0)
+        return TM_E_INVAL;
+    int st = check_tile(TM, TN);
+    if (st != TM_OK)
+        return st;
+    return promise_holds(M, N, ld_in, ld_out, TM, TN, in, out) ? TM_OK : TM_E_ALIGN;
+}
+
+int plan_tiles(int64_t M, int64_t N, int TM, int TN, int64_t *tiles_m, int64_t *tiles_n,
+               int64_t *whole) {
+    if (tiles_m == nullptr || tiles_n == nullptr || whole == nullptr || M < 0 || N < 0)
+        return TM_E_INVAL;
+    int st = check_tile(TM, TN);
+    if (st != TM_OK)
+        return st;
+    *tiles_m = ceil_div(M, TM);
+    *tiles_n = ceil_div(N, TN);
+    *whole = (M / TM) * (N / TN);  // tiles with (pm+1)*TM <= M and (pn+1)*TN <= N
+    return TM_OK;
+}
+
+// ---- element-wise maps ------------------------------------------------------------------------
+
+int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t M, int64_t N,
+             float alpha, float beta, int TM, int TN, int aligned, int variant, MapPlan *plan) {
+    *plan = MapPlan{};
+    if (op < kAffine || op > kCopy)
+        return TM_E_INVAL;
+    if (aligned != 0 && aligned != 1)
+        return TM_E_INVAL;
+    if (variant < TM_VAR_AUTO || variant > TM_VAR_VEC4)
+        return TM_E_INVAL;
+    if (M < 0 || N < 0 || TM <= 0 || TN <= 0)
+        return TM_E_INVAL;
+    const bool work = M > 0 && N > 0;
+    int st;
+    if ((st = check_view(x, M, N, ldx, work)) != TM_OK)
+        return st;
+    if ((st = check_view(y, M, N, ldy, work)) != TM_OK)
+        return st;
+    if ((st = check_tile(TM, TN)) != TM_OK)
+        return st;
+    if (aligned && !promise_holds(M, N, ldx, ldy, TM, TN, x, y))
+        return TM_E_ALIGN;  // checked once, before any launch ([ALIGNED] "When the promise is broken")
+
+    // 16-byte vectors are legal when every vector a thread moves starts on a 16-byte boundary.
+    const bool vec16 = TN % 4 == 0 && rows16(x, M, ldx) && rows16(y, M, ldy);
+    int access;
+    switch (variant) {
+    case TM_VAR_AUTO: access = vec16 ? kVec4 : kScalar; break;
+    case TM_VAR_SCALAR: access = kScalar; break;
+    case TM_VAR_VEC4_UNDERSTATED:
+        if (TN % 4 != 0)
+            return TM_E_UNSUPPORTED;
+        access = kVec4Understated;
+        break;
+    default:
+        if (!vec16)
+            return TM_E_ALIGN;
+        access = kVec4;
+        break;
+    }
+    if (!work)
+        return TM_OK;
+
+    int64_t tiles_m, tiles_n, whole;
+    plan_tiles(M, N, TM, TN, &tiles_m, &tiles_n, &whole);
+    if (tiles_m * tiles_n > INT32_MAX || tiles_n > INT32_MAX)
+        return TM_E_UNSUPPORTED;  // tile ids are 32-bit on the device
+
+    const int W = access == kScalar ? 1 : 4;
+    plan->launch = true;
+    plan->op = op;
+    plan->access = access;
+    plan->aligned = aligned;
+    plan->log_tm = ilog2(TM);
+    plan->log_tn = ilog2(TN);
+    plan->log_vr = ilog2(TN / W);
+    plan->slots = static_cast<uint32_t>(int64_t{TM} * TN / W);
+    if (plan->slots >= static_cast<uint32_t>(kBlock)) {
+        plan->unroll = static_cast<int>(std::min<uint32_t>(4, plan->slots / kBlock));
+        plan->guard = false;
+    } else {
+        plan->unroll = 1;
+        plan->guard = true;
+    }
+    plan->tiles_n = static_cast<uint32_t>(tiles_n);
+    plan->ntiles = static_cast<uint32_t>(tiles_m * tiles_n);
+    plan->grid = cap_grid(plan->ntiles);
+    plan->x = x;
+    plan->y = y;
+    plan->ldx = ldx;
+    plan->ldy = ldy;
+    plan->M = M;
+    plan->N = N;
+    plan->alpha = alpha;
+    plan->beta = beta;
+    return TM_OK;
+}
+
+// ---- row reductions ---------------------------------------------------------------------------
+
+int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TR, int TC,
+              int aligned, RowPlan *plan) {
+    *plan = RowPlan{};
+    if (op != kRowSum && op != kRowMax)
+        return TM_E_INVAL;
+    if (aligned != 0 && aligned != 1)
+        return TM_E_INVAL;
+    if (M < 0 || N < 0 || TR <= 0 || TC <= 0)
+        return TM_E_INVAL;
+    int st;
+    if ((st = check_view(x, M, N, ld, M > 0 && N > 0)) != TM_OK)
+        return st;
+    if ((st = check_vector(out, M)) != TM_OK)
+        return st;
+    if ((st = check_tile(TR, TC)) != TM_OK)
+        return st;
+    if (aligned && !promise_holds(M, N, ld, 0, TR, TC, x, nullptr))
+        return TM_E_ALIGN;
+    if (M == 0)
+        return TM_OK;
+
+    const bool vec = TC % 4 == 0 && rows16(x, M, ld);
+    const int W = vec ? 4 : 1;
+    plan->launch = true;
+    plan->op = op;
+    plan->vec = vec;
+    plan->lpr = std::min(64, TC / W);
+    plan->per_tile = TC / (W * plan->lpr);
+    plan->bc = TC;
+    split(N, TC, &plan->nfull, &plan->rem);  // whole column tiles + one masked remainder tile
+    const int64_t groups = ceil_div(M, kBlock / plan->lpr);
+    if (groups > INT32_MAX)
+        return TM_E_UNSUPPORTED;  // row-group ids are 32-bit on the device
+    plan->grid = cap_grid(groups);
+    plan->x = x;
+    plan->out = out;
+    plan->ld = ld;
+    plan->M = M;
+    plan->N = N;
+    return TM_OK;
+}
+
+// ---- column sums ------------------------------------------------------------------------------
+
+size_t colsum_ws_bytes(int64_t M, int64_t N, int TM, int TN, int walk) {
+    if (M <= 0 || N <= 0 || check_tile(TM, TN) != TM_OK)
+        return 0;
+    if (walk != TM_COL_NAIVE && walk != TM_COL_LDS)
+        return 0;
+    const int64_t slabs = ceil_div(M, TM);
+    if (slabs > INT64_MAX / 4 / N)
+        return 0;
+    return static_cast<size_t>(slabs * N * 4);
+}
+
+int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TM, int TN,
+              int aligned, int walk, void *ws, size_t ws_bytes, ColPlan *plan) {
+    *plan = ColPlan{};
+    if (walk != TM_COL_NAIVE && walk != TM_COL_LDS)
+        return TM_E_INVAL;
+    if (aligned != 0 && aligned != 1)
+        return TM_E_INVAL;
+    if (M < 0 || N < 0 || TM <= 0 || TN <= 0)
+        return TM_E_INVAL;
+    int st;
+    if ((st = check_view(x, M, N, ld, M > 0 && N > 0)) != TM_OK)
+        return st;
+    if ((st = check_vector(out, N)) != TM_OK)
+        return st;
+    if ((st = check_tile(TM, TN)) != TM_OK)
+        return st;
+    const int64_t slabs = ceil_div(M, TM);
+    const size_t need = colsum_ws_bytes(M, N, TM, TN, walk);
+    if (slabs > INT32_MAX || (M > 0 && N > 0 && need == 0))
+        return TM_E_UNSUPPORTED;  // partial count or workspace size out of range
+    if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned_to(ws, 4)))
+        return TM_E_WORKSPACE;
+    if (aligned && !promise_holds(M, N, ld, 0, TM, TN, x, nullptr))
+        return TM_E_ALIGN;
+    if (N == 0)
+        return TM_OK;
+
+    plan->finish = true;
+    plan->launch = M > 0;
+    plan->walk = walk;
+    plan->aligned = aligned;
+    plan->log_tm = ilog2(TM);
+    plan->slabs = static_cast<uint32_t>(slabs);
+    plan->vec = TN % 4 == 0 && rows16(x, M, ld);
+    if (walk == TM_COL_LDS) {
+        const int W = plan->vec ? 4 : 1;
+        plan->tw = std::min(TN, kBlock * W);
+        const int64_t strips = ceil_div(N, plan->tw);
+        if (strips > INT32_MAX)
+            return TM_E_UNSUPPORTED;
+        plan->strips = static_cast<uint32_t>(strips);
+    } else {
+        plan->naive_block = std::max(64, TM);
+        if (N > INT32_MAX)
+            return TM_E_UNSUPPORTED;
+        plan->strips = static_cast<uint32_t>(N);
+    }
+    plan->x = x;
+    plan->out = out;
+    plan->ws = static_cast<float *>(ws);
+    plan->ld = ld;
+    plan->M = M;
+    plan->N = N;
+    return TM_OK;
+}
+
+}  // namespace tmp

@@ -1,0 +1,101 @@
+// plan.h -- host-side argument checks, the alignment-promise checker and the tile scheduler of
+// libtilemap.  Pure C++17: no HIP header, so this logic builds and runs on any CPU.
+//
+// Every tm_* entry point calls one plan_* function before touching the GPU.  A plan either
+// rejects the call (status != TM_OK, nothing launched) or describes the launches completely:
+// which kernel variant, how tiles map to workgroups, and how many workgroups.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/tilemap.h"
+
+namespace tmp {
+
+constexpr int kMaxTM = 256;   // row tile (TM, BR) menu: 1, 2, 4, ..., 256
+constexpr int kMaxTN = 1024;  // column tile (TN, BC) menu: 1, 2, 4, ..., 1024
+constexpr int kBlock = 256;   // threads per workgroup of every kernel (4 wave64s)
+
+enum MapOp { kAffine = 0, kScale = 1, kCopy = 2 };
+enum Access { kScalar = 1, kVec4Understated = 2, kVec4 = 3 };
+
+int ilog2(int64_t v);  // v a power of two
+
+// ---- element-wise maps ---------------------------------------------------------------------
+struct MapPlan {
+    bool launch = false;          // false: valid call with no work
+    int op = kAffine;
+    int access = kScalar;         // resolved variant
+    int aligned = 0;              // whole tiles promised and checked: kernels carry no masks
+    int unroll = 1;               // vectors per thread per chunk (1, 2, 4)
+    bool guard = false;           // tile smaller than one workgroup pass: guard slot < slots
+    int log_tm = 0, log_tn = 0;   // tile extents
+    int log_vr = 0;               // log2(vectors per tile row)
+    uint32_t slots = 0;           // vectors per tile
+    uint32_t tiles_n = 0;         // tiles along N
+    uint32_t ntiles = 0;          // tiles in all
+    uint32_t grid = 0;            // workgroups
+    const float *x = nullptr;
+    float *y = nullptr;
+    int64_t ldx = 0, ldy = 0, M = 0, N = 0;
+    float alpha = 0.f, beta = 0.f;
+};
+
+int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t M, int64_t N,
+             float alpha, float beta, int TM, int TN, int aligned, int variant, MapPlan *plan);
+
+// ---- row reductions (sum, masked max) ------------------------------------------------------
+enum RowOp { kRowSum = 0, kRowMax = 1 };
+
+struct RowPlan {
+    bool launch = false;
+    int op = kRowSum;
+    bool vec = false;             // 16-byte loads
+    int lpr = 1;                  // lanes per row (power of two <= 64)
+    int per_tile = 1;             // vectors per lane per column tile
+    int64_t nfull = 0;            // whole column tiles (unmasked)
+    int64_t rem = 0;              // live columns of the remainder tile (0: none)
+    int bc = 1;                   // column tile width
+    uint32_t grid = 0;
+    const float *x = nullptr;
+    float *out = nullptr;
+    int64_t ld = 0, M = 0, N = 0;
+};
+
+int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TR, int TC,
+              int aligned, RowPlan *plan);
+
+// ---- column sums ---------------------------------------------------------------------------
+struct ColPlan {
+    bool launch = false;          // pass 1 needed (M > 0)
+    bool finish = false;          // pass 2 needed (N > 0)
+    int walk = TM_COL_NAIVE;
+    bool vec = false;
+    int aligned = 0;
+    int log_tm = 0;
+    int tw = 1;                   // columns per workgroup (LDS walk)
+    int naive_block = 64;         // threads per workgroup (naive walk)
+    uint32_t slabs = 0;           // ceil(M / TM): partials per column
+    uint32_t strips = 0;          // column strips (LDS walk) or columns (naive walk)
+    const float *x = nullptr;
+    float *out = nullptr;
+    float *ws = nullptr;
+    int64_t ld = 0, M = 0, N = 0;
+};
+
+size_t colsum_ws_bytes(int64_t M, int64_t N, int TM, int TN, int walk);
+
+int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TM, int TN,
+              int aligned, int walk, void *ws, size_t ws_bytes, ColPlan *plan);
+
+// ---- pieces shared by the planners (exported through the C ABI as host helpers) -------------
+// Loop remainder split: K columns in steps of T = *nfull whole tiles + one tile of *rem columns.
+int split(int64_t K, int64_t T, int64_t *nfull, int64_t *rem);
+int check_tile(int TM, int TN);
+int check_promise(int64_t M, int64_t N, int64_t ld_in, int64_t ld_out, int TM, int TN,
+                  const void *in, const void *out);
+int plan_tiles(int64_t M, int64_t N, int TM, int TN, int64_t *tiles_m, int64_t *tiles_n,
+               int64_t *whole);
+
+}  // namespace tmp

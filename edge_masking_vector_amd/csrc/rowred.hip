@@ -1,0 +1,170 @@
+// rowred.hip -- row reductions for gfx950: row sums and masked row maxima over row-major f32.
+//
+// Sources (web pages): Phobos docs "Slicing, bounds and masking" ("Loops over a dynamic extent":
+// whole tiles unmasked plus one masked remainder; "Reductions over a ragged tile": the masked
+// maximum takes -1.0e30 where iota(1) >= N - kt); teenygrad "Memory Coalescing and Tensor Layout"
+// ("What it actually costs": the stride-1 row walk).
+//
+// Mapping.  A row is owned by a group of LPR consecutive lanes (LPR = BC / W, at most 64, where W
+// = 4 elements per 16-byte chunk or 1 on the scalar path), so one column tile is one chunk per lane
+// per step and the lanes of a group read consecutive chunks of the row: a wave reads 64/LPR rows,
+// LPR*16 contiguous bytes each.  The walk over column tiles is split in two: `nfull` whole tiles
+// with no mask at all, issued 16 chunks at a time before any arithmetic, then one remainder tile
+// where a chunk element at tile-local column c is kept iff c < N - kt and otherwise replaced by the
+// operator's fill (0 for a sum, -1.0e30f for a maximum).  Lane partials are folded in a fixed tree,
+// then across the group with DPP row operations, ds_swizzle and readlane.  Rows past M re-read row
+// M-1 (so every lane stays active for the cross-lane steps) and are not stored.
+#include "device.hpp"
+#include "launch.h"
+
+namespace tmk {
+namespace {
+
+struct RowArgs {
+    const float *x;
+    float *out;
+    int64_t ld, M, N;
+    int64_t nfull;      // whole column tiles
+    int64_t rem;        // live columns of the remainder tile (0 = no remainder tile)
+    int64_t bc;         // column tile width
+    int per_tile;       // chunks per lane per column tile
+    uint32_t ngroups;   // row groups of kBlock / LPR rows
+};
+
+constexpr int kLoads = 16;  // chunks in flight per lane
+constexpr int kAcc = 4;     // independent accumulators per lane
+
+template <class Op>
+__device__ __forceinline__ float combine(float a, float b) { return Op::f(a, b); }
+template <class Op>
+__device__ __forceinline__ f4 combine(f4 a, f4 b) {
+    f4 r;
+    r.x = Op::f(a.x, b.x);
+    r.y = Op::f(a.y, b.y);
+    r.z = Op::f(a.z, b.z);
+    r.w = Op::f(a.w, b.w);
+    return r;
+}
+
+template <class Op>
+__device__ __forceinline__ float lanes(float v) { return v; }
+template <class Op>
+__device__ __forceinline__ float lanes(f4 v) { return Op::f(Op::f(v.x, v.y), Op::f(v.z, v.w)); }
+
+template <bool VEC>
+__device__ __forceinline__ auto load_whole(const float *p) {
+    if constexpr (VEC)
+        return ld16(p);
+    else
+        return *p;
+}
+
+// Chunk at p whose first `live` elements exist (live may be <= 0); the others take the fill.
+template <class Op, bool VEC>
+__device__ __forceinline__ auto load_fill(const float *p, int64_t live) {
+    if constexpr (VEC) {
+        if (live >= 4)
+            return ld16(p);
+        f4 r = f4(Op::kFill);
+        if (live > 0)
+            r.x = p[0];
+        if (live > 1)
+            r.y = p[1];
+        if (live > 2)
+            r.z = p[2];
+        return r;
+    } else {
+        return live > 0 ? *p : Op::kFill;
+    }
+}
+
+template <class Op, int LPR, bool VEC>
+__global__ __launch_bounds__(kBlock) void row_reduce(RowArgs a) {
+    using T = typename std::conditional<VEC, f4, float>::type;
+    constexpr int W = VEC ? 4 : 1;
+    constexpr int kRows = kBlock / LPR;  // rows per workgroup
+    constexpr int64_t kStep = int64_t(LPR) * W;  // columns a group covers per chunk step
+    const int t = threadIdx.x;
+    const int g = t % LPR;  // lane within the row group
+
+    for (uint32_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
+        const int64_t row = int64_t(grp) * kRows + t / LPR;
+        const int64_t rr = row < a.M ? row : a.M - 1;
+        const float *xr = a.x + rr * a.ld;
+        const float *p = xr + g * W;
+
+        T acc[kAcc];
+#pragma unroll
+        for (int i = 0; i < kAcc; ++i)
+            acc[i] = T(Op::kFill);
+
+        // Whole tiles: chunk k of this lane sits at column (k * LPR + g) * W; no masks.
+        const int64_t main_chunks = a.nfull * a.per_tile;
+        for (int64_t k = 0; k < main_chunks; k += kLoads) {
+            T v[kLoads];
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u)
+                v[u] = (k + u < main_chunks) ? load_whole<VEC>(p + (k + u) * kStep) : T(Op::kFill);
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u)
+                acc[u % kAcc] = combine<Op>(acc[u % kAcc], v[u]);
+        }
+
+        // The one remainder tile, starting at column kt: tile-local column c keeps its value iff
+        // c < N - kt.
+        if (a.rem > 0) {
+            const int64_t kt = a.nfull * a.bc;
+            for (int f = 0; f < a.per_tile; ++f) {
+                const int64_t c = int64_t(f) * kStep + g * W;  // tile-local column of the chunk
+                acc[0] = combine<Op>(acc[0], load_fill<Op, VEC>(xr + kt + c, a.N - kt - c));
+            }
+        }
+
+        // Fixed-order fold: accumulators pairwise, then the chunk's elements, then the lanes.
+        T s = combine<Op>(combine<Op>(acc[0], acc[1]), combine<Op>(acc[2], acc[3]));
+        float r = lanes<Op>(s);
+        r = group_reduce<Op, LPR>(r);
+        if (g == 0 && row < a.M)
+            a.out[row] = r;
+    }
+}
+
+template <class Op, bool VEC>
+const void *pick_lpr(int lpr) {
+    switch (lpr) {
+    case 1: return reinterpret_cast<const void *>(&row_reduce<Op, 1, VEC>);
+    case 2: return reinterpret_cast<const void *>(&row_reduce<Op, 2, VEC>);
+    case 4: return reinterpret_cast<const void *>(&row_reduce<Op, 4, VEC>);
+    case 8: return reinterpret_cast<const void *>(&row_reduce<Op, 8, VEC>);
+    case 16: return reinterpret_cast<const void *>(&row_reduce<Op, 16, VEC>);
+    case 32: return reinterpret_cast<const void *>(&row_reduce<Op, 32, VEC>);
+    default: return reinterpret_cast<const void *>(&row_reduce<Op, 64, VEC>);
+    }
+}
+
+template <class Op>
+const void *pick_vec(const tmp::RowPlan &p) {
+    return p.vec ? pick_lpr<Op, true>(p.lpr) : pick_lpr<Op, false>(p.lpr);
+}
+
+}  // namespace
+
+hipError_t launch_rows(const tmp::RowPlan &p, hipStream_t stream) {
+    RowArgs a;
+    a.x = p.x;
+    a.out = p.out;
+    a.ld = p.ld;
+    a.M = p.M;
+    a.N = p.N;
+    a.nfull = p.nfull;
+    a.rem = p.rem;
+    a.bc = p.bc;
+    a.per_tile = p.per_tile;
+    const int64_t rows_per_wg = kBlock / p.lpr;
+    a.ngroups = static_cast<uint32_t>((p.M + rows_per_wg - 1) / rows_per_wg);
+    const void *fn = p.op == tmp::kRowMax ? pick_vec<MaxOp>(p) : pick_vec<SumOp>(p);
+    void *args[] = {&a};
+    return hipLaunchKernel(fn, dim3(p.grid), dim3(kBlock), args, 0, stream);
+}
+
+}  // namespace tmk

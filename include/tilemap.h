@@ -1,0 +1,175 @@
+/*
+ * tilemap.h -- C ABI of libtilemap.so: tiled, memory-bound f32 maps, copies and row/column
+ * reductions on AMD Instinct MI355X (gfx950).
+ *
+ * Sources the operations follow (web pages, cited by title and section):
+ *   [ALIGNED]  Phobos docs, "@aligned": sections "A minimal kernel", "What it changes",
+ *              "When the promise is broken".
+ *   [P35]      Mojo GPU puzzles, puzzle 35 "Aligned Load & Store": sections "The exercise",
+ *              "Key API", "Solution".
+ *   [SLICING]  Phobos docs, "Slicing, bounds and masking": sections "Masking", "Loops over a
+ *              dynamic extent", "Promising whole tiles with @aligned", "Reductions over a ragged
+ *              tile".
+ *   [LAYOUT]   teenygrad kernels book, "Memory Coalescing and Tensor Layout": sections
+ *              "Coalescing", "What it actually costs", "Seeing it in a real kernel",
+ *              "The alignment constraint".
+ *
+ * ---- Common conventions -------------------------------------------------------------------------
+ * Layout.  Every 2-D tensor is an M x N row-major view of f32 with an explicit row stride `ld`
+ *   (elements, ld >= N): element (i, j) lives at p[i*ld + j].  The passed stride is always used,
+ *   never N ([LAYOUT] "The alignment constraint").  1-D data is the case M = 1.
+ * Tiles.  A call cuts the tensor into TM x TN tiles; tile (pm, pn) covers rows [pm*TM, pm*TM+TM) and
+ *   columns [pn*TN, pn*TN+TN) ([SLICING] subscript form `pm*TM :+ TM`).  Tile extents are powers of
+ *   two: TM (and BR) in {1, 2, 4, ..., 256}, TN (and BC) in {1, 2, 4, ..., 1024}.  A non-positive
+ *   extent is invalid (TM_E_INVAL); any other value outside these menus is TM_E_UNSUPPORTED (the
+ *   pages' tile must be a known constant, [ALIGNED] "When the promise is broken").
+ * Two paths ([ALIGNED] "What it changes"; [SLICING] "Masking"):
+ *   aligned = 0  ragged-edge path.  Any M, N >= 0 and ld >= N.  Elements past the tensor's edge
+ *                read as 0 and their stores are skipped: no byte outside { p[i*ld + j] : i < M,
+ *                j < N } of an output is ever written.
+ *   aligned = 1  the caller promises whole tiles and 16-byte rows: M % TM == 0, N % TN == 0,
+ *                TN % 4 == 0, and every row of every 2-D tensor starts on a 16-byte boundary
+ *                (base address % 16 == 0 and, when M > 1, row stride % 4 == 0).
+ *                The kernels then carry no masks and move rows as 16-byte vectors.  The promise is
+ *                checked once on the host before anything is enqueued; a broken promise returns
+ *                TM_E_ALIGN and writes nothing ([ALIGNED] "When the promise is broken" traps on the
+ *                device instead; here the check never lets a launch write past a tensor).
+ * Memory and ownership.  Every pointer is caller-owned DEVICE memory (4-byte aligned f32) that
+ *   stays valid until the enqueued work completes.  The library allocates nothing and keeps no
+ *   state between calls.  Pointers may be NULL only when the call has no work (M == 0 or N == 0).
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is enqueued
+ *   asynchronously; a call returns once it is enqueued.  Stream priorities are never changed.
+ * Errors.  All argument checks run synchronously on the host, before any HIP call.  On any error
+ *   nothing is enqueued and no output byte changes.  When several checks fail, the first of
+ *   TM_E_INVAL, TM_E_UNSUPPORTED, TM_E_WORKSPACE, TM_E_ALIGN in that order is returned.  A failed
+ *   launch returns TM_E_HIP.  Nothing aborts, prints or traps.  Calls are thread-safe (no shared
+ *   mutable state).
+ * Empty work.  M == 0 or N == 0 is a no-op returning TM_OK for the maps and the copy.  A reduction
+ *   over an empty extent still writes its result: tm_rowsum with N == 0 writes 0 to each of the M
+ *   rows, tm_colsum with M == 0 writes 0 to each of the N columns, and tm_rowmax_masked with N == 0
+ *   writes the fill -1.0e30f to each row.  Only an empty output makes a reduction a no-op.
+ * Aliasing.  y == x with ldy == ldx is allowed for the maps and the copy; any other overlap of an
+ *   output with an input is undefined.
+ */
+#ifndef TILEMAP_H
+#define TILEMAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TM_OK = 0,
+    TM_E_INVAL = -1,       /* malformed argument: negative extent, ld < N, tile <= 0, NULL with work,
+                              pointer not 4-byte aligned, unknown enum value */
+    TM_E_ALIGN = -2,       /* aligned = 1 but the promise is broken, or a 16-byte vector variant was
+                              asked for on data whose rows are not 16-byte aligned */
+    TM_E_UNSUPPORTED = -3, /* positive tile extent outside the compiled menu */
+    TM_E_WORKSPACE = -4,   /* colsum workspace NULL or smaller than tm_colsum_workspace_bytes() */
+    TM_E_HIP = -5          /* the HIP runtime refused the launch */
+} tm_status;
+
+/* Access width of the element-wise maps ([P35] "The exercise"). */
+typedef enum {
+    TM_VAR_AUTO = 0,             /* VEC4 when legal, else SCALAR */
+    TM_VAR_SCALAR = 1,           /* one 4-byte load and store per element */
+    TM_VAR_VEC4_UNDERSTATED = 2, /* 4 elements per thread, moved as four 4-byte accesses
+                                    (alignment under-stated: [P35] "Key API"); needs TN % 4 == 0,
+                                    else TM_E_UNSUPPORTED */
+    TM_VAR_VEC4 = 3              /* 4 elements per thread as one 16-byte load and store; needs
+                                    TN % 4 == 0 and rows starting on 16-byte boundaries (else
+                                    TM_E_ALIGN) */
+} tm_variant;
+
+/* How tm_colsum walks the matrix ([LAYOUT] "What it actually costs"). */
+typedef enum {
+    TM_COL_NAIVE = 0, /* each workgroup reads TM rows of ONE column: lane-varying term has stride ld */
+    TM_COL_LDS = 1    /* lanes read rows with 16-byte coalesced loads; per-column partials are folded
+                         through LDS ([LAYOUT] "Seeing it in a real kernel": tile once into fast
+                         memory, then read it in any order) */
+} tm_colwalk;
+
+/* ---- element-wise maps over tiles --------------------------------------------------------------
+ * x: input, M x N, row stride ldx.  y: output, M x N, row stride ldy.  TM, TN: tile.  aligned: 0|1.
+ * variant: tm_variant. */
+
+/* y[i,j] = fmaf(x[i,j], alpha, beta): one correctly rounded multiply-add per element
+ * ([P35] "The exercise": out = a*2 + 1; generalised to alpha, beta). */
+int tm_map_affine(const float *x, int64_t ldx, float *y, int64_t ldy, int64_t M, int64_t N,
+                  float alpha, float beta, int TM, int TN, int aligned, int variant, void *stream);
+
+/* y[i,j] = alpha * x[i,j]: one IEEE multiply, so signed zeros are kept
+ * ([ALIGNED] "A minimal kernel", kernel scale). */
+int tm_scale2d(const float *x, int64_t ldx, float *y, int64_t ldy, int64_t M, int64_t N,
+               float alpha, int TM, int TN, int aligned, int variant, void *stream);
+
+/* y[i,j] = x[i,j], bit for bit: NaN payloads and signed zeros travel unchanged
+ * ([SLICING] "Promising whole tiles with @aligned", kernel copy2d). */
+int tm_copy2d(const float *x, int64_t ldx, float *y, int64_t ldy, int64_t M, int64_t N,
+              int TM, int TN, int aligned, int variant, void *stream);
+
+/* ---- row and column reductions -------------------------------------------------------------- */
+
+/* out[i] = sum over j < N of x[i,j] for i < M (out: M floats, contiguous).  Rows are walked with
+ * coalesced 16-byte loads in TN-wide column tiles: whole tiles unmasked, then one remainder tile
+ * whose missing columns read as 0 ([SLICING] "Loops over a dynamic extent", "Masking"; [LAYOUT]
+ * "What it actually costs", the row walk).  Accumulation is f32 in a fixed order; the result is
+ * within 1e-5 * sum_j |x[i,j]| of the exact sum.  aligned = 1 promises M % TM == 0, N % TN == 0 and
+ * 16-byte rows of x (out is not checked). */
+int tm_rowsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t N,
+              int TM, int TN, int aligned, void *stream);
+
+/* Bytes of device workspace tm_colsum needs for these arguments (0 when M == 0 or N == 0, and
+ * also 0 for invalid arguments, which tm_colsum then rejects). */
+size_t tm_colsum_workspace_bytes(int64_t M, int64_t N, int TM, int TN, int walk);
+
+/* out[j] = sum over i < M of x[i,j] for j < N (out: N floats, contiguous).  Two passes: pass 1 writes
+ * one partial per (row slab of TM rows, column) into `ws`; pass 2 adds each column's partials in
+ * slab order, so the result is deterministic (no atomics).  walk: tm_colwalk.  ws: caller-owned
+ * device workspace of ws_bytes >= tm_colsum_workspace_bytes(...) bytes (contents on entry are
+ * ignored; on return they are unspecified).  Same accuracy bound as tm_rowsum, over the column.
+ * aligned = 1 promises M % TM == 0, N % TN == 0 and 16-byte rows of x; the naive walk moves single
+ * elements whatever `aligned` says ([LAYOUT] "What it actually costs", the column walk). */
+int tm_colsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t N,
+              int TM, int TN, int aligned, int walk, void *ws, size_t ws_bytes, void *stream);
+
+/* out[i] = max over j < N of s[i,j] (out: M floats, contiguous), walking BC-wide column tiles: whole
+ * tiles unmasked, then one remainder tile in which tile-local column c keeps s iff c < N - kt and
+ * is otherwise replaced by -1.0e30f (f32 bits 0xF149F2CA); the running maximum starts at that fill,
+ * so N == 0 gives -1.0e30f ([SLICING] "Reductions over a ragged tile").  Scores are assumed to lie
+ * in [-1e30, +inf); NaN entries never win.  Bit-exact (max is order-free).  BR: rows per tile.
+ * aligned = 1 promises M % BR == 0, N % BC == 0 and 16-byte rows of s. */
+int tm_rowmax_masked(const float *s, int64_t lds, float *out, int64_t M, int64_t N,
+                     int BR, int BC, int aligned, void *stream);
+
+/* ---- host-only helpers (no GPU needed) ------------------------------------------------------ */
+
+/* The checks `aligned = 1` performs, as a pure host function: TM_OK when the promise holds,
+ * TM_E_ALIGN when it is broken, TM_E_INVAL / TM_E_UNSUPPORTED for malformed arguments (checked
+ * first).  out == NULL means there is no 2-D output (reductions); ld_out is then ignored.  The
+ * addresses are only inspected, never dereferenced. */
+int tm_check_promise(int64_t M, int64_t N, int64_t ld_in, int64_t ld_out, int TM, int TN,
+                     const void *in, const void *out);
+
+/* Loop remainder split ([SLICING] "Loops over a dynamic extent"): *nfull = K / T whole tiles and
+ * *rem = K % T columns in the one masked remainder tile.  TM_E_INVAL if K < 0, T <= 0 or an output
+ * pointer is NULL. */
+int tm_split(int64_t K, int64_t T, int64_t *nfull, int64_t *rem);
+
+/* Tile scheduler counts ([SLICING] "Masking"): *tiles_m = ceil(M / TM), *tiles_n = ceil(N / TN) and
+ * *whole = the number of tiles lying entirely inside the M x N tensor; the other tiles are edge
+ * tiles, whose out-of-range elements read as 0 and whose stores are skipped.  TM_E_INVAL /
+ * TM_E_UNSUPPORTED as for the tile checks of the other calls, or if an output pointer is NULL. */
+int tm_plan_tiles(int64_t M, int64_t N, int TM, int TN, int64_t *tiles_m, int64_t *tiles_n,
+                  int64_t *whole);
+
+/* Static, human-readable name of a status code ("TM_OK", ...; "unknown status" otherwise). */
+const char *tm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TILEMAP_H */

@@ -1,0 +1,225 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every call include/tilemap.h declares,
+and its host logic -- the promise checker, the loop split, the tile scheduler counts and the whole
+error surface -- behaves as documented.  No kernel is launched: every call here either is a
+host-only helper or fails validation, which happens before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tilemap.h")
+
+tm = pytest.importorskip("edge_masking_vector_amd.tilemap")
+torch = pytest.importorskip("torch")
+
+# The error-path tests below pass fake device addresses that are never dereferenced because every
+# call fails validation before any HIP call.  Where a GPU is visible, a slip in such a test could
+# reach a launch with a fake address, so those tests only run on GPU-less hosts.
+# (device_count() does not initialise the GPU.)
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="fake-address error-path tests run only where no GPU is visible")
+
+A16 = 0x7F0000000000          # a 16-byte aligned fake device address (never dereferenced)
+B16 = 0x7F0000100000
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(tm.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_exports_nothing_else():
+    out = os.popen("nm -D --defined-only '%s'" % tm.library_path()).read()
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == _declared()
+
+
+def test_status_strings():
+    for code, name in [(0, "TM_OK"), (-1, "TM_E_INVAL"), (-2, "TM_E_ALIGN"),
+                       (-3, "TM_E_UNSUPPORTED"), (-4, "TM_E_WORKSPACE"), (-5, "TM_E_HIP")]:
+        assert tm.tm_status_string(code) == name
+    assert tm.tm_status_string(42) == "unknown status"
+
+
+# ---- loop remainder split: the product's splitter against the pages and the oracle --------------
+
+def test_split_matches_pages_and_oracle():
+    assert tm.tm_split(1000, 16) == (tm.TM_OK, 62, 8)
+    assert tm.tm_split(1000, 64) == (tm.TM_OK, 15, 40)
+    for K in range(0, 200):
+        for T in range(1, 33):
+            st, nf, rm = tm.tm_split(K, T)
+            assert st == tm.TM_OK and (nf, rm) == oracle.split(K, T)
+    assert tm.tm_split(-1, 4)[0] == tm.TM_E_INVAL
+    assert tm.tm_split(10, 0)[0] == tm.TM_E_INVAL
+
+
+# ---- tile scheduler counts ---------------------------------------------------------------------
+
+def test_plan_tiles_workload_shapes():
+    # ragged 4100 x 1000 under 64 x 64: 65 x 16 tiles, 64 x 15 = 960 whole
+    assert tm.tm_plan_tiles(4100, 1000, 64, 64) == (tm.TM_OK, 65, 16, 960)
+    # 4096 x 4096 under 32 x 128: all 128 x 32 = 4096 tiles whole
+    assert tm.tm_plan_tiles(4096, 4096, 32, 128) == (tm.TM_OK, 128, 32, 4096)
+    # the pages' edge-tile example: 20 x 28 under 8 x 8
+    assert tm.tm_plan_tiles(20, 28, 8, 8) == (tm.TM_OK, 3, 4, 6)
+
+
+def test_plan_tiles_against_oracle_brute_force():
+    for M in range(0, 19):
+        for N in range(0, 19):
+            for TM in (1, 2, 4, 8, 16):
+                for TN in (1, 4, 8, 16):
+                    st, tmm, tnn, whole = tm.tm_plan_tiles(M, N, TM, TN)
+                    assert st == tm.TM_OK
+                    assert tmm == -(-M // TM) and tnn == -(-N // TN)
+                    full = sum(1 for pm in range(tmm) for pn in range(tnn)
+                               if oracle.tile_live(M, N, TM, TN, pm, pn) == TM * TN)
+                    assert whole == full, (M, N, TM, TN)
+
+
+def test_plan_tiles_errors():
+    assert tm.tm_plan_tiles(-1, 4, 4, 4)[0] == tm.TM_E_INVAL
+    assert tm.tm_plan_tiles(4, 4, 0, 4)[0] == tm.TM_E_INVAL
+    assert tm.tm_plan_tiles(4, 4, 3, 4)[0] == tm.TM_E_UNSUPPORTED
+    assert tm.tm_plan_tiles(4, 4, 512, 4)[0] == tm.TM_E_UNSUPPORTED
+    assert tm.tm_plan_tiles(4, 4, 4, 2048)[0] == tm.TM_E_UNSUPPORTED
+
+
+# ---- the promise checker -------------------------------------------------------------------------
+
+def test_promise_checker_matches_oracle():
+    """Exhaustive over small shapes, strides and base alignments: TM_OK exactly when the oracle's
+    predicate holds, TM_E_ALIGN otherwise (all arguments well-formed)."""
+    for M in (0, 1, 4, 8, 12, 16, 20):
+        for N in (0, 4, 8, 12, 16, 28, 32):
+            for TM in (1, 4, 8):
+                for TN in (1, 2, 4, 8, 16):
+                    for ldi in (N, N + 1, N + 4):
+                        for ldo in (N, N + 2):
+                            for ia, oa in ((A16, B16), (A16 + 4, B16), (A16, B16 + 8), (A16, 0)):
+                                st = tm.tm_check_promise(M, N, ldi, ldo, TM, TN, ia, oa or None)
+                                want = oracle.promise_holds(M, N, ldi, ldo, TM, TN, ia, oa)
+                                assert st == (tm.TM_OK if want else tm.TM_E_ALIGN), \
+                                    (M, N, TM, TN, ldi, ldo, hex(ia), hex(oa))
+
+
+def test_promise_checker_workloads():
+    assert tm.tm_check_promise(4096, 4096, 4096, 4096, 32, 128, A16, B16) == tm.TM_OK
+    assert tm.tm_check_promise(4100, 1000, 1000, 1000, 64, 64, A16, B16) == tm.TM_E_ALIGN
+    assert tm.tm_check_promise(8192, 1000, 1000, 0, 16, 64, A16, None) == tm.TM_E_ALIGN
+
+
+def test_promise_checker_malformed():
+    assert tm.tm_check_promise(-4, 4, 4, 4, 4, 4, A16, B16) == tm.TM_E_INVAL
+    assert tm.tm_check_promise(4, 8, 4, 8, 4, 4, A16, B16) == tm.TM_E_INVAL     # ld_in < N
+    assert tm.tm_check_promise(4, 4, 4, 4, 0, 4, A16, B16) == tm.TM_E_INVAL
+    assert tm.tm_check_promise(4, 4, 4, 4, 4, -8, A16, B16) == tm.TM_E_INVAL
+    assert tm.tm_check_promise(4, 4, 4, 4, 6, 4, A16, B16) == tm.TM_E_UNSUPPORTED
+    # precedence: INVAL before UNSUPPORTED
+    assert tm.tm_check_promise(-4, 4, 4, 4, 6, 4, A16, B16) == tm.TM_E_INVAL
+
+
+# ---- the error surface of every compute call (returns before any HIP call) ----------------------
+
+S = 0  # null stream; never used, the calls fail validation first
+
+
+@no_gpu
+def test_map_errors():
+    f = tm.tm_map_affine
+    ok = dict(x=A16, ldx=4096, y=B16, ldy=4096, M=4096, N=4096, alpha=2.0, beta=1.0, TM=32, TN=128,
+              aligned=1, variant=tm.TM_VAR_VEC4, stream=S)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["ldx"], a["y"], a["ldy"], a["M"], a["N"], a["alpha"], a["beta"],
+                 a["TM"], a["TN"], a["aligned"], a["variant"], a["stream"])
+
+    assert call(M=-1) == tm.TM_E_INVAL
+    assert call(N=-5) == tm.TM_E_INVAL
+    assert call(ldx=4095) == tm.TM_E_INVAL
+    assert call(ldy=100) == tm.TM_E_INVAL
+    assert call(x=0) == tm.TM_E_INVAL
+    assert call(y=0) == tm.TM_E_INVAL
+    assert call(x=A16 + 2) == tm.TM_E_INVAL            # not 4-byte aligned
+    assert call(TM=0) == tm.TM_E_INVAL
+    assert call(TN=-128) == tm.TM_E_INVAL
+    assert call(aligned=2) == tm.TM_E_INVAL
+    assert call(variant=7) == tm.TM_E_INVAL
+    assert call(TM=48) == tm.TM_E_UNSUPPORTED
+    assert call(TN=2048) == tm.TM_E_UNSUPPORTED
+    assert call(TM=512) == tm.TM_E_UNSUPPORTED
+    # broken promises
+    assert call(M=4100, N=1000, ldx=1000, ldy=1000, TM=64, TN=64) == tm.TM_E_ALIGN
+    assert call(x=A16 + 4) == tm.TM_E_ALIGN
+    assert call(ldy=4098) == tm.TM_E_ALIGN
+    # 16-byte variant on a ragged path whose rows are not 16-byte aligned
+    assert call(aligned=0, x=A16 + 4) == tm.TM_E_ALIGN
+    assert call(aligned=0, ldx=4099) == tm.TM_E_ALIGN
+    assert call(aligned=0, variant=tm.TM_VAR_VEC4_UNDERSTATED, TN=2) == tm.TM_E_UNSUPPORTED
+    # precedence
+    assert call(M=-1, TM=48) == tm.TM_E_INVAL
+    assert call(TM=48, x=A16 + 4) == tm.TM_E_UNSUPPORTED
+    # no work: valid no-ops, even with NULL pointers
+    assert call(M=0, x=0, y=0) == tm.TM_OK
+    assert call(N=0, x=0, y=0, aligned=0) == tm.TM_OK
+
+
+@no_gpu
+def test_scale_copy_errors():
+    assert tm.tm_scale2d(A16, 64, B16, 64, 64, 64, 1.5, 32, 128, 1, 0, S) == tm.TM_E_ALIGN
+    assert tm.tm_scale2d(A16, 64, B16, 64, 64, 64, 1.5, 32, 3, 0, 0, S) == tm.TM_E_UNSUPPORTED
+    assert tm.tm_copy2d(A16, 8, B16, 8, 4, 9, 4, 4, 0, 0, S) == tm.TM_E_INVAL
+    assert tm.tm_copy2d(0, 8, 0, 8, 0, 8, 4, 4, 1, 0, S) == tm.TM_OK
+
+
+@no_gpu
+def test_reduction_errors():
+    assert tm.tm_rowsum(A16, 1000, B16, -1, 1000, 4, 256, 0, S) == tm.TM_E_INVAL
+    assert tm.tm_rowsum(A16, 1000, 0, 10, 1000, 4, 256, 0, S) == tm.TM_E_INVAL     # NULL out
+    assert tm.tm_rowsum(A16, 1000, B16 + 2, 10, 1000, 4, 256, 0, S) == tm.TM_E_INVAL
+    assert tm.tm_rowsum(A16, 1000, B16, 10, 1000, 4, 250, 0, S) == tm.TM_E_UNSUPPORTED
+    assert tm.tm_rowsum(A16, 1000, B16, 8, 1000, 4, 256, 1, S) == tm.TM_E_ALIGN
+    assert tm.tm_rowsum(A16, 1000, B16, 0, 1000, 4, 256, 0, S) == tm.TM_OK           # empty output
+    # masked rowmax on the score workload: aligned=1 must fail (1000 % 64 = 40)
+    assert tm.tm_rowmax_masked(A16, 1000, B16, 8192, 1000, 16, 64, 1, S) == tm.TM_E_ALIGN
+    assert tm.tm_rowmax_masked(A16, 1000, B16, 8192, 1000, 16, 0, 0, S) == tm.TM_E_INVAL
+    assert tm.tm_rowmax_masked(A16, 1000, B16, 8192, 1000, 16, 96, 0, S) == tm.TM_E_UNSUPPORTED
+
+
+@no_gpu
+def test_colsum_workspace_and_errors():
+    W = tm.tm_colsum_workspace_bytes
+    assert W(4096, 4096, 256, 64, tm.TM_COL_LDS) == 16 * 4096 * 4
+    assert W(4096, 4096, 256, 1, tm.TM_COL_NAIVE) == 16 * 4096 * 4
+    assert W(4100, 1000, 64, 64, tm.TM_COL_LDS) == 65 * 1000 * 4
+    assert W(0, 1000, 64, 64, tm.TM_COL_LDS) == 0
+    assert W(100, 0, 64, 64, tm.TM_COL_LDS) == 0
+    assert W(100, 100, 3, 64, tm.TM_COL_LDS) == 0
+    assert W(100, 100, 64, 64, 5) == 0
+    f = tm.tm_colsum
+    need = W(4096, 4096, 256, 64, tm.TM_COL_LDS)
+    assert f(A16, 4096, B16, 4096, 4096, 256, 64, 1, 9, A16, need, S) == tm.TM_E_INVAL
+    assert f(A16, 4096, B16, 4096, 4096, 256, 64, 1, tm.TM_COL_LDS, 0, need, S) == tm.TM_E_WORKSPACE
+    assert f(A16, 4096, B16, 4096, 4096, 256, 64, 1, tm.TM_COL_LDS, A16, need - 4, S) == tm.TM_E_WORKSPACE
+    assert f(A16, 4098, B16, 4096, 4096, 256, 64, 1, tm.TM_COL_LDS, A16, need, S) == tm.TM_E_ALIGN
+    assert f(A16 + 8, 4096, B16, 4096, 4096, 256, 64, 1, tm.TM_COL_LDS, A16, need, S) == tm.TM_E_ALIGN
+    assert f(A16, 4096, B16, 4096, 4096, 200, 64, 1, tm.TM_COL_LDS, A16, need, S) == tm.TM_E_UNSUPPORTED
+    # precedence: WORKSPACE before ALIGN (M = 4100 breaks the promise and needs 17 slabs)
+    assert f(A16, 4096, B16, 4100, 4096, 256, 64, 1, tm.TM_COL_LDS, 0, 0, S) == tm.TM_E_WORKSPACE
+    assert f(A16, 4096, B16, 4096, 0, 256, 64, 0, tm.TM_COL_LDS, 0, 0, S) == tm.TM_OK  # empty output
