@@ -1,0 +1,315 @@
+"""Benchmark of the tiled f32 path on one MI355X.
+
+One step is one tm_scale2d call on the 4096 x 4096 f32 matrix (X ~ N(0,1), Y = 1.5 X, 32 x 128
+tiles, aligned path, 16-byte vectors): the host promise check, the tile schedule and the unmasked
+streaming kernel.  `value` is that step's throughput in GB/s of algorithmic traffic (64 MiB read +
+64 MiB written, decimal GB), timed with HIP events on the launch stream over K steps that rotate
+through enough buffer sets (1 GiB) that neither L2 nor the 256 MiB Infinity Cache holds a set
+between its uses: the bytes come from HBM.
+
+The same JSON line carries
+  roofline      the step kernel against the 8 TB/s HBM3E peak (achieved = algorithmic bytes per
+                launch / mean launch time, the event-timed region over its K launches), and its
+                HBM traffic from rocprofv3 counters when profiles/ holds counters taken on the
+                current kernel source;
+  cpu_baseline  the CPU oracle (plain single-threaded C) on the same matrix on this host; the
+                same leg checks the timed kernel's output against the oracle's, bit for bit;
+  paths         every other path of the method, each on its own workload shape and timed the
+                same way: the ragged path on the same shape, the three 1-D access variants, the
+                ragged 4100 x 1000 map, row and column sums (naive and LDS walks) and the masked
+                row max.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--paths all|none] [--cpu-seconds S]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0            # MI355X HBM3E, published
+ROTATE_BYTES = 1 << 30       # bytes touched per rotation of buffer sets
+METRIC = "achieved HBM GB/s and % of 8 TB/s peak, aligned vs ragged, per config"
+STEP_KERNEL_SOURCES = ["edge_masking_vector_amd/csrc/map.hip", "edge_masking_vector_amd/csrc/device.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scale2d_4096_aligned.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--paths", choices=["all", "none"], default="all")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def gbs(nbytes, seconds):
+    return nbytes / seconds / 1e9
+
+
+class Timer:
+    """HIP events on the launch stream around K back-to-back launches: nothing else is enqueued in
+    between, so the host stays ahead of the GPU and the mean is the kernels' own duration."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+    def run(self, launch, n):
+        torch = self.torch
+        torch.cuda.synchronize()
+        self.region[0].record(self.stream)
+        for i in range(n):
+            launch(i)
+        self.region[1].record(self.stream)
+        torch.cuda.synchronize()
+        return self.region[0].elapsed_time(self.region[1]) * 1e-3   # seconds for n launches
+
+
+def rotated(torch, host, n_sets, dev, extra=0):
+    """n_sets device copies of `host` (plus `extra` floats of slack at the end of each)."""
+    base = torch.from_numpy(host).to(dev)
+    sets = []
+    for _ in range(n_sets):
+        t = torch.empty(host.size + extra, dtype=torch.float32, device=dev)
+        t[:host.size].copy_(base)
+        sets.append(t)
+    return sets
+
+
+def sets_for(bytes_per_set):
+    return max(2, -(-ROTATE_BYTES // max(bytes_per_set, 1)))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this benchmark runs on exactly one GPU (the tiled maps and reductions have "
+              "no cross-GPU step here); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+
+    from edge_masking_vector_amd import _build, inputs
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    from edge_masking_vector_amd import tilemap as tm
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    K, W = args.steps, args.warmup
+
+    # ---- the step: aligned scale on 4096 x 4096 ---------------------------------------------------
+    M = N = 4096
+    TM, TN, alpha = 32, 128, 1.5
+    step_bytes = 2 * M * N * 4
+    xh = inputs.scale_input(M, N)
+    R = sets_for(step_bytes)
+    xs = rotated(torch, xh, R, dev)
+    ys = [torch.empty_like(x) for x in xs]
+
+    def step(i):
+        st = tm.tm_scale2d(xs[i % R], N, ys[i % R], N, M, N, alpha, TM, TN, 1, tm.TM_VAR_VEC4, stream)
+        if st != tm.TM_OK:
+            raise tm.TilemapError(st)
+
+    for i in range(W):
+        step(i)
+    total = Timer(torch, stream).run(step, K)
+    ms_per_step = total / K * 1e3
+    value = gbs(step_bytes, total / K)
+    mean_launch = total / K   # one kernel launch per step
+    achieved = gbs(step_bytes, mean_launch)
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha256") == source_digest(STEP_KERNEL_SOURCES):
+            traffic = tr.get("traffic_bytes_per_launch")
+
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "map_tiles<scale, vec4, aligned>",
+                "algorithmic_bytes_per_launch": step_bytes,
+                "mean_launch_us": round(mean_launch * 1e6, 3)}
+
+    # ---- CPU baseline: the oracle on the same matrix, single-threaded ----------------------------
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        yh = np.empty_like(xh)
+        oracle.scale2d(xh, N, yh, N, M, N, alpha)
+        got = ys[0].cpu().numpy()
+        if not np.array_equal(got.view(np.uint32), yh.view(np.uint32)):
+            print("bench.py: the timed kernel's output differs from the oracle", file=sys.stderr)
+            return 1
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.scale2d(xh, N, yh, N, M, N, alpha)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        cpu = {"value": round(gbs(step_bytes * reps, el), 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": "oracle scale2d over the full 4096x4096 f32 matrix, %d repetitions in %.1f s "
+                         "on one host core (%s)" % (reps, el, cpu_model())}
+
+    paths = run_paths(torch, tm, inputs, dev, stream, K, W) if args.paths == "all" else None
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "scale2d Y = 1.5*X, 4096x4096 f32 row-major (X ~ N(0,1)), 32x128 tiles, "
+                               "aligned path, 16-byte vectors",
+                   "M": M, "N": N, "TM": TM, "TN": TN, "aligned": 1, "variant": "VEC4",
+                   "buffer_sets": R, "parallelism": "single GPU",
+                   "frac_of_peak": round(value / PEAK_GBS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if paths is not None:
+        line["paths"] = paths
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for l in f:
+                if l.startswith("model name"):
+                    return l.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def run_paths(torch, tm, inputs, dev, stream, K, W):
+    """Every other path, each on its workload shape, K launches after W warm-ups."""
+    out = {}
+
+    def timed(name, nbytes, n_sets, launch, note):
+        for i in range(W):
+            launch(i % n_sets)
+        mean = Timer(torch, stream).run(lambda i: launch(i % n_sets), K) / K
+        out[name] = {"gbs": round(gbs(nbytes, mean), 1), "frac": round(gbs(nbytes, mean) / PEAK_GBS, 4),
+                     "mean_us": round(mean * 1e6, 3), "bytes": nbytes, "note": note}
+
+    def ok(st):
+        if st != tm.TM_OK:
+            raise tm.TilemapError(st)
+
+    # 4096 x 4096 scale: ragged path (aligned=0) and scalar accesses
+    M = N = 4096
+    xh = inputs.scale_input(M, N)
+    nb = 2 * M * N * 4
+    R = sets_for(nb)
+    xs = rotated(torch, xh, R, dev)
+    ys = [torch.empty_like(x) for x in xs]
+    timed("scale_4096_ragged_vec4", nb, R,
+          lambda i: ok(tm.tm_scale2d(xs[i], N, ys[i], N, M, N, 1.5, 32, 128, 0, tm.TM_VAR_VEC4, stream)),
+          "same shape, ragged path (per-tile whole-tile test)")
+    timed("scale_4096_aligned_scalar", nb, R,
+          lambda i: ok(tm.tm_scale2d(xs[i], N, ys[i], N, M, N, 1.5, 32, 128, 1, tm.TM_VAR_SCALAR, stream)),
+          "same shape, aligned path, 4-byte accesses")
+    timed("ceiling_vendor_copy_64MiB", nb, R, lambda i: ys[i].copy_(xs[i]),
+          "torch device-to-device copy of the same 64 MiB (ROCm's copy kernel), for context")
+    del xs, ys
+
+    # 1-D a*2+1 over 2**20 elements, three access variants
+    n = 1 << 20
+    a = inputs.map1d_input(n)
+    nb = 2 * n * 4
+    R = sets_for(nb)
+    xs = rotated(torch, a, R, dev)
+    ys = [torch.empty_like(x) for x in xs]
+    for name, var, TN in (("map1d_scalar", tm.TM_VAR_SCALAR, 256),
+                          ("map1d_vec4_understated", tm.TM_VAR_VEC4_UNDERSTATED, 1024),
+                          ("map1d_vec4", tm.TM_VAR_VEC4, 1024)):
+        timed(name, nb, R,
+              lambda i, var=var, TN=TN: ok(tm.tm_map_affine(xs[i], n, ys[i], n, 1, n, 2.0, 1.0, 1, TN, 1,
+                                                            var, stream)),
+              "1M-element a*2+1, aligned, TN=%d" % TN)
+    del xs, ys
+
+    # ragged 4100 x 1000 affine under 64 x 64, and its aligned counterpart 4096 x 1024
+    for (M, N, aligned, var, name) in ((4100, 1000, 0, tm.TM_VAR_VEC4, "affine_4100x1000_ragged_vec4"),
+                                       (4100, 1000, 0, tm.TM_VAR_SCALAR, "affine_4100x1000_ragged_scalar"),
+                                       (4096, 1024, 1, tm.TM_VAR_VEC4, "affine_4096x1024_aligned_vec4")):
+        xh = inputs.ragged_input(M, N)
+        nb = 2 * M * N * 4
+        R = sets_for(nb)
+        xs = rotated(torch, xh, R, dev)
+        ys = [torch.empty_like(x) for x in xs]
+        timed(name, nb, R,
+              lambda i, M=M, N=N, aligned=aligned, var=var: ok(tm.tm_map_affine(
+                  xs[i], N, ys[i], N, M, N, 0.75, -0.25, 64, 64, aligned, var, stream)),
+              "y = fmaf(x, 0.75, -0.25), 64x64 tiles")
+        del xs, ys
+
+    # row and column sums of 4096 x 4096 U[0,1)
+    M = N = 4096
+    xh = inputs.colrow_input(M, N)
+    R = sets_for(M * N * 4)
+    xs = rotated(torch, xh, R, dev)
+    outs = [torch.empty(N, device=dev) for _ in range(R)]
+    nb = M * N * 4 + N * 4
+    timed("rowsum_4096", nb, R,
+          lambda i: ok(tm.tm_rowsum(xs[i], N, outs[i], M, N, 4, 256, 1, stream)),
+          "row walk, 4x256 tiles, aligned")
+    for name, walk, TM, TN in (("colsum_naive_4096", tm.TM_COL_NAIVE, 256, 1),
+                               ("colsum_lds_4096", tm.TM_COL_LDS, 256, 64)):
+        wsb = tm.tm_colsum_workspace_bytes(M, N, TM, TN, walk)
+        wss = [torch.empty(wsb // 4, device=dev) for _ in range(R)]
+        timed(name, nb, R,
+              lambda i, walk=walk, TM=TM, TN=TN, wsb=wsb, wss=wss: ok(tm.tm_colsum(
+                  xs[i], N, outs[i], M, N, TM, TN, walk == tm.TM_COL_LDS and 1 or 0, walk, wss[i], wsb,
+                  stream)),
+              "column walk, %dx%d tiles, both passes (workspace %d B not counted)" % (TM, TN, wsb))
+        del wss
+    reads_only = {k: round(gbs(M * N * 4, out[k]["mean_us"] * 1e-6), 1)
+                  for k in ("rowsum_4096", "colsum_naive_4096", "colsum_lds_4096")}
+    out["reads_only_gbs_4096"] = reads_only
+    del xs, outs
+
+    # masked row max: 8192 x 1000 ragged (15 whole 64-column tiles + 40), aligned 8192 x 1024
+    for (M, N, aligned, name) in ((8192, 1000, 0, "rowmax_8192x1000_ragged"),
+                                  (8192, 1024, 1, "rowmax_8192x1024_aligned")):
+        sh = inputs.scores_input(M, N)
+        R = sets_for(M * N * 4)
+        ss = rotated(torch, sh, R, dev)
+        outs = [torch.empty(M, device=dev) for _ in range(R)]
+        nb = M * N * 4 + M * 4
+        timed(name, nb, R,
+              lambda i, M=M, N=N, aligned=aligned: ok(tm.tm_rowmax_masked(ss[i], N, outs[i], M, N, 16, 64,
+                                                                          aligned, stream)),
+              "BC=64 column tiles, -1e30 fill")
+        del ss, outs
+    torch.cuda.synchronize()
+    return out
+
+
+if __name__ == "__main__":
+    sys.exit(main())

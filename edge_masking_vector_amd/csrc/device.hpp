@@ -8,7 +8,8 @@
 
 namespace tmk {
 
-constexpr int kBlock = 256;  // threads per workgroup: four wave64s
+constexpr int kBlock = 256;      // threads per workgroup of the reductions: four wave64s
+constexpr int kMaxBlock = 1024;  // largest workgroup (the maps: up to one 1024-chunk tile block)
 constexpr float kMaxFill = -1.0e30f;  // masked-max fill, f32 bits 0xF149F2CA
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -16,6 +17,17 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 // 16-byte load / store (global_load_dwordx4 / global_store_dwordx4); p must be 16-byte aligned.
 __device__ __forceinline__ f4 ld16(const float *p) { return *reinterpret_cast<const f4 *>(p); }
 __device__ __forceinline__ void st16(float *p, f4 v) { *reinterpret_cast<f4 *>(p) = v; }
+
+// Streaming variants with the non-temporal hint (the `nt` bit): data touched once is not kept in
+// the caches.  Same values, same ordering; only the cache policy differs.
+__device__ __forceinline__ f4 ld16_nt(const float *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f4 *>(p));
+}
+__device__ __forceinline__ void st16_nt(float *p, f4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f4 *>(p));
+}
+__device__ __forceinline__ float ld4_nt(const float *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st4_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
 
 // ---- reduction operators ------------------------------------------------------------------
 struct SumOp {

@@ -7,13 +7,16 @@
 // aligned variants); teenygrad "Memory Coalescing and Tensor Layout" ("Coalescing": consecutive
 // lanes take consecutive addresses).
 //
-// Mapping.  One workgroup (256 threads) per tile, tiles numbered row-major (pn fastest) so that
-// workgroups dispatched together cover neighbouring column tiles of the same rows; a grid smaller
-// than the tile count loops over tiles.  Inside a tile the TM*TN/W chunks (W = 4 elements for the
-// vector variants, 1 for scalar) are numbered along rows, and thread t takes chunks t, t+256, ...:
-// the lane-varying term of every address is the chunk index along a row, so a wave reads 64
-// consecutive chunks (1 KiB for 16-byte chunks) whenever the tile row is that wide.  Each thread
-// issues all of its U loads before its first store.
+// Mapping.  A tile holds TM*TN/W chunks (W = 4 elements for the vector variants, 1 for scalar),
+// numbered along its rows.  One workgroup takes one block of BS = min(chunks, 1024) consecutive
+// chunks of one tile (a tile of more than 1024 chunks spreads over several workgroups; one smaller
+// than a wave leaves lanes idle) and every thread moves exactly one chunk: the lane-varying term of
+// each address is the chunk index along a row, so a wave reads 64 consecutive chunks (1 KiB of
+// 16-byte chunks) whenever the tile row is that wide.  Work items run row-major over tiles (pn
+// fastest), so workgroups dispatched together cover neighbouring tiles of the same rows; a grid
+// smaller than the work count loops.  Whole chunks move with the non-temporal hint.  On gfx950
+// this one-chunk-per-thread shape with 1024-thread workgroups streamed faster than giving each
+// thread several chunks or several tiles, and faster than remapping workgroups across XCDs.
 //
 // Paths.  aligned=1: no masks at all (the host checked whole tiles and 16-byte rows).
 // aligned=0: a uniform per-tile test picks the same unmasked body for whole tiles; edge tiles
@@ -31,8 +34,12 @@ struct MapArgs {
     float *y;
     int64_t ldx, ldy, M, N;
     float alpha, beta;
-    uint32_t tiles_n, ntiles, slots;
+    uint32_t tiles_n;   // tiles along N
+    uint32_t slots;     // chunks per tile
+    uint32_t nwork;     // workgroup work items: tiles * 2^log_sub
     int log_tm, log_tn, log_vr;
+    int log_bs;         // threads per workgroup = chunks per work item
+    int log_sub;        // work items per tile
     // Element step inside an under-stated 4-element chunk.  Always 1; passed at run time so the
     // compiler cannot prove the four accesses adjacent and fuse them into one 16-byte access
     // (gfx950 accepts dwordx4 at 4-byte alignment, so a merely under-stated alignment would still
@@ -73,34 +80,34 @@ __device__ __forceinline__ f4 apply(f4 v, float a, float b) {
     return r;
 }
 
-// Whole chunk at p.
+// Whole chunk at p, streamed (non-temporal: every element is touched exactly once).
 template <int ACC>
 __device__ __forceinline__ typename Chunk<ACC>::T load_chunk(const float *p, int64_t e) {
     if constexpr (ACC == tmp::kVec4) {
-        return ld16(p);
+        return ld16_nt(p);
     } else if constexpr (ACC == tmp::kVec4Understated) {
         f4 r;
-        r.x = p[0];
-        r.y = p[e];
-        r.z = p[2 * e];
-        r.w = p[3 * e];
+        r.x = ld4_nt(p);
+        r.y = ld4_nt(p + e);
+        r.z = ld4_nt(p + 2 * e);
+        r.w = ld4_nt(p + 3 * e);
         return r;
     } else {
-        return *p;
+        return ld4_nt(p);
     }
 }
 
 template <int ACC>
 __device__ __forceinline__ void store_chunk(float *p, typename Chunk<ACC>::T v, int64_t e) {
     if constexpr (ACC == tmp::kVec4) {
-        st16(p, v);
+        st16_nt(p, v);
     } else if constexpr (ACC == tmp::kVec4Understated) {
-        p[0] = v.x;
-        p[e] = v.y;
-        p[2 * e] = v.z;
-        p[3 * e] = v.w;
+        st4_nt(p, v.x);
+        st4_nt(p + e, v.y);
+        st4_nt(p + 2 * e, v.z);
+        st4_nt(p + 3 * e, v.w);
     } else {
-        *p = v;
+        st4_nt(p, v);
     }
 }
 
@@ -141,20 +148,26 @@ __device__ __forceinline__ void store_masked(float *p, typename Chunk<ACC>::T v,
     }
 }
 
-template <int OP, int ACC, bool ALIGNED, int U, bool GUARD>
-__global__ __launch_bounds__(kBlock) void map_tiles(MapArgs a) {
+template <int OP, int ACC, bool ALIGNED>
+__global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
     using T = typename Chunk<ACC>::T;
     constexpr int W = Chunk<ACC>::W;
     const uint32_t t = threadIdx.x;
     const uint32_t vr_mask = (1u << a.log_vr) - 1u;
+    const uint32_t sub_mask = (1u << a.log_sub) - 1u;
 
-    for (uint32_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-        const uint32_t pm = tile / a.tiles_n;  // tile (pm, pn): pm on rows, pn on columns
+    for (uint32_t w = blockIdx.x; w < a.nwork; w += gridDim.x) {
+        const uint32_t tile = w >> a.log_sub;            // tile id, row-major over tiles
+        const uint32_t s = ((w & sub_mask) << a.log_bs) + t;  // this thread's chunk in the tile
+        const uint32_t pm = tile / a.tiles_n;            // tile (pm, pn): pm on rows, pn on columns
         const uint32_t pn = tile - pm * a.tiles_n;
         const int64_t row0 = int64_t(pm) << a.log_tm;
         const int64_t col0 = int64_t(pn) << a.log_tn;
-        const float *xt = a.x + row0 * a.ldx + col0;
-        float *yt = a.y + row0 * a.ldy + col0;
+        const uint32_t r = s >> a.log_vr;                // row within the tile
+        const uint32_t c = (s & vr_mask) * W;            // first column of the chunk within the tile
+        const float *xp = a.x + (row0 + r) * a.ldx + col0 + c;
+        float *yp = a.y + (row0 + r) * a.ldy + col0 + c;
+        const bool slot_ok = s < a.slots;                // false only for tiles smaller than a wave
 
         bool whole = true;
         int64_t rows_live = 0, cols_live = 0;
@@ -163,75 +176,26 @@ __global__ __launch_bounds__(kBlock) void map_tiles(MapArgs a) {
             cols_live = a.N - col0;
             whole = rows_live >= (int64_t(1) << a.log_tm) && cols_live >= (int64_t(1) << a.log_tn);
         }
-
         if (whole) {
-            // Unmasked body: every chunk of the tile exists.
-            for (uint32_t base = 0; base < a.slots; base += kBlock * U) {
-                T v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t s = base + t + kBlock * u;
-                    if (!GUARD || s < a.slots) {
-                        const uint32_t r = s >> a.log_vr;
-                        const uint32_t c = (s & vr_mask) * W;
-                        v[u] = load_chunk<ACC>(xt + int64_t(r) * a.ldx + c, a.estep);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t s = base + t + kBlock * u;
-                    if (!GUARD || s < a.slots) {
-                        const uint32_t r = s >> a.log_vr;
-                        const uint32_t c = (s & vr_mask) * W;
-                        store_chunk<ACC>(yt + int64_t(r) * a.ldy + c, apply<OP>(v[u], a.alpha, a.beta),
-                                         a.estep);
-                    }
-                }
-            }
+            // Unmasked: the chunk exists.
+            if (slot_ok)
+                store_chunk<ACC>(yp, apply<OP>(load_chunk<ACC>(xp, a.estep), a.alpha, a.beta), a.estep);
         } else if constexpr (!ALIGNED) {
-            // Masked body for an edge tile: out-of-range elements read as 0, stores skipped.
-            for (uint32_t base = 0; base < a.slots; base += kBlock * U) {
-                T v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t s = base + t + kBlock * u;
-                    const uint32_t r = s >> a.log_vr;
-                    const uint32_t c = (s & vr_mask) * W;
-                    const bool live = s < a.slots && int64_t(r) < rows_live && int64_t(c) < cols_live;
-                    v[u] = T(0.0f);
-                    if (live)
-                        v[u] = load_masked<ACC>(xt + int64_t(r) * a.ldx + c, cols_live - c, a.estep);
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t s = base + t + kBlock * u;
-                    const uint32_t r = s >> a.log_vr;
-                    const uint32_t c = (s & vr_mask) * W;
-                    const bool live = s < a.slots && int64_t(r) < rows_live && int64_t(c) < cols_live;
-                    if (live)
-                        store_masked<ACC>(yt + int64_t(r) * a.ldy + c, apply<OP>(v[u], a.alpha, a.beta),
-                                          cols_live - c, a.estep);
-                }
-            }
+            // Edge tile: elements past the tensor read as 0 and are never stored.
+            const bool live = slot_ok && int64_t(r) < rows_live && int64_t(c) < cols_live;
+            T v = T(0.0f);
+            if (live)
+                v = load_masked<ACC>(xp, cols_live - c, a.estep);
+            if (live)
+                store_masked<ACC>(yp, apply<OP>(v, a.alpha, a.beta), cols_live - c, a.estep);
         }
-    }
-}
-
-template <int OP, int ACC, bool AL>
-const void *pick_unroll(int unroll, bool guard) {
-    if (guard)
-        return reinterpret_cast<const void *>(&map_tiles<OP, ACC, AL, 1, true>);
-    switch (unroll) {
-    case 1: return reinterpret_cast<const void *>(&map_tiles<OP, ACC, AL, 1, false>);
-    case 2: return reinterpret_cast<const void *>(&map_tiles<OP, ACC, AL, 2, false>);
-    default: return reinterpret_cast<const void *>(&map_tiles<OP, ACC, AL, 4, false>);
     }
 }
 
 template <int OP, int ACC>
 const void *pick_aligned(const tmp::MapPlan &p) {
-    return p.aligned ? pick_unroll<OP, ACC, true>(p.unroll, p.guard)
-                     : pick_unroll<OP, ACC, false>(p.unroll, p.guard);
+    return p.aligned ? reinterpret_cast<const void *>(&map_tiles<OP, ACC, true>)
+                     : reinterpret_cast<const void *>(&map_tiles<OP, ACC, false>);
 }
 
 template <int OP>
@@ -264,14 +228,16 @@ hipError_t launch_map(const tmp::MapPlan &p, hipStream_t stream) {
     a.alpha = p.alpha;
     a.beta = p.beta;
     a.tiles_n = p.tiles_n;
-    a.ntiles = p.ntiles;
     a.slots = p.slots;
+    a.nwork = p.nwork;
     a.log_tm = p.log_tm;
     a.log_tn = p.log_tn;
     a.log_vr = p.log_vr;
+    a.log_bs = p.log_bs;
+    a.log_sub = p.log_sub;
     a.estep = 1;
     void *args[] = {&a};
-    return hipLaunchKernel(pick(p), dim3(p.grid), dim3(kBlock), args, 0, stream);
+    return hipLaunchKernel(pick(p), dim3(p.grid), dim3(1u << p.log_bs), args, 0, stream);
 }
 
 }  // namespace tmk

@@ -179,16 +179,17 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     plan->log_tn = ilog2(TN);
     plan->log_vr = ilog2(TN / W);
     plan->slots = static_cast<uint32_t>(int64_t{TM} * TN / W);
-    if (plan->slots >= static_cast<uint32_t>(kBlock)) {
-        plan->unroll = static_cast<int>(std::min<uint32_t>(4, plan->slots / kBlock));
-        plan->guard = false;
-    } else {
-        plan->unroll = 1;
-        plan->guard = true;
-    }
+    // One chunk per thread: a workgroup covers min(slots, 1024) chunks of one tile (at least a
+    // wave), and a tile of more chunks spreads over 2^log_sub workgroups.
+    const int log_slots = ilog2(plan->slots);
+    plan->log_bs = std::min(std::max(log_slots, ilog2(kMapMinBlock)), ilog2(kMapMaxBlock));
+    plan->log_sub = std::max(0, log_slots - plan->log_bs);
     plan->tiles_n = static_cast<uint32_t>(tiles_n);
     plan->ntiles = static_cast<uint32_t>(tiles_m * tiles_n);
-    plan->grid = cap_grid(plan->ntiles);
+    if ((int64_t{plan->ntiles} << plan->log_sub) > INT32_MAX)
+        return TM_E_UNSUPPORTED;  // work-item ids are 32-bit on the device
+    plan->nwork = plan->ntiles << plan->log_sub;
+    plan->grid = cap_grid(plan->nwork);
     plan->x = x;
     plan->y = y;
     plan->ldx = ldx;

@@ -15,7 +15,9 @@ namespace tmp {
 
 constexpr int kMaxTM = 256;   // row tile (TM, BR) menu: 1, 2, 4, ..., 256
 constexpr int kMaxTN = 1024;  // column tile (TN, BC) menu: 1, 2, 4, ..., 1024
-constexpr int kBlock = 256;   // threads per workgroup of every kernel (4 wave64s)
+constexpr int kBlock = 256;   // threads per workgroup of the reductions (4 wave64s)
+constexpr int kMapMinBlock = 64;    // map workgroups: at least one wave ...
+constexpr int kMapMaxBlock = 1024;  // ... and at most 1024 threads, one chunk each
 
 enum MapOp { kAffine = 0, kScale = 1, kCopy = 2 };
 enum Access { kScalar = 1, kVec4Understated = 2, kVec4 = 3 };
@@ -28,13 +30,14 @@ struct MapPlan {
     int op = kAffine;
     int access = kScalar;         // resolved variant
     int aligned = 0;              // whole tiles promised and checked: kernels carry no masks
-    int unroll = 1;               // vectors per thread per chunk (1, 2, 4)
-    bool guard = false;           // tile smaller than one workgroup pass: guard slot < slots
     int log_tm = 0, log_tn = 0;   // tile extents
-    int log_vr = 0;               // log2(vectors per tile row)
-    uint32_t slots = 0;           // vectors per tile
+    int log_vr = 0;               // log2(chunks per tile row)
+    int log_bs = 6;               // log2(threads per workgroup): one chunk per thread
+    int log_sub = 0;              // log2(workgroup blocks per tile)
+    uint32_t slots = 0;           // chunks per tile
     uint32_t tiles_n = 0;         // tiles along N
     uint32_t ntiles = 0;          // tiles in all
+    uint32_t nwork = 0;           // work items: ntiles << log_sub
     uint32_t grid = 0;            // workgroups
     const float *x = nullptr;
     float *y = nullptr;
