@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--paths", choices=["all", "none"], default="all")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the step, time K runtime device-to-device copies of the same 64 MiB "
+                         "buffers: the plain copy of known size that scales rocprofv3's byte counters")
     return ap.parse_args()
 
 
@@ -140,6 +143,15 @@ def main():
     mean_launch = total / K   # one kernel launch per step
     achieved = gbs(step_bytes, mean_launch)
 
+    calib = None
+    if args.calibrate_copy:
+        copy = lambda i: ys[i % R].copy_(xs[i % R])
+        for i in range(W):
+            copy(i)
+        t = Timer(torch, stream).run(copy, K) / K
+        calib = {"mean_us": round(t * 1e6, 3), "gbs": round(gbs(step_bytes, t), 1),
+                 "bytes_read": step_bytes // 2, "bytes_written": step_bytes // 2}
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -191,6 +203,8 @@ def main():
     }
     if paths is not None:
         line["paths"] = paths
+    if calib is not None:
+        line["calibration_copy"] = calib
     print(json.dumps(line), flush=True)
     return 0
 
