@@ -74,7 +74,7 @@ template <bool VEC>
 __device__ __forceinline__ auto chunk_or_zero(const float *p, int64_t live) {
     if constexpr (VEC) {
         if (live >= 4)
-            return ld16(p);
+            return ld16_nt(p);
         f4 r = f4(0.0f);
         if (live > 0)
             r.x = p[0];
@@ -84,7 +84,7 @@ __device__ __forceinline__ auto chunk_or_zero(const float *p, int64_t live) {
             r.z = p[2];
         return r;
     } else {
-        return live > 0 ? *p : 0.0f;
+        return live > 0 ? ld4_nt(p) : 0.0f;
     }
 }
 
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kBlock) void col_lds(ColArgs a) {
                 v[u] = T(0.0f);
                 if (rr < rows) {
                     if constexpr (ALIGNED)
-                        v[u] = ld16(p + rr * a.ld);
+                        v[u] = ld16_nt(p + rr * a.ld);
                     else
                         v[u] = chunk_or_zero<VEC>(p + rr * a.ld, live);
                 }
@@ -156,18 +156,23 @@ __global__ __launch_bounds__(kBlock) void col_lds(ColArgs a) {
 
 // ---- pass 2: fixed-order sum of the slab partials ---------------------------------------------
 
-constexpr uint32_t kFinishBlock = 32;  // partials added before joining the running total
+constexpr int kFinishBatch = 16;   // partials loaded at once, then added in slab order
+constexpr int kFinishBlock = 64;   // threads per workgroup: one column each
 
-__global__ __launch_bounds__(kBlock) void colsum_finish(const float *ws, float *out, int64_t N,
-                                                      uint32_t slabs) {
-    for (int64_t j = int64_t(blockIdx.x) * kBlock + threadIdx.x; j < N;
-         j += int64_t(gridDim.x) * kBlock) {
+__global__ __launch_bounds__(kFinishBlock) void colsum_finish(const float *ws, float *out, int64_t N,
+                                                            uint32_t slabs) {
+    for (int64_t j = int64_t(blockIdx.x) * kFinishBlock + threadIdx.x; j < N;
+         j += int64_t(gridDim.x) * kFinishBlock) {
         float total = 0.0f;
-        for (uint32_t s0 = 0; s0 < slabs; s0 += kFinishBlock) {
-            const uint32_t s1 = s0 + kFinishBlock < slabs ? s0 + kFinishBlock : slabs;
+        for (uint32_t s0 = 0; s0 < slabs; s0 += kFinishBatch) {
+            float v[kFinishBatch];
+#pragma unroll
+            for (int u = 0; u < kFinishBatch; ++u)
+                v[u] = s0 + u < slabs ? ws[int64_t(s0 + u) * N + j] : 0.0f;
             float blk = 0.0f;
-            for (uint32_t s = s0; s < s1; ++s)
-                blk += ws[int64_t(s) * N + j];
+#pragma unroll
+            for (int u = 0; u < kFinishBatch; ++u)
+                blk += v[u];
             total += blk;
         }
         out[j] = total;
@@ -223,7 +228,7 @@ hipError_t launch_cols(const tmp::ColPlan &p, hipStream_t stream) {
             return err;
     }
     if (p.finish) {
-        const int64_t blocks = (p.N + kBlock - 1) / kBlock;
+        const int64_t blocks = (p.N + kFinishBlock - 1) / kFinishBlock;
         const uint32_t grid = static_cast<uint32_t>(blocks < kGridCap ? blocks : kGridCap);
         const float *ws = p.ws;
         float *out = p.out;
@@ -231,7 +236,7 @@ hipError_t launch_cols(const tmp::ColPlan &p, hipStream_t stream) {
         uint32_t slabs = p.launch ? p.slabs : 0u;
         void *args[] = {&ws, &out, &N, &slabs};
         return hipLaunchKernel(reinterpret_cast<const void *>(&colsum_finish), dim3(grid),
-                               dim3(kBlock), args, 0, stream);
+                               dim3(kFinishBlock), args, 0, stream);
     }
     return hipSuccess;
 }

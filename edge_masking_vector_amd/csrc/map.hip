@@ -7,16 +7,19 @@
 // aligned variants); teenygrad "Memory Coalescing and Tensor Layout" ("Coalescing": consecutive
 // lanes take consecutive addresses).
 //
-// Mapping.  A tile holds TM*TN/W chunks (W = 4 elements for the vector variants, 1 for scalar),
-// numbered along its rows.  One workgroup takes one block of BS = min(chunks, 1024) consecutive
-// chunks of one tile (a tile of more than 1024 chunks spreads over several workgroups; one smaller
-// than a wave leaves lanes idle) and every thread moves exactly one chunk: the lane-varying term of
-// each address is the chunk index along a row, so a wave reads 64 consecutive chunks (1 KiB of
-// 16-byte chunks) whenever the tile row is that wide.  Work items run row-major over tiles (pn
-// fastest), so workgroups dispatched together cover neighbouring tiles of the same rows; a grid
-// smaller than the work count loops.  Whole chunks move with the non-temporal hint.  On gfx950
-// this one-chunk-per-thread shape with 1024-thread workgroups streamed faster than giving each
-// thread several chunks or several tiles, and faster than remapping workgroups across XCDs.
+// Mapping (the tile scheduler).  A tile holds TM rows of VR = TN/W chunks (W = 4 elements for the
+// vector variants, 1 for scalar).  A workgroup takes one work item: R consecutive rows of G
+// horizontally adjacent tiles of one tile row band, R*G*VR chunks, moved by up to 1024 threads
+// with U chunks per thread (U = 4 for scalar, else 1) at a stride of the workgroup size, all loads
+// before any store.  Within a work-item row the lane-varying term of every address is the chunk
+// index, so a wave reads 64 consecutive chunks (1 KiB of 16-byte chunks).  Work items run with the
+// tile groups fastest, then row strips, then tile rows, so workgroups dispatched together cover
+// neighbouring memory.  The host picks the geometry (plan.cpp): when rows start on 128-byte lines a
+// work item is one whole tile (or a strip of one), otherwise it spans as many tiles as fit across
+// the row band, so that few 128-byte lines are shared by workgroups that may run on different XCDs
+// (each XCD has its own L2 and would fetch a shared line again).  Whole chunks move with the
+// non-temporal hint.  On gfx950 one 16-byte chunk per thread in 1024-thread workgroups streamed
+// faster than fewer threads with several chunks each.
 //
 // Paths.  aligned=1: no masks at all (the host checked whole tiles and 16-byte rows).
 // aligned=0: a uniform per-tile test picks the same unmasked body for whole tiles; edge tiles
@@ -34,12 +37,16 @@ struct MapArgs {
     float *y;
     int64_t ldx, ldy, M, N;
     float alpha, beta;
-    uint32_t tiles_n;   // tiles along N
-    uint32_t slots;     // chunks per tile
-    uint32_t nwork;     // workgroup work items: tiles * 2^log_sub
-    int log_tm, log_tn, log_vr;
-    int log_bs;         // threads per workgroup = chunks per work item
-    int log_sub;        // work items per tile
+    uint32_t tiles_n;    // tiles along N
+    uint32_t group;      // G: tiles per work item along N
+    uint32_t groups_n;   // tile groups along N: ceil(tiles_n / G)
+    uint32_t nwork;      // work items: tiles_m * 2^log_strips * groups_n
+    int log_tm, log_tn;
+    int log_vr;          // chunks per tile row
+    int log_gv;          // chunks per work-item row: G * VR
+    int log_r;           // rows per work item
+    int log_strips;      // work items per tile along M: TM / R
+    int log_bs;          // threads per workgroup
     // Element step inside an under-stated 4-element chunk.  Always 1; passed at run time so the
     // compiler cannot prove the four accesses adjacent and fuse them into one 16-byte access
     // (gfx950 accepts dwordx4 at 4-byte alignment, so a merely under-stated alignment would still
@@ -148,62 +155,107 @@ __device__ __forceinline__ void store_masked(float *p, typename Chunk<ACC>::T v,
     }
 }
 
-template <int OP, int ACC, bool ALIGNED>
+template <int OP, int ACC, bool ALIGNED, int U, bool GUARD>
 __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
     using T = typename Chunk<ACC>::T;
     constexpr int W = Chunk<ACC>::W;
     const uint32_t t = threadIdx.x;
     const uint32_t vr_mask = (1u << a.log_vr) - 1u;
-    const uint32_t sub_mask = (1u << a.log_sub) - 1u;
+    const uint32_t gv_mask = (1u << a.log_gv) - 1u;
+    const uint32_t strip_mask = (1u << a.log_strips) - 1u;
+    const uint32_t chunks = 1u << (a.log_r + a.log_gv);  // chunks per work item
+    const int64_t tm = int64_t(1) << a.log_tm, tn = int64_t(1) << a.log_tn;
 
-    for (uint32_t w = blockIdx.x; w < a.nwork; w += gridDim.x) {
-        const uint32_t tile = w >> a.log_sub;            // tile id, row-major over tiles
-        const uint32_t s = ((w & sub_mask) << a.log_bs) + t;  // this thread's chunk in the tile
-        const uint32_t pm = tile / a.tiles_n;            // tile (pm, pn): pm on rows, pn on columns
-        const uint32_t pn = tile - pm * a.tiles_n;
-        const int64_t row0 = int64_t(pm) << a.log_tm;
-        const int64_t col0 = int64_t(pn) << a.log_tn;
-        const uint32_t r = s >> a.log_vr;                // row within the tile
-        const uint32_t c = (s & vr_mask) * W;            // first column of the chunk within the tile
-        const float *xp = a.x + (row0 + r) * a.ldx + col0 + c;
-        float *yp = a.y + (row0 + r) * a.ldy + col0 + c;
-        const bool slot_ok = s < a.slots;                // false only for tiles smaller than a wave
+    // The grid never exceeds the work count (the host caps it at nwork), so the first work item
+    // needs no test; a grid smaller than the work loops.
+    uint32_t w = blockIdx.x;
+    do {
+        // work item -> (tile row pm, row strip, tile group gi); tile groups vary fastest
+        const uint32_t gi = w % a.groups_n;
+        const uint32_t ps = w / a.groups_n;
+        const uint32_t strip = ps & strip_mask;
+        const uint32_t pm = ps >> a.log_strips;
+        const int64_t row0 = (int64_t(pm) << a.log_tm) + (int64_t(strip) << a.log_r);
+        const int64_t col0 = int64_t(gi) * a.group * tn;
 
-        bool whole = true;
-        int64_t rows_live = 0, cols_live = 0;
-        if constexpr (!ALIGNED) {
-            rows_live = a.M - row0;
-            cols_live = a.N - col0;
-            whole = rows_live >= (int64_t(1) << a.log_tm) && cols_live >= (int64_t(1) << a.log_tn);
-        }
-        if (whole) {
-            // Unmasked: the chunk exists.
-            if (slot_ok)
-                store_chunk<ACC>(yp, apply<OP>(load_chunk<ACC>(xp, a.estep), a.alpha, a.beta), a.estep);
+        // Chunk q of the work item: row row0 + q / (G*VR); tile gq / VR of the group; chunk gq % VR.
+        auto tile_col = [&](uint32_t q) { return col0 + int64_t((q & gv_mask) >> a.log_vr) * tn; };
+        auto chunk_col = [&](uint32_t q) { return tile_col(q) + int64_t(q & vr_mask) * W; };
+        auto chunk_row = [&](uint32_t q) { return row0 + int64_t(q >> a.log_gv); };
+
+        // Whole tiles (every tile, when the promise was checked; otherwise this work item's tiles
+        // all lie inside the tensor): no masks.
+        const bool item_whole = ALIGNED || ((int64_t(pm) + 1) * tm <= a.M &&
+                                            col0 + int64_t(a.group) * tn <= a.N);
+        if (item_whole) {
+            T v[U];
+            int64_t yo[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t q = t + (uint32_t(u) << a.log_bs);
+                const int64_t row = chunk_row(q), col = chunk_col(q);
+                yo[u] = row * a.ldy + col;
+                if (!GUARD || q < chunks)
+                    v[u] = load_chunk<ACC>(a.x + row * a.ldx + col, a.estep);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (!GUARD || t + (uint32_t(u) << a.log_bs) < chunks)
+                    store_chunk<ACC>(a.y + yo[u], apply<OP>(v[u], a.alpha, a.beta), a.estep);
         } else if constexpr (!ALIGNED) {
-            // Edge tile: elements past the tensor read as 0 and are never stored.
-            const bool live = slot_ok && int64_t(r) < rows_live && int64_t(c) < cols_live;
-            T v = T(0.0f);
-            if (live)
-                v = load_masked<ACC>(xp, cols_live - c, a.estep);
-            if (live)
-                store_masked<ACC>(yp, apply<OP>(v, a.alpha, a.beta), cols_live - c, a.estep);
+            // Edge tiles: an element past the tensor reads as 0 and its store is skipped; a chunk
+            // of a whole tile still moves unmasked.
+            T v[U];
+            bool on[U], whole[U];
+            int64_t live[U], yo[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t q = t + (uint32_t(u) << a.log_bs);
+                const uint32_t pn = gi * a.group + ((q & gv_mask) >> a.log_vr);
+                const int64_t row = chunk_row(q), col = chunk_col(q);
+                live[u] = a.N - col;  // elements of the chunk inside the tensor
+                whole[u] = row < a.M && tile_col(q) + tn <= a.N;
+                on[u] = q < chunks && pn < a.tiles_n && row < a.M && live[u] > 0;
+                yo[u] = row * a.ldy + col;
+                v[u] = T(0.0f);  // a masked element reads as 0
+                if (on[u]) {
+                    const float *xp = a.x + row * a.ldx + col;
+                    v[u] = whole[u] ? load_chunk<ACC>(xp, a.estep) : load_masked<ACC>(xp, live[u], a.estep);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (on[u]) {  // a masked store is skipped
+                    const T r = apply<OP>(v[u], a.alpha, a.beta);
+                    if (whole[u])
+                        store_chunk<ACC>(a.y + yo[u], r, a.estep);
+                    else
+                        store_masked<ACC>(a.y + yo[u], r, live[u], a.estep);
+                }
+            }
         }
-    }
+        w += gridDim.x;
+    } while (w < a.nwork);
+}
+
+template <int OP, int ACC, bool GUARD>
+const void *pick_aligned(const tmp::MapPlan &p) {
+    constexpr int U = ACC == tmp::kScalar ? tmp::kScalarChunksPerThread : 1;
+    return p.aligned ? reinterpret_cast<const void *>(&map_tiles<OP, ACC, true, U, GUARD>)
+                     : reinterpret_cast<const void *>(&map_tiles<OP, ACC, false, U, GUARD>);
 }
 
 template <int OP, int ACC>
-const void *pick_aligned(const tmp::MapPlan &p) {
-    return p.aligned ? reinterpret_cast<const void *>(&map_tiles<OP, ACC, true>)
-                     : reinterpret_cast<const void *>(&map_tiles<OP, ACC, false>);
+const void *pick_guard(const tmp::MapPlan &p) {
+    return p.guard ? pick_aligned<OP, ACC, true>(p) : pick_aligned<OP, ACC, false>(p);
 }
 
 template <int OP>
 const void *pick_access(const tmp::MapPlan &p) {
     switch (p.access) {
-    case tmp::kScalar: return pick_aligned<OP, tmp::kScalar>(p);
-    case tmp::kVec4Understated: return pick_aligned<OP, tmp::kVec4Understated>(p);
-    default: return pick_aligned<OP, tmp::kVec4>(p);
+    case tmp::kScalar: return pick_guard<OP, tmp::kScalar>(p);
+    case tmp::kVec4Understated: return pick_guard<OP, tmp::kVec4Understated>(p);
+    default: return pick_guard<OP, tmp::kVec4>(p);
     }
 }
 
@@ -228,13 +280,16 @@ hipError_t launch_map(const tmp::MapPlan &p, hipStream_t stream) {
     a.alpha = p.alpha;
     a.beta = p.beta;
     a.tiles_n = p.tiles_n;
-    a.slots = p.slots;
+    a.group = p.group;
+    a.groups_n = p.groups_n;
     a.nwork = p.nwork;
     a.log_tm = p.log_tm;
     a.log_tn = p.log_tn;
     a.log_vr = p.log_vr;
+    a.log_gv = p.log_gv;
+    a.log_r = p.log_r;
+    a.log_strips = p.log_strips;
     a.log_bs = p.log_bs;
-    a.log_sub = p.log_sub;
     a.estep = 1;
     void *args[] = {&a};
     return hipLaunchKernel(pick(p), dim3(p.grid), dim3(1u << p.log_bs), args, 0, stream);

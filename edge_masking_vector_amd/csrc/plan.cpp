@@ -167,29 +167,57 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
 
     int64_t tiles_m, tiles_n, whole;
     plan_tiles(M, N, TM, TN, &tiles_m, &tiles_n, &whole);
-    if (tiles_m * tiles_n > INT32_MAX || tiles_n > INT32_MAX)
-        return TM_E_UNSUPPORTED;  // tile ids are 32-bit on the device
 
     const int W = access == kScalar ? 1 : 4;
+    const int log_u = ilog2(access == kScalar ? kScalarChunksPerThread : 1);
+    const int log_vr = ilog2(TN / W);
+    const int log_tm = ilog2(TM);
+    const int log_target = ilog2(kMapMaxBlock) + log_u;  // chunks per work item: 1024 threads x U
+    // Widest tile group: in the aligned path it must divide the tile count (no tile checks on the
+    // device); in the ragged path it may run past the last tile (those lanes stay idle).
+    int log_gcap = 0;
+    if (aligned) {
+        while (tiles_n % (int64_t{2} << log_gcap) == 0)
+            ++log_gcap;
+    } else {
+        log_gcap = ilog2(tiles_n);
+    }
+    // Rows that start on cache lines: a work item is one tile (or a strip of one).  Otherwise it
+    // spans as many tiles across the row band as fit, so workgroups share few lines.
+    const int64_t line = kLineBytes / 4;
+    const bool line_rows = aligned_to(x, kLineBytes) && aligned_to(y, kLineBytes) &&
+                           (M <= 1 || (ldx % line == 0 && ldy % line == 0));
+    int log_r, log_g;
+    if (line_rows) {
+        log_r = std::min(log_tm, log_target - log_vr);
+        log_g = std::min(log_gcap, log_target - log_vr - log_r);
+    } else {
+        log_g = std::min(log_gcap, log_target - log_vr);
+        log_r = std::min(log_tm, log_target - log_vr - log_g);
+    }
+    const int log_chunks = log_r + log_g + log_vr;
+    const int64_t groups_n = ceil_div(tiles_n, int64_t{1} << log_g);
+    const int64_t nwork = tiles_m * (int64_t{1} << (log_tm - log_r)) * groups_n;
+    if (nwork > INT32_MAX || tiles_n > INT32_MAX)
+        return TM_E_UNSUPPORTED;  // work-item and tile ids are 32-bit on the device
+
     plan->launch = true;
     plan->op = op;
     plan->access = access;
     plan->aligned = aligned;
-    plan->log_tm = ilog2(TM);
+    plan->log_tm = log_tm;
     plan->log_tn = ilog2(TN);
-    plan->log_vr = ilog2(TN / W);
-    plan->slots = static_cast<uint32_t>(int64_t{TM} * TN / W);
-    // One chunk per thread: a workgroup covers min(slots, 1024) chunks of one tile (at least a
-    // wave), and a tile of more chunks spreads over 2^log_sub workgroups.
-    const int log_slots = ilog2(plan->slots);
-    plan->log_bs = std::min(std::max(log_slots, ilog2(kMapMinBlock)), ilog2(kMapMaxBlock));
-    plan->log_sub = std::max(0, log_slots - plan->log_bs);
+    plan->log_vr = log_vr;
+    plan->log_r = log_r;
+    plan->log_gv = log_g + log_vr;
+    plan->log_strips = log_tm - log_r;
+    plan->log_bs = std::max(ilog2(kMapMinBlock), log_chunks - log_u);
+    plan->guard = plan->log_bs + log_u > log_chunks;
+    plan->group = 1u << log_g;
+    plan->groups_n = static_cast<uint32_t>(groups_n);
     plan->tiles_n = static_cast<uint32_t>(tiles_n);
-    plan->ntiles = static_cast<uint32_t>(tiles_m * tiles_n);
-    if ((int64_t{plan->ntiles} << plan->log_sub) > INT32_MAX)
-        return TM_E_UNSUPPORTED;  // work-item ids are 32-bit on the device
-    plan->nwork = plan->ntiles << plan->log_sub;
-    plan->grid = cap_grid(plan->nwork);
+    plan->nwork = static_cast<uint32_t>(nwork);
+    plan->grid = cap_grid(nwork);
     plan->x = x;
     plan->y = y;
     plan->ldx = ldx;

@@ -17,7 +17,9 @@ constexpr int kMaxTM = 256;   // row tile (TM, BR) menu: 1, 2, 4, ..., 256
 constexpr int kMaxTN = 1024;  // column tile (TN, BC) menu: 1, 2, 4, ..., 1024
 constexpr int kBlock = 256;   // threads per workgroup of the reductions (4 wave64s)
 constexpr int kMapMinBlock = 64;    // map workgroups: at least one wave ...
-constexpr int kMapMaxBlock = 1024;  // ... and at most 1024 threads, one chunk each
+constexpr int kMapMaxBlock = 1024;  // ... and at most 1024 threads
+constexpr int kScalarChunksPerThread = 4;  // 4-byte chunks per thread (16-byte chunks: one)
+constexpr int kLineBytes = 128;     // cache line
 
 enum MapOp { kAffine = 0, kScale = 1, kCopy = 2 };
 enum Access { kScalar = 1, kVec4Understated = 2, kVec4 = 3 };
@@ -31,13 +33,17 @@ struct MapPlan {
     int access = kScalar;         // resolved variant
     int aligned = 0;              // whole tiles promised and checked: kernels carry no masks
     int log_tm = 0, log_tn = 0;   // tile extents
-    int log_vr = 0;               // log2(chunks per tile row)
-    int log_bs = 6;               // log2(threads per workgroup): one chunk per thread
-    int log_sub = 0;              // log2(workgroup blocks per tile)
-    uint32_t slots = 0;           // chunks per tile
+    int log_vr = 0;               // log2(chunks per tile row), VR = TN / W
+    // Work item = R rows x G tiles of one tile row band (R*G*VR chunks), one per workgroup.
+    int log_r = 0;                // log2(R)
+    int log_gv = 0;               // log2(G * VR): chunks per work-item row
+    int log_strips = 0;           // log2(TM / R)
+    int log_bs = 6;               // log2(threads per workgroup)
+    bool guard = false;           // threads x chunks per thread exceed the work item's chunks
+    uint32_t group = 1;           // G
+    uint32_t groups_n = 0;        // ceil(tiles_n / G)
     uint32_t tiles_n = 0;         // tiles along N
-    uint32_t ntiles = 0;          // tiles in all
-    uint32_t nwork = 0;           // work items: ntiles << log_sub
+    uint32_t nwork = 0;           // work items: tiles_m * (TM / R) * groups_n
     uint32_t grid = 0;            // workgroups
     const float *x = nullptr;
     float *y = nullptr;

@@ -9,7 +9,8 @@
 // = 4 elements per 16-byte chunk or 1 on the scalar path), so one column tile is one chunk per lane
 // per step and the lanes of a group read consecutive chunks of the row: a wave reads 64/LPR rows,
 // LPR*16 contiguous bytes each.  The walk over column tiles is split in two: `nfull` whole tiles
-// with no mask at all, issued 16 chunks at a time before any arithmetic, then one remainder tile
+// with no mask at all, issued 8 chunks at a time before any arithmetic (each workgroup starting at
+// a different whole tile), then one remainder tile
 // where a chunk element at tile-local column c is kept iff c < N - kt and otherwise replaced by the
 // operator's fill (0 for a sum, -1.0e30f for a maximum).  Lane partials are folded in a fixed tree,
 // then across the group with DPP row operations, ds_swizzle and readlane.  Rows past M re-read row
@@ -31,7 +32,7 @@ struct RowArgs {
     uint32_t ngroups;   // row groups of kBlock / LPR rows
 };
 
-constexpr int kLoads = 16;  // chunks in flight per lane
+constexpr int kLoads = 8;   // chunks in flight per lane
 constexpr int kAcc = 4;     // independent accumulators per lane
 
 template <class Op>
@@ -51,12 +52,13 @@ __device__ __forceinline__ float lanes(float v) { return v; }
 template <class Op>
 __device__ __forceinline__ float lanes(f4 v) { return Op::f(Op::f(v.x, v.y), Op::f(v.z, v.w)); }
 
+// Whole chunk, streamed (non-temporal: every element is read exactly once).
 template <bool VEC>
 __device__ __forceinline__ auto load_whole(const float *p) {
     if constexpr (VEC)
-        return ld16(p);
+        return ld16_nt(p);
     else
-        return *p;
+        return ld4_nt(p);
 }
 
 // Chunk at p whose first `live` elements exist (live may be <= 0); the others take the fill.
@@ -98,13 +100,21 @@ __global__ __launch_bounds__(kBlock) void row_reduce(RowArgs a) {
         for (int i = 0; i < kAcc; ++i)
             acc[i] = T(Op::kFill);
 
-        // Whole tiles: chunk k of this lane sits at column (k * LPR + g) * W; no masks.
+        // Whole tiles: chunk k of this lane sits at column (k * LPR + g) * W; no masks.  Each
+        // workgroup starts at a different whole tile (7 * group mod nfull) and wraps around: when the
+        // row pitch is a multiple of 4 KiB, workgroups that all walked the tiles in the same order
+        // would hit the same HBM channels at the same time.
         const int64_t main_chunks = a.nfull * a.per_tile;
+        const int64_t start = a.nfull > 0 ? (int64_t(grp) * 7 % a.nfull) * a.per_tile : 0;
         for (int64_t k = 0; k < main_chunks; k += kLoads) {
             T v[kLoads];
 #pragma unroll
-            for (int u = 0; u < kLoads; ++u)
-                v[u] = (k + u < main_chunks) ? load_whole<VEC>(p + (k + u) * kStep) : T(Op::kFill);
+            for (int u = 0; u < kLoads; ++u) {
+                int64_t idx = k + u + start;
+                if (idx >= main_chunks)
+                    idx -= main_chunks;
+                v[u] = (k + u < main_chunks) ? load_whole<VEC>(p + idx * kStep) : T(Op::kFill);
+            }
 #pragma unroll
             for (int u = 0; u < kLoads; ++u)
                 acc[u % kAcc] = combine<Op>(acc[u % kAcc], v[u]);
