@@ -49,6 +49,8 @@ def _load():
                                         ctypes.c_float, _i64, _i64]),
         "orc_rowsum_tiled_f64": (None, [_f32p, _i64, _i64, _i64, _i64, _f64p]),
         "orc_rowmax_tiled": (None, [_f32p, _i64, _i64, _i64, _i64, ctypes.c_float, _f32p]),
+        "orc_softmax_stats": (None, [_f32p, _i64, _i64, _i64, _f32p, _f64p]),
+        "orc_softmax_stats_tiled": (None, [_f32p, _i64, _i64, _i64, _i64, ctypes.c_float, _f32p, _f64p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -141,3 +143,20 @@ def rowmax_tiled(s, lds, M, N, BC, fill=MAX_FILL):
     out = np.zeros(max(M, 0), np.float32)
     _load().orc_rowmax_tiled(_p(s, _f32p), lds, M, N, BC, fill, _p(out, _f32p))
     return out
+
+
+def softmax_stats(s, lds, M, N):
+    """(m, l): row maxima (f32, from the -1e30 fill) and sum_j exp(s - m) in double."""
+    _need(s, np.float32, M, N, lds, "s")
+    m = np.zeros(max(M, 0), np.float32)
+    l = np.zeros(max(M, 0), np.float64)
+    _load().orc_softmax_stats(_p(s, _f32p), lds, M, N, _p(m, _f32p), _p(l, _f64p))
+    return m, l
+
+
+def softmax_stats_tiled(s, lds, M, N, BC, fill=MAX_FILL):
+    _need(s, np.float32, M, N, lds, "s")
+    m = np.zeros(max(M, 0), np.float32)
+    l = np.zeros(max(M, 0), np.float64)
+    _load().orc_softmax_stats_tiled(_p(s, _f32p), lds, M, N, BC, fill, _p(m, _f32p), _p(l, _f64p))
+    return m, l

@@ -192,3 +192,46 @@ void orc_rowmax_tiled(const float *s, int64_t lds, int64_t M, int64_t N, int64_t
         out[i] = m;
     }
 }
+
+void orc_softmax_stats(const float *s, int64_t lds, int64_t M, int64_t N, float *m, double *l)
+{
+    orc_rowmax(s, lds, M, N, m);
+    for (int64_t i = 0; i < M; ++i) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < N; ++j)
+            acc += exp((double)s[i * lds + j] - (double)m[i]);
+        l[i] = acc;
+    }
+}
+
+void orc_softmax_stats_tiled(const float *s, int64_t lds, int64_t M, int64_t N, int64_t BC,
+                             float fill, float *m, double *l)
+{
+    int64_t nfull, rem;
+    orc_split(N, BC, &nfull, &rem);
+    const int64_t ntiles = nfull + (rem > 0 ? 1 : 0);
+    for (int64_t i = 0; i < M; ++i) {
+        double run_m = (double)fill;
+        double run_l = 0.0;
+        for (int64_t t = 0; t < ntiles; ++t) {
+            const int64_t kt = t * BC;
+            /* the tile, with where(iota(1) < N - kt, s, fill) applied (a no-op on whole tiles) */
+            double tile_max = (double)fill;
+            for (int64_t c = 0; c < BC; ++c) {
+                double v = (c < N - kt) ? (double)s[i * lds + kt + c] : (double)fill;
+                if (v > tile_max)
+                    tile_max = v;
+            }
+            double new_m = run_m > tile_max ? run_m : tile_max;
+            double tile_sum = 0.0;
+            for (int64_t c = 0; c < BC; ++c) {
+                double v = (c < N - kt) ? (double)s[i * lds + kt + c] : (double)fill;
+                tile_sum += exp(v - new_m);
+            }
+            run_l = run_l * exp(run_m - new_m) + tile_sum;
+            run_m = new_m;
+        }
+        m[i] = (float)run_m;
+        l[i] = run_l;
+    }
+}

@@ -83,6 +83,12 @@ void orc_colsum_f64(const float *x, int64_t ldx, int64_t M, int64_t N, double *o
  * gives -1.0e30f ([SLICING] "Reductions over a ragged tile").  NaN entries never win. */
 void orc_rowmax(const float *s, int64_t lds, int64_t M, int64_t N, float *out);
 
+/* Softmax row statistics: m[i] = the row maximum exactly as orc_rowmax computes it, and
+ * l[i] = sum over 0 <= j < N of exp(s[i,j] - m[i]) in double ([SLICING] "Reductions over a ragged
+ * tile": the masked maximum is what a softmax needs; l is the normaliser that goes with it).  An
+ * empty row gives m = -1.0e30f and l = 0. */
+void orc_softmax_stats(const float *s, int64_t lds, int64_t M, int64_t N, float *m, double *l);
+
 /* ---- tiled walks: the pages' masked-tile procedure, step by step -----------------------------
  * These follow the tile-by-tile procedure (masked loads read as 0, masked stores skipped, loops
  * split into whole tiles plus a masked remainder).  The tests check that each one reproduces the
@@ -104,6 +110,14 @@ void orc_rowsum_tiled_f64(const float *x, int64_t ldx, int64_t M, int64_t N, int
  * fill = 0 reproduces the pages' counter-example. */
 void orc_rowmax_tiled(const float *s, int64_t lds, int64_t M, int64_t N, int64_t BC, float fill,
                       float *out);
+
+/* Softmax row statistics walking BC-wide column tiles online: for each tile (whole tiles, then one
+ * remainder tile whose missing columns take `fill`, as in orc_rowmax_tiled) the tile maximum
+ * t = max(tile), the new running maximum m' = max(m, t), and l' = l * exp(m - m') +
+ * sum over the tile of exp(s - m'), all in double; the running values start at m = fill, l = 0.
+ * With fill = -1.0e30f every masked column adds exp(-1e30 - m') = 0. */
+void orc_softmax_stats_tiled(const float *s, int64_t lds, int64_t M, int64_t N, int64_t BC,
+                             float fill, float *m, double *l);
 
 #ifdef __cplusplus
 }

@@ -397,3 +397,73 @@ def test_promise_whole_tiles_brute_force():
                     got = oracle.promise_holds(M, N, N + (-N % 4), 4 * ((N + 7) // 4), TM, TN,
                                                0x4000, 0x8000)
                     assert got == full, (M, N, TM, TN)
+
+
+# ---- softmax row statistics (the masked maximum's consumer) -------------------------------------
+
+def test_softmax_stats_constant_row():
+    """s == c: m = c and every exp(s - m) is exactly 1, so l = N."""
+    M, N = 5, 777
+    s = np.full(M * N, -3.25, np.float32)
+    m, l = oracle.softmax_stats(s, N, M, N)
+    assert (m == np.float32(-3.25)).all() and (l == N).all()
+
+
+def test_softmax_stats_geometric_closed_form():
+    """s_j = -j (exact in f32): m = 0 and l = sum_j e^-j = (1 - e^-N) / (1 - e^-1)."""
+    N = 1000
+    s = -np.arange(N, dtype=np.float32)
+    m, l = oracle.softmax_stats(s, N, 1, N)
+    want = (1.0 - math.exp(-N)) / (1.0 - math.exp(-1.0))
+    assert m[0] == 0.0 and abs(l[0] - want) <= 1e-14 * want
+
+
+def test_softmax_stats_against_logsumexp():
+    """l = exp(logsumexp(s) - m), with scipy's logsumexp (a different algorithm) as the reference."""
+    from scipy.special import logsumexp
+    M, N = 64, 1000
+    s = inputs.scores_input(M, N)
+    m, l = oracle.softmax_stats(s, N, M, N)
+    S = s.reshape(M, N).astype(np.float64)
+    assert np.array_equal(m, s.reshape(M, N).max(axis=1))
+    want = np.exp(logsumexp(S, axis=1) - m.astype(np.float64))
+    assert np.all(np.abs(l - want) <= 1e-12 * want)
+
+
+def test_softmax_stats_shift_invariance():
+    """Adding 0.5 to every score (exact here) moves m by 0.5 and leaves l unchanged."""
+    M, N = 16, 300
+    s = inputs.scores_input(M, N)
+    m0, l0 = oracle.softmax_stats(s, N, M, N)
+    m1, l1 = oracle.softmax_stats((s + np.float32(0.5)).astype(np.float32), N, M, N)
+    assert np.array_equal(m1, m0 + np.float32(0.5))
+    assert np.all(np.abs(l1 - l0) <= 1e-13 * l0)
+
+
+def test_softmax_stats_tiled_equals_plain():
+    """The online tile-by-tile update with the -1e30 fill reproduces the plain statistics, for
+    every small shape and tile width (m bit for bit, l to double rounding)."""
+    for M, N, ld in _tiny_cases():
+        if M == 0:
+            continue
+        s = inputs.uniform(M * 13 + N + ld, M * ld, -10.0, -1.0)
+        m, l = oracle.softmax_stats(s, ld, M, N)
+        for BC in (1, 2, 4, 8, 16):
+            mt, lt = oracle.softmax_stats_tiled(s, ld, M, N, BC)
+            assert np.array_equal(mt, m), (M, N, ld, BC)
+            assert np.all(np.abs(lt - l) <= 1e-13 * np.maximum(l, 1e-300)), (M, N, ld, BC)
+
+
+def test_softmax_stats_zero_fill_negative_control():
+    """With a 0 fill the ragged tile's missing columns win the maximum and corrupt the normaliser
+    (the pages' warning about softmax); the -1e30 fill does not."""
+    M, N, BC = 8, 1000, 64
+    s = inputs.scores_input(M, N)
+    m, l = oracle.softmax_stats(s, N, M, N)
+    mz, lz = oracle.softmax_stats_tiled(s, N, M, N, BC, fill=0.0)
+    assert (mz == 0).all() and np.all(np.abs(lz - l) > 1.0)
+
+
+def test_softmax_stats_empty_row():
+    m, l = oracle.softmax_stats(np.zeros(1, np.float32), 1, 3, 0)
+    assert (m.view(np.uint32) == 0xF149F2CA).all() and (l == 0).all()
