@@ -16,8 +16,8 @@ The same JSON line carries
                 same leg checks the timed kernel's output against the oracle's, bit for bit;
   paths         every other path of the method, each on its own workload shape and timed the
                 same way: the ragged path on the same shape, the three 1-D access variants, the
-                ragged 4100 x 1000 map, row and column sums (naive and LDS walks) and the masked
-                row max.
+                ragged 4100 x 1000 map, row and column sums (naive and LDS walks), the masked
+                row max and the softmax row statistics.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--paths all|none] [--cpu-seconds S]
 """
@@ -320,7 +320,12 @@ def run_paths(torch, tm, inputs, dev, stream, K, W):
               lambda i, M=M, N=N, aligned=aligned: ok(tm.tm_rowmax_masked(ss[i], N, outs[i], M, N, 16, 64,
                                                                           aligned, stream)),
               "BC=64 column tiles, -1e30 fill")
-        del ss, outs
+        ls = [torch.empty(M, device=dev) for _ in range(R)]
+        timed(name.replace("rowmax", "softmax_stats"), nb + M * 4, R,
+              lambda i, M=M, N=N, aligned=aligned: ok(tm.tm_softmax_stats(ss[i], N, outs[i], ls[i], M, N, 16,
+                                                                          64, aligned, stream)),
+              "row maximum and sum of exp(s - max), BC=64 column tiles")
+        del ss, outs, ls
     torch.cuda.synchronize()
     return out
 

@@ -60,6 +60,15 @@ TM_API int tm_rowmax_masked(const float *s, int64_t lds, float *out, int64_t M, 
     return launched(tmk::launch_rows(plan, static_cast<hipStream_t>(stream)));
 }
 
+TM_API int tm_softmax_stats(const float *s, int64_t lds, float *m, float *l, int64_t M, int64_t N,
+                            int BR, int BC, int aligned, void *stream) {
+    tmp::RowPlan plan;
+    const int st = tmp::plan_rows(tmp::kRowSoftmax, s, lds, m, M, N, BR, BC, aligned, &plan, l);
+    if (st != TM_OK || !plan.launch)
+        return st;
+    return launched(tmk::launch_rows(plan, static_cast<hipStream_t>(stream)));
+}
+
 TM_API size_t tm_colsum_workspace_bytes(int64_t M, int64_t N, int TM, int TN, int walk) {
     return tmp::colsum_ws_bytes(M, N, TM, TN, walk);
 }

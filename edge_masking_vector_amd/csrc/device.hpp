@@ -29,6 +29,10 @@ __device__ __forceinline__ void st16_nt(float *p, f4 v) {
 __device__ __forceinline__ float ld4_nt(const float *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st4_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
 
+// e^x in f32 with the device math library's accurate expf (ROCm's OCML exp, about 1 ulp);
+// never the reduced-precision intrinsic.
+__device__ __forceinline__ float exp_f32(float x) { return expf(x); }
+
 // ---- reduction operators ------------------------------------------------------------------
 struct SumOp {
     static constexpr float kFill = 0.0f;  // masked elements read as 0

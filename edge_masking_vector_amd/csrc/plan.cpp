@@ -232,9 +232,9 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
 // ---- row reductions ---------------------------------------------------------------------------
 
 int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TR, int TC,
-              int aligned, RowPlan *plan) {
+              int aligned, RowPlan *plan, float *out2) {
     *plan = RowPlan{};
-    if (op != kRowSum && op != kRowMax)
+    if (op != kRowSum && op != kRowMax && op != kRowSoftmax)
         return TM_E_INVAL;
     if (aligned != 0 && aligned != 1)
         return TM_E_INVAL;
@@ -244,6 +244,8 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
     if ((st = check_view(x, M, N, ld, M > 0 && N > 0)) != TM_OK)
         return st;
     if ((st = check_vector(out, M)) != TM_OK)
+        return st;
+    if (op == kRowSoftmax && (st = check_vector(out2, M)) != TM_OK)
         return st;
     if ((st = check_tile(TR, TC)) != TM_OK)
         return st;
@@ -267,6 +269,7 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
     plan->grid = cap_grid(groups);
     plan->x = x;
     plan->out = out;
+    plan->out2 = out2;
     plan->ld = ld;
     plan->M = M;
     plan->N = N;

@@ -55,7 +55,7 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
              float alpha, float beta, int TM, int TN, int aligned, int variant, MapPlan *plan);
 
 // ---- row reductions (sum, masked max) ------------------------------------------------------
-enum RowOp { kRowSum = 0, kRowMax = 1 };
+enum RowOp { kRowSum = 0, kRowMax = 1, kRowSoftmax = 2 };
 
 struct RowPlan {
     bool launch = false;
@@ -68,12 +68,13 @@ struct RowPlan {
     int bc = 1;                   // column tile width
     uint32_t grid = 0;
     const float *x = nullptr;
-    float *out = nullptr;
+    float *out = nullptr;         // sums / maxima (softmax statistics: m)
+    float *out2 = nullptr;        // softmax statistics: l
     int64_t ld = 0, M = 0, N = 0;
 };
 
 int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TR, int TC,
-              int aligned, RowPlan *plan);
+              int aligned, RowPlan *plan, float *out2 = nullptr);
 
 // ---- column sums ---------------------------------------------------------------------------
 struct ColPlan {

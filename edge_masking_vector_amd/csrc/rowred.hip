@@ -23,7 +23,8 @@ namespace {
 
 struct RowArgs {
     const float *x;
-    float *out;
+    float *out;         // sums / maxima; softmax statistics: m
+    float *out2;        // softmax statistics: l
     int64_t ld, M, N;
     int64_t nfull;      // whole column tiles
     int64_t rem;        // live columns of the remainder tile (0 = no remainder tile)
@@ -139,6 +140,120 @@ __global__ __launch_bounds__(kBlock) void row_reduce(RowArgs a) {
     }
 }
 
+// ---- softmax row statistics -------------------------------------------------------------------
+// Per lane: a running maximum m and a running sum l of exp(s - m).  Each batch of chunks first
+// raises m to the batch maximum b, then l = l * exp(m - b) + sum exp(s - b).  Masked and padding
+// elements contribute nothing (they are skipped, not left to underflow).  The lanes of a row then
+// combine: the group maximum M first, then the sum of l * exp(m - M).
+
+__device__ __forceinline__ float sum_exp(float v, float b) { return exp_f32(v - b); }
+
+template <class T>
+__device__ __forceinline__ float chunk_max(T v) { return lanes<MaxOp>(v); }
+
+__device__ __forceinline__ float sum_exp(f4 v, float b) {
+    return (exp_f32(v.x - b) + exp_f32(v.y - b)) +
+           (exp_f32(v.z - b) + exp_f32(v.w - b));
+}
+
+// Only the first `live` elements of the chunk exist.
+__device__ __forceinline__ float sum_exp_live(float v, float b, int64_t live) {
+    return live > 0 ? exp_f32(v - b) : 0.0f;
+}
+__device__ __forceinline__ float sum_exp_live(f4 v, float b, int64_t live) {
+    if (live >= 4)
+        return sum_exp(v, b);
+    float acc = exp_f32(v.x - b);
+    if (live > 1)
+        acc += exp_f32(v.y - b);
+    if (live > 2)
+        acc += exp_f32(v.z - b);
+    return acc;
+}
+
+template <int LPR, bool VEC>
+__global__ __launch_bounds__(kBlock) void row_softmax(RowArgs a) {
+    using T = typename std::conditional<VEC, f4, float>::type;
+    constexpr int W = VEC ? 4 : 1;
+    constexpr int kRows = kBlock / LPR;
+    constexpr int64_t kStep = int64_t(LPR) * W;
+    const int t = threadIdx.x;
+    const int g = t % LPR;
+
+    for (uint32_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
+        const int64_t row = int64_t(grp) * kRows + t / LPR;
+        const int64_t rr = row < a.M ? row : a.M - 1;
+        const float *xr = a.x + rr * a.ld;
+        const float *p = xr + g * W;
+        float m = kMaxFill, l = 0.0f;
+
+        // Whole tiles, in the rotated order of row_reduce; no masks.
+        const int64_t main_chunks = a.nfull * a.per_tile;
+        const int64_t start = a.nfull > 0 ? (int64_t(grp) * 7 % a.nfull) * a.per_tile : 0;
+        for (int64_t k = 0; k < main_chunks; k += kLoads) {
+            T v[kLoads];
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u) {
+                int64_t idx = k + u + start;
+                if (idx >= main_chunks)
+                    idx -= main_chunks;
+                v[u] = (k + u < main_chunks) ? load_whole<VEC>(p + idx * kStep) : T(kMaxFill);
+            }
+            float b = m;
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u)
+                b = __builtin_fmaxf(b, chunk_max(v[u]));  // padding is the fill: never above a score
+            float acc = 0.0f;
+#pragma unroll
+            for (int u = 0; u < kLoads; ++u)
+                if (k + u < main_chunks)
+                    acc += sum_exp(v[u], b);
+            l = l * exp_f32(m - b) + acc;
+            m = b;
+        }
+
+        // The one remainder tile: only its first N - kt columns exist.
+        if (a.rem > 0) {
+            const int64_t kt = a.nfull * a.bc;
+            for (int f = 0; f < a.per_tile; ++f) {
+                const int64_t c = int64_t(f) * kStep + g * W;
+                const int64_t live = a.N - kt - c;
+                if (live > 0) {
+                    const T v = load_fill<MaxOp, VEC>(xr + kt + c, live);
+                    const float b = __builtin_fmaxf(m, chunk_max(v));
+                    l = l * exp_f32(m - b) + sum_exp_live(v, b, live);
+                    m = b;
+                }
+            }
+        }
+
+        const float gm = group_reduce<MaxOp, LPR>(m);
+        const float gl = group_reduce<SumOp, LPR>(l * exp_f32(m - gm));
+        if (g == 0 && row < a.M) {
+            a.out[row] = gm;
+            a.out2[row] = gl;
+        }
+    }
+}
+
+template <int LPR>
+const void *pick_softmax_vec(bool vec) {
+    return vec ? reinterpret_cast<const void *>(&row_softmax<LPR, true>)
+               : reinterpret_cast<const void *>(&row_softmax<LPR, false>);
+}
+
+const void *pick_softmax(const tmp::RowPlan &p) {
+    switch (p.lpr) {
+    case 1: return pick_softmax_vec<1>(p.vec);
+    case 2: return pick_softmax_vec<2>(p.vec);
+    case 4: return pick_softmax_vec<4>(p.vec);
+    case 8: return pick_softmax_vec<8>(p.vec);
+    case 16: return pick_softmax_vec<16>(p.vec);
+    case 32: return pick_softmax_vec<32>(p.vec);
+    default: return pick_softmax_vec<64>(p.vec);
+    }
+}
+
 template <class Op, bool VEC>
 const void *pick_lpr(int lpr) {
     switch (lpr) {
@@ -163,6 +278,7 @@ hipError_t launch_rows(const tmp::RowPlan &p, hipStream_t stream) {
     RowArgs a;
     a.x = p.x;
     a.out = p.out;
+    a.out2 = p.out2;
     a.ld = p.ld;
     a.M = p.M;
     a.N = p.N;
@@ -172,7 +288,9 @@ hipError_t launch_rows(const tmp::RowPlan &p, hipStream_t stream) {
     a.per_tile = p.per_tile;
     const int64_t rows_per_wg = kBlock / p.lpr;
     a.ngroups = static_cast<uint32_t>((p.M + rows_per_wg - 1) / rows_per_wg);
-    const void *fn = p.op == tmp::kRowMax ? pick_vec<MaxOp>(p) : pick_vec<SumOp>(p);
+    const void *fn = p.op == tmp::kRowMax       ? pick_vec<MaxOp>(p)
+                     : p.op == tmp::kRowSoftmax ? pick_softmax(p)
+                                                : pick_vec<SumOp>(p);
     void *args[] = {&a};
     return hipLaunchKernel(fn, dim3(p.grid), dim3(kBlock), args, 0, stream);
 }

@@ -52,6 +52,7 @@ _SIGS = {
     "tm_colsum_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _int, _int, _int]),
     "tm_colsum": (_int, [_vp, _i64, _vp, _i64, _i64, _int, _int, _int, _int, _vp, ctypes.c_size_t, _vp]),
     "tm_rowmax_masked": (_int, [_vp, _i64, _vp, _i64, _i64, _int, _int, _int, _vp]),
+    "tm_softmax_stats": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "tm_check_promise": (_int, [_i64, _i64, _i64, _i64, _int, _int, _vp, _vp]),
     "tm_split": (_int, [_i64, _i64, _i64p, _i64p]),
     "tm_plan_tiles": (_int, [_i64, _i64, _int, _int, _i64p, _i64p, _i64p]),
@@ -125,6 +126,11 @@ def tm_colsum(x, ldx, out, M, N, TM, TN, aligned, walk, ws, ws_bytes, stream=Non
 
 def tm_rowmax_masked(s, lds, out, M, N, BR, BC, aligned, stream=None):
     return _lib.tm_rowmax_masked(_ptr(s), lds, _ptr(out), M, N, BR, BC, aligned, _stream(stream))
+
+
+def tm_softmax_stats(s, lds, m, l, M, N, BR, BC, aligned, stream=None):
+    return _lib.tm_softmax_stats(_ptr(s), lds, _ptr(m), _ptr(l), M, N, BR, BC, aligned,
+                                 _stream(stream))
 
 
 def tm_check_promise(M, N, ld_in, ld_out, TM, TN, inp, out):

@@ -145,6 +145,18 @@ int tm_colsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t N,
 int tm_rowmax_masked(const float *s, int64_t lds, float *out, int64_t M, int64_t N,
                      int BR, int BC, int aligned, void *stream);
 
+/* Softmax row statistics over BC-wide column tiles: m[i] = max over j < N of s[i,j], exactly as
+ * tm_rowmax_masked computes it (bit-exact), and l[i] = sum over j < N of exp(s[i,j] - m[i]), the
+ * normaliser that goes with it ([SLICING] "Reductions over a ragged tile": the masked maximum is
+ * what a softmax needs, and a 0 fill would corrupt both).  Tiles are walked as in
+ * tm_rowmax_masked; each lane keeps a running maximum and a running sum that it rescales by
+ * exp(m_old - m_new) whenever its maximum grows, and the lanes of a row are combined the same way.
+ * Masked columns contribute nothing.  l is within 1e-5 relative of the exact sum (f32 sums,
+ * device expf).  N == 0 gives m = -1.0e30f and l = 0.  m, l: M floats each, contiguous.  BR, BC,
+ * aligned and the score contract are those of tm_rowmax_masked. */
+int tm_softmax_stats(const float *s, int64_t lds, float *m, float *l, int64_t M, int64_t N,
+                     int BR, int BC, int aligned, void *stream);
+
 /* ---- host-only helpers (no GPU needed) ------------------------------------------------------ */
 
 /* The checks `aligned = 1` performs, as a pure host function: TM_OK when the promise holds,

@@ -200,6 +200,14 @@ def test_reduction_errors():
     assert tm.tm_rowmax_masked(A16, 1000, B16, 8192, 1000, 16, 64, 1, S) == tm.TM_E_ALIGN
     assert tm.tm_rowmax_masked(A16, 1000, B16, 8192, 1000, 16, 0, 0, S) == tm.TM_E_INVAL
     assert tm.tm_rowmax_masked(A16, 1000, B16, 8192, 1000, 16, 96, 0, S) == tm.TM_E_UNSUPPORTED
+    # softmax statistics: both outputs are checked
+    f = tm.tm_softmax_stats
+    assert f(A16, 1000, B16, 0, 8192, 1000, 16, 64, 0, S) == tm.TM_E_INVAL        # NULL l
+    assert f(A16, 1000, 0, B16, 8192, 1000, 16, 64, 0, S) == tm.TM_E_INVAL        # NULL m
+    assert f(A16, 1000, B16, B16 + 6, 8192, 1000, 16, 64, 0, S) == tm.TM_E_INVAL  # l not 4-aligned
+    assert f(A16, 1000, B16, B16 + 64, 8192, 1000, 16, 64, 1, S) == tm.TM_E_ALIGN
+    assert f(A16, 1000, B16, B16 + 64, 8192, 1000, 16, 48, 0, S) == tm.TM_E_UNSUPPORTED
+    assert f(A16, 1000, 0, 0, 0, 1000, 16, 64, 0, S) == tm.TM_OK                  # empty output
 
 
 @no_gpu

@@ -266,3 +266,73 @@ def test_rowmax_nan_and_fill_edge(dev):
     assert st == tm.TM_OK
     torch.cuda.synchronize()
     assert np.array_equal(bits(O.payload()), bits(oracle.rowmax(host, N, M, N)))
+
+
+# ---- softmax row statistics ----------------------------------------------------------------------
+
+def gpu_softmax(X, ld, M, N, BR, BC, aligned, dev):
+    Mo = Guarded(max(M, 1), dev)
+    Lo = Guarded(max(M, 1), dev)
+    st = tm.tm_softmax_stats(X.ptr, ld, Mo.ptr, Lo.ptr, M, N, BR, BC, aligned)
+    return st, Mo, Lo
+
+
+def check_softmax(Mo, Lo, host, ld, M, N):
+    m_ref, l_ref = oracle.softmax_stats(host, ld, M, N) if N else (
+        np.full(M, oracle.MAX_FILL, np.float32), np.zeros(M))
+    assert np.array_equal(bits(Mo.payload()), bits(m_ref))
+    l = Lo.payload().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(l - l_ref) <= 1e-5 * l_ref + 1e-30), float(np.max(np.abs(l - l_ref) / np.maximum(l_ref, 1e-30)))
+    assert Mo.guards_intact() and Lo.guards_intact()
+
+
+def test_softmax_stats_8192x1000(dev):
+    """m bit-exact with the masked row max, l within 1e-5 of the fp64 normaliser, on the ragged
+    score workload (15 whole 64-column tiles + 40) and its aligned counterpart."""
+    for (M, N, aligned) in ((8192, 1000, 0), (8192, 1024, 1), (8192, 1024, 0)):
+        note("softmax %dx%d aligned=%d" % (M, N, aligned))
+        sh = inputs.scores_input(M, N)
+        S, host = device_matrix(sh, M, N, N, dev)
+        st, Mo, Lo = gpu_softmax(S, N, M, N, 16, 64, aligned, dev)
+        assert st == tm.TM_OK
+        torch.cuda.synchronize()
+        check_softmax(Mo, Lo, host, N, M, N)
+        # m is the masked row max exactly
+        st, R = gpu_rowmax(S, N, M, N, 16, 64, aligned, dev)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(R.payload()), bits(Mo.payload()))
+    st, Mo, Lo = gpu_softmax(S, 1000, 8192, 1000, 16, 64, 1, dev)
+    assert st == tm.TM_E_ALIGN
+
+
+def test_softmax_stats_brute_force(dev):
+    tiles = [(1, 1), (4, 2), (8, 4), (16, 8), (2, 16), (1, 64), (4, 256)]
+    for M, N, ld in tiny_shapes():
+        sh = inputs.uniform(M * 101 + N * 5 + ld, M * N, -10.0, 3.0) if N else np.zeros(0, np.float32)
+        S, host = device_matrix(sh, M, N, ld, dev)
+        for BR, BC in tiles:
+            st, Mo, Lo = gpu_softmax(S, ld, M, N, BR, BC, 0, dev)
+            assert st == tm.TM_OK
+            torch.cuda.synchronize()
+            check_softmax(Mo, Lo, host, ld, M, N)
+
+
+def test_softmax_stats_wide_range_and_misaligned(dev):
+    """Scores spanning a wide range (so the running maximum grows many times and old sums are
+    rescaled by tiny factors), on a misaligned base with a padded stride."""
+    M, N, ld = 300, 5000, 5003
+    sh = inputs.uniform(77, M * N, -80.0, 80.0)
+    S, host = device_matrix(sh, M, N, ld, dev, off=1)
+    for BC in (4, 64, 1024):
+        st, Mo, Lo = gpu_softmax(S, ld, M, N, 4, BC, 0, dev)
+        assert st == tm.TM_OK
+        torch.cuda.synchronize()
+        check_softmax(Mo, Lo, host, ld, M, N)
+
+
+def test_softmax_stats_empty_rows(dev):
+    X = Guarded(1, dev)
+    st, Mo, Lo = gpu_softmax(X, 0, 9, 0, 4, 64, 0, dev)
+    assert st == tm.TM_OK
+    torch.cuda.synchronize()
+    assert (bits(Mo.payload()) == 0xF149F2CA).all() and (bits(Lo.payload()) == 0).all()
