@@ -50,6 +50,7 @@ def _load():
         "orc_rowsum_tiled_f64": (None, [_f32p, _i64, _i64, _i64, _i64, _f64p]),
         "orc_rowmax_tiled": (None, [_f32p, _i64, _i64, _i64, _i64, ctypes.c_float, _f32p]),
         "orc_softmax_stats": (None, [_f32p, _i64, _i64, _i64, _f32p, _f64p]),
+        "orc_transpose": (None, [_f32p, _i64, _i64, _f32p, _i64, _i64, _i64, _i64, _i64]),
         "orc_softmax_stats_tiled": (None, [_f32p, _i64, _i64, _i64, _i64, ctypes.c_float, _f32p, _f64p]),
     }
     for name, (res, args) in sig.items():
@@ -160,3 +161,14 @@ def softmax_stats_tiled(s, lds, M, N, BC, fill=MAX_FILL):
     l = np.zeros(max(M, 0), np.float64)
     _load().orc_softmax_stats_tiled(_p(s, _f32p), lds, M, N, BC, fill, _p(m, _f32p), _p(l, _f64p))
     return m, l
+
+
+def transpose(x, ldx, bsx, y, ldy, bsy, B, M, N):
+    """y[b][j][i] = x[b][i][j] (bit for bit), written in place into y."""
+    for a, what in ((x, "x"), (y, "y")):
+        if not isinstance(a, np.ndarray) or a.dtype != np.float32 or not a.flags.c_contiguous:
+            raise TypeError("%s must be a C-contiguous numpy float32 array" % what)
+    if B > 0 and M > 0 and N > 0:
+        if x.size < (B - 1) * bsx + (M - 1) * ldx + N or y.size < (B - 1) * bsy + (N - 1) * ldy + M:
+            raise ValueError("buffer too small")
+    _load().orc_transpose(_p(x, _f32p), ldx, bsx, _p(y, _f32p), ldy, bsy, B, M, N)

@@ -235,3 +235,12 @@ void orc_softmax_stats_tiled(const float *s, int64_t lds, int64_t M, int64_t N, 
         l[i] = run_l;
     }
 }
+
+void orc_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t ldy, int64_t bsy,
+                   int64_t B, int64_t M, int64_t N)
+{
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t i = 0; i < M; ++i)
+            for (int64_t j = 0; j < N; ++j)
+                memcpy(&y[b * bsy + j * ldy + i], &x[b * bsx + i * ldx + j], sizeof(float));
+}

@@ -89,6 +89,14 @@ void orc_rowmax(const float *s, int64_t lds, int64_t M, int64_t N, float *out);
  * empty row gives m = -1.0e30f and l = 0. */
 void orc_softmax_stats(const float *s, int64_t lds, int64_t M, int64_t N, float *m, double *l);
 
+/* Batched transpose: y[b][j][i] = x[b][i][j] for b < B, i < M, j < N, bit for bit.  Batch b of x
+ * starts at x + b*bsx with row stride ldx (M x N); batch b of y starts at y + b*bsy with row stride
+ * ldy (N x M).  With x = [B][C][H*W] (M = C, N = H*W) this is the NCHW -> NHWC layout conversion
+ * ([LAYOUT] "NCHW versus NHWC"; the flat index of [LAYOUT] "Strides, and reading an index
+ * expression"). */
+void orc_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t ldy, int64_t bsy,
+                   int64_t B, int64_t M, int64_t N);
+
 /* ---- tiled walks: the pages' masked-tile procedure, step by step -----------------------------
  * These follow the tile-by-tile procedure (masked loads read as 0, masked stores skipped, loops
  * split into whole tiles plus a masked remainder).  The tests check that each one reproduces the

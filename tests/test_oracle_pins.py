@@ -467,3 +467,46 @@ def test_softmax_stats_zero_fill_negative_control():
 def test_softmax_stats_empty_row():
     m, l = oracle.softmax_stats(np.zeros(1, np.float32), 1, 3, 0)
     assert (m.view(np.uint32) == 0xF149F2CA).all() and (l == 0).all()
+
+
+# ---- transpose / layout conversion ------------------------------------------------------------------
+
+def test_transpose_nchw_to_nhwc_index_formula():
+    """'Strides, and reading an index expression': in NCHW the element (b, c, h, w) sits at
+    b*(C*H*W) + c*(H*W) + h*W + w; in NHWC at b*(H*W*C) + (h*W + w)*C + c.  Fill x with its own
+    NCHW flat index; after the conversion each y element must hold the NCHW index of the element
+    that belongs at its NHWC position."""
+    B, C, H, W = 3, 5, 4, 7
+    HW = H * W
+    x = np.arange(B * C * HW, dtype=np.float32)
+    y = np.full(B * HW * C, -1.0, np.float32)
+    oracle.transpose(x, HW, C * HW, y, C, HW * C, B, C, HW)
+    for b in range(B):
+        for c in range(C):
+            for h in range(H):
+                for w in range(W):
+                    assert y[b * HW * C + (h * W + w) * C + c] == b * C * HW + c * HW + h * W + w
+
+
+def test_transpose_matches_numpy_and_is_an_involution():
+    M, N = 37, 53
+    x = inputs.uniform(4, M * N, -1.0, 1.0)
+    y = np.empty(N * M, np.float32)
+    oracle.transpose(x, N, 0, y, M, 0, 1, M, N)
+    assert np.array_equal(y.view(np.uint32), np.ascontiguousarray(x.reshape(M, N).T).reshape(-1).view(np.uint32))
+    z = np.empty_like(x)
+    oracle.transpose(y, M, 0, z, N, 0, 1, N, M)
+    assert np.array_equal(z.view(np.uint32), x.view(np.uint32))
+
+
+def test_transpose_strides_and_bits():
+    """Padded strides are honoured (padding never written) and NaN payloads survive."""
+    M, N, ldx, ldy = 4, 6, 9, 7
+    x = np.arange(M * ldx, dtype=np.float32)
+    x[0] = np.array([0x7FC01234], np.uint32).view(np.float32)[0]
+    y = np.full(N * ldy, 5.0, np.float32)
+    oracle.transpose(x, ldx, 0, y, ldy, 0, 1, M, N)
+    Y = y.reshape(N, ldy)
+    assert (Y[:, M:] == 5.0).all()
+    assert Y[0, 0].view(np.uint32) == 0x7FC01234
+    assert all(Y[j, i] == x[i * ldx + j] for i in range(1, M) for j in range(N))
