@@ -17,7 +17,7 @@ The same JSON line carries
   paths         every other path of the method, each on its own workload shape and timed the
                 same way: the ragged path on the same shape, the three 1-D access variants, the
                 ragged 4100 x 1000 map, row and column sums (naive and LDS walks), the masked
-                row max and the softmax row statistics.
+                row max, the softmax row statistics and the transpose / NCHW -> NHWC conversion.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--paths all|none] [--cpu-seconds S]
 """
@@ -326,6 +326,27 @@ def run_paths(torch, tm, inputs, dev, stream, K, W):
                                                                           64, aligned, stream)),
               "row maximum and sum of exp(s - max), BC=64 column tiles")
         del ss, outs, ls
+    # transpose 4096 x 4096 (64x64 tiles) and the NCHW -> NHWC conversion of [32][64][56*56]
+    M = N = 4096
+    xh = inputs.scale_input(M, N)
+    nb = 2 * M * N * 4
+    R = sets_for(nb)
+    xs = rotated(torch, xh, R, dev)
+    ys = [torch.empty_like(x) for x in xs]
+    timed("transpose_4096_aligned", nb, R,
+          lambda i: ok(tm.tm_transpose(xs[i], N, 0, ys[i], M, 0, 1, M, N, 64, 64, 1, stream)),
+          "y = x^T, 64x64 tiles staged through LDS")
+    del xs, ys
+    B, C, HW = 32, 64, 56 * 56
+    xh = inputs.uniform(6, B * C * HW, -1.0, 1.0)
+    nb = 2 * B * C * HW * 4
+    R = sets_for(nb)
+    xs = rotated(torch, xh, R, dev)
+    ys = [torch.empty_like(x) for x in xs]
+    timed("nchw_to_nhwc_32x64x56x56", nb, R,
+          lambda i: ok(tm.tm_transpose(xs[i], HW, C * HW, ys[i], C, HW * C, B, C, HW, 64, 64, 1, stream)),
+          "batched transpose [B][C][HW] -> [B][HW][C]")
+    del xs, ys
     torch.cuda.synchronize()
     return out
 

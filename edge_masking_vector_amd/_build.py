@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtilemap.so")
-SOURCES = ["plan.cpp", "map.hip", "rowred.hip", "colred.hip", "api.hip"]
+SOURCES = ["plan.cpp", "map.hip", "rowred.hip", "colred.hip", "transpose.hip", "api.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

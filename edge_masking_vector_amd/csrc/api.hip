@@ -82,6 +82,15 @@ TM_API int tm_colsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t
     return launched(tmk::launch_cols(plan, static_cast<hipStream_t>(stream)));
 }
 
+TM_API int tm_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t ldy, int64_t bsy,
+                        int64_t B, int64_t M, int64_t N, int TM, int TN, int aligned, void *stream) {
+    tmp::TransposePlan plan;
+    const int st = tmp::plan_transpose(x, ldx, bsx, y, ldy, bsy, B, M, N, TM, TN, aligned, &plan);
+    if (st != TM_OK || !plan.launch)
+        return st;
+    return launched(tmk::launch_transpose(plan, static_cast<hipStream_t>(stream)));
+}
+
 TM_API int tm_check_promise(int64_t M, int64_t N, int64_t ld_in, int64_t ld_out, int TM, int TN,
                             const void *in, const void *out) {
     return tmp::check_promise(M, N, ld_in, ld_out, TM, TN, in, out);

@@ -345,4 +345,62 @@ int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int 
     return TM_OK;
 }
 
+// ---- batched transpose -------------------------------------------------------------------------
+
+int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t ldy, int64_t bsy,
+                   int64_t B, int64_t M, int64_t N, int TM, int TN, int aligned,
+                   TransposePlan *plan) {
+    *plan = TransposePlan{};
+    if (aligned != 0 && aligned != 1)
+        return TM_E_INVAL;
+    if (B < 0 || M < 0 || N < 0 || bsx < 0 || bsy < 0 || TM <= 0 || TN <= 0)
+        return TM_E_INVAL;
+    const bool work = B > 0 && M > 0 && N > 0;
+    int st;
+    if ((st = check_view(x, M, N, ldx, work)) != TM_OK)   // x: M x N
+        return st;
+    if ((st = check_view(y, N, M, ldy, work)) != TM_OK)   // y: N x M
+        return st;
+    if (work && B > 1) {
+        // batches of y must not overlap (their writes would race); x batches may be read twice
+        if (bsy < (N - 1) * ldy + M || (bsx > 0 && (B - 1) > (INT64_MAX / 4) / bsx) ||
+            (B - 1) > (INT64_MAX / 4) / std::max<int64_t>(bsy, 1))
+            return TM_E_INVAL;
+    }
+    if ((st = check_tile(TM, TN)) != TM_OK)
+        return st;
+    // 16-byte chunks: x rows read along N, y rows written along M, every row on a 16-byte boundary
+    // in every batch.
+    const bool vec = TM % 4 == 0 && TN % 4 == 0 && rows16(x, M, ldx) && rows16(y, N, ldy) &&
+                     (B <= 1 || (bsx % 4 == 0 && bsy % 4 == 0));
+    if (aligned && !(M % TM == 0 && N % TN == 0 && vec))
+        return TM_E_ALIGN;
+    if (!work)
+        return TM_OK;
+    plan->launch = true;
+    plan->vec = vec;
+    plan->aligned = aligned;
+    plan->sm = std::min(TM, 64);
+    plan->sn = std::min(TN, 64);
+    const int64_t subs_m = ceil_div(M, plan->sm), subs_n = ceil_div(N, plan->sn);
+    if (subs_m > INT32_MAX || subs_n > INT32_MAX)
+        return TM_E_UNSUPPORTED;
+    plan->subs_m = static_cast<uint32_t>(subs_m);
+    plan->subs_n = static_cast<uint32_t>(subs_n);
+    if (subs_m * subs_n > INT64_MAX / B)
+        return TM_E_UNSUPPORTED;
+    plan->nwork = static_cast<uint64_t>(B * subs_m * subs_n);
+    plan->grid = cap_grid(static_cast<int64_t>(std::min<uint64_t>(plan->nwork, INT64_MAX)));
+    plan->x = x;
+    plan->y = y;
+    plan->ldx = ldx;
+    plan->ldy = ldy;
+    plan->bsx = bsx;
+    plan->bsy = bsy;
+    plan->B = B;
+    plan->M = M;
+    plan->N = N;
+    return TM_OK;
+}
+
 }  // namespace tmp

@@ -99,6 +99,24 @@ size_t colsum_ws_bytes(int64_t M, int64_t N, int TM, int TN, int walk);
 int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TM, int TN,
               int aligned, int walk, void *ws, size_t ws_bytes, ColPlan *plan);
 
+// ---- batched transpose -----------------------------------------------------------------------
+struct TransposePlan {
+    bool launch = false;
+    bool vec = false;             // 16-byte chunks on both sides
+    int aligned = 0;
+    int sm = 1, sn = 1;           // sub-tile extents: min(TM, 64), min(TN, 64)
+    uint32_t subs_m = 0, subs_n = 0;
+    uint64_t nwork = 0;
+    uint32_t grid = 0;
+    const float *x = nullptr;
+    float *y = nullptr;
+    int64_t ldx = 0, ldy = 0, bsx = 0, bsy = 0, B = 0, M = 0, N = 0;
+};
+
+int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t ldy, int64_t bsy,
+                   int64_t B, int64_t M, int64_t N, int TM, int TN, int aligned,
+                   TransposePlan *plan);
+
 // ---- pieces shared by the planners (exported through the C ABI as host helpers) -------------
 // Loop remainder split: K columns in steps of T = *nfull whole tiles + one tile of *rem columns.
 int split(int64_t K, int64_t T, int64_t *nfull, int64_t *rem);

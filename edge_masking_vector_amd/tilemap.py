@@ -53,6 +53,7 @@ _SIGS = {
     "tm_colsum": (_int, [_vp, _i64, _vp, _i64, _i64, _int, _int, _int, _int, _vp, ctypes.c_size_t, _vp]),
     "tm_rowmax_masked": (_int, [_vp, _i64, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "tm_softmax_stats": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
+    "tm_transpose": (_int, [_vp, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _vp]),
     "tm_check_promise": (_int, [_i64, _i64, _i64, _i64, _int, _int, _vp, _vp]),
     "tm_split": (_int, [_i64, _i64, _i64p, _i64p]),
     "tm_plan_tiles": (_int, [_i64, _i64, _int, _int, _i64p, _i64p, _i64p]),
@@ -131,6 +132,11 @@ def tm_rowmax_masked(s, lds, out, M, N, BR, BC, aligned, stream=None):
 def tm_softmax_stats(s, lds, m, l, M, N, BR, BC, aligned, stream=None):
     return _lib.tm_softmax_stats(_ptr(s), lds, _ptr(m), _ptr(l), M, N, BR, BC, aligned,
                                  _stream(stream))
+
+
+def tm_transpose(x, ldx, bsx, y, ldy, bsy, B, M, N, TM, TN, aligned, stream=None):
+    return _lib.tm_transpose(_ptr(x), ldx, bsx, _ptr(y), ldy, bsy, B, M, N, TM, TN, aligned,
+                             _stream(stream))
 
 
 def tm_check_promise(M, N, ld_in, ld_out, TM, TN, inp, out):

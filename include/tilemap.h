@@ -157,6 +157,23 @@ int tm_rowmax_masked(const float *s, int64_t lds, float *out, int64_t M, int64_t
 int tm_softmax_stats(const float *s, int64_t lds, float *m, float *l, int64_t M, int64_t N,
                      int BR, int BC, int aligned, void *stream);
 
+/* ---- layout conversion ----------------------------------------------------------------------- */
+
+/* Batched transpose: y[b][j][i] = x[b][i][j] for b < B, i < M, j < N, bit for bit.  Batch b of x
+ * (M x N, row stride ldx) starts at x + b*bsx; batch b of y (N x M, row stride ldy) at y + b*bsy.
+ * With x = [B][C][H*W], M = C, N = H*W, ldx = H*W, bsx = C*H*W, ldy = C, bsy = H*W*C this converts
+ * NCHW to NHWC; the same call with M and N swapped converts back ([LAYOUT] "NCHW versus NHWC": a
+ * conversion costs one full pass over memory; "Strides, and reading an index expression").
+ * x is cut into TM x TN tiles (y into TN x TM); each is staged through LDS so that both the reads
+ * of x and the writes of y are coalesced rows ([LAYOUT] "Seeing it in a real kernel").  Ragged
+ * edges: elements past the tensor read as 0 and are never stored.  aligned = 1 promises
+ * M % TM == 0, N % TN == 0, TM % 4 == 0, TN % 4 == 0 and 16-byte rows of x and y in every batch
+ * (16-byte bases, row strides % 4 == 0, batch strides % 4 == 0 when B > 1), else TM_E_ALIGN.
+ * For B > 1, bsy must be at least (N - 1)*ldy + M (batches of y may not overlap), else TM_E_INVAL.
+ * x and y must not overlap.  B, M or N == 0 is a no-op. */
+int tm_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t ldy, int64_t bsy,
+                 int64_t B, int64_t M, int64_t N, int TM, int TN, int aligned, void *stream);
+
 /* ---- host-only helpers (no GPU needed) ------------------------------------------------------ */
 
 /* The checks `aligned = 1` performs, as a pure host function: TM_OK when the promise holds,

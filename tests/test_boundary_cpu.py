@@ -231,3 +231,28 @@ def test_colsum_workspace_and_errors():
     # precedence: WORKSPACE before ALIGN (M = 4100 breaks the promise and needs 17 slabs)
     assert f(A16, 4096, B16, 4100, 4096, 256, 64, 1, tm.TM_COL_LDS, 0, 0, S) == tm.TM_E_WORKSPACE
     assert f(A16, 4096, B16, 4096, 0, 256, 64, 0, tm.TM_COL_LDS, 0, 0, S) == tm.TM_OK  # empty output
+
+
+@no_gpu
+def test_transpose_errors():
+    f = tm.tm_transpose
+    # x: 64 x 128 (ldx 128), y: 128 x 64 (ldy 64)
+    ok = dict(x=A16, ldx=128, bsx=0, y=B16, ldy=64, bsy=0, B=1, M=64, N=128, TM=32, TN=64, aligned=1)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["ldx"], a["bsx"], a["y"], a["ldy"], a["bsy"], a["B"], a["M"], a["N"],
+                 a["TM"], a["TN"], a["aligned"], S)
+
+    assert call(M=-1) == tm.TM_E_INVAL
+    assert call(B=-1) == tm.TM_E_INVAL
+    assert call(ldx=100) == tm.TM_E_INVAL          # ldx < N
+    assert call(ldy=60) == tm.TM_E_INVAL           # ldy < M
+    assert call(y=0) == tm.TM_E_INVAL
+    assert call(B=2, bsy=64 * 127) == tm.TM_E_INVAL   # y batches would overlap
+    assert call(TM=24) == tm.TM_E_UNSUPPORTED
+    assert call(M=60, ldy=64) == tm.TM_E_ALIGN     # 60 % 32
+    assert call(TM=2) == tm.TM_E_ALIGN             # y rows not whole 16-byte chunks
+    assert call(ldy=66) == tm.TM_E_ALIGN
+    assert call(B=2, bsx=64 * 128 + 2, bsy=128 * 64) == tm.TM_E_ALIGN
+    assert call(B=0, x=0, y=0) == tm.TM_OK
