@@ -380,8 +380,18 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     plan->launch = true;
     plan->vec = vec;
     plan->aligned = aligned;
-    plan->sm = std::min(TM, 64);
-    plan->sn = std::min(TN, 64);
+    // Staged sub-tiles: 64 x 64, except that under the promise they must divide the extents
+    // (whole sub-tiles, no masks): then the largest power of two up to 64 that divides M (resp.
+    // N), which the promised tile divides.
+    auto sub = [&](int64_t extent) {
+        int e = 64;
+        if (aligned)
+            while (extent % e != 0)
+                e /= 2;
+        return e;
+    };
+    plan->sm = sub(M);
+    plan->sn = sub(N);
     const int64_t subs_m = ceil_div(M, plan->sm), subs_n = ceil_div(N, plan->sn);
     if (subs_m > INT32_MAX || subs_n > INT32_MAX)
         return TM_E_UNSUPPORTED;

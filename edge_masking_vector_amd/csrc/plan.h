@@ -104,7 +104,7 @@ struct TransposePlan {
     bool launch = false;
     bool vec = false;             // 16-byte chunks on both sides
     int aligned = 0;
-    int sm = 1, sn = 1;           // sub-tile extents: min(TM, 64), min(TN, 64)
+    int sm = 1, sn = 1;           // staged sub-tile extents (powers of two <= 64)
     uint32_t subs_m = 0, subs_n = 0;
     uint64_t nwork = 0;
     uint32_t grid = 0;
