@@ -51,6 +51,7 @@ def _load():
         "orc_rowmax_tiled": (None, [_f32p, _i64, _i64, _i64, _i64, ctypes.c_float, _f32p]),
         "orc_softmax_stats": (None, [_f32p, _i64, _i64, _i64, _f32p, _f64p]),
         "orc_transpose": (None, [_f32p, _i64, _i64, _f32p, _i64, _i64, _i64, _i64, _i64]),
+        "orc_channel_affine": (None, [_f32p, _i64, _f32p, _f32p, _f32p, _i64, _i64, _i64]),
         "orc_softmax_stats_tiled": (None, [_f32p, _i64, _i64, _i64, _i64, ctypes.c_float, _f32p, _f64p]),
     }
     for name, (res, args) in sig.items():
@@ -172,3 +173,13 @@ def transpose(x, ldx, bsx, y, ldy, bsy, B, M, N):
         if x.size < (B - 1) * bsx + (M - 1) * ldx + N or y.size < (B - 1) * bsy + (N - 1) * ldy + M:
             raise ValueError("buffer too small")
     _load().orc_transpose(_p(x, _f32p), ldx, bsx, _p(y, _f32p), ldy, bsy, B, M, N)
+
+
+def channel_affine(x, ldx, scale, bias, y, ldy, M, N):
+    """y[i,j] = fmaf(x[i,j], scale[j], bias[j]) (or x + bias[j] when scale is None), in place."""
+    _need(x, np.float32, M, N, ldx, "x"); _need(y, np.float32, M, N, ldy, "y")
+    _need(bias, np.float32, 1, N, N, "bias")
+    if scale is not None:
+        _need(scale, np.float32, 1, N, N, "scale")
+    _load().orc_channel_affine(_p(x, _f32p), ldx, None if scale is None else _p(scale, _f32p),
+                               _p(bias, _f32p), _p(y, _f32p), ldy, M, N)

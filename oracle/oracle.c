@@ -244,3 +244,16 @@ void orc_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
             for (int64_t j = 0; j < N; ++j)
                 memcpy(&y[b * bsy + j * ldy + i], &x[b * bsx + i * ldx + j], sizeof(float));
 }
+
+void orc_channel_affine(const float *x, int64_t ldx, const float *scale, const float *bias, float *y,
+                        int64_t ldy, int64_t M, int64_t N)
+{
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            if (scale != 0)
+                y[i * ldy + j] = fmaf(x[i * ldx + j], scale[j], bias[j]);
+            else
+                y[i * ldy + j] = x[i * ldx + j] + bias[j];
+        }
+    }
+}

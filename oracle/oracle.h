@@ -89,6 +89,14 @@ void orc_rowmax(const float *s, int64_t lds, int64_t M, int64_t N, float *out);
  * empty row gives m = -1.0e30f and l = 0. */
 void orc_softmax_stats(const float *s, int64_t lds, int64_t M, int64_t N, float *m, double *l);
 
+/* Per-channel affine on an NC view: y[i,j] = fmaf(x[i,j], scale[j], bias[j]), or x[i,j] + bias[j]
+ * when scale is NULL (one IEEE add).  Columns are channels: a (B, C, H, W) tensor stored NHWC is
+ * the M = B*H*W by N = C view ([LAYOUT] "NCHW versus NHWC": per-channel scale and bias want the
+ * channel dimension contiguous; the tree's channel_bias_add reads the tensor as NC with
+ * N = B*H*W). */
+void orc_channel_affine(const float *x, int64_t ldx, const float *scale, const float *bias, float *y,
+                        int64_t ldy, int64_t M, int64_t N);
+
 /* Batched transpose: y[b][j][i] = x[b][i][j] for b < B, i < M, j < N, bit for bit.  Batch b of x
  * starts at x + b*bsx with row stride ldx (M x N); batch b of y starts at y + b*bsy with row stride
  * ldy (N x M).  With x = [B][C][H*W] (M = C, N = H*W) this is the NCHW -> NHWC layout conversion

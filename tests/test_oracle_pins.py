@@ -510,3 +510,54 @@ def test_transpose_strides_and_bits():
     assert (Y[:, M:] == 5.0).all()
     assert Y[0, 0].view(np.uint32) == 0x7FC01234
     assert all(Y[j, i] == x[i * ldx + j] for i in range(1, M) for j in range(N))
+
+
+# ---- per-channel affine on an NC view ----------------------------------------------------------------
+
+def test_channel_bias_add_is_ieee_add():
+    """Without a scale the op is one f32 add per element: numpy's f32 add is that operation."""
+    M, N = 50, 70
+    x = inputs.uniform(1, M * N, -4.0, 4.0)
+    b = inputs.uniform(2, N, -1.0, 1.0)
+    y = np.empty_like(x)
+    oracle.channel_affine(x, N, None, b, y, N, M, N)
+    assert np.array_equal(y.view(np.uint32), (x.reshape(M, N) + b[None, :]).reshape(-1).view(np.uint32))
+
+
+def test_channel_affine_single_rounding():
+    """With a scale it is one fused multiply-add: scale values 0.75 and 1.5 keep the double
+    expression exact on these inputs, so rounding it once is the correctly rounded result."""
+    M, N = 40, 64
+    x = inputs.ragged_input(M, N)
+    s = np.where(np.arange(N) % 2 == 0, 0.75, 1.5).astype(np.float32)
+    b = (inputs.integers(3, N, -64, 64) * np.float32(0.25)).astype(np.float32)
+    y = np.empty_like(x)
+    oracle.channel_affine(x, N, s, b, y, N, M, N)
+    want = (x.reshape(M, N).astype(np.float64) * s[None, :] + b[None, :]).astype(np.float32).reshape(-1)
+    assert np.array_equal(y.view(np.uint32), want.view(np.uint32))
+
+
+def test_channel_affine_broadcasts_along_columns():
+    """Rows of constant x with a distinct bias per column: y[i, j] depends on j through the bias
+    (a transposed broadcast would make it depend on i)."""
+    M, N = 6, 9
+    x = np.repeat(np.arange(M, dtype=np.float32), N)
+    b = np.arange(N, dtype=np.float32) * 100
+    y = np.empty_like(x)
+    oracle.channel_affine(x, N, None, b, y, N, M, N)
+    assert all(y[i * N + j] == i + 100 * j for i in range(M) for j in range(N))
+
+
+def test_channel_affine_on_nhwc_view():
+    """A (B, C, H, W) tensor stored NHWC is the (B*H*W) x C view: element (b, c, h, w) sits at
+    ((b*H + h)*W + w)*C + c and receives bias[c]."""
+    B, C, H, W = 2, 3, 4, 5
+    x = np.zeros(B * H * W * C, np.float32)
+    b = np.array([1.0, 20.0, 300.0], np.float32)
+    y = np.empty_like(x)
+    oracle.channel_affine(x, C, None, b, y, C, B * H * W, C)
+    for bb in range(B):
+        for c in range(C):
+            for h in range(H):
+                for w in range(W):
+                    assert y[((bb * H + h) * W + w) * C + c] == b[c]
