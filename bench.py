@@ -17,7 +17,8 @@ The same JSON line carries
   paths         every other path of the method, each on its own workload shape and timed the
                 same way: the ragged path on the same shape, the three 1-D access variants, the
                 ragged 4100 x 1000 map, row and column sums (naive and LDS walks), the masked
-                row max, the softmax row statistics and the transpose / NCHW -> NHWC conversion.
+                row max, the softmax row statistics, the per-channel bias add and the transpose /
+                NCHW -> NHWC conversion.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--paths all|none] [--cpu-seconds S]
 """
@@ -326,6 +327,20 @@ def run_paths(torch, tm, inputs, dev, stream, K, W):
                                                                           64, aligned, stream)),
               "row maximum and sum of exp(s - max), BC=64 column tiles")
         del ss, outs, ls
+    # per-channel bias add on the NHWC tensor (32, 64, 56, 56) read as a 100352 x 64 NC view
+    M, N = 32 * 56 * 56, 64
+    xh = inputs.uniform(7, M * N, -1.0, 1.0)
+    nb = 2 * M * N * 4 + N * 4
+    R = sets_for(nb)
+    xs = rotated(torch, xh, R, dev)
+    ys = [torch.empty_like(x) for x in xs]
+    bias = torch.from_numpy(inputs.uniform(8, N, -1.0, 1.0)).to(dev)
+    timed("channel_bias_add_nhwc_32x64x56x56", nb, R,
+          lambda i: ok(tm.tm_channel_affine(xs[i], N, None, bias, ys[i], N, M, N, 64, 64, 1,
+                                            tm.TM_VAR_VEC4, stream)),
+          "y[n, c] = x[n, c] + bias[c] on the NC view of an NHWC tensor, 64x64 tiles")
+    del xs, ys
+
     # transpose 4096 x 4096 (64x64 tiles) and the NCHW -> NHWC conversion of [32][64][56*56]
     M = N = 4096
     xh = inputs.scale_input(M, N)

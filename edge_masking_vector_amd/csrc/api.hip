@@ -42,6 +42,17 @@ TM_API int tm_copy2d(const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     return run_map(tmp::kCopy, x, ldx, y, ldy, M, N, 0.0f, 0.0f, TM, TN, aligned, variant, stream);
 }
 
+TM_API int tm_channel_affine(const float *x, int64_t ldx, const float *scale, const float *bias,
+                             float *y, int64_t ldy, int64_t M, int64_t N, int TM, int TN, int aligned,
+                             int variant, void *stream) {
+    tmp::MapPlan plan;
+    const int st = tmp::plan_map(tmp::kChannel, x, ldx, y, ldy, M, N, 0.0f, 0.0f, TM, TN, aligned,
+                                 variant, &plan, scale, bias);
+    if (st != TM_OK || !plan.launch)
+        return st;
+    return launched(tmk::launch_map(plan, static_cast<hipStream_t>(stream)));
+}
+
 TM_API int tm_rowsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t N, int TM, int TN,
                      int aligned, void *stream) {
     tmp::RowPlan plan;

@@ -1,11 +1,12 @@
-// map.hip -- tiled element-wise maps for gfx950: y = fmaf(x, alpha, beta), y = alpha * x and the
-// bitwise copy, over TM x TN tiles of row-major f32 views.
+// map.hip -- tiled element-wise maps for gfx950: y = fmaf(x, alpha, beta), y = alpha * x, the
+// bitwise copy and the per-channel y = fmaf(x, scale[col], bias[col]), over TM x TN tiles of
+// row-major f32 views.
 //
 // Sources (web pages): Phobos docs "@aligned" ("A minimal kernel", "What it changes"); Phobos docs
 // "Slicing, bounds and masking" ("Masking", "Promising whole tiles with @aligned"); Mojo GPU
 // puzzle 35 "Aligned Load & Store" ("The exercise", "Solution": the scalar, under-aligned and
 // aligned variants); teenygrad "Memory Coalescing and Tensor Layout" ("Coalescing": consecutive
-// lanes take consecutive addresses).
+// lanes take consecutive addresses; "NCHW versus NHWC": per-channel scale and bias on an NC view).
 //
 // Mapping (the tile scheduler).  A tile holds TM rows of VR = TN/W chunks (W = 4 elements for the
 // vector variants, 1 for scalar).  A workgroup takes one work item: R consecutive rows of G
@@ -47,6 +48,9 @@ struct MapArgs {
     int log_r;           // rows per work item
     int log_strips;      // work items per tile along M: TM / R
     int log_bs;          // threads per workgroup
+    const float *scale;  // channel op: per-column scale (null: 1) and bias
+    const float *bias;
+    int cvec16;          // channel op: the column vectors are 16-byte aligned
     // Element step inside an under-stated 4-element chunk.  Always 1; passed at run time so the
     // compiler cannot prove the four accesses adjacent and fuse them into one 16-byte access
     // (gfx950 accepts dwordx4 at 4-byte alignment, so a merely under-stated alignment would still
@@ -84,6 +88,41 @@ __device__ __forceinline__ f4 apply(f4 v, float a, float b) {
     r.y = apply1<OP>(v.y, a, b);
     r.z = apply1<OP>(v.z, a, b);
     r.w = apply1<OP>(v.w, a, b);
+    return r;
+}
+
+// Channel op: per-column scale and bias of a chunk (the columns the chunk covers).  They are read
+// by every row, so they are plain (cached) loads.  A missing scale is 1: fmaf(x, 1, b) is exactly
+// the rounded sum x + b.
+template <int ACC>
+__device__ __forceinline__ typename Chunk<ACC>::T load_cvec(const float *v, int64_t col, int64_t live,
+                                                             int vec16, float absent) {
+    if constexpr (Chunk<ACC>::W == 1) {
+        return v ? v[col] : absent;
+    } else {
+        f4 r = f4(absent);
+        if (!v)
+            return r;
+        if (live >= 4 && vec16)
+            return ld16(v + col);
+        r.x = v[col];
+        if (live > 1)
+            r.y = v[col + 1];
+        if (live > 2)
+            r.z = v[col + 2];
+        if (live > 3)
+            r.w = v[col + 3];
+        return r;
+    }
+}
+
+__device__ __forceinline__ float apply_channel(float v, float s, float b) { return __builtin_fmaf(v, s, b); }
+__device__ __forceinline__ f4 apply_channel(f4 v, f4 s, f4 b) {
+    f4 r;
+    r.x = __builtin_fmaf(v.x, s.x, b.x);
+    r.y = __builtin_fmaf(v.y, s.y, b.y);
+    r.z = __builtin_fmaf(v.z, s.z, b.z);
+    r.w = __builtin_fmaf(v.w, s.w, b.w);
     return r;
 }
 
@@ -188,24 +227,36 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
         const bool item_whole = ALIGNED || ((int64_t(pm) + 1) * tm <= a.M &&
                                             col0 + int64_t(a.group) * tn <= a.N);
         if (item_whole) {
-            T v[U];
+            T v[U], cs[U], cb[U];
             int64_t yo[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t q = t + (uint32_t(u) << a.log_bs);
                 const int64_t row = chunk_row(q), col = chunk_col(q);
                 yo[u] = row * a.ldy + col;
-                if (!GUARD || q < chunks)
+                if (!GUARD || q < chunks) {
                     v[u] = load_chunk<ACC>(a.x + row * a.ldx + col, a.estep);
+                    if constexpr (OP == tmp::kChannel) {
+                        cs[u] = load_cvec<ACC>(a.scale, col, W, a.cvec16, 1.0f);
+                        cb[u] = load_cvec<ACC>(a.bias, col, W, a.cvec16, 0.0f);
+                    }
+                }
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (!GUARD || t + (uint32_t(u) << a.log_bs) < chunks)
-                    store_chunk<ACC>(a.y + yo[u], apply<OP>(v[u], a.alpha, a.beta), a.estep);
+            for (int u = 0; u < U; ++u) {
+                if (!GUARD || t + (uint32_t(u) << a.log_bs) < chunks) {
+                    T r;
+                    if constexpr (OP == tmp::kChannel)
+                        r = apply_channel(v[u], cs[u], cb[u]);
+                    else
+                        r = apply<OP>(v[u], a.alpha, a.beta);
+                    store_chunk<ACC>(a.y + yo[u], r, a.estep);
+                }
+            }
         } else if constexpr (!ALIGNED) {
             // Edge tiles: an element past the tensor reads as 0 and its store is skipped; a chunk
             // of a whole tile still moves unmasked.
-            T v[U];
+            T v[U], cs[U], cb[U];
             bool on[U], whole[U];
             int64_t live[U], yo[U];
 #pragma unroll
@@ -221,12 +272,20 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
                 if (on[u]) {
                     const float *xp = a.x + row * a.ldx + col;
                     v[u] = whole[u] ? load_chunk<ACC>(xp, a.estep) : load_masked<ACC>(xp, live[u], a.estep);
+                    if constexpr (OP == tmp::kChannel) {
+                        cs[u] = load_cvec<ACC>(a.scale, col, live[u], a.cvec16, 1.0f);
+                        cb[u] = load_cvec<ACC>(a.bias, col, live[u], a.cvec16, 0.0f);
+                    }
                 }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (on[u]) {  // a masked store is skipped
-                    const T r = apply<OP>(v[u], a.alpha, a.beta);
+                    T r;
+                    if constexpr (OP == tmp::kChannel)
+                        r = apply_channel(v[u], cs[u], cb[u]);
+                    else
+                        r = apply<OP>(v[u], a.alpha, a.beta);
                     if (whole[u])
                         store_chunk<ACC>(a.y + yo[u], r, a.estep);
                     else
@@ -263,7 +322,8 @@ const void *pick(const tmp::MapPlan &p) {
     switch (p.op) {
     case tmp::kAffine: return pick_access<tmp::kAffine>(p);
     case tmp::kScale: return pick_access<tmp::kScale>(p);
-    default: return pick_access<tmp::kCopy>(p);
+    case tmp::kCopy: return pick_access<tmp::kCopy>(p);
+    default: return pick_access<tmp::kChannel>(p);
     }
 }
 
@@ -290,6 +350,9 @@ hipError_t launch_map(const tmp::MapPlan &p, hipStream_t stream) {
     a.log_r = p.log_r;
     a.log_strips = p.log_strips;
     a.log_bs = p.log_bs;
+    a.scale = p.scale;
+    a.bias = p.bias;
+    a.cvec16 = p.cvec16 ? 1 : 0;
     a.estep = 1;
     void *args[] = {&a};
     return hipLaunchKernel(pick(p), dim3(p.grid), dim3(1u << p.log_bs), args, 0, stream);

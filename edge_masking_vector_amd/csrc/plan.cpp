@@ -124,9 +124,10 @@ int plan_tiles(int64_t M, int64_t N, int TM, int TN, int64_t *tiles_m, int64_t *
 // ---- element-wise maps ------------------------------------------------------------------------
 
 int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t M, int64_t N,
-             float alpha, float beta, int TM, int TN, int aligned, int variant, MapPlan *plan) {
+             float alpha, float beta, int TM, int TN, int aligned, int variant, MapPlan *plan,
+             const float *scale, const float *bias) {
     *plan = MapPlan{};
-    if (op < kAffine || op > kCopy)
+    if (op < kAffine || op > kChannel)
         return TM_E_INVAL;
     if (aligned != 0 && aligned != 1)
         return TM_E_INVAL;
@@ -140,6 +141,13 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
         return st;
     if ((st = check_view(y, M, N, ldy, work)) != TM_OK)
         return st;
+    if (op == kChannel && work) {
+        // per-column vectors: bias required, scale optional (1 when absent)
+        if ((st = check_vector(bias, N)) != TM_OK)
+            return st;
+        if (scale != nullptr && (st = check_vector(scale, N)) != TM_OK)
+            return st;
+    }
     if ((st = check_tile(TM, TN)) != TM_OK)
         return st;
     if (aligned && !promise_holds(M, N, ldx, ldy, TM, TN, x, y))
@@ -226,6 +234,9 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     plan->N = N;
     plan->alpha = alpha;
     plan->beta = beta;
+    plan->scale = scale;
+    plan->bias = bias;
+    plan->cvec16 = aligned_to(bias, 16) && aligned_to(scale, 16);
     return TM_OK;
 }
 

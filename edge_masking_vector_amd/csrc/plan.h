@@ -21,7 +21,7 @@ constexpr int kMapMaxBlock = 1024;  // ... and at most 1024 threads
 constexpr int kScalarChunksPerThread = 4;  // 4-byte chunks per thread (16-byte chunks: one)
 constexpr int kLineBytes = 128;     // cache line
 
-enum MapOp { kAffine = 0, kScale = 1, kCopy = 2 };
+enum MapOp { kAffine = 0, kScale = 1, kCopy = 2, kChannel = 3 };
 enum Access { kScalar = 1, kVec4Understated = 2, kVec4 = 3 };
 
 int ilog2(int64_t v);  // v a power of two
@@ -49,10 +49,14 @@ struct MapPlan {
     float *y = nullptr;
     int64_t ldx = 0, ldy = 0, M = 0, N = 0;
     float alpha = 0.f, beta = 0.f;
+    const float *scale = nullptr;  // per-column vectors of the channel op (scale may be null)
+    const float *bias = nullptr;
+    bool cvec16 = false;           // both column vectors 16-byte aligned
 };
 
 int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t M, int64_t N,
-             float alpha, float beta, int TM, int TN, int aligned, int variant, MapPlan *plan);
+             float alpha, float beta, int TM, int TN, int aligned, int variant, MapPlan *plan,
+             const float *scale = nullptr, const float *bias = nullptr);
 
 // ---- row reductions (sum, masked max) ------------------------------------------------------
 enum RowOp { kRowSum = 0, kRowMax = 1, kRowSoftmax = 2 };

@@ -48,6 +48,7 @@ _SIGS = {
     "tm_map_affine": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _f32, _f32, _int, _int, _int, _int, _vp]),
     "tm_scale2d": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _f32, _int, _int, _int, _int, _vp]),
     "tm_copy2d": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _int, _int, _int, _int, _vp]),
+    "tm_channel_affine": (_int, [_vp, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int, _vp]),
     "tm_rowsum": (_int, [_vp, _i64, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "tm_colsum_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _int, _int, _int]),
     "tm_colsum": (_int, [_vp, _i64, _vp, _i64, _i64, _int, _int, _int, _int, _vp, ctypes.c_size_t, _vp]),
@@ -110,6 +111,12 @@ def tm_scale2d(x, ldx, y, ldy, M, N, alpha, TM, TN, aligned, variant=TM_VAR_AUTO
 def tm_copy2d(x, ldx, y, ldy, M, N, TM, TN, aligned, variant=TM_VAR_AUTO, stream=None):
     return _lib.tm_copy2d(_ptr(x), ldx, _ptr(y), ldy, M, N, TM, TN, aligned, variant,
                           _stream(stream))
+
+
+def tm_channel_affine(x, ldx, scale, bias, y, ldy, M, N, TM, TN, aligned, variant=TM_VAR_AUTO,
+                      stream=None):
+    return _lib.tm_channel_affine(_ptr(x), ldx, _ptr(scale), _ptr(bias), _ptr(y), ldy, M, N, TM, TN,
+                                  aligned, variant, _stream(stream))
 
 
 def tm_rowsum(x, ldx, out, M, N, TM, TN, aligned, stream=None):

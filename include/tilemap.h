@@ -111,6 +111,17 @@ int tm_scale2d(const float *x, int64_t ldx, float *y, int64_t ldy, int64_t M, in
 int tm_copy2d(const float *x, int64_t ldx, float *y, int64_t ldy, int64_t M, int64_t N,
               int TM, int TN, int aligned, int variant, void *stream);
 
+/* Per-channel affine on an NC view: y[i,j] = fmaf(x[i,j], scale[j], bias[j]), one rounding per
+ * element; scale == NULL means 1, which gives exactly the rounded sum x[i,j] + bias[j] (the bias
+ * add).  Columns are channels: a (B, C, H, W) tensor stored NHWC is the M = B*H*W by N = C view
+ * ([LAYOUT] "NCHW versus NHWC": per-channel scale and bias want the channels contiguous, and
+ * reading the tensor as NC moves no data).  scale, bias: N floats each, device memory, 4-byte
+ * aligned (16-byte aligned lets them load as 16-byte vectors); bias may be NULL only when there is
+ * no work.  Tiles, paths and variants as for tm_map_affine (the promise covers x and y). */
+int tm_channel_affine(const float *x, int64_t ldx, const float *scale, const float *bias, float *y,
+                      int64_t ldy, int64_t M, int64_t N, int TM, int TN, int aligned, int variant,
+                      void *stream);
+
 /* ---- row and column reductions -------------------------------------------------------------- */
 
 /* out[i] = sum over j < N of x[i,j] for i < M (out: M floats, contiguous).  Rows are walked with

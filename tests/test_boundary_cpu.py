@@ -256,3 +256,15 @@ def test_transpose_errors():
     assert call(ldy=66) == tm.TM_E_ALIGN
     assert call(B=2, bsx=64 * 128 + 2, bsy=128 * 64) == tm.TM_E_ALIGN
     assert call(B=0, x=0, y=0) == tm.TM_OK
+
+
+@no_gpu
+def test_channel_affine_errors():
+    f = tm.tm_channel_affine
+    C16 = 0x7F0000200000
+    assert f(A16, 64, C16, 0, B16, 64, 128, 64, 64, 64, 1, 0, S) == tm.TM_E_INVAL        # NULL bias
+    assert f(A16, 64, C16 + 2, C16, B16, 64, 128, 64, 64, 64, 1, 0, S) == tm.TM_E_INVAL  # scale not 4-aligned
+    assert f(A16, 64, 0, C16 + 1, B16, 64, 128, 64, 64, 64, 1, 0, S) == tm.TM_E_INVAL    # bias not 4-aligned
+    assert f(A16, 64, 0, C16, B16, 64, 130, 64, 64, 64, 1, 0, S) == tm.TM_E_ALIGN        # 130 % 64
+    assert f(A16, 64, 0, C16, B16, 64, 128, 64, 64, 48, 0, 0, S) == tm.TM_E_UNSUPPORTED
+    assert f(0, 64, 0, 0, 0, 64, 0, 64, 64, 64, 1, 0, S) == tm.TM_OK                     # no work

@@ -334,3 +334,56 @@ def test_beyond_2g_elements(dev):
         assert np.array_equal(bits(got), bits(want)), r
     del x, y
     torch.cuda.empty_cache()
+
+
+# ---- per-channel affine on an NC view ----------------------------------------------------------------
+
+def check_channel(dev, M, N, ldx, ldy, TM, TN, aligned, variant, with_scale, coff=0, seed=5,
+                  expect=tm.TM_OK):
+    xh = inputs.uniform(seed, max((M - 1) * ldx + N, 1), -8.0, 8.0)
+    sh = inputs.uniform(seed + 1, max(N, 1), -2.0, 2.0)
+    bh = inputs.uniform(seed + 2, max(N, 1), -1.0, 1.0)
+    X = Guarded(xh.size, dev)
+    X.upload(xh)
+    Sv = Guarded(sh.size, dev, coff)
+    Sv.upload(sh)
+    Bv = Guarded(bh.size, dev, coff)
+    Bv.upload(bh)
+    Y = Guarded(max(M * ldy, 1), dev)
+    st = tm.tm_channel_affine(X.ptr, ldx, Sv.ptr if with_scale else 0, Bv.ptr, Y.ptr, ldy, M, N, TM,
+                              TN, aligned, variant)
+    assert st == expect, (M, N, ldx, ldy, TM, TN, aligned, variant, tm.tm_status_string(st))
+    torch.cuda.synchronize()
+    want = sentinel_host(Y.buf.numel())
+    if st == tm.TM_OK and M and N:
+        region = want[Y.off:Y.off + Y.n].copy()
+        oracle.channel_affine(xh, ldx, sh if with_scale else None, bh, region, ldy, M, N)
+        want[Y.off:Y.off + Y.n] = region
+    assert np.array_equal(bits(Y.host()), bits(want)), (M, N, ldx, ldy, TM, TN, aligned, variant, with_scale)
+    assert Sv.guards_intact() and Bv.guards_intact() and X.guards_intact()
+
+
+def test_channel_affine_nhwc_batches(dev):
+    """(B, C, H, W) = (32, 64, 56, 56) stored NHWC as a 100352 x 64 NC view, aligned; then channel
+    counts that are not multiples of the tile or of 4 (3 = RGB, 130) on the ragged path."""
+    for with_scale in (False, True):
+        note("channel affine nhwc 32x56x56x64 scale=%d" % with_scale)
+        check_channel(dev, 32 * 56 * 56, 64, 64, 64, 64, 64, 1, tm.TM_VAR_AUTO, with_scale)
+        for C in (3, 130):
+            check_channel(dev, 8 * 28 * 28, C, C, C, 64, 64, 0, tm.TM_VAR_AUTO, with_scale)
+    check_channel(dev, 100, 64, 64, 64, 64, 64, 1, tm.TM_VAR_AUTO, True, expect=tm.TM_E_ALIGN)
+
+
+def test_channel_affine_variants_and_unaligned_vectors(dev):
+    for variant in (tm.TM_VAR_SCALAR, tm.TM_VAR_VEC4_UNDERSTATED, tm.TM_VAR_VEC4):
+        for coff in (0, 1):
+            check_channel(dev, 257, 1000, 1000, 1004, 16, 64, 0, variant, True, coff=coff)
+
+
+def test_channel_affine_brute_force_tiny(dev):
+    for M in (1, 2, 5, 17):
+        for N in (1, 3, 4, 7, 16, 17):
+            for (TM, TN) in ((1, 1), (2, 4), (8, 8), (16, 1024)):
+                for with_scale in (False, True):
+                    check_channel(dev, M, N, N + 1, N + 2, TM, TN, 0, tm.TM_VAR_AUTO, with_scale,
+                                  seed=M * 100 + N)
