@@ -17,8 +17,8 @@ The same JSON line carries
   paths         every other path of the method, each on its own workload shape and timed the
                 same way: the ragged path on the same shape, the three 1-D access variants, the
                 ragged 4100 x 1000 map, row and column sums (naive and LDS walks), the masked
-                row max, the softmax row statistics, the per-channel bias add and the transpose /
-                NCHW -> NHWC conversion.
+                row max, the softmax row statistics, the per-channel bias add, a tile-size sweep
+                and the transpose / NCHW -> NHWC conversion.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--paths all|none] [--cpu-seconds S]
 """
@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--paths", choices=["all", "none"], default="all")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--sweep-out", default=None,
+                    help="write the full tile-size sweep table (JSON) to this file")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the step, time K runtime device-to-device copies of the same 64 MiB "
                          "buffers: the plain copy of known size that scales rocprofv3's byte counters")
@@ -188,7 +190,7 @@ def main():
                "sample": "oracle scale2d over the full 4096x4096 f32 matrix, %d repetitions in %.1f s "
                          "on one host core (%s)" % (reps, el, cpu_model())}
 
-    paths = run_paths(torch, tm, inputs, dev, stream, K, W) if args.paths == "all" else None
+    paths = run_paths(torch, tm, inputs, dev, stream, K, W, args.sweep_out) if args.paths == "all" else None
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
@@ -221,7 +223,7 @@ def cpu_model():
     return "unknown CPU"
 
 
-def run_paths(torch, tm, inputs, dev, stream, K, W):
+def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None):
     """Every other path, each on its workload shape, K launches after W warm-ups."""
     out = {}
 
@@ -340,6 +342,31 @@ def run_paths(torch, tm, inputs, dev, stream, K, W):
                                             tm.TM_VAR_VEC4, stream)),
           "y[n, c] = x[n, c] + bias[c] on the NC view of an NHWC tensor, 64x64 tiles")
     del xs, ys
+
+    # tile-size sweep: every tile that keeps the promise for Y = 1.5 X on 8192 x 8192 (512 MiB
+    # touched per launch, more than the Infinity Cache holds)
+    M = N = 8192
+    x = torch.from_numpy(inputs.scale_input(M, N, seed=9)).to(dev)
+    y = torch.empty_like(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st, TMb, TNb, us, table = tm.tm_autotune_map(1, x, N, y, N, M, N, 1.5, 0.0, 1, tm.TM_VAR_AUTO, 5, e0, e1,
+                                                 stream)
+    ok(st)
+    nb = 2 * M * N * 4
+    runs = sorted((t, 1 << i, 1 << j) for i, row in enumerate(table) for j, t in enumerate(row) if t > 0)
+    top = runs[:max(1, len(runs) // 10)]
+    out["autotune_scale_8192"] = {
+        "best_tile": [TMb, TNb], "mean_us": round(us, 3), "gbs": round(gbs(nb, us * 1e-6), 1),
+        "frac": round(gbs(nb, us * 1e-6) / PEAK_GBS, 4), "tiles_run": len(runs),
+        "plateau_gbs": round(gbs(nb, float(np.median([t for t, _, _ in top])) * 1e-6), 1),
+        "slowest": {"tile": [runs[-1][1], runs[-1][2]], "gbs": round(gbs(nb, runs[-1][0] * 1e-6), 1)},
+        "note": "tm_autotune_map over every menu tile keeping the promise, 5 launches each; plateau = "
+                "median of the fastest tenth"}
+    if sweep_out:
+        with open(sweep_out, "w") as f:
+            json.dump({"workload": "scale2d 8192x8192 f32, aligned", "bytes_per_launch": nb,
+                       "us_per_launch": {"%dx%d" % (a, b): round(t, 3) for t, a, b in runs}}, f, indent=1)
+    del x, y
 
     # transpose 4096 x 4096 (64x64 tiles) and the NCHW -> NHWC conversion of [32][64][56*56]
     M = N = 4096

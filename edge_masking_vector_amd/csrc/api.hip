@@ -116,6 +116,73 @@ TM_API int tm_plan_tiles(int64_t M, int64_t N, int TM, int TN, int64_t *tiles_m,
     return tmp::plan_tiles(M, N, TM, TN, tiles_m, tiles_n, whole);
 }
 
+TM_API int tm_pad_extents(int64_t M, int64_t N, int TM, int TN, int64_t *Mp, int64_t *Np,
+                          int64_t *ldp) {
+    return tmp::pad_extents(M, N, TM, TN, Mp, Np, ldp);
+}
+
+TM_API int tm_autotune_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t M,
+                           int64_t N, float alpha, float beta, int aligned, int variant, int reps,
+                           void *ev_start, void *ev_stop, int *TM_best, int *TN_best, float *us_best,
+                           float *table, void *stream) {
+    if (op < tmp::kAffine || op > tmp::kCopy || reps < 1 || ev_start == nullptr ||
+        ev_stop == nullptr || TM_best == nullptr || TN_best == nullptr || us_best == nullptr)
+        return TM_E_INVAL;
+    if (x != nullptr && x == y)
+        return TM_E_INVAL;  // the op runs many times: it must read the same input each time
+    constexpr int kRowsT = 9, kColsT = 11;  // TM = 2^0..2^8, TN = 2^0..2^10
+    // Validate the shared arguments once, with a tile every call accepts.
+    tmp::MapPlan plan;
+    int st = tmp::plan_map(op, x, ldx, y, ldy, M, N, alpha, beta, 1, 4, 0, variant, &plan);
+    if (st != TM_OK && st != TM_E_ALIGN && st != TM_E_UNSUPPORTED)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
+    float best = -1.0f;
+    int best_tm = 0, best_tn = 0;
+    for (int i = 0; i < kRowsT; ++i) {
+        for (int j = 0; j < kColsT; ++j) {
+            const int TM = 1 << i, TN = 1 << j;
+            float us = -1.0f;
+            st = tmp::plan_map(op, x, ldx, y, ldy, M, N, alpha, beta, TM, TN, aligned, variant, &plan);
+            if (st == TM_OK && plan.launch) {
+                if (tmk::launch_map(plan, s) != hipSuccess)  // warm-up
+                    return TM_E_HIP;
+                if (hipEventRecord(e0, s) != hipSuccess)
+                    return TM_E_HIP;
+                for (int r = 0; r < reps; ++r)
+                    if (tmk::launch_map(plan, s) != hipSuccess)
+                        return TM_E_HIP;
+                float ms = 0.0f;
+                if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                    hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
+                    return TM_E_HIP;
+                us = ms * 1000.0f / reps;
+                if (best < 0.0f || us < best) {
+                    best = us;
+                    best_tm = TM;
+                    best_tn = TN;
+                }
+            } else if (st == TM_OK) {
+                us = 0.0f;  // valid call with no work (M or N is 0)
+                if (best < 0.0f) {
+                    best = 0.0f;
+                    best_tm = TM;
+                    best_tn = TN;
+                }
+            }
+            if (table != nullptr)
+                table[i * kColsT + j] = us;
+        }
+    }
+    if (best < 0.0f)
+        return TM_E_ALIGN;  // no tile of the menu is accepted (under the promise: none keeps it)
+    *TM_best = best_tm;
+    *TN_best = best_tn;
+    *us_best = best;
+    return TM_OK;
+}
+
 TM_API const char *tm_status_string(int status) {
     switch (status) {
     case TM_OK: return "TM_OK";

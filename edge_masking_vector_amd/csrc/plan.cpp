@@ -121,6 +121,22 @@ int plan_tiles(int64_t M, int64_t N, int TM, int TN, int64_t *tiles_m, int64_t *
     return TM_OK;
 }
 
+int pad_extents(int64_t M, int64_t N, int TM, int TN, int64_t *Mp, int64_t *Np, int64_t *ldp) {
+    if (Mp == nullptr || Np == nullptr || ldp == nullptr || M < 0 || N < 0 || TM <= 0 || TN <= 0)
+        return TM_E_INVAL;
+    int st = check_tile(TM, TN);
+    if (st != TM_OK)
+        return st;
+    if (TN % 4 != 0)
+        return TM_E_ALIGN;  // tile rows shorter than a 16-byte vector cannot keep the promise
+    if (M > INT64_MAX / 4 - TM || N > INT64_MAX / 4 - TN)
+        return TM_E_INVAL;
+    *Mp = ceil_div(M, TM) * TM;
+    *Np = ceil_div(N, TN) * TN;
+    *ldp = *Np;  // a multiple of TN, hence of 4
+    return TM_OK;
+}
+
 // ---- element-wise maps ------------------------------------------------------------------------
 
 int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t M, int64_t N,

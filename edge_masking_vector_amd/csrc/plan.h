@@ -129,5 +129,6 @@ int check_promise(int64_t M, int64_t N, int64_t ld_in, int64_t ld_out, int TM, i
                   const void *in, const void *out);
 int plan_tiles(int64_t M, int64_t N, int TM, int TN, int64_t *tiles_m, int64_t *tiles_n,
                int64_t *whole);
+int pad_extents(int64_t M, int64_t N, int TM, int TN, int64_t *Mp, int64_t *Np, int64_t *ldp);
 
 }  // namespace tmp

@@ -58,6 +58,10 @@ _SIGS = {
     "tm_check_promise": (_int, [_i64, _i64, _i64, _i64, _int, _int, _vp, _vp]),
     "tm_split": (_int, [_i64, _i64, _i64p, _i64p]),
     "tm_plan_tiles": (_int, [_i64, _i64, _int, _int, _i64p, _i64p, _i64p]),
+    "tm_pad_extents": (_int, [_i64, _i64, _int, _int, _i64p, _i64p, _i64p]),
+    "tm_autotune_map": (_int, [_int, _vp, _i64, _vp, _i64, _i64, _i64, _f32, _f32, _int, _int, _int,
+                               _vp, _vp, ctypes.POINTER(_int), ctypes.POINTER(_int),
+                               ctypes.POINTER(_f32), ctypes.POINTER(_f32), _vp]),
     "tm_status_string": (ctypes.c_char_p, [_int]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -162,6 +166,36 @@ def tm_plan_tiles(M, N, TM, TN):
     a, b, c = ctypes.c_int64(-1), ctypes.c_int64(-1), ctypes.c_int64(-1)
     st = _lib.tm_plan_tiles(M, N, TM, TN, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
     return st, a.value, b.value, c.value
+
+
+def tm_pad_extents(M, N, TM, TN):
+    """Returns (status, Mp, Np, ldp)."""
+    a, b, c = ctypes.c_int64(-1), ctypes.c_int64(-1), ctypes.c_int64(-1)
+    st = _lib.tm_pad_extents(M, N, TM, TN, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    return st, a.value, b.value, c.value
+
+
+TUNE_ROWS, TUNE_COLS = 9, 11
+
+
+def tm_autotune_map(op, x, ldx, y, ldy, M, N, alpha, beta, aligned, variant, reps, ev_start, ev_stop,
+                    stream=None):
+    """Returns (status, TM_best, TN_best, us_best, table) with table a 9 x 11 list of lists
+    (TM = 2^i rows, TN = 2^j columns; -1 where not run).  ev_start / ev_stop: torch.cuda.Event
+    objects created with enable_timing=True (or raw hipEvent_t integers)."""
+    tmb, tnb, usb = _int(0), _int(0), _f32(0.0)
+    table = (_f32 * (TUNE_ROWS * TUNE_COLS))()
+    def ev(e):
+        if isinstance(e, int):
+            return e
+        if e.cuda_event == 0:  # torch creates the event on its first record
+            e.record(torch.cuda.current_stream() if stream is None else stream)
+        return e.cuda_event
+    st = _lib.tm_autotune_map(op, _ptr(x), ldx, _ptr(y), ldy, M, N, alpha, beta, aligned, variant,
+                              reps, ev(ev_start), ev(ev_stop), ctypes.byref(tmb), ctypes.byref(tnb),
+                              ctypes.byref(usb), table, _stream(stream))
+    rows = [[table[i * TUNE_COLS + j] for j in range(TUNE_COLS)] for i in range(TUNE_ROWS)]
+    return st, tmb.value, tnb.value, usb.value, rows
 
 
 def tm_status_string(status):

@@ -207,6 +207,34 @@ int tm_split(int64_t K, int64_t T, int64_t *nfull, int64_t *rem);
 int tm_plan_tiles(int64_t M, int64_t N, int TM, int TN, int64_t *tiles_m, int64_t *tiles_n,
                   int64_t *whole);
 
+/* Padding that keeps the alignment promise ([ALIGNED] "Interactions": when a tuner picks the tile,
+ * the host must pad or pick shapes that keep the promise for every candidate).  Writes the
+ * smallest *Mp >= M and *Np >= N that are multiples of TM and TN, and *ldp = *Np, a row stride of
+ * whole 16-byte units.  An Mp x Np tensor with row stride ldp on a 16-byte aligned base (its
+ * padding zero-filled by the caller) then keeps the promise for TM x TN tiles; to keep it for every
+ * tile of a set of candidates, pass the largest TM and TN of the set (menu extents are powers of
+ * two, so the largest is a multiple of the others).  TM_E_ALIGN if TN % 4 != 0 (no tile row can be
+ * 16-byte vectors); TM_E_INVAL / TM_E_UNSUPPORTED for malformed arguments or NULL outputs. */
+int tm_pad_extents(int64_t M, int64_t N, int TM, int TN, int64_t *Mp, int64_t *Np, int64_t *ldp);
+
+/* Tile-size sweep for the element-wise maps ([ALIGNED] "Interactions", @autotune; [LAYOUT] "What it
+ * actually costs": measure rather than predict).  Runs op (0 = tm_map_affine, 1 = tm_scale2d,
+ * 2 = tm_copy2d) from x to y with every tile of the menu (TM = 1..256, TN = 1..1024, powers of
+ * two) that the call accepts -- with aligned = 1, only tiles that keep the promise -- reps times
+ * each on `stream` after one warm-up launch, timing each candidate between the caller's two HIP
+ * events (hipEvent_t passed as void*).  Returns the fastest tile in *TM_best, *TN_best and its mean
+ * time per launch in *us_best.  If table != NULL it receives 9 x 11 floats, row i for TM = 2^i and
+ * column j for TN = 2^j: the candidate's mean microseconds per launch, or -1 where it was not run.
+ * The caller's buffers are used as they are: buffers that fit in the 256 MiB Infinity Cache time
+ * cache bandwidth, not HBM.  Synchronizes `stream`; y holds the op's result afterwards.  x and y
+ * must not overlap.  Errors: those of the op's own call for the shared arguments; TM_E_INVAL for
+ * an unknown op, reps < 1, a NULL event or result pointer, or x == y; TM_E_ALIGN when no tile keeps
+ * the promise; TM_E_HIP if a launch or event call fails. */
+int tm_autotune_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t M, int64_t N,
+                    float alpha, float beta, int aligned, int variant, int reps, void *ev_start,
+                    void *ev_stop, int *TM_best, int *TN_best, float *us_best, float *table,
+                    void *stream);
+
 /* Static, human-readable name of a status code ("TM_OK", ...; "unknown status" otherwise). */
 const char *tm_status_string(int status);
 

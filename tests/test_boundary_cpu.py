@@ -268,3 +268,41 @@ def test_channel_affine_errors():
     assert f(A16, 64, 0, C16, B16, 64, 130, 64, 64, 64, 1, 0, S) == tm.TM_E_ALIGN        # 130 % 64
     assert f(A16, 64, 0, C16, B16, 64, 128, 64, 64, 48, 0, 0, S) == tm.TM_E_UNSUPPORTED
     assert f(0, 64, 0, 0, 0, 64, 0, 64, 64, 64, 1, 0, S) == tm.TM_OK                     # no work
+
+
+def test_pad_extents_keep_the_promise():
+    """The padded extents keep the oracle's promise predicate and are the smallest that do."""
+    for M in range(0, 40):
+        for N in range(0, 40):
+            for TM in (1, 2, 4, 8, 16):
+                for TN in (4, 8, 16, 32):
+                    st, Mp, Np, ldp = tm.tm_pad_extents(M, N, TM, TN)
+                    assert st == tm.TM_OK
+                    assert Mp >= M and Np >= N and ldp >= Np
+                    assert oracle.promise_holds(Mp, Np, ldp, ldp, TM, TN, 0x1000, 0x2000)
+                    assert not any(oracle.promise_holds(m, Np, ldp, ldp, TM, TN, 0x1000, 0x2000)
+                                   for m in range(M, Mp))
+                    assert not any(oracle.promise_holds(Mp, n, ldp, ldp, TM, TN, 0x1000, 0x2000)
+                                   for n in range(N, Np))
+    # the ragged workloads: 4100 x 1000 under 64 x 64 pads to 4160 x 1024
+    assert tm.tm_pad_extents(4100, 1000, 64, 64) == (tm.TM_OK, 4160, 1024, 1024)
+    assert tm.tm_pad_extents(8192, 1000, 16, 64) == (tm.TM_OK, 8192, 1024, 1024)
+    assert tm.tm_pad_extents(10, 10, 4, 2)[0] == tm.TM_E_ALIGN
+    assert tm.tm_pad_extents(10, 10, 3, 4)[0] == tm.TM_E_UNSUPPORTED
+    assert tm.tm_pad_extents(-1, 10, 4, 4)[0] == tm.TM_E_INVAL
+
+
+@no_gpu
+def test_autotune_errors():
+    f = tm._lib.tm_autotune_map
+    import ctypes
+    i1, i2, u = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_float(0)
+    E = 0x7F0000300000
+    args = lambda op=1, x=A16, y=B16, reps=3, e0=E, e1=E: (op, x, 64, y, 64, 64, 64, 1.5, 0.0, 1, 0, reps,
+                                                             e0, e1, ctypes.byref(i1), ctypes.byref(i2),
+                                                             ctypes.byref(u), None, S)
+    assert f(*args(op=7)) == tm.TM_E_INVAL
+    assert f(*args(reps=0)) == tm.TM_E_INVAL
+    assert f(*args(e0=0)) == tm.TM_E_INVAL
+    assert f(*args(y=A16)) == tm.TM_E_INVAL          # in place
+    assert f(*args(x=A16 + 2)) == tm.TM_E_INVAL      # malformed shared argument

@@ -387,3 +387,37 @@ def test_channel_affine_brute_force_tiny(dev):
                 for with_scale in (False, True):
                     check_channel(dev, M, N, N + 1, N + 2, TM, TN, 0, tm.TM_VAR_AUTO, with_scale,
                                   seed=M * 100 + N)
+
+
+# ---- tile-size sweep / autotune ------------------------------------------------------------------
+
+def test_autotune_map(dev):
+    """The sweep runs every tile that keeps the promise (and only those), returns the fastest, and
+    leaves y holding the op's result."""
+    M = N = 1024
+    xh = inputs.scale_input(M, N, seed=21)
+    x = torch.from_numpy(xh).to(dev)
+    y = torch.zeros_like(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st, TMb, TNb, us, table = tm.tm_autotune_map(1, x, N, y, N, M, N, 1.5, 0.0, 1,
+                                                 tm.TM_VAR_AUTO, 3, e0, e1)
+    assert st == tm.TM_OK
+    want = np.empty_like(xh)
+    oracle.scale2d(xh, N, want, N, M, N, 1.5)
+    assert np.array_equal(bits(y), bits(want))
+    ran = [(1 << i, 1 << j, table[i][j]) for i in range(9) for j in range(11) if table[i][j] >= 0]
+    assert ran and all(oracle.promise_holds(M, N, N, N, a, b, x.data_ptr(), y.data_ptr()) for a, b, _ in ran)
+    assert len(ran) == sum(oracle.promise_holds(M, N, N, N, 1 << i, 1 << j, x.data_ptr(), y.data_ptr())
+                           for i in range(9) for j in range(11))
+    assert (TMb, TNb) in [(a, b) for a, b, _ in ran] and us == min(t for _, _, t in ran) and us > 0
+    # ragged shapes: all tiles run; no tile keeps the promise on an odd column count
+    x2 = torch.from_numpy(inputs.ragged_input(99, 1001)).to(dev)
+    y2 = torch.zeros_like(x2)
+    st, TMb, TNb, us, table = tm.tm_autotune_map(0, x2, 1001, y2, 1001, 99, 1001, 0.75, -0.25, 0,
+                                                 tm.TM_VAR_SCALAR, 1, e0, e1)
+    assert st == tm.TM_OK and all(v >= 0 for row in table for v in row)
+    want = np.empty(99 * 1001, np.float32)
+    oracle.map_affine(x2.cpu().numpy(), 1001, want, 1001, 99, 1001, 0.75, -0.25)
+    assert np.array_equal(bits(y2), bits(want))
+    st = tm.tm_autotune_map(0, x2, 1001, y2, 1001, 99, 1001, 0.75, -0.25, 1, tm.TM_VAR_AUTO, 1, e0, e1)[0]
+    assert st == tm.TM_E_ALIGN
