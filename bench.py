@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 
 PEAK_GBS = 8000.0            # MI355X HBM3E, published
 ROTATE_BYTES = 1 << 30       # bytes touched per rotation of buffer sets
+BATCHES, BATCH_LAUNCHES = 10, 50   # step batch statistics
 METRIC = "achieved HBM GB/s and % of 8 TB/s peak, aligned vs ragged, per config"
 STEP_KERNEL_SOURCES = ["edge_masking_vector_amd/csrc/map.hip", "edge_masking_vector_amd/csrc/device.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scale2d_4096_aligned.json")
@@ -47,10 +48,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--paths", choices=["all", "none"], default="all")
+    ap.add_argument("--paths", choices=["main", "all", "none"], default="main",
+                    help="other paths to time after the step: main (every path but the tile sweep, "
+                         "whose 8192x8192 launches share the step's kernel), all (main plus the sweep), "
+                         "or none")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep-out", default=None,
-                    help="write the full tile-size sweep table (JSON) to this file")
+                    help="with --paths all: write the full tile-size sweep table (JSON) to this file")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the step, time K runtime device-to-device copies of the same 64 MiB "
                          "buffers: the plain copy of known size that scales rocprofv3's byte counters")
@@ -145,6 +149,9 @@ def main():
     value = gbs(step_bytes, total / K)
     mean_launch = total / K   # one kernel launch per step
     achieved = gbs(step_bytes, mean_launch)
+    # Batch statistics, after the timed region: BATCHES batches of BATCH_LAUNCHES launches, each
+    # bracketed by its own events.
+    batch = sorted(Timer(torch, stream).run(step, BATCH_LAUNCHES) / BATCH_LAUNCHES for _ in range(BATCHES))
 
     calib = None
     if args.calibrate_copy:
@@ -166,7 +173,10 @@ def main():
                 "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "map_tiles<scale, vec4, aligned>",
                 "algorithmic_bytes_per_launch": step_bytes,
-                "mean_launch_us": round(mean_launch * 1e6, 3)}
+                "mean_launch_us": round(mean_launch * 1e6, 3),
+                "batches": {"count": BATCHES, "launches_each": BATCH_LAUNCHES,
+                            "median_launch_us": round(float(np.median(batch)) * 1e6, 3),
+                            "min_launch_us": round(batch[0] * 1e6, 3)}}
 
     # ---- CPU baseline: the oracle on the same matrix, single-threaded ----------------------------
     cpu = None
@@ -178,19 +188,27 @@ def main():
         if not np.array_equal(got.view(np.uint32), yh.view(np.uint32)):
             print("bench.py: the timed kernel's output differs from the oracle", file=sys.stderr)
             return 1
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            oracle.scale2d(xh, N, yh, N, M, N, alpha)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
+        # one thread, pinned to one of the cores this process may use
+        allowed = os.sched_getaffinity(0)
+        core = min(allowed)
+        os.sched_setaffinity(0, {core})
+        try:
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                oracle.scale2d(xh, N, yh, N, M, N, alpha)
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= args.cpu_seconds:
+                    break
+        finally:
+            os.sched_setaffinity(0, allowed)
         cpu = {"value": round(gbs(step_bytes * reps, el), 3), "unit": "GB/s", "cores": 1,
                "kind": "oracle",
                "sample": "oracle scale2d over the full 4096x4096 f32 matrix, %d repetitions in %.1f s "
-                         "on one host core (%s)" % (reps, el, cpu_model())}
+                         "on host core %d (%s)" % (reps, el, core, cpu_model())}
 
-    paths = run_paths(torch, tm, inputs, dev, stream, K, W, args.sweep_out) if args.paths == "all" else None
+    paths = (run_paths(torch, tm, inputs, dev, stream, K, W, args.sweep_out, sweep=args.paths == "all")
+             if args.paths != "none" else None)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
@@ -205,6 +223,9 @@ def main():
         "cpu_baseline": cpu,
     }
     if paths is not None:
+        ceiling = paths["ceiling_probe_copy_512MiB"]
+        roofline["ceiling_gbs"] = max(ceiling["tm_copy2d_gbs"], ceiling["runtime_copy_gbs"])
+        roofline["frac_of_ceiling"] = round(achieved / roofline["ceiling_gbs"], 4)
         line["paths"] = paths
     if calib is not None:
         line["calibration_copy"] = calib
@@ -223,8 +244,9 @@ def cpu_model():
     return "unknown CPU"
 
 
-def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None):
-    """Every other path, each on its workload shape, K launches after W warm-ups."""
+def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True):
+    """Every other path, each on its workload shape, K launches after W warm-ups (the tile sweep
+    only if `sweep`)."""
     out = {}
 
     def timed(name, nbytes, n_sets, launch, note):
@@ -237,6 +259,23 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None):
     def ok(st):
         if st != tm.TM_OK:
             raise tm.TilemapError(st)
+
+    # ceiling probe: the aligned copy and the runtime's device-to-device copy of 8192 x 8192 f32
+    # (256 MiB read + 256 MiB written per launch, twice the Infinity Cache)
+    M = N = 8192
+    nb = 2 * M * N * 4
+    R = sets_for(nb)
+    xs = rotated(torch, inputs.uniform(10, M * N, -1.0, 1.0), R, dev)
+    ys = [torch.empty_like(x) for x in xs]
+    timed("_probe_tm", nb, R, lambda i: ok(tm.tm_copy2d(xs[i], N, ys[i], N, M, N, 32, 128, 1,
+                                                         tm.TM_VAR_VEC4, stream)), "")
+    timed("_probe_rt", nb, R, lambda i: ys[i].copy_(xs[i]), "")
+    a, b = out.pop("_probe_tm"), out.pop("_probe_rt")
+    out["ceiling_probe_copy_512MiB"] = {
+        "tm_copy2d_gbs": a["gbs"], "tm_copy2d_us": a["mean_us"], "runtime_copy_gbs": b["gbs"],
+        "runtime_copy_us": b["mean_us"], "bytes": nb,
+        "note": "8192x8192 f32: tm_copy2d aligned 32x128 vec4, and torch's device-to-device copy"}
+    del xs, ys
 
     # 4096 x 4096 scale: ragged path (aligned=0) and scalar accesses
     M = N = 4096
@@ -345,6 +384,17 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None):
 
     # tile-size sweep: every tile that keeps the promise for Y = 1.5 X on 8192 x 8192 (512 MiB
     # touched per launch, more than the Infinity Cache holds)
+    if sweep:
+        sweep_paths(torch, tm, inputs, dev, stream, out, sweep_out)
+    transpose_paths(torch, tm, inputs, dev, stream, timed, ok)
+    torch.cuda.synchronize()
+    return out
+
+
+def sweep_paths(torch, tm, inputs, dev, stream, out, sweep_out):
+    def ok(st):
+        if st != tm.TM_OK:
+            raise tm.TilemapError(st)
     M = N = 8192
     x = torch.from_numpy(inputs.scale_input(M, N, seed=9)).to(dev)
     y = torch.empty_like(x)
@@ -368,6 +418,8 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None):
                        "us_per_launch": {"%dx%d" % (a, b): round(t, 3) for t, a, b in runs}}, f, indent=1)
     del x, y
 
+
+def transpose_paths(torch, tm, inputs, dev, stream, timed, ok):
     # transpose 4096 x 4096 (64x64 tiles) and the NCHW -> NHWC conversion of [32][64][56*56]
     M = N = 4096
     xh = inputs.scale_input(M, N)
@@ -389,8 +441,6 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None):
           lambda i: ok(tm.tm_transpose(xs[i], HW, C * HW, ys[i], C, HW * C, B, C, HW, 64, 64, 1, stream)),
           "batched transpose [B][C][HW] -> [B][HW][C]")
     del xs, ys
-    torch.cuda.synchronize()
-    return out
 
 
 if __name__ == "__main__":

@@ -10,17 +10,19 @@
 //
 // Mapping (the tile scheduler).  A tile holds TM rows of VR = TN/W chunks (W = 4 elements for the
 // vector variants, 1 for scalar).  A workgroup takes one work item: R consecutive rows of G
-// horizontally adjacent tiles of one tile row band, R*G*VR chunks, moved by up to 1024 threads
+// horizontally adjacent tiles of one tile row band, R*G*VR chunks, moved by 64 to 1024 threads
 // with U chunks per thread (U = 4 for scalar, else 1) at a stride of the workgroup size, all loads
 // before any store.  Within a work-item row the lane-varying term of every address is the chunk
-// index, so a wave reads 64 consecutive chunks (1 KiB of 16-byte chunks).  Work items run with the
-// tile groups fastest, then row strips, then tile rows, so workgroups dispatched together cover
-// neighbouring memory.  The host picks the geometry (plan.cpp): when rows start on 128-byte lines a
-// work item is one whole tile (or a strip of one), otherwise it spans as many tiles as fit across
-// the row band, so that few 128-byte lines are shared by workgroups that may run on different XCDs
-// (each XCD has its own L2 and would fetch a shared line again).  Whole chunks move with the
-// non-temporal hint.  On gfx950 one 16-byte chunk per thread in 1024-thread workgroups streamed
-// faster than fewer threads with several chunks each.
+// index, so a wave reads consecutive chunks of a row.  Work items run with the tile groups
+// fastest, then row strips, then tile rows, so workgroups dispatched together cover neighbouring
+// memory.  The host picks the geometry (plan.cpp): when rows start on 128-byte lines a work item
+// is one wave's worth of chunks (a strip of rows of one tile, widened across tiles only to whole
+// lines), otherwise it spans as many tiles as fit in 1024 threads across the row band, so that
+// few 128-byte lines are shared by workgroups that may run on different XCDs (each XCD has its
+// own L2 and would fetch a shared line again).  Whole chunks move with the non-temporal hint.  On
+// gfx950 one 16-byte chunk per thread streamed faster than several chunks per thread, and
+// one-wave workgroups at least as fast as 1024-thread ones (up to 11% faster on jobs of a few
+// thousand workgroups, whose last round of workgroups is otherwise ragged).
 //
 // Paths.  aligned=1: no masks at all (the host checked whole tiles and 16-byte rows).
 // aligned=0: a uniform per-tile test picks the same unmasked body for whole tiles; edge tiles

@@ -196,7 +196,6 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     const int log_u = ilog2(access == kScalar ? kScalarChunksPerThread : 1);
     const int log_vr = ilog2(TN / W);
     const int log_tm = ilog2(TM);
-    const int log_target = ilog2(kMapMaxBlock) + log_u;  // chunks per work item: 1024 threads x U
     // Widest tile group: in the aligned path it must divide the tile count (no tile checks on the
     // device); in the ragged path it may run past the last tile (those lanes stay idle).
     int log_gcap = 0;
@@ -206,18 +205,25 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     } else {
         log_gcap = ilog2(tiles_n);
     }
-    // Rows that start on cache lines: a work item is one tile (or a strip of one).  Otherwise it
-    // spans as many tiles across the row band as fit, so workgroups share few lines.
+    // Rows that start on cache lines: a work item is one wave's worth of chunks (64 x U) -- a strip
+    // of rows of one tile, widened to neighbouring tiles only as far as needed to cover whole
+    // 128-byte lines, so no two work items share a line.  One-wave workgroups fill whatever wave
+    // slots a CU has free; 1024-thread ones need 16 free slots on one CU at once.  Otherwise (rows
+    // off the line grid) a work item spans as many tiles across the row band as fit in 1024 x U
+    // chunks, so that workgroups share few lines.
     const int64_t line = kLineBytes / 4;
     const bool line_rows = aligned_to(x, kLineBytes) && aligned_to(y, kLineBytes) &&
                            (M <= 1 || (ldx % line == 0 && ldy % line == 0));
     int log_r, log_g;
     if (line_rows) {
-        log_r = std::min(log_tm, log_target - log_vr);
-        log_g = std::min(log_gcap, log_target - log_vr - log_r);
+        const int log_target = ilog2(kMapMinBlock) + log_u;
+        log_g = std::min(log_gcap, std::max(0, ilog2(line) - ilog2(TN)));  // tiles per line
+        log_r = std::min(log_tm, std::max(0, log_target - log_vr - log_g));
+        log_g = std::min(log_gcap, std::max(log_g, log_target - log_vr - log_r));
     } else {
-        log_g = std::min(log_gcap, log_target - log_vr);
-        log_r = std::min(log_tm, log_target - log_vr - log_g);
+        const int log_target = ilog2(kMapMaxBlock) + log_u;
+        log_g = std::min(log_gcap, std::max(0, log_target - log_vr));
+        log_r = std::min(log_tm, std::max(0, log_target - log_vr - log_g));
     }
     const int log_chunks = log_r + log_g + log_vr;
     const int64_t groups_n = ceil_div(tiles_n, int64_t{1} << log_g);
