@@ -29,9 +29,17 @@ __device__ __forceinline__ void st16_nt(float *p, f4 v) {
 __device__ __forceinline__ float ld4_nt(const float *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st4_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
 
-// e^x in f32 with the device math library's accurate expf (ROCm's OCML exp, about 1 ulp);
-// never the reduced-precision intrinsic.
-__device__ __forceinline__ float exp_f32(float x) { return expf(x); }
+// e^x in f32 for the softmax statistics, by the change of base e^x = 2^(x * log2 e) and the
+// hardware base-2 exponential (V_EXP_F32 of the CDNA ISA, about 1 ulp): two instructions where
+// the math library's expf takes a dozen, which made the statistics ALU-bound.  The callers pass
+// x = s - b with b the running maximum, so x <= 0; the product x * log2(e) is within about 2^-23
+// of its exact value (relative), so the result is within about |x| * 1.2e-7 (relative) of e^x.
+// A term's weight in the normaliser is e^x, so terms far below the maximum, where this grows,
+// barely count: the sum stays within about ln(n) * 1.2e-7 for n terms.  Results below 2^-126 may
+// flush to 0; such a term is under 1.2e-38 of the row's largest term (which is 1).
+__device__ __forceinline__ float exp_f32(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+}
 
 // ---- reduction operators ------------------------------------------------------------------
 struct SumOp {
