@@ -62,7 +62,8 @@ __global__ __launch_bounds__(kBlock) void col_naive(ColArgs a) {
                 s += wave_sum[i];
             a.ws[int64_t(slab) * a.N + c] = s;
         }
-        __syncthreads();
+        if (w + gridDim.x < nwork)
+            __syncthreads();  // the next work item reuses wave_sum (uniform test)
     }
 }
 
@@ -150,7 +151,8 @@ __global__ __launch_bounds__(kBlock) void col_lds(ColArgs a) {
             if (col0 + cl < a.N)
                 a.ws[int64_t(slab) * a.N + col0 + cl] = colsum;
         }
-        __syncthreads();
+        if (w + gridDim.x < nwork)
+            __syncthreads();  // the next work item reuses the LDS partials (uniform test)
     }
 }
 

@@ -29,6 +29,17 @@ __device__ __forceinline__ void st16_nt(float *p, f4 v) {
 __device__ __forceinline__ float ld4_nt(const float *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st4_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
 
+// a / d and a % d for a 32-bit a and a fixed divisor d, given c = ceil(2^64 / d) (0 when d = 1):
+// the multiply-high method of Lemire, Kaser and Kurz ("Faster remainder by direct computation",
+// 2019), exact for every 32-bit a.  A handful of scalar instructions where a run-time division
+// takes dozens.
+__device__ __forceinline__ uint32_t fast_div(uint32_t a, uint64_t c, uint32_t d) {
+    return d == 1 ? a : static_cast<uint32_t>(__umul64hi(c, a));
+}
+__device__ __forceinline__ uint32_t fast_mod(uint32_t a, uint64_t c, uint32_t d) {
+    return d == 1 ? 0u : static_cast<uint32_t>(__umul64hi(c * a, d));
+}
+
 // e^x in f32 for the softmax statistics, by the change of base e^x = 2^(x * log2 e) and the
 // hardware base-2 exponential (V_EXP_F32 of the CDNA ISA, about 1 ulp): two instructions where
 // the math library's expf takes a dozen, which made the statistics ALU-bound.  The callers pass

@@ -73,6 +73,13 @@ uint32_t cap_grid(int64_t work_items) {
 
 }  // namespace
 
+Div32 make_div32(uint32_t d) {
+    Div32 r;
+    r.d = d;
+    r.c = d > 1 ? ~uint64_t{0} / d + 1 : 0;  // ceil(2^64 / d) for d > 1
+    return r;
+}
+
 int ilog2(int64_t v) {
     int l = 0;
     while ((int64_t{1} << l) < v)
@@ -413,11 +420,11 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     plan->launch = true;
     plan->vec = vec;
     plan->aligned = aligned;
-    // Staged sub-tiles: 64 x 64, except that under the promise they must divide the extents
-    // (whole sub-tiles, no masks): then the largest power of two up to 64 that divides M (resp.
-    // N), which the promised tile divides.
+    // Staged sub-tiles: kTrSub x kTrSub, except that under the promise they must divide the
+    // extents (whole sub-tiles, no masks): then the largest power of two up to kTrSub that
+    // divides M (resp. N), which the promised tile divides.
     auto sub = [&](int64_t extent) {
-        int e = 64;
+        int e = kTrSub;
         if (aligned)
             while (extent % e != 0)
                 e /= 2;
@@ -433,6 +440,12 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     if (subs_m * subs_n > INT64_MAX / B)
         return TM_E_UNSUPPORTED;
     plan->nwork = static_cast<uint64_t>(B * subs_m * subs_n);
+    plan->wide = plan->nwork > UINT32_MAX;
+    if (!plan->wide) {
+        plan->per_b = make_div32(static_cast<uint32_t>(subs_m * subs_n));
+        plan->by_m = make_div32(plan->subs_m);
+        plan->by_n = make_div32(plan->subs_n);
+    }
     plan->grid = cap_grid(static_cast<int64_t>(std::min<uint64_t>(plan->nwork, INT64_MAX)));
     plan->x = x;
     plan->y = y;

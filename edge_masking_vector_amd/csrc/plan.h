@@ -20,6 +20,7 @@ constexpr int kMapMinBlock = 64;    // map workgroups: at least one wave ...
 constexpr int kMapMaxBlock = 1024;  // ... and at most 1024 threads
 constexpr int kScalarChunksPerThread = 4;  // 4-byte chunks per thread (16-byte chunks: one)
 constexpr int kLineBytes = 128;     // cache line
+constexpr int kTrSub = 32;          // transpose: largest staged sub-tile edge (one 128-byte line of f32)
 
 enum MapOp { kAffine = 0, kScale = 1, kCopy = 2, kChannel = 3 };
 enum Access { kScalar = 1, kVec4Understated = 2, kVec4 = 3 };
@@ -104,13 +105,25 @@ int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int 
               int aligned, int walk, void *ws, size_t ws_bytes, ColPlan *plan);
 
 // ---- batched transpose -----------------------------------------------------------------------
+// Division by a fixed divisor d >= 1 through a precomputed multiplier (Lemire, Kaser and Kurz,
+// "Faster remainder by direct computation", 2019): with c = ceil(2^64 / d), every 32-bit a has
+// a / d = the high 64 bits of c * a and a % d = the high 64 bits of (c * a mod 2^64) * d.  For
+// d = 1 the multiplier (2^64) does not fit; c is then 0 and the device takes the identity.
+struct Div32 {
+    uint64_t c = 0;
+    uint32_t d = 1;
+};
+Div32 make_div32(uint32_t d);
+
 struct TransposePlan {
     bool launch = false;
     bool vec = false;             // 16-byte chunks on both sides
     int aligned = 0;
-    int sm = 1, sn = 1;           // staged sub-tile extents (powers of two <= 64)
+    int sm = 1, sn = 1;           // staged sub-tile extents (powers of two <= kTrSub)
     uint32_t subs_m = 0, subs_n = 0;
     uint64_t nwork = 0;
+    bool wide = false;            // nwork >= 2^32: 64-bit work-item arithmetic
+    Div32 per_b, by_m, by_n;      // divisors subs_m * subs_n, subs_m, subs_n (when !wide)
     uint32_t grid = 0;
     const float *x = nullptr;
     float *y = nullptr;

@@ -7,60 +7,84 @@
 // "Strides, and reading an index expression"); Phobos docs "Slicing, bounds and masking"
 // ("Masking": out-of-range elements read as 0 and their stores are skipped).
 //
-// Mapping.  A workgroup (512 threads) takes one SM x SN sub-tile of x (64 x 64; under the alignment
-// promise the largest power of two up to 64 that divides the extent, which the caller's tile
-// divides); sub-tiles are visited in diagonal order (see below).  It reads the sub-tile along x's rows -- lanes take consecutive chunks of a row,
-// so the lane-varying term of the address is the column -- and stages it in LDS with a row stride
-// of SN + 1 floats.  After a barrier it reads the staged tile down its columns and writes y's rows,
+// Mapping.  A workgroup (256 threads) takes one SM x SN sub-tile of x (32 x 32: a row segment is
+// one 128-byte line; under the alignment promise the largest power of two up to 32 that divides
+// the extent, which the caller's tile divides); sub-tiles are visited in diagonal order (see
+// below).  It reads the sub-tile along x's rows -- lanes take consecutive chunks of a row, so the
+// lane-varying term of the address is the column -- and stages it in LDS with a row stride of
+// SN + 1 floats.  After a barrier it reads the staged tile down its columns and writes y's rows,
 // again with consecutive lanes on consecutive chunks of a y row.  Both global sides are coalesced;
 // only LDS sees the column order.  Chunks are 16 bytes when both tensors have 16-byte rows, else
 // single elements.  Under the alignment promise every sub-tile is whole and no mask is evaluated.
-// Diagonal order took the 4096 x 4096 transpose from 30.8 to 25.8 us, and 512 threads per
-// workgroup to 24.4 us.
+// Diagonal order took the 4096 x 4096 transpose from 30.8 to 25.8 us.  Sub-tile and workgroup
+// size, measured on 4096 x 4096 and on NCHW -> NHWC of [32][64][3136]: 64 x 64 with 512 threads
+// 24.6 / 10.6 us, 128 x 128 with 1024 threads 24.4 / -, 32 x 32 with 256 threads (one 16-byte
+// chunk per thread) 24.2 / 9.7 us.  Reading the staged tile by rows instead of columns (a
+// timing-only variant) changed nothing: LDS bank conflicts do not limit this kernel.
 #include "device.hpp"
 #include "launch.h"
 
 namespace tmk {
 namespace {
 
-constexpr int kSub = 64;            // largest sub-tile edge
+constexpr int kSub = tmp::kTrSub;   // largest sub-tile edge
 constexpr int kPad = kSub + 1;      // LDS row stride (floats) of the staged sub-tile
-constexpr int kTrBlock = 512;       // threads per workgroup (2 x 16-byte chunks each per sub-tile)
+constexpr int kTrBlock = 256;       // threads per workgroup (one 16-byte chunk each per sub-tile)
 
+// Kernel arguments: kept within 128 bytes so that one batch of scalar loads fetches them all
+// before the first global load (a field past that was fetched by a second, dependent load).
 struct TrArgs {
     const float *x;
     float *y;
     int64_t ldx, ldy, bsx, bsy;
-    int64_t B, M, N;
-    int sm, sn;                      // staged sub-tile extents (powers of two <= 64)
-    uint32_t subs_m, subs_n;         // sub-tiles along M and N per batch
+    int64_t M, N;
     uint64_t nwork;                  // B * subs_m * subs_n
+    uint64_t c_pb, c_m, c_n;         // multipliers of per_b, subs_m, subs_n for fast_div
+    uint32_t subs_m, subs_n;         // sub-tiles along M and N per batch
+    uint32_t per_b;                  // subs_m * subs_n (when the work count fits 32 bits)
+    int log_sm, log_sn;              // staged sub-tile extents: 2^log_sm x 2^log_sn (<= kSub)
 };
+static_assert(sizeof(TrArgs) <= 128, "transpose arguments outgrew one scalar load batch");
 
-template <bool VEC, bool ALIGNED, int BS>
+template <bool VEC, bool ALIGNED, int BS, bool WIDE>
 __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
-    constexpr int W = VEC ? 4 : 1;
-    constexpr int K = kSub * kSub / W / BS;   // chunks per thread for a full 64 x 64 sub-tile
+    constexpr int LOG_W = VEC ? 2 : 0;
+    constexpr int W = 1 << LOG_W;
+    constexpr int K = kSub * kSub / W / BS;   // chunks per thread for a full kSub x kSub sub-tile
     __shared__ float tile[kSub * kPad];
     const int t = threadIdx.x;
-    const int cpr_x = a.sn / W;     // chunks per staged x row
-    const int cpr_y = a.sm / W;     // chunks per y row
-    const int nchunks = a.sm * a.sn / W;
+    // Sub-tile extents are powers of two of at least W elements: chunk coordinates are shifts
+    // and masks (run-time divisions per chunk took the 4096 x 4096 transpose from 25.5 to 27.5 us).
+    const int lcx = a.log_sn - LOG_W;   // log2 of the chunks per staged x row
+    const int lcy = a.log_sm - LOG_W;   // log2 of the chunks per y row
+    const int nchunks = 1 << (a.log_sm + a.log_sn - LOG_W);
+    const int sm = 1 << a.log_sm, sn = 1 << a.log_sn;
 
     uint64_t w = blockIdx.x;
     do {
-        const uint64_t per_b = uint64_t(a.subs_m) * a.subs_n;
-        const uint64_t b = w / per_b;
-        const uint64_t rest = w - b * per_b;
         // Diagonal order: consecutive work items step one sub-tile down AND one across, so the
         // workgroups running together read x and write y at different column offsets (in row-major
-        // order they would all write y at one column offset, rows 64 * ldy apart, and crowd the
+        // order they would all write y at one column offset, rows SN * ldy apart, and crowd the
         // same HBM channels).  For each pm, q runs over every sub-tile column once.
-        const uint64_t pm = rest % a.subs_m;
-        const uint64_t q = rest / a.subs_m;
-        const uint64_t pn = (q + pm) % a.subs_n;
-        const int64_t row0 = int64_t(pm) * a.sm;   // x rows = y columns
-        const int64_t col0 = int64_t(pn) * a.sn;   // x columns = y rows
+        uint64_t b, pm, pn;
+        if constexpr (!WIDE) {  // the work count fits 32 bits: multiply-high divisions
+            const uint32_t w32 = static_cast<uint32_t>(w);
+            const uint32_t b32 = fast_div(w32, a.c_pb, a.per_b);
+            const uint32_t rest = w32 - b32 * a.per_b;
+            const uint32_t q = fast_div(rest, a.c_m, a.subs_m);
+            const uint32_t pm32 = rest - q * a.subs_m;
+            b = b32;
+            pm = pm32;
+            pn = fast_mod(q + pm32, a.c_n, a.subs_n);  // q + pm32 < subs_n + subs_m < 2^32
+        } else {
+            const uint64_t per_b = uint64_t(a.subs_m) * a.subs_n;
+            b = w / per_b;
+            const uint64_t rest = w - b * per_b;
+            pm = rest % a.subs_m;
+            pn = (rest / a.subs_m + pm) % a.subs_n;
+        }
+        const int64_t row0 = int64_t(pm) * sm;     // x rows = y columns
+        const int64_t col0 = int64_t(pn) * sn;     // x columns = y rows
         const float *xb = a.x + int64_t(b) * a.bsx;
         float *yb = a.y + int64_t(b) * a.bsy;
         const int64_t rows_live = a.M - row0, cols_live = a.N - col0;
@@ -71,7 +95,7 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int e = t + k * BS;
-            const int r = e / cpr_x, c = (e - r * cpr_x) * W;
+            const int r = e >> lcx, c = (e & ((1 << lcx) - 1)) << LOG_W;
             const float *p = xb + (row0 + r) * a.ldx + col0 + c;
             if (e < nchunks) {
                 if (ALIGNED || (r < rows_live && c + W <= cols_live)) {
@@ -91,7 +115,7 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int e = t + k * BS;
-            const int r = e / cpr_x, c = (e - r * cpr_x) * W;
+            const int r = e >> lcx, c = (e & ((1 << lcx) - 1)) << LOG_W;
             if (e < nchunks) {
 #pragma unroll
                 for (int i = 0; i < W; ++i)
@@ -105,7 +129,7 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int e = t + k * BS;
-            const int j = e / cpr_y, i = (e - j * cpr_y) * W;
+            const int j = e >> lcy, i = (e & ((1 << lcy) - 1)) << LOG_W;
             if (e < nchunks) {
 #pragma unroll
                 for (int q = 0; q < W; ++q)
@@ -115,7 +139,7 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int e = t + k * BS;
-            const int j = e / cpr_y, i = (e - j * cpr_y) * W;
+            const int j = e >> lcy, i = (e & ((1 << lcy) - 1)) << LOG_W;
             float *q = yb + (col0 + j) * a.ldy + row0 + i;
             if (e < nchunks) {
                 if (ALIGNED || (j < cols_live && i + W <= rows_live)) {
@@ -131,9 +155,20 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
                 }
             }
         }
-        __syncthreads();
         w += gridDim.x;
-    } while (w < a.nwork);
+        if (w >= a.nwork)
+            break;  // uniform; no barrier after the last sub-tile (it would hold the workgroup
+                    // until its stores complete)
+        __syncthreads();  // the next sub-tile reuses the LDS tile
+    } while (true);
+}
+
+template <bool WIDE>
+const void *pick(const tmp::TransposePlan &p) {
+    if (!p.vec)
+        return reinterpret_cast<const void *>(&transpose_tiles<false, false, kTrBlock, WIDE>);
+    return p.aligned ? reinterpret_cast<const void *>(&transpose_tiles<true, true, kTrBlock, WIDE>)
+                     : reinterpret_cast<const void *>(&transpose_tiles<true, false, kTrBlock, WIDE>);
 }
 
 }  // namespace
@@ -146,17 +181,18 @@ hipError_t launch_transpose(const tmp::TransposePlan &p, hipStream_t stream) {
     a.ldy = p.ldy;
     a.bsx = p.bsx;
     a.bsy = p.bsy;
-    a.B = p.B;
     a.M = p.M;
     a.N = p.N;
-    a.sm = p.sm;
-    a.sn = p.sn;
+    a.log_sm = tmp::ilog2(p.sm);
+    a.log_sn = tmp::ilog2(p.sn);
     a.subs_m = p.subs_m;
     a.subs_n = p.subs_n;
+    a.per_b = p.per_b.d;
+    a.c_pb = p.per_b.c;
+    a.c_m = p.by_m.c;
+    a.c_n = p.by_n.c;
     a.nwork = p.nwork;
-    const void *fn = p.vec ? (p.aligned ? reinterpret_cast<const void *>(&transpose_tiles<true, true, kTrBlock>)
-                                        : reinterpret_cast<const void *>(&transpose_tiles<true, false, kTrBlock>))
-                           : reinterpret_cast<const void *>(&transpose_tiles<false, false, kTrBlock>);
+    const void *fn = p.wide ? pick<true>(p) : pick<false>(p);
     void *args[] = {&a};
     return hipLaunchKernel(fn, dim3(p.grid), dim3(kTrBlock), args, 0, stream);
 }
