@@ -16,8 +16,8 @@
 // index, so a wave reads consecutive chunks of a row.  Work items run with the tile groups
 // fastest, then row strips, then tile rows, so workgroups dispatched together cover neighbouring
 // memory.  The host picks the geometry (plan.cpp): when rows start on 128-byte lines a work item
-// is one wave's worth of chunks (a strip of rows of one tile, widened across tiles only to whole
-// lines), otherwise it spans as many tiles as fit in 1024 threads across the row band, so that
+// is one wave's worth of chunks (a strip of rows of a tile group with 512-byte row segments),
+// otherwise it spans as many tiles as fit in 1024 threads across the row band, so that
 // few 128-byte lines are shared by workgroups that may run on different XCDs (each XCD has its
 // own L2 and would fetch a shared line again).  Whole chunks move with the non-temporal hint.  On
 // gfx950 one 16-byte chunk per thread streamed faster than several chunks per thread, and

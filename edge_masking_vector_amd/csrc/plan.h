@@ -20,6 +20,7 @@ constexpr int kMapMinBlock = 64;    // map workgroups: at least one wave ...
 constexpr int kMapMaxBlock = 1024;  // ... and at most 1024 threads
 constexpr int kScalarChunksPerThread = 4;  // 4-byte chunks per thread (16-byte chunks: one)
 constexpr int kLineBytes = 128;     // cache line
+constexpr int kRowSegmentBytes = 512;  // map work items: bytes of each row they move, at least
 constexpr int kTrSub = 32;          // transpose: largest staged sub-tile edge (one 128-byte line of f32)
 
 enum MapOp { kAffine = 0, kScale = 1, kCopy = 2, kChannel = 3 };
