@@ -14,12 +14,15 @@ import concurrent.futures
 import os
 import shutil
 import subprocess
+import sysconfig
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtilemap.so")
+# The CPython extension that binds the C ABI (csrc/pyext.c), next to the library it links.
+EXT = os.path.join(HERE, "_tilemap" + sysconfig.get_config_var("EXT_SUFFIX"))
 SOURCES = ["plan.cpp", "map.hip", "rowred.hip", "colred.hip", "transpose.hip", "api.hip"]
 
 ARCH = "gfx950"
@@ -67,7 +70,25 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
     os.replace(tmp, LIB)
+    build_ext()
     return LIB
+
+
+def build_ext() -> str:
+    """Compile csrc/pyext.c with the host C compiler into the `_tilemap` extension module, linked
+    against libtilemap.so and finding it through an $ORIGIN run path."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no host C compiler (gcc) to build the _tilemap extension")
+    tmp = EXT + ".tmp%d" % os.getpid()
+    cmd = [cc, "-std=c11", "-O2", "-fPIC", "-shared", "-Wall", "-Wextra", "-Werror",
+           "-I", os.path.join(ROOT, "include"), "-I", sysconfig.get_paths()["include"],
+           os.path.join(CSRC, "pyext.c"), "-L", HERE, "-ltilemap", "-Wl,-rpath,$ORIGIN", "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("building the _tilemap extension failed:\n" + r.stderr)
+    os.replace(tmp, EXT)
+    return EXT
 
 
 if __name__ == "__main__":

@@ -48,6 +48,32 @@ def test_exports_nothing_else():
     assert exported == _declared()
 
 
+def test_extension_binds_every_declared_call():
+    """The _tilemap extension has one function per C call, under the same name, and so does the
+    Python binding."""
+    for n in _declared():
+        assert hasattr(tm._ext, n), n
+        assert callable(getattr(tm, n)), n
+
+
+def test_extension_rejects_bad_arguments_before_calling():
+    f = tm._ext.tm_map_affine
+    good = [0, 16, 0, 16, 0, 16, 2.0, 1.0, 1, 1024, 0, 3, 0]   # M = 0: a no-op call
+    assert f(*good) == tm.TM_OK
+    with pytest.raises(TypeError):
+        f(*good[:-1])                          # argument count
+    with pytest.raises(TypeError):
+        f(*(good[:1] + ["16"] + good[2:]))     # a string where a size goes
+    with pytest.raises(OverflowError):
+        f(*([-1] + good[1:]))                  # a negative address
+    with pytest.raises(OverflowError):
+        f(*(good[:8] + [1 << 40] + good[9:]))  # an int argument past C int
+    with pytest.raises(TypeError):
+        f(*(good[:6] + [None] + good[7:]))     # alpha must be a number
+    assert tm._ext.tm_split(1000, 16) == (tm.TM_OK, 62, 8)
+    assert tm._ext.tm_status_string(-2) == "TM_E_ALIGN"
+
+
 def test_status_strings():
     for code, name in [(0, "TM_OK"), (-1, "TM_E_INVAL"), (-2, "TM_E_ALIGN"),
                        (-3, "TM_E_UNSUPPORTED"), (-4, "TM_E_WORKSPACE"), (-5, "TM_E_HIP")]:
@@ -294,15 +320,24 @@ def test_pad_extents_keep_the_promise():
 
 @no_gpu
 def test_autotune_errors():
-    f = tm._lib.tm_autotune_map
-    import ctypes
-    i1, i2, u = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_float(0)
     E = 0x7F0000300000
     args = lambda op=1, x=A16, y=B16, reps=3, e0=E, e1=E: (op, x, 64, y, 64, 64, 64, 1.5, 0.0, 1, 0, reps,
-                                                             e0, e1, ctypes.byref(i1), ctypes.byref(i2),
-                                                             ctypes.byref(u), None, S)
-    assert f(*args(op=7)) == tm.TM_E_INVAL
-    assert f(*args(reps=0)) == tm.TM_E_INVAL
-    assert f(*args(e0=0)) == tm.TM_E_INVAL
-    assert f(*args(y=A16)) == tm.TM_E_INVAL          # in place
-    assert f(*args(x=A16 + 2)) == tm.TM_E_INVAL      # malformed shared argument
+                                                             e0, e1, S)
+    assert tm.tm_autotune_map(*args(op=7), table=False)[0] == tm.TM_E_INVAL
+    assert tm.tm_autotune_map(*args(reps=0), table=False)[0] == tm.TM_E_INVAL
+    assert tm.tm_autotune_map(*args(e0=0))[0] == tm.TM_E_INVAL
+    assert tm.tm_autotune_map(*args(y=A16))[0] == tm.TM_E_INVAL          # in place
+    assert tm.tm_autotune_map(*args(x=A16 + 2))[0] == tm.TM_E_INVAL      # malformed shared argument
+    # NULL result pointers, through the C ABI itself
+    lib = ctypes.CDLL(tm.library_path())
+    f = lib.tm_autotune_map
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_float, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    i1, i2, u = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_float(0)
+    base = (1, A16, 64, B16, 64, 64, 64, 1.5, 0.0, 1, 0, 3, E, E)
+    assert f(*base, None, ctypes.byref(i2), ctypes.byref(u), None, S) == tm.TM_E_INVAL
+    assert f(*base, ctypes.byref(i1), None, ctypes.byref(u), None, S) == tm.TM_E_INVAL
+    assert f(*base, ctypes.byref(i1), ctypes.byref(i2), None, None, S) == tm.TM_E_INVAL
