@@ -84,6 +84,35 @@ def test_rowsum_4096(dev):
         assert O.guards_intact()
 
 
+def test_sums_long_rows_and_tall_columns(dev):
+    """Rows of a million elements (each lane then folds hundreds of batches serially) and columns
+    of a million rows (thousands of slab partials in the second pass), ragged in both directions,
+    still within 1e-5 of the fp64 sums."""
+    M, N = 3, (1 << 20) + 13
+    xh = inputs.uniform(91, M * N, 0.0, 1.0)
+    X, host = device_matrix(xh, M, N, N, dev)
+    ref = oracle.rowsum_f64(host, N, M, N)
+    for TM, TN in ((4, 256), (1, 1024), (2, 64)):
+        note("rowsum long rows %dx%d tile=%dx%d" % (M, N, TM, TN))
+        st, O = gpu_rowsum(X, N, M, N, TM, TN, 0, dev)
+        assert st == tm.TM_OK
+        torch.cuda.synchronize()
+        assert_sums(O.payload().cpu().numpy(), ref, ref)
+        assert O.guards_intact()
+    M, N = (1 << 20) + 7, 37
+    xh = inputs.uniform(92, M * N, -1.0, 1.0)
+    X, host = device_matrix(xh, M, N, N, dev)
+    ref = oracle.colsum_f64(host, N, M, N)
+    absref = oracle.colsum_f64(np.abs(host), N, M, N)
+    for walk, TM, TN in ((tm.TM_COL_LDS, 256, 64), (tm.TM_COL_LDS, 16, 4), (tm.TM_COL_NAIVE, 256, 1)):
+        note("colsum tall columns %dx%d walk=%d tile=%dx%d" % (M, N, walk, TM, TN))
+        st, O, W = gpu_colsum(X, N, M, N, TM, TN, 0, walk, dev)
+        assert st == tm.TM_OK
+        torch.cuda.synchronize()
+        assert_sums(O.payload().cpu().numpy(), ref, absref)
+        assert O.guards_intact() and W.guards_intact()
+
+
 @pytest.mark.parametrize("walk", [tm.TM_COL_NAIVE, tm.TM_COL_LDS])
 def test_colsum_4096(dev, walk):
     M = N = 4096
@@ -328,6 +357,20 @@ def test_softmax_stats_wide_range_and_misaligned(dev):
         assert st == tm.TM_OK
         torch.cuda.synchronize()
         check_softmax(Mo, Lo, host, ld, M, N)
+
+
+def test_softmax_stats_long_rows(dev):
+    """Rows of a million scores (ragged: 2^20 + 13 columns), where each lane rescales and adds
+    hundreds of batch sums into its running l: still within 1e-5 of the fp64 normaliser."""
+    M, N = 3, (1 << 20) + 13
+    sh = inputs.uniform(93, M * N, -10.0, -1.0)
+    S, host = device_matrix(sh, M, N, N, dev)
+    for BC in (64, 1024, 4):
+        note("softmax long rows %dx%d BC=%d" % (M, N, BC))
+        st, Mo, Lo = gpu_softmax(S, N, M, N, 4, BC, 0, dev)
+        assert st == tm.TM_OK
+        torch.cuda.synchronize()
+        check_softmax(Mo, Lo, host, N, M, N)
 
 
 def test_softmax_stats_empty_rows(dev):
