@@ -117,7 +117,7 @@ def main():
     import torch
 
     from edge_masking_vector_amd import _build, inputs
-    if not os.path.exists(_build.LIB):
+    if not (os.path.exists(_build.LIB) and os.path.exists(_build.EXT)):
         _build.build()
     from edge_masking_vector_amd import tilemap as tm
 
