@@ -1,0 +1,269 @@
+// plan_check.cpp -- host checks of libtilemap's planner (edge_masking_vector_amd/csrc/plan.cpp),
+// built with g++ under AddressSanitizer and UndefinedBehaviorSanitizer by
+// tests/test_sanitizers_cpu.py.  No GPU is involved.
+//
+// For every accepted call over a grid of shapes, strides, base offsets, tiles and paths, the
+// device-side index mapping that the kernels apply to a plan is replayed here, and the test
+// requires that it covers the tensor exactly:
+//  * maps: every element (i, j) of the M x N view is moved by exactly one (work item, thread,
+//    chunk), and on the aligned path (no masks) every chunk lies wholly inside the view;
+//  * transpose: every staged sub-tile of every batch is visited by exactly one work item, with the
+//    work-item number split by the plan's multiply-high divisors (checked against plain division).
+// Row and column reduction plans are checked for their documented invariants.
+//
+// The replay restates the mapping the kernels document (map.hip: work item -> tile row pm, row
+// strip, tile group gi, tile groups fastest; chunk q -> row q >> log_gv, tile (q & gv_mask) >>
+// log_vr, chunk q & vr_mask.  transpose.hip: work item -> batch, then diagonal order pm = rest %
+// subs_m, pn = (rest / subs_m + pm) % subs_n).  Exit status 0 when every check passes.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "../../edge_masking_vector_amd/csrc/plan.h"
+
+static long g_checked = 0, g_failed = 0;
+
+#define CHECK(cond, ...)                                   \
+    do {                                                   \
+        if (!(cond)) {                                     \
+            if (g_failed++ < 20) {                         \
+                std::fprintf(stderr, "FAIL %s: ", #cond);  \
+                std::fprintf(stderr, __VA_ARGS__);         \
+                std::fprintf(stderr, "\n");                \
+            }                                              \
+        }                                                  \
+    } while (0)
+
+static const float *fake(uintptr_t addr) { return reinterpret_cast<const float *>(addr); }
+
+static uint32_t umulhi_div(uint32_t a, const tmp::Div32 &d) {
+    if (d.d == 1)
+        return a;
+    return static_cast<uint32_t>((static_cast<unsigned __int128>(d.c) * a) >> 64);
+}
+static uint32_t umulhi_mod(uint32_t a, const tmp::Div32 &d) {
+    if (d.d == 1)
+        return 0;
+    const uint64_t low = d.c * a;
+    return static_cast<uint32_t>((static_cast<unsigned __int128>(low) * d.d) >> 64);
+}
+
+// ---- maps --------------------------------------------------------------------------------------
+static void replay_map(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, uintptr_t xbase,
+                       const char *tag) {
+    const int W = p.access == tmp::kScalar ? 1 : 4;
+    const int U = p.access == tmp::kScalar ? tmp::kScalarChunksPerThread : 1;
+    const uint32_t bs = 1u << p.log_bs;
+    const uint32_t chunks = 1u << (p.log_r + p.log_gv);
+    const uint32_t vr_mask = (1u << p.log_vr) - 1u, gv_mask = (1u << p.log_gv) - 1u;
+    const uint32_t strip_mask = (1u << p.log_strips) - 1u;
+    const int64_t tm = int64_t(1) << p.log_tm, tn = int64_t(1) << p.log_tn;
+    CHECK(p.grid >= 1 && p.grid <= p.nwork, "%s grid %u nwork %u", tag, p.grid, p.nwork);
+    CHECK(bs >= 64 && bs <= 1024, "%s block %u", tag, bs);
+    CHECK(uint64_t(bs) * U >= chunks, "%s block %u x %d < chunks %u", tag, bs, U, chunks);
+    CHECK(p.guard == (uint64_t(bs) * U > chunks), "%s guard flag", tag);
+    CHECK(tn * p.group * p.groups_n >= N, "%s tile groups do not reach column N", tag);
+    if (p.aligned) {
+        CHECK(xbase % 16 == 0 && (M <= 1 || ld % 4 == 0) || W == 1, "%s 16-byte chunks off", tag);
+    }
+    std::vector<uint8_t> hits(size_t(M * N), 0);
+    for (uint32_t w = 0; w < p.nwork; ++w) {
+        const uint32_t gi = w % p.groups_n, ps = w / p.groups_n;
+        const uint32_t strip = ps & strip_mask, pm = ps >> p.log_strips;
+        const int64_t row0 = (int64_t(pm) << p.log_tm) + (int64_t(strip) << p.log_r);
+        const int64_t col0 = int64_t(gi) * p.group * tn;
+        const bool item_whole = p.aligned || ((int64_t(pm) + 1) * tm <= M && col0 + int64_t(p.group) * tn <= N);
+        for (uint32_t t = 0; t < bs; ++t) {
+            for (int u = 0; u < U; ++u) {
+                const uint32_t q = t + (uint32_t(u) << p.log_bs);
+                if (q >= chunks)
+                    continue;  // guarded lanes (or beyond the item) do nothing
+                const uint32_t pn = gi * p.group + ((q & gv_mask) >> p.log_vr);
+                const int64_t tile_col = col0 + int64_t((q & gv_mask) >> p.log_vr) * tn;
+                const int64_t col = tile_col + int64_t(q & vr_mask) * W;
+                const int64_t row = row0 + int64_t(q >> p.log_gv);
+                if (item_whole) {
+                    // unmasked body: the whole chunk moves
+                    CHECK(row < M && col + W <= N, "%s unmasked chunk outside (%ld, %ld)", tag,
+                          (long)row, (long)col);
+                    for (int e = 0; e < W; ++e)
+                        if (row < M && col + e < N)
+                            ++hits[size_t(row * N + col + e)];
+                } else {
+                    if (!(pn < p.tiles_n && row < M && N - col > 0))
+                        continue;  // masked: nothing read or stored
+                    for (int e = 0; e < W && col + e < N; ++e)
+                        ++hits[size_t(row * N + col + e)];
+                }
+            }
+        }
+    }
+    for (size_t k = 0; k < hits.size(); ++k) {
+        if (hits[k] != 1) {
+            CHECK(hits[k] == 1, "%s element (%ld, %ld) moved %d times", tag, long(k / N), long(k % N),
+                  int(hits[k]));
+            break;
+        }
+    }
+    ++g_checked;
+}
+
+static void check_maps() {
+    const int64_t Ms[] = {0, 1, 3, 17, 64, 100};
+    const int64_t Ns[] = {0, 1, 4, 17, 64, 129, 1000};
+    const int TMs[] = {1, 4, 32, 256};
+    const int TNs[] = {1, 4, 16, 128, 1024};
+    const uintptr_t bases[] = {0x100000, 0x100004, 0x100010};  // line-aligned, 4-byte, 16-byte
+    for (int64_t M : Ms)
+        for (int64_t N : Ns) {
+            const int64_t lds[] = {N, N + 3, (N + 3) / 4 * 4, (N + 31) / 32 * 32};
+            for (int64_t ld : lds)
+                for (int TM : TMs)
+                    for (int TN : TNs)
+                        for (int aligned = 0; aligned <= 1; ++aligned)
+                            for (int variant = 1; variant <= 3; ++variant)
+                                for (uintptr_t base : bases)
+                                    for (int op : {int(tmp::kScale), int(tmp::kChannel)}) {
+                                        tmp::MapPlan p;
+                                        const uintptr_t ybase = base + 0x40000000;
+                                        const int st = tmp::plan_map(
+                                            op, fake(base), ld, const_cast<float *>(fake(ybase)), ld,
+                                            M, N, 1.5f, 0.f, TM, TN, aligned, variant, &p, nullptr,
+                                            fake(0x200000));
+                                        if (st != TM_OK || !p.launch)
+                                            continue;
+                                        char tag[160];
+                                        std::snprintf(tag, sizeof tag,
+                                                      "map M=%ld N=%ld ld=%ld TM=%d TN=%d al=%d var=%d base=%#lx op=%d",
+                                                      long(M), long(N), long(ld), TM, TN, aligned, variant,
+                                                      (unsigned long)base, op);
+                                        replay_map(p, M, N, ld, base, tag);
+                                    }
+        }
+}
+
+// ---- transpose --------------------------------------------------------------------------------
+static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, int64_t N, const char *tag) {
+    CHECK(!p.wide, "%s small job planned as wide", tag);
+    CHECK(p.subs_m == uint32_t((M + p.sm - 1) / p.sm) && p.subs_n == uint32_t((N + p.sn - 1) / p.sn),
+          "%s sub-tile counts", tag);
+    CHECK(p.nwork == uint64_t(B) * p.subs_m * p.subs_n && p.grid >= 1 && p.grid <= p.nwork, "%s work", tag);
+    CHECK(p.sm <= tmp::kTrSub && p.sn <= tmp::kTrSub, "%s sub-tile above %d", tag, tmp::kTrSub);
+    if (p.aligned)
+        CHECK(M % p.sm == 0 && N % p.sn == 0, "%s promised sub-tiles are not whole", tag);
+    if (p.vec)
+        CHECK(p.sm >= 4 && p.sn >= 4, "%s 16-byte chunks need sub-tiles of 4+", tag);
+    std::vector<uint8_t> seen(size_t(p.nwork), 0);
+    for (uint64_t w = 0; w < p.nwork; ++w) {
+        const uint32_t w32 = uint32_t(w);
+        const uint32_t b = umulhi_div(w32, p.per_b);
+        const uint32_t rest = w32 - b * p.per_b.d;
+        const uint32_t q = umulhi_div(rest, p.by_m);
+        const uint32_t pm = rest - q * p.by_m.d;
+        const uint32_t pn = umulhi_mod(q + pm, p.by_n);
+        // the same split with plain division
+        const uint32_t per_b = p.subs_m * p.subs_n;
+        CHECK(b == w32 / per_b && rest == w32 % per_b && pm == rest % p.subs_m &&
+                  pn == (rest / p.subs_m + rest % p.subs_m) % p.subs_n,
+              "%s multiply-high split of work item %u", tag, w32);
+        CHECK(b < B && pm < p.subs_m && pn < p.subs_n, "%s work item %u out of range", tag, w32);
+        const uint64_t slot = (uint64_t(b) * p.subs_m + pm) * p.subs_n + pn;
+        if (slot < seen.size())
+            ++seen[size_t(slot)];
+    }
+    for (size_t k = 0; k < seen.size(); ++k) {
+        if (seen[k] != 1) {
+            CHECK(seen[k] == 1, "%s sub-tile %zu visited %d times", tag, k, int(seen[k]));
+            break;
+        }
+    }
+    ++g_checked;
+}
+
+static void check_transposes() {
+    const int64_t Bs[] = {1, 3, 32};
+    const int64_t Ms[] = {1, 4, 24, 64, 100};
+    const int64_t Ns[] = {1, 5, 32, 100, 3136};
+    for (int64_t B : Bs)
+        for (int64_t M : Ms)
+            for (int64_t N : Ns)
+                for (int T : {4, 32, 64})
+                    for (int aligned = 0; aligned <= 1; ++aligned) {
+                        tmp::TransposePlan p;
+                        const int64_t ldx = (N + 3) / 4 * 4, ldy = (M + 3) / 4 * 4;
+                        const int st = tmp::plan_transpose(fake(0x100000), ldx, M * ldx,
+                                                           const_cast<float *>(fake(0x40000000)), ldy,
+                                                           N * ldy, B, M, N, T, T, aligned, &p);
+                        if (st != TM_OK || !p.launch)
+                            continue;
+                        char tag[128];
+                        std::snprintf(tag, sizeof tag, "transpose B=%ld M=%ld N=%ld T=%d al=%d", long(B),
+                                      long(M), long(N), T, aligned);
+                        replay_transpose(p, B, M, N, tag);
+                    }
+    // divisors of every size up to 5000, against plain division
+    for (uint32_t d = 1; d <= 5000; ++d) {
+        const tmp::Div32 v = tmp::make_div32(d);
+        for (uint32_t a : {0u, 1u, d - 1, d, 2 * d + 1, 65535u, 0x7fffffffu, 0xffffffffu}) {
+            CHECK(umulhi_div(a, v) == a / d && umulhi_mod(a, v) == a % d, "div32 a=%u d=%u", a, d);
+        }
+    }
+    ++g_checked;
+}
+
+// ---- row and column reductions ----------------------------------------------------------------
+static void check_reductions() {
+    const int64_t Ms[] = {0, 1, 7, 300};
+    const int64_t Ns[] = {0, 1, 5, 64, 1000, 4096};
+    for (int64_t M : Ms)
+        for (int64_t N : Ns)
+            for (int TR : {1, 4, 16, 256})
+                for (int TC : {1, 4, 64, 256, 1024})
+                    for (int aligned = 0; aligned <= 1; ++aligned) {
+                        const int64_t ld = (N + 3) / 4 * 4;
+                        for (int op : {int(tmp::kRowSum), int(tmp::kRowMax), int(tmp::kRowSoftmax)}) {
+                            tmp::RowPlan p;
+                            float *o = const_cast<float *>(fake(0x200000));
+                            const int st = tmp::plan_rows(op, fake(0x100000), ld, o, M, N, TR, TC, aligned, &p,
+                                                          op == tmp::kRowSoftmax ? o + 4096 : nullptr);
+                            if (st != TM_OK || !p.launch)
+                                continue;
+                            CHECK(p.lpr >= 1 && p.lpr <= 64 && (p.lpr & (p.lpr - 1)) == 0, "rows lpr %d", p.lpr);
+                            CHECK(p.nfull * p.bc + p.rem == N && p.rem >= 0 && p.rem < p.bc,
+                                  "rows split N=%ld bc=%d nfull=%ld rem=%ld", long(N), p.bc, long(p.nfull),
+                                  long(p.rem));
+                            CHECK(p.grid >= 1, "rows grid");
+                            ++g_checked;
+                        }
+                        for (int walk : {TM_COL_NAIVE, TM_COL_LDS}) {
+                            tmp::ColPlan c;
+                            const size_t wsb = tmp::colsum_ws_bytes(M, N, TR, TC, walk);
+                            const int st = tmp::plan_cols(fake(0x100000), ld, const_cast<float *>(fake(0x200000)),
+                                                          M, N, TR, TC, aligned, walk,
+                                                          const_cast<float *>(fake(0x300000)), wsb, &c);
+                            if (st != TM_OK)
+                                continue;
+                            if (c.launch) {
+                                CHECK(c.slabs == uint32_t((M + TR - 1) / TR), "cols slabs");
+                                CHECK(uint64_t(c.slabs) * uint64_t(N) * 4 <= wsb, "cols workspace too small");
+                            }
+                            if (wsb >= 4) {  // one float less is refused
+                                const int st2 = tmp::plan_cols(fake(0x100000), ld,
+                                                               const_cast<float *>(fake(0x200000)), M, N, TR, TC,
+                                                               aligned, walk, const_cast<float *>(fake(0x300000)),
+                                                               wsb - 4, &c);
+                                CHECK(st2 == TM_E_WORKSPACE, "cols short workspace accepted (st %d)", st2);
+                            }
+                            ++g_checked;
+                        }
+                    }
+}
+
+int main() {
+    check_maps();
+    check_transposes();
+    check_reductions();
+    std::printf("plan_check: %ld plans checked, %ld failures\n", g_checked, g_failed);
+    return g_failed == 0 ? 0 : 1;
+}
