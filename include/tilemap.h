@@ -94,7 +94,9 @@ typedef enum {
 
 /* ---- element-wise maps over tiles --------------------------------------------------------------
  * x: input, M x N, row stride ldx.  y: output, M x N, row stride ldy.  TM, TN: tile.  aligned: 0|1.
- * variant: tm_variant. */
+ * variant: tm_variant.  The tile is what the alignment promise is made for and, on the ragged
+ * path, what decides which chunks take the masked code; how the work is cut into workgroups is
+ * the library's choice and never changes a result. */
 
 /* y[i,j] = fmaf(x[i,j], alpha, beta): one correctly rounded multiply-add per element
  * ([P35] "The exercise": out = a*2 + 1; generalised to alpha, beta). */
@@ -175,7 +177,7 @@ int tm_softmax_stats(const float *s, int64_t lds, float *m, float *l, int64_t M,
  * With x = [B][C][H*W], M = C, N = H*W, ldx = H*W, bsx = C*H*W, ldy = C, bsy = H*W*C this converts
  * NCHW to NHWC; the same call with M and N swapped converts back ([LAYOUT] "NCHW versus NHWC": a
  * conversion costs one full pass over memory; "Strides, and reading an index expression").
- * x is staged through LDS in sub-tiles of up to 64 x 64 so that both the reads of x and the
+ * x is staged through LDS in sub-tiles of up to 32 x 32 so that both the reads of x and the
  * writes of y are coalesced rows ([LAYOUT] "Seeing it in a real kernel"); TM x TN is the tile the
  * alignment promise is made for (under the promise the sub-tiles are whole).  Ragged edges:
  * elements past the tensor read as 0 and are never stored.  aligned = 1 promises
