@@ -35,6 +35,7 @@ struct RowArgs {
 
 constexpr int kLoads = 8;   // chunks in flight per lane
 constexpr int kAcc = 4;     // independent accumulators per lane
+constexpr int kRemPrefetch = 4;  // remainder-tile chunks per lane loaded ahead of the whole tiles
 
 template <class Op>
 __device__ __forceinline__ float combine(float a, float b) { return Op::f(a, b); }
@@ -81,7 +82,9 @@ __device__ __forceinline__ auto load_fill(const float *p, int64_t live) {
     }
 }
 
-template <class Op, int LPR, bool VEC>
+// PRE: the call has a remainder tile of at most kRemPrefetch chunks per lane, loaded ahead of the
+// whole tiles (chosen on the host; without a remainder the plain walk is 2% faster).
+template <class Op, int LPR, bool VEC, bool PRE>
 __global__ __launch_bounds__(kBlock) void row_reduce(RowArgs a) {
     using T = typename std::conditional<VEC, f4, float>::type;
     constexpr int W = VEC ? 4 : 1;
@@ -100,6 +103,19 @@ __global__ __launch_bounds__(kBlock) void row_reduce(RowArgs a) {
 #pragma unroll
         for (int i = 0; i < kAcc; ++i)
             acc[i] = T(Op::kFill);
+
+        // The remainder tile (columns kt .. N-1) is loaded first, so that its latency overlaps the
+        // whole tiles instead of adding one more round trip after them (8.1 -> 7.6 us on the
+        // 8192 x 1000 masked row max); it is still combined last.
+        const int64_t kt = a.nfull * a.bc;
+        T rv[PRE ? kRemPrefetch : 1];
+        if constexpr (PRE) {
+#pragma unroll
+            for (int f = 0; f < kRemPrefetch; ++f) {
+                const int64_t c = int64_t(f) * kStep + g * W;  // tile-local column of the chunk
+                rv[f] = f < a.per_tile ? load_fill<Op, VEC>(xr + kt + c, a.N - kt - c) : T(Op::kFill);
+            }
+        }
 
         // Whole tiles: chunk k of this lane sits at column (k * LPR + g) * W; no masks.  Each
         // workgroup starts at a different whole tile (7 * group mod nfull) and wraps around: when the
@@ -123,8 +139,12 @@ __global__ __launch_bounds__(kBlock) void row_reduce(RowArgs a) {
 
         // The one remainder tile, starting at column kt: tile-local column c keeps its value iff
         // c < N - kt.
-        if (a.rem > 0) {
-            const int64_t kt = a.nfull * a.bc;
+        if constexpr (PRE) {
+#pragma unroll
+            for (int f = 0; f < kRemPrefetch; ++f)
+                if (f < a.per_tile)
+                    acc[0] = combine<Op>(acc[0], rv[f]);
+        } else if (a.rem > 0) {
             for (int f = 0; f < a.per_tile; ++f) {
                 const int64_t c = int64_t(f) * kStep + g * W;  // tile-local column of the chunk
                 acc[0] = combine<Op>(acc[0], load_fill<Op, VEC>(xr + kt + c, a.N - kt - c));
@@ -171,7 +191,7 @@ __device__ __forceinline__ float sum_exp_live(f4 v, float b, int64_t live) {
     return acc;
 }
 
-template <int LPR, bool VEC>
+template <int LPR, bool VEC, bool PRE>
 __global__ __launch_bounds__(kBlock) void row_softmax(RowArgs a) {
     using T = typename std::conditional<VEC, f4, float>::type;
     constexpr int W = VEC ? 4 : 1;
@@ -186,6 +206,18 @@ __global__ __launch_bounds__(kBlock) void row_softmax(RowArgs a) {
         const float *xr = a.x + rr * a.ld;
         const float *p = xr + g * W;
         float m = kMaxFill, l = 0.0f;
+
+        // The remainder tile's chunks are loaded ahead of the whole tiles (as in row_reduce) and
+        // folded in after them.
+        const int64_t kt = a.nfull * a.bc;
+        T rv[PRE ? kRemPrefetch : 1];
+        if constexpr (PRE) {
+#pragma unroll
+            for (int f = 0; f < kRemPrefetch; ++f) {
+                const int64_t c = int64_t(f) * kStep + g * W;
+                rv[f] = f < a.per_tile ? load_fill<MaxOp, VEC>(xr + kt + c, a.N - kt - c) : T(kMaxFill);
+            }
+        }
 
         // Whole tiles, in the rotated order of row_reduce; no masks.
         const int64_t main_chunks = a.nfull * a.per_tile;
@@ -213,8 +245,17 @@ __global__ __launch_bounds__(kBlock) void row_softmax(RowArgs a) {
         }
 
         // The one remainder tile: only its first N - kt columns exist.
-        if (a.rem > 0) {
-            const int64_t kt = a.nfull * a.bc;
+        if constexpr (PRE) {
+#pragma unroll
+            for (int f = 0; f < kRemPrefetch; ++f) {
+                const int64_t live = a.N - kt - (int64_t(f) * kStep + g * W);
+                if (f < a.per_tile && live > 0) {
+                    const float b = __builtin_fmaxf(m, chunk_max(rv[f]));
+                    l = l * exp_f32(m - b) + sum_exp_live(rv[f], b, live);
+                    m = b;
+                }
+            }
+        } else if (a.rem > 0) {
             for (int f = 0; f < a.per_tile; ++f) {
                 const int64_t c = int64_t(f) * kStep + g * W;
                 const int64_t live = a.N - kt - c;
@@ -236,40 +277,48 @@ __global__ __launch_bounds__(kBlock) void row_softmax(RowArgs a) {
     }
 }
 
-template <int LPR>
+template <int LPR, bool PRE>
 const void *pick_softmax_vec(bool vec) {
-    return vec ? reinterpret_cast<const void *>(&row_softmax<LPR, true>)
-               : reinterpret_cast<const void *>(&row_softmax<LPR, false>);
+    return vec ? reinterpret_cast<const void *>(&row_softmax<LPR, true, PRE>)
+               : reinterpret_cast<const void *>(&row_softmax<LPR, false, PRE>);
 }
 
+template <bool PRE>
 const void *pick_softmax(const tmp::RowPlan &p) {
     switch (p.lpr) {
-    case 1: return pick_softmax_vec<1>(p.vec);
-    case 2: return pick_softmax_vec<2>(p.vec);
-    case 4: return pick_softmax_vec<4>(p.vec);
-    case 8: return pick_softmax_vec<8>(p.vec);
-    case 16: return pick_softmax_vec<16>(p.vec);
-    case 32: return pick_softmax_vec<32>(p.vec);
-    default: return pick_softmax_vec<64>(p.vec);
+    case 1: return pick_softmax_vec<1, PRE>(p.vec);
+    case 2: return pick_softmax_vec<2, PRE>(p.vec);
+    case 4: return pick_softmax_vec<4, PRE>(p.vec);
+    case 8: return pick_softmax_vec<8, PRE>(p.vec);
+    case 16: return pick_softmax_vec<16, PRE>(p.vec);
+    case 32: return pick_softmax_vec<32, PRE>(p.vec);
+    default: return pick_softmax_vec<64, PRE>(p.vec);
     }
 }
 
-template <class Op, bool VEC>
+template <class Op, bool VEC, bool PRE>
 const void *pick_lpr(int lpr) {
     switch (lpr) {
-    case 1: return reinterpret_cast<const void *>(&row_reduce<Op, 1, VEC>);
-    case 2: return reinterpret_cast<const void *>(&row_reduce<Op, 2, VEC>);
-    case 4: return reinterpret_cast<const void *>(&row_reduce<Op, 4, VEC>);
-    case 8: return reinterpret_cast<const void *>(&row_reduce<Op, 8, VEC>);
-    case 16: return reinterpret_cast<const void *>(&row_reduce<Op, 16, VEC>);
-    case 32: return reinterpret_cast<const void *>(&row_reduce<Op, 32, VEC>);
-    default: return reinterpret_cast<const void *>(&row_reduce<Op, 64, VEC>);
+    case 1: return reinterpret_cast<const void *>(&row_reduce<Op, 1, VEC, PRE>);
+    case 2: return reinterpret_cast<const void *>(&row_reduce<Op, 2, VEC, PRE>);
+    case 4: return reinterpret_cast<const void *>(&row_reduce<Op, 4, VEC, PRE>);
+    case 8: return reinterpret_cast<const void *>(&row_reduce<Op, 8, VEC, PRE>);
+    case 16: return reinterpret_cast<const void *>(&row_reduce<Op, 16, VEC, PRE>);
+    case 32: return reinterpret_cast<const void *>(&row_reduce<Op, 32, VEC, PRE>);
+    default: return reinterpret_cast<const void *>(&row_reduce<Op, 64, VEC, PRE>);
     }
 }
 
-template <class Op>
+template <class Op, bool PRE>
 const void *pick_vec(const tmp::RowPlan &p) {
-    return p.vec ? pick_lpr<Op, true>(p.lpr) : pick_lpr<Op, false>(p.lpr);
+    return p.vec ? pick_lpr<Op, true, PRE>(p.lpr) : pick_lpr<Op, false, PRE>(p.lpr);
+}
+
+template <bool PRE>
+const void *pick_op(const tmp::RowPlan &p) {
+    return p.op == tmp::kRowMax       ? pick_vec<MaxOp, PRE>(p)
+           : p.op == tmp::kRowSoftmax ? pick_softmax<PRE>(p)
+                                      : pick_vec<SumOp, PRE>(p);
 }
 
 }  // namespace
@@ -288,9 +337,8 @@ hipError_t launch_rows(const tmp::RowPlan &p, hipStream_t stream) {
     a.per_tile = p.per_tile;
     const int64_t rows_per_wg = kBlock / p.lpr;
     a.ngroups = static_cast<uint32_t>((p.M + rows_per_wg - 1) / rows_per_wg);
-    const void *fn = p.op == tmp::kRowMax       ? pick_vec<MaxOp>(p)
-                     : p.op == tmp::kRowSoftmax ? pick_softmax(p)
-                                                : pick_vec<SumOp>(p);
+    const bool pre = p.rem > 0 && p.per_tile <= kRemPrefetch;
+    const void *fn = pre ? pick_op<true>(p) : pick_op<false>(p);
     void *args[] = {&a};
     return hipLaunchKernel(fn, dim3(p.grid), dim3(kBlock), args, 0, stream);
 }
