@@ -69,7 +69,8 @@ __global__ __launch_bounds__(kBlock) void col_naive(ColArgs a) {
 
 // ---- LDS-staged walk -------------------------------------------------------------------------
 
-constexpr int kRowsInFlight = 8;  // rows each thread loads before adding
+constexpr int kRowsInFlight = 16;  // rows each thread loads before adding
+constexpr int kColAcc = 8;         // independent column accumulators per thread
 
 template <bool VEC>
 __device__ __forceinline__ auto chunk_or_zero(const float *p, int64_t live) {
@@ -113,9 +114,9 @@ __global__ __launch_bounds__(kBlock) void col_lds(ColArgs a) {
         const float *p = a.x + row0 * a.ld + c;
         const int64_t rows = ALIGNED ? tm : (a.M - row0 < tm ? a.M - row0 : tm);
 
-        T acc[kRowsInFlight];
+        T acc[kColAcc];
 #pragma unroll
-        for (int u = 0; u < kRowsInFlight; ++u)
+        for (int u = 0; u < kColAcc; ++u)
             acc[u] = T(0.0f);
         for (int64_t r = q; r < rows; r += int64_t(RP) * kRowsInFlight) {
             T v[kRowsInFlight];
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kBlock) void col_lds(ColArgs a) {
             }
 #pragma unroll
             for (int u = 0; u < kRowsInFlight; ++u)
-                acc[u] += v[u];
+                acc[u % kColAcc] += v[u];
         }
         // Fixed-order fold of the row accumulators.
         T s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
