@@ -71,6 +71,14 @@ def test_nchw_nhwc_round_trip(dev):
     assert torch.equal(y.view(B, HW, C), x.view(B, C, HW).transpose(1, 2).contiguous())
 
 
+def test_nchw_to_nhwc_full_workload(dev):
+    """The bench's conversion at its size: (32, 64, 56, 56) NCHW -> NHWC with 64 x 64 tiles,
+    aligned, bit for bit against the oracle."""
+    B, C, HW = 32, 64, 56 * 56
+    note("nchw->nhwc full %dx%dx%d" % (B, C, HW))
+    check_transpose(dev, B, C, HW, HW, C, C * HW, HW * C, 64, 64, 1, seed=6)
+
+
 def test_nchw_nhwc_ragged_channels(dev):
     """Channel counts and spatial sizes that are not multiples of the tile (or of 4)."""
     for (B, C, HW) in ((3, 3, 50), (2, 17, 1001), (4, 130, 49)):

@@ -391,6 +391,35 @@ def test_channel_affine_brute_force_tiny(dev):
 
 # ---- tile-size sweep / autotune ------------------------------------------------------------------
 
+def test_every_sweep_tile_at_8192(dev):
+    """The tile sweep's workload at full size: Y = 1.5 X on 8192 x 8192 (aligned) with every menu
+    tile that keeps the promise, and the 8192 x 8192 copy of the ceiling probe -- each output equal
+    bit for bit to the oracle's, compared on the device against the oracle's result uploaded once."""
+    M = N = 8192
+    xh = inputs.scale_input(M, N, seed=9)
+    want = np.empty_like(xh)
+    oracle.scale2d(xh, N, want, N, M, N, 1.5)
+    x = torch.from_numpy(xh).to(dev)
+    ref = torch.from_numpy(want).to(dev)
+    y = torch.empty_like(x)
+    ran = 0
+    for i in range(9):
+        for j in range(11):
+            TM, TN = 1 << i, 1 << j
+            if not oracle.promise_holds(M, N, N, N, TM, TN, x.data_ptr(), y.data_ptr()):
+                continue
+            note("sweep tile %dx%d" % (TM, TN))
+            y.fill_(-7.0)
+            assert tm.tm_scale2d(x, N, y, N, M, N, 1.5, TM, TN, 1, tm.TM_VAR_AUTO) == tm.TM_OK
+            assert torch.equal(y.view(torch.int32), ref.view(torch.int32)), (TM, TN)
+            ran += 1
+    assert ran == 81
+    note("copy 8192x8192 32x128")
+    y.fill_(-7.0)
+    assert tm.tm_copy2d(x, N, y, N, M, N, 32, 128, 1, tm.TM_VAR_VEC4) == tm.TM_OK
+    assert torch.equal(y.view(torch.int32), x.view(torch.int32))
+
+
 def test_autotune_map(dev):
     """The sweep runs every tile that keeps the promise (and only those), returns the fastest, and
     leaves y holding the op's result."""
