@@ -336,6 +336,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True):
           lambda i: ok(tm.tm_rowsum(xs[i], N, outs[i], M, N, 4, 256, 1, stream)),
           "row walk, 4x256 tiles, aligned")
     for name, walk, TM, TN in (("colsum_naive_4096", tm.TM_COL_NAIVE, 256, 1),
+                               ("colsum_naive_xcd_4096", tm.TM_COL_NAIVE_XCD, 256, 1),
                                ("colsum_lds_4096", tm.TM_COL_LDS, 256, 64)):
         wsb = tm.tm_colsum_workspace_bytes(M, N, TM, TN, walk)
         wss = [torch.empty(wsb // 4, device=dev) for _ in range(R)]
@@ -346,7 +347,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True):
               "column walk, %dx%d tiles, both passes (workspace %d B not counted)" % (TM, TN, wsb))
         del wss
     reads_only = {k: round(gbs(M * N * 4, out[k]["mean_us"] * 1e-6), 1)
-                  for k in ("rowsum_4096", "colsum_naive_4096", "colsum_lds_4096")}
+                  for k in ("rowsum_4096", "colsum_naive_4096", "colsum_naive_xcd_4096", "colsum_lds_4096")}
     out["reads_only_gbs_4096"] = reads_only
     del xs, outs
 

@@ -13,7 +13,9 @@
 //
 // Naive walk: one workgroup per (slab, column), column fastest; lane t reads row slab*TM + t of
 // that column.  The lane-varying term of the address is row * ld: every lane touches its own
-// cache line.
+// cache line.  In plain id order neighbouring columns run on different XCDs and every XCD fetches
+// every line (8x the matrix on MI355X); the XCD-aware variant renumbers the workgroups so that
+// each XCD walks a contiguous range of columns and shares its lines through one L2.
 //
 // LDS walk: one workgroup per (slab, strip of TW columns), strip fastest.  LPR = TW / W lanes
 // cover one row of the strip with consecutive 16-byte chunks (W = 4; W = 1 on the scalar path), so
@@ -39,13 +41,28 @@ struct ColArgs {
 
 // ---- naive walk ------------------------------------------------------------------------------
 
+constexpr uint32_t kXcds = 8;  // MI355X: accelerator complex dies (XCDs), each with its own L2
+
+// XCD: workgroup ids are dispatched to the XCDs in turn (id mod kXcds), so in plain column order
+// the 32 workgroups whose columns share a 128-byte line run on different XCDs, each of which
+// fetches the line into its own L2.  With XCD set, the ids are renumbered so that each XCD takes a
+// contiguous range of work items (column order within it) and the line is fetched once.
+template <bool XCD>
 __global__ __launch_bounds__(kBlock) void col_naive(ColArgs a) {
     __shared__ float wave_sum[kBlock / 64];
     const int t = threadIdx.x;
     const int nwaves = blockDim.x / 64;
     const int64_t tm = int64_t(1) << a.log_tm;
     const uint64_t nwork = uint64_t(a.slabs) * uint64_t(a.N);
-    for (uint64_t w = blockIdx.x; w < nwork; w += gridDim.x) {
+    uint64_t first = blockIdx.x;
+    if constexpr (XCD) {
+        // A bijection of [0, G): XCD x (the ids x, x + kXcds, ...) gets the contiguous range
+        // starting at x * q + min(x, r), where G = q * kXcds + r.
+        const uint32_t G = gridDim.x, q = G / kXcds, r = G % kXcds;
+        const uint32_t x = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
+        first = uint64_t(x) * q + (x < r ? x : r) + i;
+    }
+    for (uint64_t w = first; w < nwork; w += gridDim.x) {
         const uint64_t slab = w / uint64_t(a.N);
         const int64_t c = int64_t(w - slab * uint64_t(a.N));
         const int64_t row = int64_t(slab) * tm + t;
@@ -224,8 +241,9 @@ hipError_t launch_cols(const tmp::ColPlan &p, hipStream_t stream) {
                                    : pick_lpr<false, false>(lpr);
             err = hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, stream);
         } else {
-            err = hipLaunchKernel(reinterpret_cast<const void *>(&col_naive), dim3(grid),
-                                  dim3(p.naive_block), args, 0, stream);
+            const void *fn = p.walk == TM_COL_NAIVE_XCD ? reinterpret_cast<const void *>(&col_naive<true>)
+                                                        : reinterpret_cast<const void *>(&col_naive<false>);
+            err = hipLaunchKernel(fn, dim3(grid), dim3(p.naive_block), args, 0, stream);
         }
         if (err != hipSuccess)
             return err;

@@ -329,7 +329,7 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
 size_t colsum_ws_bytes(int64_t M, int64_t N, int TM, int TN, int walk) {
     if (M <= 0 || N <= 0 || check_tile(TM, TN) != TM_OK)
         return 0;
-    if (walk != TM_COL_NAIVE && walk != TM_COL_LDS)
+    if (walk != TM_COL_NAIVE && walk != TM_COL_LDS && walk != TM_COL_NAIVE_XCD)
         return 0;
     const int64_t slabs = ceil_div(M, TM);
     if (slabs > INT64_MAX / 4 / N)
@@ -340,7 +340,7 @@ size_t colsum_ws_bytes(int64_t M, int64_t N, int TM, int TN, int walk) {
 int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TM, int TN,
               int aligned, int walk, void *ws, size_t ws_bytes, ColPlan *plan) {
     *plan = ColPlan{};
-    if (walk != TM_COL_NAIVE && walk != TM_COL_LDS)
+    if (walk != TM_COL_NAIVE && walk != TM_COL_LDS && walk != TM_COL_NAIVE_XCD)
         return TM_E_INVAL;
     if (aligned != 0 && aligned != 1)
         return TM_E_INVAL;

@@ -32,6 +32,7 @@ TM_VAR_VEC4 = 3
 
 TM_COL_NAIVE = 0
 TM_COL_LDS = 1
+TM_COL_NAIVE_XCD = 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libtilemap.so is not built (expected at %s); run "

@@ -86,10 +86,16 @@ typedef enum {
 
 /* How tm_colsum walks the matrix ([LAYOUT] "What it actually costs"). */
 typedef enum {
-    TM_COL_NAIVE = 0, /* each workgroup reads TM rows of ONE column: lane-varying term has stride ld */
-    TM_COL_LDS = 1    /* lanes read rows with 16-byte coalesced loads; per-column partials are folded
-                         through LDS ([LAYOUT] "Seeing it in a real kernel": tile once into fast
-                         memory, then read it in any order) */
+    TM_COL_NAIVE = 0,    /* each workgroup reads TM rows of ONE column: lane-varying term has stride
+                            ld; workgroups in column order, as the pages' strided walk */
+    TM_COL_LDS = 1,      /* lanes read rows with 16-byte coalesced loads; per-column partials are
+                            folded through LDS ([LAYOUT] "Seeing it in a real kernel": tile once
+                            into fast memory, then read it in any order) */
+    TM_COL_NAIVE_XCD = 2 /* the naive walk with its workgroups spread so that each of the GPU's
+                            XCDs (each with its own L2) takes a contiguous range of columns: the
+                            neighbouring columns that share a 128-byte line are then read through
+                            one L2, the reuse [LAYOUT] "What it actually costs" credits for the
+                            strided walk's modest cost.  Same results as TM_COL_NAIVE. */
 } tm_colwalk;
 
 /* ---- element-wise maps over tiles --------------------------------------------------------------

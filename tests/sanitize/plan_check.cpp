@@ -236,7 +236,7 @@ static void check_reductions() {
                             CHECK(p.grid >= 1, "rows grid");
                             ++g_checked;
                         }
-                        for (int walk : {TM_COL_NAIVE, TM_COL_LDS}) {
+                        for (int walk : {TM_COL_NAIVE, TM_COL_LDS, TM_COL_NAIVE_XCD}) {
                             tmp::ColPlan c;
                             const size_t wsb = tmp::colsum_ws_bytes(M, N, TR, TC, walk);
                             const int st = tmp::plan_cols(fake(0x100000), ld, const_cast<float *>(fake(0x200000)),

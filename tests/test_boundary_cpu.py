@@ -241,6 +241,8 @@ def test_colsum_workspace_and_errors():
     W = tm.tm_colsum_workspace_bytes
     assert W(4096, 4096, 256, 64, tm.TM_COL_LDS) == 16 * 4096 * 4
     assert W(4096, 4096, 256, 1, tm.TM_COL_NAIVE) == 16 * 4096 * 4
+    assert W(4096, 4096, 256, 1, tm.TM_COL_NAIVE_XCD) == 16 * 4096 * 4
+    assert W(4096, 4096, 256, 1, 3) == 0
     assert W(4100, 1000, 64, 64, tm.TM_COL_LDS) == 65 * 1000 * 4
     assert W(0, 1000, 64, 64, tm.TM_COL_LDS) == 0
     assert W(100, 0, 64, 64, tm.TM_COL_LDS) == 0

@@ -104,7 +104,8 @@ def test_sums_long_rows_and_tall_columns(dev):
     X, host = device_matrix(xh, M, N, N, dev)
     ref = oracle.colsum_f64(host, N, M, N)
     absref = oracle.colsum_f64(np.abs(host), N, M, N)
-    for walk, TM, TN in ((tm.TM_COL_LDS, 256, 64), (tm.TM_COL_LDS, 16, 4), (tm.TM_COL_NAIVE, 256, 1)):
+    for walk, TM, TN in ((tm.TM_COL_LDS, 256, 64), (tm.TM_COL_LDS, 16, 4), (tm.TM_COL_NAIVE, 256, 1),
+                         (tm.TM_COL_NAIVE_XCD, 64, 1)):
         note("colsum tall columns %dx%d walk=%d tile=%dx%d" % (M, N, walk, TM, TN))
         st, O, W = gpu_colsum(X, N, M, N, TM, TN, 0, walk, dev)
         assert st == tm.TM_OK
@@ -113,13 +114,13 @@ def test_sums_long_rows_and_tall_columns(dev):
         assert O.guards_intact() and W.guards_intact()
 
 
-@pytest.mark.parametrize("walk", [tm.TM_COL_NAIVE, tm.TM_COL_LDS])
+@pytest.mark.parametrize("walk", [tm.TM_COL_NAIVE, tm.TM_COL_LDS, tm.TM_COL_NAIVE_XCD])
 def test_colsum_4096(dev, walk):
     M = N = 4096
     xh = inputs.colrow_input(M, N)
     X, host = device_matrix(xh, M, N, N, dev)
     ref = oracle.colsum_f64(host, N, M, N)
-    tiles = ((256, 1, 0), (256, 4, 1)) if walk == tm.TM_COL_NAIVE else \
+    tiles = ((256, 1, 0), (256, 4, 1), (64, 1, 0), (8, 1, 0)) if walk != tm.TM_COL_LDS else \
         ((256, 64, 1), (64, 256, 1), (128, 1024, 1), (256, 64, 0), (32, 16, 1))
     for TM, TN, aligned in tiles:
         note("colsum4096 walk=%d tile=%dx%d aligned=%d" % (walk, TM, TN, aligned))
@@ -142,7 +143,7 @@ def test_sums_integer_inputs_bit_exact(dev):
     assert st == tm.TM_OK
     torch.cuda.synchronize()
     assert np.array_equal(bits(O.payload()), bits(rref))
-    for walk, TM, TN in ((tm.TM_COL_LDS, 256, 64), (tm.TM_COL_NAIVE, 256, 1)):
+    for walk, TM, TN in ((tm.TM_COL_LDS, 256, 64), (tm.TM_COL_NAIVE, 256, 1), (tm.TM_COL_NAIVE_XCD, 256, 1)):
         st, O, W = gpu_colsum(X, N, M, N, TM, TN, 0, walk, dev)
         assert st == tm.TM_OK
         torch.cuda.synchronize()
@@ -215,7 +216,7 @@ def test_brute_force_sums_integer(dev):
         for TM, TN in tiles:
             st, O = gpu_rowsum(X, ld, M, N, TM, TN, 0, dev)
             assert st == tm.TM_OK
-            for walk in (tm.TM_COL_NAIVE, tm.TM_COL_LDS):
+            for walk in (tm.TM_COL_NAIVE, tm.TM_COL_LDS, tm.TM_COL_NAIVE_XCD):
                 st2, C, W = gpu_colsum(X, ld, M, N, TM, TN, 0, walk, dev)
                 assert st2 == tm.TM_OK
                 torch.cuda.synchronize()
@@ -242,7 +243,7 @@ def test_ragged_sums_float(dev):
             assert st == tm.TM_OK
             torch.cuda.synchronize()
             assert_sums(O.payload().cpu().numpy(), rref, rabs)
-            for walk in (tm.TM_COL_NAIVE, tm.TM_COL_LDS):
+            for walk in (tm.TM_COL_NAIVE, tm.TM_COL_LDS, tm.TM_COL_NAIVE_XCD):
                 st, C, W = gpu_colsum(X, ld, M, N, TM, TN, 0, walk, dev)
                 assert st == tm.TM_OK
                 torch.cuda.synchronize()
