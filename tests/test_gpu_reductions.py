@@ -374,6 +374,36 @@ def test_softmax_stats_long_rows(dev):
         check_softmax(Mo, Lo, host, N, M, N)
 
 
+def test_softmax_stats_special_values(dev):
+    """Degenerate rows, on the ragged path (70 columns under BC = 64): all -inf (m is the fill,
+    l = 0), a +inf score (m = +inf, l = NaN since e^(inf - inf) is undefined), every score equal to
+    the fill itself (l = N), a NaN score (never the maximum; l = NaN), -inf mixed with finite
+    scores, and scores of magnitude 1e4.  m bit-exact, l as the oracle (NaN where it is NaN)."""
+    M, N = 6, 70
+    sh = inputs.uniform(17, M * N, -5.0, 5.0).reshape(M, N)
+    sh[0] = -np.inf
+    sh[1, 33] = np.inf
+    sh[2] = oracle.MAX_FILL
+    sh[3, 66] = np.nan
+    sh[4, ::3] = -np.inf
+    sh[5] = inputs.uniform(18, N, -1e4, 1e4)
+    sh = np.ascontiguousarray(sh.reshape(-1), dtype=np.float32)
+    S, host = device_matrix(sh, M, N, N, dev)
+    for BC, aligned in ((64, 0), (1, 0), (16, 0)):
+        note("softmax special values BC=%d" % BC)
+        st, Mo, Lo = gpu_softmax(S, N, M, N, 2, BC, aligned, dev)
+        assert st == tm.TM_OK
+        torch.cuda.synchronize()
+        m_ref, l_ref = oracle.softmax_stats(host, N, M, N)
+        assert np.array_equal(bits(Mo.payload()), bits(m_ref))
+        l = Lo.payload().cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isnan(l), np.isnan(l_ref)), (l, l_ref)
+        ok = ~np.isnan(l_ref)
+        assert np.all(np.abs(l[ok] - l_ref[ok]) <= 1e-5 * l_ref[ok] + 1e-30), (l, l_ref)
+        assert l_ref[0] == 0 and l_ref[2] == N and np.isnan(l_ref[1]) and np.isnan(l_ref[3])
+        assert Mo.guards_intact() and Lo.guards_intact()
+
+
 def test_softmax_stats_empty_rows(dev):
     X = Guarded(1, dev)
     st, Mo, Lo = gpu_softmax(X, 0, 9, 0, 4, 64, 0, dev)
