@@ -170,9 +170,11 @@ int tm_rowmax_masked(const float *s, int64_t lds, float *out, int64_t M, int64_t
  * what a softmax needs, and a 0 fill would corrupt both).  Tiles are walked as in
  * tm_rowmax_masked; each lane keeps a running maximum and a running sum that it rescales by
  * exp(m_old - m_new) whenever its maximum grows, and the lanes of a row are combined the same way.
- * Masked columns contribute nothing.  l is within 1e-5 relative of the exact sum (f32 sums,
- * device expf).  N == 0 gives m = -1.0e30f and l = 0.  m, l: M floats each, contiguous.  BR, BC,
- * aligned and the score contract are those of tm_rowmax_masked. */
+ * Masked columns contribute nothing.  l is within 1e-5 relative of the exact sum (f32 sums;
+ * e^x evaluated as 2^(x log2 e) with the hardware base-2 exponential).  N == 0 gives
+ * m = -1.0e30f and l = 0; a row of -inf gives the same; a +inf score gives m = +inf and l = NaN
+ * (e^(inf - inf)), a NaN score leaves m alone and makes l NaN.  m, l: M floats each, contiguous.
+ * BR, BC, aligned and the score contract are those of tm_rowmax_masked. */
 int tm_softmax_stats(const float *s, int64_t lds, float *m, float *l, int64_t M, int64_t N,
                      int BR, int BC, int aligned, void *stream);
 
