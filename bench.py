@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep-out", default=None,
                     help="with --paths all: write the full tile-size sweep table (JSON) to this file")
+    ap.add_argument("--size-curve", default=None,
+                    help="also time the step's call (aligned scale, 32x128 tiles) on square matrices from "
+                         "512 to 16384 and write per-size times and a least-squares fit of "
+                         "time = bytes / bandwidth + fixed cost (JSON) to this file")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the step, time K runtime device-to-device copies of the same 64 MiB "
                          "buffers: the plain copy of known size that scales rocprofv3's byte counters")
@@ -152,6 +156,9 @@ def main():
     # Batch statistics, after the timed region: BATCHES batches of BATCH_LAUNCHES launches, each
     # bracketed by its own events.
     batch = sorted(Timer(torch, stream).run(step, BATCH_LAUNCHES) / BATCH_LAUNCHES for _ in range(BATCHES))
+
+    if args.size_curve:
+        size_curve(torch, tm, inputs, dev, stream, args.size_curve)
 
     calib = None
     if args.calibrate_copy:
@@ -390,6 +397,39 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True):
     transpose_paths(torch, tm, inputs, dev, stream, timed, ok)
     torch.cuda.synchronize()
     return out
+
+
+def size_curve(torch, tm, inputs, dev, stream, path):
+    """Y = 1.5 X (aligned, VEC4, 32x128 tiles) on n x n for n = 512 .. 16384, each size over buffer
+    sets rotated through at least 1 GiB; fits time = bytes / bandwidth + fixed cost (least squares
+    over the sizes of at least 64 MiB moved, where the fit is not dominated by the fixed cost)."""
+    rows = []
+    for n in (512, 1024, 2048, 2944, 4096, 5760, 8192, 11520, 16384):  # multiples of the tile
+        nb = 2 * n * n * 4
+        R = sets_for(nb)
+        xs = [torch.empty(n * n, device=dev).uniform_(-1.0, 1.0) for _ in range(R)]
+        ys = [torch.empty_like(x) for x in xs]
+
+        def launch(i):
+            st = tm.tm_scale2d(xs[i % R], n, ys[i % R], n, n, n, 1.5, 32, 128, 1, tm.TM_VAR_VEC4, stream)
+            if st != tm.TM_OK:
+                raise tm.TilemapError(st)
+        K = max(20, min(400, int(2e9 // nb)))
+        for i in range(10):
+            launch(i)
+        t = Timer(torch, stream).run(launch, K) / K
+        rows.append({"n": n, "bytes": nb, "us": round(t * 1e6, 3), "gbs": round(gbs(nb, t), 1),
+                     "launches": K, "buffer_sets": R})
+        del xs, ys
+    big = [r for r in rows if r["bytes"] >= 64 << 20]
+    A = np.array([[r["bytes"], 1.0] for r in big])
+    b = np.array([r["us"] * 1e-6 for r in big])
+    (inv_bw, fixed), *_ = np.linalg.lstsq(A, b, rcond=None)
+    with open(path, "w") as f:
+        json.dump({"workload": "scale2d Y = 1.5 X, n x n f32, aligned, VEC4, 32x128 tiles",
+                   "sizes": rows, "fit": {"bandwidth_gbs": round(1.0 / inv_bw / 1e9, 1),
+                                          "fixed_us": round(fixed * 1e6, 3),
+                                          "sizes_used": [r["n"] for r in big]}}, f, indent=1)
 
 
 def sweep_paths(torch, tm, inputs, dev, stream, out, sweep_out):
