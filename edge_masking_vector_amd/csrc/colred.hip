@@ -7,17 +7,20 @@
 // fast memory, then read it in any order); Phobos docs "Slicing, bounds and masking" ("Masking":
 // out-of-range elements read as 0).
 //
-// Both walks cut the rows into slabs of TM rows and write one partial per (slab, column) into the
-// caller's workspace ws[slab * N + column]; colsum_finish then adds each column's partials in slab
-// order.  Nothing uses atomics, so results are deterministic.
+// Both walks cut the rows into slabs and write one partial per (slab, column) into the caller's
+// workspace ws[slab * N + column]; colsum_finish then adds each column's partials in a fixed order
+// (a group of lanes per column, each taking every FL-th slab, then a lane tree).  Nothing uses
+// atomics, so results are deterministic.
 //
-// Naive walk: one workgroup per (slab, column), column fastest; lane t reads row slab*TM + t of
-// that column.  The lane-varying term of the address is row * ld: every lane touches its own
+// Naive walk: slabs of the caller's TM rows; one workgroup per (slab, column), column fastest;
+// lane t reads row slab*TM + t of that column.  The lane-varying term of the address is row * ld: every lane touches its own
 // cache line.  In plain id order neighbouring columns run on different XCDs and every XCD fetches
 // every line (8x the matrix on MI355X); the XCD-aware variant renumbers the workgroups so that
 // each XCD walks a contiguous range of columns and shares its lines through one L2.
 //
-// LDS walk: one workgroup per (slab, strip of TW columns), strip fastest.  LPR = TW / W lanes
+// LDS walk: slabs and strips of the walk's own size (256 rows or more, up to 128 columns; the
+// caller's tile only states the promise); one workgroup per (slab, strip of TW columns), strip
+// fastest.  LPR = TW / W lanes
 // cover one row of the strip with consecutive 16-byte chunks (W = 4; W = 1 on the scalar path), so
 // the 256 threads read RP = 256 / LPR rows at a time, fully coalesced, and each thread keeps
 // running column partials in registers while walking down the slab.  The RP x TW partials are then
@@ -176,26 +179,49 @@ __global__ __launch_bounds__(kBlock) void col_lds(ColArgs a) {
 
 // ---- pass 2: fixed-order sum of the slab partials ---------------------------------------------
 
-constexpr int kFinishBatch = 16;   // partials loaded at once, then added in slab order
-constexpr int kFinishBlock = 64;   // threads per workgroup: one column each
+constexpr int kFinishBatch = 16;   // partials loaded at once per lane, then added in slab order
+constexpr int kFinishBlock = 256;  // threads per workgroup: kFinishBlock / FL columns
 
+// FL lanes per column: lane f adds slabs f, f + FL, f + 2 FL, ... in order (batches of
+// kFinishBatch loads in flight), then the FL lane values meet in a fixed DPP tree.  Columns past N
+// re-read column N - 1 so that every lane takes part in the tree; they are not stored.
+template <int FL>
 __global__ __launch_bounds__(kFinishBlock) void colsum_finish(const float *ws, float *out, int64_t N,
                                                             uint32_t slabs) {
-    for (int64_t j = int64_t(blockIdx.x) * kFinishBlock + threadIdx.x; j < N;
-         j += int64_t(gridDim.x) * kFinishBlock) {
+    constexpr int kCols = kFinishBlock / FL;  // columns per workgroup and step
+    const int f = threadIdx.x % FL;
+    for (int64_t j0 = int64_t(blockIdx.x) * kCols; j0 < N; j0 += int64_t(gridDim.x) * kCols) {
+        const int64_t j = j0 + threadIdx.x / FL;
+        const int64_t jc = j < N ? j : N - 1;
         float total = 0.0f;
-        for (uint32_t s0 = 0; s0 < slabs; s0 += kFinishBatch) {
+        for (uint32_t s0 = f; s0 < slabs; s0 += uint32_t(FL) * kFinishBatch) {
             float v[kFinishBatch];
 #pragma unroll
-            for (int u = 0; u < kFinishBatch; ++u)
-                v[u] = s0 + u < slabs ? ws[int64_t(s0 + u) * N + j] : 0.0f;
+            for (int u = 0; u < kFinishBatch; ++u) {
+                const uint32_t s = s0 + uint32_t(u) * FL;
+                v[u] = s < slabs ? ws[int64_t(s) * N + jc] : 0.0f;
+            }
             float blk = 0.0f;
 #pragma unroll
             for (int u = 0; u < kFinishBatch; ++u)
                 blk += v[u];
             total += blk;
         }
-        out[j] = total;
+        total = group_reduce<SumOp, FL>(total);
+        if (f == 0 && j < N)
+            out[j] = total;
+    }
+}
+
+const void *pick_finish(int fl) {
+    switch (fl) {
+    case 1: return reinterpret_cast<const void *>(&colsum_finish<1>);
+    case 2: return reinterpret_cast<const void *>(&colsum_finish<2>);
+    case 4: return reinterpret_cast<const void *>(&colsum_finish<4>);
+    case 8: return reinterpret_cast<const void *>(&colsum_finish<8>);
+    case 16: return reinterpret_cast<const void *>(&colsum_finish<16>);
+    case 32: return reinterpret_cast<const void *>(&colsum_finish<32>);
+    default: return reinterpret_cast<const void *>(&colsum_finish<64>);
     }
 }
 
@@ -236,8 +262,8 @@ hipError_t launch_cols(const tmp::ColPlan &p, hipStream_t stream) {
             const int W = p.vec ? 4 : 1;
             const int lpr = p.tw / W;
             // 16-byte chunks are only used when the host checked 16-byte rows; the unmasked body
-            // only when it also checked whole tiles.
-            const void *fn = p.vec ? (p.aligned ? pick_lpr<true, true>(lpr) : pick_lpr<true, false>(lpr))
+            // only when it also found whole slabs and strips.
+            const void *fn = p.vec ? (p.whole ? pick_lpr<true, true>(lpr) : pick_lpr<true, false>(lpr))
                                    : pick_lpr<false, false>(lpr);
             err = hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, stream);
         } else {
@@ -249,15 +275,15 @@ hipError_t launch_cols(const tmp::ColPlan &p, hipStream_t stream) {
             return err;
     }
     if (p.finish) {
-        const int64_t blocks = (p.N + kFinishBlock - 1) / kFinishBlock;
+        const int64_t cols = kFinishBlock / p.fl;
+        const int64_t blocks = (p.N + cols - 1) / cols;
         const uint32_t grid = static_cast<uint32_t>(blocks < kGridCap ? blocks : kGridCap);
         const float *ws = p.ws;
         float *out = p.out;
         int64_t N = p.N;
         uint32_t slabs = p.launch ? p.slabs : 0u;
         void *args[] = {&ws, &out, &N, &slabs};
-        return hipLaunchKernel(reinterpret_cast<const void *>(&colsum_finish), dim3(grid),
-                               dim3(kFinishBlock), args, 0, stream);
+        return hipLaunchKernel(pick_finish(p.fl), dim3(grid), dim3(kFinishBlock), args, 0, stream);
     }
     return hipSuccess;
 }

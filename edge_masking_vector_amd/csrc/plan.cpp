@@ -302,16 +302,51 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
     if (M == 0)
         return TM_OK;
 
-    const bool vec = TC % 4 == 0 && rows16(x, M, ld);
+    // The walk is shaped by the row length and the row count only: the caller's tile states the
+    // promise (checked above) and nothing else.  With lanes per row set from the tile, tiles 1 to
+    // 16 columns wide made a 4096 x 4096 row sum 4 to 58 times slower (one to four lanes per
+    // row), and a few long rows (8 x 2^20) ran on two workgroups.  Rows with 16-byte starts take
+    // 16-byte chunks whatever N is: whole tiles hold whole chunks, and the remainder tile masks
+    // the chunk that straddles N element by element.
+    const bool vec = rows16(x, M, ld);
     const int W = vec ? 4 : 1;
+    const int64_t chunks = ceil_div(N, W);  // chunks per row
+    int lpr, per_tile;
+    if (chunks <= (vec ? kShortRowChunksVec : kShortRowChunksScalar)) {
+        // Short rows: about 4 chunks per lane (16-byte chunks, the whole row in one tile) or 8
+        // chunks per lane with at most 16 lanes (4-byte chunks); within 8% of the fastest lane
+        // count measured for each N from 4 to 2000 at 32 MB, where the worst was 3 to 15x slower.
+        if (vec) {
+            lpr = 1 << std::min(6, ilog2(ceil_div(chunks, 4)));
+            per_tile = 1 << ilog2(ceil_div(chunks, lpr));
+        } else {
+            lpr = 1 << std::min(4, ilog2(ceil_div(chunks, 8)));
+            per_tile = 1;
+        }
+    } else {
+        // Long rows: one wave per row, walking tiles of 64 chunks (4-byte chunks: two per lane).
+        lpr = 64;
+        per_tile = vec ? 1 : 2;
+        if (M < kRowWideWaves) {
+            // Too few rows to fill the GPU with one wave each: a workgroup of several waves per
+            // row, keeping at least 4 chunks per lane.
+            int64_t l = int64_t{64} << ilog2(ceil_div(kRowWideWaves, M));
+            l = std::min<int64_t>(l, kRowMaxLanes);
+            while (l > 64 && l * 4 > chunks)
+                l >>= 1;
+            lpr = static_cast<int>(l);
+            per_tile = 1;
+        }
+    }
     plan->launch = true;
     plan->op = op;
     plan->vec = vec;
-    plan->lpr = std::min(64, TC / W);
-    plan->per_tile = TC / (W * plan->lpr);
-    plan->bc = TC;
-    split(N, TC, &plan->nfull, &plan->rem);  // whole column tiles + one masked remainder tile
-    const int64_t groups = ceil_div(M, kBlock / plan->lpr);
+    plan->lpr = lpr;
+    plan->block = lpr > 64 ? lpr : kBlock;
+    plan->per_tile = per_tile;
+    plan->bc = lpr * W * per_tile;
+    split(N, plan->bc, &plan->nfull, &plan->rem);  // whole column tiles + one masked remainder tile
+    const int64_t groups = ceil_div(M, plan->block / lpr);
     if (groups > INT32_MAX)
         return TM_E_UNSUPPORTED;  // row-group ids are 32-bit on the device
     plan->grid = cap_grid(groups);
@@ -326,12 +361,30 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
 
 // ---- column sums ------------------------------------------------------------------------------
 
+namespace {
+
+// Rows per slab, as a power of two: the naive walks keep the caller's TM (one workgroup per TM
+// rows of a column, the pages' geometry); the LDS walk uses kColSlab-row slabs, taller when more
+// than kColMaxSlabs of them would leave pass 2 too many partials per column.  On 4096 x 4096 the
+// LDS walk took 14.6-15.6 us with 64- to 256-row slabs and 64- or 128-column strips against
+// 22-44 us with tiles 16-32 rows tall or 256-1024 columns wide.
+int slab_log(int64_t M, int TM, int walk) {
+    if (walk != TM_COL_LDS)
+        return ilog2(TM);
+    int l = ilog2(kColSlab);
+    while (ceil_div(M, int64_t{1} << l) > kColMaxSlabs)
+        ++l;
+    return l;
+}
+
+}  // namespace
+
 size_t colsum_ws_bytes(int64_t M, int64_t N, int TM, int TN, int walk) {
     if (M <= 0 || N <= 0 || check_tile(TM, TN) != TM_OK)
         return 0;
     if (walk != TM_COL_NAIVE && walk != TM_COL_LDS && walk != TM_COL_NAIVE_XCD)
         return 0;
-    const int64_t slabs = ceil_div(M, TM);
+    const int64_t slabs = ceil_div(M, int64_t{1} << slab_log(M, TM, walk));
     if (slabs > INT64_MAX / 4 / N)
         return 0;
     return static_cast<size_t>(slabs * N * 4);
@@ -353,7 +406,8 @@ int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int 
         return st;
     if ((st = check_tile(TM, TN)) != TM_OK)
         return st;
-    const int64_t slabs = ceil_div(M, TM);
+    const int log_ts = M > 0 ? slab_log(M, TM, walk) : 0;
+    const int64_t slabs = ceil_div(M, int64_t{1} << log_ts);
     const size_t need = colsum_ws_bytes(M, N, TM, TN, walk);
     if (slabs > INT32_MAX || (M > 0 && N > 0 && need == 0))
         return TM_E_UNSUPPORTED;  // partial count or workspace size out of range
@@ -367,22 +421,35 @@ int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int 
     plan->finish = true;
     plan->launch = M > 0;
     plan->walk = walk;
-    plan->aligned = aligned;
-    plan->log_tm = ilog2(TM);
+    plan->log_tm = log_ts;
     plan->slabs = static_cast<uint32_t>(slabs);
-    plan->vec = TN % 4 == 0 && rows16(x, M, ld);
     if (walk == TM_COL_LDS) {
+        // Like the slabs, the strips are the walk's own: the caller's tile states the promise.
+        plan->vec = rows16(x, M, ld);
         const int W = plan->vec ? 4 : 1;
-        plan->tw = std::min(TN, kBlock * W);
+        plan->tw = std::max(W, N >= kColStrip ? kColStrip : 1 << ilog2(N));
         const int64_t strips = ceil_div(N, plan->tw);
         if (strips > INT32_MAX)
             return TM_E_UNSUPPORTED;
         plan->strips = static_cast<uint32_t>(strips);
+        // No masks when the shape is whole slabs by whole strips of 16-byte rows, promised or not.
+        plan->whole = plan->vec && M % (int64_t{1} << log_ts) == 0 && N % plan->tw == 0;
     } else {
+        plan->vec = TN % 4 == 0 && rows16(x, M, ld);
         plan->naive_block = std::max(64, TM);
         if (N > INT32_MAX)
             return TM_E_UNSUPPORTED;
         plan->strips = static_cast<uint32_t>(N);
+    }
+    // Pass 2: a group of fl lanes per column (each adding every fl-th slab in order, then a fixed
+    // lane tree), so that tall, narrow inputs do not leave a few threads adding thousands of
+    // partials one after another.
+    {
+        int64_t fl = kFinishThreads / N;
+        int l = 0;
+        while (l < 6 && (int64_t{2} << l) <= fl)
+            ++l;
+        plan->fl = std::min(1 << l, 1 << ilog2(std::max<int64_t>(slabs, 1)));
     }
     plan->x = x;
     plan->out = out;

@@ -22,6 +22,21 @@ constexpr int kScalarChunksPerThread = 4;  // 4-byte chunks per thread (16-byte 
 constexpr int kLineBytes = 128;     // cache line
 constexpr int kRowSegmentBytes = 512;  // map work items: bytes of each row they move, at least
 constexpr int kTrSub = 32;          // transpose: largest staged sub-tile edge (one 128-byte line of f32)
+// Row reductions: rows of at most this many chunks are short: lanes per row are set from the
+// row length (about 4 chunks per lane, or 8 with 4-byte chunks) ...
+constexpr int kShortRowChunksVec = 256;
+constexpr int kShortRowChunksScalar = 512;
+// ... and below this many rows (one wave each), a longer row gets a workgroup of up to
+// kRowMaxLanes threads, so that about this many waves run.
+constexpr int kRowWideWaves = 2048;
+constexpr int kRowMaxLanes = 1024;
+// LDS column walk: slabs of kColSlab rows (taller when there would be more than kColMaxSlabs of
+// them) by strips of at most kColStrip columns.
+constexpr int kColSlab = 256;
+constexpr int64_t kColMaxSlabs = 4096;
+constexpr int kColStrip = 128;
+// Column-sum pass 2: lanes per column chosen so that about this many threads run.
+constexpr int kFinishThreads = 16384;
 
 enum MapOp { kAffine = 0, kScale = 1, kCopy = 2, kChannel = 3 };
 enum Access { kScalar = 1, kVec4Understated = 2, kVec4 = 3 };
@@ -67,7 +82,8 @@ struct RowPlan {
     bool launch = false;
     int op = kRowSum;
     bool vec = false;             // 16-byte loads
-    int lpr = 1;                  // lanes per row (power of two <= 64)
+    int lpr = 1;                  // lanes per row (power of two <= kRowMaxLanes)
+    int block = kBlock;           // threads per workgroup: kBlock, or lpr when lpr > 64 (one row each)
     int per_tile = 1;             // vectors per lane per column tile
     int64_t nfull = 0;            // whole column tiles (unmasked)
     int64_t rem = 0;              // live columns of the remainder tile (0: none)
@@ -88,11 +104,12 @@ struct ColPlan {
     bool finish = false;          // pass 2 needed (N > 0)
     int walk = TM_COL_NAIVE;
     bool vec = false;
-    int aligned = 0;
-    int log_tm = 0;
+    int log_tm = 0;               // rows per slab: the caller's TM (naive walks) or the LDS walk's own
     int tw = 1;                   // columns per workgroup (LDS walk)
+    bool whole = false;           // LDS walk: whole slabs and strips with 16-byte rows (no masks)
+    int fl = 1;                   // pass 2: lanes per column (power of two <= 64)
     int naive_block = 64;         // threads per workgroup (naive walk)
-    uint32_t slabs = 0;           // ceil(M / TM): partials per column
+    uint32_t slabs = 0;           // ceil(M / rows per slab): partials per column
     uint32_t strips = 0;          // column strips (LDS walk) or columns (naive walk)
     const float *x = nullptr;
     float *out = nullptr;

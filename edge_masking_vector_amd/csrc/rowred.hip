@@ -5,15 +5,18 @@
 // maximum takes -1.0e30 where iota(1) >= N - kt); teenygrad "Memory Coalescing and Tensor Layout"
 // ("What it actually costs": the stride-1 row walk).
 //
-// Mapping.  A row is owned by a group of LPR consecutive lanes (LPR = BC / W, at most 64, where W
-// = 4 elements per 16-byte chunk or 1 on the scalar path), so one column tile is one chunk per lane
-// per step and the lanes of a group read consecutive chunks of the row: a wave reads 64/LPR rows,
-// LPR*16 contiguous bytes each.  The walk over column tiles is split in two: `nfull` whole tiles
+// Mapping.  A row is owned by a group of LPR consecutive lanes (W = 4 elements per 16-byte chunk,
+// or 1 on the scalar path), so one column tile is one chunk per lane per step and the lanes of a
+// group read consecutive chunks of the row: with LPR <= 64 a wave reads 64/LPR rows, LPR*W*4
+// contiguous bytes each; with LPR > 64 a workgroup of LPR threads owns one row.  The host picks
+// LPR from the row length and count (about 4 or 8 chunks per lane for short rows, a wave per long
+// row, a whole workgroup per row when there are too few rows to fill the GPU).  The walk over column tiles is split in two: `nfull` whole tiles
 // with no mask at all, issued 8 chunks at a time before any arithmetic (each workgroup starting at
 // a different whole tile), then one remainder tile
 // where a chunk element at tile-local column c is kept iff c < N - kt and otherwise replaced by the
 // operator's fill (0 for a sum, -1.0e30f for a maximum).  Lane partials are folded in a fixed tree,
-// then across the group with DPP row operations, ds_swizzle and readlane.  Rows past M re-read row
+// then across the group with DPP row operations, ds_swizzle and readlane, and for LPR > 64 across
+// the row's waves through LDS in wave order.  Rows past M re-read row
 // M-1 (so every lane stays active for the cross-lane steps) and are not stored.
 #include "device.hpp"
 #include "launch.h"
@@ -54,13 +57,18 @@ __device__ __forceinline__ float lanes(float v) { return v; }
 template <class Op>
 __device__ __forceinline__ float lanes(f4 v) { return Op::f(Op::f(v.x, v.y), Op::f(v.z, v.w)); }
 
-// Whole chunk, streamed (non-temporal: every element is read exactly once).
-template <bool VEC>
+// Whole chunk of a whole tile.  When the LPR lanes of a row cover at least one 128-byte line per
+// load instruction, it is streamed (non-temporal: every element is read exactly once).  Narrower
+// groups read a line over several instructions, so the line must stay cached between them: with
+// the non-temporal hint, 16-float rows read by one lane each took 11.5 us for 32 MB against
+// 7.5 us with plain loads.
+template <bool VEC, int LPR>
 __device__ __forceinline__ auto load_whole(const float *p) {
+    constexpr bool kStream = LPR * (VEC ? 16 : 4) >= 128;
     if constexpr (VEC)
-        return ld16_nt(p);
+        return kStream ? ld16_nt(p) : ld16(p);
     else
-        return ld4_nt(p);
+        return kStream ? ld4_nt(p) : *p;
 }
 
 // Chunk at p whose first `live` elements exist (live may be <= 0); the others take the fill.
@@ -82,13 +90,38 @@ __device__ __forceinline__ auto load_fill(const float *p, int64_t live) {
     }
 }
 
+// Threads per workgroup for LPR lanes per row: kBlock (several rows), or LPR (one row).
+template <int LPR>
+constexpr int block_threads() { return LPR > 64 ? LPR : kBlock; }
+
+// The value of a row, from the per-lane values of its LPR lanes: the wave-level tree, then (LPR >
+// 64) the row's waves in order through `wv` (LPR / 64 floats of LDS).  Every lane gets the
+// result.  With LPR > 64 every thread of the workgroup must call it (it has barriers).
+template <class Op, int LPR>
+__device__ __forceinline__ float row_combine(float v, float *wv) {
+    v = group_reduce<Op, (LPR < 64 ? LPR : 64)>(v);
+    if constexpr (LPR > 64) {
+        const int t = threadIdx.x;
+        if ((t & 63) == 0)
+            wv[t >> 6] = v;
+        __syncthreads();
+        v = wv[0];
+#pragma unroll
+        for (int k = 1; k < LPR / 64; ++k)
+            v = Op::f(v, wv[k]);
+        __syncthreads();  // wv is written again by the next combine
+    }
+    return v;
+}
+
 // PRE: the call has a remainder tile of at most kRemPrefetch chunks per lane, loaded ahead of the
 // whole tiles (chosen on the host; without a remainder the plain walk is 2% faster).
 template <class Op, int LPR, bool VEC, bool PRE>
-__global__ __launch_bounds__(kBlock) void row_reduce(RowArgs a) {
+__global__ __launch_bounds__(block_threads<LPR>()) void row_reduce(RowArgs a) {
     using T = typename std::conditional<VEC, f4, float>::type;
     constexpr int W = VEC ? 4 : 1;
-    constexpr int kRows = kBlock / LPR;  // rows per workgroup
+    constexpr int kRows = block_threads<LPR>() / LPR;  // rows per workgroup
+    __shared__ float wv[LPR > 64 ? LPR / 64 : 1];
     constexpr int64_t kStep = int64_t(LPR) * W;  // columns a group covers per chunk step
     const int t = threadIdx.x;
     const int g = t % LPR;  // lane within the row group
@@ -130,7 +163,7 @@ __global__ __launch_bounds__(kBlock) void row_reduce(RowArgs a) {
                 int64_t idx = k + u + start;
                 if (idx >= main_chunks)
                     idx -= main_chunks;
-                v[u] = (k + u < main_chunks) ? load_whole<VEC>(p + idx * kStep) : T(Op::kFill);
+                v[u] = (k + u < main_chunks) ? load_whole<VEC, LPR>(p + idx * kStep) : T(Op::kFill);
             }
 #pragma unroll
             for (int u = 0; u < kLoads; ++u)
@@ -154,7 +187,7 @@ __global__ __launch_bounds__(kBlock) void row_reduce(RowArgs a) {
         // Fixed-order fold: accumulators pairwise, then the chunk's elements, then the lanes.
         T s = combine<Op>(combine<Op>(acc[0], acc[1]), combine<Op>(acc[2], acc[3]));
         float r = lanes<Op>(s);
-        r = group_reduce<Op, LPR>(r);
+        r = row_combine<Op, LPR>(r, wv);
         if (g == 0 && row < a.M)
             a.out[row] = r;
     }
@@ -192,10 +225,11 @@ __device__ __forceinline__ float sum_exp_live(f4 v, float b, int64_t live) {
 }
 
 template <int LPR, bool VEC, bool PRE>
-__global__ __launch_bounds__(kBlock) void row_softmax(RowArgs a) {
+__global__ __launch_bounds__(block_threads<LPR>()) void row_softmax(RowArgs a) {
     using T = typename std::conditional<VEC, f4, float>::type;
     constexpr int W = VEC ? 4 : 1;
-    constexpr int kRows = kBlock / LPR;
+    constexpr int kRows = block_threads<LPR>() / LPR;
+    __shared__ float wv[LPR > 64 ? LPR / 64 : 1];
     constexpr int64_t kStep = int64_t(LPR) * W;
     const int t = threadIdx.x;
     const int g = t % LPR;
@@ -229,7 +263,7 @@ __global__ __launch_bounds__(kBlock) void row_softmax(RowArgs a) {
                 int64_t idx = k + u + start;
                 if (idx >= main_chunks)
                     idx -= main_chunks;
-                v[u] = (k + u < main_chunks) ? load_whole<VEC>(p + idx * kStep) : T(kMaxFill);
+                v[u] = (k + u < main_chunks) ? load_whole<VEC, LPR>(p + idx * kStep) : T(kMaxFill);
             }
             float b = m;
 #pragma unroll
@@ -268,8 +302,8 @@ __global__ __launch_bounds__(kBlock) void row_softmax(RowArgs a) {
             }
         }
 
-        const float gm = group_reduce<MaxOp, LPR>(m);
-        const float gl = group_reduce<SumOp, LPR>(l * exp_f32(m - gm));
+        const float gm = row_combine<MaxOp, LPR>(m, wv);
+        const float gl = row_combine<SumOp, LPR>(l * exp_f32(m - gm), wv);
         if (g == 0 && row < a.M) {
             a.out[row] = gm;
             a.out2[row] = gl;
@@ -292,7 +326,11 @@ const void *pick_softmax(const tmp::RowPlan &p) {
     case 8: return pick_softmax_vec<8, PRE>(p.vec);
     case 16: return pick_softmax_vec<16, PRE>(p.vec);
     case 32: return pick_softmax_vec<32, PRE>(p.vec);
-    default: return pick_softmax_vec<64, PRE>(p.vec);
+    case 64: return pick_softmax_vec<64, PRE>(p.vec);
+    case 128: return pick_softmax_vec<128, PRE>(p.vec);
+    case 256: return pick_softmax_vec<256, PRE>(p.vec);
+    case 512: return pick_softmax_vec<512, PRE>(p.vec);
+    default: return pick_softmax_vec<1024, PRE>(p.vec);
     }
 }
 
@@ -305,7 +343,11 @@ const void *pick_lpr(int lpr) {
     case 8: return reinterpret_cast<const void *>(&row_reduce<Op, 8, VEC, PRE>);
     case 16: return reinterpret_cast<const void *>(&row_reduce<Op, 16, VEC, PRE>);
     case 32: return reinterpret_cast<const void *>(&row_reduce<Op, 32, VEC, PRE>);
-    default: return reinterpret_cast<const void *>(&row_reduce<Op, 64, VEC, PRE>);
+    case 64: return reinterpret_cast<const void *>(&row_reduce<Op, 64, VEC, PRE>);
+    case 128: return reinterpret_cast<const void *>(&row_reduce<Op, 128, VEC, PRE>);
+    case 256: return reinterpret_cast<const void *>(&row_reduce<Op, 256, VEC, PRE>);
+    case 512: return reinterpret_cast<const void *>(&row_reduce<Op, 512, VEC, PRE>);
+    default: return reinterpret_cast<const void *>(&row_reduce<Op, 1024, VEC, PRE>);
     }
 }
 
@@ -335,12 +377,12 @@ hipError_t launch_rows(const tmp::RowPlan &p, hipStream_t stream) {
     a.rem = p.rem;
     a.bc = p.bc;
     a.per_tile = p.per_tile;
-    const int64_t rows_per_wg = kBlock / p.lpr;
+    const int64_t rows_per_wg = p.block / p.lpr;
     a.ngroups = static_cast<uint32_t>((p.M + rows_per_wg - 1) / rows_per_wg);
     const bool pre = p.rem > 0 && p.per_tile <= kRemPrefetch;
     const void *fn = pre ? pick_op<true>(p) : pick_op<false>(p);
     void *args[] = {&a};
-    return hipLaunchKernel(fn, dim3(p.grid), dim3(kBlock), args, 0, stream);
+    return hipLaunchKernel(fn, dim3(p.grid), dim3(p.block), args, 0, stream);
 }
 
 }  // namespace tmk

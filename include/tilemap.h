@@ -130,24 +130,31 @@ int tm_channel_affine(const float *x, int64_t ldx, const float *scale, const flo
                       int64_t ldy, int64_t M, int64_t N, int TM, int TN, int aligned, int variant,
                       void *stream);
 
-/* ---- row and column reductions -------------------------------------------------------------- */
+/* ---- row and column reductions --------------------------------------------------------------
+ * As for the maps, the caller's tile (TM x TN, BR x BC) is what the alignment promise is made
+ * for; the column tiles a row is walked in, the lanes per row and the slabs and strips of the
+ * column walk are the library's choice, set from M, N and the row alignment.  The choice decides
+ * the order of floating-point additions (within the stated bounds), never a maximum.  A row is
+ * walked by one workgroup at most, so a handful of very long rows cannot use the whole GPU. */
 
 /* out[i] = sum over j < N of x[i,j] for i < M (out: M floats, contiguous).  Rows are walked with
- * coalesced 16-byte loads in TN-wide column tiles: whole tiles unmasked, then one remainder tile
- * whose missing columns read as 0 ([SLICING] "Loops over a dynamic extent", "Masking"; [LAYOUT]
- * "What it actually costs", the row walk).  Accumulation is f32 in a fixed order; the result is
- * within 1e-5 * sum_j |x[i,j]| of the exact sum.  aligned = 1 promises M % TM == 0, N % TN == 0 and
- * 16-byte rows of x (out is not checked). */
+ * coalesced loads (16-byte when the rows start on 16-byte boundaries) in column tiles: whole tiles
+ * unmasked, then one remainder tile whose missing columns read as 0 ([SLICING] "Loops over a
+ * dynamic extent", "Masking"; [LAYOUT] "What it actually costs", the row walk).  Accumulation is
+ * f32 in a fixed order; the result is within 1e-5 * sum_j |x[i,j]| of the exact sum.  aligned = 1
+ * promises M % TM == 0, N % TN == 0 and 16-byte rows of x (out is not checked). */
 int tm_rowsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t N,
               int TM, int TN, int aligned, void *stream);
 
 /* Bytes of device workspace tm_colsum needs for these arguments (0 when M == 0 or N == 0, and
- * also 0 for invalid arguments, which tm_colsum then rejects). */
+ * also 0 for invalid arguments, which tm_colsum then rejects): 4 * N * (number of row slabs), where
+ * a slab is TM rows for the naive walks and 256 rows for the LDS walk (taller, doubling, while
+ * there would be more than 4096 slabs). */
 size_t tm_colsum_workspace_bytes(int64_t M, int64_t N, int TM, int TN, int walk);
 
 /* out[j] = sum over i < M of x[i,j] for j < N (out: N floats, contiguous).  Two passes: pass 1 writes
- * one partial per (row slab of TM rows, column) into `ws`; pass 2 adds each column's partials in
- * slab order, so the result is deterministic (no atomics).  walk: tm_colwalk.  ws: caller-owned
+ * one partial per (row slab, column) into `ws`; pass 2 adds each column's partials in a fixed
+ * order, so the result is deterministic (no atomics).  walk: tm_colwalk.  ws: caller-owned
  * device workspace of ws_bytes >= tm_colsum_workspace_bytes(...) bytes (contents on entry are
  * ignored; on return they are unspecified).  Same accuracy bound as tm_rowsum, over the column.
  * aligned = 1 promises M % TM == 0, N % TN == 0 and 16-byte rows of x; the naive walk moves single
@@ -155,7 +162,7 @@ size_t tm_colsum_workspace_bytes(int64_t M, int64_t N, int TM, int TN, int walk)
 int tm_colsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t N,
               int TM, int TN, int aligned, int walk, void *ws, size_t ws_bytes, void *stream);
 
-/* out[i] = max over j < N of s[i,j] (out: M floats, contiguous), walking BC-wide column tiles: whole
+/* out[i] = max over j < N of s[i,j] (out: M floats, contiguous), walking column tiles: whole
  * tiles unmasked, then one remainder tile in which tile-local column c keeps s iff c < N - kt and
  * is otherwise replaced by -1.0e30f (f32 bits 0xF149F2CA); the running maximum starts at that fill,
  * so N == 0 gives -1.0e30f ([SLICING] "Reductions over a ragged tile").  Scores are assumed to lie
@@ -164,7 +171,7 @@ int tm_colsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t N,
 int tm_rowmax_masked(const float *s, int64_t lds, float *out, int64_t M, int64_t N,
                      int BR, int BC, int aligned, void *stream);
 
-/* Softmax row statistics over BC-wide column tiles: m[i] = max over j < N of s[i,j], exactly as
+/* Softmax row statistics over column tiles: m[i] = max over j < N of s[i,j], exactly as
  * tm_rowmax_masked computes it (bit-exact), and l[i] = sum over j < N of exp(s[i,j] - m[i]), the
  * normaliser that goes with it ([SLICING] "Reductions over a ragged tile": the masked maximum is
  * what a softmax needs, and a 0 fill would corrupt both).  Tiles are walked as in

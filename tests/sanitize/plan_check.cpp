@@ -214,8 +214,8 @@ static void check_transposes() {
 
 // ---- row and column reductions ----------------------------------------------------------------
 static void check_reductions() {
-    const int64_t Ms[] = {0, 1, 7, 300};
-    const int64_t Ns[] = {0, 1, 5, 64, 1000, 4096};
+    const int64_t Ms[] = {0, 1, 7, 300, 2047, 1048583};
+    const int64_t Ns[] = {0, 1, 5, 64, 100, 1000, 4096, 1048576};
     for (int64_t M : Ms)
         for (int64_t N : Ns)
             for (int TR : {1, 4, 16, 256})
@@ -229,7 +229,11 @@ static void check_reductions() {
                                                           op == tmp::kRowSoftmax ? o + 4096 : nullptr);
                             if (st != TM_OK || !p.launch)
                                 continue;
-                            CHECK(p.lpr >= 1 && p.lpr <= 64 && (p.lpr & (p.lpr - 1)) == 0, "rows lpr %d", p.lpr);
+                            CHECK(p.lpr >= 1 && p.lpr <= tmp::kRowMaxLanes && (p.lpr & (p.lpr - 1)) == 0,
+                                  "rows lpr %d", p.lpr);
+                            CHECK(p.block == (p.lpr > 64 ? p.lpr : tmp::kBlock), "rows block %d", p.block);
+                            CHECK(p.bc == p.lpr * (p.vec ? 4 : 1) * p.per_tile, "rows bc %d", p.bc);
+                            CHECK(p.per_tile >= 1 && p.per_tile <= 4, "rows per_tile %d", p.per_tile);
                             CHECK(p.nfull * p.bc + p.rem == N && p.rem >= 0 && p.rem < p.bc,
                                   "rows split N=%ld bc=%d nfull=%ld rem=%ld", long(N), p.bc, long(p.nfull),
                                   long(p.rem));
@@ -245,7 +249,15 @@ static void check_reductions() {
                             if (st != TM_OK)
                                 continue;
                             if (c.launch) {
-                                CHECK(c.slabs == uint32_t((M + TR - 1) / TR), "cols slabs");
+                                const int64_t ts = int64_t{1} << c.log_tm;
+                                CHECK(c.slabs == uint32_t((M + ts - 1) / ts), "cols slabs");
+                                CHECK(walk == TM_COL_LDS ? ts >= tmp::kColSlab : ts == TR, "cols slab rows");
+                                CHECK(c.fl >= 1 && c.fl <= 64 && (c.fl & (c.fl - 1)) == 0, "cols fl %d", c.fl);
+                                if (walk == TM_COL_LDS) {
+                                    CHECK(c.tw >= 1 && c.tw <= tmp::kColStrip && uint64_t(c.strips) * c.tw >= uint64_t(N),
+                                          "cols strips");
+                                    CHECK(!c.whole || (c.vec && M % ts == 0 && N % c.tw == 0), "cols whole");
+                                }
                                 CHECK(uint64_t(c.slabs) * uint64_t(N) * 4 <= wsb, "cols workspace too small");
                             }
                             if (wsb >= 4) {  // one float less is refused

@@ -243,7 +243,12 @@ def test_colsum_workspace_and_errors():
     assert W(4096, 4096, 256, 1, tm.TM_COL_NAIVE) == 16 * 4096 * 4
     assert W(4096, 4096, 256, 1, tm.TM_COL_NAIVE_XCD) == 16 * 4096 * 4
     assert W(4096, 4096, 256, 1, 3) == 0
-    assert W(4100, 1000, 64, 64, tm.TM_COL_LDS) == 65 * 1000 * 4
+    # the LDS walk's slabs are its own (256 rows; taller past 4096 slabs), not the caller's TM
+    assert W(4100, 1000, 64, 64, tm.TM_COL_LDS) == 17 * 1000 * 4
+    assert W(4100, 1000, 1, 1, tm.TM_COL_LDS) == 17 * 1000 * 4
+    assert W(4100, 1000, 64, 1, tm.TM_COL_NAIVE) == 65 * 1000 * 4
+    assert W(1 << 21, 8, 256, 8, tm.TM_COL_LDS) == 4096 * 8 * 4
+    assert W((1 << 21) + 1, 8, 256, 8, tm.TM_COL_LDS) == 2049 * 8 * 4
     assert W(0, 1000, 64, 64, tm.TM_COL_LDS) == 0
     assert W(100, 0, 64, 64, tm.TM_COL_LDS) == 0
     assert W(100, 100, 3, 64, tm.TM_COL_LDS) == 0

@@ -114,6 +114,58 @@ def test_sums_long_rows_and_tall_columns(dev):
         assert O.guards_intact() and W.guards_intact()
 
 
+@pytest.mark.parametrize("M", [1, 7, 300, 700, 1500])
+def test_row_reductions_multiwave_rows(dev, M):
+    """Few long rows get a workgroup of several waves per row, combined across the waves through
+    LDS: 1500 rows -> 128 lanes per row, 700 -> 256, 300 -> 512, 7 and 1 -> 1024.  Ragged N
+    (16411 columns), 16-byte rows (pitch 16412) and 4-byte rows (pitch 16413 on a base off the
+    16-byte grid); sums within 1e-5 of fp64, maxima and softmax m bit-exact, l within 1e-5."""
+    N = 16411
+    for ld, off in ((16412, 0), (16413, 1)):
+        xh = inputs.uniform(100 + M, M * N, -10.0, -1.0)
+        X, host = device_matrix(xh, M, N, ld, dev, off)
+        ref = oracle.rowsum_f64(host, ld, M, N)
+        absref = oracle.rowsum_f64(np.abs(host), ld, M, N)
+        for TM, TN in ((1, 1), (4, 256)):
+            note("multiwave rows %dx%d ld=%d tile=%dx%d" % (M, N, ld, TM, TN))
+            st, O = gpu_rowsum(X, ld, M, N, TM, TN, 0, dev)
+            assert st == tm.TM_OK
+            torch.cuda.synchronize()
+            assert_sums(O.payload().cpu().numpy(), ref, absref)
+            assert O.guards_intact()
+            st, O = gpu_rowmax(X, ld, M, N, TM, TN, 0, dev)
+            assert st == tm.TM_OK
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(O.payload()), bits(oracle.rowmax(host, ld, M, N)))
+            assert O.guards_intact()
+            st, Mo, Lo = gpu_softmax(X, ld, M, N, TM, TN, 0, dev)
+            assert st == tm.TM_OK
+            torch.cuda.synchronize()
+            check_softmax(Mo, Lo, host, ld, M, N)
+
+
+def test_row_results_do_not_depend_on_the_tile(dev):
+    """The caller's tile states the promise only: every menu tile width gives the oracle's maxima
+    (bit for bit) and sums within tolerance on 2048 x 1001 with 16-byte rows, whose N is not a
+    multiple of 4 (the chunk straddling column N is masked element by element)."""
+    M, N, ld = 2048, 1001, 1004
+    xh = inputs.uniform(57, M * N, -10.0, 10.0)
+    X, host = device_matrix(xh, M, N, ld, dev)
+    want = bits(oracle.rowmax(host, ld, M, N))
+    ref = oracle.rowsum_f64(host, ld, M, N)
+    absref = oracle.rowsum_f64(np.abs(host), ld, M, N)
+    for TC in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
+        note("rows any tile TC=%d" % TC)
+        st, O = gpu_rowmax(X, ld, M, N, 1, TC, 0, dev)
+        assert st == tm.TM_OK
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(O.payload()), want), TC
+        st, O = gpu_rowsum(X, ld, M, N, 1, TC, 0, dev)
+        assert st == tm.TM_OK
+        torch.cuda.synchronize()
+        assert_sums(O.payload().cpu().numpy(), ref, absref)
+
+
 @pytest.mark.parametrize("walk", [tm.TM_COL_NAIVE, tm.TM_COL_LDS, tm.TM_COL_NAIVE_XCD])
 def test_colsum_4096(dev, walk):
     M = N = 4096
@@ -374,12 +426,14 @@ def test_softmax_stats_long_rows(dev):
         check_softmax(Mo, Lo, host, N, M, N)
 
 
-def test_softmax_stats_special_values(dev):
-    """Degenerate rows, on the ragged path (70 columns under BC = 64): all -inf (m is the fill,
+@pytest.mark.parametrize("N", [70, 16411])
+def test_softmax_stats_special_values(dev, N):
+    """Degenerate rows, on the ragged path (70 columns under BC = 64; and 16411 columns, where each
+    of the 6 rows gets 1024 lanes whose waves combine through LDS): all -inf (m is the fill,
     l = 0), a +inf score (m = +inf, l = NaN since e^(inf - inf) is undefined), every score equal to
     the fill itself (l = N), a NaN score (never the maximum; l = NaN), -inf mixed with finite
     scores, and scores of magnitude 1e4.  m bit-exact, l as the oracle (NaN where it is NaN)."""
-    M, N = 6, 70
+    M = 6
     sh = inputs.uniform(17, M * N, -5.0, 5.0).reshape(M, N)
     sh[0] = -np.inf
     sh[1, 33] = np.inf
@@ -390,7 +444,7 @@ def test_softmax_stats_special_values(dev):
     sh = np.ascontiguousarray(sh.reshape(-1), dtype=np.float32)
     S, host = device_matrix(sh, M, N, N, dev)
     for BC, aligned in ((64, 0), (1, 0), (16, 0)):
-        note("softmax special values BC=%d" % BC)
+        note("softmax special values N=%d BC=%d" % (N, BC))
         st, Mo, Lo = gpu_softmax(S, N, M, N, 2, BC, aligned, dev)
         assert st == tm.TM_OK
         torch.cuda.synchronize()
