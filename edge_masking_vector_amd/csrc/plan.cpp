@@ -311,21 +311,20 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
     const bool vec = rows16(x, M, ld);
     const int W = vec ? 4 : 1;
     const int64_t chunks = ceil_div(N, W);  // chunks per row
+    // Lanes per row, fitted to HBM-streamed sweeps of forced lane counts (N = 4 to 2000 at 32 MB,
+    // 1 GiB of rotating inputs, both chunk widths) and an interleaved comparison at 8192 x 1000
+    // (16 / 32 / 64 lanes: 7.31 / 7.24 / 7.97 us): rows of up to 64 16-byte chunks are one tile
+    // with about 4 chunks per lane; longer rows get about 8 chunks per lane per pass, up to a wave.
     int lpr, per_tile;
-    if (chunks <= (vec ? kShortRowChunksVec : kShortRowChunksScalar)) {
-        // Short rows: about 4 chunks per lane (16-byte chunks, the whole row in one tile) or 8
-        // chunks per lane with at most 16 lanes (4-byte chunks); within 8% of the fastest lane
-        // count measured for each N from 4 to 2000 at 32 MB, where the worst was 3 to 15x slower.
-        if (vec) {
-            lpr = 1 << std::min(6, ilog2(ceil_div(chunks, 4)));
-            per_tile = 1 << ilog2(ceil_div(chunks, lpr));
-        } else {
-            lpr = 1 << std::min(4, ilog2(ceil_div(chunks, 8)));
-            per_tile = 1;
-        }
+    if (vec && chunks <= kTinyRowChunks) {
+        lpr = 1 << ilog2(ceil_div(chunks, 4));
+        per_tile = 1 << ilog2(ceil_div(chunks, lpr));
     } else {
+        lpr = 1 << std::min(6, ilog2(ceil_div(chunks, 8)));
+        per_tile = 1;
+    }
+    if (chunks > (vec ? kShortRowChunksVec : kShortRowChunksScalar)) {
         // Long rows: one wave per row, walking tiles of 64 chunks (4-byte chunks: two per lane).
-        lpr = 64;
         per_tile = vec ? 1 : 2;
         if (M < kRowWideWaves) {
             // Too few rows to fill the GPU with one wave each: a workgroup of several waves per

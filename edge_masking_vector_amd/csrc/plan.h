@@ -22,8 +22,10 @@ constexpr int kScalarChunksPerThread = 4;  // 4-byte chunks per thread (16-byte 
 constexpr int kLineBytes = 128;     // cache line
 constexpr int kRowSegmentBytes = 512;  // map work items: bytes of each row they move, at least
 constexpr int kTrSub = 32;          // transpose: largest staged sub-tile edge (one 128-byte line of f32)
-// Row reductions: rows of at most this many chunks are short: lanes per row are set from the
-// row length (about 4 chunks per lane, or 8 with 4-byte chunks) ...
+// Row reductions: rows of at most kTinyRowChunks 16-byte chunks are walked as one tile with
+// about 4 chunks per lane, longer ones with about 8 per lane per pass; rows of more than
+// kShortRowChunks* chunks are long: one wave each ...
+constexpr int kTinyRowChunks = 64;
 constexpr int kShortRowChunksVec = 256;
 constexpr int kShortRowChunksScalar = 512;
 // ... and below this many rows (one wave each), a longer row gets a workgroup of up to
