@@ -60,8 +60,8 @@ __device__ __forceinline__ float lanes(f4 v) { return Op::f(Op::f(v.x, v.y), Op:
 // Whole chunk of a whole tile.  When the LPR lanes of a row cover at least one 128-byte line per
 // load instruction, it is streamed (non-temporal: every element is read exactly once).  Narrower
 // groups read a line over several instructions, so the line must stay cached between them: with
-// the non-temporal hint, 16-float rows read by one lane each took 11.5 us for 32 MB against
-// 7.5 us with plain loads.
+// the non-temporal hint, 16-float rows read by one lane each took 11.5 us for 32 MB (held in the
+// Infinity Cache) against 7.5 us with plain loads.
 template <bool VEC, int LPR>
 __device__ __forceinline__ auto load_whole(const float *p) {
     constexpr bool kStream = LPR * (VEC ? 16 : 4) >= 128;
