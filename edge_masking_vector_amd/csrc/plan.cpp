@@ -484,10 +484,10 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     if ((st = check_tile(TM, TN)) != TM_OK)
         return st;
     // 16-byte chunks: x rows read along N, y rows written along M, every row on a 16-byte boundary
-    // in every batch.
-    const bool vec = TM % 4 == 0 && TN % 4 == 0 && rows16(x, M, ldx) && rows16(y, N, ldy) &&
-                     (B <= 1 || (bsx % 4 == 0 && bsy % 4 == 0));
-    if (aligned && !(M % TM == 0 && N % TN == 0 && vec))
+    // in every batch.  Whether they are used depends on the data only (a chunk that straddles the
+    // edge of a ragged view moves element by element); the promise also covers the tile.
+    const bool vec = rows16(x, M, ldx) && rows16(y, N, ldy) && (B <= 1 || (bsx % 4 == 0 && bsy % 4 == 0));
+    if (aligned && !(M % TM == 0 && N % TN == 0 && TM % 4 == 0 && TN % 4 == 0 && vec))
         return TM_E_ALIGN;
     if (!work)
         return TM_OK;
