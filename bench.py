@@ -15,7 +15,8 @@ The same JSON line carries
   cpu_baseline  the CPU oracle (plain single-threaded C) on the same matrix on this host; the
                 same leg checks the timed kernel's output against the oracle's, bit for bit;
   paths         every other path of the method, each on its own workload shape and timed the
-                same way: the ragged path on the same shape, the three 1-D access variants, the
+                same way: the ragged path on the same shape, the three 1-D access variants and
+                the 1-D ragged path, the
                 ragged 4100 x 1000 map, row and column sums (naive and LDS walks), the masked
                 row max, the softmax row statistics, the per-channel bias add, a tile-size sweep
                 and the transpose / NCHW -> NHWC conversion.
@@ -53,6 +54,9 @@ def parse():
                          "whose 8192x8192 launches share the step's kernel), all (main plus the sweep), "
                          "or none")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--path-batches", type=int, default=BATCHES,
+                    help="after each path's timed region, this many batches of %d launches for its median "
+                         "and minimum per-launch time (0: mean only)" % BATCH_LAUNCHES)
     ap.add_argument("--sweep-out", default=None,
                     help="with --paths all: write the full tile-size sweep table (JSON) to this file")
     ap.add_argument("--size-curve", default=None,
@@ -214,7 +218,8 @@ def main():
                "sample": "oracle scale2d over the full 4096x4096 f32 matrix, %d repetitions in %.1f s "
                          "on host core %d (%s)" % (reps, el, core, cpu_model())}
 
-    paths = (run_paths(torch, tm, inputs, dev, stream, K, W, args.sweep_out, sweep=args.paths == "all")
+    paths = (run_paths(torch, tm, inputs, dev, stream, K, W, args.sweep_out, sweep=args.paths == "all",
+                       path_batches=args.path_batches)
              if args.paths != "none" else None)
 
     line = {
@@ -251,7 +256,7 @@ def cpu_model():
     return "unknown CPU"
 
 
-def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True):
+def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, path_batches=BATCHES):
     """Every other path, each on its workload shape, K launches after W warm-ups (the tile sweep
     only if `sweep`)."""
     out = {}
@@ -262,6 +267,16 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True):
         mean = Timer(torch, stream).run(lambda i: launch(i % n_sets), K) / K
         out[name] = {"gbs": round(gbs(nbytes, mean), 1), "frac": round(gbs(nbytes, mean) / PEAK_GBS, 4),
                      "mean_us": round(mean * 1e6, 3), "bytes": nbytes, "note": note}
+        if path_batches > 0:
+            # batches of BATCH_LAUNCHES launches that carry on the rotation through the buffer sets
+            batch = []
+            for b in range(path_batches):
+                first = K + b * BATCH_LAUNCHES
+                batch.append(Timer(torch, stream).run(lambda i: launch((first + i) % n_sets),
+                                                      BATCH_LAUNCHES) / BATCH_LAUNCHES)
+            batch.sort()
+            out[name]["median_us"] = round(batch[len(batch) // 2] * 1e6, 3)
+            out[name]["min_us"] = round(batch[0] * 1e6, 3)
 
     def ok(st):
         if st != tm.TM_OK:
@@ -301,20 +316,21 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True):
           "torch device-to-device copy of the same 64 MiB (ROCm's copy kernel), for context")
     del xs, ys
 
-    # 1-D a*2+1 over 2**20 elements, three access variants
+    # 1-D a*2+1 over 2**20 elements: three access variants (aligned) and the ragged VEC4 path
     n = 1 << 20
     a = inputs.map1d_input(n)
     nb = 2 * n * 4
     R = sets_for(nb)
     xs = rotated(torch, a, R, dev)
     ys = [torch.empty_like(x) for x in xs]
-    for name, var, TN in (("map1d_scalar", tm.TM_VAR_SCALAR, 256),
-                          ("map1d_vec4_understated", tm.TM_VAR_VEC4_UNDERSTATED, 1024),
-                          ("map1d_vec4", tm.TM_VAR_VEC4, 1024)):
+    for name, var, TN, aligned in (("map1d_scalar", tm.TM_VAR_SCALAR, 256, 1),
+                                   ("map1d_vec4_understated", tm.TM_VAR_VEC4_UNDERSTATED, 1024, 1),
+                                   ("map1d_vec4", tm.TM_VAR_VEC4, 1024, 1),
+                                   ("map1d_vec4_ragged", tm.TM_VAR_VEC4, 1024, 0)):
         timed(name, nb, R,
-              lambda i, var=var, TN=TN: ok(tm.tm_map_affine(xs[i], n, ys[i], n, 1, n, 2.0, 1.0, 1, TN, 1,
-                                                            var, stream)),
-              "1M-element a*2+1, aligned, TN=%d" % TN)
+              lambda i, var=var, TN=TN, aligned=aligned: ok(tm.tm_map_affine(
+                  xs[i], n, ys[i], n, 1, n, 2.0, 1.0, 1, TN, aligned, var, stream)),
+              "1M-element a*2+1, %s, TN=%d" % ("aligned" if aligned else "ragged path", TN))
     del xs, ys
 
     # ragged 4100 x 1000 affine under 64 x 64, and its aligned counterpart 4096 x 1024
