@@ -71,19 +71,20 @@ def check_case(dev, op, M, N, ldx, ldy, TM, TN, aligned, variant, xh, alpha=0.75
 
 # ---- the workload shapes at full size -----------------------------------------------------------
 
-@pytest.mark.parametrize("variant,TN", [(tm.TM_VAR_SCALAR, 256), (tm.TM_VAR_VEC4_UNDERSTATED, 1024),
-                                        (tm.TM_VAR_VEC4, 1024)])
-def test_map1d_three_variants_closed_form(dev, variant, TN):
-    """The 1M-element a*2+1 map, in each of the three access variants, equals the closed form
-    (k - 2**22) * 2**-22 computed from the generator's integers -- and hence the oracle."""
+@pytest.mark.parametrize("variant,TN,aligned", [(tm.TM_VAR_SCALAR, 256, 1), (tm.TM_VAR_VEC4_UNDERSTATED, 1024, 1),
+                                                (tm.TM_VAR_VEC4, 1024, 1), (tm.TM_VAR_VEC4, 1024, 0)])
+def test_map1d_three_variants_closed_form(dev, variant, TN, aligned):
+    """The 1M-element a*2+1 map, in each of the three access variants and on the ragged path,
+    equals the closed form (k - 2**22) * 2**-22 computed from the generator's integers -- and
+    hence the oracle."""
     n = 1 << 20
-    note("map1d variant=%d TN=%d" % (variant, TN))
+    note("map1d variant=%d TN=%d aligned=%d" % (variant, TN, aligned))
     a = inputs.map1d_input(n)
     k = inputs.u24(1, n)
     want = ((k - 2 ** 22) * 2.0 ** -22).astype(np.float32)
     x = torch.from_numpy(a).to(dev)
     Y = Guarded(n, dev)
-    assert tm.tm_map_affine(x, n, Y.ptr, n, 1, n, 2.0, 1.0, 1, TN, 1, variant) == tm.TM_OK
+    assert tm.tm_map_affine(x, n, Y.ptr, n, 1, n, 2.0, 1.0, 1, TN, aligned, variant) == tm.TM_OK
     torch.cuda.synchronize()
     assert np.array_equal(bits(Y.payload()), bits(want))
     assert Y.guards_intact()
