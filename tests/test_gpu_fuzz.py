@@ -178,6 +178,49 @@ def test_fuzz_reductions(dev):
         assert O.guards_intact()
 
 
+def test_fuzz_long_rows(dev):
+    """Row reductions on long rows (N from 1025 to 60000) with few to many rows (M from 1 to 4000,
+    at most 6M elements): rows of one wave and rows of a 128- to 1024-lane workgroup whose waves
+    combine through LDS, on 16-byte and 4-byte rows (random strides and base offsets)."""
+    rng = random.Random(78)
+    for case in range(40):
+        kind = rng.choice(["rowsum", "rowmax", "softmax"])
+        N = int(1025 * (60000 / 1025) ** rng.random())               # log-uniform
+        M = max(1, int(min(4000, 6_000_000 // N) ** rng.random()))   # log-uniform from 1
+        ld = N + rng.choice([0, 0, 0, 4, 1, 3])
+        off = rng.choice([0, 0, 0, 1])
+        TM, TN = rng.choice(TMS), rng.choice(TNS)
+        note("fuzz long rows %d: %s M=%d N=%d ld=%d off=%d tile=%dx%d" % (case, kind, M, N, ld, off, TM, TN))
+        n = (M - 1) * ld + N
+        lo, hi = (0.0, 1.0) if kind == "rowsum" else (-10.0, -1.0)
+        xh = inputs.uniform(900 + case, n, lo, hi)
+        X = Guarded(n, dev, off)
+        X.upload(xh)
+        O = Guarded(M, dev)
+        if kind == "rowsum":
+            st = tm.tm_rowsum(X.ptr, ld, O.ptr, M, N, TM, TN, 0)
+        elif kind == "rowmax":
+            st = tm.tm_rowmax_masked(X.ptr, ld, O.ptr, M, N, TM, TN, 0)
+        else:
+            L = Guarded(M, dev)
+            st = tm.tm_softmax_stats(X.ptr, ld, O.ptr, L.ptr, M, N, TM, TN, 0)
+        assert st == tm.TM_OK, tm.tm_status_string(st)
+        torch.cuda.synchronize()
+        got = O.payload().cpu().numpy()
+        if kind == "rowsum":
+            ref = oracle.rowsum_f64(xh, ld, M, N)
+            assert (np.abs(got.astype(np.float64) - ref) <= sum_tol(ref)).all(), "case %d" % case
+        elif kind == "rowmax":
+            assert np.array_equal(bits(got), bits(oracle.rowmax(xh, ld, M, N))), "case %d" % case
+        else:
+            m_ref, l_ref = oracle.softmax_stats(xh, ld, M, N)
+            assert np.array_equal(bits(got), bits(m_ref)), "case %d" % case
+            l = L.payload().cpu().numpy().astype(np.float64)
+            assert (np.abs(l - l_ref) <= 1e-5 * l_ref).all(), "case %d" % case
+            assert L.guards_intact()
+        assert O.guards_intact()
+
+
 def test_fuzz_transposes(dev):
     rng = random.Random(5150)
     ok = 0
