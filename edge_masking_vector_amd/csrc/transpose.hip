@@ -19,8 +19,10 @@
 // Diagonal order took the 4096 x 4096 transpose from 30.8 to 25.8 us.  Sub-tile and workgroup
 // size, measured on 4096 x 4096 and on NCHW -> NHWC of [32][64][3136]: 64 x 64 with 512 threads
 // 24.6 / 10.6 us, 128 x 128 with 1024 threads 24.4 / -, 32 x 32 with 256 threads (one 16-byte
-// chunk per thread) 24.2 / 9.7 us.  Reading the staged tile by rows instead of columns (a
-// timing-only variant) changed nothing: LDS bank conflicts do not limit this kernel.
+// chunk per thread) 24.2 / 9.7 us; in a standalone kernel on 4096 x 4096, longer row segments on
+// one or both sides with 2-8 chunks per thread (32 x 64 up to 128 x 64, 256 threads) took
+// 24.4-26.3 us against 23.9 us for 32 x 32.  Reading the staged tile by rows instead of columns
+// (a timing-only variant) changed nothing: LDS bank conflicts do not limit this kernel.
 #include "device.hpp"
 #include "launch.h"
 
