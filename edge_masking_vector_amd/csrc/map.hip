@@ -16,7 +16,9 @@
 // index, so a wave reads consecutive chunks of a row.  Work items run with the tile groups
 // fastest, then row strips, then tile rows, so workgroups dispatched together cover neighbouring
 // memory.  The host picks the geometry (plan.cpp): when rows start on 128-byte lines a work item
-// is one wave's worth of chunks (a strip of rows of a tile group with 512-byte row segments),
+// is one wave's worth of chunks -- with 16-byte chunks, where the tile group allows, one 1 KiB
+// row segment whose whole items move through buffer accesses of device scope with the streaming
+// hint (sc1 nt); else a strip of rows of a tile group with 512-byte row segments -- and
 // otherwise it spans as many tiles as fit in 1024 threads across the row band, so that
 // few 128-byte lines are shared by workgroups that may run on different XCDs (each XCD has its
 // own L2 and would fetch a shared line again).  Whole chunks move with the non-temporal hint.  On
@@ -196,7 +198,9 @@ __device__ __forceinline__ void store_masked(float *p, typename Chunk<ACC>::T v,
     }
 }
 
-template <int OP, int ACC, bool ALIGNED, int U, bool GUARD>
+// STREAM: every work item is one row segment of tmp::kStreamSegmentBytes (one wave of 16-byte
+// chunks, chosen on the host); whole items move it with device-scope streaming buffer accesses.
+template <int OP, int ACC, bool ALIGNED, int U, bool GUARD, bool STREAM>
 __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
     using T = typename Chunk<ACC>::T;
     constexpr int W = Chunk<ACC>::W;
@@ -228,7 +232,25 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
         // all lie inside the tensor): no masks.
         const bool item_whole = ALIGNED || ((int64_t(pm) + 1) * tm <= a.M &&
                                             col0 + int64_t(a.group) * tn <= a.N);
-        if (item_whole) {
+        if constexpr (STREAM) {
+            static_assert(ACC == tmp::kVec4 && U == 1 && !GUARD, "a stream item is one wave of 16-byte chunks");
+        }
+        if (STREAM && item_whole) {
+            // The segment starts at (row0, col0); thread t moves its 16-byte chunk t.
+            const __amdgpu_buffer_rsrc_t rx = segment_rsrc(a.x + row0 * a.ldx + col0, tmp::kStreamSegmentBytes);
+            const __amdgpu_buffer_rsrc_t ry = segment_rsrc(a.y + row0 * a.ldy + col0, tmp::kStreamSegmentBytes);
+            const int off = int(t) * 16;
+            const f4 v = ld16_seg(rx, off);
+            f4 r;
+            if constexpr (OP == tmp::kChannel) {
+                const int64_t col = col0 + int64_t(t) * 4;
+                r = apply_channel(v, load_cvec<ACC>(a.scale, col, 4, a.cvec16, 1.0f),
+                                  load_cvec<ACC>(a.bias, col, 4, a.cvec16, 0.0f));
+            } else {
+                r = apply<OP>(v, a.alpha, a.beta);
+            }
+            st16_seg(ry, off, r);
+        } else if (item_whole) {
             T v[U], cs[U], cb[U];
             int64_t yo[U];
 #pragma unroll
@@ -302,12 +324,17 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
 template <int OP, int ACC, bool GUARD>
 const void *pick_aligned(const tmp::MapPlan &p) {
     constexpr int U = ACC == tmp::kScalar ? tmp::kScalarChunksPerThread : 1;
-    return p.aligned ? reinterpret_cast<const void *>(&map_tiles<OP, ACC, true, U, GUARD>)
-                     : reinterpret_cast<const void *>(&map_tiles<OP, ACC, false, U, GUARD>);
+    return p.aligned ? reinterpret_cast<const void *>(&map_tiles<OP, ACC, true, U, GUARD, false>)
+                     : reinterpret_cast<const void *>(&map_tiles<OP, ACC, false, U, GUARD, false>);
 }
 
 template <int OP, int ACC>
 const void *pick_guard(const tmp::MapPlan &p) {
+    if constexpr (ACC == tmp::kVec4) {
+        if (p.stream)
+            return p.aligned ? reinterpret_cast<const void *>(&map_tiles<OP, ACC, true, 1, false, true>)
+                             : reinterpret_cast<const void *>(&map_tiles<OP, ACC, false, 1, false, true>);
+    }
     return p.guard ? pick_aligned<OP, ACC, true>(p) : pick_aligned<OP, ACC, false>(p);
 }
 

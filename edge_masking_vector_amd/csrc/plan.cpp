@@ -226,11 +226,29 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     // slots a CU has free; 1024-thread ones need 16 free slots on one CU at once.  Otherwise (rows
     // off the line grid) a work item spans as many tiles across the row band as fit in 1024 x U
     // chunks, so that workgroups share few lines.
+    //
+    // With 16-byte chunks, when the tile group can be a whole 1 KiB row segment, the work item is
+    // that one segment instead, moved with buffer accesses of device scope and the streaming hint
+    // (sc1 nt): on 4096 x 4096 21.2 us against 21.7-22.0 us for the 512-byte items with global nt
+    // accesses (8192 x 8192: 79.6 against 79.7; 4096 x 1024: 6.9 against 7.0).  With shorter
+    // segments the same accesses were slower (4096 x 4096 with 512-byte segments: 22.3 us; 256-byte
+    // rows of 100352 x 64: 9.5 against 9.2 us), so those keep global nt accesses.
     const int64_t line = kLineBytes / 4;
     const bool line_rows = aligned_to(x, kLineBytes) && aligned_to(y, kLineBytes) &&
                            (M <= 1 || (ldx % line == 0 && ldy % line == 0));
     int log_r, log_g;
-    if (line_rows) {
+    bool stream = false;
+    if (line_rows && access == kVec4) {
+        const int lg = ilog2(kStreamSegmentBytes / 4) - ilog2(TNs);  // tiles in one segment
+        if (lg >= 0 && lg <= log_gcap && lg + log_vr == ilog2(kMapMinBlock)) {
+            stream = true;
+            log_g = lg;
+            log_r = 0;
+        }
+    }
+    if (stream) {
+        // set above
+    } else if (line_rows) {
         const int log_target = ilog2(kMapMinBlock) + log_u;
         log_g = std::min(log_gcap, std::max(0, ilog2(kRowSegmentBytes / 4) - ilog2(TNs)));
         log_r = std::min(log_tm, std::max(0, log_target - log_vr - log_g));
@@ -258,6 +276,7 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     plan->log_strips = log_tm - log_r;
     plan->log_bs = std::max(ilog2(kMapMinBlock), log_chunks - log_u);
     plan->guard = plan->log_bs + log_u > log_chunks;
+    plan->stream = stream;
     plan->group = 1u << log_g;
     plan->groups_n = static_cast<uint32_t>(groups_n);
     plan->tiles_n = static_cast<uint32_t>(tiles_n);

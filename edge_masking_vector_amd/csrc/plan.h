@@ -20,7 +20,9 @@ constexpr int kMapMinBlock = 64;    // map workgroups: at least one wave ...
 constexpr int kMapMaxBlock = 1024;  // ... and at most 1024 threads
 constexpr int kScalarChunksPerThread = 4;  // 4-byte chunks per thread (16-byte chunks: one)
 constexpr int kLineBytes = 128;     // cache line
-constexpr int kRowSegmentBytes = 512;  // map work items: bytes of each row they move, at least
+constexpr int kRowSegmentBytes = 512;  // map work items: bytes of each row they move, at least ...
+constexpr int kStreamSegmentBytes = 1024;  // ... or one row segment of this many bytes, moved
+                                           // with device-scope streaming buffer accesses
 constexpr int kTrSub = 32;          // transpose: largest staged sub-tile edge (one 128-byte line of f32)
 // Row reductions: rows of at most kTinyRowChunks 16-byte chunks are walked as one tile with
 // about 4 chunks per lane, longer ones with about 8 per lane per pass; rows of more than
@@ -59,6 +61,8 @@ struct MapPlan {
     int log_strips = 0;           // log2(TM / R)
     int log_bs = 6;               // log2(threads per workgroup)
     bool guard = false;           // threads x chunks per thread exceed the work item's chunks
+    bool stream = false;          // work item = one row segment of kStreamSegmentBytes (one wave,
+                                  // 16-byte chunks); whole items use buffer accesses sc1 nt
     uint32_t group = 1;           // G
     uint32_t groups_n = 0;        // ceil(tiles_n / G)
     uint32_t tiles_n = 0;         // tiles along N
