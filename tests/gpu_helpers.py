@@ -8,6 +8,7 @@ import numpy as np
 import torch
 
 GUARD_FLOATS = 16                      # 64 bytes
+LINE_GUARD_FLOATS = 32                 # 128 bytes: one cache line
 SENTINEL_BITS = 0x7F7F7F7F
 SENTINEL = np.array([SENTINEL_BITS], np.uint32).view(np.float32)[0]
 
@@ -24,13 +25,16 @@ def sentinel_buffer(n_floats, device):
 
 
 class Guarded:
-    """One region of `n` floats inside a sentinel-filled device buffer, with GUARD_FLOATS guard
-    floats before and after and an optional start offset (in floats) to break 16-byte alignment."""
+    """One region of `n` floats inside a sentinel-filled device buffer, with `guard` guard floats
+    before and after (GUARD_FLOATS = 64 bytes by default; LINE_GUARD_FLOATS = 128 bytes puts the
+    region on a 128-byte line, since device allocations start on 256-byte boundaries) and an
+    optional start offset (in floats) to break the alignment."""
 
-    def __init__(self, n, device, offset=0):
+    def __init__(self, n, device, offset=0, guard=GUARD_FLOATS):
         self.n = n
-        self.off = GUARD_FLOATS + offset
-        self.buf = sentinel_buffer(self.off + n + GUARD_FLOATS, device)
+        self.off = guard + offset
+        self.buf = sentinel_buffer(self.off + n + guard, device)
+        assert self.buf.data_ptr() % 256 == 0
 
     @property
     def ptr(self):

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from edge_masking_vector_amd import inputs
-from gpu_helpers import Guarded, bits, sentinel_host, sum_tol
+from gpu_helpers import LINE_GUARD_FLOATS, Guarded, bits, sentinel_host, sum_tol
 
 pytestmark = pytest.mark.gpu
 tm = pytest.importorskip("edge_masking_vector_amd.tilemap")
@@ -118,6 +118,68 @@ def test_fuzz_maps(dev):
         assert X.guards_intact()
     note("fuzz maps: %s" % ran)
     assert ran["ok"] >= 200
+
+
+def test_fuzz_maps_line_grid(dev):
+    """Maps on views whose bases and row strides sit on 128-byte lines (one-wave work items of
+    whole lines; with 16-byte chunks mostly one 1 KiB row segment moved with buffer accesses):
+    random shapes, tiles, variants and paths, bit for bit against the oracle, one-line guards."""
+    rng = random.Random(2025)
+    ran = 0
+    for case in range(200):
+        op = rng.choice(["affine", "scale", "copy", "channel"])
+        TM, TN = rng.choice(TMS), rng.choice(TNS)
+        variant = rng.choice([tm.TM_VAR_AUTO, tm.TM_VAR_VEC4, tm.TM_VAR_VEC4, tm.TM_VAR_SCALAR])
+        aligned = rng.random() < 0.4 and TN % 4 == 0
+        if aligned:
+            M = TM * rng.randint(1, max(1, 300 // TM))
+            N = TN * rng.randint(1, max(1, 2100 // TN))
+        else:
+            M, N = rng.randint(1, 300), rng.randint(1, 2100)
+        ldx = (N + 31) // 32 * 32 + 32 * rng.randint(0, 2)
+        ldy = (N + 31) // 32 * 32 + 32 * rng.randint(0, 2)
+        note("fuzz line-grid map %d: %s M=%d N=%d ldx=%d ldy=%d tile=%dx%d aligned=%d variant=%d"
+             % (case, op, M, N, ldx, ldy, TM, TN, aligned, variant))
+        nx, ny = (M - 1) * ldx + N, M * ldy
+        xh = inputs.uniform(3000 + case, nx, -8.0, 8.0)
+        X = Guarded(nx, dev, 0, LINE_GUARD_FLOATS)
+        X.upload(xh)
+        Y = Guarded(ny, dev, 0, LINE_GUARD_FLOATS)
+        if op == "channel":
+            bh = inputs.uniform(4000 + case, N, -1.0, 1.0)
+            sh = inputs.uniform(5000 + case, N, 0.5, 1.5) if rng.random() < 0.5 else None
+            B = Guarded(N, dev)
+            B.upload(bh)
+            S = Guarded(N, dev)
+            if sh is not None:
+                S.upload(sh)
+            st = tm.tm_channel_affine(X.ptr, ldx, S.ptr if sh is not None else None, B.ptr, Y.ptr, ldy, M, N,
+                                      TM, TN, int(aligned), variant)
+        elif op == "affine":
+            st = tm.tm_map_affine(X.ptr, ldx, Y.ptr, ldy, M, N, 0.75, -0.25, TM, TN, int(aligned), variant)
+        elif op == "scale":
+            st = tm.tm_scale2d(X.ptr, ldx, Y.ptr, ldy, M, N, 1.5, TM, TN, int(aligned), variant)
+        else:
+            st = tm.tm_copy2d(X.ptr, ldx, Y.ptr, ldy, M, N, TM, TN, int(aligned), variant)
+        assert st == expected_map_status(X, Y, M, N, ldx, ldy, TM, TN, aligned, variant), tm.tm_status_string(st)
+        torch.cuda.synchronize()
+        want = sentinel_host(Y.buf.numel())
+        if st == tm.TM_OK:
+            region = want[Y.off:Y.off + Y.n].copy()
+            if op == "affine":
+                oracle.map_affine(xh, ldx, region, ldy, M, N, 0.75, -0.25)
+            elif op == "scale":
+                oracle.scale2d(xh, ldx, region, ldy, M, N, 1.5)
+            elif op == "copy":
+                oracle.copy2d(xh, ldx, region, ldy, M, N)
+            else:
+                oracle.channel_affine(xh, ldx, sh, bh, region, ldy, M, N)
+            want[Y.off:Y.off + Y.n] = region
+            ran += 1
+        assert np.array_equal(bits(Y.host()), bits(want)), "case %d" % case
+        assert X.guards_intact()
+    note("fuzz line-grid maps: %d ran" % ran)
+    assert ran >= 120
 
 
 def test_fuzz_reductions(dev):

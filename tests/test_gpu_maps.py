@@ -10,8 +10,8 @@ import torch
 
 import oracle
 from edge_masking_vector_amd import inputs
-from gpu_helpers import (GUARD_FLOATS, SENTINEL, SENTINEL_BITS, Guarded, bits, sentinel_buffer,
-                         sentinel_host)
+from gpu_helpers import (GUARD_FLOATS, LINE_GUARD_FLOATS, SENTINEL, SENTINEL_BITS, Guarded, bits,
+                         sentinel_buffer, sentinel_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,13 +48,13 @@ def ref_map(op, x, ldx, y, ldy, M, N, alpha, beta):
 
 
 def check_case(dev, op, M, N, ldx, ldy, TM, TN, aligned, variant, xh, alpha=0.75, beta=-0.25,
-               xoff=0, yoff=0, expect=tm.TM_OK):
+               xoff=0, yoff=0, expect=tm.TM_OK, guard=GUARD_FLOATS):
     """Run one map with guarded input and output and compare with the oracle bit for bit."""
     nx = max((M - 1) * ldx + N if M > 0 and N > 0 else 0, 1)
     ny = M * ldy if M > 0 else 0
-    X = Guarded(nx, dev, xoff)
+    X = Guarded(nx, dev, xoff, guard)
     X.upload(np.resize(xh, nx).astype(np.float32))
-    Y = Guarded(ny, dev, yoff)
+    Y = Guarded(ny, dev, yoff, guard)
     st = run_map(op, X.ptr, ldx, Y.ptr, ldy, M, N, alpha, beta, TM, TN, aligned, variant)
     assert st == expect, (op, M, N, ldx, ldy, TM, TN, aligned, variant, tm.tm_status_string(st))
     torch.cuda.synchronize()
@@ -337,20 +337,60 @@ def test_beyond_2g_elements(dev):
     torch.cuda.empty_cache()
 
 
+# ---- work items on the 128-byte line grid ---------------------------------------------------------
+# Inputs and outputs whose bases and row strides sit on 128-byte lines get one-wave work items of
+# whole lines: one 1 KiB row segment moved with buffer accesses (16-byte chunks, when the tile
+# group can span it), else strips of 512-byte segments.  The guard bands here are one line long
+# so that the regions start on a line.
+
+LINE_CASES = [  # (M, N, ldx, ldy, TM, TN, aligned)
+    (4096, 4096, 4096, 4096, 32, 128, 1),      # the bench's step configuration
+    (4096, 4096, 4096, 4096, 32, 128, 0),      # its ragged path: every item whole
+    (1000, 1000, 1024, 1024, 8, 128, 0),       # last tile group past column N: edge items
+    (513, 777, 800, 832, 16, 64, 0),           # ragged in both directions, different pitches
+    (64, 256, 256, 256, 4, 4, 1),              # 4-column tiles: 64 tiles per segment
+    (32, 128, 128, 128, 32, 128, 1),           # one tile per row: 512-byte strips instead
+    (1, (1 << 20) + 5, (1 << 20) + 32, (1 << 20) + 32, 1, 1024, 0),   # one long ragged row
+    (256, 2048, 2048, 2048, 256, 1024, 1),     # wide tiles cut into scheduling tiles
+]
+
+
+@pytest.mark.parametrize("case", LINE_CASES)
+def test_line_grid_items_parity(dev, case):
+    M, N, ldx, ldy, TM, TN, aligned = case
+    xh = inputs.uniform(M * 7 + N, max((M - 1) * ldx + N, 1), -8.0, 8.0)
+    for op in ("affine", "scale", "copy"):
+        for variant in (tm.TM_VAR_VEC4, tm.TM_VAR_SCALAR):
+            note("line grid %s %dx%d ld=%d/%d tile=%dx%d aligned=%d variant=%d"
+                 % (op, M, N, ldx, ldy, TM, TN, aligned, variant))
+            check_case(dev, op, M, N, ldx, ldy, TM, TN, aligned, variant, xh,
+                       guard=LINE_GUARD_FLOATS)
+
+
+def test_line_grid_channel_affine(dev):
+    """The per-channel op through one-segment work items (N >= 256 channels, line-aligned NC views),
+    with and without a scale vector, aligned and ragged."""
+    for (M, N, ld, aligned) in ((3136, 256, 256, 1), (1000, 520, 544, 0), (64, 1024, 1024, 1)):
+        for with_scale in (False, True):
+            note("line grid channel %dx%d ld=%d aligned=%d scale=%d" % (M, N, ld, aligned, with_scale))
+            check_channel(dev, M, N, ld, ld, 64 if aligned else 16, 64, aligned, tm.TM_VAR_VEC4, with_scale,
+                          guard=LINE_GUARD_FLOATS)
+
+
 # ---- per-channel affine on an NC view ----------------------------------------------------------------
 
 def check_channel(dev, M, N, ldx, ldy, TM, TN, aligned, variant, with_scale, coff=0, seed=5,
-                  expect=tm.TM_OK):
+                  expect=tm.TM_OK, guard=GUARD_FLOATS):
     xh = inputs.uniform(seed, max((M - 1) * ldx + N, 1), -8.0, 8.0)
     sh = inputs.uniform(seed + 1, max(N, 1), -2.0, 2.0)
     bh = inputs.uniform(seed + 2, max(N, 1), -1.0, 1.0)
-    X = Guarded(xh.size, dev)
+    X = Guarded(xh.size, dev, 0, guard)
     X.upload(xh)
     Sv = Guarded(sh.size, dev, coff)
     Sv.upload(sh)
     Bv = Guarded(bh.size, dev, coff)
     Bv.upload(bh)
-    Y = Guarded(max(M * ldy, 1), dev)
+    Y = Guarded(max(M * ldy, 1), dev, 0, guard)
     st = tm.tm_channel_affine(X.ptr, ldx, Sv.ptr if with_scale else 0, Bv.ptr, Y.ptr, ldy, M, N, TM,
                               TN, aligned, variant)
     assert st == expect, (M, N, ldx, ldy, TM, TN, aligned, variant, tm.tm_status_string(st))
