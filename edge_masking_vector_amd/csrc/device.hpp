@@ -29,18 +29,15 @@ __device__ __forceinline__ void st16_nt(float *p, f4 v) {
 __device__ __forceinline__ float ld4_nt(const float *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st4_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
 
-// One row segment of `bytes` bytes addressed through a buffer resource (raw buffer: stride 0,
-// 32-bit data format in the fourth descriptor word); an offset at or past `bytes` reads 0 and its
-// store is dropped by the hardware's range check.  Accesses carry the device-scope (sc1) and
-// non-temporal (nt) cache-policy bits: the same values and ordering as plain accesses.
+// One contiguous block of `bytes` bytes addressed through a buffer resource (raw buffer: stride 0,
+// 32-bit data format in the fourth descriptor word); a store at or past `bytes` is dropped by the
+// hardware's range check.  Stores carry the device-scope (sc1) and non-temporal (nt) cache-policy
+// bits: the same values and ordering as plain stores.
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kPolicyDeviceStream = 16 | 2;  // sc1 | nt
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t segment_rsrc(const float *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, bytes, kRawBufferWord3);
-}
-__device__ __forceinline__ f4 ld16_seg(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kPolicyDeviceStream));
 }
 __device__ __forceinline__ void st16_seg(__amdgpu_buffer_rsrc_t r, int byte_off, f4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, byte_off, 0, kPolicyDeviceStream);

@@ -17,8 +17,9 @@
 // fastest, then row strips, then tile rows, so workgroups dispatched together cover neighbouring
 // memory.  The host picks the geometry (plan.cpp): when rows start on 128-byte lines a work item
 // is one wave's worth of chunks -- with 16-byte chunks, where the tile group allows, one 1 KiB
-// row segment whose whole items move through buffer accesses of device scope with the streaming
-// hint (sc1 nt); else a strip of rows of a tile group with 512-byte row segments -- and
+// row segment; else a strip of rows of a tile group with 512-byte row segments; when a whole
+// item's output is one contiguous 1 KiB (a segment, or whole rows of contiguous rows) it is
+// stored through a buffer resource with device scope and the streaming hint (sc1 nt) -- and
 // otherwise it spans as many tiles as fit in 1024 threads across the row band, so that
 // few 128-byte lines are shared by workgroups that may run on different XCDs (each XCD has its
 // own L2 and would fetch a shared line again).  Whole chunks move with the non-temporal hint.  On
@@ -198,8 +199,10 @@ __device__ __forceinline__ void store_masked(float *p, typename Chunk<ACC>::T v,
     }
 }
 
-// STREAM: every work item is one row segment of tmp::kStreamSegmentBytes (one wave of 16-byte
-// chunks, chosen on the host); whole items move it with device-scope streaming buffer accesses.
+// STREAM: every work item is one wave of 16-byte chunks whose output is one contiguous block of
+// tmp::kStreamSegmentBytes (one row segment, or whole rows of a view whose rows are contiguous;
+// chosen on the host); whole items store it through a buffer resource with the device-scope
+// streaming policy.
 template <int OP, int ACC, bool ALIGNED, int U, bool GUARD, bool STREAM>
 __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
     using T = typename Chunk<ACC>::T;
@@ -236,20 +239,17 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
             static_assert(ACC == tmp::kVec4 && U == 1 && !GUARD, "a stream item is one wave of 16-byte chunks");
         }
         if (STREAM && item_whole) {
-            // The segment starts at (row0, col0); thread t moves its 16-byte chunk t.
-            const __amdgpu_buffer_rsrc_t rx = segment_rsrc(a.x + row0 * a.ldx + col0, tmp::kStreamSegmentBytes);
-            const __amdgpu_buffer_rsrc_t ry = segment_rsrc(a.y + row0 * a.ldy + col0, tmp::kStreamSegmentBytes);
-            const int off = int(t) * 16;
-            const f4 v = ld16_seg(rx, off);
+            // Thread t moves chunk t; the item's output block starts at (row0, col0) and chunk t
+            // lies 16 t bytes into it.
+            const int64_t row = chunk_row(t), col = chunk_col(t);
+            const f4 v = ld16_nt(a.x + row * a.ldx + col);
             f4 r;
-            if constexpr (OP == tmp::kChannel) {
-                const int64_t col = col0 + int64_t(t) * 4;
+            if constexpr (OP == tmp::kChannel)
                 r = apply_channel(v, load_cvec<ACC>(a.scale, col, 4, a.cvec16, 1.0f),
                                   load_cvec<ACC>(a.bias, col, 4, a.cvec16, 0.0f));
-            } else {
+            else
                 r = apply<OP>(v, a.alpha, a.beta);
-            }
-            st16_seg(ry, off, r);
+            st16_seg(segment_rsrc(a.y + row0 * a.ldy + col0, tmp::kStreamSegmentBytes), int(t) * 16, r);
         } else if (item_whole) {
             T v[U], cs[U], cb[U];
             int64_t yo[U];

@@ -228,11 +228,11 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     // chunks, so that workgroups share few lines.
     //
     // With 16-byte chunks, when the tile group can be a whole 1 KiB row segment, the work item is
-    // that one segment instead, moved with buffer accesses of device scope and the streaming hint
-    // (sc1 nt): on 4096 x 4096 21.2 us against 21.7-22.0 us for the 512-byte items with global nt
-    // accesses (8192 x 8192: 79.6 against 79.7; 4096 x 1024: 6.9 against 7.0).  With shorter
-    // segments the same accesses were slower (4096 x 4096 with 512-byte segments: 22.3 us; 256-byte
-    // rows of 100352 x 64: 9.5 against 9.2 us), so those keep global nt accesses.
+    // that one segment instead, and whole items store it through a buffer resource with device
+    // scope and the streaming hint (sc1 nt): on 4096 x 4096 21.1-21.2 us against 21.6-22.0 us for
+    // global nt stores (8192 x 8192: 79.6 against 79.7; 4096 x 1024: 6.9 against 7.0).  The gain
+    // is the stores': the same policy on the loads changed nothing, and on shorter row segments
+    // (4096 x 4096 with 512-byte segments: 22.3 us) or a transpose's 128-byte ones it was slower.
     const int64_t line = kLineBytes / 4;
     const bool line_rows = aligned_to(x, kLineBytes) && aligned_to(y, kLineBytes) &&
                            (M <= 1 || (ldx % line == 0 && ldy % line == 0));
@@ -258,6 +258,11 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
         log_g = std::min(log_gcap, std::max(0, log_target - log_vr));
         log_r = std::min(log_tm, std::max(0, log_target - log_vr - log_g));
     }
+    // A strip of whole rows of an output whose rows are contiguous (ldy == N) is one contiguous
+    // 1 KiB block too: stored like a segment (100352 x 64 bias add: 9.35 against 9.44 us).
+    if (!stream && line_rows && access == kVec4 && ldy == N && (int64_t{TNs} << log_g) == N &&
+        log_r + log_g + log_vr == ilog2(kMapMinBlock))
+        stream = true;
     const int log_chunks = log_r + log_g + log_vr;
     const int64_t groups_n = ceil_div(tiles_n, int64_t{1} << log_g);
     const int64_t nwork = tiles_m * (int64_t{1} << (log_tm - log_r)) * groups_n;

@@ -352,6 +352,10 @@ LINE_CASES = [  # (M, N, ldx, ldy, TM, TN, aligned)
     (32, 128, 128, 128, 32, 128, 1),           # one tile per row: 512-byte strips instead
     (1, (1 << 20) + 5, (1 << 20) + 32, (1 << 20) + 32, 1, 1024, 0),   # one long ragged row
     (256, 2048, 2048, 2048, 256, 1024, 1),     # wide tiles cut into scheduling tiles
+    (1001, 64, 96, 64, 16, 64, 0),             # whole rows of a contiguous output, x pitch 96
+    (4097, 128, 128, 128, 32, 128, 0),         # two contiguous rows per item, ragged last band
+    (4096, 32, 32, 32, 32, 32, 1),             # eight contiguous rows per item
+    (1000, 64, 64, 96, 16, 64, 0),             # output rows not contiguous: global stores
 ]
 
 
@@ -368,9 +372,11 @@ def test_line_grid_items_parity(dev, case):
 
 
 def test_line_grid_channel_affine(dev):
-    """The per-channel op through one-segment work items (N >= 256 channels, line-aligned NC views),
-    with and without a scale vector, aligned and ragged."""
-    for (M, N, ld, aligned) in ((3136, 256, 256, 1), (1000, 520, 544, 0), (64, 1024, 1024, 1)):
+    """The per-channel op through work items whose output is one contiguous 1 KiB (a 256-channel
+    segment, or four rows of a contiguous 64-channel NC view), with and without a scale vector,
+    aligned and ragged."""
+    for (M, N, ld, aligned) in ((3136, 256, 256, 1), (1000, 520, 544, 0), (64, 1024, 1024, 1),
+                                (3001, 64, 64, 0), (6272, 64, 64, 1)):
         for with_scale in (False, True):
             note("line grid channel %dx%d ld=%d aligned=%d scale=%d" % (M, N, ld, aligned, with_scale))
             check_channel(dev, M, N, ld, ld, 64 if aligned else 16, 64, aligned, tm.TM_VAR_VEC4, with_scale,
