@@ -73,10 +73,12 @@ def test_nchw_nhwc_round_trip(dev):
 
 def test_nchw_to_nhwc_full_workload(dev):
     """The bench's conversion at its size: (32, 64, 56, 56) NCHW -> NHWC with 64 x 64 tiles,
-    aligned, bit for bit against the oracle."""
+    aligned, bit for bit against the oracle; and the reverse conversion of the same tensor."""
     B, C, HW = 32, 64, 56 * 56
     note("nchw->nhwc full %dx%dx%d" % (B, C, HW))
     check_transpose(dev, B, C, HW, HW, C, C * HW, HW * C, 64, 64, 1, seed=6)
+    note("nhwc->nchw full %dx%dx%d" % (B, HW, C))
+    check_transpose(dev, B, HW, C, C, HW, HW * C, C * HW, 64, 64, 1, seed=7)
 
 
 def test_nchw_nhwc_ragged_channels(dev):
