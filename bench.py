@@ -216,7 +216,8 @@ def main():
         cpu = {"value": round(gbs(step_bytes * reps, el), 3), "unit": "GB/s", "cores": 1,
                "kind": "oracle",
                "sample": "oracle scale2d over the full 4096x4096 f32 matrix, %d repetitions in %.1f s "
-                         "on host core %d (%s)" % (reps, el, core, cpu_model())}
+                         "on host core %d, one of %d this process may use (%s)"
+                         % (reps, el, core, len(allowed), cpu_model())}
 
     paths = (run_paths(torch, tm, inputs, dev, stream, K, W, args.sweep_out, sweep=args.paths == "all",
                        path_batches=args.path_batches)
