@@ -1,6 +1,7 @@
-"""GPU parity of the tiled maps (tm_map_affine, tm_scale2d, tm_copy2d) against the CPU oracle,
-through the C ABI.  Maps are compared bit for bit; every output sits between 64-byte 0x7F guard
-bands and its padding columns start as 0x7F, and all of those bytes must survive the call.
+"""GPU parity of the tiled maps (tm_map_affine, tm_scale2d, tm_copy2d, tm_channel_affine) against
+the CPU oracle, through the C ABI.  Maps are compared bit for bit; every output sits between 0x7F
+guard bands (64 bytes, or one 128-byte line where the views must start on lines) and its padding
+columns start as 0x7F, and all of those bytes must survive the call.
 """
 import sys
 
