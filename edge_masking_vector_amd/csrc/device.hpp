@@ -42,6 +42,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t segment_rsrc(const float *base
 __device__ __forceinline__ void st16_seg(__amdgpu_buffer_rsrc_t r, int byte_off, f4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, byte_off, 0, kPolicyDeviceStream);
 }
+__device__ __forceinline__ void st4_seg(__amdgpu_buffer_rsrc_t r, int byte_off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, byte_off, 0, kPolicyDeviceStream);
+}
 
 // a / d and a % d for a 32-bit a and a fixed divisor d, given c = ceil(2^64 / d) (0 when d = 1):
 // the multiply-high method of Lemire, Kaser and Kurz ("Faster remainder by direct computation",

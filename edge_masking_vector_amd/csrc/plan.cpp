@@ -227,20 +227,24 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     // off the line grid) a work item spans as many tiles across the row band as fit in 1024 x U
     // chunks, so that workgroups share few lines.
     //
-    // With 16-byte chunks, when the tile group can be a whole 1 KiB row segment, the work item is
-    // that one segment instead, and whole items store it through a buffer resource with device
-    // scope and the streaming hint (sc1 nt): on 4096 x 4096 21.1-21.2 us against 21.6-22.0 us for
-    // global nt stores (8192 x 8192: 79.6 against 79.7; 4096 x 1024: 6.9 against 7.0).  The gain
-    // is the stores': the same policy on the loads changed nothing, and on shorter row segments
-    // (4096 x 4096 with 512-byte segments: 22.3 us) or a transpose's 128-byte ones it was slower.
+    // When the tile group can be a whole 1 KiB row segment, the work item is that one segment
+    // instead, and whole items store it through a buffer resource with device scope and the
+    // streaming hint (sc1 nt): on 4096 x 4096 21.1-21.2 us against 21.6-22.0 us for global nt
+    // stores, with 16-byte chunks and with 4-byte ones alike (8192 x 8192: 79.6 against 79.7;
+    // 4096 x 1024: 6.9 against 7.0).  The gain is the stores': the same policy on the loads
+    // changed nothing, and on 2 x 512-byte items (21.9 us either way) or a transpose's 128-byte
+    // row pieces it was no better or slower.
     const int64_t line = kLineBytes / 4;
     const bool line_rows = aligned_to(x, kLineBytes) && aligned_to(y, kLineBytes) &&
                            (M <= 1 || (ldx % line == 0 && ldy % line == 0));
     int log_r, log_g;
     bool stream = false;
-    if (line_rows && access == kVec4) {
+    const int log_wave_chunks = ilog2(kMapMinBlock) + log_u;  // chunks of one wave's work item
+    // (Not for the under-stated variant: each of its store instructions writes every fourth word.)
+    const bool contiguous_stores = access != kVec4Understated;
+    if (line_rows && contiguous_stores) {
         const int lg = ilog2(kStreamSegmentBytes / 4) - ilog2(TNs);  // tiles in one segment
-        if (lg >= 0 && lg <= log_gcap && lg + log_vr == ilog2(kMapMinBlock)) {
+        if (lg >= 0 && lg <= log_gcap && lg + log_vr == log_wave_chunks) {
             stream = true;
             log_g = lg;
             log_r = 0;
@@ -260,8 +264,8 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     }
     // A strip of whole rows of an output whose rows are contiguous (ldy == N) is one contiguous
     // 1 KiB block too: stored like a segment (100352 x 64 bias add: 9.35 against 9.44 us).
-    if (!stream && line_rows && access == kVec4 && ldy == N && (int64_t{TNs} << log_g) == N &&
-        log_r + log_g + log_vr == ilog2(kMapMinBlock))
+    if (!stream && line_rows && contiguous_stores && ldy == N && (int64_t{TNs} << log_g) == N &&
+        log_r + log_g + log_vr == log_wave_chunks)
         stream = true;
     const int log_chunks = log_r + log_g + log_vr;
     const int64_t groups_n = ceil_div(tiles_n, int64_t{1} << log_g);

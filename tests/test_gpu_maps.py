@@ -340,9 +340,10 @@ def test_beyond_2g_elements(dev):
 
 # ---- work items on the 128-byte line grid ---------------------------------------------------------
 # Inputs and outputs whose bases and row strides sit on 128-byte lines get one-wave work items of
-# whole lines: one 1 KiB row segment moved with buffer accesses (16-byte chunks, when the tile
-# group can span it), else strips of 512-byte segments.  The guard bands here are one line long
-# so that the regions start on a line.
+# whole lines: one 1 KiB row segment when the tile group can span it, else strips of 512-byte
+# segments; a whole item whose output is one contiguous 1 KiB is stored through a buffer resource
+# (every access variant).  The guard bands here are one line long so that the regions start on a
+# line.
 
 LINE_CASES = [  # (M, N, ldx, ldy, TM, TN, aligned)
     (4096, 4096, 4096, 4096, 32, 128, 1),      # the bench's step configuration
@@ -365,7 +366,9 @@ def test_line_grid_items_parity(dev, case):
     M, N, ldx, ldy, TM, TN, aligned = case
     xh = inputs.uniform(M * 7 + N, max((M - 1) * ldx + N, 1), -8.0, 8.0)
     for op in ("affine", "scale", "copy"):
-        for variant in (tm.TM_VAR_VEC4, tm.TM_VAR_SCALAR):
+        for variant in (tm.TM_VAR_VEC4, tm.TM_VAR_SCALAR, tm.TM_VAR_VEC4_UNDERSTATED):
+            if variant == tm.TM_VAR_VEC4_UNDERSTATED and TN % 4:
+                continue
             note("line grid %s %dx%d ld=%d/%d tile=%dx%d aligned=%d variant=%d"
                  % (op, M, N, ldx, ldy, TM, TN, aligned, variant))
             check_case(dev, op, M, N, ldx, ldy, TM, TN, aligned, variant, xh,
