@@ -50,6 +50,9 @@ static uint32_t umulhi_mod(uint32_t a, const tmp::Div32 &d) {
 }
 
 // ---- maps --------------------------------------------------------------------------------------
+// The replay walks the plan's own view (a contiguous caller view may be planned as one flat row)
+// and counts the stores per output address; every element of the caller's view must be stored
+// exactly once and no other address (row padding) at all.
 static void replay_map(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, uintptr_t xbase,
                        const char *tag) {
     const int W = p.access == tmp::kScalar ? 1 : 4;
@@ -59,21 +62,30 @@ static void replay_map(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, 
     const uint32_t vr_mask = (1u << p.log_vr) - 1u, gv_mask = (1u << p.log_gv) - 1u;
     const uint32_t strip_mask = (1u << p.log_strips) - 1u;
     const int64_t tm = int64_t(1) << p.log_tm, tn = int64_t(1) << p.log_tn;
+    const int64_t PM = p.M, PN = p.N, pld = p.ldy;
     CHECK(p.grid >= 1 && p.grid <= p.nwork, "%s grid %u nwork %u", tag, p.grid, p.nwork);
     CHECK(bs >= 64 && bs <= 1024, "%s block %u", tag, bs);
     CHECK(uint64_t(bs) * U >= chunks, "%s block %u x %d < chunks %u", tag, bs, U, chunks);
     CHECK(p.guard == (uint64_t(bs) * U > chunks), "%s guard flag", tag);
-    CHECK(tn * p.group * p.groups_n >= N, "%s tile groups do not reach column N", tag);
+    CHECK(tn * p.group * p.groups_n >= PN, "%s tile groups do not reach column N", tag);
+    CHECK(PM * PN == M * N && (PM == M || (PM == 1 && ld == N && p.ldx == PN && pld == PN)),
+          "%s planned view %ldx%ld is not the caller's or its flat row", tag, long(PM), long(PN));
     if (p.aligned) {
-        CHECK(xbase % 16 == 0 && (M <= 1 || ld % 4 == 0) || W == 1, "%s 16-byte chunks off", tag);
+        CHECK(xbase % 16 == 0 && (PM <= 1 || p.ldx % 4 == 0) || W == 1, "%s 16-byte chunks off", tag);
     }
-    std::vector<uint8_t> hits(size_t(M * N), 0);
+    if (p.stream) {
+        CHECK(p.access != tmp::kVec4Understated && !p.guard && (int64_t(W) * chunks * 4 == tmp::kStreamSegmentBytes),
+              "%s stream item is not one wave over 1 KiB", tag);
+        CHECK(p.log_r == 0 || pld == PN, "%s stream item over rows that are not contiguous", tag);
+    }
+    const int64_t span = (M - 1) * ld + N;  // addresses of the caller's view, in elements
+    std::vector<uint8_t> hits(size_t(span), 0);
     for (uint32_t w = 0; w < p.nwork; ++w) {
         const uint32_t gi = w % p.groups_n, ps = w / p.groups_n;
         const uint32_t strip = ps & strip_mask, pm = ps >> p.log_strips;
         const int64_t row0 = (int64_t(pm) << p.log_tm) + (int64_t(strip) << p.log_r);
         const int64_t col0 = int64_t(gi) * p.group * tn;
-        const bool item_whole = p.aligned || ((int64_t(pm) + 1) * tm <= M && col0 + int64_t(p.group) * tn <= N);
+        const bool item_whole = p.aligned || ((int64_t(pm) + 1) * tm <= PM && col0 + int64_t(p.group) * tn <= PN);
         for (uint32_t t = 0; t < bs; ++t) {
             for (int u = 0; u < U; ++u) {
                 const uint32_t q = t + (uint32_t(u) << p.log_bs);
@@ -85,24 +97,31 @@ static void replay_map(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, 
                 const int64_t row = row0 + int64_t(q >> p.log_gv);
                 if (item_whole) {
                     // unmasked body: the whole chunk moves
-                    CHECK(row < M && col + W <= N, "%s unmasked chunk outside (%ld, %ld)", tag,
+                    CHECK(row < PM && col + W <= PN, "%s unmasked chunk outside (%ld, %ld)", tag,
                           (long)row, (long)col);
+                    if (p.stream) {
+                        // the buffer store lands at byte 4 W q of the item's block
+                        const int64_t a0 = row0 * pld + col0;
+                        CHECK(row * pld + col == a0 + int64_t(q) * W, "%s stream chunk %u off its block", tag, q);
+                    }
                     for (int e = 0; e < W; ++e)
-                        if (row < M && col + e < N)
-                            ++hits[size_t(row * N + col + e)];
+                        if (row < PM && col + e < PN && row * pld + col + e < span)
+                            ++hits[size_t(row * pld + col + e)];
                 } else {
-                    if (!(pn < p.tiles_n && row < M && N - col > 0))
+                    if (!(pn < p.tiles_n && row < PM && PN - col > 0))
                         continue;  // masked: nothing read or stored
-                    for (int e = 0; e < W && col + e < N; ++e)
-                        ++hits[size_t(row * N + col + e)];
+                    for (int e = 0; e < W && col + e < PN; ++e)
+                        if (row * pld + col + e < span)
+                            ++hits[size_t(row * pld + col + e)];
                 }
             }
         }
     }
-    for (size_t k = 0; k < hits.size(); ++k) {
-        if (hits[k] != 1) {
-            CHECK(hits[k] == 1, "%s element (%ld, %ld) moved %d times", tag, long(k / N), long(k % N),
-                  int(hits[k]));
+    for (int64_t a = 0; a < span; ++a) {
+        const bool inside = ld == 0 || a % ld < N;
+        if (hits[size_t(a)] != (inside ? 1 : 0)) {
+            CHECK(false, "%s address %ld (element %ld, %ld) stored %d times", tag, long(a),
+                  long(ld ? a / ld : 0), long(ld ? a % ld : a), int(hits[size_t(a)]));
             break;
         }
     }
