@@ -15,7 +15,9 @@
 // before any store.  Within a work-item row the lane-varying term of every address is the chunk
 // index, so a wave reads consecutive chunks of a row.  Work items run with the tile groups
 // fastest, then row strips, then tile rows, so workgroups dispatched together cover neighbouring
-// memory.  The host picks the geometry (plan.cpp): when rows start on 128-byte lines a work item
+// memory.  The host picks the geometry (plan.cpp).  Views whose rows are contiguous in both
+// tensors (row stride N) are planned as one row of M*N elements, except for the channel op, so
+// that only the flat row's end can be ragged.  When rows start on 128-byte lines a work item
 // is one wave's worth of chunks -- with 16-byte chunks, where the tile group allows, one 1 KiB
 // row segment; else a strip of rows of a tile group with 512-byte row segments; when a whole
 // item's output is one contiguous 1 KiB (a segment, or whole rows of contiguous rows) it is

@@ -124,12 +124,27 @@ def test_scale_4096(dev, aligned, variant):
 
 def test_ragged_affine_4100x1000_guards(dev):
     """Y = fmaf(X, 0.75, -0.25) on 4100 x 1000 under 64 x 64 tiles (65 x 16 tiles, 80 of them at
-    an edge): bit-exact, guard bands untouched."""
+    an edge): bit-exact, guard bands untouched.  Rows are contiguous here, so the library walks
+    the view as one row of 4.1M elements."""
     M, N = 4100, 1000
     xh = inputs.ragged_input(M, N)
     for variant in (tm.TM_VAR_AUTO, tm.TM_VAR_VEC4, tm.TM_VAR_SCALAR, tm.TM_VAR_VEC4_UNDERSTATED):
         note("ragged4100 variant=%d" % variant)
         check_case(dev, "affine", M, N, N, N, 64, 64, 0, variant, xh)
+
+
+@pytest.mark.parametrize("ldx,ldy", [(1001, 1001), (1000, 1004), (1004, 1000), (1004, 1004)])
+def test_ragged_affine_4100x1000_padded_rows(dev, ldx, ldy):
+    """The same map over views whose rows are not contiguous in at least one tensor: the 2-D
+    schedule (work items spanning the row band, rows off the 128-byte line grid or with 16-byte
+    rows but ragged tiles), every padding column left at its 0x7F pre-fill."""
+    M, N = 4100, 1000
+    xh = inputs.uniform(31 + ldx + ldy, (M - 1) * ldx + N, -8.0, 8.0)
+    for variant in (tm.TM_VAR_AUTO, tm.TM_VAR_SCALAR, tm.TM_VAR_VEC4_UNDERSTATED, tm.TM_VAR_VEC4):
+        vec_ok = ldx % 4 == 0 and ldy % 4 == 0
+        expect = tm.TM_E_ALIGN if variant == tm.TM_VAR_VEC4 and not vec_ok else tm.TM_OK
+        note("ragged4100 ld=%d/%d variant=%d" % (ldx, ldy, variant))
+        check_case(dev, "affine", M, N, ldx, ldy, 64, 64, 0, variant, xh, expect=expect)
 
 
 def test_ragged_shape_refuses_aligned_and_writes_nothing(dev):
