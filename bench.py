@@ -18,7 +18,8 @@ The same JSON line carries
                 same way: the ragged path on the same shape, the three 1-D access variants and
                 the 1-D ragged path, the
                 ragged 4100 x 1000 map, row and column sums (naive and LDS walks), the masked
-                row max, the softmax row statistics, the per-channel bias add, a tile-size sweep
+                row max, the softmax row statistics (also over 8 rows of 2^18, in one pass and
+                split with a workspace), the per-channel bias add, a tile-size sweep
                 and the transpose / NCHW -> NHWC conversion.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--paths all|none] [--cpu-seconds S]
@@ -393,6 +394,25 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
                                                                           64, aligned, stream)),
               "row maximum and sum of exp(s - max), BC=64 column tiles")
         del ss, outs, ls
+    # a few long rows: softmax statistics over 8 rows of 2^18 scores, in one pass (one workgroup
+    # per row) and with a workspace (row segments on separate workgroups, then one combine)
+    M, N = 8, 1 << 18
+    sh = inputs.uniform(6, M * N, -10.0, -1.0)
+    R = sets_for(M * N * 4)
+    ss = rotated(torch, sh, R, dev)
+    outs = [torch.empty(M, device=dev) for _ in range(R)]
+    ls = [torch.empty(M, device=dev) for _ in range(R)]
+    wsb = tm.tm_rows_workspace_bytes(M, N)
+    ws = torch.empty(wsb // 4, device=dev)
+    nb = M * N * 4 + 2 * M * 4
+    timed("softmax_stats_8x262144_one_pass", nb, R,
+          lambda i: ok(tm.tm_softmax_stats(ss[i], N, outs[i], ls[i], M, N, 1, 64, 0, stream)),
+          "one workgroup per row")
+    timed("softmax_stats_8x262144_split", nb, R,
+          lambda i: ok(tm.tm_softmax_stats_ws(ss[i], N, outs[i], ls[i], M, N, 1, 64, 0, ws, wsb, stream)),
+          "tm_softmax_stats_ws: %d-element row segments on separate workgroups, then a combine "
+          "(workspace %d B not counted)" % (N * M * 8 // wsb, wsb))
+    del ss, outs, ls, ws
     # per-channel bias add on the NHWC tensor (32, 64, 56, 56) read as a 100352 x 64 NC view
     M, N = 32 * 56 * 56, 64
     xh = inputs.uniform(7, M * N, -1.0, 1.0)

@@ -80,6 +80,38 @@ TM_API int tm_softmax_stats(const float *s, int64_t lds, float *m, float *l, int
     return launched(tmk::launch_rows(plan, static_cast<hipStream_t>(stream)));
 }
 
+TM_API size_t tm_rows_workspace_bytes(int64_t M, int64_t N) { return tmp::rows_ws_bytes(M, N); }
+
+TM_API int tm_rowsum_ws(const float *x, int64_t ldx, float *out, int64_t M, int64_t N, int TM, int TN,
+                        int aligned, void *ws, size_t ws_bytes, void *stream) {
+    tmp::RowPlan plan;
+    const int st = tmp::plan_rows(tmp::kRowSum, x, ldx, out, M, N, TM, TN, aligned, &plan, nullptr,
+                                  true, ws, ws_bytes);
+    if (st != TM_OK || !plan.launch)
+        return st;
+    return launched(tmk::launch_rows(plan, static_cast<hipStream_t>(stream)));
+}
+
+TM_API int tm_rowmax_masked_ws(const float *s, int64_t lds, float *out, int64_t M, int64_t N, int BR,
+                               int BC, int aligned, void *ws, size_t ws_bytes, void *stream) {
+    tmp::RowPlan plan;
+    const int st = tmp::plan_rows(tmp::kRowMax, s, lds, out, M, N, BR, BC, aligned, &plan, nullptr,
+                                  true, ws, ws_bytes);
+    if (st != TM_OK || !plan.launch)
+        return st;
+    return launched(tmk::launch_rows(plan, static_cast<hipStream_t>(stream)));
+}
+
+TM_API int tm_softmax_stats_ws(const float *s, int64_t lds, float *m, float *l, int64_t M, int64_t N,
+                               int BR, int BC, int aligned, void *ws, size_t ws_bytes, void *stream) {
+    tmp::RowPlan plan;
+    const int st = tmp::plan_rows(tmp::kRowSoftmax, s, lds, m, M, N, BR, BC, aligned, &plan, l, true,
+                                  ws, ws_bytes);
+    if (st != TM_OK || !plan.launch)
+        return st;
+    return launched(tmk::launch_rows(plan, static_cast<hipStream_t>(stream)));
+}
+
 TM_API size_t tm_colsum_workspace_bytes(int64_t M, int64_t N, int TM, int TN, int walk) {
     return tmp::colsum_ws_bytes(M, N, TM, TN, walk);
 }

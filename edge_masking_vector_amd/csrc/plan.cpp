@@ -321,8 +321,30 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
 
 // ---- row reductions ---------------------------------------------------------------------------
 
+bool row_split_geometry(int64_t M, int64_t N, int *log_k, int64_t *seg, int64_t *segs) {
+    if (M <= 0 || M >= kRowSplitRows || N < kRowSplitMinN)
+        return false;
+    // K: about kRowSplitTarget segments over all rows, at least one unit per segment.
+    const int64_t units = ceil_div(N, kRowSegUnit) * M;
+    int lk = 0;
+    while (lk < kRowSegMaxLogK && (kRowSplitTarget << (lk + 1)) <= units)
+        ++lk;
+    *log_k = lk;
+    *seg = int64_t{kRowSegUnit} << lk;
+    *segs = ceil_div(N, *seg);
+    return true;
+}
+
+size_t rows_ws_bytes(int64_t M, int64_t N) {
+    int lk;
+    int64_t seg, segs;
+    if (!row_split_geometry(M, N, &lk, &seg, &segs))
+        return 0;
+    return static_cast<size_t>(M) * static_cast<size_t>(segs) * kRowPartialBytes;
+}
+
 int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TR, int TC,
-              int aligned, RowPlan *plan, float *out2) {
+              int aligned, RowPlan *plan, float *out2, bool with_ws, void *ws, size_t ws_bytes) {
     *plan = RowPlan{};
     if (op != kRowSum && op != kRowMax && op != kRowSoftmax)
         return TM_E_INVAL;
@@ -339,10 +361,42 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
         return st;
     if ((st = check_tile(TR, TC)) != TM_OK)
         return st;
+    int log_k = 0;
+    int64_t seg = 0, segs = 0;
+    const bool split_rows = with_ws && row_split_geometry(M, N, &log_k, &seg, &segs);
+    if (split_rows && (ws == nullptr || ws_bytes < rows_ws_bytes(M, N) || !aligned_to(ws, 4)))
+        return TM_E_WORKSPACE;
     if (aligned && !promise_holds(M, N, ld, 0, TR, TC, x, nullptr))
         return TM_E_ALIGN;
     if (M == 0)
         return TM_OK;
+    if (split_rows) {
+        // A few long rows: one workgroup per row would leave most of the GPU idle, so each row
+        // segment gets a workgroup of its own.  Measured against the one-pass walk (1 GiB of
+        // rotating inputs): 1 x 2^23 578 -> 11.1 us, 1 x 2^20 74.7 -> 7.3, 8 x 2^18 21.2 -> 7.5,
+        // 64 x 2^18 23.1 -> 13.5, 96 x 2^17 13.8 -> 11.4; even at 65536 columns and from 128 rows
+        // on (128 x 2^17 15.0 -> 13.5, 192 x 2^18 32.5 -> 34.9), slower at 32768 columns.
+        if (M * segs > INT32_MAX)
+            return TM_E_UNSUPPORTED;  // segment ids are 32-bit on the device
+        plan->launch = true;
+        plan->split = true;
+        plan->op = op;
+        plan->vec = rows16(x, M, ld);
+        plan->log_k = log_k;
+        plan->seg = seg;
+        plan->segs = static_cast<uint32_t>(segs);
+        plan->nwork = static_cast<uint32_t>(M * segs);
+        plan->grid = cap_grid(M * segs);
+        plan->block = kBlock;
+        plan->x = x;
+        plan->out = out;
+        plan->out2 = out2;
+        plan->ws = static_cast<float *>(ws);
+        plan->ld = ld;
+        plan->M = M;
+        plan->N = N;
+        return TM_OK;
+    }
 
     // The walk is shaped by the row length and the row count only: the caller's tile states the
     // promise (checked above) and nothing else.  With lanes per row set from the tile, tiles 1 to

@@ -34,6 +34,16 @@ constexpr int kShortRowChunksScalar = 512;
 // kRowMaxLanes threads, so that about this many waves run.
 constexpr int kRowWideWaves = 2048;
 constexpr int kRowMaxLanes = 1024;
+// Split rows (the row calls that take a workspace): fewer than kRowSplitRows rows of at least
+// kRowSplitMinN elements are cut into segments of kRowSegUnit * K elements (K = 1, 2, 4, 8 or 16,
+// chosen for about kRowSplitTarget segments in all), one workgroup each; a second kernel combines
+// each row's partials in segment order.
+constexpr int64_t kRowSplitRows = 128;
+constexpr int64_t kRowSplitMinN = 98304;
+constexpr int64_t kRowSplitTarget = 2048;
+constexpr int kRowSegUnit = 1024;
+constexpr int kRowSegMaxLogK = 4;
+constexpr int kRowPartialBytes = 8;  // workspace per segment: one float, or the pair (m, l)
 // LDS column walk: slabs of kColSlab rows (taller when there would be more than kColMaxSlabs of
 // them) by strips of at most kColStrip columns.
 constexpr int kColSlab = 256;
@@ -99,10 +109,25 @@ struct RowPlan {
     float *out = nullptr;         // sums / maxima (softmax statistics: m)
     float *out2 = nullptr;        // softmax statistics: l
     int64_t ld = 0, M = 0, N = 0;
+    // Split walk (only when the call brings a workspace and the rows are few and long): pass 1
+    // writes one partial per row segment to ws, pass 2 combines them.
+    bool split = false;
+    int log_k = 0;                // segment = kRowSegUnit << log_k elements
+    int64_t seg = 0;              // elements per segment
+    uint32_t segs = 0;            // segments per row
+    uint32_t nwork = 0;           // M * segs pass-1 workgroups' worth of segments
+    float *ws = nullptr;
 };
 
+// Segment geometry of the split walk for M rows of N elements: false when the rows are walked in
+// one pass (then no workspace is needed).
+bool row_split_geometry(int64_t M, int64_t N, int *log_k, int64_t *seg, int64_t *segs);
+size_t rows_ws_bytes(int64_t M, int64_t N);
+
+// with_ws: the call brings a workspace (ws, ws_bytes), which licenses the split walk.
 int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TR, int TC,
-              int aligned, RowPlan *plan, float *out2 = nullptr);
+              int aligned, RowPlan *plan, float *out2 = nullptr, bool with_ws = false,
+              void *ws = nullptr, size_t ws_bytes = 0);
 
 // ---- column sums ---------------------------------------------------------------------------
 struct ColPlan {

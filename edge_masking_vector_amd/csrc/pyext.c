@@ -145,6 +145,56 @@ static PyObject *py_rowsum(ARGS) {
     return PyLong_FromLong(tm_rowsum((const float *)x, ldx, (float *)out, M, N, TM, TN, al, s));
 }
 
+static PyObject *py_rows_workspace_bytes(ARGS) {
+    int64_t M, N;
+    (void)self;
+    OK(want(n, 2, "tm_rows_workspace_bytes"));
+    OK(as_i64(a[0], &M) && as_i64(a[1], &N));
+    return PyLong_FromSize_t(tm_rows_workspace_bytes(M, N));
+}
+
+static PyObject *py_rowsum_ws(ARGS) {
+    void *x, *out, *ws, *s;
+    int64_t ldx, M, N;
+    int TM, TN, al;
+    size_t wsb;
+    (void)self;
+    OK(want(n, 11, "tm_rowsum_ws"));
+    OK(as_ptr(a[0], &x) && as_i64(a[1], &ldx) && as_ptr(a[2], &out) && as_i64(a[3], &M) &&
+       as_i64(a[4], &N) && as_int(a[5], &TM) && as_int(a[6], &TN) && as_int(a[7], &al) &&
+       as_ptr(a[8], &ws) && as_size(a[9], &wsb) && as_ptr(a[10], &s));
+    return PyLong_FromLong(
+        tm_rowsum_ws((const float *)x, ldx, (float *)out, M, N, TM, TN, al, ws, wsb, s));
+}
+
+static PyObject *py_rowmax_masked_ws(ARGS) {
+    void *x, *out, *ws, *s;
+    int64_t ld, M, N;
+    int BR, BC, al;
+    size_t wsb;
+    (void)self;
+    OK(want(n, 11, "tm_rowmax_masked_ws"));
+    OK(as_ptr(a[0], &x) && as_i64(a[1], &ld) && as_ptr(a[2], &out) && as_i64(a[3], &M) &&
+       as_i64(a[4], &N) && as_int(a[5], &BR) && as_int(a[6], &BC) && as_int(a[7], &al) &&
+       as_ptr(a[8], &ws) && as_size(a[9], &wsb) && as_ptr(a[10], &s));
+    return PyLong_FromLong(
+        tm_rowmax_masked_ws((const float *)x, ld, (float *)out, M, N, BR, BC, al, ws, wsb, s));
+}
+
+static PyObject *py_softmax_stats_ws(ARGS) {
+    void *x, *m, *l, *ws, *s;
+    int64_t ld, M, N;
+    int BR, BC, al;
+    size_t wsb;
+    (void)self;
+    OK(want(n, 12, "tm_softmax_stats_ws"));
+    OK(as_ptr(a[0], &x) && as_i64(a[1], &ld) && as_ptr(a[2], &m) && as_ptr(a[3], &l) &&
+       as_i64(a[4], &M) && as_i64(a[5], &N) && as_int(a[6], &BR) && as_int(a[7], &BC) &&
+       as_int(a[8], &al) && as_ptr(a[9], &ws) && as_size(a[10], &wsb) && as_ptr(a[11], &s));
+    return PyLong_FromLong(tm_softmax_stats_ws((const float *)x, ld, (float *)m, (float *)l, M, N,
+                                               BR, BC, al, ws, wsb, s));
+}
+
 static PyObject *py_colsum_workspace_bytes(ARGS) {
     int64_t M, N;
     int TM, TN, walk;
@@ -309,6 +359,10 @@ static PyMethodDef methods[] = {
     FAST("tm_copy2d", py_copy2d),
     FAST("tm_channel_affine", py_channel_affine),
     FAST("tm_rowsum", py_rowsum),
+    FAST("tm_rows_workspace_bytes", py_rows_workspace_bytes),
+    FAST("tm_rowsum_ws", py_rowsum_ws),
+    FAST("tm_rowmax_masked_ws", py_rowmax_masked_ws),
+    FAST("tm_softmax_stats_ws", py_softmax_stats_ws),
     FAST("tm_colsum_workspace_bytes", py_colsum_workspace_bytes),
     FAST("tm_colsum", py_colsum),
     FAST("tm_rowmax_masked", py_rowmax_masked),

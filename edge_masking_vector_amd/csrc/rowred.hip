@@ -311,6 +311,166 @@ __global__ __launch_bounds__(block_threads<LPR>()) void row_softmax(RowArgs a) {
     }
 }
 
+// ---- split rows --------------------------------------------------------------------------------
+// For a few long rows (the calls that bring a workspace): segment s of row i, columns
+// [s*seg, min(N, (s+1)*seg)), is walked by one workgroup of kBlock threads, which writes the
+// segment's partial -- its sum, its maximum, or its softmax pair (m, l) -- to the workspace at
+// i*segs + s; a second kernel combines each row's partials in segment order.  Both are fixed-order
+// folds, so results are deterministic.  A segment is kRowSegUnit * K elements: 4K per thread, as
+// K 16-byte chunks or 4K single elements, at a stride of the workgroup's width so that a wave reads
+// consecutive chunks.  Masked elements (past column N) take the operator's fill and contribute
+// nothing to a softmax sum.
+struct SplitArgs {
+    const float *x;
+    float *out;         // sums / maxima; softmax statistics: m
+    float *out2;        // softmax statistics: l
+    float *ws;          // partials: one float per segment, or (m, l) pairs
+    int64_t ld, M, N;
+    int64_t seg;        // elements per segment
+    uint32_t segs;      // segments per row
+    uint32_t nwork;     // M * segs
+};
+
+// v[0] = v[0] op v[1] op ... op v[C-1], pairwise in a fixed order (C a power of two).
+template <class Op, int C, class T>
+__device__ __forceinline__ T fold(T *v) {
+#pragma unroll
+    for (int st = 1; st < C; st <<= 1)
+#pragma unroll
+        for (int i = 0; i + st < C; i += 2 * st)
+            v[i] = combine<Op>(v[i], v[i + st]);
+    return v[0];
+}
+
+template <int OPK, bool VEC, int K>
+__global__ __launch_bounds__(kBlock) void row_split_partial(SplitArgs a) {
+    using T = typename std::conditional<VEC, f4, float>::type;
+    using Op = typename std::conditional<OPK == tmp::kRowSum, SumOp, MaxOp>::type;
+    constexpr int W = VEC ? 4 : 1;
+    constexpr int C = tmp::kRowSegUnit / kBlock * K / W;  // chunks per thread
+    constexpr int64_t kStride = int64_t(kBlock) * W;      // columns between a thread's chunks
+    static_assert(C * kStride == int64_t(tmp::kRowSegUnit) * K, "segment = C chunks per thread");
+    __shared__ float wv[kBlock / 64];
+    const int t = threadIdx.x;
+
+    for (uint32_t w = blockIdx.x; w < a.nwork; w += gridDim.x) {
+        const uint32_t row = w / a.segs;
+        const int64_t c0 = int64_t(w - row * a.segs) * a.seg;  // first column of the segment
+        const float *p = a.x + int64_t(row) * a.ld + c0 + int64_t(t) * W;
+        const int64_t live0 = a.N - c0 - int64_t(t) * W;     // columns from this thread's first chunk on
+        const bool whole = c0 + a.seg <= a.N;                // uniform over the workgroup
+        T v[C];
+        if (whole) {
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                v[c] = load_whole<VEC, kBlock>(p + c * kStride);
+        } else {
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                v[c] = load_fill<Op, VEC>(p + c * kStride, live0 - c * kStride);
+        }
+        if constexpr (OPK != tmp::kRowSoftmax) {
+            const float r = row_combine<Op, kBlock>(lanes<Op>(fold<Op, C>(v)), wv);
+            if (t == 0)
+                a.ws[w] = r;
+        } else {
+            float m = kMaxFill;
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                m = __builtin_fmaxf(m, chunk_max(v[c]));  // the fill never exceeds a score
+            float l = 0.0f;
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                l += whole ? sum_exp(v[c], m)
+                           : (live0 - c * kStride > 0 ? sum_exp_live(v[c], m, live0 - c * kStride) : 0.0f);
+            const float gm = row_combine<MaxOp, kBlock>(m, wv);
+            const float gl = row_combine<SumOp, kBlock>(l * exp_f32(m - gm), wv);
+            if (t == 0) {
+                a.ws[2 * int64_t(w)] = gm;
+                a.ws[2 * int64_t(w) + 1] = gl;
+            }
+        }
+    }
+}
+
+// One workgroup per row: thread t folds partials t, t + kBlock, ... in order, then the workgroup
+// combines the threads in a fixed tree.
+template <int OPK>
+__global__ __launch_bounds__(kBlock) void row_split_finish(SplitArgs a) {
+    __shared__ float wv[kBlock / 64];
+    const int t = threadIdx.x;
+    for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x) {
+        if constexpr (OPK != tmp::kRowSoftmax) {
+            using Op = typename std::conditional<OPK == tmp::kRowSum, SumOp, MaxOp>::type;
+            const float *pp = a.ws + row * a.segs;
+            float r = Op::kFill;
+            for (uint32_t sg = t; sg < a.segs; sg += kBlock)
+                r = Op::f(r, pp[sg]);
+            r = row_combine<Op, kBlock>(r, wv);
+            if (t == 0)
+                a.out[row] = r;
+        } else {
+            const float *pp = a.ws + 2 * row * a.segs;
+            float m = kMaxFill, l = 0.0f;
+            for (uint32_t sg = t; sg < a.segs; sg += kBlock) {
+                const float ms = pp[2 * sg], ls = pp[2 * sg + 1];
+                const float b = __builtin_fmaxf(m, ms);
+                l = l * exp_f32(m - b) + ls * exp_f32(ms - b);
+                m = b;
+            }
+            const float gm = row_combine<MaxOp, kBlock>(m, wv);
+            const float gl = row_combine<SumOp, kBlock>(l * exp_f32(m - gm), wv);
+            if (t == 0) {
+                a.out[row] = gm;
+                a.out2[row] = gl;
+            }
+        }
+    }
+}
+
+template <int OPK, bool VEC>
+const void *pick_split_k(int log_k) {
+    switch (log_k) {
+    case 0: return reinterpret_cast<const void *>(&row_split_partial<OPK, VEC, 1>);
+    case 1: return reinterpret_cast<const void *>(&row_split_partial<OPK, VEC, 2>);
+    case 2: return reinterpret_cast<const void *>(&row_split_partial<OPK, VEC, 4>);
+    case 3: return reinterpret_cast<const void *>(&row_split_partial<OPK, VEC, 8>);
+    default: return reinterpret_cast<const void *>(&row_split_partial<OPK, VEC, 16>);
+    }
+}
+
+template <int OPK>
+const void *pick_split(const tmp::RowPlan &p) {
+    return p.vec ? pick_split_k<OPK, true>(p.log_k) : pick_split_k<OPK, false>(p.log_k);
+}
+
+hipError_t launch_split(const tmp::RowPlan &p, hipStream_t stream) {
+    static_assert(tmp::kRowSegMaxLogK == 4, "pick_split_k instantiates K = 1 .. 16");
+    SplitArgs a;
+    a.x = p.x;
+    a.out = p.out;
+    a.out2 = p.out2;
+    a.ws = p.ws;
+    a.ld = p.ld;
+    a.M = p.M;
+    a.N = p.N;
+    a.seg = p.seg;
+    a.segs = p.segs;
+    a.nwork = p.nwork;
+    void *args[] = {&a};
+    const void *part = p.op == tmp::kRowMax       ? pick_split<tmp::kRowMax>(p)
+                       : p.op == tmp::kRowSoftmax ? pick_split<tmp::kRowSoftmax>(p)
+                                                  : pick_split<tmp::kRowSum>(p);
+    const void *fin = p.op == tmp::kRowMax       ? reinterpret_cast<const void *>(&row_split_finish<tmp::kRowMax>)
+                      : p.op == tmp::kRowSoftmax ? reinterpret_cast<const void *>(&row_split_finish<tmp::kRowSoftmax>)
+                                                 : reinterpret_cast<const void *>(&row_split_finish<tmp::kRowSum>);
+    hipError_t e = hipLaunchKernel(part, dim3(p.grid), dim3(kBlock), args, 0, stream);
+    if (e != hipSuccess)
+        return e;
+    const uint32_t fgrid = static_cast<uint32_t>(p.M < (int64_t{1} << 20) ? p.M : (int64_t{1} << 20));
+    return hipLaunchKernel(fin, dim3(fgrid), dim3(kBlock), args, 0, stream);
+}
+
 template <int LPR, bool PRE>
 const void *pick_softmax_vec(bool vec) {
     return vec ? reinterpret_cast<const void *>(&row_softmax<LPR, true, PRE>)
@@ -366,6 +526,8 @@ const void *pick_op(const tmp::RowPlan &p) {
 }  // namespace
 
 hipError_t launch_rows(const tmp::RowPlan &p, hipStream_t stream) {
+    if (p.split)
+        return launch_split(p, stream);
     RowArgs a;
     a.x = p.x;
     a.out = p.out;

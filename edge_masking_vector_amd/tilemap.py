@@ -117,6 +117,25 @@ def tm_softmax_stats(s, lds, m, l, M, N, BR, BC, aligned, stream=None):
                                  _stream(stream))
 
 
+def tm_rows_workspace_bytes(M, N):
+    return _ext.tm_rows_workspace_bytes(M, N)
+
+
+def tm_rowsum_ws(x, ldx, out, M, N, TM, TN, aligned, ws, ws_bytes, stream=None):
+    return _ext.tm_rowsum_ws(_ptr(x), ldx, _ptr(out), M, N, TM, TN, aligned, _ptr(ws), ws_bytes,
+                             _stream(stream))
+
+
+def tm_rowmax_masked_ws(s, lds, out, M, N, BR, BC, aligned, ws, ws_bytes, stream=None):
+    return _ext.tm_rowmax_masked_ws(_ptr(s), lds, _ptr(out), M, N, BR, BC, aligned, _ptr(ws),
+                                    ws_bytes, _stream(stream))
+
+
+def tm_softmax_stats_ws(s, lds, m, l, M, N, BR, BC, aligned, ws, ws_bytes, stream=None):
+    return _ext.tm_softmax_stats_ws(_ptr(s), lds, _ptr(m), _ptr(l), M, N, BR, BC, aligned,
+                                    _ptr(ws), ws_bytes, _stream(stream))
+
+
 def tm_transpose(x, ldx, bsx, y, ldy, bsy, B, M, N, TM, TN, aligned, stream=None):
     return _ext.tm_transpose(_ptr(x), ldx, bsx, _ptr(y), ldy, bsy, B, M, N, TM, TN, aligned,
                              _stream(stream))

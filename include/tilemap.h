@@ -68,7 +68,8 @@ typedef enum {
     TM_E_ALIGN = -2,       /* aligned = 1 but the promise is broken, or a 16-byte vector variant was
                               asked for on data whose rows are not 16-byte aligned */
     TM_E_UNSUPPORTED = -3, /* positive tile extent outside the compiled menu */
-    TM_E_WORKSPACE = -4,   /* colsum workspace NULL or smaller than tm_colsum_workspace_bytes() */
+    TM_E_WORKSPACE = -4,   /* workspace NULL or smaller than tm_colsum_workspace_bytes() /
+                              tm_rows_workspace_bytes() */
     TM_E_HIP = -5          /* the HIP runtime refused the launch */
 } tm_status;
 
@@ -135,7 +136,8 @@ int tm_channel_affine(const float *x, int64_t ldx, const float *scale, const flo
  * for; the column tiles a row is walked in, the lanes per row and the slabs and strips of the
  * column walk are the library's choice, set from M, N and the row alignment.  The choice decides
  * the order of floating-point additions (within the stated bounds), never a maximum.  A row is
- * walked by one workgroup at most, so a handful of very long rows cannot use the whole GPU. */
+ * walked by one workgroup at most, so a handful of very long rows cannot use the whole GPU; the
+ * *_ws variants below take a workspace and split such rows across workgroups. */
 
 /* out[i] = sum over j < N of x[i,j] for i < M (out: M floats, contiguous).  Rows are walked with
  * coalesced loads (16-byte when the rows start on 16-byte boundaries) in column tiles: whole tiles
@@ -184,6 +186,37 @@ int tm_rowmax_masked(const float *s, int64_t lds, float *out, int64_t M, int64_t
  * BR, BC, aligned and the score contract are those of tm_rowmax_masked. */
 int tm_softmax_stats(const float *s, int64_t lds, float *m, float *l, int64_t M, int64_t N,
                      int BR, int BC, int aligned, void *stream);
+
+/* ---- row reductions over a few long rows ----------------------------------------------------
+ * tm_rowsum_ws, tm_rowmax_masked_ws and tm_softmax_stats_ws compute exactly what tm_rowsum,
+ * tm_rowmax_masked and tm_softmax_stats compute, under the same contracts and bounds (maxima bit
+ * for bit), and take a device workspace.  With fewer than 128 rows of at least 98304 elements, each
+ * row is cut into segments of 1024 * K elements (K = 1, 2, 4, 8 or 16, chosen for about 2048
+ * segments in all) that separate workgroups walk, each writing its segment's partial (sum,
+ * maximum, or the pair (m, l) of [SLICING] "Reductions over a ragged tile" over the segment's live
+ * columns) into the workspace; a second launch combines each row's partials in segment order
+ * (for the softmax pair: m = max m_s, l = sum l_s * exp(m_s - m)).  Both are fixed-order folds, so
+ * results are deterministic.  For other shapes the call is the one-pass call and the workspace is
+ * not touched.  One row of 2^23 floats takes about 11 us this way and 0.58 ms in one pass. */
+
+/* Bytes of device workspace the *_ws row calls need for M rows of N elements: 8 * M * (segments
+ * per row) when rows are split, else 0 (also 0 for invalid extents, which the calls reject). */
+size_t tm_rows_workspace_bytes(int64_t M, int64_t N);
+
+/* tm_rowsum with a workspace: ws is caller-owned device memory of ws_bytes >=
+ * tm_rows_workspace_bytes(M, N) bytes, 4-byte aligned (may be NULL when that is 0); contents on
+ * entry are ignored and on return unspecified.  A missing or short workspace returns
+ * TM_E_WORKSPACE (checked after the tile, before the promise). */
+int tm_rowsum_ws(const float *x, int64_t ldx, float *out, int64_t M, int64_t N,
+                 int TM, int TN, int aligned, void *ws, size_t ws_bytes, void *stream);
+
+/* tm_rowmax_masked with a workspace (ws as for tm_rowsum_ws). */
+int tm_rowmax_masked_ws(const float *s, int64_t lds, float *out, int64_t M, int64_t N,
+                        int BR, int BC, int aligned, void *ws, size_t ws_bytes, void *stream);
+
+/* tm_softmax_stats with a workspace (ws as for tm_rowsum_ws). */
+int tm_softmax_stats_ws(const float *s, int64_t lds, float *m, float *l, int64_t M, int64_t N,
+                        int BR, int BC, int aligned, void *ws, size_t ws_bytes, void *stream);
 
 /* ---- layout conversion ----------------------------------------------------------------------- */
 

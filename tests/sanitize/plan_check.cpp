@@ -9,7 +9,8 @@
 //    chunk), and on the aligned path (no masks) every chunk lies wholly inside the view;
 //  * transpose: every staged sub-tile of every batch is visited by exactly one work item, with the
 //    work-item number split by the plan's multiply-high divisors (checked against plain division).
-// Row and column reduction plans are checked for their documented invariants.
+// Row and column reduction plans are checked for their documented invariants, and the split row
+// walk's segments and chunks are replayed.
 //
 // The replay restates the mapping the kernels document (map.hip: work item -> tile row pm, row
 // strip, tile group gi, tile groups fastest; chunk q -> row q >> log_gv, tile (q & gv_mask) >>
@@ -291,10 +292,72 @@ static void check_reductions() {
                     }
 }
 
+// Split row walks (the calls with a workspace): the segments of a row cover its N columns once,
+// each segment's chunks (C per thread at a stride of the workgroup's width, as row_split_partial
+// documents) cover the segment once, and the workspace holds M * segs partials.
+static void check_split_rows() {
+    const int64_t Ms[] = {1, 2, 7, 63, 127, 128, 300};
+    const int64_t Ns[] = {1000, 65536, 98303, 98304, 98305, 262144, (int64_t{1} << 23) + 3, int64_t{1} << 30};
+    for (int64_t M : Ms)
+        for (int64_t N : Ns)
+            for (uintptr_t base : {uintptr_t{0x100000}, uintptr_t{0x100004}})
+                for (int op : {int(tmp::kRowSum), int(tmp::kRowMax), int(tmp::kRowSoftmax)}) {
+                    tmp::RowPlan p;
+                    float *o = const_cast<float *>(fake(0x200000));
+                    float *ws = const_cast<float *>(fake(0x400000));
+                    const size_t wsb = tmp::rows_ws_bytes(M, N);
+                    const int64_t ld = N + (N & 1);
+                    const int st = tmp::plan_rows(op, fake(base), ld, o, M, N, 1, 1, 0, &p,
+                                                  op == tmp::kRowSoftmax ? o + 4096 : nullptr, true, ws, wsb);
+                    CHECK(st == TM_OK, "split rows status %d M=%ld N=%ld", st, long(M), long(N));
+                    const bool want_split = M < tmp::kRowSplitRows && N >= tmp::kRowSplitMinN;
+                    CHECK(p.split == want_split, "split chosen %d for M=%ld N=%ld", int(p.split), long(M), long(N));
+                    CHECK(want_split == (wsb > 0), "workspace %zu for M=%ld N=%ld", wsb, long(M), long(N));
+                    ++g_checked;
+                    if (!p.split)
+                        continue;
+                    CHECK(p.log_k >= 0 && p.log_k <= tmp::kRowSegMaxLogK, "log_k %d", p.log_k);
+                    CHECK(p.seg == (int64_t{tmp::kRowSegUnit} << p.log_k), "seg %ld", long(p.seg));
+                    CHECK(int64_t(p.segs) * p.seg >= N && (int64_t(p.segs) - 1) * p.seg < N, "segs %u", p.segs);
+                    CHECK(p.nwork == uint64_t(M) * p.segs, "nwork %u", p.nwork);
+                    CHECK(p.grid == (p.nwork < (1u << 20) ? p.nwork : (1u << 20)), "grid %u", p.grid);
+                    CHECK(uint64_t(M) * p.segs * tmp::kRowPartialBytes <= wsb, "workspace too small");
+                    CHECK(p.vec == (base % 16 == 0 && (M <= 1 || ld % 4 == 0)), "vec %d", int(p.vec));
+                    CHECK(p.ws == ws && p.block == tmp::kBlock, "ws / block");
+                    // Fewer segments would do only with K = 16 (the largest) or when the target is met.
+                    CHECK(p.log_k == tmp::kRowSegMaxLogK || int64_t(p.segs) * M >= tmp::kRowSplitTarget / 2 ||
+                              p.log_k == 0,
+                          "K too small: log_k %d segs %u", p.log_k, p.segs);
+                    // one segment's columns: thread t, chunk c -> t * W + c * kBlock * W, W wide
+                    const int W = p.vec ? 4 : 1;
+                    const int C = tmp::kRowSegUnit / tmp::kBlock * (1 << p.log_k) / W;
+                    std::vector<uint8_t> hit(size_t(p.seg), 0);
+                    for (int t = 0; t < tmp::kBlock; ++t)
+                        for (int c = 0; c < C; ++c)
+                            for (int i = 0; i < W; ++i)
+                                ++hit[size_t(int64_t(t) * W + int64_t(c) * tmp::kBlock * W + i)];
+                    bool once = true;
+                    for (uint8_t h : hit)
+                        once = once && h == 1;
+                    CHECK(once, "segment chunks do not cover the segment once (seg %ld)", long(p.seg));
+                    if (wsb >= 4) {
+                        const int st2 = tmp::plan_rows(op, fake(base), ld, o, M, N, 1, 1, 0, &p,
+                                                       op == tmp::kRowSoftmax ? o + 4096 : nullptr, true, ws,
+                                                       wsb - 4);
+                        CHECK(st2 == TM_E_WORKSPACE, "rows short workspace accepted (st %d)", st2);
+                    }
+                    tmp::RowPlan q;
+                    tmp::plan_rows(op, fake(base), ld, o, M, N, 1, 1, 0, &q,
+                                   op == tmp::kRowSoftmax ? o + 4096 : nullptr);
+                    CHECK(!q.split, "a call without a workspace was split");
+                }
+}
+
 int main() {
     check_maps();
     check_transposes();
     check_reductions();
+    check_split_rows();
     std::printf("plan_check: %ld plans checked, %ld failures\n", g_checked, g_failed);
     return g_failed == 0 ? 0 : 1;
 }

@@ -267,6 +267,38 @@ def test_colsum_workspace_and_errors():
 
 
 @no_gpu
+def test_rows_workspace_and_errors():
+    W = tm.tm_rows_workspace_bytes
+    # fewer than 128 rows of at least 98304 elements are split; K sized for about 2048 segments
+    assert W(1, 1 << 23) == 1 * 2048 * 8        # K = 4: segments of 4096
+    assert W(8, 1 << 18) == 8 * 256 * 8         # K = 1: segments of 1024
+    assert W(63, 98304) == 63 * 48 * 8          # K = 2
+    assert W(127, 1 << 20) == 127 * 64 * 8      # K = 16
+    assert W(1, 98305) == 97 * 8                # a ragged last segment
+    assert W(2, 1 << 30) == 2 * 65536 * 8       # K = 16 at most
+    assert W(128, 1 << 20) == 0                 # enough rows: one pass
+    assert W(8, 98303) == 0
+    assert W(0, 1 << 20) == 0
+    assert W(-1, 1 << 20) == 0
+    assert W(8, -5) == 0
+    M, N = 8, 1 << 18
+    need = W(M, N)
+    for f in (tm.tm_rowsum_ws, tm.tm_rowmax_masked_ws):
+        assert f(A16, N, B16, M, N, 4, 256, 1, 0, need, S) == tm.TM_E_WORKSPACE
+        assert f(A16, N, B16, M, N, 4, 256, 1, A16, need - 1, S) == tm.TM_E_WORKSPACE
+        assert f(A16, N, B16, M, N, 4, 256, 1, A16 + 2, need, S) == tm.TM_E_WORKSPACE
+        assert f(A16, N, B16, M, N, 4, 48, 1, 0, 0, S) == tm.TM_E_UNSUPPORTED   # tile before workspace
+        assert f(A16, N - 1, B16, M, N, 4, 256, 1, 0, 0, S) == tm.TM_E_INVAL    # ld < N first
+        assert f(A16, N + 2, B16, M, N, 4, 256, 1, 0, 0, S) == tm.TM_E_WORKSPACE  # before ALIGN
+        assert f(A16, N + 2, B16, M, N, 4, 256, 1, A16, need, S) == tm.TM_E_ALIGN
+        assert f(A16, N, 0, 0, N, 4, 256, 0, 0, 0, S) == tm.TM_OK              # empty output
+    f = tm.tm_softmax_stats_ws
+    assert f(A16, N, B16, 0, M, N, 4, 256, 0, A16, need, S) == tm.TM_E_INVAL    # NULL l
+    assert f(A16, N, B16, B16 + 64, M, N, 4, 256, 0, 0, need, S) == tm.TM_E_WORKSPACE
+    assert f(A16, N, B16, B16 + 64, M, N, 4, 256, 1, A16, 16, S) == tm.TM_E_WORKSPACE
+
+
+@no_gpu
 def test_transpose_errors():
     f = tm.tm_transpose
     # x: 64 x 128 (ldx 128), y: 128 x 64 (ldy 64)
