@@ -283,6 +283,53 @@ def test_fuzz_long_rows(dev):
         assert O.guards_intact()
 
 
+def test_fuzz_split_rows(dev):
+    """The row calls with a workspace on random shapes around the split rule (M from 1 to 200,
+    N from 60000 to 600000, at most 12M elements): split and one-pass walks, 16-byte and 4-byte
+    rows, random strides, base offsets and tiles; a workspace of exactly the reported size between
+    guard bands."""
+    rng = random.Random(79)
+    for case in range(40):
+        kind = rng.choice(["rowsum", "rowmax", "softmax"])
+        N = int(60000 * 10 ** rng.random())                          # log-uniform
+        M = max(1, int(min(200, 12_000_000 // N) ** rng.random()))   # log-uniform from 1
+        ld = N + rng.choice([0, 0, 0, 4, 1, 3])
+        off = rng.choice([0, 0, 0, 1])
+        TM, TN = rng.choice(TMS), rng.choice(TNS)
+        wsb = tm.tm_rows_workspace_bytes(M, N)
+        note("fuzz split rows %d: %s M=%d N=%d ld=%d off=%d tile=%dx%d ws=%d" % (case, kind, M, N, ld, off,
+                                                                                TM, TN, wsb))
+        n = (M - 1) * ld + N
+        lo, hi = (0.0, 1.0) if kind == "rowsum" else (-10.0, -1.0)
+        xh = inputs.uniform(950 + case, n, lo, hi)
+        X = Guarded(n, dev, off)
+        X.upload(xh)
+        O = Guarded(M, dev)
+        W = Guarded(max(wsb // 4, 1), dev)
+        if kind == "rowsum":
+            st = tm.tm_rowsum_ws(X.ptr, ld, O.ptr, M, N, TM, TN, 0, W.ptr, wsb)
+        elif kind == "rowmax":
+            st = tm.tm_rowmax_masked_ws(X.ptr, ld, O.ptr, M, N, TM, TN, 0, W.ptr, wsb)
+        else:
+            L = Guarded(M, dev)
+            st = tm.tm_softmax_stats_ws(X.ptr, ld, O.ptr, L.ptr, M, N, TM, TN, 0, W.ptr, wsb)
+        assert st == tm.TM_OK, tm.tm_status_string(st)
+        torch.cuda.synchronize()
+        got = O.payload().cpu().numpy()
+        if kind == "rowsum":
+            ref = oracle.rowsum_f64(xh, ld, M, N)
+            assert (np.abs(got.astype(np.float64) - ref) <= sum_tol(ref)).all(), "case %d" % case
+        elif kind == "rowmax":
+            assert np.array_equal(bits(got), bits(oracle.rowmax(xh, ld, M, N))), "case %d" % case
+        else:
+            m_ref, l_ref = oracle.softmax_stats(xh, ld, M, N)
+            assert np.array_equal(bits(got), bits(m_ref)), "case %d" % case
+            l = L.payload().cpu().numpy().astype(np.float64)
+            assert (np.abs(l - l_ref) <= 1e-5 * l_ref).all(), "case %d" % case
+            assert L.guards_intact()
+        assert O.guards_intact() and W.guards_intact()
+
+
 def test_fuzz_transposes(dev):
     rng = random.Random(5150)
     ok = 0

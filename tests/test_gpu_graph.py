@@ -79,6 +79,39 @@ def test_captured_sequence_replays(dev):
         assert torch.equal(other["y"].view(torch.int32), want["y"].view(torch.int32))
 
 
+def test_captured_split_rows_replay(dev):
+    """The split softmax statistics (two launches sharing a workspace) captured into a graph:
+    every replay reproduces the eager m and l bit for bit."""
+    M, N = 8, 1 << 17
+    s = torch.from_numpy(inputs.uniform(44, M * N, -10.0, -1.0)).to(dev)
+    wsb = tm.tm_rows_workspace_bytes(M, N)
+    assert wsb > 0
+    ws = torch.empty(wsb // 4, device=dev)
+    m0, l0 = torch.empty(M, device=dev), torch.empty(M, device=dev)
+    tm.check(tm.tm_softmax_stats_ws(s, N, m0, l0, M, N, 1, 64, 0, ws, wsb))
+    torch.cuda.synchronize()
+    m, l = torch.empty(M, device=dev), torch.empty(M, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        tm.check(tm.tm_softmax_stats_ws(s, N, m, l, M, N, 1, 64, 0, ws, wsb))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tm.check(tm.tm_softmax_stats_ws(s, N, m, l, M, N, 1, 64, 0, ws, wsb))
+    for replay in range(4):
+        note("split rows graph replay %d" % replay)
+        m.fill_(-7.0)
+        l.fill_(-7.0)
+        ws.fill_(3.0)                # stale partials must be overwritten
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(m.view(torch.int32), m0.view(torch.int32)), replay
+        assert torch.equal(l.view(torch.int32), l0.view(torch.int32)), replay
+
+
 def test_threads_on_separate_streams(dev):
     """Four host threads, each with its own stream and buffers, run the sequence ten times at
     once; every thread's results equal the single-threaded ones (the library keeps no shared
