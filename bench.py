@@ -20,7 +20,8 @@ The same JSON line carries
                 ragged 4100 x 1000 map, row and column sums (naive and LDS walks), the masked
                 row max, the softmax row statistics (also over 8 rows of 2^18, in one pass and
                 split with a workspace), the per-channel bias add, a tile-size sweep
-                and the transpose / NCHW -> NHWC conversion.
+                and the transpose / NCHW -> NHWC conversion (64 channels, and 3 channels both
+                ways).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--paths all|none] [--cpu-seconds S]
 """
@@ -518,6 +519,20 @@ def transpose_paths(torch, tm, inputs, dev, stream, timed, ok):
     timed("nchw_to_nhwc_32x64x56x56", nb, R,
           lambda i: ok(tm.tm_transpose(xs[i], HW, C * HW, ys[i], C, HW * C, B, C, HW, 64, 64, 1, stream)),
           "batched transpose [B][C][HW] -> [B][HW][C]")
+    del xs, ys
+    # three channels (RGB images, 32 x 3 x 224 x 224) both ways: narrow 4 x 256 sub-tiles
+    B, C, HW = 32, 3, 224 * 224
+    xh = inputs.uniform(8, B * C * HW, -1.0, 1.0)
+    nb = 2 * B * C * HW * 4
+    R = sets_for(nb)
+    xs = rotated(torch, xh, R, dev)
+    ys = [torch.empty_like(x) for x in xs]
+    timed("nchw_to_nhwc_32x3x224x224", nb, R,
+          lambda i: ok(tm.tm_transpose(xs[i], HW, C * HW, ys[i], C, HW * C, B, C, HW, 1, 64, 0, stream)),
+          "batched transpose [B][3][HW] -> [B][HW][3], ragged path, 4-byte chunks")
+    timed("nhwc_to_nchw_32x3x224x224", nb, R,
+          lambda i: ok(tm.tm_transpose(xs[i], C, HW * C, ys[i], HW, C * HW, B, HW, C, 64, 1, 0, stream)),
+          "batched transpose [B][HW][3] -> [B][3][HW], ragged path, 4-byte chunks")
     del xs, ys
 
 

@@ -590,18 +590,27 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     plan->launch = true;
     plan->vec = vec;
     plan->aligned = aligned;
-    // Staged sub-tiles: kTrSub x kTrSub, except that under the promise they must divide the
-    // extents (whole sub-tiles, no masks): then the largest power of two up to kTrSub that
-    // divides M (resp. N), which the promised tile divides.
-    auto sub = [&](int64_t extent) {
-        int e = kTrSub;
+    // Staged sub-tiles: kTrSub x kTrSub.  A narrow extent (fewer than kTrSub rows or columns, as
+    // the 3 channels of an RGB image) gets a sub-tile just as narrow and as much longer, up to
+    // kTrSubElems elements, so that no lanes are spent on rows or columns that do not exist.
+    // Under the promise a sub-tile must divide the extents (whole sub-tiles, no masks): the
+    // largest power of two up to the cap that divides the extent, which the promised tile
+    // divides.  16-byte chunks need both sub-tile extents to be at least 4.
+    const int64_t lo = vec ? 4 : 1;
+    auto fit = [&](int64_t extent, int64_t cap) {
+        int64_t e = aligned ? cap : std::min<int64_t>(cap, int64_t{1} << ilog2(extent));
         if (aligned)
             while (extent % e != 0)
                 e /= 2;
-        return e;
+        return static_cast<int>(std::max(e, lo));
     };
-    plan->sm = sub(M);
-    plan->sn = sub(N);
+    if (N < kTrSub && M >= kTrSub) {  // narrow rows of x: long along M
+        plan->sn = fit(N, kTrSub);
+        plan->sm = fit(M, kTrSubElems / plan->sn);
+    } else {
+        plan->sm = fit(M, kTrSub);
+        plan->sn = fit(N, kTrSubElems / plan->sm);
+    }
     const int64_t subs_m = ceil_div(M, plan->sm), subs_n = ceil_div(N, plan->sn);
     if (subs_m > INT32_MAX || subs_n > INT32_MAX)
         return TM_E_UNSUPPORTED;

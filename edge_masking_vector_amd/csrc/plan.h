@@ -23,7 +23,9 @@ constexpr int kLineBytes = 128;     // cache line
 constexpr int kRowSegmentBytes = 512;  // map work items: bytes of each row they move, at least ...
 constexpr int kStreamSegmentBytes = 1024;  // ... or one row segment of this many bytes, moved
                                            // with device-scope streaming buffer accesses
-constexpr int kTrSub = 32;          // transpose: largest staged sub-tile edge (one 128-byte line of f32)
+constexpr int kTrSub = 32;          // transpose: staged sub-tile edge (one 128-byte line of f32) ...
+constexpr int kTrSubElems = kTrSub * kTrSub;  // ... and elements; a narrow tensor's sub-tile is
+                                              // narrower and longer (up to kTrSubElems long)
 // Row reductions: rows of at most kTinyRowChunks 16-byte chunks are walked as one tile with
 // about 4 chunks per lane, longer ones with about 8 per lane per pass; rows of more than
 // kShortRowChunks* chunks are long: one wave each ...
@@ -168,7 +170,7 @@ struct TransposePlan {
     bool launch = false;
     bool vec = false;             // 16-byte chunks on both sides
     int aligned = 0;
-    int sm = 1, sn = 1;           // staged sub-tile extents (powers of two <= kTrSub)
+    int sm = 1, sn = 1;           // staged sub-tile extents (powers of two, sm * sn <= kTrSubElems)
     uint32_t subs_m = 0, subs_n = 0;
     uint64_t nwork = 0;
     bool wide = false;            // nwork >= 2^32: 64-bit work-item arithmetic

@@ -9,7 +9,10 @@
 //
 // Mapping.  A workgroup (256 threads) takes one SM x SN sub-tile of x (32 x 32: a row segment is
 // one 128-byte line; under the alignment promise the largest power of two up to 32 that divides
-// the extent, which the caller's tile divides); sub-tiles are visited in diagonal order (see
+// the extent, which the caller's tile divides).  A narrow tensor -- fewer than 32 rows or columns,
+// as the 3 channels of an RGB image in NCHW -> NHWC -- gets a sub-tile just as narrow and as much
+// longer (4 x 256 for 3 channels), so that no lanes idle on rows that do not exist; sub-tiles
+// hold at most 1024 elements.  Sub-tiles are visited in diagonal order (see
 // below).  It reads the sub-tile along x's rows -- lanes take consecutive chunks of a row, so the
 // lane-varying term of the address is the column -- and stages it in LDS with a row stride of
 // SN + 1 floats.  After a barrier it reads the staged tile down its columns and writes y's rows,
@@ -29,8 +32,10 @@
 namespace tmk {
 namespace {
 
-constexpr int kSub = tmp::kTrSub;   // largest sub-tile edge
-constexpr int kPad = kSub + 1;      // LDS row stride (floats) of the staged sub-tile
+constexpr int kSubElems = tmp::kTrSubElems;  // largest sub-tile (elements)
+// LDS of the staged sub-tile: SM rows of stride SN + 1 floats, SM * SN <= kSubElems, so at most
+// 2 * kSubElems floats (SN = 1: 1024 rows of stride 2).
+constexpr int kStage = 2 * kSubElems;
 constexpr int kTrBlock = 256;       // threads per workgroup (one 16-byte chunk each per sub-tile)
 
 // Kernel arguments: kept within 128 bytes so that one batch of scalar loads fetches them all
@@ -44,7 +49,7 @@ struct TrArgs {
     uint64_t c_pb, c_m, c_n;         // multipliers of per_b, subs_m, subs_n for fast_div
     uint32_t subs_m, subs_n;         // sub-tiles along M and N per batch
     uint32_t per_b;                  // subs_m * subs_n (when the work count fits 32 bits)
-    int log_sm, log_sn;              // staged sub-tile extents: 2^log_sm x 2^log_sn (<= kSub)
+    int log_sm, log_sn;              // staged sub-tile extents: 2^log_sm x 2^log_sn (<= kSubElems)
 };
 static_assert(sizeof(TrArgs) <= 128, "transpose arguments outgrew one scalar load batch");
 
@@ -52,8 +57,8 @@ template <bool VEC, bool ALIGNED, int BS, bool WIDE>
 __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
     constexpr int LOG_W = VEC ? 2 : 0;
     constexpr int W = 1 << LOG_W;
-    constexpr int K = kSub * kSub / W / BS;   // chunks per thread for a full kSub x kSub sub-tile
-    __shared__ float tile[kSub * kPad];
+    constexpr int K = kSubElems / W / BS;     // chunks per thread for a full sub-tile
+    __shared__ float tile[kStage];
     const int t = threadIdx.x;
     // Sub-tile extents are powers of two of at least W elements: chunk coordinates are shifts
     // and masks (run-time divisions per chunk took the 4096 x 4096 transpose from 25.5 to 27.5 us).
@@ -61,6 +66,7 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
     const int lcy = a.log_sm - LOG_W;   // log2 of the chunks per y row
     const int nchunks = 1 << (a.log_sm + a.log_sn - LOG_W);
     const int sm = 1 << a.log_sm, sn = 1 << a.log_sn;
+    const int pad = sn + 1;             // LDS row stride: odd for SN >= 2, so columns spread over banks
 
     uint64_t w = blockIdx.x;
     do {
@@ -121,7 +127,7 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
             if (e < nchunks) {
 #pragma unroll
                 for (int i = 0; i < W; ++i)
-                    tile[r * kPad + c + i] = v[k][i];
+                    tile[r * pad + c + i] = v[k][i];
             }
         }
         __syncthreads();
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
             if (e < nchunks) {
 #pragma unroll
                 for (int q = 0; q < W; ++q)
-                    v[k][q] = tile[(i + q) * kPad + j];
+                    v[k][q] = tile[(i + q) * pad + j];
             }
         }
 #pragma unroll

@@ -16,6 +16,7 @@
 // strip, tile group gi, tile groups fastest; chunk q -> row q >> log_gv, tile (q & gv_mask) >>
 // log_vr, chunk q & vr_mask.  transpose.hip: work item -> batch, then diagonal order pm = rest %
 // subs_m, pn = (rest / subs_m + pm) % subs_n).  Exit status 0 when every check passes.
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -169,7 +170,19 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
     CHECK(p.subs_m == uint32_t((M + p.sm - 1) / p.sm) && p.subs_n == uint32_t((N + p.sn - 1) / p.sn),
           "%s sub-tile counts", tag);
     CHECK(p.nwork == uint64_t(B) * p.subs_m * p.subs_n && p.grid >= 1 && p.grid <= p.nwork, "%s work", tag);
-    CHECK(p.sm <= tmp::kTrSub && p.sn <= tmp::kTrSub, "%s sub-tile above %d", tag, tmp::kTrSub);
+    CHECK((p.sm & (p.sm - 1)) == 0 && (p.sn & (p.sn - 1)) == 0 && int64_t(p.sm) * p.sn <= tmp::kTrSubElems,
+          "%s sub-tile %dx%d above %d elements", tag, p.sm, p.sn, tmp::kTrSubElems);
+    // the staged sub-tile (rows of stride SN + 1 floats) fits the kernel's LDS of 2 * kTrSubElems
+    CHECK(int64_t(p.sm) * (p.sn + 1) <= 2 * tmp::kTrSubElems, "%s staged sub-tile exceeds LDS", tag);
+    // a narrow extent gets a narrow sub-tile (no sub-tile row or column is wholly outside the view,
+    // beyond the minimum of 4 that 16-byte chunks need)
+    auto p2 = [](int64_t v) { int64_t e = 1; while (e < v) e <<= 1; return e; };
+    if (!p.aligned) {
+        CHECK(p.sm <= std::max<int64_t>(p.vec ? 4 : 1, p2(M)) && p.sn <= std::max<int64_t>(p.vec ? 4 : 1, p2(N)),
+              "%s sub-tile %dx%d wider than the view", tag, p.sm, p.sn);
+        if (M >= tmp::kTrSub && N >= tmp::kTrSub)
+            CHECK(p.sm == tmp::kTrSub && p.sn == tmp::kTrSub, "%s wide view not on 32 x 32", tag);
+    }
     if (p.aligned)
         CHECK(M % p.sm == 0 && N % p.sn == 0, "%s promised sub-tiles are not whole", tag);
     if (p.vec)
@@ -203,8 +216,8 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
 
 static void check_transposes() {
     const int64_t Bs[] = {1, 3, 32};
-    const int64_t Ms[] = {1, 4, 24, 64, 100};
-    const int64_t Ns[] = {1, 5, 32, 100, 3136};
+    const int64_t Ms[] = {1, 2, 3, 4, 24, 64, 100, 50176};
+    const int64_t Ns[] = {1, 3, 5, 16, 32, 100, 3136};
     for (int64_t B : Bs)
         for (int64_t M : Ms)
             for (int64_t N : Ns)

@@ -89,6 +89,31 @@ def test_nchw_nhwc_ragged_channels(dev):
         check_transpose(dev, B, HW, C, C, HW, HW * C, C * HW, 32, 64, 0)
 
 
+@pytest.mark.parametrize("C", [1, 2, 3, 4, 8, 16, 31])
+def test_nchw_nhwc_few_channels(dev, C):
+    """Few channels (RGB images and the like): the sub-tile is as narrow as the channel count and
+    up to 1024 elements long.  Both directions at (4, C, 224, 224), ragged path with 4-byte or
+    16-byte chunks as the channel count allows, and the promised path where the tile keeps it."""
+    B, HW = 4, 224 * 224
+    note("few channels C=%d: NCHW -> NHWC, NHWC -> NCHW" % C)
+    check_transpose(dev, B, C, HW, HW, C, C * HW, HW * C, 1, 64, 0, seed=C)
+    check_transpose(dev, B, HW, C, C, HW, HW * C, C * HW, 64, 1, 0, seed=C + 100)
+    if C % 4 == 0:
+        check_transpose(dev, B, C, HW, HW, C, C * HW, HW * C, 4, 64, 1, seed=C + 200)
+        check_transpose(dev, B, HW, C, C, HW, HW * C, C * HW, 64, 4, 1, seed=C + 300)
+
+
+def test_transpose_narrow_edges(dev):
+    """Single rows and columns, narrow and ragged both ways, odd strides, misaligned bases."""
+    for (M, N, ldx, ldy, xoff, yoff) in ((1, 5000, 5000, 1, 0, 0), (5000, 1, 1, 5000, 0, 0),
+                                         (1, 5003, 5003, 4, 0, 0), (3, 7001, 7004, 3, 1, 0),
+                                         (7001, 3, 5, 7004, 0, 1), (2, 2, 3, 2, 0, 0),
+                                         (31, 999, 1000, 33, 0, 0), (999, 31, 31, 1000, 0, 0)):
+        note("narrow transpose M=%d N=%d ld=%d/%d off=%d/%d" % (M, N, ldx, ldy, xoff, yoff))
+        check_transpose(dev, 2, M, N, ldx, ldy, M * ldx + 3, N * ldy + 5, 64, 64, 0, xoff, yoff,
+                        seed=M + N)
+
+
 def test_transpose_padded_and_misaligned(dev):
     check_transpose(dev, 1, 300, 500, 503, 301, 0, 0, 64, 64, 0)           # odd strides: scalar
     check_transpose(dev, 1, 300, 500, 504, 304, 0, 0, 64, 64, 0)           # padded 16-byte rows
