@@ -16,12 +16,11 @@ The same JSON line carries
                 same leg checks the timed kernel's output against the oracle's, bit for bit;
   paths         every other path of the method, each on its own workload shape and timed the
                 same way: the ragged path on the same shape, the three 1-D access variants and
-                the 1-D ragged path, the
-                ragged 4100 x 1000 map, row and column sums (naive and LDS walks), the masked
-                row max, the softmax row statistics (also over 8 rows of 2^18, in one pass and
-                split with a workspace), the per-channel bias add, a tile-size sweep
-                and the transpose / NCHW -> NHWC conversion (64 channels, and 3 channels both
-                ways).
+                the 1-D ragged path, the ragged 4100 x 1000 map, row and column sums (naive and
+                LDS walks; the LDS walk's one-pass form on 16 x 2^20), the masked row max, the
+                softmax row statistics (also over 8 rows of 2^18, in one pass and split with a
+                workspace), the per-channel bias add, a tile-size sweep and the transpose /
+                NCHW -> NHWC conversion (64 channels, and 3 channels both ways).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--paths all|none] [--cpu-seconds S]
 """
@@ -375,6 +374,17 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     reads_only = {k: round(gbs(M * N * 4, out[k]["mean_us"] * 1e-6), 1)
                   for k in ("rowsum_4096", "colsum_naive_4096", "colsum_naive_xcd_4096", "colsum_lds_4096")}
     out["reads_only_gbs_4096"] = reads_only
+    del xs, outs
+    # column sums of a short, wide matrix (16 x 2^20): the LDS walk's one-pass form
+    M, N = 16, 1 << 20
+    xh = inputs.uniform(11, M * N, 0.0, 1.0)
+    R = sets_for(M * N * 4)
+    xs = rotated(torch, xh, R, dev)
+    outs = [torch.empty(N, device=dev) for _ in range(R)]
+    assert tm.tm_colsum_workspace_bytes(M, N, 16, 64, tm.TM_COL_LDS) == 0
+    timed("colsum_lds_16x1048576", M * N * 4 + N * 4, R,
+          lambda i: ok(tm.tm_colsum(xs[i], N, outs[i], M, N, 16, 64, 1, tm.TM_COL_LDS, None, 0, stream)),
+          "one pass: each thread adds a 16-byte column chunk down the 16 rows (no workspace)")
     del xs, outs
 
     # masked row max: 8192 x 1000 ragged (15 whole 64-column tiles + 40), aligned 8192 x 1024

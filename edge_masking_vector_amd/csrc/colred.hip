@@ -36,10 +36,12 @@ namespace {
 struct ColArgs {
     const float *x;
     float *ws;
+    float *out;       // direct walk: the column sums
     int64_t ld, M, N;
     int log_tm;
     uint32_t strips;  // LDS walk: strips of TW columns; naive walk: N
     uint32_t slabs;
+    int out16;        // direct walk: out is 16-byte aligned
 };
 
 // ---- naive walk ------------------------------------------------------------------------------
@@ -177,6 +179,54 @@ __global__ __launch_bounds__(kBlock) void col_lds(ColArgs a) {
     }
 }
 
+// ---- direct walk ---------------------------------------------------------------------------------
+// For few rows, or columns enough to fill the GPU by themselves: each thread owns one chunk of W
+// columns and adds all M rows down it -- kRowsInFlight coalesced loads at a time (consecutive
+// threads on consecutive chunks of a row) into kColAcc accumulators -- then folds the
+// accumulators in a fixed order and stores the W sums.  One pass: no partials, no pass 2.
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void col_direct(ColArgs a) {
+    using T = typename std::conditional<VEC, f4, float>::type;
+    constexpr int W = VEC ? 4 : 1;
+    const int64_t nchunks = (a.N + W - 1) / W;
+    for (int64_t q = int64_t(blockIdx.x) * kBlock + threadIdx.x; q < nchunks;
+         q += int64_t(gridDim.x) * kBlock) {
+        const int64_t c = q * W;
+        const int64_t live = a.N - c;  // columns of this chunk inside the tensor
+        const float *p = a.x + c;
+        T acc[kColAcc];
+#pragma unroll
+        for (int u = 0; u < kColAcc; ++u)
+            acc[u] = T(0.0f);
+        for (int64_t r = 0; r < a.M; r += kRowsInFlight) {
+            T v[kRowsInFlight];
+#pragma unroll
+            for (int u = 0; u < kRowsInFlight; ++u)
+                v[u] = r + u < a.M ? chunk_or_zero<VEC>(p + (r + u) * a.ld, live) : T(0.0f);
+#pragma unroll
+            for (int u = 0; u < kRowsInFlight; ++u)
+                acc[u % kColAcc] += v[u];
+        }
+        const T s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+        float *o = a.out + c;
+        if constexpr (VEC) {
+            if (live >= 4 && a.out16) {
+                *reinterpret_cast<f4 *>(o) = s;
+            } else {
+                o[0] = s.x;
+                if (live > 1)
+                    o[1] = s.y;
+                if (live > 2)
+                    o[2] = s.z;
+                if (live > 3)
+                    o[3] = s.w;
+            }
+        } else {
+            *o = s;
+        }
+    }
+}
+
 // ---- pass 2: fixed-order sum of the slab partials ---------------------------------------------
 
 constexpr int kFinishBatch = 16;   // partials loaded at once per lane, then added in slab order
@@ -244,10 +294,32 @@ const void *pick_lpr(int lpr) {
 
 hipError_t launch_cols(const tmp::ColPlan &p, hipStream_t stream) {
     constexpr uint32_t kGridCap = 1u << 20;
+    if (p.direct) {
+        ColArgs a;
+        a.x = p.x;
+        a.ws = nullptr;
+        a.out = p.out;
+        a.ld = p.ld;
+        a.M = p.M;
+        a.N = p.N;
+        a.log_tm = 0;
+        a.strips = 0;
+        a.slabs = 0;
+        a.out16 = p.out16 ? 1 : 0;
+        void *args[] = {&a};
+        const int64_t nchunks = (p.N + (p.vec ? 3 : 0)) / (p.vec ? 4 : 1);
+        const int64_t blocks = (nchunks + kBlock - 1) / kBlock;
+        const uint32_t grid = static_cast<uint32_t>(blocks < kGridCap ? blocks : kGridCap);
+        const void *fn = p.vec ? reinterpret_cast<const void *>(&col_direct<true>)
+                               : reinterpret_cast<const void *>(&col_direct<false>);
+        return hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, stream);
+    }
     if (p.launch) {
         ColArgs a;
         a.x = p.x;
         a.ws = p.ws;
+        a.out = p.out;
+        a.out16 = 0;
         a.ld = p.ld;
         a.M = p.M;
         a.N = p.N;

@@ -53,6 +53,11 @@ constexpr int64_t kColMaxSlabs = 4096;
 constexpr int kColStrip = 128;
 // Column-sum pass 2: lanes per column chosen so that about this many threads run.
 constexpr int kFinishThreads = 16384;
+// The LDS walk goes direct (one thread per 16-byte column chunk down all rows, one pass) for at
+// most kColDirectRows rows, or at most kColDirectRowsWide rows of at least kColDirectMinN columns.
+constexpr int64_t kColDirectRows = 64;
+constexpr int64_t kColDirectRowsWide = 256;
+constexpr int64_t kColDirectMinN = int64_t{1} << 18;
 
 enum MapOp { kAffine = 0, kScale = 1, kCopy = 2, kChannel = 3 };
 enum Access { kScalar = 1, kVec4Understated = 2, kVec4 = 3 };
@@ -140,6 +145,8 @@ struct ColPlan {
     int log_tm = 0;               // rows per slab: the caller's TM (naive walks) or the LDS walk's own
     int tw = 1;                   // columns per workgroup (LDS walk)
     bool whole = false;           // LDS walk: whole slabs and strips with 16-byte rows (no masks)
+    bool direct = false;          // LDS walk over few rows or many columns: one pass, no partials
+    bool out16 = false;           // direct walk: out is 16-byte aligned
     int fl = 1;                   // pass 2: lanes per column (power of two <= 64)
     int naive_block = 64;         // threads per workgroup (naive walk)
     uint32_t slabs = 0;           // ceil(M / rows per slab): partials per column
@@ -150,6 +157,7 @@ struct ColPlan {
     int64_t ld = 0, M = 0, N = 0;
 };
 
+bool col_direct(int64_t M, int64_t N, int walk);
 size_t colsum_ws_bytes(int64_t M, int64_t N, int TM, int TN, int walk);
 
 int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TM, int TN,

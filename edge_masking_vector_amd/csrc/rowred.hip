@@ -34,6 +34,8 @@ struct RowArgs {
     int64_t bc;         // column tile width
     int per_tile;       // chunks per lane per column tile
     uint32_t ngroups;   // row groups of kBlock / LPR rows
+    uint64_t nf_c;      // multiply-high divisor of nfull (0: nfull too large, 64-bit modulo)
+    uint32_t nf_d;
 };
 
 constexpr int kLoads = 8;   // chunks in flight per lane
@@ -88,6 +90,18 @@ __device__ __forceinline__ auto load_fill(const float *p, int64_t live) {
     } else {
         return live > 0 ? *p : Op::kFill;
     }
+}
+
+// First whole tile of row group grp in the rotated walk: 7 * grp mod nfull, by multiply-high
+// division (exact: fast_mod(grp) * 7 stays below 2^32 for the divisors the host passes).  A 64-bit
+// modulo costs about a hundred scalar instructions, paid by every row group before its first
+// load: it took 16M one-element row sums to 49 us.
+__device__ __forceinline__ int64_t first_tile(uint32_t grp, const RowArgs &a) {
+    if (a.nfull <= 1)
+        return 0;
+    if (a.nf_c != 0)
+        return fast_mod(fast_mod(grp, a.nf_c, a.nf_d) * 7u, a.nf_c, a.nf_d);
+    return static_cast<int64_t>(uint64_t(grp) * 7u % uint64_t(a.nfull));
 }
 
 // Threads per workgroup for LPR lanes per row: kBlock (several rows), or LPR (one row).
@@ -155,7 +169,7 @@ __global__ __launch_bounds__(block_threads<LPR>()) void row_reduce(RowArgs a) {
         // row pitch is a multiple of 4 KiB, workgroups that all walked the tiles in the same order
         // would hit the same HBM channels at the same time.
         const int64_t main_chunks = a.nfull * a.per_tile;
-        const int64_t start = a.nfull > 0 ? (int64_t(grp) * 7 % a.nfull) * a.per_tile : 0;
+        const int64_t start = first_tile(grp, a) * a.per_tile;
         for (int64_t k = 0; k < main_chunks; k += kLoads) {
             T v[kLoads];
 #pragma unroll
@@ -255,7 +269,7 @@ __global__ __launch_bounds__(block_threads<LPR>()) void row_softmax(RowArgs a) {
 
         // Whole tiles, in the rotated order of row_reduce; no masks.
         const int64_t main_chunks = a.nfull * a.per_tile;
-        const int64_t start = a.nfull > 0 ? (int64_t(grp) * 7 % a.nfull) * a.per_tile : 0;
+        const int64_t start = first_tile(grp, a) * a.per_tile;
         for (int64_t k = 0; k < main_chunks; k += kLoads) {
             T v[kLoads];
 #pragma unroll
@@ -541,6 +555,11 @@ hipError_t launch_rows(const tmp::RowPlan &p, hipStream_t stream) {
     a.per_tile = p.per_tile;
     const int64_t rows_per_wg = p.block / p.lpr;
     a.ngroups = static_cast<uint32_t>((p.M + rows_per_wg - 1) / rows_per_wg);
+    // 7 * (grp mod nfull) < 2^32 keeps the two-step multiply-high modulo exact
+    const bool small = p.nfull > 1 && p.nfull < int64_t{0xFFFFFFFF} / 7;
+    const tmp::Div32 nf = small ? tmp::make_div32(static_cast<uint32_t>(p.nfull)) : tmp::Div32{};
+    a.nf_c = small ? nf.c : 0;
+    a.nf_d = nf.d;
     const bool pre = p.rem > 0 && p.per_tile <= kRemPrefetch;
     const void *fn = pre ? pick_op<true>(p) : pick_op<false>(p);
     void *args[] = {&a};

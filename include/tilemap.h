@@ -151,12 +151,15 @@ int tm_rowsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t N,
 /* Bytes of device workspace tm_colsum needs for these arguments (0 when M == 0 or N == 0, and
  * also 0 for invalid arguments, which tm_colsum then rejects): 4 * N * (number of row slabs), where
  * a slab is TM rows for the naive walks and 256 rows for the LDS walk (taller, doubling, while
- * there would be more than 4096 slabs). */
+ * there would be more than 4096 slabs); 0 when the LDS walk takes its one-pass form (at most 64
+ * rows, or at most 256 rows of at least 262144 columns: each thread adds one 16-byte column chunk
+ * down all M rows and writes the sums, so there are no partials). */
 size_t tm_colsum_workspace_bytes(int64_t M, int64_t N, int TM, int TN, int walk);
 
 /* out[j] = sum over i < M of x[i,j] for j < N (out: N floats, contiguous).  Two passes: pass 1 writes
  * one partial per (row slab, column) into `ws`; pass 2 adds each column's partials in a fixed
- * order, so the result is deterministic (no atomics).  walk: tm_colwalk.  ws: caller-owned
+ * order, so the result is deterministic (no atomics).  (The LDS walk over few rows is one pass in
+ * a fixed order down each column and needs no workspace; ws may then be NULL.)  walk: tm_colwalk.  ws: caller-owned
  * device workspace of ws_bytes >= tm_colsum_workspace_bytes(...) bytes (contents on entry are
  * ignored; on return they are unspecified).  Same accuracy bound as tm_rowsum, over the column.
  * aligned = 1 promises M % TM == 0, N % TN == 0 and 16-byte rows of x; the naive walk moves single

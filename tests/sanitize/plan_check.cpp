@@ -281,6 +281,11 @@ static void check_reductions() {
                                                           const_cast<float *>(fake(0x300000)), wsb, &c);
                             if (st != TM_OK)
                                 continue;
+                            CHECK(c.direct == (N > 0 && tmp::col_direct(M, N, walk)), "cols direct M=%ld N=%ld", long(M),
+                                  long(N));
+                            if (c.direct)
+                                CHECK(!c.launch && wsb == 0 && c.vec == (M <= 1 || ld % 4 == 0) && c.out16,
+                                      "cols direct plan M=%ld N=%ld", long(M), long(N));
                             if (c.launch) {
                                 const int64_t ts = int64_t{1} << c.log_tm;
                                 CHECK(c.slabs == uint32_t((M + ts - 1) / ts), "cols slabs");

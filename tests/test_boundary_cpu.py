@@ -249,6 +249,13 @@ def test_colsum_workspace_and_errors():
     assert W(4100, 1000, 64, 1, tm.TM_COL_NAIVE) == 65 * 1000 * 4
     assert W(1 << 21, 8, 256, 8, tm.TM_COL_LDS) == 4096 * 8 * 4
     assert W((1 << 21) + 1, 8, 256, 8, tm.TM_COL_LDS) == 2049 * 8 * 4
+    # the LDS walk's one-pass form needs no partials: at most 64 rows, or 256 rows of 2^18 columns
+    assert W(64, 1000, 64, 64, tm.TM_COL_LDS) == 0
+    assert W(64, 1000, 64, 1, tm.TM_COL_NAIVE) == 1000 * 4
+    assert W(65, 1000, 64, 64, tm.TM_COL_LDS) == 1000 * 4
+    assert W(256, 1 << 18, 64, 64, tm.TM_COL_LDS) == 0
+    assert W(256, (1 << 18) - 1, 64, 64, tm.TM_COL_LDS) == ((1 << 18) - 1) * 4
+    assert W(257, 1 << 18, 64, 64, tm.TM_COL_LDS) == 2 * (1 << 18) * 4
     assert W(0, 1000, 64, 64, tm.TM_COL_LDS) == 0
     assert W(100, 0, 64, 64, tm.TM_COL_LDS) == 0
     assert W(100, 100, 3, 64, tm.TM_COL_LDS) == 0
@@ -264,6 +271,9 @@ def test_colsum_workspace_and_errors():
     # precedence: WORKSPACE before ALIGN (M = 4100 breaks the promise and needs 17 slabs)
     assert f(A16, 4096, B16, 4100, 4096, 256, 64, 1, tm.TM_COL_LDS, 0, 0, S) == tm.TM_E_WORKSPACE
     assert f(A16, 4096, B16, 4096, 0, 256, 64, 0, tm.TM_COL_LDS, 0, 0, S) == tm.TM_OK  # empty output
+    # a one-pass shape takes no workspace, so a missing one is no error (the promise still is)
+    assert f(A16, 4098, B16, 64, 4096, 64, 64, 1, tm.TM_COL_LDS, 0, 0, S) == tm.TM_E_ALIGN
+    assert f(A16, 4096, B16, 64, 4096, 64, 64, 1, tm.TM_COL_NAIVE, 0, 0, S) == tm.TM_E_WORKSPACE
 
 
 @no_gpu

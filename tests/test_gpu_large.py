@@ -87,6 +87,24 @@ def test_column_sums_beyond_2g(big):
         del ws
 
 
+def test_direct_column_sums_across_2g(big):
+    """The one-pass column walk (64 rows) over rows 65504 .. 65567, which straddle element 2^31:
+    every column against the oracle's sum of the same block rows."""
+    dev, x, blk = big
+    r0, M = 65504, 64
+    assert tm.tm_colsum_workspace_bytes(M, N, 64, 64, tm.TM_COL_LDS) == 0
+    view = x.view(-1)[r0 * N:]
+    rows = np.concatenate([block_row(blk, r) for r in range(r0, r0 + M)])
+    ref = oracle.colsum_f64(rows, N, M, N)
+    absref = oracle.colsum_f64(np.abs(rows), N, M, N)
+    out = torch.empty(N, device=dev)
+    note("direct colsum rows %d..%d" % (r0, r0 + M - 1))
+    assert tm.tm_colsum(view, N, out, M, N, 64, 64, 1, tm.TM_COL_LDS, None, 0) == tm.TM_OK
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert (np.abs(got - ref) <= sum_tol(absref)).all()
+
+
 def test_transpose_beyond_2g(big):
     dev, x, blk = big
     note("transpose %dx%d" % (M, N))
