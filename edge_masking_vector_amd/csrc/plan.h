@@ -179,6 +179,7 @@ struct TransposePlan {
     bool vec = false;             // 16-byte chunks on both sides
     int aligned = 0;
     int sm = 1, sn = 1;           // staged sub-tile extents (powers of two, sm * sn <= kTrSubElems)
+    int log_g = 0;                // batches per work item: 2^log_g (whole matrices in one sub-tile)
     uint32_t subs_m = 0, subs_n = 0;
     uint64_t nwork = 0;
     bool wide = false;            // nwork >= 2^32: 64-bit work-item arithmetic

@@ -50,10 +50,14 @@ struct TrArgs {
     uint32_t subs_m, subs_n;         // sub-tiles along M and N per batch
     uint32_t per_b;                  // subs_m * subs_n (when the work count fits 32 bits)
     int log_sm, log_sn;              // staged sub-tile extents: 2^log_sm x 2^log_sn (<= kSubElems)
+    int log_g;                       // batches per work item (whole matrices in one sub-tile)
+    int64_t B;                       // batches
 };
 static_assert(sizeof(TrArgs) <= 128, "transpose arguments outgrew one scalar load batch");
 
-template <bool VEC, bool ALIGNED, int BS, bool WIDE>
+// PACK: every matrix fits in one sub-tile, and a work item takes 2^log_g consecutive batches, each
+// staged in its own LDS region (a 256-thread workgroup per 4 x 4 matrix left 240 threads idle).
+template <bool VEC, bool ALIGNED, int BS, bool WIDE, bool PACK>
 __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
     constexpr int LOG_W = VEC ? 2 : 0;
     constexpr int W = 1 << LOG_W;
@@ -64,9 +68,11 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
     // and masks (run-time divisions per chunk took the 4096 x 4096 transpose from 25.5 to 27.5 us).
     const int lcx = a.log_sn - LOG_W;   // log2 of the chunks per staged x row
     const int lcy = a.log_sm - LOG_W;   // log2 of the chunks per y row
-    const int nchunks = 1 << (a.log_sm + a.log_sn - LOG_W);
+    const int lt = a.log_sm + a.log_sn - LOG_W;         // log2 of the chunks of one sub-tile
+    const int nchunks = 1 << (lt + (PACK ? a.log_g : 0));  // chunks of the work item
     const int sm = 1 << a.log_sm, sn = 1 << a.log_sn;
     const int pad = sn + 1;             // LDS row stride: odd for SN >= 2, so columns spread over banks
+    const int stage = sm * pad;         // LDS floats of one staged sub-tile (PACK: one per batch)
 
     uint64_t w = blockIdx.x;
     do {
@@ -93,19 +99,26 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
         }
         const int64_t row0 = int64_t(pm) * sm;     // x rows = y columns
         const int64_t col0 = int64_t(pn) * sn;     // x columns = y rows
-        const float *xb = a.x + int64_t(b) * a.bsx;
-        float *yb = a.y + int64_t(b) * a.bsy;
         const int64_t rows_live = a.M - row0, cols_live = a.N - col0;
+        // Chunk e of the work item belongs to batch b0 + (e >> lt) (PACK; else b) and is chunk
+        // e & (2^lt - 1) of that batch's sub-tile.
+        const int64_t b0 = PACK ? int64_t(b) << a.log_g : int64_t(b);
+        auto batch_of = [&](int e) { return PACK ? b0 + (e >> lt) : b0; };
+        auto in_tile = [&](int e) { return PACK ? e & ((1 << lt) - 1) : e; };
 
         // Read x's sub-tile along its rows (all of this thread's chunks first); an element past
         // the tensor reads as 0.
         float v[K][W];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const int e = t + k * BS;
-            const int r = e >> lcx, c = (e & ((1 << lcx) - 1)) << LOG_W;
-            const float *p = xb + (row0 + r) * a.ldx + col0 + c;
-            if (e < nchunks) {
+            const int e = t + k * BS, et = in_tile(e);
+            const int r = et >> lcx, c = (et & ((1 << lcx) - 1)) << LOG_W;
+            const int64_t bb = batch_of(e);
+            const float *p = a.x + bb * a.bsx + (row0 + r) * a.ldx + col0 + c;
+#pragma unroll
+            for (int i = 0; i < W; ++i)
+                v[k][i] = 0.0f;
+            if (e < nchunks && (!PACK || bb < a.B)) {
                 if (ALIGNED || (r < rows_live && c + W <= cols_live)) {
                     if constexpr (VEC) {
                         const f4 q = ld16_nt(p);
@@ -122,12 +135,13 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const int e = t + k * BS;
-            const int r = e >> lcx, c = (e & ((1 << lcx) - 1)) << LOG_W;
+            const int e = t + k * BS, et = in_tile(e);
+            const int r = et >> lcx, c = (et & ((1 << lcx) - 1)) << LOG_W;
+            const int g = PACK ? e >> lt : 0;
             if (e < nchunks) {
 #pragma unroll
                 for (int i = 0; i < W; ++i)
-                    tile[r * pad + c + i] = v[k][i];
+                    tile[g * stage + r * pad + c + i] = v[k][i];
             }
         }
         __syncthreads();
@@ -136,20 +150,22 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
         // tensor is skipped.
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const int e = t + k * BS;
-            const int j = e >> lcy, i = (e & ((1 << lcy) - 1)) << LOG_W;
+            const int e = t + k * BS, et = in_tile(e);
+            const int j = et >> lcy, i = (et & ((1 << lcy) - 1)) << LOG_W;
+            const int g = PACK ? e >> lt : 0;
             if (e < nchunks) {
 #pragma unroll
                 for (int q = 0; q < W; ++q)
-                    v[k][q] = tile[(i + q) * pad + j];
+                    v[k][q] = tile[g * stage + (i + q) * pad + j];
             }
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            const int e = t + k * BS;
-            const int j = e >> lcy, i = (e & ((1 << lcy) - 1)) << LOG_W;
-            float *q = yb + (col0 + j) * a.ldy + row0 + i;
-            if (e < nchunks) {
+            const int e = t + k * BS, et = in_tile(e);
+            const int j = et >> lcy, i = (et & ((1 << lcy) - 1)) << LOG_W;
+            const int64_t bb = batch_of(e);
+            float *q = a.y + bb * a.bsy + (col0 + j) * a.ldy + row0 + i;
+            if (e < nchunks && (!PACK || bb < a.B)) {
                 if (ALIGNED || (j < cols_live && i + W <= rows_live)) {
                     if constexpr (VEC)
                         st16_nt(q, f4{v[k][0], v[k][1], v[k][2], v[k][3]});
@@ -171,12 +187,12 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
     } while (true);
 }
 
-template <bool WIDE>
+template <bool WIDE, bool PACK>
 const void *pick(const tmp::TransposePlan &p) {
     if (!p.vec)
-        return reinterpret_cast<const void *>(&transpose_tiles<false, false, kTrBlock, WIDE>);
-    return p.aligned ? reinterpret_cast<const void *>(&transpose_tiles<true, true, kTrBlock, WIDE>)
-                     : reinterpret_cast<const void *>(&transpose_tiles<true, false, kTrBlock, WIDE>);
+        return reinterpret_cast<const void *>(&transpose_tiles<false, false, kTrBlock, WIDE, PACK>);
+    return p.aligned ? reinterpret_cast<const void *>(&transpose_tiles<true, true, kTrBlock, WIDE, PACK>)
+                     : reinterpret_cast<const void *>(&transpose_tiles<true, false, kTrBlock, WIDE, PACK>);
 }
 
 }  // namespace
@@ -200,7 +216,10 @@ hipError_t launch_transpose(const tmp::TransposePlan &p, hipStream_t stream) {
     a.c_m = p.by_m.c;
     a.c_n = p.by_n.c;
     a.nwork = p.nwork;
-    const void *fn = p.wide ? pick<true>(p) : pick<false>(p);
+    a.log_g = p.log_g;
+    a.B = p.B;
+    const void *fn = p.log_g > 0 ? (p.wide ? pick<true, true>(p) : pick<false, true>(p))
+                                 : (p.wide ? pick<true, false>(p) : pick<false, false>(p));
     void *args[] = {&a};
     return hipLaunchKernel(fn, dim3(p.grid), dim3(kTrBlock), args, 0, stream);
 }

@@ -169,7 +169,8 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
     CHECK(!p.wide, "%s small job planned as wide", tag);
     CHECK(p.subs_m == uint32_t((M + p.sm - 1) / p.sm) && p.subs_n == uint32_t((N + p.sn - 1) / p.sn),
           "%s sub-tile counts", tag);
-    CHECK(p.nwork == uint64_t(B) * p.subs_m * p.subs_n && p.grid >= 1 && p.grid <= p.nwork, "%s work", tag);
+    CHECK((p.log_g > 0 || p.nwork == uint64_t(B) * p.subs_m * p.subs_n) && p.grid >= 1 && p.grid <= p.nwork,
+          "%s work", tag);
     CHECK((p.sm & (p.sm - 1)) == 0 && (p.sn & (p.sn - 1)) == 0 && int64_t(p.sm) * p.sn <= tmp::kTrSubElems,
           "%s sub-tile %dx%d above %d elements", tag, p.sm, p.sn, tmp::kTrSubElems);
     // the staged sub-tile (rows of stride SN + 1 floats) fits the kernel's LDS of 2 * kTrSubElems
@@ -187,6 +188,28 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
         CHECK(M % p.sm == 0 && N % p.sn == 0, "%s promised sub-tiles are not whole", tag);
     if (p.vec)
         CHECK(p.sm >= 4 && p.sn >= 4, "%s 16-byte chunks need sub-tiles of 4+", tag);
+    if (p.log_g > 0) {
+        // packed: every matrix in one sub-tile, work item w takes batches w * G .. w * G + G - 1
+        const int64_t G = int64_t{1} << p.log_g;
+        CHECK(p.subs_m == 1 && p.subs_n == 1 && B > 1, "%s packed plan with several sub-tiles", tag);
+        CHECK(G * p.sm * p.sn <= tmp::kTrSubElems && G * p.sm * (p.sn + 1) <= 2 * tmp::kTrSubElems,
+              "%s %ld packed sub-tiles of %dx%d exceed the work item", tag, long(G), p.sm, p.sn);
+        CHECK(G < 2 * B, "%s more packed batches than needed", tag);
+        CHECK(p.nwork == uint64_t((B + G - 1) / G), "%s packed work count", tag);
+        std::vector<uint8_t> hit(size_t(B), 0);
+        for (uint64_t w = 0; w < p.nwork; ++w)
+            for (int64_t g = 0; g < G; ++g)
+                if (int64_t(w) * G + g < B)
+                    ++hit[size_t(int64_t(w) * G + g)];
+        bool once = true;
+        for (uint8_t h : hit)
+            once = once && h == 1;
+        CHECK(once, "%s packed batches not covered once", tag);
+        ++g_checked;
+        return;
+    }
+    CHECK(!(p.subs_m == 1 && p.subs_n == 1 && B > 1 && int64_t(p.sm) * p.sn * 2 <= tmp::kTrSubElems),
+          "%s small matrices not packed", tag);
     std::vector<uint8_t> seen(size_t(p.nwork), 0);
     for (uint64_t w = 0; w < p.nwork; ++w) {
         const uint32_t w32 = uint32_t(w);
@@ -215,7 +238,7 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
 }
 
 static void check_transposes() {
-    const int64_t Bs[] = {1, 3, 32};
+    const int64_t Bs[] = {1, 3, 32, 1000};
     const int64_t Ms[] = {1, 2, 3, 4, 24, 64, 100, 50176};
     const int64_t Ns[] = {1, 3, 5, 16, 32, 100, 3136};
     for (int64_t B : Bs)
@@ -223,6 +246,8 @@ static void check_transposes() {
             for (int64_t N : Ns)
                 for (int T : {4, 32, 64})
                     for (int aligned = 0; aligned <= 1; ++aligned) {
+                        if (B * M * N > 100000000)
+                            continue;  // the replay visits every work item
                         tmp::TransposePlan p;
                         const int64_t ldx = (N + 3) / 4 * 4, ldy = (M + 3) / 4 * 4;
                         const int st = tmp::plan_transpose(fake(0x100000), ldx, M * ldx,

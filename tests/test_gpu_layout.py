@@ -114,6 +114,24 @@ def test_transpose_narrow_edges(dev):
                         seed=M + N)
 
 
+def test_transpose_many_small_matrices(dev):
+    """Batches of small matrices, several per workgroup (each matrix fits one sub-tile): whole
+    and partial last work items, batch strides with gaps, padded and odd row strides, misaligned
+    bases, the promised path, and fewer batches than a work item holds."""
+    for (B, M, N, ldx, ldy, bsx, bsy, TM, TN, al, xoff) in (
+            (1000, 4, 4, 4, 4, 16, 16, 4, 4, 1, 0),
+            (1001, 4, 4, 4, 4, 16, 16, 4, 4, 0, 0),
+            (777, 3, 5, 5, 3, 15, 15, 1, 1, 0, 0),
+            (513, 8, 8, 9, 8, 80, 70, 8, 8, 0, 0),
+            (300, 16, 16, 16, 16, 256, 260, 16, 16, 1, 0),
+            (100, 1, 7, 7, 1, 7, 7, 1, 1, 0, 0),
+            (3, 16, 16, 16, 16, 256, 256, 16, 16, 1, 0),
+            (2000, 2, 2, 2, 2, 4, 4, 2, 2, 0, 1),
+            (64, 32, 8, 8, 32, 256, 256, 32, 8, 1, 0)):
+        note("small matrices B=%d M=%d N=%d ld=%d/%d bs=%d/%d aligned=%d" % (B, M, N, ldx, ldy, bsx, bsy, al))
+        check_transpose(dev, B, M, N, ldx, ldy, bsx, bsy, TM, TN, al, xoff=xoff, seed=B + M)
+
+
 def test_transpose_padded_and_misaligned(dev):
     check_transpose(dev, 1, 300, 500, 503, 301, 0, 0, 64, 64, 0)           # odd strides: scalar
     check_transpose(dev, 1, 300, 500, 504, 304, 0, 0, 64, 64, 0)           # padded 16-byte rows
