@@ -58,6 +58,11 @@ struct MapArgs {
     const float *scale;  // channel op: per-column scale (null: 1) and bias
     const float *bias;
     int cvec16;          // channel op: the column vectors are 16-byte aligned
+    // Channel op over a flat view (rows of C contiguous channels planned as one row): the channel
+    // of flat column col is col mod C.  chan_n = 0: the channel is the column.
+    uint32_t chan_n;     // C
+    uint32_t chan_step;  // (columns per work item) mod C
+    uint64_t chan_c;     // multiply-high divisor of C
     // Element step inside an under-stated 4-element chunk.  Always 1; passed at run time so the
     // compiler cannot prove the four accesses adjacent and fuse them into one 16-byte access
     // (gfx950 accepts dwordx4 at 4-byte alignment, so a merely under-stated alignment would still
@@ -119,6 +124,32 @@ __device__ __forceinline__ typename Chunk<ACC>::T load_cvec(const float *v, int6
             r.z = v[col + 2];
         if (live > 3)
             r.w = v[col + 3];
+        return r;
+    }
+}
+
+// Flat channel view: element i of the chunk has channel (c0 + i) mod C (c0 < C).  With C % 4 == 0
+// (and 16-byte aligned vectors) a 16-byte chunk's channels are one aligned vector chunk; otherwise
+// they are gathered, wrapping at C.
+template <int ACC>
+__device__ __forceinline__ typename Chunk<ACC>::T load_cvec_flat(const float *v, uint32_t c0, uint32_t C,
+                                                                  int vec16, float absent) {
+    if constexpr (Chunk<ACC>::W == 1) {
+        return v ? v[c0] : absent;
+    } else {
+        if (!v)
+            return f4(absent);
+        if (vec16)
+            return ld16(v + c0);
+        f4 r;
+        uint32_t c = c0;
+        r.x = v[c];
+        c = c + 1 == C ? 0 : c + 1;
+        r.y = v[c];
+        c = c + 1 == C ? 0 : c + 1;
+        r.z = v[c];
+        c = c + 1 == C ? 0 : c + 1;
+        r.w = v[c];
         return r;
     }
 }
@@ -247,6 +278,26 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
         auto chunk_col = [&](uint32_t q) { return tile_col(q) + int64_t(q & vr_mask) * W; };
         auto chunk_row = [&](uint32_t q) { return row0 + int64_t(q >> a.log_gv); };
 
+        // Channel vectors of the chunk at column col (live: its columns inside the tensor).  On a
+        // flat view the channel of col is col mod C: col0 mod C = (gi mod C) * (columns per item
+        // mod C) mod C (below C * C < 2^32), and col - col0 is below a work item's 4096 chunks.
+        // A power-of-two C takes a mask instead (the 64-channel bias add paid 3% for the modulo).
+        const bool chan_pow2 = (a.chan_n & (a.chan_n - 1)) == 0;
+        auto chan_mod = [&](uint32_t v) {
+            return chan_pow2 ? v & (a.chan_n - 1) : fast_mod(v, a.chan_c, a.chan_n);
+        };
+        uint32_t chan_base = 0;
+        if constexpr (OP == tmp::kChannel) {
+            if (a.chan_n != 0)
+                chan_base = chan_mod(chan_mod(gi) * a.chan_step);
+        }
+        auto cvec = [&](const float *v, int64_t col, int64_t live, float absent) {
+            if (a.chan_n != 0)
+                return load_cvec_flat<ACC>(v, chan_mod(chan_base + uint32_t(col - col0)), a.chan_n, a.cvec16,
+                                           absent);
+            return load_cvec<ACC>(v, col, live, a.cvec16, absent);
+        };
+
         // Whole tiles (every tile, when the promise was checked; otherwise this work item's tiles
         // all lie inside the tensor): no masks.
         const bool item_whole = ALIGNED || ((int64_t(pm) + 1) * tm <= a.M &&
@@ -265,8 +316,8 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
                     const int64_t row = chunk_row(q), col = chunk_col(q);
                     v[u] = load_chunk<ACC>(a.x + row * a.ldx + col, a.estep);
                     if constexpr (OP == tmp::kChannel) {
-                        cs[u] = load_cvec<ACC>(a.scale, col, W, a.cvec16, 1.0f);
-                        cb[u] = load_cvec<ACC>(a.bias, col, W, a.cvec16, 0.0f);
+                        cs[u] = cvec(a.scale, col, W, 1.0f);
+                        cb[u] = cvec(a.bias, col, W, 0.0f);
                     }
                 }
 #pragma unroll
@@ -290,8 +341,8 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
                     if (!GUARD || q < chunks) {
                         v[u] = load_chunk<ACC>(a.x + row * a.ldx + col, a.estep);
                         if constexpr (OP == tmp::kChannel) {
-                            cs[u] = load_cvec<ACC>(a.scale, col, W, a.cvec16, 1.0f);
-                            cb[u] = load_cvec<ACC>(a.bias, col, W, a.cvec16, 0.0f);
+                            cs[u] = cvec(a.scale, col, W, 1.0f);
+                            cb[u] = cvec(a.bias, col, W, 0.0f);
                         }
                     }
                 }
@@ -327,8 +378,8 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
                     const float *xp = a.x + row * a.ldx + col;
                     v[u] = whole[u] ? load_chunk<ACC>(xp, a.estep) : load_masked<ACC>(xp, live[u], a.estep);
                     if constexpr (OP == tmp::kChannel) {
-                        cs[u] = load_cvec<ACC>(a.scale, col, live[u], a.cvec16, 1.0f);
-                        cb[u] = load_cvec<ACC>(a.bias, col, live[u], a.cvec16, 0.0f);
+                        cs[u] = cvec(a.scale, col, live[u], 1.0f);
+                        cb[u] = cvec(a.bias, col, live[u], 0.0f);
                     }
                 }
             }
@@ -413,6 +464,9 @@ hipError_t launch_map(const tmp::MapPlan &p, hipStream_t stream) {
     a.scale = p.scale;
     a.bias = p.bias;
     a.cvec16 = p.cvec16 ? 1 : 0;
+    a.chan_n = p.chan_n;
+    a.chan_step = p.chan_step;
+    a.chan_c = p.chan.c;
     a.estep = 1;
     void *args[] = {&a};
     return hipLaunchKernel(pick(p), dim3(p.grid), dim3(1u << p.log_bs), args, 0, stream);

@@ -23,6 +23,8 @@ constexpr int kLineBytes = 128;     // cache line
 constexpr int kRowSegmentBytes = 512;  // map work items: bytes of each row they move, at least ...
 constexpr int kStreamSegmentBytes = 1024;  // ... or one row segment of this many bytes, moved
                                            // with device-scope streaming buffer accesses
+constexpr int64_t kChanFlatMax = 65535;  // channel op: flat views up to this many channels
+                                         // (C * C < 2^32 for the device's 32-bit modulo)
 constexpr int kTrSub = 32;          // transpose: staged sub-tile edge (one 128-byte line of f32) ...
 constexpr int kTrSubElems = kTrSub * kTrSub;  // ... and elements; a narrow tensor's sub-tile is
                                               // narrower and longer (up to kTrSubElems long)
@@ -64,6 +66,16 @@ enum Access { kScalar = 1, kVec4Understated = 2, kVec4 = 3 };
 
 int ilog2(int64_t v);  // v a power of two
 
+// Division by a fixed divisor d >= 1 through a precomputed multiplier (Lemire, Kaser and Kurz,
+// "Faster remainder by direct computation", 2019): with c = ceil(2^64 / d), every 32-bit a has
+// a / d = the high 64 bits of c * a and a % d = the high 64 bits of (c * a mod 2^64) * d.  For
+// d = 1 the multiplier (2^64) does not fit; c is then 0 and the device takes the identity.
+struct Div32 {
+    uint64_t c = 0;
+    uint32_t d = 1;
+};
+Div32 make_div32(uint32_t d);
+
 // ---- element-wise maps ---------------------------------------------------------------------
 struct MapPlan {
     bool launch = false;          // false: valid call with no work
@@ -91,7 +103,12 @@ struct MapPlan {
     float alpha = 0.f, beta = 0.f;
     const float *scale = nullptr;  // per-column vectors of the channel op (scale may be null)
     const float *bias = nullptr;
-    bool cvec16 = false;           // both column vectors 16-byte aligned
+    bool cvec16 = false;           // both column vectors 16-byte aligned (flat view: and C % 4 == 0)
+    // Channel op over a view with contiguous rows, planned as one flat row: element (i, j) is flat
+    // column i*C + j, whose channel is (flat column) mod C.  0: the channel is the column.
+    uint32_t chan_n = 0;          // C
+    Div32 chan;                   // divisor C
+    uint32_t chan_step = 0;       // (columns per work item) mod C
 };
 
 int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t M, int64_t N,
@@ -164,15 +181,6 @@ int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int 
               int aligned, int walk, void *ws, size_t ws_bytes, ColPlan *plan);
 
 // ---- batched transpose -----------------------------------------------------------------------
-// Division by a fixed divisor d >= 1 through a precomputed multiplier (Lemire, Kaser and Kurz,
-// "Faster remainder by direct computation", 2019): with c = ceil(2^64 / d), every 32-bit a has
-// a / d = the high 64 bits of c * a and a % d = the high 64 bits of (c * a mod 2^64) * d.  For
-// d = 1 the multiplier (2^64) does not fit; c is then 0 and the device takes the identity.
-struct Div32 {
-    uint64_t c = 0;
-    uint32_t d = 1;
-};
-Div32 make_div32(uint32_t d);
 
 struct TransposePlan {
     bool launch = false;

@@ -80,6 +80,25 @@ static void replay_map(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, 
               "%s stream item is not one wave over 1 KiB", tag);
         CHECK(p.log_r == 0 || pld == PN, "%s stream item over rows that are not contiguous", tag);
     }
+    // Channel op: a flat view carries C (the caller's N) and the device finds each element's
+    // channel as (chan_base + col - col0) mod C, then steps it with a wrap at C.
+    CHECK(p.chan_n == ((p.op == tmp::kChannel && PM != M) ? uint32_t(N) : 0u), "%s channel count %u", tag,
+          p.chan_n);
+    long chan_bad = 0;
+    auto check_chan = [&](uint32_t gi, int64_t col0, int64_t col) {
+        if (p.chan_n == 0)
+            return;
+        const uint64_t prod = uint64_t(umulhi_mod(gi, p.chan)) * p.chan_step;
+        const uint64_t arg = uint64_t(umulhi_mod(uint32_t(prod), p.chan)) + uint64_t(col - col0);
+        uint32_t c = umulhi_mod(uint32_t(arg), p.chan);
+        if (prod > 0xFFFFFFFFull || arg > 0xFFFFFFFFull)
+            ++chan_bad;
+        for (int e = 0; e < W && col + e < PN; ++e) {
+            if (c != uint32_t((col + e) % int64_t(p.chan_n)))
+                ++chan_bad;
+            c = c + 1 == p.chan_n ? 0 : c + 1;
+        }
+    };
     const int64_t span = (M - 1) * ld + N;  // addresses of the caller's view, in elements
     std::vector<uint8_t> hits(size_t(span), 0);
     for (uint32_t w = 0; w < p.nwork; ++w) {
@@ -109,9 +128,11 @@ static void replay_map(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, 
                     for (int e = 0; e < W; ++e)
                         if (row < PM && col + e < PN && row * pld + col + e < span)
                             ++hits[size_t(row * pld + col + e)];
+                    check_chan(gi, col0, col);
                 } else {
                     if (!(pn < p.tiles_n && row < PM && PN - col > 0))
                         continue;  // masked: nothing read or stored
+                    check_chan(gi, col0, col);
                     for (int e = 0; e < W && col + e < PN; ++e)
                         if (row * pld + col + e < span)
                             ++hits[size_t(row * pld + col + e)];
@@ -119,6 +140,7 @@ static void replay_map(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, 
             }
         }
     }
+    CHECK(chan_bad == 0, "%s %ld channel indices wrong", tag, chan_bad);
     for (int64_t a = 0; a < span; ++a) {
         const bool inside = ld == 0 || a % ld < N;
         if (hits[size_t(a)] != (inside ? 1 : 0)) {

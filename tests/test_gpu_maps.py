@@ -446,6 +446,35 @@ def test_channel_affine_variants_and_unaligned_vectors(dev):
             check_channel(dev, 257, 1000, 1000, 1004, 16, 64, 0, variant, True, coff=coff)
 
 
+@pytest.mark.parametrize("C", [1, 2, 3, 4, 5, 8, 17, 64, 100])
+def test_channel_affine_flat_views(dev, C):
+    """Views whose rows are contiguous (ld = C) are walked as one flat row and each element finds
+    its channel as (flat column) mod C: few and many channels, every access variant, with and
+    without a scale, channel vectors 16-byte aligned or not (gathered), a ragged flat end."""
+    M = 300007 // C
+    for variant in (tm.TM_VAR_AUTO, tm.TM_VAR_SCALAR, tm.TM_VAR_VEC4_UNDERSTATED, tm.TM_VAR_VEC4):
+        TN = 4 if variant == tm.TM_VAR_VEC4_UNDERSTATED else 1
+        expect = tm.TM_OK
+        if variant == tm.TM_VAR_VEC4:
+            TN = 4
+            expect = tm.TM_OK if C % 4 == 0 else tm.TM_E_ALIGN
+        for with_scale, coff in ((False, 0), (True, 0), (True, 1)):
+            note("flat channel C=%d M=%d var=%d scale=%d coff=%d" % (C, M, variant, with_scale, coff))
+            check_channel(dev, M, C, C, C, 1, TN, 0, variant, with_scale, coff=coff, seed=C,
+                          expect=expect)
+    if C % 4 == 0:
+        Mp = M - M % 64
+        note("flat channel C=%d aligned" % C)
+        check_channel(dev, Mp, C, C, C, 64, 4, 1, tm.TM_VAR_VEC4, True, seed=C + 1)
+
+
+def test_channel_affine_flat_brute_force_tiny(dev):
+    for M in (2, 3, 5, 17, 64):
+        for N in (1, 2, 3, 4, 7, 16, 17):
+            for (TM, TN) in ((1, 1), (2, 4), (8, 8), (16, 1024)):
+                check_channel(dev, M, N, N, N, TM, TN, 0, tm.TM_VAR_AUTO, True, seed=M * 100 + N)
+
+
 def test_channel_affine_brute_force_tiny(dev):
     for M in (1, 2, 5, 17):
         for N in (1, 3, 4, 7, 16, 17):
