@@ -530,7 +530,8 @@ def transpose_paths(torch, tm, inputs, dev, stream, timed, ok):
           lambda i: ok(tm.tm_transpose(xs[i], HW, C * HW, ys[i], C, HW * C, B, C, HW, 64, 64, 1, stream)),
           "batched transpose [B][C][HW] -> [B][HW][C]")
     del xs, ys
-    # three channels (RGB images, 32 x 3 x 224 x 224) both ways: narrow 4 x 256 sub-tiles
+    # three channels (RGB images, 32 x 3 x 224 x 224) both ways: the packed side (rows of 3 floats)
+    # moves as one contiguous block per work item
     B, C, HW = 32, 3, 224 * 224
     xh = inputs.uniform(8, B * C * HW, -1.0, 1.0)
     nb = 2 * B * C * HW * 4
@@ -539,10 +540,10 @@ def transpose_paths(torch, tm, inputs, dev, stream, timed, ok):
     ys = [torch.empty_like(x) for x in xs]
     timed("nchw_to_nhwc_32x3x224x224", nb, R,
           lambda i: ok(tm.tm_transpose(xs[i], HW, C * HW, ys[i], C, HW * C, B, C, HW, 1, 64, 0, stream)),
-          "batched transpose [B][3][HW] -> [B][HW][3], ragged path, 4-byte chunks")
+          "batched transpose [B][3][HW] -> [B][HW][3], ragged path, packed side as one block")
     timed("nhwc_to_nchw_32x3x224x224", nb, R,
           lambda i: ok(tm.tm_transpose(xs[i], C, HW * C, ys[i], HW, C * HW, B, HW, C, 64, 1, 0, stream)),
-          "batched transpose [B][HW][3] -> [B][3][HW], ragged path, 4-byte chunks")
+          "batched transpose [B][HW][3] -> [B][3][HW], ragged path, packed side as one block")
     del xs, ys
 
 

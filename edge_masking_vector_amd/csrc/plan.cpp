@@ -680,6 +680,24 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     }
     plan->nwork = static_cast<uint64_t>(plan->log_g > 0 ? ceil_div(B, int64_t{1} << plan->log_g)
                                                         : B * subs_m * subs_n);
+    // Few channels whose packed side is not 16-byte rows (3 channels: rows of 12 bytes): the packed
+    // side of a work item is one contiguous block, moved in 16-byte chunks by transpose_packed.
+    // (32, 3, 224, 224) NCHW -> NHWC and back: 13.9 -> 8.9 us; 1 to 31 channels gain 1.25-1.7x
+    // (in one process, over 1 GiB of rotating buffers, outputs compared bit for bit).
+    if (!vec && plan->log_g == 0 && !(M < kTrSub && N < kTrSub)) {
+        const bool bs16y = B <= 1 || bsy % 4 == 0, bs16x = B <= 1 || bsx % 4 == 0;
+        if (M < kTrSub && ldy == M && subs_m == 1) {
+            plan->packed = 1;
+            plan->pvec = rows16(x, M, ldx) && bs16x;
+            plan->flat16 = aligned_to(y, 16) && bs16y;
+        } else if (N < kTrSub && ldx == N && subs_n == 1) {
+            plan->packed = 2;
+            plan->pvec = rows16(y, N, ldy) && bs16y;
+            plan->flat16 = aligned_to(x, 16) && bs16x;
+        }
+        if (plan->packed != 0 && ((!plan->pvec && !plan->flat16) || plan->nwork > UINT32_MAX))
+            plan->packed = 0;  // nothing to gain, or work ids beyond 32 bits
+    }
     plan->wide = plan->nwork > UINT32_MAX;
     if (!plan->wide) {
         plan->per_b = make_div32(static_cast<uint32_t>(subs_m * subs_n));

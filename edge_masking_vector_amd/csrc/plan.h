@@ -188,6 +188,11 @@ struct TransposePlan {
     int aligned = 0;
     int sm = 1, sn = 1;           // staged sub-tile extents (powers of two, sm * sn <= kTrSubElems)
     int log_g = 0;                // batches per work item: 2^log_g (whole matrices in one sub-tile)
+    // Few channels with a packed side (transpose_packed): 1 = y rows of exactly M < kTrSub floats
+    // (NCHW -> NHWC), 2 = x rows of exactly N < kTrSub floats (NHWC -> NCHW); 0 = neither.
+    int packed = 0;
+    bool pvec = false;            // packed kernel: the strided side moves 16-byte chunks
+    bool flat16 = false;          // packed kernel: the packed block starts on 16-byte boundaries
     uint32_t subs_m = 0, subs_n = 0;
     uint64_t nwork = 0;
     bool wide = false;            // nwork >= 2^32: 64-bit work-item arithmetic

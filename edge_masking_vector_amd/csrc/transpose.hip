@@ -187,6 +187,204 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
     } while (true);
 }
 
+// ---- few channels, packed side -------------------------------------------------------------------
+// NCHW -> NHWC with C < 32 channels (MODE 0: x = [C][P] rows, y = [P][C] with row stride C) writes
+// each work item's output -- S positions of all C channels -- as one contiguous block of S*C
+// floats; NHWC -> NCHW (MODE 1: x = [P][C] with row stride C, y = [C][P]) reads its input that way.
+// The packed block moves in 16-byte chunks when it starts on 16-byte boundaries: element o of the
+// block is position o / C, channel o % C (multiply-high division, then a wrapping step), staged
+// through LDS as C rows of S positions with a row stride of S + 1 floats.  The strided side moves
+// as C rows of S positions, in 16-byte chunks when its rows allow (V).  With rows of 3 floats the
+// general kernel moved every element alone.
+struct PackedArgs {
+    const float *x;
+    float *y;
+    int64_t ldx, ldy, bsx, bsy;
+    int64_t P;            // positions (H*W)
+    uint64_t c_s, c_k;    // multiply-high divisors of subs and of C
+    uint32_t subs;        // work items per batch: ceil(P / S)
+    uint32_t k;           // C
+    uint32_t nwork;       // B * subs
+    int log_s;            // positions per work item: S = 2^log_s, S * 2^ceil(log2 C) <= kSubElems
+    int flat16;           // the packed block starts on 16-byte boundaries
+};
+
+template <int MODE, bool V>
+__global__ __launch_bounds__(kTrBlock) void transpose_packed(PackedArgs a) {
+    constexpr int W = V ? 4 : 1;                       // strided side: elements per chunk
+    constexpr int KS = kSubElems / W / kTrBlock;       // strided chunks per thread (at most)
+    constexpr int KF = kSubElems / 4 / kTrBlock;       // packed 16-byte chunks per thread (at most)
+    __shared__ float tile[kStage];
+    const int t = threadIdx.x;
+    const int S = 1 << a.log_s, pad = S + 1;
+    const int lcs = a.log_s - (V ? 2 : 0);             // log2 of the strided chunks per channel row
+    const int C = static_cast<int>(a.k);
+    const int nstr = C << lcs;                         // strided chunks of a work item
+    for (uint32_t w = blockIdx.x; w < a.nwork; w += gridDim.x) {
+        const uint32_t b = fast_div(w, a.c_s, a.subs), ps = w - b * a.subs;
+        const int64_t p0 = int64_t(ps) << a.log_s;
+        const int L = static_cast<int>(a.P - p0 < S ? a.P - p0 : S);  // live positions
+        const int nflat = L * C;                                       // live packed elements
+        // strided side: channel row ch, positions p0 + pc .. (x rows in MODE 0, y rows in MODE 1)
+        auto strided_at = [&](int ch, int pc) {
+            if constexpr (MODE == 0)
+                return a.x + int64_t(b) * a.bsx + int64_t(ch) * a.ldx + p0 + pc;
+            else
+                return a.y + int64_t(b) * a.bsy + int64_t(ch) * a.ldy + p0 + pc;
+        };
+        // packed side: the block of nflat floats at position p0
+        auto packed_at = [&](int o) {
+            if constexpr (MODE == 0)
+                return a.y + int64_t(b) * a.bsy + p0 * C + o;
+            else
+                return a.x + int64_t(b) * a.bsx + p0 * C + o;
+        };
+        if constexpr (MODE == 0) {
+            float v[KS][W];
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const int e = t + k * kTrBlock;
+                const int ch = e >> lcs, pc = (e & ((1 << lcs) - 1)) * W;
+#pragma unroll
+                for (int i = 0; i < W; ++i)
+                    v[k][i] = 0.0f;
+                if (e < nstr && pc < L) {
+                    const float *p = strided_at(ch, pc);
+                    if (V && pc + 4 <= L) {
+                        const f4 q = ld16_nt(p);
+                        v[k][0] = q.x, v[k][1] = q.y, v[k][2] = q.z, v[k][3] = q.w;
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < W; ++i)
+                            if (pc + i < L)
+                                v[k][i] = ld4_nt(p + i);
+                    }
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const int e = t + k * kTrBlock;
+                const int ch = e >> lcs, pc = (e & ((1 << lcs) - 1)) * W;
+                if (e < nstr) {
+#pragma unroll
+                    for (int i = 0; i < W; ++i)
+                        tile[ch * pad + pc + i] = v[k][i];
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < KF; ++k) {
+                const int o = 4 * (t + k * kTrBlock);
+                if (o < nflat) {
+                    uint32_t j = fast_div(uint32_t(o), a.c_k, a.k);  // position
+                    uint32_t i = uint32_t(o) - j * a.k;              // channel
+                    float r[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        r[q] = tile[i * pad + j];
+                        if (++i == a.k) {
+                            i = 0;
+                            ++j;
+                        }
+                    }
+                    float *p = packed_at(o);
+                    if (a.flat16 && o + 4 <= nflat) {
+                        st16_nt(p, f4{r[0], r[1], r[2], r[3]});
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (o + q < nflat)
+                                st4_nt(p + q, r[q]);
+                    }
+                }
+            }
+        } else {
+            float r[KF][4];
+#pragma unroll
+            for (int k = 0; k < KF; ++k) {
+                const int o = 4 * (t + k * kTrBlock);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    r[k][q] = 0.0f;
+                if (o < nflat) {
+                    const float *p = packed_at(o);
+                    if (a.flat16 && o + 4 <= nflat) {
+                        const f4 f = ld16_nt(p);
+                        r[k][0] = f.x, r[k][1] = f.y, r[k][2] = f.z, r[k][3] = f.w;
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (o + q < nflat)
+                                r[k][q] = ld4_nt(p + q);
+                    }
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < KF; ++k) {
+                const int o = 4 * (t + k * kTrBlock);
+                if (o < nflat) {
+                    uint32_t j = fast_div(uint32_t(o), a.c_k, a.k);
+                    uint32_t i = uint32_t(o) - j * a.k;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (o + q < nflat)
+                            tile[i * pad + j] = r[k][q];
+                        if (++i == a.k) {
+                            i = 0;
+                            ++j;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const int e = t + k * kTrBlock;
+                const int ch = e >> lcs, pc = (e & ((1 << lcs) - 1)) * W;
+                if (e < nstr && pc < L) {
+                    float *p = strided_at(ch, pc);
+                    if (V && pc + 4 <= L) {
+                        st16_nt(p, f4{tile[ch * pad + pc], tile[ch * pad + pc + 1], tile[ch * pad + pc + 2],
+                                      tile[ch * pad + pc + 3]});
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < W; ++i)
+                            if (pc + i < L)
+                                st4_nt(p + i, tile[ch * pad + pc + i]);
+                    }
+                }
+            }
+        }
+        if (w + gridDim.x < a.nwork)
+            __syncthreads();  // the next work item reuses the LDS tile (uniform test)
+    }
+}
+
+hipError_t launch_packed(const tmp::TransposePlan &p, hipStream_t stream) {
+    PackedArgs a;
+    a.x = p.x;
+    a.y = p.y;
+    a.ldx = p.ldx;
+    a.ldy = p.ldy;
+    a.bsx = p.bsx;
+    a.bsy = p.bsy;
+    const bool m0 = p.packed == 1;
+    a.P = m0 ? p.N : p.M;
+    a.k = static_cast<uint32_t>(m0 ? p.M : p.N);
+    a.subs = m0 ? p.subs_n : p.subs_m;
+    a.c_s = tmp::make_div32(a.subs).c;
+    a.c_k = tmp::make_div32(a.k).c;
+    a.nwork = static_cast<uint32_t>(p.nwork);
+    a.log_s = tmp::ilog2(m0 ? p.sn : p.sm);
+    a.flat16 = p.flat16 ? 1 : 0;
+    void *args[] = {&a};
+    const void *fn = m0 ? (p.pvec ? reinterpret_cast<const void *>(&transpose_packed<0, true>)
+                                  : reinterpret_cast<const void *>(&transpose_packed<0, false>))
+                        : (p.pvec ? reinterpret_cast<const void *>(&transpose_packed<1, true>)
+                                  : reinterpret_cast<const void *>(&transpose_packed<1, false>));
+    return hipLaunchKernel(fn, dim3(p.grid), dim3(kTrBlock), args, 0, stream);
+}
+
 template <bool WIDE, bool PACK>
 const void *pick(const tmp::TransposePlan &p) {
     if (!p.vec)
@@ -198,6 +396,8 @@ const void *pick(const tmp::TransposePlan &p) {
 }  // namespace
 
 hipError_t launch_transpose(const tmp::TransposePlan &p, hipStream_t stream) {
+    if (p.packed != 0)
+        return launch_packed(p, stream);
     TrArgs a;
     a.x = p.x;
     a.y = p.y;

@@ -229,12 +229,13 @@ int tm_softmax_stats_ws(const float *s, int64_t lds, float *m, float *l, int64_t
  * NCHW to NHWC; the same call with M and N swapped converts back ([LAYOUT] "NCHW versus NHWC": a
  * conversion costs one full pass over memory; "Strides, and reading an index expression").
  * x is staged through LDS in sub-tiles of 32 x 32 (for fewer than 32 rows or columns, as the
- * channels of an RGB image, as narrow as the tensor and up to 1024 elements long) so that both
- * the reads of x and the writes of y are coalesced rows ([LAYOUT] "Seeing it in a real kernel"),
- * in 16-byte chunks whenever every row of x and y starts on a 16-byte boundary, whatever the tile;
- * TM x TN is the tile the alignment promise is made for (under the promise the sub-tiles are
- * whole).  Ragged edges:
- * elements past the tensor read as 0 and are never stored.  aligned = 1 promises
+ * channels of an RGB image, as narrow as the tensor and up to 1024 elements long; when the narrow
+ * side's rows are packed, C floats each, a work item moves that side as one contiguous block) so
+ * that both the reads of x and the writes of y are coalesced rows ([LAYOUT] "Seeing it in a real
+ * kernel"), in 16-byte chunks whenever every row of x and y starts on a 16-byte boundary, whatever
+ * the tile; TM x TN is the tile the alignment promise is made for (under the promise the sub-tiles
+ * are whole).  Ragged edges: elements past the tensor read as 0 and are never stored.  aligned = 1
+ * promises
  * M % TM == 0, N % TN == 0, TM % 4 == 0, TN % 4 == 0 and 16-byte rows of x and y in every batch
  * (16-byte bases, row strides % 4 == 0, batch strides % 4 == 0 when B > 1), else TM_E_ALIGN.
  * For B > 1, bsy must be at least (N - 1)*ldy + M (batches of y may not overlap), else TM_E_INVAL.

@@ -210,6 +210,20 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
         CHECK(M % p.sm == 0 && N % p.sn == 0, "%s promised sub-tiles are not whole", tag);
     if (p.vec)
         CHECK(p.sm >= 4 && p.sn >= 4, "%s 16-byte chunks need sub-tiles of 4+", tag);
+    if (p.packed != 0) {
+        // few channels with a packed side: C = the narrow extent, S positions per work item
+        const bool m0 = p.packed == 1;
+        const int64_t C = m0 ? M : N, S = m0 ? p.sn : p.sm;
+        int64_t c2 = 1;
+        while (c2 < C)
+            c2 <<= 1;
+        CHECK(!p.vec && p.log_g == 0 && C < tmp::kTrSub && (m0 ? M : N) == C, "%s packed mode", tag);
+        CHECK(m0 ? (p.ldy == M && p.subs_m == 1 && N >= tmp::kTrSub) : (p.ldx == N && p.subs_n == 1 && M >= tmp::kTrSub),
+              "%s packed side is not one block per work item", tag);
+        CHECK(S >= 32 && S * c2 <= tmp::kTrSubElems && C * (S + 1) + 2 <= 2 * tmp::kTrSubElems,
+              "%s packed work item of %ld x %ld exceeds the kernel", tag, long(C), long(S));
+        CHECK(p.pvec || p.flat16, "%s packed mode with nothing in 16-byte chunks", tag);
+    }
     if (p.log_g > 0) {
         // packed: every matrix in one sub-tile, work item w takes batches w * G .. w * G + G - 1
         const int64_t G = int64_t{1} << p.log_g;
@@ -282,6 +296,27 @@ static void check_transposes() {
                                       long(M), long(N), T, aligned);
                         replay_transpose(p, B, M, N, tag);
                     }
+    // packed strides (NCHW <-> NHWC with few channels: y rows of exactly M, or x rows of exactly N)
+    long packed_plans = 0;
+    for (int64_t B : {int64_t{1}, int64_t{3}, int64_t{32}})
+        for (int64_t C : {int64_t{1}, int64_t{2}, int64_t{3}, int64_t{5}, int64_t{31}})
+            for (int64_t P : {int64_t{32}, int64_t{100}, int64_t{50176}})
+                for (int dir = 0; dir < 2; ++dir)
+                    for (uintptr_t off : {uintptr_t{0}, uintptr_t{4}}) {
+                        const int64_t M = dir == 0 ? C : P, N = dir == 0 ? P : C;
+                        tmp::TransposePlan p;
+                        const int st = tmp::plan_transpose(fake(0x100000 + off), N, M * N,
+                                                           const_cast<float *>(fake(0x40000000)), M, M * N, B, M,
+                                                           N, 1, 1, 0, &p);
+                        if (st != TM_OK || !p.launch)
+                            continue;
+                        packed_plans += p.packed != 0;
+                        char tag[128];
+                        std::snprintf(tag, sizeof tag, "packed transpose B=%ld M=%ld N=%ld off=%lu", long(B), long(M),
+                                      long(N), (unsigned long)off);
+                        replay_transpose(p, B, M, N, tag);
+                    }
+    CHECK(packed_plans > 0, "no packed-side transpose planned");
     // divisors of every size up to 5000, against plain division
     for (uint32_t d = 1; d <= 5000; ++d) {
         const tmp::Div32 v = tmp::make_div32(d);

@@ -114,6 +114,25 @@ def test_transpose_narrow_edges(dev):
                         seed=M + N)
 
 
+def test_transpose_packed_side(dev):
+    """Few channels whose packed side (rows of exactly C floats) moves as one contiguous block per
+    work item: both directions, ragged last work items, 16-byte or 4-byte strided sides, packed
+    blocks on and off 16-byte boundaries, single and several batches."""
+    for (B, M, N, ldx, ldy, bsx, bsy, xoff, yoff) in (
+            (1, 3, 7001, 7001, 3, 0, 0, 0, 0),            # NCHW -> NHWC, ragged
+            (1, 7001, 3, 3, 7004, 0, 0, 0, 0),            # NHWC -> NCHW, ragged
+            (5, 3, 1000, 1000, 3, 3000, 3000, 0, 0),
+            (5, 1000, 3, 3, 1000, 3000, 3000, 0, 0),
+            (2, 5, 999, 1000, 5, 5000, 5000, 0, 1),       # packed block off 16 bytes
+            (2, 999, 5, 5, 1000, 5000, 5000, 1, 0),
+            (3, 31, 513, 513, 31, 31 * 513, 31 * 513, 0, 0),
+            (3, 513, 31, 31, 516, 31 * 513, 31 * 516, 0, 0),
+            (2, 1, 4099, 4099, 1, 4099, 4099, 0, 0),
+            (2, 4099, 1, 1, 4100, 4099, 4100, 0, 0)):
+        note("packed side B=%d M=%d N=%d ld=%d/%d bs=%d/%d off=%d/%d" % (B, M, N, ldx, ldy, bsx, bsy, xoff, yoff))
+        check_transpose(dev, B, M, N, ldx, ldy, bsx, bsy, 1, 1, 0, xoff, yoff, seed=M * 3 + N)
+
+
 def test_transpose_many_small_matrices(dev):
     """Batches of small matrices, several per workgroup (each matrix fits one sub-tile): whole
     and partial last work items, batch strides with gaps, padded and odd row strides, misaligned
