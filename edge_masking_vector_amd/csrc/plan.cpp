@@ -469,7 +469,11 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
     const int64_t groups = ceil_div(M, plan->block / lpr);
     if (groups > INT32_MAX)
         return TM_E_UNSUPPORTED;  // row-group ids are 32-bit on the device
-    plan->grid = cap_grid(groups);
+    // One lane per row (rows of a few elements): a wave's work is a few hundred bytes, so its fixed
+    // cost dominates; workgroups that loop over several row groups spread it (1 GiB of rotating
+    // inputs: 2^24 one-element rows 52.4 -> 38.8 us, 2^23 x 2 33.5 -> 27.2, 2^22 x 4 22.2 -> 17.5;
+    // results unchanged, since each row is walked the same way).
+    plan->grid = cap_grid(lpr == 1 ? std::min(groups, kRowTinyGrid) : groups);
     plan->x = x;
     plan->out = out;
     plan->out2 = out2;

@@ -38,6 +38,8 @@ constexpr int kShortRowChunksScalar = 512;
 // kRowMaxLanes threads, so that about this many waves run.
 constexpr int kRowWideWaves = 2048;
 constexpr int kRowMaxLanes = 1024;
+// Rows of one lane each run on at most this many workgroups, each looping over several row groups.
+constexpr int64_t kRowTinyGrid = 4096;
 // Split rows (the row calls that take a workspace): fewer than kRowSplitRows rows of at least
 // kRowSplitMinN elements are cut into segments of kRowSegUnit * K elements (K = 1, 2, 4, 8 or 16,
 // chosen for about kRowSplitTarget segments in all), one workgroup each; a second kernel combines

@@ -352,7 +352,12 @@ static void check_reductions() {
                             CHECK(p.nfull * p.bc + p.rem == N && p.rem >= 0 && p.rem < p.bc,
                                   "rows split N=%ld bc=%d nfull=%ld rem=%ld", long(N), p.bc, long(p.nfull),
                                   long(p.rem));
-                            CHECK(p.grid >= 1, "rows grid");
+                            {
+                                const int64_t groups = (M + p.block / p.lpr - 1) / (p.block / p.lpr);
+                                const int64_t cap = p.lpr == 1 ? tmp::kRowTinyGrid : int64_t{1} << 20;
+                                CHECK(p.grid >= 1 && p.grid == uint32_t(groups < cap ? groups : cap),
+                                      "rows grid %u for %ld row groups", p.grid, long(groups));
+                            }
                             ++g_checked;
                         }
                         for (int walk : {TM_COL_NAIVE, TM_COL_LDS, TM_COL_NAIVE_XCD}) {
