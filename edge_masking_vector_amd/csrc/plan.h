@@ -38,6 +38,10 @@ constexpr int kShortRowChunksScalar = 512;
 // kRowMaxLanes threads, so that about this many waves run.
 constexpr int kRowWideWaves = 2048;
 constexpr int kRowMaxLanes = 1024;
+// Rows of at least kRowLongChunks 16-byte chunks get kRowLongLanes lanes (a workgroup per row), so
+// that each lane's chunks are in flight in one or two batches rather than many.
+constexpr int64_t kRowLongChunks = 1024;
+constexpr int kRowLongLanes = 256;
 // Rows of one lane each run on at most this many workgroups, each looping over several row groups.
 constexpr int64_t kRowTinyGrid = 4096;
 // Split rows (the row calls that take a workspace): fewer than kRowSplitRows rows of at least
