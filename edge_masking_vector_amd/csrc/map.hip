@@ -48,7 +48,7 @@ struct MapArgs {
     uint32_t tiles_n;    // tiles along N
     uint32_t group;      // G: tiles per work item along N
     uint32_t groups_n;   // tile groups along N: ceil(tiles_n / G)
-    uint32_t nwork;      // work items: tiles_m * 2^log_strips * groups_n
+    uint32_t nwork;      // work items: ceil(M / R) row strips * groups_n
     int log_tm, log_tn;
     int log_vr;          // chunks per tile row
     int log_gv;          // chunks per work-item row: G * VR

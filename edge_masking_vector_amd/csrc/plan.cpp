@@ -301,7 +301,11 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
         stream = true;
     const int log_chunks = log_r + log_g + log_vr;
     const int64_t groups_n = ceil_div(tiles_n, int64_t{1} << log_g);
-    const int64_t nwork = tiles_m * (int64_t{1} << (log_tm - log_r)) * groups_n;
+    // Row strips are numbered across the whole view (strip s = rows s*R .. s*R + R - 1; the kernel
+    // splits s into tile row and strip within it), and only strips that hold a row are scheduled:
+    // with 4 rows under a 64-row tile, 60 of every 64 strips used to launch, find no row and exit
+    // (4 x 534137 with padded rows: 27 us for 17 MB).
+    const int64_t nwork = ceil_div(M, int64_t{1} << log_r) * groups_n;
     if (nwork > INT32_MAX || tiles_n > INT32_MAX)
         return TM_E_UNSUPPORTED;  // work-item and tile ids are 32-bit on the device
 
@@ -499,12 +503,23 @@ namespace {
 // than kColMaxSlabs of them would leave pass 2 too many partials per column.  On 4096 x 4096 the
 // LDS walk took 14.6-15.6 us with 64- to 256-row slabs and 64- or 128-column strips against
 // 22-44 us with tiles 16-32 rows tall or 256-1024 columns wide.
-int slab_log(int64_t M, int TM, int walk) {
+int slab_log(int64_t M, int64_t N, int TM, int walk) {
     if (walk != TM_COL_LDS)
         return ilog2(TM);
     int l = ilog2(kColSlab);
     while (ceil_div(M, int64_t{1} << l) > kColMaxSlabs)
         ++l;
+    // Few strips (narrow matrices): shorter slabs, halved while there would be fewer than
+    // kColTargetWork workgroups, keeping at least 4 row steps per thread (a step is 1024 / TW rows
+    // at 16-byte chunks).  1 GiB of rotating inputs: 1280 x 1338 14.7 -> 7.8 us (32-row slabs),
+    // 2476 x 3397 15.8 -> 11.9, 21963 x 286 15.6 -> 11.4, 8192 x 1000 12.4 -> 11.9, 4096 x 1024
+    // 10.6 -> 9.2; 4096 x 4096 within 1%; slabs below 4 row steps were slower (59048 x 59, 32
+    // rows: 12.0 against 10.0 us).
+    const int64_t tw = N >= kColStrip ? kColStrip : std::max<int64_t>(1, int64_t{1} << ilog2(N));
+    const int64_t strips = ceil_div(N, tw);
+    const int lmin = std::max(5, ilog2(std::max<int64_t>(1, 4096 / tw)));
+    while (l > lmin && ceil_div(M, int64_t{1} << l) * strips < kColTargetWork)
+        --l;
     return l;
 }
 
@@ -527,7 +542,7 @@ size_t colsum_ws_bytes(int64_t M, int64_t N, int TM, int TN, int walk) {
         return 0;
     if (col_direct(M, N, walk))
         return 0;  // one pass, no partials
-    const int64_t slabs = ceil_div(M, int64_t{1} << slab_log(M, TM, walk));
+    const int64_t slabs = ceil_div(M, int64_t{1} << slab_log(M, N, TM, walk));
     if (slabs > INT64_MAX / 4 / N)
         return 0;
     return static_cast<size_t>(slabs * N * 4);
@@ -549,7 +564,7 @@ int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int 
         return st;
     if ((st = check_tile(TM, TN)) != TM_OK)
         return st;
-    const int log_ts = M > 0 ? slab_log(M, TM, walk) : 0;
+    const int log_ts = M > 0 ? slab_log(M, N, TM, walk) : 0;
     const int64_t slabs = ceil_div(M, int64_t{1} << log_ts);
     const size_t need = colsum_ws_bytes(M, N, TM, TN, walk);
     const bool direct = col_direct(M, N, walk);

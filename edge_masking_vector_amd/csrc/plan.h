@@ -59,6 +59,7 @@ constexpr int kRowPartialBytes = 8;  // workspace per segment: one float, or the
 constexpr int kColSlab = 256;
 constexpr int64_t kColMaxSlabs = 4096;
 constexpr int kColStrip = 128;
+constexpr int64_t kColTargetWork = 1024;  // LDS walk: fewer (slab, strip) workgroups shorten the slabs
 // Column-sum pass 2: lanes per column chosen so that about this many threads run.
 constexpr int kFinishThreads = 16384;
 // The LDS walk goes direct (one thread per 16-byte column chunk down all rows, one pass) for at
@@ -101,7 +102,7 @@ struct MapPlan {
     uint32_t group = 1;           // G
     uint32_t groups_n = 0;        // ceil(tiles_n / G)
     uint32_t tiles_n = 0;         // tiles along N
-    uint32_t nwork = 0;           // work items: tiles_m * (TM / R) * groups_n
+    uint32_t nwork = 0;           // work items: ceil(M / R) row strips * groups_n
     uint32_t grid = 0;            // workgroups
     const float *x = nullptr;
     float *y = nullptr;

@@ -376,7 +376,16 @@ static void check_reductions() {
                             if (c.launch) {
                                 const int64_t ts = int64_t{1} << c.log_tm;
                                 CHECK(c.slabs == uint32_t((M + ts - 1) / ts), "cols slabs");
-                                CHECK(walk == TM_COL_LDS ? ts >= tmp::kColSlab : ts == TR, "cols slab rows");
+                                if (walk == TM_COL_LDS) {
+                                    // 256-row slabs (taller past 4096 slabs), halved while there
+                                    // would be fewer than kColTargetWork workgroups, to 32 rows
+                                    CHECK(ts >= 32 && (ts >= tmp::kColSlab ||
+                                                       int64_t((M + 2 * ts - 1) / (2 * ts)) * c.strips <
+                                                           tmp::kColTargetWork),
+                                          "cols slab rows %ld", long(ts));
+                                } else {
+                                    CHECK(ts == TR, "cols slab rows");
+                                }
                                 CHECK(c.fl >= 1 && c.fl <= 64 && (c.fl & (c.fl - 1)) == 0, "cols fl %d", c.fl);
                                 if (walk == TM_COL_LDS) {
                                     CHECK(c.tw >= 1 && c.tw <= tmp::kColStrip && uint64_t(c.strips) * c.tw >= uint64_t(N),

@@ -239,20 +239,24 @@ def test_reduction_errors():
 @no_gpu
 def test_colsum_workspace_and_errors():
     W = tm.tm_colsum_workspace_bytes
-    assert W(4096, 4096, 256, 64, tm.TM_COL_LDS) == 16 * 4096 * 4
+    # LDS walk: 256-row slabs, halved while there would be fewer than 1024 (slab, strip)
+    # workgroups (32 strips of 128 columns here: 128-row slabs)
+    assert W(4096, 4096, 256, 64, tm.TM_COL_LDS) == 32 * 4096 * 4
     assert W(4096, 4096, 256, 1, tm.TM_COL_NAIVE) == 16 * 4096 * 4
     assert W(4096, 4096, 256, 1, tm.TM_COL_NAIVE_XCD) == 16 * 4096 * 4
     assert W(4096, 4096, 256, 1, 3) == 0
     # the LDS walk's slabs are its own (256 rows; taller past 4096 slabs), not the caller's TM
-    assert W(4100, 1000, 64, 64, tm.TM_COL_LDS) == 17 * 1000 * 4
-    assert W(4100, 1000, 1, 1, tm.TM_COL_LDS) == 17 * 1000 * 4
+    assert W(4100, 1000, 64, 64, tm.TM_COL_LDS) == 129 * 1000 * 4   # 8 strips: 32-row slabs
+    assert W(4100, 1000, 1, 1, tm.TM_COL_LDS) == 129 * 1000 * 4
+    assert W(59048, 59, 1, 1, tm.TM_COL_LDS) == 923 * 59 * 4      # 64-column strips: 64 rows at least
+    assert W(65536, 512, 1, 1, tm.TM_COL_LDS) == 256 * 512 * 4    # 256 x 4 workgroups: 256 rows
     assert W(4100, 1000, 64, 1, tm.TM_COL_NAIVE) == 65 * 1000 * 4
     assert W(1 << 21, 8, 256, 8, tm.TM_COL_LDS) == 4096 * 8 * 4
     assert W((1 << 21) + 1, 8, 256, 8, tm.TM_COL_LDS) == 2049 * 8 * 4
     # the LDS walk's one-pass form needs no partials: at most 64 rows, or 256 rows of 2^18 columns
     assert W(64, 1000, 64, 64, tm.TM_COL_LDS) == 0
     assert W(64, 1000, 64, 1, tm.TM_COL_NAIVE) == 1000 * 4
-    assert W(65, 1000, 64, 64, tm.TM_COL_LDS) == 1000 * 4
+    assert W(65, 1000, 64, 64, tm.TM_COL_LDS) == 3 * 1000 * 4
     assert W(256, 1 << 18, 64, 64, tm.TM_COL_LDS) == 0
     assert W(256, (1 << 18) - 1, 64, 64, tm.TM_COL_LDS) == ((1 << 18) - 1) * 4
     assert W(257, 1 << 18, 64, 64, tm.TM_COL_LDS) == 2 * (1 << 18) * 4
@@ -268,7 +272,7 @@ def test_colsum_workspace_and_errors():
     assert f(A16, 4098, B16, 4096, 4096, 256, 64, 1, tm.TM_COL_LDS, A16, need, S) == tm.TM_E_ALIGN
     assert f(A16 + 8, 4096, B16, 4096, 4096, 256, 64, 1, tm.TM_COL_LDS, A16, need, S) == tm.TM_E_ALIGN
     assert f(A16, 4096, B16, 4096, 4096, 200, 64, 1, tm.TM_COL_LDS, A16, need, S) == tm.TM_E_UNSUPPORTED
-    # precedence: WORKSPACE before ALIGN (M = 4100 breaks the promise and needs 17 slabs)
+    # precedence: WORKSPACE before ALIGN (M = 4100 breaks the promise and needs partials)
     assert f(A16, 4096, B16, 4100, 4096, 256, 64, 1, tm.TM_COL_LDS, 0, 0, S) == tm.TM_E_WORKSPACE
     assert f(A16, 4096, B16, 4096, 0, 256, 64, 0, tm.TM_COL_LDS, 0, 0, S) == tm.TM_OK  # empty output
     # a one-pass shape takes no workspace, so a missing one is no error (the promise still is)
