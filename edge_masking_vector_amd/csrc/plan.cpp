@@ -660,7 +660,9 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     // 16-byte chunks: x rows read along N, y rows written along M, every row on a 16-byte boundary
     // in every batch.  Whether they are used depends on the data only (a chunk that straddles the
     // edge of a ragged view moves element by element); the promise also covers the tile.
-    const bool vec = rows16(x, M, ldx) && rows16(y, N, ldy) && (B <= 1 || (bsx % 4 == 0 && bsy % 4 == 0));
+    const bool vx = rows16(x, M, ldx) && (B <= 1 || bsx % 4 == 0);
+    const bool vy = rows16(y, N, ldy) && (B <= 1 || bsy % 4 == 0);
+    const bool vec = vx && vy;
     if (aligned && !(M % TM == 0 && N % TN == 0 && TM % 4 == 0 && TN % 4 == 0 && vec))
         return TM_E_ALIGN;
     if (!work)
@@ -674,21 +676,25 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     // Under the promise a sub-tile must divide the extents (whole sub-tiles, no masks): the
     // largest power of two up to the cap that divides the extent, which the promised tile
     // divides.  16-byte chunks need both sub-tile extents to be at least 4.
-    const int64_t lo = vec ? 4 : 1;
-    auto fit = [&](int64_t extent, int64_t cap) {
+    // x rows (read along N) need sub-tiles at least a chunk wide (sn >= 4 for 16-byte reads), y
+    // rows (written along M) likewise (sm >= 4 for 16-byte writes).
+    auto fit = [&](int64_t extent, int64_t cap, int64_t lo) {
         int64_t e = aligned ? cap : std::min<int64_t>(cap, int64_t{1} << ilog2(extent));
         if (aligned)
             while (extent % e != 0)
                 e /= 2;
         return static_cast<int>(std::max(e, lo));
     };
+    const int64_t lo_n = vx ? 4 : 1, lo_m = vy ? 4 : 1;
     if (N < kTrSub && M >= kTrSub) {  // narrow rows of x: long along M
-        plan->sn = fit(N, kTrSub);
-        plan->sm = fit(M, kTrSubElems / plan->sn);
+        plan->sn = fit(N, kTrSub, lo_n);
+        plan->sm = fit(M, kTrSubElems / plan->sn, lo_m);
     } else {
-        plan->sm = fit(M, kTrSub);
-        plan->sn = fit(N, kTrSubElems / plan->sm);
+        plan->sm = fit(M, kTrSub, lo_m);
+        plan->sn = fit(N, kTrSubElems / plan->sm, lo_n);
     }
+    plan->vx = vx;
+    plan->vy = vy;
     const int64_t subs_m = ceil_div(M, plan->sm), subs_n = ceil_div(N, plan->sn);
     if (subs_m > INT32_MAX || subs_n > INT32_MAX)
         return TM_E_UNSUPPORTED;

@@ -191,7 +191,8 @@ int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int 
 
 struct TransposePlan {
     bool launch = false;
-    bool vec = false;             // 16-byte chunks on both sides
+    bool vec = false;             // 16-byte chunks on both sides (vx && vy)
+    bool vx = false, vy = false;  // 16-byte chunks on the read side (x rows) / the write side (y rows)
     int aligned = 0;
     int sm = 1, sn = 1;           // staged sub-tile extents (powers of two, sm * sn <= kTrSubElems)
     int log_g = 0;                // batches per work item: 2^log_g (whole matrices in one sub-tile)

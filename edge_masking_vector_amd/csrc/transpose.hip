@@ -57,19 +57,26 @@ static_assert(sizeof(TrArgs) <= 128, "transpose arguments outgrew one scalar loa
 
 // PACK: every matrix fits in one sub-tile, and a work item takes 2^log_g consecutive batches, each
 // staged in its own LDS region (a 256-thread workgroup per 4 x 4 matrix left 240 threads idle).
-template <bool VEC, bool ALIGNED, int BS, bool WIDE, bool PACK>
+// VX / VY: x's rows (the reads) / y's rows (the writes) move in 16-byte chunks, each side as its
+// own rows allow (a 9163 x 1051 transpose with 16-byte x rows and 4-byte y rows took 42 us with
+// 4-byte chunks on both sides).
+template <bool VX, bool VY, bool ALIGNED, int BS, bool WIDE, bool PACK>
 __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
-    constexpr int LOG_W = VEC ? 2 : 0;
-    constexpr int W = 1 << LOG_W;
-    constexpr int K = kSubElems / W / BS;     // chunks per thread for a full sub-tile
+    static_assert(!ALIGNED || (VX && VY), "the promise implies 16-byte rows on both sides");
+    constexpr int LOG_WX = VX ? 2 : 0, LOG_WY = VY ? 2 : 0;
+    constexpr int WX = 1 << LOG_WX, WY = 1 << LOG_WY;
+    constexpr int KX = kSubElems / WX / BS;   // read chunks per thread for a full sub-tile
+    constexpr int KY = kSubElems / WY / BS;   // write chunks per thread
     __shared__ float tile[kStage];
     const int t = threadIdx.x;
-    // Sub-tile extents are powers of two of at least W elements: chunk coordinates are shifts
+    // Sub-tile extents are powers of two of at least the chunk width: chunk coordinates are shifts
     // and masks (run-time divisions per chunk took the 4096 x 4096 transpose from 25.5 to 27.5 us).
-    const int lcx = a.log_sn - LOG_W;   // log2 of the chunks per staged x row
-    const int lcy = a.log_sm - LOG_W;   // log2 of the chunks per y row
-    const int lt = a.log_sm + a.log_sn - LOG_W;         // log2 of the chunks of one sub-tile
-    const int nchunks = 1 << (lt + (PACK ? a.log_g : 0));  // chunks of the work item
+    const int lcx = a.log_sn - LOG_WX;  // log2 of the chunks per staged x row
+    const int lcy = a.log_sm - LOG_WY;  // log2 of the chunks per y row
+    const int ltx = a.log_sm + a.log_sn - LOG_WX;  // log2 of the read chunks of one sub-tile
+    const int lty = a.log_sm + a.log_sn - LOG_WY;  // log2 of the write chunks of one sub-tile
+    const int nx = 1 << (ltx + (PACK ? a.log_g : 0));  // read chunks of the work item
+    const int ny = 1 << (lty + (PACK ? a.log_g : 0));  // write chunks of the work item
     const int sm = 1 << a.log_sm, sn = 1 << a.log_sn;
     const int pad = sn + 1;             // LDS row stride: odd for SN >= 2, so columns spread over banks
     const int stage = sm * pad;         // LDS floats of one staged sub-tile (PACK: one per batch)
@@ -101,26 +108,26 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
         const int64_t col0 = int64_t(pn) * sn;     // x columns = y rows
         const int64_t rows_live = a.M - row0, cols_live = a.N - col0;
         // Chunk e of the work item belongs to batch b0 + (e >> lt) (PACK; else b) and is chunk
-        // e & (2^lt - 1) of that batch's sub-tile.
+        // e & (2^lt - 1) of that batch's sub-tile (lt: ltx for reads, lty for writes).
         const int64_t b0 = PACK ? int64_t(b) << a.log_g : int64_t(b);
-        auto batch_of = [&](int e) { return PACK ? b0 + (e >> lt) : b0; };
-        auto in_tile = [&](int e) { return PACK ? e & ((1 << lt) - 1) : e; };
+        auto batch_of = [&](int e, int lt) { return PACK ? b0 + (e >> lt) : b0; };
+        auto in_tile = [&](int e, int lt) { return PACK ? e & ((1 << lt) - 1) : e; };
 
         // Read x's sub-tile along its rows (all of this thread's chunks first); an element past
         // the tensor reads as 0.
-        float v[K][W];
+        float v[KX][WX];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int e = t + k * BS, et = in_tile(e);
-            const int r = et >> lcx, c = (et & ((1 << lcx) - 1)) << LOG_W;
-            const int64_t bb = batch_of(e);
+        for (int k = 0; k < KX; ++k) {
+            const int e = t + k * BS, et = in_tile(e, ltx);
+            const int r = et >> lcx, c = (et & ((1 << lcx) - 1)) << LOG_WX;
+            const int64_t bb = batch_of(e, ltx);
             const float *p = a.x + bb * a.bsx + (row0 + r) * a.ldx + col0 + c;
 #pragma unroll
-            for (int i = 0; i < W; ++i)
+            for (int i = 0; i < WX; ++i)
                 v[k][i] = 0.0f;
-            if (e < nchunks && (!PACK || bb < a.B)) {
-                if (ALIGNED || (r < rows_live && c + W <= cols_live)) {
-                    if constexpr (VEC) {
+            if (e < nx && (!PACK || bb < a.B)) {
+                if (ALIGNED || (r < rows_live && c + WX <= cols_live)) {
+                    if constexpr (VX) {
                         const f4 q = ld16_nt(p);
                         v[k][0] = q.x, v[k][1] = q.y, v[k][2] = q.z, v[k][3] = q.w;
                     } else {
@@ -128,19 +135,19 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
                     }
                 } else {
 #pragma unroll
-                    for (int i = 0; i < W; ++i)
+                    for (int i = 0; i < WX; ++i)
                         v[k][i] = (r < rows_live && c + i < cols_live) ? p[i] : 0.0f;
                 }
             }
         }
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int e = t + k * BS, et = in_tile(e);
-            const int r = et >> lcx, c = (et & ((1 << lcx) - 1)) << LOG_W;
-            const int g = PACK ? e >> lt : 0;
-            if (e < nchunks) {
+        for (int k = 0; k < KX; ++k) {
+            const int e = t + k * BS, et = in_tile(e, ltx);
+            const int r = et >> lcx, c = (et & ((1 << lcx) - 1)) << LOG_WX;
+            const int g = PACK ? e >> ltx : 0;
+            if (e < nx) {
 #pragma unroll
-                for (int i = 0; i < W; ++i)
+                for (int i = 0; i < WX; ++i)
                     tile[g * stage + r * pad + c + i] = v[k][i];
             }
         }
@@ -148,34 +155,35 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
 
         // Write y's rows: y row j (x column col0 + j) takes the staged column j; a store past the
         // tensor is skipped.
+        float u[KY][WY];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int e = t + k * BS, et = in_tile(e);
-            const int j = et >> lcy, i = (et & ((1 << lcy) - 1)) << LOG_W;
-            const int g = PACK ? e >> lt : 0;
-            if (e < nchunks) {
+        for (int k = 0; k < KY; ++k) {
+            const int e = t + k * BS, et = in_tile(e, lty);
+            const int j = et >> lcy, i = (et & ((1 << lcy) - 1)) << LOG_WY;
+            const int g = PACK ? e >> lty : 0;
+            if (e < ny) {
 #pragma unroll
-                for (int q = 0; q < W; ++q)
-                    v[k][q] = tile[g * stage + (i + q) * pad + j];
+                for (int q = 0; q < WY; ++q)
+                    u[k][q] = tile[g * stage + (i + q) * pad + j];
             }
         }
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int e = t + k * BS, et = in_tile(e);
-            const int j = et >> lcy, i = (et & ((1 << lcy) - 1)) << LOG_W;
-            const int64_t bb = batch_of(e);
+        for (int k = 0; k < KY; ++k) {
+            const int e = t + k * BS, et = in_tile(e, lty);
+            const int j = et >> lcy, i = (et & ((1 << lcy) - 1)) << LOG_WY;
+            const int64_t bb = batch_of(e, lty);
             float *q = a.y + bb * a.bsy + (col0 + j) * a.ldy + row0 + i;
-            if (e < nchunks && (!PACK || bb < a.B)) {
-                if (ALIGNED || (j < cols_live && i + W <= rows_live)) {
-                    if constexpr (VEC)
-                        st16_nt(q, f4{v[k][0], v[k][1], v[k][2], v[k][3]});
+            if (e < ny && (!PACK || bb < a.B)) {
+                if (ALIGNED || (j < cols_live && i + WY <= rows_live)) {
+                    if constexpr (VY)
+                        st16_nt(q, f4{u[k][0], u[k][1], u[k][2], u[k][3]});
                     else
-                        st4_nt(q, v[k][0]);
+                        st4_nt(q, u[k][0]);
                 } else if (j < cols_live) {
 #pragma unroll
-                    for (int z = 0; z < W; ++z)
+                    for (int z = 0; z < WY; ++z)
                         if (i + z < rows_live)
-                            q[z] = v[k][z];
+                            q[z] = u[k][z];
                 }
             }
         }
@@ -387,10 +395,14 @@ hipError_t launch_packed(const tmp::TransposePlan &p, hipStream_t stream) {
 
 template <bool WIDE, bool PACK>
 const void *pick(const tmp::TransposePlan &p) {
-    if (!p.vec)
-        return reinterpret_cast<const void *>(&transpose_tiles<false, false, kTrBlock, WIDE, PACK>);
-    return p.aligned ? reinterpret_cast<const void *>(&transpose_tiles<true, true, kTrBlock, WIDE, PACK>)
-                     : reinterpret_cast<const void *>(&transpose_tiles<true, false, kTrBlock, WIDE, PACK>);
+    if (p.vx && p.vy)
+        return p.aligned ? reinterpret_cast<const void *>(&transpose_tiles<true, true, true, kTrBlock, WIDE, PACK>)
+                         : reinterpret_cast<const void *>(&transpose_tiles<true, true, false, kTrBlock, WIDE, PACK>);
+    if (p.vx)
+        return reinterpret_cast<const void *>(&transpose_tiles<true, false, false, kTrBlock, WIDE, PACK>);
+    if (p.vy)
+        return reinterpret_cast<const void *>(&transpose_tiles<false, true, false, kTrBlock, WIDE, PACK>);
+    return reinterpret_cast<const void *>(&transpose_tiles<false, false, false, kTrBlock, WIDE, PACK>);
 }
 
 }  // namespace

@@ -201,15 +201,18 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
     // beyond the minimum of 4 that 16-byte chunks need)
     auto p2 = [](int64_t v) { int64_t e = 1; while (e < v) e <<= 1; return e; };
     if (!p.aligned) {
-        CHECK(p.sm <= std::max<int64_t>(p.vec ? 4 : 1, p2(M)) && p.sn <= std::max<int64_t>(p.vec ? 4 : 1, p2(N)),
+        CHECK(p.sm <= std::max<int64_t>(p.vy ? 4 : 1, p2(M)) && p.sn <= std::max<int64_t>(p.vx ? 4 : 1, p2(N)),
               "%s sub-tile %dx%d wider than the view", tag, p.sm, p.sn);
         if (M >= tmp::kTrSub && N >= tmp::kTrSub)
             CHECK(p.sm == tmp::kTrSub && p.sn == tmp::kTrSub, "%s wide view not on 32 x 32", tag);
     }
     if (p.aligned)
         CHECK(M % p.sm == 0 && N % p.sn == 0, "%s promised sub-tiles are not whole", tag);
-    if (p.vec)
-        CHECK(p.sm >= 4 && p.sn >= 4, "%s 16-byte chunks need sub-tiles of 4+", tag);
+    CHECK(p.vec == (p.vx && p.vy), "%s vec flag", tag);
+    if (p.vx)
+        CHECK(p.sn >= 4, "%s 16-byte reads need sub-tile rows of 4+", tag);
+    if (p.vy)
+        CHECK(p.sm >= 4, "%s 16-byte writes need sub-tile columns of 4+", tag);
     if (p.packed != 0) {
         // few channels with a packed side: C = the narrow extent, S positions per work item
         const bool m0 = p.packed == 1;

@@ -133,6 +133,23 @@ def test_transpose_packed_side(dev):
         check_transpose(dev, B, M, N, ldx, ldy, bsx, bsy, 1, 1, 0, xoff, yoff, seed=M * 3 + N)
 
 
+def test_transpose_one_side_aligned(dev):
+    """Only x's rows (or only y's rows) start on 16-byte boundaries: that side moves 16-byte
+    chunks, the other single elements; ragged edges, batches, misaligned bases."""
+    for (B, M, N, ldx, ldy, bsx, bsy, xoff, yoff) in (
+            (1, 2951, 2696, 2700, 2951, 0, 0, 0, 0),          # 16-byte reads only
+            (1, 2696, 2951, 2951, 2700, 0, 0, 0, 0),          # 16-byte writes only
+            (1, 1001, 1003, 1004, 1001, 0, 0, 0, 0),
+            (2, 333, 777, 780, 335, 333 * 780, 777 * 335 + 1, 0, 0),
+            (2, 777, 333, 333, 780, 777 * 333 + 3, 333 * 780, 0, 0),
+            (1, 1000, 1000, 1000, 1000, 0, 0, 1, 0),          # x base off 16 bytes
+            (1, 1000, 1000, 1000, 1000, 0, 0, 0, 3),          # y base off 16 bytes
+            (3, 2, 50, 52, 3, 120, 150, 0, 0),                # narrow, writes of rows of 2
+            (3, 50, 2, 2, 52, 100, 110, 0, 0)):
+        note("one side aligned B=%d M=%d N=%d ld=%d/%d off=%d/%d" % (B, M, N, ldx, ldy, xoff, yoff))
+        check_transpose(dev, B, M, N, ldx, ldy, bsx, bsy, 64, 64, 0, xoff, yoff, seed=M + 2 * N)
+
+
 def test_transpose_many_small_matrices(dev):
     """Batches of small matrices, several per workgroup (each matrix fits one sub-tile): whole
     and partial last work items, batch strides with gaps, padded and odd row strides, misaligned
