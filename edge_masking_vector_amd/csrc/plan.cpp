@@ -693,6 +693,15 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
         plan->sm = fit(M, kTrSub, lo_m);
         plan->sn = fit(N, kTrSubElems / plan->sm, lo_n);
     }
+    // Rows on no 16-byte boundary on either side (odd strides): every 128-byte row piece straddles
+    // two lines, and taller sub-tiles with longer y-row pieces did better.  64 x 16 against 32 x 32
+    // (1 GiB of rotating buffers, outputs compared bit for bit): 4099 x 4099 66.5 -> 56.0 us,
+    // 9163 x 1051 43.5 -> 31.8, 2951 x 2697 36.8 -> 32.2, 17827 x 767 64.0 -> 59.3; small
+    // matrices (1001 x 1001: 5.0 against 5.4 us) keep 32 x 32.
+    if (!vx && !vy && !aligned && M >= 2 * kTrSub && N >= kTrSub && M * N >= (int64_t{1} << 22)) {
+        plan->sm = 2 * kTrSub;
+        plan->sn = kTrSub / 2;
+    }
     plan->vx = vx;
     plan->vy = vy;
     const int64_t subs_m = ceil_div(M, plan->sm), subs_n = ceil_div(N, plan->sn);

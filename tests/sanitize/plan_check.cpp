@@ -203,8 +203,13 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
     if (!p.aligned) {
         CHECK(p.sm <= std::max<int64_t>(p.vy ? 4 : 1, p2(M)) && p.sn <= std::max<int64_t>(p.vx ? 4 : 1, p2(N)),
               "%s sub-tile %dx%d wider than the view", tag, p.sm, p.sn);
-        if (M >= tmp::kTrSub && N >= tmp::kTrSub)
-            CHECK(p.sm == tmp::kTrSub && p.sn == tmp::kTrSub, "%s wide view not on 32 x 32", tag);
+        if (M >= tmp::kTrSub && N >= tmp::kTrSub) {
+            // 32 x 32, or 64 x 16 for large views with no 16-byte rows on either side
+            const bool tall = !p.vx && !p.vy && M >= 2 * tmp::kTrSub && M * N >= (int64_t{1} << 22);
+            CHECK(tall ? (p.sm == 2 * tmp::kTrSub && p.sn == tmp::kTrSub / 2)
+                       : (p.sm == tmp::kTrSub && p.sn == tmp::kTrSub),
+                  "%s wide view on %dx%d sub-tiles", tag, p.sm, p.sn);
+        }
     }
     if (p.aligned)
         CHECK(M % p.sm == 0 && N % p.sn == 0, "%s promised sub-tiles are not whole", tag);
@@ -320,6 +325,17 @@ static void check_transposes() {
                         replay_transpose(p, B, M, N, tag);
                     }
     CHECK(packed_plans > 0, "no packed-side transpose planned");
+    // odd strides on both sides (no 16-byte rows): large views take 64 x 16 sub-tiles
+    for (int64_t M : {int64_t{64}, int64_t{4099}, int64_t{9163}})
+        for (int64_t N : {int64_t{33}, int64_t{1051}, int64_t{4099}}) {
+            tmp::TransposePlan p;
+            const int st = tmp::plan_transpose(fake(0x100004), N, 0, const_cast<float *>(fake(0x40000004)), M, 0, 1, M,
+                                               N, 1, 1, 0, &p);
+            CHECK(st == TM_OK && p.launch, "odd-stride transpose %ldx%ld refused", long(M), long(N));
+            char tag[96];
+            std::snprintf(tag, sizeof tag, "odd-stride transpose M=%ld N=%ld", long(M), long(N));
+            replay_transpose(p, 1, M, N, tag);
+        }
     // divisors of every size up to 5000, against plain division
     for (uint32_t d = 1; d <= 5000; ++d) {
         const tmp::Div32 v = tmp::make_div32(d);

@@ -150,6 +150,16 @@ def test_transpose_one_side_aligned(dev):
         check_transpose(dev, B, M, N, ldx, ldy, bsx, bsy, 64, 64, 0, xoff, yoff, seed=M + 2 * N)
 
 
+def test_transpose_odd_strides_large(dev):
+    """Large views with no 16-byte rows on either side (odd strides, 64 x 16 sub-tiles), ragged in
+    both directions and batched."""
+    for (B, M, N, ldx, ldy, bsx, bsy) in ((1, 4099, 4099, 4099, 4099, 0, 0),
+                                          (1, 9163, 1051, 1051, 9163, 0, 0),
+                                          (2, 2951, 1423, 1425, 2953, 2951 * 1425 + 1, 1423 * 2953 + 3)):
+        note("odd strides B=%d M=%d N=%d ld=%d/%d" % (B, M, N, ldx, ldy))
+        check_transpose(dev, B, M, N, ldx, ldy, bsx, bsy, 64, 64, 0, seed=M + N)
+
+
 def test_transpose_many_small_matrices(dev):
     """Batches of small matrices, several per workgroup (each matrix fits one sub-tile): whole
     and partial last work items, batch strides with gaps, padded and odd row strides, misaligned
