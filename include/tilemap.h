@@ -151,7 +151,9 @@ int tm_rowsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t N,
 /* Bytes of device workspace tm_colsum needs for these arguments (0 when M == 0 or N == 0, and
  * also 0 for invalid arguments, which tm_colsum then rejects): 4 * N * (number of row slabs), where
  * a slab is TM rows for the naive walks and 256 rows for the LDS walk (taller, doubling, while
- * there would be more than 4096 slabs); 0 when the LDS walk takes its one-pass form (at most 64
+ * there would be more than 4096 slabs; shorter, halving, while there would be fewer than 1024
+ * slabs x column strips of up to 128 columns, down to 32 rows, or 4096 / strip width rows for
+ * narrower strips); 0 when the LDS walk takes its one-pass form (at most 64
  * rows, or at most 256 rows of at least 262144 columns: each thread adds one 16-byte column chunk
  * down all M rows and writes the sums, so there are no partials). */
 size_t tm_colsum_workspace_bytes(int64_t M, int64_t N, int TM, int TN, int walk);
