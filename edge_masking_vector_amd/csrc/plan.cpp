@@ -23,7 +23,9 @@ bool aligned_to(const void *p, uintptr_t a) {
     return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
 
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// a >= 0, b > 0; no intermediate sum, so it holds up to INT64_MAX (the size queries take any
+// extents).
+int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
 
 // One M x N view with row stride ld.  `work`: the call will touch it (M > 0 and N > 0).
 int check_view(const void *p, int64_t M, int64_t N, int64_t ld, bool work) {
@@ -82,7 +84,7 @@ Div32 make_div32(uint32_t d) {
 
 int ilog2(int64_t v) {
     int l = 0;
-    while ((int64_t{1} << l) < v)
+    while (l < 62 && (int64_t{1} << l) < v)  // saturates at 2^62 (no shift past the sign bit)
         ++l;
     return l;
 }
@@ -518,7 +520,11 @@ int slab_log(int64_t M, int64_t N, int TM, int walk) {
     const int64_t tw = N >= kColStrip ? kColStrip : std::max<int64_t>(1, int64_t{1} << ilog2(N));
     const int64_t strips = ceil_div(N, tw);
     const int lmin = std::max(5, ilog2(std::max<int64_t>(1, 4096 / tw)));
-    while (l > lmin && ceil_div(M, int64_t{1} << l) * strips < kColTargetWork)
+    if (strips == 0)
+        return l;  // N == 0: no columns, nothing to balance
+    // slabs * strips < kColTargetWork, without the product: slabs < ceil(kColTargetWork / strips)
+    const int64_t few = ceil_div(kColTargetWork, strips);
+    while (l > lmin && ceil_div(M, int64_t{1} << l) < few)
         --l;
     return l;
 }

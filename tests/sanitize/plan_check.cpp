@@ -486,7 +486,38 @@ static void check_split_rows() {
                 }
 }
 
+// Extreme extents: every planner either refuses the call or returns a plan, with no signed
+// overflow (the build runs under UndefinedBehaviorSanitizer) in the shape rules: flat views, split
+// rows, column slabs, transposes.
+static void check_extremes() {
+    const int64_t big[] = {int64_t{1} << 31, (int64_t{1} << 31) + 3, int64_t{1} << 40, int64_t{1} << 52,
+                           INT64_MAX / 8, INT64_MAX / 4, INT64_MAX};
+    float *o = const_cast<float *>(fake(0x200000));
+    for (int64_t a : big)
+        for (int64_t b : {int64_t{1}, int64_t{3}, int64_t{64}, int64_t{4096}, a}) {
+            for (int dir = 0; dir < 2; ++dir) {
+                const int64_t M = dir ? a : b, N = dir ? b : a;
+                tmp::MapPlan mp;
+                tmp::plan_map(tmp::kScale, fake(0x100000), N, o, N, M, N, 1.f, 0.f, 1, 4, 0, 0, &mp);
+                tmp::plan_map(tmp::kChannel, fake(0x100000), N, o, N, M, N, 0.f, 0.f, 1, 1, 0, 0, &mp, nullptr,
+                              fake(0x300000));
+                tmp::RowPlan rp;
+                tmp::plan_rows(tmp::kRowSoftmax, fake(0x100000), N, o, M, N, 1, 1, 0, &rp, o, true, o,
+                               tmp::rows_ws_bytes(M, N));
+                tmp::plan_rows(tmp::kRowSum, fake(0x100000), N, o, M, N, 1, 1, 0, &rp);
+                tmp::ColPlan cp;
+                const size_t w = tmp::colsum_ws_bytes(M, N, 1, 1, TM_COL_LDS);
+                tmp::plan_cols(fake(0x100000), N, o, M, N, 1, 1, 0, TM_COL_LDS, o, w, &cp);
+                tmp::TransposePlan tp;
+                tmp::plan_transpose(fake(0x100000), N, 0, o, M, 0, 1, M, N, 1, 1, 0, &tp);
+                tmp::plan_transpose(fake(0x100000), N, M * 0 + N, o, M, N, 2, M, N, 1, 1, 0, &tp);
+                ++g_checked;
+            }
+        }
+}
+
 int main() {
+    check_extremes();
     check_maps();
     check_transposes();
     check_reductions();
