@@ -124,9 +124,12 @@ int plan_tiles(int64_t M, int64_t N, int TM, int TN, int64_t *tiles_m, int64_t *
     int st = check_tile(TM, TN);
     if (st != TM_OK)
         return st;
+    const int64_t wm = M / TM, wn = N / TN;  // whole tiles along each extent
+    if (wn > 0 && wm > INT64_MAX / wn)
+        return TM_E_INVAL;  // the whole-tile count does not fit 64 bits
     *tiles_m = ceil_div(M, TM);
     *tiles_n = ceil_div(N, TN);
-    *whole = (M / TM) * (N / TN);  // tiles with (pm+1)*TM <= M and (pn+1)*TN <= N
+    *whole = wm * wn;  // tiles with (pm+1)*TM <= M and (pn+1)*TN <= N
     return TM_OK;
 }
 

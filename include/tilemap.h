@@ -262,7 +262,8 @@ int tm_split(int64_t K, int64_t T, int64_t *nfull, int64_t *rem);
 /* Tile scheduler counts ([SLICING] "Masking"): *tiles_m = ceil(M / TM), *tiles_n = ceil(N / TN) and
  * *whole = the number of tiles lying entirely inside the M x N tensor; the other tiles are edge
  * tiles, whose out-of-range elements read as 0 and whose stores are skipped.  TM_E_INVAL /
- * TM_E_UNSUPPORTED as for the tile checks of the other calls, or if an output pointer is NULL. */
+ * TM_E_UNSUPPORTED as for the tile checks of the other calls, or TM_E_INVAL if an output pointer
+ * is NULL or the whole-tile count does not fit 64 bits. */
 int tm_plan_tiles(int64_t M, int64_t N, int TM, int TN, int64_t *tiles_m, int64_t *tiles_n,
                   int64_t *whole);
 

@@ -511,6 +511,16 @@ static void check_extremes() {
                 tmp::TransposePlan tp;
                 tmp::plan_transpose(fake(0x100000), N, 0, o, M, 0, 1, M, N, 1, 1, 0, &tp);
                 tmp::plan_transpose(fake(0x100000), N, M * 0 + N, o, M, N, 2, M, N, 1, 1, 0, &tp);
+                // the host helpers exported through the C ABI
+                int64_t p1, p2, p3;
+                tmp::split(M, N, &p1, &p2);
+                tmp::split(M, 1, &p1, &p2);
+                tmp::plan_tiles(M, N, 256, 1024, &p1, &p2, &p3);
+                tmp::plan_tiles(M, N, 1, 1, &p1, &p2, &p3);
+                tmp::pad_extents(M, N, 256, 1024, &p1, &p2, &p3);
+                tmp::check_promise(M, N, N, N, 256, 1024, fake(0x100000), o);
+                tmp::rows_ws_bytes(M, N);
+                tmp::colsum_ws_bytes(M, N, 256, 64, TM_COL_NAIVE);
                 ++g_checked;
             }
         }

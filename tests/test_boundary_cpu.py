@@ -99,6 +99,9 @@ def test_split_matches_pages_and_oracle():
 def test_plan_tiles_workload_shapes():
     # ragged 4100 x 1000 under 64 x 64: 65 x 16 tiles, 64 x 15 = 960 whole
     assert tm.tm_plan_tiles(4100, 1000, 64, 64) == (tm.TM_OK, 65, 16, 960)
+    # a whole-tile count beyond 64 bits is refused, not wrapped
+    assert tm.tm_plan_tiles(1 << 40, 1 << 40, 1, 1)[0] == tm.TM_E_INVAL
+    assert tm.tm_plan_tiles(1 << 40, 1 << 22, 1, 1) == (tm.TM_OK, 1 << 40, 1 << 22, 1 << 62)
     # 4096 x 4096 under 32 x 128: all 128 x 32 = 4096 tiles whole
     assert tm.tm_plan_tiles(4096, 4096, 32, 128) == (tm.TM_OK, 128, 32, 4096)
     # the pages' edge-tile example: 20 x 28 under 8 x 8
