@@ -238,14 +238,32 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     // checked) and, on the ragged path, which chunks take the masked body; neither changes a
     // result, and TN = 512 / 1024 tiles otherwise made work items of whole 2-4 KiB tile rows,
     // 6% slower on 8192 x 8192.
-    const int TNs = static_cast<int>(std::min<int64_t>(TN, kRowSegmentBytes / 4));
+    //
+    //
+    // On the ragged path a row narrower than a row segment is scheduled as one tile exactly as
+    // wide as the row's next power of two (at least one chunk), whatever the caller's tile: with
+    // a 64-column tile, rows of 3 floats ran 3 live lanes of 64 (8.7M x 3 with row stride 7: 653
+    // against 142 us).
+    const int W = access == kScalar ? 1 : 4;
+    int TNs = static_cast<int>(std::min<int64_t>(TN, kRowSegmentBytes / 4));
+    if (!aligned && N < kRowSegmentBytes / 4) {
+        TNs = W;
+        while (TNs < N)
+            TNs *= 2;
+    }
     int64_t tiles_m, tiles_n, whole;
     plan_tiles(M, N, TM, TNs, &tiles_m, &tiles_n, &whole);
 
-    const int W = access == kScalar ? 1 : 4;
     const int log_u = ilog2(access == kScalar ? kScalarChunksPerThread : 1);
     const int log_vr = ilog2(TNs / W);
-    const int log_tm = ilog2(TM);
+    int log_tm = ilog2(TM);
+    // A row that fits one scheduling tile cannot widen a work item, so on the ragged path (where
+    // the tile's height shapes no result either) it is scheduled in tile rows tall enough for
+    // 256 threads' chunks: a 1 x 64 tile over rows of 3 floats made work items of 3 elements.
+    // (2M x 16 with row stride 17, 4-byte chunks: items of 16 / 64 / 256 rows took 68 / 61 /
+    // 63 us; rows of 3, 5 or 8 floats within 3% of each other from 16 to 256 rows.)
+    if (!aligned && tiles_n == 1)
+        log_tm = std::max(log_tm, ilog2(kMapNarrowThreads) + log_u - log_vr);
     // Widest tile group: in the aligned path it must divide the tile count (no tile checks on the
     // device); in the ragged path it may run past the last tile (those lanes stay idle).
     int log_gcap = 0;

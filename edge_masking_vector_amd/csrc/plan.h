@@ -18,6 +18,7 @@ constexpr int kMaxTN = 1024;  // column tile (TN, BC) menu: 1, 2, 4, ..., 1024
 constexpr int kBlock = 256;   // threads per workgroup of the reductions (4 wave64s)
 constexpr int kMapMinBlock = 64;    // map workgroups: at least one wave ...
 constexpr int kMapMaxBlock = 1024;  // ... and at most 1024 threads
+constexpr int kMapNarrowThreads = 256;  // ragged rows narrower than a segment: threads per work item
 constexpr int kScalarChunksPerThread = 4;  // 4-byte chunks per thread (16-byte chunks: one)
 constexpr int kLineBytes = 128;     // cache line
 constexpr int kRowSegmentBytes = 512;  // map work items: bytes of each row they move, at least ...

@@ -153,7 +153,7 @@ static void replay_map(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, 
 }
 
 static void check_maps() {
-    const int64_t Ms[] = {0, 1, 3, 17, 64, 100};
+    const int64_t Ms[] = {0, 1, 3, 17, 64, 100, 1000};
     const int64_t Ns[] = {0, 1, 4, 17, 64, 129, 1000};
     const int TMs[] = {1, 4, 32, 256};
     const int TNs[] = {1, 4, 16, 128, 1024};
@@ -165,7 +165,7 @@ static void check_maps() {
                 for (int TM : TMs)
                     for (int TN : TNs)
                         for (int aligned = 0; aligned <= 1; ++aligned)
-                            for (int variant = 1; variant <= 3; ++variant)
+                            for (int variant = 0; variant <= 3; ++variant)
                                 for (uintptr_t base : bases)
                                     for (int op : {int(tmp::kScale), int(tmp::kChannel)}) {
                                         tmp::MapPlan p;

@@ -484,6 +484,23 @@ def test_channel_affine_brute_force_tiny(dev):
                                   seed=M * 100 + N)
 
 
+@pytest.mark.parametrize("N,ld", [(1, 3), (3, 7), (5, 6), (8, 12), (3, 32)])
+def test_narrow_padded_rows(dev, N, ld):
+    """Rows narrower than the tile on the ragged path are scheduled in narrower, taller tiles:
+    rows of 1-8 floats with padded strides (16-byte rows for ld 12 and 32), tiles from 1 x 64 to
+    64 x 1024, a row count that ends inside a tile row, every op and the channel op, bit for
+    bit with the oracle and guard bands intact."""
+    M = 70001
+    xh = inputs.uniform(N * 31 + ld, (M - 1) * ld + N, -8.0, 8.0)
+    for (TM, TN) in ((1, 64), (64, 64), (64, 1024), (4, 4)):
+        for variant in (tm.TM_VAR_AUTO, tm.TM_VAR_SCALAR):
+            for op in ("affine", "copy"):
+                note("narrow rows %s M=%d N=%d ld=%d tile %dx%d var=%d" % (op, M, N, ld, TM, TN, variant))
+                check_case(dev, op, M, N, ld, ld, TM, TN, 0, variant, xh)
+            note("narrow rows channel M=%d N=%d ld=%d tile %dx%d var=%d" % (M, N, ld, TM, TN, variant))
+            check_channel(dev, M, N, ld, ld, TM, TN, 0, variant, True, seed=N + ld)
+
+
 # ---- tile-size sweep / autotune ------------------------------------------------------------------
 
 def test_every_sweep_tile_at_8192(dev):
