@@ -314,7 +314,12 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
         log_g = std::min(log_gcap, std::max(log_g, log_target - log_vr - log_r));
     } else {
         const int log_target = ilog2(kMapMaxBlock) + log_u;
-        log_g = std::min(log_gcap, std::max(0, log_target - log_vr));
+        // The channel op's U chunks per thread (4-byte chunks) share one read of the channel
+        // vectors when the item spans at least U rows, so it keeps room for them (a bias add over
+        // 4270 x 3017 with row stride 3049: 1024-column items of 4 rows instead of 4096-column
+        // items of one row, of which 3017 columns live).
+        const int log_rows_min = op == kChannel ? std::min(log_tm, log_u) : 0;
+        log_g = std::min(log_gcap, std::max(0, log_target - log_vr - log_rows_min));
         log_r = std::min(log_tm, std::max(0, log_target - log_vr - log_g));
     }
     // A strip of whole rows of an output whose rows are contiguous (ldy == N) is one contiguous
