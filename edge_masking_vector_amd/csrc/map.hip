@@ -250,7 +250,13 @@ __device__ __forceinline__ void store_seg(__amdgpu_buffer_rsrc_t r, int off, typ
 // tmp::kStreamSegmentBytes (one row segment, or whole rows of a view whose rows are contiguous;
 // chosen on the host); whole items store it through a buffer resource with the device-scope
 // streaming policy.
-template <int OP, int ACC, bool ALIGNED, int U, bool GUARD, bool STREAM>
+//
+// SHARE (channel op, 4-byte chunks): every thread's U chunks lie in one column (the work item is no
+// wider than the workgroup's chunks, G * VR <= threads; chunk q + u * threads then sits in the
+// column of chunk q), so its channel vectors are read once, for the first chunk, and held in one
+// register each (a live chunk implies its thread's first chunk is: rows grow with u).  Known when
+// compiling, this keeps the scalar channel kernel's registers near the plain map's.
+template <int OP, int ACC, bool ALIGNED, int U, bool GUARD, bool STREAM, bool SHARE>
 __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
     using T = typename Chunk<ACC>::T;
     constexpr int W = Chunk<ACC>::W;
@@ -297,13 +303,7 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
                                            absent);
             return load_cvec<ACC>(v, col, live, a.cvec16, absent);
         };
-        // When a work item is no wider than the workgroup's chunks (G * VR <= threads), chunk
-        // q + u * threads lies in the column of chunk q: a thread's U chunks share one column, and
-        // its channel vectors are read once, for the first chunk (a chunk that is live implies
-        // its thread's first chunk is: rows grow with u, the column is the same).  The shared
-        // vectors are picked where they are used, after every load is issued: copying them at
-        // the loads made each copy wait for the first read (10% slower on 41698 x 561).
-        const bool share = U > 1 && a.log_gv <= a.log_bs;
+        constexpr int CV = SHARE ? 1 : U;  // channel vector registers per thread
 
         // Whole tiles (every tile, when the promise was checked; otherwise this work item's tiles
         // all lie inside the tensor): no masks.
@@ -316,14 +316,14 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
             if constexpr (STREAM) {
                 // The item's output block starts at (row0, col0); chunk q lies 4 W q bytes into it.
                 const __amdgpu_buffer_rsrc_t ry = segment_rsrc(a.y + row0 * a.ldy + col0, tmp::kStreamSegmentBytes);
-                T v[U], cs[U], cb[U];
+                T v[U], cs[CV], cb[CV];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const uint32_t q = t + (uint32_t(u) << a.log_bs);
                     const int64_t row = chunk_row(q), col = chunk_col(q);
                     v[u] = load_chunk<ACC>(a.x + row * a.ldx + col, a.estep);
                     if constexpr (OP == tmp::kChannel) {
-                        if (u == 0 || !share) {
+                        if (!SHARE || u == 0) {
                             cs[u] = cvec(a.scale, col, W, 1.0f);
                             cb[u] = cvec(a.bias, col, W, 0.0f);
                         }
@@ -334,13 +334,13 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
                     const uint32_t q = t + (uint32_t(u) << a.log_bs);
                     T r;
                     if constexpr (OP == tmp::kChannel)
-                        r = apply_channel(v[u], cs[share ? 0 : u], cb[share ? 0 : u]);
+                        r = apply_channel(v[u], cs[SHARE ? 0 : u], cb[SHARE ? 0 : u]);
                     else
                         r = apply<OP>(v[u], a.alpha, a.beta);
                     store_seg<ACC>(ry, int(q) * (4 * W), r);
                 }
             } else {
-                T v[U], cs[U], cb[U];
+                T v[U], cs[CV], cb[CV];
                 int64_t yo[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
                     if (!GUARD || q < chunks) {
                         v[u] = load_chunk<ACC>(a.x + row * a.ldx + col, a.estep);
                         if constexpr (OP == tmp::kChannel) {
-                            if (u == 0 || !share) {
+                            if (!SHARE || u == 0) {
                                 cs[u] = cvec(a.scale, col, W, 1.0f);
                                 cb[u] = cvec(a.bias, col, W, 0.0f);
                             }
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
                     if (!GUARD || t + (uint32_t(u) << a.log_bs) < chunks) {
                         T r;
                         if constexpr (OP == tmp::kChannel)
-                            r = apply_channel(v[u], cs[share ? 0 : u], cb[share ? 0 : u]);
+                            r = apply_channel(v[u], cs[SHARE ? 0 : u], cb[SHARE ? 0 : u]);
                         else
                             r = apply<OP>(v[u], a.alpha, a.beta);
                         store_chunk<ACC>(a.y + yo[u], r, a.estep);
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
         } else if constexpr (!ALIGNED) {
             // Edge tiles: an element past the tensor reads as 0 and its store is skipped; a chunk
             // of a whole tile still moves unmasked.
-            T v[U], cs[U], cb[U];
+            T v[U], cs[CV], cb[CV];
             bool on[U], whole[U];
             int64_t live[U], yo[U];
 #pragma unroll
@@ -387,9 +387,11 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
                 v[u] = T(0.0f);  // a masked element reads as 0
                 if (on[u]) {
                     const float *xp = a.x + row * a.ldx + col;
-                    v[u] = whole[u] ? load_chunk<ACC>(xp, a.estep) : load_masked<ACC>(xp, live[u], a.estep);
+                    // (A live 4-byte chunk is always whole: one streamed access, whatever its tile.)
+                    v[u] = W == 1 || whole[u] ? load_chunk<ACC>(xp, a.estep)
+                                              : load_masked<ACC>(xp, live[u], a.estep);
                     if constexpr (OP == tmp::kChannel) {
-                        if (u == 0 || !share) {
+                        if (!SHARE || u == 0) {
                             cs[u] = cvec(a.scale, col, live[u], 1.0f);
                             cb[u] = cvec(a.bias, col, live[u], 0.0f);
                         }
@@ -401,10 +403,10 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
                 if (on[u]) {  // a masked store is skipped
                     T r;
                     if constexpr (OP == tmp::kChannel)
-                        r = apply_channel(v[u], cs[share ? 0 : u], cb[share ? 0 : u]);
+                        r = apply_channel(v[u], cs[SHARE ? 0 : u], cb[SHARE ? 0 : u]);
                     else
                         r = apply<OP>(v[u], a.alpha, a.beta);
-                    if (whole[u])
+                    if (W == 1 || whole[u])
                         store_chunk<ACC>(a.y + yo[u], r, a.estep);
                     else
                         store_masked<ACC>(a.y + yo[u], r, live[u], a.estep);
@@ -415,30 +417,35 @@ __global__ __launch_bounds__(kMaxBlock) void map_tiles(MapArgs a) {
     } while (w < a.nwork);
 }
 
-template <int OP, int ACC, bool GUARD>
+template <int OP, int ACC, bool GUARD, bool SHARE>
 const void *pick_aligned(const tmp::MapPlan &p) {
     constexpr int U = ACC == tmp::kScalar ? tmp::kScalarChunksPerThread : 1;
-    return p.aligned ? reinterpret_cast<const void *>(&map_tiles<OP, ACC, true, U, GUARD, false>)
-                     : reinterpret_cast<const void *>(&map_tiles<OP, ACC, false, U, GUARD, false>);
+    return p.aligned ? reinterpret_cast<const void *>(&map_tiles<OP, ACC, true, U, GUARD, false, SHARE>)
+                     : reinterpret_cast<const void *>(&map_tiles<OP, ACC, false, U, GUARD, false, SHARE>);
 }
 
-template <int OP, int ACC>
+template <int OP, int ACC, bool SHARE>
 const void *pick_guard(const tmp::MapPlan &p) {
     constexpr int U = ACC == tmp::kScalar ? tmp::kScalarChunksPerThread : 1;
     if constexpr (ACC != tmp::kVec4Understated) {
         if (p.stream)
-            return p.aligned ? reinterpret_cast<const void *>(&map_tiles<OP, ACC, true, U, false, true>)
-                             : reinterpret_cast<const void *>(&map_tiles<OP, ACC, false, U, false, true>);
+            return p.aligned ? reinterpret_cast<const void *>(&map_tiles<OP, ACC, true, U, false, true, SHARE>)
+                             : reinterpret_cast<const void *>(&map_tiles<OP, ACC, false, U, false, true, SHARE>);
     }
-    return p.guard ? pick_aligned<OP, ACC, true>(p) : pick_aligned<OP, ACC, false>(p);
+    return p.guard ? pick_aligned<OP, ACC, true, SHARE>(p) : pick_aligned<OP, ACC, false, SHARE>(p);
 }
 
 template <int OP>
 const void *pick_access(const tmp::MapPlan &p) {
     switch (p.access) {
-    case tmp::kScalar: return pick_guard<OP, tmp::kScalar>(p);
-    case tmp::kVec4Understated: return pick_guard<OP, tmp::kVec4Understated>(p);
-    default: return pick_guard<OP, tmp::kVec4>(p);
+    case tmp::kScalar:
+        if constexpr (OP == tmp::kChannel) {
+            if (p.share)
+                return pick_guard<OP, tmp::kScalar, true>(p);
+        }
+        return pick_guard<OP, tmp::kScalar, false>(p);
+    case tmp::kVec4Understated: return pick_guard<OP, tmp::kVec4Understated, false>(p);
+    default: return pick_guard<OP, tmp::kVec4, false>(p);
     }
 }
 

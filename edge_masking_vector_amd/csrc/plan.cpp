@@ -349,6 +349,8 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     plan->log_strips = log_tm - log_r;
     plan->log_bs = std::max(ilog2(kMapMinBlock), log_chunks - log_u);
     plan->guard = plan->log_bs + log_u > log_chunks;
+    // A thread's chunks t + u * threads share one column when the item is no wider than that.
+    plan->share = op == kChannel && log_u > 0 && plan->log_gv <= plan->log_bs;
     plan->stream = stream;
     plan->group = 1u << log_g;
     plan->groups_n = static_cast<uint32_t>(groups_n);

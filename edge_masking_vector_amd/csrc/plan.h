@@ -98,6 +98,7 @@ struct MapPlan {
     int log_strips = 0;           // log2(TM / R)
     int log_bs = 6;               // log2(threads per workgroup)
     bool guard = false;           // threads x chunks per thread exceed the work item's chunks
+    bool share = false;           // channel op: a thread's chunks share one column's vectors
     bool stream = false;          // work item = one row segment of kStreamSegmentBytes (one wave,
                                   // 16-byte chunks); whole items use buffer accesses sc1 nt
     uint32_t group = 1;           // G
