@@ -561,3 +561,76 @@ def test_channel_affine_on_nhwc_view():
             for h in range(H):
                 for w in range(W):
                     assert y[((bb * H + h) * W + w) * C + c] == b[c]
+
+
+# ---- row strides of scale, copy and the per-channel op ------------------------------------------
+# teenygrad "Memory Coalescing and Tensor Layout", "The alignment constraint" (and item 5 of "A
+# checklist"): a kernel must use the row stride it is passed, never the row length, because rows
+# may be padded.  Each function below gets M > 1 rows with ldx != ldy (both ways round), inputs
+# whose padding columns hold sentinels, outputs pre-filled with another sentinel, and an
+# expectation built index by index from the passed strides: element (i, j) of y at i*ldy + j
+# comes from i*ldx + j of x, and nothing else in y changes.
+
+_STRIDE_CASES = [(6, 5, 9, 7), (5, 7, 7, 12), (4, 3, 3, 8), (7, 4, 11, 4)]  # (M, N, ldx, ldy)
+_X_PAD = np.float32(-9.5e37)   # never a legal output of the ops on these inputs
+_Y_PAD = np.float32(7.25e37)
+
+
+def _strided_input(M, N, ldx, ldy, seed):
+    """x with distinct values in its M x N window, sentinels in its padding, and room for a reader
+    that uses the wrong stride (M * max(ldx, ldy) elements) so that such a mistake reads
+    sentinels instead of running off the buffer."""
+    size = M * max(ldx, ldy) + 1
+    x = np.full(size, _X_PAD, np.float32)
+    vals = inputs.uniform(seed, M * N, 1.0, 2.0)
+    for i in range(M):
+        x[i * ldx:i * ldx + N] = vals[i * N:(i + 1) * N]
+    return x
+
+
+def _expect(x, ldx, ldy, M, N, size, f):
+    """Expected y, built element by element from the passed strides."""
+    want = np.full(size, _Y_PAD, np.float32)
+    for i in range(M):
+        for j in range(N):
+            want[i * ldy + j] = f(x[i * ldx + j], j)
+    return want
+
+
+def test_scale_uses_passed_strides():
+    for k, (M, N, ldx, ldy) in enumerate(_STRIDE_CASES):
+        x = _strided_input(M, N, ldx, ldy, 40 + k)
+        size = M * max(ldx, ldy) + 1
+        y = np.full(size, _Y_PAD, np.float32)
+        oracle.scale2d(x, ldx, y, ldy, M, N, 1.5)
+        want = _expect(x, ldx, ldy, M, N, size, lambda v, j: np.float32(1.5) * v)
+        assert np.array_equal(_bits(y), _bits(want)), (M, N, ldx, ldy)
+
+
+def test_copy_uses_passed_strides():
+    for k, (M, N, ldx, ldy) in enumerate(_STRIDE_CASES):
+        x = _strided_input(M, N, ldx, ldy, 50 + k)
+        x[0] = np.array([0x7FC0BEEF], np.uint32).view(np.float32)[0]  # a NaN payload travels too
+        size = M * max(ldx, ldy) + 1
+        y = np.full(size, _Y_PAD, np.float32)
+        oracle.copy2d(x, ldx, y, ldy, M, N)
+        want = _expect(x, ldx, ldy, M, N, size, lambda v, j: v)
+        assert np.array_equal(_bits(y), _bits(want)), (M, N, ldx, ldy)
+
+
+def test_channel_affine_uses_passed_strides():
+    for k, (M, N, ldx, ldy) in enumerate(_STRIDE_CASES):
+        x = _strided_input(M, N, ldx, ldy, 60 + k)
+        size = M * max(ldx, ldy) + 1
+        b = (np.arange(N, dtype=np.float32) + 1) * np.float32(0.5)
+        s = np.where(np.arange(N) % 2 == 0, 0.75, 1.5).astype(np.float32)
+        y = np.full(size, _Y_PAD, np.float32)
+        oracle.channel_affine(x, ldx, None, b, y, ldy, M, N)
+        want = _expect(x, ldx, ldy, M, N, size, lambda v, j: v + b[j])
+        assert np.array_equal(_bits(y), _bits(want)), ("bias", M, N, ldx, ldy)
+        y = np.full(size, _Y_PAD, np.float32)
+        oracle.channel_affine(x, ldx, s, b, y, ldy, M, N)
+        # fmaf(v, s, b) with s in {0.75, 1.5} and these inputs is exact in double: one rounding
+        want = _expect(x, ldx, ldy, M, N, size,
+                       lambda v, j: np.float32(np.float64(v) * np.float64(s[j]) + np.float64(b[j])))
+        assert np.array_equal(_bits(y), _bits(want)), ("scale", M, N, ldx, ldy)
