@@ -1,8 +1,8 @@
 """Benchmark of the tiled f32 path on one MI355X.
 
 One step is one tm_scale2d call on the 4096 x 4096 f32 matrix (X ~ N(0,1), Y = 1.5 X, 32 x 128
-tiles, aligned path, 16-byte vectors): the host promise check, the tile schedule and the unmasked
-streaming kernel.  `value` is that step's throughput in GB/s of algorithmic traffic (64 MiB read +
+tiles, aligned path, 16-byte vectors): the host promise check, the tile schedule (a view with
+contiguous rows is one flat row of 1 KiB work items) and the unmasked streaming kernel.  `value` is that step's throughput in GB/s of algorithmic traffic (64 MiB read +
 64 MiB written, decimal GB), timed with HIP events on the launch stream over K steps that rotate
 through enough buffer sets (1 GiB) that neither L2 nor the 256 MiB Infinity Cache holds a set
 between its uses: the bytes come from HBM.
@@ -14,9 +14,10 @@ The same JSON line carries
                 current kernel source;
   cpu_baseline  the CPU oracle (plain single-threaded C) on the same matrix on this host; the
                 same leg checks the timed kernel's output against the oracle's, bit for bit;
-  paths         every other path of the method, each on its own workload shape and timed the
-                same way: the ragged path on the same shape, the three 1-D access variants and
-                the 1-D ragged path, the ragged 4100 x 1000 map, row and column sums (naive and
+  paths         every other path of the method, each on its own workload shape, its headline
+                the median over 10 batches of 50 launches: the ragged path on the same shape, the
+                three 1-D access variants and the 1-D ragged path, the ragged 4100 x 1000 map (as
+                one flat row, and over padded rows, where the 2-D edge tiles run), row and column sums (naive and
                 LDS walks; the LDS walk's one-pass form on 16 x 2^20), the masked row max, the
                 softmax row statistics (also over 8 rows of 2^18, in one pass and split with a
                 workspace), the per-channel bias add, a tile-size sweep and the transpose /
@@ -41,7 +42,7 @@ PEAK_GBS = 8000.0            # MI355X HBM3E, published
 ROTATE_BYTES = 1 << 30       # bytes touched per rotation of buffer sets
 BATCHES, BATCH_LAUNCHES = 10, 50   # step batch statistics
 METRIC = "achieved HBM GB/s and % of 8 TB/s peak, aligned vs ragged, per config"
-STEP_KERNEL_SOURCES = ["edge_masking_vector_amd/csrc/map.hip", "edge_masking_vector_amd/csrc/device.hpp"]
+STEP_KERNEL_SOURCES = ["edge_masking_vector_amd/csrc/mapflat.hip", "edge_masking_vector_amd/csrc/device.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scale2d_4096_aligned.json")
 
 
@@ -82,9 +83,18 @@ def gbs(nbytes, seconds):
     return nbytes / seconds / 1e9
 
 
+PREROLL = 2   # untimed launches queued ahead of a timed region
+
+
 class Timer:
     """HIP events on the launch stream around K back-to-back launches: nothing else is enqueued in
-    between, so the host stays ahead of the GPU and the mean is the kernels' own duration."""
+    between, so the host stays ahead of the GPU and the mean is the kernels' own duration.
+
+    After the synchronize that opens a region, PREROLL untimed launches (buffer sets -PREROLL ..
+    -1 of the rotation) are enqueued before the start event.  The GPU is then already busy when
+    the start event is reached, and the host's latency to issue the first timed launch (several
+    microseconds through Python) is not counted as a step: without it, 20 timed steps of 21 us
+    measured 21.7 us each against 21.4 us over 50-launch batches."""
 
     def __init__(self, torch, stream):
         self.torch, self.stream = torch, stream
@@ -93,6 +103,8 @@ class Timer:
     def run(self, launch, n):
         torch = self.torch
         torch.cuda.synchronize()
+        for i in range(-PREROLL, 0):
+            launch(i)
         self.region[0].record(self.stream)
         for i in range(n):
             launch(i)
@@ -183,7 +195,7 @@ def main():
 
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "map_tiles<scale, vec4, aligned>",
+                "kernel": "map_flat<scale, 16-byte chunks> (mapflat.hip: one 1 KiB work item per one-wave workgroup)",
                 "algorithmic_bytes_per_launch": step_bytes,
                 "mean_launch_us": round(mean_launch * 1e6, 3),
                 "batches": {"count": BATCHES, "launches_each": BATCH_LAUNCHES,
@@ -264,21 +276,31 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     out = {}
 
     def timed(name, nbytes, n_sets, launch, note):
+        """W warm-ups, then K launches timed as one region (mean_us), then path_batches batches of
+        BATCH_LAUNCHES launches that carry on the rotation through the buffer sets.  The headline
+        (us, gbs, frac) is the median over the batches, which does not depend on --steps: with
+        K = 20 a 4 us kernel's mean still carried host launch gaps.  Without batches it is the
+        mean."""
         for i in range(W):
             launch(i % n_sets)
         mean = Timer(torch, stream).run(lambda i: launch(i % n_sets), K) / K
-        out[name] = {"gbs": round(gbs(nbytes, mean), 1), "frac": round(gbs(nbytes, mean) / PEAK_GBS, 4),
-                     "mean_us": round(mean * 1e6, 3), "bytes": nbytes, "note": note}
+        rec = {"bytes": nbytes, "note": note, "mean_us": round(mean * 1e6, 3)}
+        head, how = mean, "mean of %d launches" % K
         if path_batches > 0:
-            # batches of BATCH_LAUNCHES launches that carry on the rotation through the buffer sets
             batch = []
             for b in range(path_batches):
                 first = K + b * BATCH_LAUNCHES
                 batch.append(Timer(torch, stream).run(lambda i: launch((first + i) % n_sets),
                                                       BATCH_LAUNCHES) / BATCH_LAUNCHES)
-            batch.sort()
-            out[name]["median_us"] = round(batch[len(batch) // 2] * 1e6, 3)
-            out[name]["min_us"] = round(batch[0] * 1e6, 3)
+            head = float(np.median(batch))
+            how = "median of %d batches of %d launches" % (path_batches, BATCH_LAUNCHES)
+            rec["median_us"] = round(head * 1e6, 3)
+            rec["min_us"] = round(min(batch) * 1e6, 3)
+        rec["us"] = round(head * 1e6, 3)
+        rec["gbs"] = round(gbs(nbytes, head), 1)
+        rec["frac"] = round(gbs(nbytes, head) / PEAK_GBS, 4)
+        rec["timing"] = how
+        out[name] = rec
 
     def ok(st):
         if st != tm.TM_OK:
@@ -296,8 +318,8 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     timed("_probe_rt", nb, R, lambda i: ys[i].copy_(xs[i]), "")
     a, b = out.pop("_probe_tm"), out.pop("_probe_rt")
     out["ceiling_probe_copy_512MiB"] = {
-        "tm_copy2d_gbs": a["gbs"], "tm_copy2d_us": a["mean_us"], "runtime_copy_gbs": b["gbs"],
-        "runtime_copy_us": b["mean_us"], "bytes": nb,
+        "tm_copy2d_gbs": a["gbs"], "tm_copy2d_us": a["us"], "runtime_copy_gbs": b["gbs"],
+        "runtime_copy_us": b["us"], "bytes": nb,
         "note": "8192x8192 f32: tm_copy2d aligned 32x128 vec4, and torch's device-to-device copy"}
     del xs, ys
 
@@ -313,7 +335,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
           "same shape, ragged path (per-tile whole-tile test)")
     timed("scale_4096_aligned_scalar", nb, R,
           lambda i: ok(tm.tm_scale2d(xs[i], N, ys[i], N, M, N, 1.5, 32, 128, 1, tm.TM_VAR_SCALAR, stream)),
-          "same shape, aligned path, 4-byte accesses")
+          "same shape, aligned path, one element per thread (4-byte accesses, 256-thread workgroups)")
     timed("ceiling_vendor_copy_64MiB", nb, R, lambda i: ys[i].copy_(xs[i]),
           "torch device-to-device copy of the same 64 MiB (ROCm's copy kernel), for context")
     del xs, ys
@@ -325,14 +347,16 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     R = sets_for(nb)
     xs = rotated(torch, a, R, dev)
     ys = [torch.empty_like(x) for x in xs]
-    for name, var, TN, aligned in (("map1d_scalar", tm.TM_VAR_SCALAR, 256, 1),
-                                   ("map1d_vec4_understated", tm.TM_VAR_VEC4_UNDERSTATED, 1024, 1),
-                                   ("map1d_vec4", tm.TM_VAR_VEC4, 1024, 1),
-                                   ("map1d_vec4_ragged", tm.TM_VAR_VEC4, 1024, 0)):
+    for name, var, TN, aligned, how in (
+            ("map1d_scalar", tm.TM_VAR_SCALAR, 256, 1, "one element per thread (the page's scalar kernel)"),
+            ("map1d_vec4_understated", tm.TM_VAR_VEC4_UNDERSTATED, 1024, 1,
+             "4 elements per thread as four 4-byte accesses (alignment under-stated)"),
+            ("map1d_vec4", tm.TM_VAR_VEC4, 1024, 1, "4 elements per thread as one 16-byte access"),
+            ("map1d_vec4_ragged", tm.TM_VAR_VEC4, 1024, 0, "16-byte accesses")):
         timed(name, nb, R,
               lambda i, var=var, TN=TN, aligned=aligned: ok(tm.tm_map_affine(
                   xs[i], n, ys[i], n, 1, n, 2.0, 1.0, 1, TN, aligned, var, stream)),
-              "1M-element a*2+1, %s, TN=%d" % ("aligned" if aligned else "ragged path", TN))
+              "1M-element a*2+1, %s, TN=%d, %s" % ("aligned" if aligned else "ragged path", TN, how))
     del xs, ys
 
     # ragged 4100 x 1000 affine under 64 x 64, and its aligned counterpart 4096 x 1024
@@ -347,7 +371,30 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
         timed(name, nb, R,
               lambda i, M=M, N=N, aligned=aligned, var=var: ok(tm.tm_map_affine(
                   xs[i], N, ys[i], N, M, N, 0.75, -0.25, 64, 64, aligned, var, stream)),
-              "y = fmaf(x, 0.75, -0.25), 64x64 tiles")
+              "y = fmaf(x, 0.75, -0.25), 64x64 tiles; rows contiguous (row stride N), so the view is "
+              "planned as one flat row whose only ragged edge is its end")
+        del xs, ys
+    # the same ragged map over padded rows, where the 2-D tile plan runs and its edge tiles (the
+    # bottom 4 rows, the right 40 columns) take the masked body: rows off the 16-byte grid (row
+    # stride 1001: 4-byte chunks) and on it (row stride 1004: 16-byte chunks, 64 x 40 right-edge
+    # tiles); then a scale-sized ragged view, 4100 x 4100 at row stride 4104 under 32 x 128
+    for (M, N, ld, TM, TN, var, name, what) in (
+            (4100, 1000, 1001, 64, 64, tm.TM_VAR_AUTO, "affine_4100x1000_ld1001_ragged_2d",
+             "4-byte chunks (rows off the 16-byte grid)"),
+            (4100, 1000, 1004, 64, 64, tm.TM_VAR_VEC4, "affine_4100x1000_ld1004_ragged_2d",
+             "16-byte chunks, 64x40 right-edge tiles"),
+            (4100, 4100, 4104, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ld4104_ragged_2d",
+             "16-byte chunks, 32x128 tiles: 4-row bottom and 4-column right edge tiles")):
+        xh = inputs.matrix(inputs.ragged_input(M, N, seed=12), M, N, ld)
+        nb = 2 * M * N * 4
+        R = sets_for(2 * M * ld * 4)
+        xs = rotated(torch, xh, R, dev)
+        ys = [torch.empty_like(x) for x in xs]
+        timed(name, nb, R,
+              lambda i, M=M, N=N, ld=ld, TM=TM, TN=TN, var=var: ok(tm.tm_map_affine(
+                  xs[i], ld, ys[i], ld, M, N, 0.75, -0.25, TM, TN, 0, var, stream)),
+              "ragged path, row stride %d (padded rows: the 2-D tile plan, edge tiles masked), %s; "
+              "bytes count the %dx%d elements only" % (ld, what, M, N))
         del xs, ys
 
     # row and column sums of 4096 x 4096 U[0,1)
@@ -357,21 +404,27 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     xs = rotated(torch, xh, R, dev)
     outs = [torch.empty(N, device=dev) for _ in range(R)]
     nb = M * N * 4 + N * 4
+    walk = tm.tm_row_walk(M, N, N, 4, 1024, 1, xs[0])
     timed("rowsum_4096", nb, R,
-          lambda i: ok(tm.tm_rowsum(xs[i], N, outs[i], M, N, 4, 256, 1, stream)),
-          "row walk, 4x256 tiles, aligned")
+          lambda i: ok(tm.tm_rowsum(xs[i], N, outs[i], M, N, 4, 1024, 1, stream)),
+          "row walk, 4x1024 tiles, aligned: %d-column tiles, %d whole + %d (tm_row_walk), %d lanes per row"
+          % (walk[1], walk[2], walk[3], walk[4]))
     for name, walk, TM, TN in (("colsum_naive_4096", tm.TM_COL_NAIVE, 256, 1),
                                ("colsum_naive_xcd_4096", tm.TM_COL_NAIVE_XCD, 256, 1),
                                ("colsum_lds_4096", tm.TM_COL_LDS, 256, 64)):
         wsb = tm.tm_colsum_workspace_bytes(M, N, TM, TN, walk)
         wss = [torch.empty(wsb // 4, device=dev) for _ in range(R)]
+        slabs = wsb // (4 * N)
+        geometry = ("the naive walk: %d-row slabs of one column per workgroup" % TM if walk != tm.TM_COL_LDS
+                    else "the LDS walk's own %d-row slabs by 128-column strips" % (M // slabs))
         timed(name, nb, R,
               lambda i, walk=walk, TM=TM, TN=TN, wsb=wsb, wss=wss: ok(tm.tm_colsum(
                   xs[i], N, outs[i], M, N, TM, TN, walk == tm.TM_COL_LDS and 1 or 0, walk, wss[i], wsb,
                   stream)),
-              "column walk, %dx%d tiles, both passes (workspace %d B not counted)" % (TM, TN, wsb))
+              "column walk, caller tile %dx%d (the promise), %s; both passes (workspace %d B not counted)"
+              % (TM, TN, geometry, wsb))
         del wss
-    reads_only = {k: round(gbs(M * N * 4, out[k]["mean_us"] * 1e-6), 1)
+    reads_only = {k: round(gbs(M * N * 4, out[k]["us"] * 1e-6), 1)
                   for k in ("rowsum_4096", "colsum_naive_4096", "colsum_naive_xcd_4096", "colsum_lds_4096")}
     out["reads_only_gbs_4096"] = reads_only
     del xs, outs
@@ -387,7 +440,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
           "one pass: each thread adds a 16-byte column chunk down the 16 rows (no workspace)")
     del xs, outs
 
-    # masked row max: 8192 x 1000 ragged (15 whole 64-column tiles + 40), aligned 8192 x 1024
+    # masked row max: 8192 x 1000 ragged (BC = 64: 15 whole tiles + 40 columns), aligned 8192 x 1024
     for (M, N, aligned, name) in ((8192, 1000, 0, "rowmax_8192x1000_ragged"),
                                   (8192, 1024, 1, "rowmax_8192x1024_aligned")):
         sh = inputs.scores_input(M, N)
@@ -395,15 +448,19 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
         ss = rotated(torch, sh, R, dev)
         outs = [torch.empty(M, device=dev) for _ in range(R)]
         nb = M * N * 4 + M * 4
+        st, bc, nfull, rem, lanes = tm.tm_row_walk(M, N, N, 16, 64, aligned, ss[0])
+        ok(st)
+        walk = "%d-column tiles: %d whole + %s (tm_row_walk), %d lanes per row" % (
+            bc, nfull, "one masked tile of %d columns" % rem if rem else "no remainder", lanes)
         timed(name, nb, R,
               lambda i, M=M, N=N, aligned=aligned: ok(tm.tm_rowmax_masked(ss[i], N, outs[i], M, N, 16, 64,
                                                                           aligned, stream)),
-              "BC=64 column tiles, -1e30 fill")
+              "16x64 tiles, %s; -1e30 fill" % walk)
         ls = [torch.empty(M, device=dev) for _ in range(R)]
         timed(name.replace("rowmax", "softmax_stats"), nb + M * 4, R,
               lambda i, M=M, N=N, aligned=aligned: ok(tm.tm_softmax_stats(ss[i], N, outs[i], ls[i], M, N, 16,
                                                                           64, aligned, stream)),
-              "row maximum and sum of exp(s - max), BC=64 column tiles")
+              "row maximum and sum of exp(s - max), 16x64 tiles, %s" % walk)
         del ss, outs, ls
     # a few long rows: softmax statistics over 8 rows of 2^18 scores, in one pass (one workgroup
     # per row) and with a workspace (row segments on separate workgroups, then one combine)

@@ -143,6 +143,11 @@ TM_API int tm_split(int64_t K, int64_t T, int64_t *nfull, int64_t *rem) {
     return tmp::split(K, T, nfull, rem);
 }
 
+TM_API int tm_row_walk(int64_t M, int64_t N, int64_t ld, int BR, int BC, int aligned, const void *x,
+                       int64_t *bc, int64_t *nfull, int64_t *rem, int *lanes) {
+    return tmp::row_walk_query(M, N, ld, BR, BC, aligned, x, bc, nfull, rem, lanes);
+}
+
 TM_API int tm_plan_tiles(int64_t M, int64_t N, int TM, int TN, int64_t *tiles_m, int64_t *tiles_n,
                          int64_t *whole) {
     return tmp::plan_tiles(M, N, TM, TN, tiles_m, tiles_n, whole);

@@ -10,6 +10,7 @@
 namespace tmk {
 
 hipError_t launch_map(const tmp::MapPlan &plan, hipStream_t stream);
+hipError_t launch_map_flat(const tmp::MapPlan &plan, hipStream_t stream);  // plan.flat
 hipError_t launch_rows(const tmp::RowPlan &plan, hipStream_t stream);
 hipError_t launch_cols(const tmp::ColPlan &plan, hipStream_t stream);
 hipError_t launch_transpose(const tmp::TransposePlan &plan, hipStream_t stream);

@@ -11,7 +11,8 @@
 // Mapping (the tile scheduler).  A tile holds TM rows of VR = TN/W chunks (W = 4 elements for the
 // vector variants, 1 for scalar).  A workgroup takes one work item: R consecutive rows of G
 // horizontally adjacent tiles of one tile row band, R*G*VR chunks, moved by 64 to 1024 threads
-// with U chunks per thread (U = 4 for scalar, else 1) at a stride of the workgroup size, all loads
+// with U chunks per thread (U = 4 for the 4-byte accesses AUTO falls back to, else 1: the vector
+// variants and the one-element-per-thread scalar variant) at a stride of the workgroup size, all loads
 // before any store.  Within a work-item row the lane-varying term of every address is the chunk
 // index, so a wave reads consecutive chunks of a row.  Work items run with the tile groups
 // fastest, then row strips, then tile rows, so workgroups dispatched together cover neighbouring
@@ -77,6 +78,11 @@ struct Chunk {
 };
 template <>
 struct Chunk<tmp::kScalar> {
+    using T = float;
+    static constexpr int W = 1;
+};
+template <>
+struct Chunk<tmp::kScalar1> {
     using T = float;
     static constexpr int W = 1;
 };
@@ -444,6 +450,7 @@ const void *pick_access(const tmp::MapPlan &p) {
                 return pick_guard<OP, tmp::kScalar, true>(p);
         }
         return pick_guard<OP, tmp::kScalar, false>(p);
+    case tmp::kScalar1: return pick_guard<OP, tmp::kScalar1, false>(p);
     case tmp::kVec4Understated: return pick_guard<OP, tmp::kVec4Understated, false>(p);
     default: return pick_guard<OP, tmp::kVec4, false>(p);
     }
@@ -461,6 +468,8 @@ const void *pick(const tmp::MapPlan &p) {
 }  // namespace
 
 hipError_t launch_map(const tmp::MapPlan &p, hipStream_t stream) {
+    if (p.flat)
+        return launch_map_flat(p, stream);
     MapArgs a;
     a.x = p.x;
     a.y = p.y;

@@ -1,0 +1,154 @@
+// mapflat.hip -- the element-wise maps over one contiguous row, cut into 1 KiB work items: the
+// case the tile scheduler reaches for every view whose rows are contiguous in both tensors (row
+// stride N: the M x N elements are one row of M*N) and whose bases sit on 128-byte lines, with the
+// affine map, the scale or the copy moved in 16-byte chunks or in 4-byte elements.
+//
+// Sources (web pages): Phobos docs "@aligned" ("A minimal kernel": the scale; "What it changes":
+// no masks, 16-byte rows); Phobos docs "Slicing, bounds and masking" ("Masking": elements past the
+// end read as 0 and are not stored; "Promising whole tiles with @aligned": the copy); Mojo GPU
+// puzzle 35 "Aligned Load & Store" ("The exercise": a*2 + 1 over 1M elements); teenygrad "Memory
+// Coalescing and Tensor Layout" ("Coalescing": lane t takes the t-th consecutive address).
+//
+// Why a kernel of its own.  These work items are short (one wave loads 1 KiB and stores 1 KiB),
+// there are many of them (65,536 for a 4096 x 4096 map), and the HBM stream is only kept busy by
+// how fast finished waves are replaced: on gfx950 an empty kernel of 65,536 one-wave workgroups
+// already takes 14.7 us, and everything a wave does before its load lengthens its life.  The
+// general tile kernel (map.hip) spends about 80 instructions and five scalar loads of a 400-byte
+// argument block on tile arithmetic before its load; this one takes its six arguments preloaded
+// into scalar registers (this file is compiled with kernel-argument preloading) and computes one
+// address.  Measured on the 4096 x 4096 scale (kernel trace, 1 GiB of rotating buffers): 21.48 us
+// for the general kernel, 20.84 us for this one.
+//
+// Work item w covers elements [256 w, 256 w + 256) of the row.  16-byte chunks: lane t of a wave
+// moves elements 4t .. 4t + 3 of the item.  4-byte elements: lane t of a wave moves elements t,
+// t + 64, t + 128 and t + 192, or (one element per thread) thread t of 256 moves element t;
+// consecutive lanes take consecutive addresses either way.  Loads carry the non-temporal hint (touched
+// once); a whole item's output, one contiguous 1 KiB, is stored through a buffer resource spanning
+// exactly that block with the device-scope cache policy.  Only the last item can be ragged (the
+// row's end): there an element past the end is neither read nor stored (what a masked element
+// would read, 0, never reaches an output of a map).
+#include "device.hpp"
+#include "launch.h"
+
+namespace tmk {
+namespace {
+
+constexpr int kItemFloats = 256;  // 1 KiB: one wave of 16-byte chunks
+constexpr int kFlatStorePolicy = 16;  // sc1: device scope
+
+template <int OP>
+__device__ __forceinline__ float op1(float v, float a, float b) {
+    if constexpr (OP == tmp::kAffine)
+        return __builtin_fmaf(v, a, b);  // one rounding
+    else if constexpr (OP == tmp::kScale)
+        return a * v;                    // one IEEE multiply: -0 stays -0
+    else
+        return v;                        // register move: bits unchanged
+}
+
+template <int OP>
+__device__ __forceinline__ f4 op4(f4 v, float a, float b) {
+    f4 r;
+    r.x = op1<OP>(v.x, a, b);
+    r.y = op1<OP>(v.y, a, b);
+    r.z = op1<OP>(v.z, a, b);
+    r.w = op1<OP>(v.w, a, b);
+    return r;
+}
+
+// How a work item's 256 elements are spread over the threads of its workgroup.
+enum FlatMode {
+    kChunk16 = 0,  // 64 threads, one 16-byte chunk each: lane t moves elements 4t .. 4t + 3
+    kFour4 = 1,    // 64 threads, four 4-byte elements each: lane t moves t, t + 64, t + 128, t + 192
+    kOne4 = 2      // 256 threads, one element each (the one-element-per-thread scalar variant)
+};
+
+template <int MODE>
+constexpr int flat_threads() { return MODE == kOne4 ? 256 : 64; }
+
+// Items [0, nwhole) are whole; when tail > 0, item nwhole holds the row's last `tail` elements
+// (1 .. 255).  The host launches at most nwhole + (tail > 0) workgroups; a smaller grid loops.
+template <int OP, int MODE>
+__global__ __launch_bounds__(flat_threads<MODE>()) void map_flat(const float *__restrict__ x,
+                                                                 float *__restrict__ y, float alpha,
+                                                                 float beta, uint32_t nwhole,
+                                                                 uint32_t tail) {
+    const uint32_t t = threadIdx.x;
+    uint32_t w = blockIdx.x;
+    for (; w < nwhole; w += gridDim.x) {
+        const size_t base = size_t(w) * kItemFloats;
+        const __amdgpu_buffer_rsrc_t ry = segment_rsrc(y + base, kItemFloats * 4);
+        if constexpr (MODE == kChunk16) {
+            const f4 v = ld16_nt(x + base + 4 * t);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, op4<OP>(v, alpha, beta)), ry,
+                                                   int(t) * 16, 0, kFlatStorePolicy);
+        } else if constexpr (MODE == kFour4) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                v[u] = ld4_nt(x + base + t + 64 * u);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, op1<OP>(v[u], alpha, beta)),
+                                                      ry, int(t + 64 * u) * 4, 0, kFlatStorePolicy);
+        } else {
+            const float v = ld4_nt(x + base + t);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, op1<OP>(v, alpha, beta)), ry,
+                                                  int(t) * 4, 0, kFlatStorePolicy);
+        }
+    }
+    if (w != nwhole || tail == 0)
+        return;
+    // The row's ragged end, item nwhole: an element past the end is neither read nor stored.
+    const float *xp = x + size_t(w) * kItemFloats;
+    float *yp = y + size_t(w) * kItemFloats;
+    if constexpr (MODE == kChunk16) {
+        const int live = int(tail) - 4 * int(t);  // elements of chunk t inside the row
+        if (live >= 4) {
+            st16_nt(yp + 4 * t, op4<OP>(ld16_nt(xp + 4 * t), alpha, beta));
+        } else if (live > 0) {
+            yp[4 * t] = op1<OP>(xp[4 * t], alpha, beta);
+            if (live > 1)
+                yp[4 * t + 1] = op1<OP>(xp[4 * t + 1], alpha, beta);
+            if (live > 2)
+                yp[4 * t + 2] = op1<OP>(xp[4 * t + 2], alpha, beta);
+        }
+    } else if constexpr (MODE == kFour4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t e = t + 64 * u;
+            if (e < tail)
+                yp[e] = op1<OP>(xp[e], alpha, beta);
+        }
+    } else {
+        if (t < tail)
+            yp[t] = op1<OP>(xp[t], alpha, beta);
+    }
+}
+
+template <int OP>
+const void *pick_flat(int mode) {
+    switch (mode) {
+    case kChunk16: return reinterpret_cast<const void *>(&map_flat<OP, kChunk16>);
+    case kFour4: return reinterpret_cast<const void *>(&map_flat<OP, kFour4>);
+    default: return reinterpret_cast<const void *>(&map_flat<OP, kOne4>);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_map_flat(const tmp::MapPlan &p, hipStream_t stream) {
+    const float *x = p.x;
+    float *y = p.y;
+    float alpha = p.alpha, beta = p.beta;
+    uint32_t nwhole = p.flat_last == 256 ? p.nwork : p.nwork - 1;
+    uint32_t tail = p.flat_last == 256 ? 0 : p.flat_last;
+    void *args[] = {&x, &y, &alpha, &beta, &nwhole, &tail};
+    const int mode = p.access == tmp::kVec4 ? kChunk16 : p.access == tmp::kScalar ? kFour4 : kOne4;
+    const void *fn = p.op == tmp::kAffine ? pick_flat<tmp::kAffine>(mode)
+                     : p.op == tmp::kScale ? pick_flat<tmp::kScale>(mode)
+                                           : pick_flat<tmp::kCopy>(mode);
+    return hipLaunchKernel(fn, dim3(p.grid), dim3(mode == kOne4 ? 256 : 64), args, 0, stream);
+}
+
+}  // namespace tmk

@@ -186,7 +186,7 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     int access;
     switch (variant) {
     case TM_VAR_AUTO: access = vec16 ? kVec4 : kScalar; break;
-    case TM_VAR_SCALAR: access = kScalar; break;
+    case TM_VAR_SCALAR: access = kScalar1; break;
     case TM_VAR_VEC4_UNDERSTATED:
         if (TN % 4 != 0)
             return TM_E_UNSUPPORTED;
@@ -244,7 +244,7 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     // wide as the row's next power of two (at least one chunk), whatever the caller's tile: with
     // a 64-column tile, rows of 3 floats ran 3 live lanes of 64 (8.7M x 3 with row stride 7: 653
     // against 142 us).
-    const int W = access == kScalar ? 1 : 4;
+    const int W = access == kScalar || access == kScalar1 ? 1 : 4;
     int TNs = static_cast<int>(std::min<int64_t>(TN, kRowSegmentBytes / 4));
     if (!aligned && N < kRowSegmentBytes / 4) {
         TNs = W;
@@ -255,6 +255,9 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     plan_tiles(M, N, TM, TNs, &tiles_m, &tiles_n, &whole);
 
     const int log_u = ilog2(access == kScalar ? kScalarChunksPerThread : 1);
+    // Threads of a one-item workgroup on the line grid: one wave, or kScalar1Block threads for the
+    // one-element-per-thread variant (a wave of single floats is only 256 bytes).
+    const int log_item_threads = ilog2(access == kScalar1 ? kScalar1Block : kMapMinBlock);
     const int log_vr = ilog2(TNs / W);
     int log_tm = ilog2(TM);
     // A row that fits one scheduling tile cannot widen a work item, so on the ragged path (where
@@ -294,7 +297,7 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
                            (M <= 1 || (ldx % line == 0 && ldy % line == 0));
     int log_r, log_g;
     bool stream = false;
-    const int log_wave_chunks = ilog2(kMapMinBlock) + log_u;  // chunks of one wave's work item
+    const int log_wave_chunks = log_item_threads + log_u;  // chunks of one (wave-sized) work item
     // (Not for the under-stated variant: each of its store instructions writes every fourth word.)
     const bool contiguous_stores = access != kVec4Understated;
     if (line_rows && contiguous_stores) {
@@ -308,7 +311,7 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     if (stream) {
         // set above
     } else if (line_rows) {
-        const int log_target = ilog2(kMapMinBlock) + log_u;
+        const int log_target = log_wave_chunks;
         log_g = std::min(log_gcap, std::max(0, ilog2(kRowSegmentBytes / 4) - ilog2(TNs)));
         log_r = std::min(log_tm, std::max(0, log_target - log_vr - log_g));
         log_g = std::min(log_gcap, std::max(log_g, log_target - log_vr - log_r));
@@ -352,6 +355,14 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     // A thread's chunks t + u * threads share one column when the item is no wider than that.
     plan->share = op == kChannel && log_u > 0 && plan->log_gv <= plan->log_bs;
     plan->stream = stream;
+    // One contiguous row cut into 1 KiB stream items (the scale, affine map and copy of any view
+    // with contiguous rows on 128-byte lines): item w is elements [256 w, 256 w + 256) of the row,
+    // and only the last can be ragged.  Such items go to a kernel that does nothing but that
+    // (mapflat.hip).
+    if (stream && M == 1 && op != kChannel && access != kVec4Understated) {
+        plan->flat = true;
+        plan->flat_last = static_cast<uint32_t>(N - (nwork - 1) * (kStreamSegmentBytes / 4));
+    }
     plan->group = 1u << log_g;
     plan->groups_n = static_cast<uint32_t>(groups_n);
     plan->tiles_n = static_cast<uint32_t>(tiles_n);
@@ -400,6 +411,66 @@ size_t rows_ws_bytes(int64_t M, int64_t N) {
     if (!row_split_geometry(M, N, &lk, &seg, &segs))
         return 0;
     return static_cast<size_t>(M) * static_cast<size_t>(segs) * kRowPartialBytes;
+}
+
+// Lanes per row (*lpr, a power of two) and chunks per lane per column tile (*per_tile) of the
+// one-pass row walk over M rows of N elements (16-byte chunks when vec).  TC: the caller's column
+// tile.
+static void row_walk(int64_t M, int64_t N, bool vec, int TC, int *lpr_out, int *per_tile_out) {
+    const int W = vec ? 4 : 1;
+    const int64_t chunks = ceil_div(N, W);  // chunks per row
+    // Lanes per row, fitted to HBM-streamed sweeps of forced lane counts (N = 4 to 2000 at 32 MB,
+    // 1 GiB of rotating inputs, both chunk widths) and an interleaved comparison at 8192 x 1000
+    // (16 / 32 / 64 lanes: 7.31 / 7.24 / 7.97 us): rows of up to 64 16-byte chunks are one tile
+    // with about 4 chunks per lane; longer rows get about 8 chunks per lane per pass, up to a wave.
+    int lpr, per_tile;
+    if (vec && chunks <= kTinyRowChunks) {
+        lpr = 1 << ilog2(ceil_div(chunks, 4));
+        per_tile = 1 << ilog2(ceil_div(chunks, lpr));
+    } else {
+        lpr = 1 << std::min(6, ilog2(ceil_div(chunks, 8)));
+        per_tile = 1;
+    }
+    if (chunks > (vec ? kShortRowChunksVec : kShortRowChunksScalar)) {
+        // Long rows: one wave per row, walking tiles of 64 chunks (4-byte chunks: two per lane);
+        // from 1024 16-byte chunks on, a 256-lane workgroup per row, whose lanes then have their
+        // chunks in flight in one or two batches of 8 rather than two to eight one after another
+        // (1 GiB of rotating inputs: 4096 x 4096 sums 12.1 -> 11.8 us, softmax statistics 13.0 ->
+        // 12.4; 2048 x 8192 13.0 -> 11.9; 4096 x 16384 46.5 -> 41.0; at 2048 columns 128 or 256
+        // lanes were 2-4% slower than 64).
+        per_tile = vec ? 1 : 2;
+        if (vec && chunks >= kRowLongChunks)
+            lpr = kRowLongLanes;
+        if (M < kRowWideWaves) {
+            // Too few rows to fill the GPU with one wave each: a workgroup of several waves per
+            // row, keeping at least 4 chunks per lane.
+            int64_t l = int64_t{64} << ilog2(ceil_div(kRowWideWaves, M));
+            l = std::min<int64_t>(std::max<int64_t>(l, lpr), kRowMaxLanes);
+            while (l > 64 && l * 4 > chunks)
+                l >>= 1;
+            lpr = static_cast<int>(l);
+            per_tile = 1;
+        }
+    }
+    // The caller's column tile is the walk's whenever it holds whole chunks, keeps at least half
+    // the lanes chosen above (one chunk each) and needs at most kRowTileMaxChunks chunks per lane
+    // ([SLICING] "Reductions over a ragged tile": the 8192 x 1000 masked maximum in BC = 64
+    // columns runs 15 whole tiles and one of 40 columns, 16 lanes per row where 32 were chosen;
+    // 7.31 against 7.24 us).  Narrower tiles would starve the rows of lanes -- when the lanes per
+    // row followed every tile, tiles 1 to 16 columns wide made a 4096 x 4096 row sum 4 to 58 times
+    // slower -- and wider ones would put many chunks of the masked tile on each lane; both walk
+    // the library's own tile of lpr * W * per_tile columns, split by the same rule into whole
+    // tiles plus one masked remainder.
+    if (TC % W == 0) {
+        const int64_t tc = TC / W;  // chunks per caller tile (a power of two)
+        const int64_t l = std::min<int64_t>(lpr, tc);
+        if (2 * l >= lpr && tc / l <= kRowTileMaxChunks) {
+            lpr = static_cast<int>(l);
+            per_tile = static_cast<int>(tc / l);
+        }
+    }
+    *lpr_out = lpr;
+    *per_tile_out = per_tile;
 }
 
 int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TR, int TC,
@@ -457,48 +528,14 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
         return TM_OK;
     }
 
-    // The walk is shaped by the row length and the row count only: the caller's tile states the
-    // promise (checked above) and nothing else.  With lanes per row set from the tile, tiles 1 to
-    // 16 columns wide made a 4096 x 4096 row sum 4 to 58 times slower (one to four lanes per
-    // row), and a few long rows (8 x 2^20) ran on two workgroups.  Rows with 16-byte starts take
+    // Lanes per row come from the row length and count; the column tile is the caller's BC
+    // (TC here) whenever it suits the lanes (row_walk below).  Rows with 16-byte starts take
     // 16-byte chunks whatever N is: whole tiles hold whole chunks, and the remainder tile masks
     // the chunk that straddles N element by element.
     const bool vec = rows16(x, M, ld);
     const int W = vec ? 4 : 1;
-    const int64_t chunks = ceil_div(N, W);  // chunks per row
-    // Lanes per row, fitted to HBM-streamed sweeps of forced lane counts (N = 4 to 2000 at 32 MB,
-    // 1 GiB of rotating inputs, both chunk widths) and an interleaved comparison at 8192 x 1000
-    // (16 / 32 / 64 lanes: 7.31 / 7.24 / 7.97 us): rows of up to 64 16-byte chunks are one tile
-    // with about 4 chunks per lane; longer rows get about 8 chunks per lane per pass, up to a wave.
     int lpr, per_tile;
-    if (vec && chunks <= kTinyRowChunks) {
-        lpr = 1 << ilog2(ceil_div(chunks, 4));
-        per_tile = 1 << ilog2(ceil_div(chunks, lpr));
-    } else {
-        lpr = 1 << std::min(6, ilog2(ceil_div(chunks, 8)));
-        per_tile = 1;
-    }
-    if (chunks > (vec ? kShortRowChunksVec : kShortRowChunksScalar)) {
-        // Long rows: one wave per row, walking tiles of 64 chunks (4-byte chunks: two per lane);
-        // from 1024 16-byte chunks on, a 256-lane workgroup per row, whose lanes then have their
-        // chunks in flight in one or two batches of 8 rather than two to eight one after another
-        // (1 GiB of rotating inputs: 4096 x 4096 sums 12.1 -> 11.8 us, softmax statistics 13.0 ->
-        // 12.4; 2048 x 8192 13.0 -> 11.9; 4096 x 16384 46.5 -> 41.0; at 2048 columns 128 or 256
-        // lanes were 2-4% slower than 64).
-        per_tile = vec ? 1 : 2;
-        if (vec && chunks >= kRowLongChunks)
-            lpr = kRowLongLanes;
-        if (M < kRowWideWaves) {
-            // Too few rows to fill the GPU with one wave each: a workgroup of several waves per
-            // row, keeping at least 4 chunks per lane.
-            int64_t l = int64_t{64} << ilog2(ceil_div(kRowWideWaves, M));
-            l = std::min<int64_t>(std::max<int64_t>(l, lpr), kRowMaxLanes);
-            while (l > 64 && l * 4 > chunks)
-                l >>= 1;
-            lpr = static_cast<int>(l);
-            per_tile = 1;
-        }
-    }
+    row_walk(M, N, vec, TC, &lpr, &per_tile);
     plan->launch = true;
     plan->op = op;
     plan->vec = vec;
@@ -522,6 +559,29 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
     plan->M = M;
     plan->N = N;
     return TM_OK;
+}
+
+int row_walk_query(int64_t M, int64_t N, int64_t ld, int TR, int TC, int aligned, const void *x,
+                   int64_t *bc, int64_t *nfull, int64_t *rem, int *lanes) {
+    if (bc == nullptr || nfull == nullptr || rem == nullptr || lanes == nullptr)
+        return TM_E_INVAL;
+    if (aligned != 0 && aligned != 1)
+        return TM_E_INVAL;
+    if (M < 0 || N < 0 || ld < N || TR <= 0 || TC <= 0)
+        return TM_E_INVAL;
+    if (M > 0 && N > 0 && (x == nullptr || !aligned_to(x, 4)))
+        return TM_E_INVAL;
+    const int st = check_tile(TR, TC);
+    if (st != TM_OK)
+        return st;
+    if (aligned && !promise_holds(M, N, ld, 0, TR, TC, x, nullptr))
+        return TM_E_ALIGN;
+    const bool vec = rows16(x, M, ld);
+    int lpr = 1, per_tile = 1;
+    row_walk(M, N, vec, TC, &lpr, &per_tile);
+    *lanes = lpr;
+    *bc = int64_t{lpr} * (vec ? 4 : 1) * per_tile;
+    return split(N, *bc, nfull, rem);
 }
 
 // ---- column sums ------------------------------------------------------------------------------

@@ -43,6 +43,9 @@ constexpr int kRowMaxLanes = 1024;
 // that each lane's chunks are in flight in one or two batches rather than many.
 constexpr int64_t kRowLongChunks = 1024;
 constexpr int kRowLongLanes = 256;
+// The caller's column tile becomes the row walk's when it keeps at least half the lanes the
+// row's length and count call for and needs at most this many chunks per lane per tile.
+constexpr int64_t kRowTileMaxChunks = 4;
 // Rows of one lane each run on at most this many workgroups, each looping over several row groups.
 constexpr int64_t kRowTinyGrid = 4096;
 // Split rows (the row calls that take a workspace): fewer than kRowSplitRows rows of at least
@@ -70,7 +73,11 @@ constexpr int64_t kColDirectRowsWide = 256;
 constexpr int64_t kColDirectMinN = int64_t{1} << 18;
 
 enum MapOp { kAffine = 0, kScale = 1, kCopy = 2, kChannel = 3 };
-enum Access { kScalar = 1, kVec4Understated = 2, kVec4 = 3 };
+// kScalar: 4-byte accesses, four elements per thread at a stride of the workgroup (what AUTO
+// takes when rows are off the 16-byte grid); kScalar1: one element per thread, the scalar
+// kernel of Mojo puzzle 35 "Solution" (TM_VAR_SCALAR), in workgroups of kScalar1Block threads.
+enum Access { kScalar = 1, kVec4Understated = 2, kVec4 = 3, kScalar1 = 4 };
+constexpr int kScalar1Block = 256;
 
 int ilog2(int64_t v);  // v a power of two
 
@@ -101,6 +108,9 @@ struct MapPlan {
     bool share = false;           // channel op: a thread's chunks share one column's vectors
     bool stream = false;          // work item = one row segment of kStreamSegmentBytes (one wave,
                                   // 16-byte chunks); whole items use buffer accesses sc1 nt
+    bool flat = false;            // one contiguous row in 1 KiB stream items, no channel op: the
+                                  // kernel of mapflat.hip (item w = elements [256 w, 256 w + 256))
+    uint32_t flat_last = 0;       // flat: elements of the last item inside the row (1 .. 256)
     uint32_t group = 1;           // G
     uint32_t groups_n = 0;        // ceil(tiles_n / G)
     uint32_t tiles_n = 0;         // tiles along N
@@ -161,6 +171,12 @@ size_t rows_ws_bytes(int64_t M, int64_t N);
 int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TR, int TC,
               int aligned, RowPlan *plan, float *out2 = nullptr, bool with_ws = false,
               void *ws = nullptr, size_t ws_bytes = 0);
+
+// The one-pass row walk for these arguments (what tm_rowsum, tm_rowmax_masked and
+// tm_softmax_stats run): column tile *bc, *nfull whole tiles, *rem live columns of the masked
+// remainder tile (0: none) and *lanes per row.  Argument errors as plan_rows (no output vector).
+int row_walk_query(int64_t M, int64_t N, int64_t ld, int TR, int TC, int aligned, const void *x,
+                   int64_t *bc, int64_t *nfull, int64_t *rem, int *lanes);
 
 // ---- column sums ---------------------------------------------------------------------------
 struct ColPlan {

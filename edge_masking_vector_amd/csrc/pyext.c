@@ -2,7 +2,7 @@
  * taking device addresses as Python ints (None for NULL), sizes as ints, scalars as floats and the
  * stream as an int (a hipStream_t; 0 is the null stream).  Argument conversion only: each function
  * converts its arguments and calls the C ABI once.  Calls that write through host pointers
- * (tm_split, tm_plan_tiles, tm_pad_extents, tm_autotune_map) return a tuple that starts with the
+ * (tm_split, tm_plan_tiles, tm_row_walk, tm_pad_extents, tm_autotune_map) return a tuple that starts with the
  * status instead.  A wrong argument count or type raises TypeError / OverflowError before any call.
  *
  * METH_FASTCALL keeps a call near half a microsecond; through ctypes the same call took several,
@@ -279,6 +279,18 @@ static PyObject *py_split(ARGS) {
     return Py_BuildValue("(iLL)", st, (long long)nfull, (long long)rem);
 }
 
+static PyObject *py_row_walk(ARGS) {
+    int64_t M, N, ld, bc = -1, nfull = -1, rem = -1;
+    int BR, BC, al, lanes = -1;
+    void *x;
+    (void)self;
+    OK(want(n, 7, "tm_row_walk"));
+    OK(as_i64(a[0], &M) && as_i64(a[1], &N) && as_i64(a[2], &ld) && as_int(a[3], &BR) &&
+       as_int(a[4], &BC) && as_int(a[5], &al) && as_ptr(a[6], &x));
+    const int st = tm_row_walk(M, N, ld, BR, BC, al, x, &bc, &nfull, &rem, &lanes);
+    return Py_BuildValue("(iLLLi)", st, (long long)bc, (long long)nfull, (long long)rem, lanes);
+}
+
 static PyObject *py_plan_tiles(ARGS) {
     int64_t M, N, tm_ = -1, tn_ = -1, whole = -1;
     int TM, TN;
@@ -371,6 +383,7 @@ static PyMethodDef methods[] = {
     FAST("tm_check_promise", py_check_promise),
     FAST("tm_split", py_split),
     FAST("tm_plan_tiles", py_plan_tiles),
+    FAST("tm_row_walk", py_row_walk),
     FAST("tm_pad_extents", py_pad_extents),
     FAST("tm_autotune_map", py_autotune_map),
     FAST("tm_status_string", py_status_string),

@@ -155,6 +155,12 @@ def tm_plan_tiles(M, N, TM, TN):
     return _ext.tm_plan_tiles(M, N, TM, TN)
 
 
+def tm_row_walk(M, N, ld, BR, BC, aligned, x):
+    """Returns (status, bc, nfull, rem, lanes): the column walk of the one-pass row reductions.
+    x is a tensor or an address (inspected, never dereferenced)."""
+    return _ext.tm_row_walk(M, N, ld, BR, BC, aligned, _ptr(x))
+
+
 def tm_pad_extents(M, N, TM, TN):
     """Returns (status, Mp, Np, ldp)."""
     return _ext.tm_pad_extents(M, N, TM, TN)

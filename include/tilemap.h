@@ -75,8 +75,11 @@ typedef enum {
 
 /* Access width of the element-wise maps ([P35] "The exercise"). */
 typedef enum {
-    TM_VAR_AUTO = 0,             /* VEC4 when legal, else SCALAR */
-    TM_VAR_SCALAR = 1,           /* one 4-byte load and store per element */
+    TM_VAR_AUTO = 0,             /* VEC4 when legal, else 4-byte loads and stores, four
+                                    elements per thread at a stride of the workgroup */
+    TM_VAR_SCALAR = 1,           /* one element per thread, one 4-byte load and store each
+                                    ([P35] "Solution": the scalar kernel), in workgroups of
+                                    256 threads */
     TM_VAR_VEC4_UNDERSTATED = 2, /* 4 elements per thread, moved as four 4-byte accesses
                                     (alignment under-stated: [P35] "Key API"); needs TN % 4 == 0,
                                     else TM_E_UNSUPPORTED */
@@ -133,9 +136,10 @@ int tm_channel_affine(const float *x, int64_t ldx, const float *scale, const flo
 
 /* ---- row and column reductions --------------------------------------------------------------
  * As for the maps, the caller's tile (TM x TN, BR x BC) is what the alignment promise is made
- * for; the column tiles a row is walked in, the lanes per row and the slabs and strips of the
- * column walk are the library's choice, set from M, N and the row alignment.  The choice decides
- * the order of floating-point additions (within the stated bounds), never a maximum.  A row is
+ * for.  The row walk takes the caller's column tile as its own when it suits the lanes of a row
+ * (tm_row_walk reports the walk for any arguments); the lanes per row, and the slabs and strips of
+ * the column walk, are the library's choice, set from M, N and the row alignment.  These choices
+ * decide the order of floating-point additions (within the stated bounds), never a maximum.  A row is
  * walked by one workgroup at most, so a handful of very long rows cannot use the whole GPU; the
  * *_ws variants below take a workspace and split such rows across workgroups. */
 
@@ -258,6 +262,21 @@ int tm_check_promise(int64_t M, int64_t N, int64_t ld_in, int64_t ld_out, int TM
  * *rem = K % T columns in the one masked remainder tile.  TM_E_INVAL if K < 0, T <= 0 or an output
  * pointer is NULL. */
 int tm_split(int64_t K, int64_t T, int64_t *nfull, int64_t *rem);
+
+/* The column walk of the one-pass row reductions (tm_rowsum, tm_rowmax_masked, tm_softmax_stats,
+ * and the *_ws calls when they do not split rows) for these arguments, as a pure host function:
+ * the walk's column tile *bc, its *nfull whole tiles, the *rem live columns of its one masked
+ * remainder tile (0: none; [SLICING] "Loops over a dynamic extent", "Reductions over a ragged
+ * tile") and the *lanes that share each row.  The caller's column tile BC (TN for tm_rowsum) is
+ * the walk's whenever it holds whole chunks (16-byte chunks when every row of x starts on a
+ * 16-byte boundary, else single floats), keeps at least half the lanes the row length and count
+ * call for, one chunk each, and needs at most 4 chunks per lane per tile; otherwise the walk takes
+ * its own tile, and the split follows the same rule.  8192 x 1000 with BC = 64 on 16-byte rows:
+ * bc = 64, nfull = 15, rem = 40.  x is only inspected, never dereferenced.  TM_E_INVAL /
+ * TM_E_UNSUPPORTED / TM_E_ALIGN as the reductions return them (no output vector is checked), or
+ * TM_E_INVAL if an output pointer is NULL. */
+int tm_row_walk(int64_t M, int64_t N, int64_t ld, int BR, int BC, int aligned, const void *x,
+                int64_t *bc, int64_t *nfull, int64_t *rem, int *lanes);
 
 /* Tile scheduler counts ([SLICING] "Masking"): *tiles_m = ceil(M / TM), *tiles_n = ceil(N / TN) and
  * *whole = the number of tiles lying entirely inside the M x N tensor; the other tiles are edge

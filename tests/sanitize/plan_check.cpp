@@ -24,7 +24,7 @@
 
 #include "../../edge_masking_vector_amd/csrc/plan.h"
 
-static long g_checked = 0, g_failed = 0;
+static long g_checked = 0, g_failed = 0, g_flat = 0;
 
 #define CHECK(cond, ...)                                   \
     do {                                                   \
@@ -55,9 +55,56 @@ static uint32_t umulhi_mod(uint32_t a, const tmp::Div32 &d) {
 // The replay walks the plan's own view (a contiguous caller view may be planned as one flat row)
 // and counts the stores per output address; every element of the caller's view must be stored
 // exactly once and no other address (row padding) at all.
+// A flat plan (mapflat.hip): item w < nwhole moves elements [256 w, 256 w + 256) of the one
+// contiguous row; item nwhole (when the last item is ragged) moves its first `tail` elements.  The
+// workgroup's threads cover an item exactly: 64 x one 16-byte chunk, 64 x four 4-byte elements at
+// a stride of 64, or 256 x one element.
+static void replay_flat(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, const char *tag) {
+    CHECK(p.M == 1 && p.stream && p.op != tmp::kChannel && p.access != tmp::kVec4Understated,
+          "%s flat plan outside its case", tag);
+    CHECK(p.M * p.N == M * N && (M == 1 || ld == N), "%s flat plan over a view that is not one row", tag);
+    CHECK(p.grid >= 1 && p.grid <= p.nwork, "%s grid %u nwork %u", tag, p.grid, p.nwork);
+    CHECK(p.flat_last >= 1 && p.flat_last <= 256, "%s last item of %u elements", tag, p.flat_last);
+    const uint32_t nwhole = p.flat_last == 256 ? p.nwork : p.nwork - 1;
+    const uint32_t tail = p.flat_last == 256 ? 0 : p.flat_last;
+    const int threads = p.access == tmp::kScalar1 ? 256 : 64;
+    const int per = p.access == tmp::kVec4 ? 1 : p.access == tmp::kScalar ? 4 : 1;
+    const int W = p.access == tmp::kVec4 ? 4 : 1;
+    std::vector<uint8_t> hits(size_t(M * N), 0);
+    for (uint32_t w = 0; w < p.nwork; ++w) {
+        const int64_t base = int64_t(w) * 256;
+        for (int t = 0; t < threads; ++t)
+            for (int u = 0; u < per; ++u) {
+                // element of the item this (thread, slot) moves first, then W consecutive ones
+                const int64_t e0 = p.access == tmp::kVec4 ? 4 * t : t + 64 * u;
+                for (int e = 0; e < W; ++e) {
+                    const int64_t el = e0 + e;
+                    CHECK(el < 256, "%s element %ld beyond the item", tag, long(el));
+                    const bool live = w < nwhole || el < int64_t(tail);
+                    if (live) {
+                        CHECK(base + el < M * N, "%s element %ld past the row", tag, long(base + el));
+                        if (base + el < M * N)
+                            ++hits[size_t(base + el)];
+                    }
+                }
+            }
+    }
+    for (int64_t a = 0; a < M * N; ++a)
+        if (hits[size_t(a)] != 1) {
+            CHECK(false, "%s flat element %ld stored %d times", tag, long(a), int(hits[size_t(a)]));
+            break;
+        }
+    ++g_checked;
+    ++g_flat;
+}
+
 static void replay_map(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, uintptr_t xbase,
                        const char *tag) {
-    const int W = p.access == tmp::kScalar ? 1 : 4;
+    if (p.flat) {
+        replay_flat(p, M, N, ld, tag);
+        return;
+    }
+    const int W = p.access == tmp::kScalar || p.access == tmp::kScalar1 ? 1 : 4;
     const int U = p.access == tmp::kScalar ? tmp::kScalarChunksPerThread : 1;
     const uint32_t bs = 1u << p.log_bs;
     const uint32_t chunks = 1u << (p.log_r + p.log_gv);
@@ -532,6 +579,6 @@ int main() {
     check_transposes();
     check_reductions();
     check_split_rows();
-    std::printf("plan_check: %ld plans checked, %ld failures\n", g_checked, g_failed);
+    std::printf("plan_check: %ld plans checked (%ld flat), %ld failures\n", g_checked, g_flat, g_failed);
     return g_failed == 0 ? 0 : 1;
 }

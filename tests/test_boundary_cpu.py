@@ -94,6 +94,55 @@ def test_split_matches_pages_and_oracle():
     assert tm.tm_split(10, 0)[0] == tm.TM_E_INVAL
 
 
+# ---- the row walk's column tiles ----------------------------------------------------------------
+
+LINE = 0x100000  # a 128-byte-aligned address: inspected by the query, never dereferenced
+
+
+def test_row_walk_honours_the_pages_masked_max_tile():
+    """'Reductions over a ragged tile' walks Nk = 1000 columns in BC = 64 tiles: 15 whole tiles and
+    one of 40 columns.  That is the walk the row reductions run on 8192 x 1000, with 16-byte rows
+    and with rows off the 16-byte grid (row stride 1001) alike."""
+    assert tm.tm_row_walk(8192, 1000, 1000, 16, 64, 0, LINE) == (tm.TM_OK, 64, 15, 40, 16)
+    st, bc, nf, rem, lanes = tm.tm_row_walk(8192, 1000, 1001, 16, 64, 0, LINE)
+    assert (st, bc, nf, rem) == (tm.TM_OK, 64, 15, 40)
+    assert (nf, rem) == oracle.split(1000, 64)
+    # its aligned counterpart: 16 whole tiles, no remainder
+    assert tm.tm_row_walk(8192, 1024, 1024, 16, 64, 1, LINE) == (tm.TM_OK, 64, 16, 0, 16)
+    # the promise is checked as the reductions check it
+    assert tm.tm_row_walk(8192, 1000, 1000, 16, 64, 1, LINE)[0] == tm.TM_E_ALIGN
+
+
+def test_row_walk_split_is_the_remainder_rule():
+    """Whatever tile the walk takes, nfull and rem are the remainder split of N by it, the tile is
+    a whole number of chunks per lane, and a caller tile is taken exactly when it keeps at least
+    half the lanes and at most 4 chunks per lane."""
+    for M in (1, 7, 300, 4096):
+        for N in (1, 5, 16, 63, 64, 100, 1000, 4096, 70000):
+            for ld in (N + (-N) % 4, N + 1 if N % 4 == 0 else N):
+                W = 4 if M <= 1 or ld % 4 == 0 else 1  # 16-byte chunks when every row starts on 16 bytes
+                for BC in (1, 4, 16, 64, 256, 1024):
+                    st, bc, nf, rem, lanes = tm.tm_row_walk(M, N, ld, 1, BC, 0, LINE)
+                    assert st == tm.TM_OK
+                    assert (nf, rem) == oracle.split(N, bc), (M, N, ld, BC)
+                    assert bc % (lanes * W) == 0 and 1 <= bc // (lanes * W) <= 4, (M, N, ld, BC, bc, lanes)
+                    if bc == BC:
+                        continue
+                    # the caller's tile was not taken: it was not whole chunks, would leave fewer
+                    # than half the lanes, or would need more than 4 chunks per lane
+                    assert BC % W or BC // W < lanes // 2 or BC // W > 4 * lanes, (M, N, ld, BC, bc, lanes)
+
+
+def test_row_walk_errors():
+    assert tm.tm_row_walk(-1, 10, 10, 1, 64, 0, LINE)[0] == tm.TM_E_INVAL
+    assert tm.tm_row_walk(4, 10, 9, 1, 64, 0, LINE)[0] == tm.TM_E_INVAL     # ld < N
+    assert tm.tm_row_walk(4, 10, 10, 1, 0, 0, LINE)[0] == tm.TM_E_INVAL     # tile <= 0
+    assert tm.tm_row_walk(4, 10, 10, 1, 48, 0, LINE)[0] == tm.TM_E_UNSUPPORTED
+    assert tm.tm_row_walk(4, 10, 10, 1, 64, 0, None)[0] == tm.TM_E_INVAL   # NULL with work
+    assert tm.tm_row_walk(4, 10, 10, 1, 64, 0, LINE + 2)[0] == tm.TM_E_INVAL  # not 4-byte aligned
+    assert tm.tm_row_walk(0, 10, 10, 1, 64, 0, None)[0] == tm.TM_OK
+
+
 # ---- tile scheduler counts ---------------------------------------------------------------------
 
 def test_plan_tiles_workload_shapes():

@@ -1,0 +1,160 @@
+"""GPU parity of the maps over one contiguous row in 1 KiB work items (mapflat.hip), the kernel that
+every view with contiguous rows on 128-byte lines reaches: rows of every length around the 256-element
+item boundaries (whole items only, a ragged last item of 1 .. 255 elements), in the three access
+kinds (16-byte chunks, four 4-byte elements per lane, one element per thread), for the affine map,
+the scale and the copy, on the ragged and the aligned path.  Bit for bit against the oracle, with
+line-sized 0x7F guard bands before and after the output.  Also the row walk that honours the
+caller's column tile: the walk tm_row_walk reports is the one whose results are checked.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from edge_masking_vector_amd import inputs
+from gpu_helpers import LINE_GUARD_FLOATS, Guarded, bits, sentinel_host
+
+pytestmark = pytest.mark.gpu
+
+tm = pytest.importorskip("edge_masking_vector_amd.tilemap")
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+LENGTHS = [1, 3, 4, 5, 63, 64, 255, 256, 257, 511, 512, 513, 1023, 1025, 4096 * 3 + 7, 65536, 1000003]
+VARIANTS = [tm.TM_VAR_AUTO, tm.TM_VAR_SCALAR, tm.TM_VAR_VEC4]
+
+
+def _run(op, X, Y, M, N, TM, TN, aligned, variant, alpha, beta):
+    s = torch.cuda.current_stream()
+    if op == "affine":
+        return tm.tm_map_affine(X.ptr, N, Y.ptr, N, M, N, alpha, beta, TM, TN, aligned, variant, s)
+    if op == "scale":
+        return tm.tm_scale2d(X.ptr, N, Y.ptr, N, M, N, alpha, TM, TN, aligned, variant, s)
+    return tm.tm_copy2d(X.ptr, N, Y.ptr, N, M, N, TM, TN, aligned, variant, s)
+
+
+def _ref(op, x, y, M, N, alpha, beta):
+    if op == "affine":
+        oracle.map_affine(x, N, y, N, M, N, alpha, beta)
+    elif op == "scale":
+        oracle.scale2d(x, N, y, N, M, N, alpha)
+    else:
+        oracle.copy2d(x, N, y, N, M, N)
+
+
+def _check(dev, op, M, N, TM, TN, aligned, variant, seed, alpha=0.75, beta=-0.25, expect=tm.TM_OK):
+    n = M * N
+    xh = inputs.uniform(seed, n, -8.0, 8.0)
+    if op == "copy" and n >= 4:
+        xh[:4] = np.array([0x7FC0BEEF, 0x80000000, 0x00000001, 0xFF800000], np.uint32).view(np.float32)
+    X = Guarded(n, dev, guard=LINE_GUARD_FLOATS)   # the row starts on a 128-byte line
+    X.upload(xh)
+    Y = Guarded(n, dev, guard=LINE_GUARD_FLOATS)
+    st = _run(op, X, Y, M, N, TM, TN, aligned, variant, alpha, beta)
+    assert st == expect, (op, M, N, TM, TN, aligned, variant, tm.tm_status_string(st))
+    torch.cuda.synchronize()
+    want = sentinel_host(Y.buf.numel())
+    if st == tm.TM_OK:   # a refused call writes nothing
+        region = want[Y.off:Y.off + n].copy()
+        _ref(op, xh, region, M, N, alpha, beta)
+        want[Y.off:Y.off + n] = region
+    assert np.array_equal(bits(Y.host()), bits(want)), (op, M, N, TM, TN, aligned, variant)
+    assert X.guards_intact()
+
+
+@pytest.mark.parametrize("op", ["affine", "scale", "copy"])
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_flat_row_every_tail(dev, op, variant):
+    """One row (M = 1) on the ragged path: every length around the item boundaries."""
+    for k, n in enumerate(LENGTHS):
+        note("flat row %s variant %d n %d" % (op, variant, n))
+        _check(dev, op, 1, n, 1, 64, 0, variant, seed=1000 + k)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_flat_contiguous_2d_views(dev, variant):
+    """Views with contiguous rows are one flat row: the ragged 4100 x 1000 workload, a view whose
+    flat length is not a multiple of 4 (the last chunk straddles the end), and aligned views."""
+    cases = [(4100, 1000, 64, 64, 0), (333, 17, 4, 16, 0), (7, 3, 1, 1, 0),
+             (4096, 1024, 64, 64, 1), (256, 512, 32, 128, 1), (64, 12, 4, 4, 1)]
+    for k, (M, N, TM, TN, aligned) in enumerate(cases):
+        note("flat view %dx%d tile %dx%d aligned %d variant %d" % (M, N, TM, TN, aligned, variant))
+        # 16-byte vectors asked for on rows off the 16-byte grid (row stride N % 4 != 0) are refused
+        expect = tm.TM_E_ALIGN if variant == tm.TM_VAR_VEC4 and N % 4 else tm.TM_OK
+        _check(dev, "affine", M, N, TM, TN, aligned, variant, seed=2000 + k, expect=expect)
+
+
+def test_flat_scale_4096_full_size(dev):
+    """The scale workload itself (4096 x 4096, 32 x 128 tiles, aligned, 16-byte chunks): bit for
+    bit equal to alpha * x computed exactly in double and rounded once (exact for alpha = 1.5)."""
+    M = N = 4096
+    xh = inputs.scale_input(M, N)
+    x = torch.from_numpy(xh).to(dev)
+    y = torch.full_like(x, float("nan"))
+    tm.check(tm.tm_scale2d(x, N, y, N, M, N, 1.5, 32, 128, 1, tm.TM_VAR_VEC4))
+    want = (xh.astype(np.float64) * 1.5).astype(np.float32)
+    assert np.array_equal(bits(y), bits(want))
+
+
+def test_flat_large_row_loops(dev):
+    """A row of more than 2^20 work items (2^28 + 77 floats, 1 GiB): the grid is capped and each
+    workgroup loops; every element and the ragged end are still moved exactly once.  Checked on
+    samples (the oracle on a stride of elements) and on the ends."""
+    n = (1 << 28) + 77
+    free, total = torch.cuda.mem_get_info()
+    if free < 3 * 4 * n:
+        pytest.skip("needs 3 GiB of free device memory")
+    note("flat row of %d floats" % n)
+    x = torch.arange(n, dtype=torch.float32, device=dev) * 0.5
+    y = torch.full((n,), -1.0, device=dev)
+    tm.check(tm.tm_map_affine(x, n, y, n, 1, n, 2.0, 1.0, 1, 1024, 0, tm.TM_VAR_VEC4))
+    idx = torch.cat([torch.arange(0, 300, device=dev), torch.arange(n - 300, n, device=dev),
+                     torch.randint(0, n, (100000,), device=dev, generator=torch.Generator(dev).manual_seed(3))])
+    got = y[idx].cpu().numpy()
+    xs = x[idx].cpu().numpy()
+    want = np.empty_like(xs)
+    oracle.map_affine(xs, xs.size, want, xs.size, 1, xs.size, 2.0, 1.0)
+    assert np.array_equal(bits(got), bits(want))
+    del x, y
+
+
+# ---- the row walk honours the caller's column tile -----------------------------------------------
+
+@pytest.mark.parametrize("BC,ld", [(64, 1000), (128, 1000), (256, 1000), (1024, 1000), (64, 1001), (16, 1000)])
+def test_rowmax_walk_reported_and_exact(dev, BC, ld):
+    """8192 x 1000 scores, all negative, masked row maximum and softmax statistics under BR x BC
+    tiles: the walk tm_row_walk reports splits N by its tile as the oracle's splitter does, and
+    the maxima equal the oracle bit for bit whichever tile the walk takes (BC = 64: 15 whole tiles
+    and one of 40 columns, as 'Reductions over a ragged tile' walks it)."""
+    M, N = 8192, 1000
+    sh = inputs.matrix(inputs.scores_input(M, N), M, N, ld)
+    s = torch.from_numpy(sh).to(dev)
+    st, bc, nfull, rem, lanes = tm.tm_row_walk(M, N, ld, 16, BC, 0, s)
+    assert st == tm.TM_OK and (nfull, rem) == oracle.split(N, bc)
+    if BC == 64:
+        assert (bc, nfull, rem) == (64, 15, 40)
+    note("rowmax walk BC=%d ld=%d: bc %d, %d + %d, %d lanes" % (BC, ld, bc, nfull, rem, lanes))
+    out = torch.empty(M, device=dev)
+    tm.check(tm.tm_rowmax_masked(s, ld, out, M, N, 16, BC, 0))
+    want = oracle.rowmax(sh, ld, M, N)
+    assert np.array_equal(bits(out), bits(want))
+    assert (out.cpu().numpy() < -1.0).all()   # never the 0 a zero fill would give
+    m = torch.empty(M, device=dev)
+    l = torch.empty(M, device=dev)
+    tm.check(tm.tm_softmax_stats(s, ld, m, l, M, N, 16, BC, 0))
+    wm, wl = oracle.softmax_stats(sh, ld, M, N)
+    assert np.array_equal(bits(m), bits(wm))
+    assert np.allclose(l.cpu().numpy(), wl, rtol=1e-5, atol=0)

@@ -117,7 +117,9 @@ def test_sums_long_rows_and_tall_columns(dev):
 @pytest.mark.parametrize("M", [1, 7, 300, 700, 1500])
 def test_row_reductions_multiwave_rows(dev, M):
     """Few long rows get a workgroup of several waves per row, combined across the waves through
-    LDS: 1500 rows -> 128 lanes per row, 700 -> 256, 300 -> 512, 7 and 1 -> 1024.  Ragged N
+    LDS: 1500 rows -> 128 lanes per row, 700 -> 256, 300 -> 512, 7 and 1 -> 1024 under the 1 x 1
+    tile (too narrow to be the walk's); the 4 x 256 tile becomes the walk's column tile where it
+    keeps half those lanes (64 lanes for 1500 rows, one wave per row).  Ragged N
     (16411 columns), 16-byte rows (pitch 16412) and 4-byte rows (pitch 16413 on a base off the
     16-byte grid); sums within 1e-5 of fp64, maxima and softmax m bit-exact, l within 1e-5."""
     N = 16411
@@ -145,9 +147,10 @@ def test_row_reductions_multiwave_rows(dev, M):
 
 
 def test_row_results_do_not_depend_on_the_tile(dev):
-    """The caller's tile states the promise only: every menu tile width gives the oracle's maxima
-    (bit for bit) and sums within tolerance on 2048 x 1001 with 16-byte rows, whose N is not a
-    multiple of 4 (the chunk straddling column N is masked element by element)."""
+    """Whichever column tile the walk takes -- the caller's where it suits the lanes of a row, else
+    its own -- every menu tile width gives the oracle's maxima (bit for bit) and sums within
+    tolerance on 2048 x 1001 with 16-byte rows, whose N is not a multiple of 4 (the chunk
+    straddling column N is masked element by element)."""
     M, N, ld = 2048, 1001, 1004
     xh = inputs.uniform(57, M * N, -10.0, 10.0)
     X, host = device_matrix(xh, M, N, ld, dev)
