@@ -93,8 +93,10 @@ class Timer:
     After the synchronize that opens a region, PREROLL untimed launches (buffer sets -PREROLL ..
     -1 of the rotation) are enqueued before the start event.  The GPU is then already busy when
     the start event is reached, and the host's latency to issue the first timed launch (several
-    microseconds through Python) is not counted as a step: without it, 20 timed steps of 21 us
-    measured 21.7 us each against 21.4 us over 50-launch batches."""
+    microseconds through Python) is not counted as a step: without it, 20 timed steps of 21.4 us
+    measured 21.7 us each.  A region still carries the events' own cost, about 3-4 us (two events
+    recorded back to back on a busy GPU measure that far apart), so 20-launch regions read about
+    0.1-0.2 us per launch above 50-launch batches of the same kernel."""
 
     def __init__(self, torch, stream):
         self.torch, self.stream = torch, stream
@@ -114,7 +116,9 @@ class Timer:
 
 
 def rotated(torch, host, n_sets, dev, extra=0):
-    """n_sets device copies of `host` (plus `extra` floats of slack at the end of each)."""
+    """n_sets device copies of `host` (plus `extra` floats of slack at the end of each).  Output
+    buffers are allocated zero-filled (torch.zeros), so that, like the inputs, every page they span
+    has been written before anything is timed."""
     base = torch.from_numpy(host).to(dev)
     sets = []
     for _ in range(n_sets):
@@ -156,7 +160,7 @@ def main():
     xh = inputs.scale_input(M, N)
     R = sets_for(step_bytes)
     xs = rotated(torch, xh, R, dev)
-    ys = [torch.empty_like(x) for x in xs]
+    ys = [torch.zeros_like(x) for x in xs]
 
     def step(i):
         st = tm.tm_scale2d(xs[i % R], N, ys[i % R], N, M, N, alpha, TM, TN, 1, tm.TM_VAR_VEC4, stream)
@@ -312,7 +316,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     nb = 2 * M * N * 4
     R = sets_for(nb)
     xs = rotated(torch, inputs.uniform(10, M * N, -1.0, 1.0), R, dev)
-    ys = [torch.empty_like(x) for x in xs]
+    ys = [torch.zeros_like(x) for x in xs]
     timed("_probe_tm", nb, R, lambda i: ok(tm.tm_copy2d(xs[i], N, ys[i], N, M, N, 32, 128, 1,
                                                          tm.TM_VAR_VEC4, stream)), "")
     timed("_probe_rt", nb, R, lambda i: ys[i].copy_(xs[i]), "")
@@ -329,7 +333,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     nb = 2 * M * N * 4
     R = sets_for(nb)
     xs = rotated(torch, xh, R, dev)
-    ys = [torch.empty_like(x) for x in xs]
+    ys = [torch.zeros_like(x) for x in xs]
     timed("scale_4096_ragged_vec4", nb, R,
           lambda i: ok(tm.tm_scale2d(xs[i], N, ys[i], N, M, N, 1.5, 32, 128, 0, tm.TM_VAR_VEC4, stream)),
           "same shape, ragged path (per-tile whole-tile test)")
@@ -346,7 +350,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     nb = 2 * n * 4
     R = sets_for(nb)
     xs = rotated(torch, a, R, dev)
-    ys = [torch.empty_like(x) for x in xs]
+    ys = [torch.zeros_like(x) for x in xs]
     for name, var, TN, aligned, how in (
             ("map1d_scalar", tm.TM_VAR_SCALAR, 256, 1, "one element per thread (the page's scalar kernel)"),
             ("map1d_vec4_understated", tm.TM_VAR_VEC4_UNDERSTATED, 1024, 1,
@@ -367,7 +371,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
         nb = 2 * M * N * 4
         R = sets_for(nb)
         xs = rotated(torch, xh, R, dev)
-        ys = [torch.empty_like(x) for x in xs]
+        ys = [torch.zeros_like(x) for x in xs]
         timed(name, nb, R,
               lambda i, M=M, N=N, aligned=aligned, var=var: ok(tm.tm_map_affine(
                   xs[i], N, ys[i], N, M, N, 0.75, -0.25, 64, 64, aligned, var, stream)),
@@ -389,7 +393,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
         nb = 2 * M * N * 4
         R = sets_for(2 * M * ld * 4)
         xs = rotated(torch, xh, R, dev)
-        ys = [torch.empty_like(x) for x in xs]
+        ys = [torch.zeros_like(x) for x in xs]
         timed(name, nb, R,
               lambda i, M=M, N=N, ld=ld, TM=TM, TN=TN, var=var: ok(tm.tm_map_affine(
                   xs[i], ld, ys[i], ld, M, N, 0.75, -0.25, TM, TN, 0, var, stream)),
@@ -402,7 +406,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     xh = inputs.colrow_input(M, N)
     R = sets_for(M * N * 4)
     xs = rotated(torch, xh, R, dev)
-    outs = [torch.empty(N, device=dev) for _ in range(R)]
+    outs = [torch.zeros(N, device=dev) for _ in range(R)]
     nb = M * N * 4 + N * 4
     walk = tm.tm_row_walk(M, N, N, 4, 1024, 1, xs[0])
     timed("rowsum_4096", nb, R,
@@ -413,7 +417,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
                                ("colsum_naive_xcd_4096", tm.TM_COL_NAIVE_XCD, 256, 1),
                                ("colsum_lds_4096", tm.TM_COL_LDS, 256, 64)):
         wsb = tm.tm_colsum_workspace_bytes(M, N, TM, TN, walk)
-        wss = [torch.empty(wsb // 4, device=dev) for _ in range(R)]
+        wss = [torch.zeros(wsb // 4, device=dev) for _ in range(R)]
         slabs = wsb // (4 * N)
         geometry = ("the naive walk: %d-row slabs of one column per workgroup" % TM if walk != tm.TM_COL_LDS
                     else "the LDS walk's own %d-row slabs by 128-column strips" % (M // slabs))
@@ -433,7 +437,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     xh = inputs.uniform(11, M * N, 0.0, 1.0)
     R = sets_for(M * N * 4)
     xs = rotated(torch, xh, R, dev)
-    outs = [torch.empty(N, device=dev) for _ in range(R)]
+    outs = [torch.zeros(N, device=dev) for _ in range(R)]
     assert tm.tm_colsum_workspace_bytes(M, N, 16, 64, tm.TM_COL_LDS) == 0
     timed("colsum_lds_16x1048576", M * N * 4 + N * 4, R,
           lambda i: ok(tm.tm_colsum(xs[i], N, outs[i], M, N, 16, 64, 1, tm.TM_COL_LDS, None, 0, stream)),
@@ -446,7 +450,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
         sh = inputs.scores_input(M, N)
         R = sets_for(M * N * 4)
         ss = rotated(torch, sh, R, dev)
-        outs = [torch.empty(M, device=dev) for _ in range(R)]
+        outs = [torch.zeros(M, device=dev) for _ in range(R)]
         nb = M * N * 4 + M * 4
         st, bc, nfull, rem, lanes = tm.tm_row_walk(M, N, N, 16, 64, aligned, ss[0])
         ok(st)
@@ -456,7 +460,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
               lambda i, M=M, N=N, aligned=aligned: ok(tm.tm_rowmax_masked(ss[i], N, outs[i], M, N, 16, 64,
                                                                           aligned, stream)),
               "16x64 tiles, %s; -1e30 fill" % walk)
-        ls = [torch.empty(M, device=dev) for _ in range(R)]
+        ls = [torch.zeros(M, device=dev) for _ in range(R)]
         timed(name.replace("rowmax", "softmax_stats"), nb + M * 4, R,
               lambda i, M=M, N=N, aligned=aligned: ok(tm.tm_softmax_stats(ss[i], N, outs[i], ls[i], M, N, 16,
                                                                           64, aligned, stream)),
@@ -468,10 +472,10 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     sh = inputs.uniform(6, M * N, -10.0, -1.0)
     R = sets_for(M * N * 4)
     ss = rotated(torch, sh, R, dev)
-    outs = [torch.empty(M, device=dev) for _ in range(R)]
-    ls = [torch.empty(M, device=dev) for _ in range(R)]
+    outs = [torch.zeros(M, device=dev) for _ in range(R)]
+    ls = [torch.zeros(M, device=dev) for _ in range(R)]
     wsb = tm.tm_rows_workspace_bytes(M, N)
-    ws = torch.empty(wsb // 4, device=dev)
+    ws = torch.zeros(wsb // 4, device=dev)
     nb = M * N * 4 + 2 * M * 4
     timed("softmax_stats_8x262144_one_pass", nb, R,
           lambda i: ok(tm.tm_softmax_stats(ss[i], N, outs[i], ls[i], M, N, 1, 64, 0, stream)),
@@ -487,7 +491,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     nb = 2 * M * N * 4 + N * 4
     R = sets_for(nb)
     xs = rotated(torch, xh, R, dev)
-    ys = [torch.empty_like(x) for x in xs]
+    ys = [torch.zeros_like(x) for x in xs]
     bias = torch.from_numpy(inputs.uniform(8, N, -1.0, 1.0)).to(dev)
     timed("channel_bias_add_nhwc_32x64x56x56", nb, R,
           lambda i: ok(tm.tm_channel_affine(xs[i], N, None, bias, ys[i], N, M, N, 64, 64, 1,
@@ -513,7 +517,7 @@ def size_curve(torch, tm, inputs, dev, stream, path):
         nb = 2 * n * n * 4
         R = sets_for(nb)
         xs = [torch.empty(n * n, device=dev).uniform_(-1.0, 1.0) for _ in range(R)]
-        ys = [torch.empty_like(x) for x in xs]
+        ys = [torch.zeros_like(x) for x in xs]
 
         def launch(i):
             st = tm.tm_scale2d(xs[i % R], n, ys[i % R], n, n, n, 1.5, 32, 128, 1, tm.TM_VAR_VEC4, stream)
@@ -572,7 +576,7 @@ def transpose_paths(torch, tm, inputs, dev, stream, timed, ok):
     nb = 2 * M * N * 4
     R = sets_for(nb)
     xs = rotated(torch, xh, R, dev)
-    ys = [torch.empty_like(x) for x in xs]
+    ys = [torch.zeros_like(x) for x in xs]
     timed("transpose_4096_aligned", nb, R,
           lambda i: ok(tm.tm_transpose(xs[i], N, 0, ys[i], M, 0, 1, M, N, 64, 64, 1, stream)),
           "y = x^T, 64x64 tiles staged through LDS")
@@ -582,7 +586,7 @@ def transpose_paths(torch, tm, inputs, dev, stream, timed, ok):
     nb = 2 * B * C * HW * 4
     R = sets_for(nb)
     xs = rotated(torch, xh, R, dev)
-    ys = [torch.empty_like(x) for x in xs]
+    ys = [torch.zeros_like(x) for x in xs]
     timed("nchw_to_nhwc_32x64x56x56", nb, R,
           lambda i: ok(tm.tm_transpose(xs[i], HW, C * HW, ys[i], C, HW * C, B, C, HW, 64, 64, 1, stream)),
           "batched transpose [B][C][HW] -> [B][HW][C]")
@@ -594,7 +598,7 @@ def transpose_paths(torch, tm, inputs, dev, stream, timed, ok):
     nb = 2 * B * C * HW * 4
     R = sets_for(nb)
     xs = rotated(torch, xh, R, dev)
-    ys = [torch.empty_like(x) for x in xs]
+    ys = [torch.zeros_like(x) for x in xs]
     timed("nchw_to_nhwc_32x3x224x224", nb, R,
           lambda i: ok(tm.tm_transpose(xs[i], HW, C * HW, ys[i], C, HW * C, B, C, HW, 1, 64, 0, stream)),
           "batched transpose [B][3][HW] -> [B][HW][3], ragged path, packed side as one block")

@@ -36,6 +36,7 @@ __device__ __forceinline__ void st4_nt(float *p, float v) { __builtin_nontempora
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kPolicyDeviceStream = 16 | 2;  // sc1 | nt
+constexpr int kPolicyStream = 2;              // nt
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t segment_rsrc(const float *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, bytes, kRawBufferWord3);
 }

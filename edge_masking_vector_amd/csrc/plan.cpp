@@ -413,12 +413,37 @@ size_t rows_ws_bytes(int64_t M, int64_t N) {
     return static_cast<size_t>(M) * static_cast<size_t>(segs) * kRowPartialBytes;
 }
 
-// Lanes per row (*lpr, a power of two) and chunks per lane per column tile (*per_tile) of the
-// one-pass row walk over M rows of N elements (16-byte chunks when vec).  TC: the caller's column
-// tile.
-static void row_walk(int64_t M, int64_t N, bool vec, int TC, int *lpr_out, int *per_tile_out) {
+// The one-pass row walk over M rows of N elements (16-byte chunks when vec) under the caller's
+// column tile TC.
+struct RowWalk {
+    int lpr = 1;        // lanes per row (a power of two)
+    int per_tile = 1;   // chunks per lane per column tile (the batched walk)
+    int64_t bc = 1;     // column tile
+    bool once = false;  // every chunk of a row in flight at once (row_once)
+    int once_k = 0;     // chunks per lane of a one-batch row
+};
+
+static RowWalk row_walk(int64_t M, int64_t N, bool vec, int TC) {
     const int W = vec ? 4 : 1;
     const int64_t chunks = ceil_div(N, W);  // chunks per row
+    RowWalk rw;
+    // Rows longer than a tiny row and short enough for one batch: lpr lanes (at least
+    // kRowOnceMinLanes) with K chunks each cover the row, all issued before any arithmetic, and
+    // the caller's tile decides which chunks are whole tiles (read without a mask) and which
+    // belong to the one masked remainder tile; it cannot starve the row of lanes, so it is always
+    // the walk's tile (a tile narrower than a chunk counts as one chunk).  Against the batched
+    // walk below, on 8192 x 1000 masked maxima (1 GiB of rotating inputs, one process): 6.6-6.8 us
+    // with 16, 32 or 64 lanes per row against 7.3-7.4 us.  Rows of more than half the batch's
+    // lanes' reach with too few rows to fill the GPU keep the multi-wave walk.
+    const int K = vec ? kRowOnceK : kRowOnceKScalar;
+    const bool few_long = chunks > int64_t{K} * 32 && M < kRowWideWaves;
+    if (chunks > int64_t{K} * kRowOnceMinLanes / 2 && chunks <= int64_t{K} * 64 && !few_long) {
+        rw.once = true;
+        rw.once_k = K;
+        rw.lpr = std::max(kRowOnceMinLanes, 1 << ilog2(ceil_div(chunks, K)));
+        rw.bc = std::max(TC, W);
+        return rw;
+    }
     // Lanes per row, fitted to HBM-streamed sweeps of forced lane counts (N = 4 to 2000 at 32 MB,
     // 1 GiB of rotating inputs, both chunk widths) and an interleaved comparison at 8192 x 1000
     // (16 / 32 / 64 lanes: 7.31 / 7.24 / 7.97 us): rows of up to 64 16-byte chunks are one tile
@@ -469,8 +494,10 @@ static void row_walk(int64_t M, int64_t N, bool vec, int TC, int *lpr_out, int *
             per_tile = static_cast<int>(tc / l);
         }
     }
-    *lpr_out = lpr;
-    *per_tile_out = per_tile;
+    rw.lpr = lpr;
+    rw.per_tile = per_tile;
+    rw.bc = int64_t{lpr} * W * per_tile;
+    return rw;
 }
 
 int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t N, int TR, int TC,
@@ -533,16 +560,17 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
     // 16-byte chunks whatever N is: whole tiles hold whole chunks, and the remainder tile masks
     // the chunk that straddles N element by element.
     const bool vec = rows16(x, M, ld);
-    const int W = vec ? 4 : 1;
-    int lpr, per_tile;
-    row_walk(M, N, vec, TC, &lpr, &per_tile);
+    const RowWalk rw = row_walk(M, N, vec, TC);
+    const int lpr = rw.lpr;
     plan->launch = true;
     plan->op = op;
     plan->vec = vec;
     plan->lpr = lpr;
     plan->block = lpr > 64 ? lpr : kBlock;
-    plan->per_tile = per_tile;
-    plan->bc = lpr * W * per_tile;
+    plan->per_tile = rw.per_tile;
+    plan->bc = static_cast<int>(rw.bc);
+    plan->once = rw.once;
+    plan->once_k = rw.once_k;
     split(N, plan->bc, &plan->nfull, &plan->rem);  // whole column tiles + one masked remainder tile
     const int64_t groups = ceil_div(M, plan->block / lpr);
     if (groups > INT32_MAX)
@@ -576,11 +604,9 @@ int row_walk_query(int64_t M, int64_t N, int64_t ld, int TR, int TC, int aligned
         return st;
     if (aligned && !promise_holds(M, N, ld, 0, TR, TC, x, nullptr))
         return TM_E_ALIGN;
-    const bool vec = rows16(x, M, ld);
-    int lpr = 1, per_tile = 1;
-    row_walk(M, N, vec, TC, &lpr, &per_tile);
-    *lanes = lpr;
-    *bc = int64_t{lpr} * (vec ? 4 : 1) * per_tile;
+    const RowWalk rw = row_walk(M, N, rows16(x, M, ld), TC);
+    *lanes = rw.lpr;
+    *bc = rw.bc;
     return split(N, *bc, nfull, rem);
 }
 

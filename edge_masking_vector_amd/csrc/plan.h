@@ -46,6 +46,12 @@ constexpr int kRowLongLanes = 256;
 // The caller's column tile becomes the row walk's when it keeps at least half the lanes the
 // row's length and count call for and needs at most this many chunks per lane per tile.
 constexpr int64_t kRowTileMaxChunks = 4;
+// Rows of more than kTinyRowChunks and at most kRowOnceK * 64 chunks (16-byte chunks; 4-byte
+// chunks: kRowOnceKScalar * 64) are read in one batch: at least kRowOnceMinLanes lanes per row,
+// every chunk in flight at once.
+constexpr int kRowOnceK = 8;
+constexpr int kRowOnceKScalar = 16;
+constexpr int kRowOnceMinLanes = 16;
 // Rows of one lane each run on at most this many workgroups, each looping over several row groups.
 constexpr int64_t kRowTinyGrid = 4096;
 // Split rows (the row calls that take a workspace): fewer than kRowSplitRows rows of at least
@@ -147,6 +153,10 @@ struct RowPlan {
     int64_t nfull = 0;            // whole column tiles (unmasked)
     int64_t rem = 0;              // live columns of the remainder tile (0: none)
     int bc = 1;                   // column tile width
+    // Rows read in one batch (row_once): every chunk of a row is in flight at once, `once_k`
+    // chunks per lane at a stride of lpr chunks; chunks below nfull * bc / W are whole tiles.
+    bool once = false;
+    int once_k = 0;
     uint32_t grid = 0;
     const float *x = nullptr;
     float *out = nullptr;         // sums / maxima (softmax statistics: m)

@@ -262,6 +262,114 @@ __device__ __forceinline__ float sum_exp_live(f4 v, float b, int64_t live) {
     return acc;
 }
 
+// ---- rows read in one batch ---------------------------------------------------------------------
+// Rows of a few hundred chunks: LPR lanes per row (16, 32 or 64; kBlock / LPR rows per workgroup)
+// and K chunks per lane cover the row, lane g taking chunks g, g + LPR, ..., so a row costs one
+// memory round trip.  The loads carry no control flow: every one is issued before any wait (a
+// branch around each load had the compiler wait for each before the next, 8 round trips instead
+// of 1: 7.9 against 6.9 us on 8192 x 1000).  A slot past the row loads the row's last chunk again
+// and is then replaced by the fill.  The caller's column tile decides the masks ([SLICING] "Loops
+// over a dynamic extent"): chunks below `whole` (the nfull whole tiles) are used as loaded;
+// elements of the one remainder tile keep their value iff their column is below N and take the
+// operator's fill otherwise ("Reductions over a ragged tile": -1.0e30 for the maximum).
+//
+// PART (16-byte chunks, N % 4 != 0): the chunk holding column N - 1 runs past the row, so every
+// load goes through a buffer resource spanning exactly the row's N floats, whose range check
+// returns 0 for each 4-byte word past the end (per word on gfx950) instead of reading it.
+struct OnceArgs {
+    const float *x;
+    float *out;    // sums / maxima; softmax statistics: m
+    float *out2;   // softmax statistics: l
+    int64_t ld, M, N;
+    int32_t whole;   // chunks of the whole tiles: nfull * bc / W
+    int32_t last;    // the row's last chunk: ceil(N / W) - 1
+};
+
+// OPK: tmp::kRowSum, kRowMax or kRowSoftmax.
+template <int OPK, int LPR, int K, bool VEC, bool PART>
+__global__ __launch_bounds__(kBlock) void row_once(OnceArgs a) {
+    using T = typename std::conditional<VEC, f4, float>::type;
+    using Op = typename std::conditional<OPK == tmp::kRowSum, SumOp, MaxOp>::type;
+    constexpr int W = VEC ? 4 : 1;
+    static_assert(VEC || !PART, "4-byte chunks never straddle the row's end");
+    const int t = threadIdx.x;
+    const int g = t % LPR;
+    const int64_t row = int64_t(blockIdx.x) * (kBlock / LPR) + t / LPR;
+    const int64_t rr = row < a.M ? row : a.M - 1;  // rows past M re-read row M-1, never stored
+    const float *xr = a.x + rr * a.ld;
+
+    T v[K];
+    if constexpr (PART) {
+        const __amdgpu_buffer_rsrc_t rx = segment_rsrc(xr, int(a.N * 4));
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int c = k * LPR + g;
+            v[k] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rx, (c < a.last ? c : a.last) * 16, 0,
+                                                                               kPolicyStream));
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int c = k * LPR + g;
+            v[k] = load_whole<VEC, LPR>(xr + int64_t(c < a.last ? c : a.last) * W);
+        }
+    }
+    // Masks of the remainder tile (and of the slots past the row): element e of chunk c is live
+    // iff its column c * W + e is below N.
+    auto live = [&](int c, int e) { return c < a.whole || int64_t(c) * W + e < a.N; };
+    auto masked = [&](T x, int c, float fill) {
+        if constexpr (VEC) {
+            x.x = live(c, 0) ? x.x : fill;
+            x.y = live(c, 1) ? x.y : fill;
+            x.z = live(c, 2) ? x.z : fill;
+            x.w = live(c, 3) ? x.w : fill;
+            return x;
+        } else {
+            return live(c, 0) ? x : fill;
+        }
+    };
+    if constexpr (OPK != tmp::kRowSoftmax) {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            v[k] = masked(v[k], k * LPR + g, Op::kFill);
+        // fixed-order fold: the K chunks pairwise, the chunk's elements, then the lanes
+#pragma unroll
+        for (int st = 1; st < K; st <<= 1)
+#pragma unroll
+            for (int i = 0; i + st < K; i += 2 * st)
+                v[i] = combine<Op>(v[i], v[i + st]);
+        const float r = group_reduce<Op, LPR>(lanes<Op>(v[0]));
+        if (g == 0 && row < a.M)
+            a.out[row] = r;
+    } else {
+        // m: the lane's maximum (the fill never exceeds a score); l: sum of exp(s - m) over the
+        // live elements only; then the group maximum and the sum of l * exp(m - m_group).
+        float m = kMaxFill;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            v[k] = masked(v[k], k * LPR + g, kMaxFill);
+            m = __builtin_fmaxf(m, chunk_max(v[k]));
+        }
+        float l = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int c = k * LPR + g;
+            if constexpr (VEC) {
+                l += (live(c, 0) ? exp_f32(v[k].x - m) : 0.0f) + (live(c, 1) ? exp_f32(v[k].y - m) : 0.0f) +
+                     (live(c, 2) ? exp_f32(v[k].z - m) : 0.0f) + (live(c, 3) ? exp_f32(v[k].w - m) : 0.0f);
+            } else {
+                l += live(c, 0) ? exp_f32(v[k] - m) : 0.0f;
+            }
+        }
+        const float gm = group_reduce<MaxOp, LPR>(m);
+        const float gl = group_reduce<SumOp, LPR>(l * exp_f32(m - gm));
+        if (g == 0 && row < a.M) {
+            a.out[row] = gm;
+            a.out2[row] = gl;
+        }
+    }
+}
+
 template <int LPR, bool VEC, bool PRE>
 __global__ __launch_bounds__(block_threads<LPR>()) void row_softmax(RowArgs a) {
     using T = typename std::conditional<VEC, f4, float>::type;
@@ -567,11 +675,48 @@ const void *pick_op(const tmp::RowPlan &p) {
                                       : pick_vec<SumOp, PRE>(p);
 }
 
+template <int OPK, bool VEC, int K, bool PART>
+const void *pick_once_lpr(int lpr) {
+    switch (lpr) {
+    case 16: return reinterpret_cast<const void *>(&row_once<OPK, 16, K, VEC, PART>);
+    case 32: return reinterpret_cast<const void *>(&row_once<OPK, 32, K, VEC, PART>);
+    default: return reinterpret_cast<const void *>(&row_once<OPK, 64, K, VEC, PART>);
+    }
+}
+
+template <int OPK>
+const void *pick_once(const tmp::RowPlan &p) {
+    if (!p.vec)
+        return pick_once_lpr<OPK, false, tmp::kRowOnceKScalar, false>(p.lpr);
+    return p.N % 4 != 0 ? pick_once_lpr<OPK, true, tmp::kRowOnceK, true>(p.lpr)
+                        : pick_once_lpr<OPK, true, tmp::kRowOnceK, false>(p.lpr);
+}
+
+hipError_t launch_once(const tmp::RowPlan &p, hipStream_t stream) {
+    OnceArgs a;
+    a.x = p.x;
+    a.out = p.out;
+    a.out2 = p.out2;
+    a.ld = p.ld;
+    a.M = p.M;
+    a.N = p.N;
+    const int W = p.vec ? 4 : 1;
+    a.whole = static_cast<int32_t>(p.nfull * (p.bc / W));
+    a.last = static_cast<int32_t>((p.N + W - 1) / W - 1);
+    const void *fn = p.op == tmp::kRowMax       ? pick_once<tmp::kRowMax>(p)
+                     : p.op == tmp::kRowSoftmax ? pick_once<tmp::kRowSoftmax>(p)
+                                                : pick_once<tmp::kRowSum>(p);
+    void *args[] = {&a};
+    return hipLaunchKernel(fn, dim3(p.grid), dim3(kBlock), args, 0, stream);
+}
+
 }  // namespace
 
 hipError_t launch_rows(const tmp::RowPlan &p, hipStream_t stream) {
     if (p.split)
         return launch_split(p, stream);
+    if (p.once)
+        return launch_once(p, stream);
     RowArgs a;
     a.x = p.x;
     a.out = p.out;

@@ -396,7 +396,7 @@ static void check_transposes() {
 // ---- row and column reductions ----------------------------------------------------------------
 static void check_reductions() {
     const int64_t Ms[] = {0, 1, 7, 300, 2047, 1048583};
-    const int64_t Ns[] = {0, 1, 5, 64, 100, 1000, 4096, 1048576};
+    const int64_t Ns[] = {0, 1, 5, 64, 100, 257, 513, 1000, 2048, 2051, 4096, 1048576};
     for (int64_t M : Ms)
         for (int64_t N : Ns)
             for (int TR : {1, 4, 16, 256})
@@ -413,8 +413,35 @@ static void check_reductions() {
                             CHECK(p.lpr >= 1 && p.lpr <= tmp::kRowMaxLanes && (p.lpr & (p.lpr - 1)) == 0,
                                   "rows lpr %d", p.lpr);
                             CHECK(p.block == (p.lpr > 64 ? p.lpr : tmp::kBlock), "rows block %d", p.block);
-                            CHECK(p.bc == p.lpr * (p.vec ? 4 : 1) * p.per_tile, "rows bc %d", p.bc);
-                            CHECK(p.per_tile >= 1 && p.per_tile <= 4, "rows per_tile %d", p.per_tile);
+                            if (p.once) {
+                                // one batch (row_once): lane g of a row takes chunks g + k * lpr for
+                                // k < once_k; chunks below whole = nfull * bc / W load unmasked and
+                                // must lie inside the row; every chunk of the row is taken once
+                                const int W = p.vec ? 4 : 1;
+                                const int64_t chunks = (N + W - 1) / W;
+                                CHECK(p.bc == std::max(TC, W) && p.lpr >= tmp::kRowOnceMinLanes && p.lpr <= 64 &&
+                                          int64_t(p.lpr) * p.once_k >= chunks,
+                                      "rows once bc %d lpr %d k %d N %ld", p.bc, p.lpr, p.once_k, long(N));
+                                const int64_t whole = p.nfull * (p.bc / W);
+                                std::vector<uint8_t> seen(size_t(chunks), 0);
+                                for (int g = 0; g < p.lpr; ++g)
+                                    for (int k = 0; k < p.once_k; ++k) {
+                                        const int64_t c = int64_t(k) * p.lpr + g;
+                                        if (c < whole)
+                                            CHECK((c + 1) * W <= N, "rows once unmasked chunk %ld past N=%ld", long(c),
+                                                  long(N));
+                                        if (c < chunks)
+                                            ++seen[size_t(c)];
+                                    }
+                                for (int64_t c = 0; c < chunks; ++c)
+                                    if (seen[size_t(c)] != 1) {
+                                        CHECK(false, "rows once chunk %ld taken %d times", long(c), int(seen[size_t(c)]));
+                                        break;
+                                    }
+                            } else {
+                                CHECK(p.bc == p.lpr * (p.vec ? 4 : 1) * p.per_tile, "rows bc %d", p.bc);
+                                CHECK(p.per_tile >= 1 && p.per_tile <= 4, "rows per_tile %d", p.per_tile);
+                            }
                             CHECK(p.nfull * p.bc + p.rem == N && p.rem >= 0 && p.rem < p.bc,
                                   "rows split N=%ld bc=%d nfull=%ld rem=%ld", long(N), p.bc, long(p.nfull),
                                   long(p.rem));

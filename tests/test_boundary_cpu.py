@@ -103,20 +103,26 @@ def test_row_walk_honours_the_pages_masked_max_tile():
     """'Reductions over a ragged tile' walks Nk = 1000 columns in BC = 64 tiles: 15 whole tiles and
     one of 40 columns.  That is the walk the row reductions run on 8192 x 1000, with 16-byte rows
     and with rows off the 16-byte grid (row stride 1001) alike."""
-    assert tm.tm_row_walk(8192, 1000, 1000, 16, 64, 0, LINE) == (tm.TM_OK, 64, 15, 40, 16)
+    # rows of 250 16-byte chunks are read in one batch, 32 lanes of 8 chunks each; the tile
+    # decides which chunks are read unmasked
+    assert tm.tm_row_walk(8192, 1000, 1000, 16, 64, 0, LINE) == (tm.TM_OK, 64, 15, 40, 32)
     st, bc, nf, rem, lanes = tm.tm_row_walk(8192, 1000, 1001, 16, 64, 0, LINE)
     assert (st, bc, nf, rem) == (tm.TM_OK, 64, 15, 40)
     assert (nf, rem) == oracle.split(1000, 64)
     # its aligned counterpart: 16 whole tiles, no remainder
-    assert tm.tm_row_walk(8192, 1024, 1024, 16, 64, 1, LINE) == (tm.TM_OK, 64, 16, 0, 16)
+    assert tm.tm_row_walk(8192, 1024, 1024, 16, 64, 1, LINE) == (tm.TM_OK, 64, 16, 0, 32)
+    # the loop split example of 'Loops over a dynamic extent': K = 1000 in 16-column tiles
+    assert tm.tm_row_walk(8192, 1000, 1000, 16, 16, 0, LINE)[1:4] == (16, 62, 8)
     # the promise is checked as the reductions check it
     assert tm.tm_row_walk(8192, 1000, 1000, 16, 64, 1, LINE)[0] == tm.TM_E_ALIGN
 
 
 def test_row_walk_split_is_the_remainder_rule():
-    """Whatever tile the walk takes, nfull and rem are the remainder split of N by it, the tile is
-    a whole number of chunks per lane, and a caller tile is taken exactly when it keeps at least
-    half the lanes and at most 4 chunks per lane."""
+    """Whatever tile the walk takes, nfull and rem are the remainder split of N by it.  The
+    caller's tile (at least one chunk wide) is the walk's for rows read in one batch (more than
+    half of 16 lanes' and at most 64 lanes' batch of chunks) and, for other rows, whenever it
+    keeps at least half the lanes and at most 4 chunks per lane; otherwise the walk's own tile is
+    a whole number of chunks per lane."""
     for M in (1, 7, 300, 4096):
         for N in (1, 5, 16, 63, 64, 100, 1000, 4096, 70000):
             for ld in (N + (-N) % 4, N + 1 if N % 4 == 0 else N):
@@ -125,6 +131,12 @@ def test_row_walk_split_is_the_remainder_rule():
                     st, bc, nf, rem, lanes = tm.tm_row_walk(M, N, ld, 1, BC, 0, LINE)
                     assert st == tm.TM_OK
                     assert (nf, rem) == oracle.split(N, bc), (M, N, ld, BC)
+                    chunks = -(-N // W)
+                    K = 8 if W == 4 else 16
+                    if 8 * K < chunks <= 64 * K and not (chunks > 32 * K and M < 2048):
+                        # one batch: at least 16 lanes cover the row, and the tile is the caller's
+                        assert lanes >= 16 and lanes * K >= chunks and bc == max(BC, W), (M, N, ld, BC)
+                        continue
                     assert bc % (lanes * W) == 0 and 1 <= bc // (lanes * W) <= 4, (M, N, ld, BC, bc, lanes)
                     if bc == BC:
                         continue
