@@ -23,7 +23,8 @@ OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtilemap.so")
 # The CPython extension that binds the C ABI (csrc/pyext.c), next to the library it links.
 EXT = os.path.join(HERE, "_tilemap" + sysconfig.get_config_var("EXT_SUFFIX"))
-SOURCES = ["plan.cpp", "map.hip", "mapflat.hip", "rowred.hip", "colred.hip", "transpose.hip", "api.hip"]
+SOURCES = ["plan.cpp", "map.hip", "mapflat.hip", "rowred.hip", "colred.hip", "transpose.hip", "api.hip",
+           "noalloc.hip"]
 # Per-source flags.  mapflat.hip: its kernels' arguments are preloaded into scalar registers at
 # wave launch (gfx940-family kernel-argument preloading; the code object keeps the plain argument
 # loads as a prologue for firmware without it), so a short-lived wave starts its load sooner.

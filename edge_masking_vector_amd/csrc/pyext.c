@@ -195,6 +195,18 @@ static PyObject *py_softmax_stats_ws(ARGS) {
                                                BR, BC, al, ws, wsb, s));
 }
 
+static PyObject *py_colsum_noalloc(ARGS) {
+    void *x, *out, *s;
+    int64_t ldx, M, N;
+    int TM, TN, al, walk;
+    (void)self;
+    OK(want(n, 10, "tm_colsum_noalloc"));
+    OK(as_ptr(a[0], &x) && as_i64(a[1], &ldx) && as_ptr(a[2], &out) && as_i64(a[3], &M) &&
+       as_i64(a[4], &N) && as_int(a[5], &TM) && as_int(a[6], &TN) && as_int(a[7], &al) &&
+       as_int(a[8], &walk) && as_ptr(a[9], &s));
+    return PyLong_FromLong(tm_colsum_noalloc((const float *)x, ldx, (float *)out, M, N, TM, TN, al, walk, s));
+}
+
 static PyObject *py_colsum_workspace_bytes(ARGS) {
     int64_t M, N;
     int TM, TN, walk;
@@ -383,6 +395,7 @@ static PyMethodDef methods[] = {
     FAST("tm_check_promise", py_check_promise),
     FAST("tm_split", py_split),
     FAST("tm_plan_tiles", py_plan_tiles),
+    FAST("tm_colsum_noalloc", py_colsum_noalloc),
     FAST("tm_row_walk", py_row_walk),
     FAST("tm_pad_extents", py_pad_extents),
     FAST("tm_autotune_map", py_autotune_map),

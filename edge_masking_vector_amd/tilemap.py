@@ -108,6 +108,15 @@ def tm_colsum(x, ldx, out, M, N, TM, TN, aligned, walk, ws, ws_bytes, stream=Non
                           _stream(stream))
 
 
+TM_COLSUM_NOALLOC_MAX_BYTES = 16 << 20
+
+
+def tm_colsum_noalloc(x, ldx, out, M, N, TM, TN, aligned, walk, stream=None):
+    """tm_colsum with its partials in the library's static device array (no workspace, no
+    allocation); calls overlapping on one device race."""
+    return _ext.tm_colsum_noalloc(_ptr(x), ldx, _ptr(out), M, N, TM, TN, aligned, walk, _stream(stream))
+
+
 def tm_rowmax_masked(s, lds, out, M, N, BR, BC, aligned, stream=None):
     return _ext.tm_rowmax_masked(_ptr(s), lds, _ptr(out), M, N, BR, BC, aligned, _stream(stream))
 

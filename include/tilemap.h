@@ -173,6 +173,22 @@ size_t tm_colsum_workspace_bytes(int64_t M, int64_t N, int TM, int TN, int walk)
 int tm_colsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t N,
               int TM, int TN, int aligned, int walk, void *ws, size_t ws_bytes, void *stream);
 
+/* The most workspace tm_colsum_noalloc can stand in for: 16 MiB per device. */
+#define TM_COLSUM_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+
+/* tm_colsum for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments (no workspace), same kernels,
+ * same results bit for bit as tm_colsum with a workspace.  The slab partials live in a static
+ * device array of TM_COLSUM_NOALLOC_MAX_BYTES that the library holds on every device it runs on
+ * until the process ends; the call allocates nothing (no hipMalloc, no hipFree).  A call whose
+ * tm_colsum_workspace_bytes(...) exceeds the array returns TM_E_WORKSPACE and enqueues nothing
+ * (argument errors as tm_colsum, checked first, before any HIP call).  The first call on a device
+ * looks up the array's device address (HIP calls that enqueue nothing); TM_E_HIP if that fails.
+ * The array is shared by every call on a device and keeps the last call's partials: calls that
+ * overlap on one device race, so issue them on one stream (which orders them) or serialize them. */
+int tm_colsum_noalloc(const float *x, int64_t ldx, float *out, int64_t M, int64_t N, int TM, int TN,
+                      int aligned, int walk, void *stream);
+
 /* out[i] = max over j < N of s[i,j] (out: M floats, contiguous), walking column tiles: whole
  * tiles unmasked, then one remainder tile in which tile-local column c keeps s iff c < N - kt and
  * is otherwise replaced by -1.0e30f (f32 bits 0xF149F2CA); the running maximum starts at that fill,
