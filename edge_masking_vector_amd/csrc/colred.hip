@@ -179,6 +179,86 @@ __global__ __launch_bounds__(kBlock) void col_lds(ColArgs a) {
     }
 }
 
+// ---- strip walk (wide matrices) -------------------------------------------------------------------
+// A workgroup takes (slab, strip): tm rows by tmp::kColRowStrip columns, strip fastest, so the
+// workgroups running together read whole rows.  Thread t owns 16-byte column chunk t of the strip
+// and adds the slab's rows down it, 16 loads in flight into 4 accumulators, folded in a fixed order;
+// its four column sums are the slab's partial for those columns, stored as one 16-byte vector at
+// ws[slab * N + column] (the workspace is 16-byte aligned and N % 4 == 0).  The loads carry no
+// control flow: a row past M re-reads row M - 1 and a chunk past N re-reads the row's last chunk,
+// and both are then replaced by 0 ([SLICING] "Masking": out-of-range elements read as 0).
+// WHOLE: the host found whole slabs and strips, so there is nothing to replace.
+constexpr int kStripBatch = 16;
+
+template <bool WHOLE>
+__global__ __launch_bounds__(kBlock) void col_strip(ColArgs a) {
+    const int t = threadIdx.x;
+    const uint32_t strip = blockIdx.x % a.strips, slab = blockIdx.x / a.strips;
+    const int64_t nch = a.N / 4;                          // 16-byte chunks per row
+    const int64_t ch = int64_t(strip) * kBlock + t;       // this thread's column chunk
+    const int64_t chc = ch < nch ? ch : nch - 1;
+    const int64_t tm = int64_t(1) << a.log_tm;
+    const int64_t row0 = int64_t(slab) * tm;
+    const float *p = a.x + chc * 4;
+    f4 acc[4] = {f4(0.0f), f4(0.0f), f4(0.0f), f4(0.0f)};
+    for (int64_t r0 = 0; r0 < tm; r0 += kStripBatch) {
+        f4 v[kStripBatch];
+#pragma unroll
+        for (int u = 0; u < kStripBatch; ++u) {
+            const int64_t row = row0 + r0 + u;
+            v[u] = ld16_nt(p + (WHOLE || row < a.M ? row : a.M - 1) * a.ld);
+        }
+#pragma unroll
+        for (int u = 0; u < kStripBatch; ++u) {
+            if constexpr (!WHOLE)
+                v[u] = row0 + r0 + u < a.M ? v[u] : f4(0.0f);
+            acc[u % 4] += v[u];
+        }
+    }
+    const f4 s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    if (WHOLE || ch < nch)
+        *reinterpret_cast<f4 *>(a.ws + int64_t(slab) * a.N + ch * 4) = s;
+}
+
+// Pass 2 after the strip walk: workgroup b takes 16-byte column chunks 64 b .. 64 b + 63; wave w of
+// its kFold waves adds slabs [w S / kFold, (w + 1) S / kFold) of its lane's chunk in order, 16
+// coalesced loads in flight (consecutive lanes on consecutive chunks), and the waves' sums meet
+// in LDS in wave order.  Fixed order throughout: the result is deterministic.
+constexpr int kFold = 4;  // waves per workgroup
+
+__global__ __launch_bounds__(kFold * 64) void colsum_fold16(const float *ws, float *out, int64_t N,
+                                                              uint32_t slabs) {
+    __shared__ f4 wsum[kFold][64];
+    const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
+    const int64_t nch = N / 4;
+    const int64_t ch = int64_t(blockIdx.x) * 64 + lane;
+    const int64_t chc = ch < nch ? ch : nch - 1;
+    const uint32_t s_begin = uint32_t(uint64_t(slabs) * w / kFold);
+    const uint32_t s_end = uint32_t(uint64_t(slabs) * (w + 1) / kFold);
+    const f4 *p = reinterpret_cast<const f4 *>(ws) + chc;
+    f4 acc = f4(0.0f);
+    for (uint32_t s0 = s_begin; s0 < s_end; s0 += kStripBatch) {
+        f4 v[kStripBatch];
+#pragma unroll
+        for (int u = 0; u < kStripBatch; ++u) {
+            const uint32_t s = s0 + u < s_end ? s0 + u : s_end - 1;
+            v[u] = p[int64_t(s) * nch];
+        }
+#pragma unroll
+        for (int u = 0; u < kStripBatch; ++u)
+            acc += s0 + u < s_end ? v[u] : f4(0.0f);
+    }
+    wsum[w][lane] = acc;
+    __syncthreads();
+    if (w == 0 && ch < nch) {
+        f4 total = wsum[0][lane];
+#pragma unroll
+        for (int k = 1; k < kFold; ++k)
+            total += wsum[k][lane];
+        *reinterpret_cast<f4 *>(out + ch * 4) = total;
+    }
+}
+
 // ---- direct walk ---------------------------------------------------------------------------------
 // For few rows, or columns enough to fill the GPU by themselves: each thread owns one chunk of W
 // columns and adds all M rows down it -- kRowsInFlight coalesced loads at a time (consecutive
@@ -313,6 +393,33 @@ hipError_t launch_cols(const tmp::ColPlan &p, hipStream_t stream) {
         const void *fn = p.vec ? reinterpret_cast<const void *>(&col_direct<true>)
                                : reinterpret_cast<const void *>(&col_direct<false>);
         return hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, stream);
+    }
+    if (p.strip) {
+        ColArgs a;
+        a.x = p.x;
+        a.ws = p.ws;
+        a.out = p.out;
+        a.out16 = 0;
+        a.ld = p.ld;
+        a.M = p.M;
+        a.N = p.N;
+        a.log_tm = p.log_tm;
+        a.strips = p.strips;
+        a.slabs = p.slabs;
+        void *args[] = {&a};
+        const void *fn = p.whole ? reinterpret_cast<const void *>(&col_strip<true>)
+                                 : reinterpret_cast<const void *>(&col_strip<false>);
+        hipError_t err = hipLaunchKernel(fn, dim3(p.slabs * p.strips), dim3(kBlock), args, 0, stream);
+        if (err != hipSuccess)
+            return err;
+        const float *ws = p.ws;
+        float *out = p.out;
+        int64_t N = p.N;
+        uint32_t slabs = p.slabs;
+        void *fargs[] = {&ws, &out, &N, &slabs};
+        const uint32_t fgrid = static_cast<uint32_t>((p.N / 4 + 63) / 64);
+        return hipLaunchKernel(reinterpret_cast<const void *>(&colsum_fold16), dim3(fgrid), dim3(kFold * 64),
+                               fargs, 0, stream);
     }
     if (p.launch) {
         ColArgs a;

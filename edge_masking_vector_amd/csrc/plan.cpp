@@ -645,6 +645,18 @@ int slab_log(int64_t M, int64_t N, int TM, int walk) {
 
 }  // namespace
 
+// The LDS walk over wide matrices (N >= kColRowStrip, whole 16-byte chunks): rows per slab for
+// the strip kernel, or 0 when the shape takes the LDS-staged kernel instead.
+int strip_slab_log(int64_t M, int64_t N, int walk) {
+    if (walk != TM_COL_LDS || N < kColRowStrip || N % 4 != 0 || M <= 0)
+        return 0;
+    int l = ilog2(kColRowSlab);
+    while (ceil_div(M, int64_t{1} << l) > kColRowMaxSlabs)
+        ++l;
+    const int64_t work = ceil_div(M, int64_t{1} << l) * ceil_div(N, kColRowStrip);
+    return work >= kColRowMinWork ? l : 0;
+}
+
 // Measured against the two-pass walk (1 GiB of rotating inputs): 1 x 2^20 21.8 -> 6.5 us,
 // 4 x 2^22 75.3 -> 18.2, 16 x 2^20 25.9 -> 15.0, 64 x 2^18 16.9 -> 13.1, 16 x 65536 7.3 -> 5.8,
 // 256 x 2^18 45.2 -> 43.1; slower from 128 rows of fewer columns (256 x 65536: 14.5 against 28.1
@@ -662,7 +674,11 @@ size_t colsum_ws_bytes(int64_t M, int64_t N, int TM, int TN, int walk) {
         return 0;
     if (col_direct(M, N, walk))
         return 0;  // one pass, no partials
-    const int64_t slabs = ceil_div(M, int64_t{1} << slab_log(M, N, TM, walk));
+    int64_t slabs = ceil_div(M, int64_t{1} << slab_log(M, N, TM, walk));
+    // A wide matrix takes the strip kernel when its rows and the workspace allow 16-byte chunks,
+    // and the LDS-staged kernel otherwise: room for the larger of the two.
+    if (const int ls = strip_slab_log(M, N, walk))
+        slabs = std::max(slabs, ceil_div(M, int64_t{1} << ls));
     if (slabs > INT64_MAX / 4 / N)
         return 0;
     return static_cast<size_t>(slabs * N * 4);
@@ -716,6 +732,30 @@ int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int 
     plan->walk = walk;
     plan->log_tm = log_ts;
     plan->slabs = static_cast<uint32_t>(slabs);
+    // Wide matrices with 16-byte rows and a 16-byte aligned workspace: the strip kernel.  Each
+    // thread owns one 16-byte column chunk of a kColRowStrip-column strip and adds kColRowSlab
+    // rows down it, 16 loads in flight; each row of a strip is one 4 KiB run of memory, and no
+    // partial has to meet another thread's.  On 4096 x 4096 (1 GiB of rotating inputs) pass 1
+    // took 12.2 us against 13.8 us for the LDS-staged kernel's 128 x 128 tiles, whose 1024
+    // workgroups all issue their loads in one round and then fold through LDS together.
+    const int lstrip = strip_slab_log(M, N, walk);
+    if (lstrip > 0 && rows16(x, M, ld) && aligned_to(ws, 16)) {
+        const int64_t sslabs = ceil_div(M, int64_t{1} << lstrip);
+        plan->strip = true;
+        plan->vec = true;
+        plan->log_tm = lstrip;
+        plan->slabs = static_cast<uint32_t>(sslabs);
+        plan->tw = kColRowStrip;
+        plan->strips = static_cast<uint32_t>(ceil_div(N, kColRowStrip));
+        plan->whole = M % (int64_t{1} << lstrip) == 0 && N % kColRowStrip == 0;
+        plan->x = x;
+        plan->out = out;
+        plan->ws = static_cast<float *>(ws);
+        plan->ld = ld;
+        plan->M = M;
+        plan->N = N;
+        return TM_OK;
+    }
     if (walk == TM_COL_LDS) {
         // Like the slabs, the strips are the walk's own: the caller's tile states the promise.
         plan->vec = rows16(x, M, ld);

@@ -70,6 +70,13 @@ constexpr int kColSlab = 256;
 constexpr int64_t kColMaxSlabs = 4096;
 constexpr int kColStrip = 128;
 constexpr int64_t kColTargetWork = 1024;  // LDS walk: fewer (slab, strip) workgroups shorten the slabs
+// LDS walk over wide matrices: strips of kColRowStrip columns (one 16-byte chunk per thread of a
+// kBlock workgroup) by slabs of kColRowSlab rows (doubled while there would be more than
+// kColRowMaxSlabs), when that makes at least kColRowMinWork workgroups.
+constexpr int kColRowStrip = 1024;
+constexpr int kColRowSlab = 64;
+constexpr int64_t kColRowMaxSlabs = 256;
+constexpr int64_t kColRowMinWork = 256;
 // Column-sum pass 2: lanes per column chosen so that about this many threads run.
 constexpr int kFinishThreads = 16384;
 // The LDS walk goes direct (one thread per 16-byte column chunk down all rows, one pass) for at
@@ -199,6 +206,9 @@ struct ColPlan {
     bool whole = false;           // LDS walk: whole slabs and strips with 16-byte rows (no masks)
     bool direct = false;          // LDS walk over few rows or many columns: one pass, no partials
     bool out16 = false;           // direct walk: out is 16-byte aligned
+    // LDS walk over wide matrices (col_strip + colsum_fold16): a workgroup per (slab, strip of
+    // kColRowStrip columns), each thread one 16-byte column chunk; partials as 16-byte vectors.
+    bool strip = false;
     int fl = 1;                   // pass 2: lanes per column (power of two <= 64)
     int naive_block = 64;         // threads per workgroup (naive walk)
     uint32_t slabs = 0;           // ceil(M / rows per slab): partials per column

@@ -395,8 +395,8 @@ static void check_transposes() {
 
 // ---- row and column reductions ----------------------------------------------------------------
 static void check_reductions() {
-    const int64_t Ms[] = {0, 1, 7, 300, 2047, 1048583};
-    const int64_t Ns[] = {0, 1, 5, 64, 100, 257, 513, 1000, 2048, 2051, 4096, 1048576};
+    const int64_t Ms[] = {0, 1, 7, 300, 2047, 4096, 1048583};
+    const int64_t Ns[] = {0, 1, 5, 64, 100, 257, 513, 1000, 2048, 2051, 4096, 5000, 1048576};
     for (int64_t M : Ms)
         for (int64_t N : Ns)
             for (int TR : {1, 4, 16, 256})
@@ -466,7 +466,33 @@ static void check_reductions() {
                             if (c.direct)
                                 CHECK(!c.launch && wsb == 0 && c.vec == (M <= 1 || ld % 4 == 0) && c.out16,
                                       "cols direct plan M=%ld N=%ld", long(M), long(N));
-                            if (c.launch) {
+                            if (c.strip) {
+                                // strip walk: workgroup (slab, strip), thread t of 256 owns column chunk
+                                // strip * 256 + t; its partial lands at ws[slab * N + 4 * chunk]; every
+                                // (slab, column) partial is written exactly once, rows read stay < M
+                                const int64_t ts = int64_t{1} << c.log_tm, nch = N / 4;
+                                CHECK(walk == TM_COL_LDS && c.vec && N % 4 == 0 && ts >= tmp::kColRowSlab &&
+                                          c.slabs == uint32_t((M + ts - 1) / ts) &&
+                                          uint64_t(c.strips) * tmp::kColRowStrip >= uint64_t(N) &&
+                                          uint64_t(c.slabs) * uint64_t(N) * 4 <= wsb,
+                                      "cols strip plan M=%ld N=%ld", long(M), long(N));
+                                CHECK(!c.whole || (M % ts == 0 && N % tmp::kColRowStrip == 0), "cols strip whole");
+                                std::vector<uint8_t> hit(size_t(c.slabs) * size_t(nch), 0);
+                                for (uint32_t b = 0; b < c.slabs * c.strips; ++b) {
+                                    const uint32_t strip = b % c.strips, slab = b / c.strips;
+                                    for (int t = 0; t < tmp::kBlock; ++t) {
+                                        const int64_t ch = int64_t(strip) * tmp::kBlock + t;
+                                        if (ch < nch)
+                                            ++hit[size_t(slab) * size_t(nch) + size_t(ch)];
+                                    }
+                                }
+                                for (size_t k = 0; k < hit.size(); ++k)
+                                    if (hit[k] != 1) {
+                                        CHECK(false, "cols strip partial %zu written %d times", k, int(hit[k]));
+                                        break;
+                                    }
+                            }
+                            if (c.launch && !c.strip) {
                                 const int64_t ts = int64_t{1} << c.log_tm;
                                 CHECK(c.slabs == uint32_t((M + ts - 1) / ts), "cols slabs");
                                 if (walk == TM_COL_LDS) {

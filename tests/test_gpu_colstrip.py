@@ -1,0 +1,78 @@
+"""GPU parity of the LDS walk's kernel for wide matrices (a workgroup per slab of rows and strip of
+1024 columns, each thread one 16-byte column chunk; then a fold of the slab partials), against the
+fp64 oracle: the column-sum workload, matrices ragged in rows and columns, integer data (every
+partial sum exact, so the result is exact too), and the same call with a workspace off the
+16-byte grid, which takes the LDS-staged kernel instead and must agree within the bound.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from edge_masking_vector_amd import inputs
+from gpu_helpers import Guarded, bits, sum_tol
+
+pytestmark = pytest.mark.gpu
+
+tm = pytest.importorskip("edge_masking_vector_amd.tilemap")
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _colsum(dev, xh, M, N, ld, TM, TN, aligned, ws_offset=0):
+    x = torch.from_numpy(xh).to(dev)
+    wsb = tm.tm_colsum_workspace_bytes(M, N, TM, TN, tm.TM_COL_LDS)
+    ws = torch.empty(wsb // 4 + 8, device=dev)
+    out = Guarded(N, dev)
+    st = tm.tm_colsum(x, ld, out.ptr, M, N, TM, TN, aligned, tm.TM_COL_LDS, ws.data_ptr() + 4 * ws_offset,
+                      wsb, torch.cuda.current_stream())
+    assert st == tm.TM_OK, tm.tm_status_string(st)
+    torch.cuda.synchronize()
+    assert out.guards_intact()
+    return out.payload().cpu().numpy()
+
+
+@pytest.mark.parametrize("M,N,ld,TM,TN,aligned", [
+    (4096, 4096, 4096, 256, 64, 1),     # the column-sum workload
+    (7000, 3000, 3000, 1, 4, 0),        # ragged rows (7000 = 109 slabs of 64 + 24) and strips (2 x 1024 + 952)
+    (16384, 1024, 1028, 64, 256, 0),    # padded rows, one strip
+    (2048, 8192, 8192, 64, 1024, 1),    # short and wide
+])
+def test_strip_walk_against_oracle(dev, M, N, ld, TM, TN, aligned):
+    note("strip colsum %dx%d ld %d" % (M, N, ld))
+    xh = inputs.matrix(inputs.uniform(M + N, M * N, 0.0, 1.0), M, N, ld)
+    got = _colsum(dev, xh, M, N, ld, TM, TN, aligned)
+    want = oracle.colsum_f64(xh, ld, M, N)
+    assert np.all(np.abs(got.astype(np.float64) - want) <= sum_tol(want))
+    # the same call with the workspace 4 bytes off the 16-byte grid runs the LDS-staged kernel
+    other = _colsum(dev, xh, M, N, ld, TM, TN, aligned, ws_offset=1)
+    assert np.all(np.abs(other.astype(np.float64) - want) <= sum_tol(want))
+
+
+def test_strip_walk_exact_on_integers(dev):
+    """Integers 0..15: every partial sum is an exact f32 integer, so the sums are bit-exact."""
+    M, N = 7000, 3000
+    xh = inputs.integers(5, M * N, 0, 16).astype(np.float32)
+    got = _colsum(dev, xh, M, N, N, 1, 4, 0)
+    want = oracle.colsum_f64(xh, N, M, N)
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_strip_workspace_query_covers_both_kernels(dev):
+    """The size query does not know the workspace's alignment: it covers the strip kernel's slabs
+    and the LDS-staged kernel's, whichever is more."""
+    for M, N in ((4096, 4096), (7000, 3000), (16384, 1024)):
+        wsb = tm.tm_colsum_workspace_bytes(M, N, 1, 4, tm.TM_COL_LDS)
+        assert wsb >= -(-M // 64) * N * 4 or wsb >= 256 * N * 4
