@@ -858,9 +858,19 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     // (1 GiB of rotating buffers, outputs compared bit for bit): 4099 x 4099 66.5 -> 56.0 us,
     // 9163 x 1051 43.5 -> 31.8, 2951 x 2697 36.8 -> 32.2, 17827 x 767 64.0 -> 59.3; small
     // matrices (1001 x 1001: 5.0 against 5.4 us) keep 32 x 32.
-    if (!vx && !vy && !aligned && M >= 2 * kTrSub && N >= kTrSub && M * N >= (int64_t{1} << 22)) {
+    //
+    // Rows of y off the 16-byte grid (4-byte stores; every y-row piece shares its end lines with
+    // the neighbouring sub-tiles') do better still with 64 x 32 sub-tiles, staged in a 2048-element
+    // instance: y-row pieces of 256 bytes, x-row pieces of 128.  Against 32 x 32 / 64 x 16, in the
+    // kernel itself over 1 GiB of rotating buffers: 5450 x 2568 (y stride 5450) 63.2 / 51.8 ->
+    // 47.9 us, 57348 x 252 (y stride 57349) 58.6 / 47.8 -> 45.3 us, 1707 x 7425 (strides 7428,
+    // 1707) 48.7 / 43.7 -> 38.5 us, 4099 x 4099 with both sides off 65.4 / 55.2 -> 51.2 us;
+    // 128 x 16, 128 x 32, 64 x 64 and 256 x 16 were slower than 64 x 32 on at least three of the
+    // four.
+    if (!vy && !aligned && M >= 2 * kTrSub && N >= kTrSub && M * N >= (int64_t{1} << 22)) {
         plan->sm = 2 * kTrSub;
-        plan->sn = kTrSub / 2;
+        plan->sn = kTrSub;
+        plan->sub = 2 * kTrSubElems;
     }
     plan->vx = vx;
     plan->vy = vy;

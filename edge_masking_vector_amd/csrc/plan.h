@@ -232,7 +232,8 @@ struct TransposePlan {
     bool vec = false;             // 16-byte chunks on both sides (vx && vy)
     bool vx = false, vy = false;  // 16-byte chunks on the read side (x rows) / the write side (y rows)
     int aligned = 0;
-    int sm = 1, sn = 1;           // staged sub-tile extents (powers of two, sm * sn <= kTrSubElems)
+    int sm = 1, sn = 1;           // staged sub-tile extents (powers of two, sm * sn <= sub)
+    int sub = kTrSubElems;        // the kernel instance's largest sub-tile: kTrSubElems or twice that
     int log_g = 0;                // batches per work item: 2^log_g (whole matrices in one sub-tile)
     // Few channels with a packed side (transpose_packed): 1 = y rows of exactly M < kTrSub floats
     // (NCHW -> NHWC), 2 = x rows of exactly N < kTrSub floats (NHWC -> NCHW); 0 = neither.

@@ -33,8 +33,8 @@ namespace tmk {
 namespace {
 
 constexpr int kSubElems = tmp::kTrSubElems;  // largest sub-tile (elements)
-// LDS of the staged sub-tile: SM rows of stride SN + 1 floats, SM * SN <= kSubElems, so at most
-// 2 * kSubElems floats (SN = 1: 1024 rows of stride 2).
+// LDS of a staged sub-tile: SM rows of stride SN + 1 floats, SM * SN <= SUB (the instance's
+// largest sub-tile), so at most 2 * SUB floats (SN = 1: SUB rows of stride 2).
 constexpr int kStage = 2 * kSubElems;
 constexpr int kTrBlock = 256;       // threads per workgroup (one 16-byte chunk each per sub-tile)
 
@@ -60,14 +60,15 @@ static_assert(sizeof(TrArgs) <= 128, "transpose arguments outgrew one scalar loa
 // VX / VY: x's rows (the reads) / y's rows (the writes) move in 16-byte chunks, each side as its
 // own rows allow (a 9163 x 1051 transpose with 16-byte x rows and 4-byte y rows took 42 us with
 // 4-byte chunks on both sides).
-template <bool VX, bool VY, bool ALIGNED, int BS, bool WIDE, bool PACK>
+// SUB: the largest sub-tile (elements) the instance stages.
+template <bool VX, bool VY, bool ALIGNED, int BS, bool WIDE, bool PACK, int SUB = kSubElems>
 __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
     static_assert(!ALIGNED || (VX && VY), "the promise implies 16-byte rows on both sides");
     constexpr int LOG_WX = VX ? 2 : 0, LOG_WY = VY ? 2 : 0;
     constexpr int WX = 1 << LOG_WX, WY = 1 << LOG_WY;
-    constexpr int KX = kSubElems / WX / BS;   // read chunks per thread for a full sub-tile
-    constexpr int KY = kSubElems / WY / BS;   // write chunks per thread
-    __shared__ float tile[kStage];
+    constexpr int KX = SUB / WX / BS;   // read chunks per thread for a full sub-tile
+    constexpr int KY = SUB / WY / BS;   // write chunks per thread
+    __shared__ float tile[2 * SUB];
     const int t = threadIdx.x;
     // Sub-tile extents are powers of two of at least the chunk width: chunk coordinates are shifts
     // and masks (run-time divisions per chunk took the 4096 x 4096 transpose from 25.5 to 27.5 us).
@@ -395,6 +396,9 @@ hipError_t launch_packed(const tmp::TransposePlan &p, hipStream_t stream) {
 
 template <bool WIDE, bool PACK>
 const void *pick(const tmp::TransposePlan &p) {
+    if (!PACK && !p.vy && p.sub == 2 * kSubElems)  // y rows off the 16-byte grid: 64 x 32 sub-tiles
+        return p.vx ? reinterpret_cast<const void *>(&transpose_tiles<true, false, false, kTrBlock, WIDE, false, 2 * kSubElems>)
+                    : reinterpret_cast<const void *>(&transpose_tiles<false, false, false, kTrBlock, WIDE, false, 2 * kSubElems>);
     if (p.vx && p.vy)
         return p.aligned ? reinterpret_cast<const void *>(&transpose_tiles<true, true, true, kTrBlock, WIDE, PACK>)
                          : reinterpret_cast<const void *>(&transpose_tiles<true, true, false, kTrBlock, WIDE, PACK>);

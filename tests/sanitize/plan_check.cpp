@@ -240,10 +240,15 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
           "%s sub-tile counts", tag);
     CHECK((p.log_g > 0 || p.nwork == uint64_t(B) * p.subs_m * p.subs_n) && p.grid >= 1 && p.grid <= p.nwork,
           "%s work", tag);
-    CHECK((p.sm & (p.sm - 1)) == 0 && (p.sn & (p.sn - 1)) == 0 && int64_t(p.sm) * p.sn <= tmp::kTrSubElems,
-          "%s sub-tile %dx%d above %d elements", tag, p.sm, p.sn, tmp::kTrSubElems);
-    // the staged sub-tile (rows of stride SN + 1 floats) fits the kernel's LDS of 2 * kTrSubElems
-    CHECK(int64_t(p.sm) * (p.sn + 1) <= 2 * tmp::kTrSubElems, "%s staged sub-tile exceeds LDS", tag);
+    // the instance's capacity: kTrSubElems, or twice that for the 64 x 32 sub-tiles of views whose
+    // y rows are off the 16-byte grid
+    CHECK(p.sub == tmp::kTrSubElems || (p.sub == 2 * tmp::kTrSubElems && !p.vy && p.log_g == 0 && p.packed == 0 &&
+                                        p.sm == 2 * tmp::kTrSub && p.sn == tmp::kTrSub),
+          "%s instance of %d elements", tag, p.sub);
+    CHECK((p.sm & (p.sm - 1)) == 0 && (p.sn & (p.sn - 1)) == 0 && int64_t(p.sm) * p.sn <= p.sub,
+          "%s sub-tile %dx%d above %d elements", tag, p.sm, p.sn, p.sub);
+    // the staged sub-tile (rows of stride SN + 1 floats) fits the instance's LDS of 2 * sub floats
+    CHECK(int64_t(p.sm) * (p.sn + 1) <= 2 * p.sub, "%s staged sub-tile exceeds LDS", tag);
     // a narrow extent gets a narrow sub-tile (no sub-tile row or column is wholly outside the view,
     // beyond the minimum of 4 that 16-byte chunks need)
     auto p2 = [](int64_t v) { int64_t e = 1; while (e < v) e <<= 1; return e; };
@@ -251,9 +256,9 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
         CHECK(p.sm <= std::max<int64_t>(p.vy ? 4 : 1, p2(M)) && p.sn <= std::max<int64_t>(p.vx ? 4 : 1, p2(N)),
               "%s sub-tile %dx%d wider than the view", tag, p.sm, p.sn);
         if (M >= tmp::kTrSub && N >= tmp::kTrSub) {
-            // 32 x 32, or 64 x 16 for large views with no 16-byte rows on either side
-            const bool tall = !p.vx && !p.vy && M >= 2 * tmp::kTrSub && M * N >= (int64_t{1} << 22);
-            CHECK(tall ? (p.sm == 2 * tmp::kTrSub && p.sn == tmp::kTrSub / 2)
+            // 32 x 32, or 64 x 32 for large views whose y rows are off the 16-byte grid
+            const bool tall = !p.vy && M >= 2 * tmp::kTrSub && M * N >= (int64_t{1} << 22);
+            CHECK(tall ? (p.sm == 2 * tmp::kTrSub && p.sn == tmp::kTrSub && p.sub == 2 * tmp::kTrSubElems)
                        : (p.sm == tmp::kTrSub && p.sn == tmp::kTrSub),
                   "%s wide view on %dx%d sub-tiles", tag, p.sm, p.sn);
         }
@@ -372,7 +377,7 @@ static void check_transposes() {
                         replay_transpose(p, B, M, N, tag);
                     }
     CHECK(packed_plans > 0, "no packed-side transpose planned");
-    // odd strides on both sides (no 16-byte rows): large views take 64 x 16 sub-tiles
+    // odd strides on both sides (no 16-byte rows): large views take 64 x 32 sub-tiles
     for (int64_t M : {int64_t{64}, int64_t{4099}, int64_t{9163}})
         for (int64_t N : {int64_t{33}, int64_t{1051}, int64_t{4099}}) {
             tmp::TransposePlan p;

@@ -203,3 +203,17 @@ def test_transpose_empty(dev):
         assert tm.tm_transpose(0, 4, 16, Y.ptr, 4, 16, B, M, N, 4, 4, 0) == tm.TM_OK
     torch.cuda.synchronize()
     assert np.array_equal(bits(Y.buf), before)
+
+
+@pytest.mark.parametrize("M,N,ldx,ldy,xoff,yoff", [
+    (5450, 2568, 2568, 5450, 0, 0),     # y rows off the 16-byte grid (y stride 5450)
+    (57348, 252, 252, 57349, 0, 0),     # y stride 57349
+    (1707, 7425, 7428, 1707, 0, 0),     # both strides padded, y off the grid
+    (4099, 4099, 4099, 4099, 1, 1),     # neither side on the grid, bases 4 bytes off
+    (2051, 1030, 1031, 2053, 0, 3),     # ragged sub-tiles at both edges
+])
+def test_transpose_y_rows_off_the_grid(dev, M, N, ldx, ldy, xoff, yoff):
+    """Large views whose y rows are not 16-byte aligned take 64 x 32 sub-tiles staged in a
+    2048-element instance: bit for bit, padding and guard bands untouched, ragged edges masked."""
+    note("transpose off-grid %dx%d ldx %d ldy %d" % (M, N, ldx, ldy))
+    check_transpose(dev, 1, M, N, ldx, ldy, 0, 0, 1, 1, 0, xoff=xoff, yoff=yoff, seed=M + N)
