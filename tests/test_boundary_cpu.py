@@ -303,9 +303,10 @@ def test_reduction_errors():
 @no_gpu
 def test_colsum_workspace_and_errors():
     W = tm.tm_colsum_workspace_bytes
-    # LDS walk: 256-row slabs, halved while there would be fewer than 1024 (slab, strip)
-    # workgroups (32 strips of 128 columns here: 128-row slabs)
-    assert W(4096, 4096, 256, 64, tm.TM_COL_LDS) == 32 * 4096 * 4
+    # LDS walk over a wide matrix: room for the strip kernel's 64-row slabs (64 of them here) and
+    # for the LDS-staged kernel's (256-row slabs, halved while there would be fewer than 1024
+    # (slab, strip) workgroups: 32 slabs of 128 rows), whichever is more
+    assert W(4096, 4096, 256, 64, tm.TM_COL_LDS) == 64 * 4096 * 4
     assert W(4096, 4096, 256, 1, tm.TM_COL_NAIVE) == 16 * 4096 * 4
     assert W(4096, 4096, 256, 1, tm.TM_COL_NAIVE_XCD) == 16 * 4096 * 4
     assert W(4096, 4096, 256, 1, 3) == 0
@@ -323,7 +324,7 @@ def test_colsum_workspace_and_errors():
     assert W(65, 1000, 64, 64, tm.TM_COL_LDS) == 3 * 1000 * 4
     assert W(256, 1 << 18, 64, 64, tm.TM_COL_LDS) == 0
     assert W(256, (1 << 18) - 1, 64, 64, tm.TM_COL_LDS) == ((1 << 18) - 1) * 4
-    assert W(257, 1 << 18, 64, 64, tm.TM_COL_LDS) == 2 * (1 << 18) * 4
+    assert W(257, 1 << 18, 64, 64, tm.TM_COL_LDS) == 5 * (1 << 18) * 4   # strip kernel: 64-row slabs
     assert W(0, 1000, 64, 64, tm.TM_COL_LDS) == 0
     assert W(100, 0, 64, 64, tm.TM_COL_LDS) == 0
     assert W(100, 100, 3, 64, tm.TM_COL_LDS) == 0
