@@ -560,11 +560,17 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
     // 16-byte chunks whatever N is: whole tiles hold whole chunks, and the remainder tile masks
     // the chunk that straddles N element by element.
     const bool vec = rows16(x, M, ld);
-    const RowWalk rw = row_walk(M, N, vec, TC);
+    // Long rows off the 16-byte grid are read in 16-byte chunks all the same: each from the 16-byte
+    // boundary at or before its start (within the same aligned 16 bytes, so never past a page the
+    // row does not touch), its first one to three elements masked, the walk laid out for N + 3
+    // elements.  133 x 64954 at row stride 64986 read as 4-byte chunks streamed 2.8 TB/s.
+    const bool shift = !vec && N > kRowShiftMinN;
+    const RowWalk rw = shift ? row_walk(M, N + 3, true, TC) : row_walk(M, N, vec, TC);
     const int lpr = rw.lpr;
     plan->launch = true;
     plan->op = op;
     plan->vec = vec;
+    plan->shift = shift;
     plan->lpr = lpr;
     plan->block = lpr > 64 ? lpr : kBlock;
     plan->per_tile = rw.per_tile;
@@ -604,7 +610,8 @@ int row_walk_query(int64_t M, int64_t N, int64_t ld, int TR, int TC, int aligned
         return st;
     if (aligned && !promise_holds(M, N, ld, 0, TR, TC, x, nullptr))
         return TM_E_ALIGN;
-    const RowWalk rw = row_walk(M, N, rows16(x, M, ld), TC);
+    const bool vec = rows16(x, M, ld);
+    const RowWalk rw = !vec && N > kRowShiftMinN ? row_walk(M, N + 3, true, TC) : row_walk(M, N, vec, TC);
     *lanes = rw.lpr;
     *bc = rw.bc;
     return split(N, *bc, nfull, rem);
@@ -867,10 +874,19 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     // 1707) 48.7 / 43.7 -> 38.5 us, 4099 x 4099 with both sides off 65.4 / 55.2 -> 51.2 us;
     // 128 x 16, 128 x 32, 64 x 64 and 256 x 16 were slower than 64 x 32 on at least three of the
     // four.
-    if (!vy && !aligned && M >= 2 * kTrSub && N >= kTrSub && M * N >= (int64_t{1} << 22)) {
+    //
+    // When y's rows are off the 128-byte line grid (16-byte rows or not), the lines at the ends of
+    // each y-row piece are shared with the sub-tiles above and below, and a line written in parts
+    // by two XCDs reaches HBM as partial writes (read-modify-write in the controller: 4096 x 4096
+    // with y stride 4100 took 55.7 against 24.4 us with stride 4096).  One matrix then takes the
+    // 64 x 32 sub-tiles in vertical pairs on one XCD (transpose.hip, PAIRS).
+    const bool y_lines = aligned_to(y, kLineBytes) && (N <= 1 || ldy % (kLineBytes / 4) == 0);
+    const bool large = !aligned && M >= 2 * kTrSub && N >= kTrSub && M * N >= (int64_t{1} << 22);
+    if (large && (!vy || (B == 1 && !y_lines))) {
         plan->sm = 2 * kTrSub;
         plan->sn = kTrSub;
         plan->sub = 2 * kTrSubElems;
+        plan->pairs = B == 1 && !y_lines;
     }
     plan->vx = vx;
     plan->vy = vy;
@@ -909,9 +925,21 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
         if (plan->packed != 0 && ((!plan->pvec && !plan->flat16) || plan->nwork > UINT32_MAX))
             plan->packed = 0;  // nothing to gain, or work ids beyond 32 bits
     }
+    if (plan->pairs) {
+        // work items: 16 per 8 pairs (pair p -> items 16 (p / 8) + p mod 8 and that + 8)
+        const int64_t pair_rows = ceil_div(subs_m, 2);
+        const int64_t items = ceil_div(pair_rows * subs_n, 8) * 16;
+        if (items <= UINT32_MAX && plan->packed == 0 && plan->log_g == 0) {
+            plan->nwork = static_cast<uint64_t>(items);
+            plan->per_b = make_div32(static_cast<uint32_t>(pair_rows));
+        } else {
+            plan->pairs = false;
+        }
+    }
     plan->wide = plan->nwork > UINT32_MAX;
-    if (!plan->wide) {
+    if (!plan->wide && !plan->pairs)
         plan->per_b = make_div32(static_cast<uint32_t>(subs_m * subs_n));
+    if (!plan->wide) {
         plan->by_m = make_div32(plan->subs_m);
         plan->by_n = make_div32(plan->subs_n);
     }

@@ -52,6 +52,9 @@ constexpr int64_t kRowTileMaxChunks = 4;
 constexpr int kRowOnceK = 8;
 constexpr int kRowOnceKScalar = 16;
 constexpr int kRowOnceMinLanes = 16;
+// Rows off the 16-byte grid of more than this many elements are read as 16-byte chunks from the
+// 16-byte boundary at or before each row's start.
+constexpr int64_t kRowShiftMinN = 2048;
 // Rows of one lane each run on at most this many workgroups, each looping over several row groups.
 constexpr int64_t kRowTinyGrid = 4096;
 // Split rows (the row calls that take a workspace): fewer than kRowSplitRows rows of at least
@@ -164,6 +167,10 @@ struct RowPlan {
     // chunks per lane at a stride of lpr chunks; chunks below nfull * bc / W are whole tiles.
     bool once = false;
     int once_k = 0;
+    // Long rows off the 16-byte grid: each row is read in 16-byte chunks from the 16-byte boundary
+    // at or before its start, with the elements before the row masked; bc, per_tile and lpr are
+    // those of 16-byte chunks, and each row's split is that of N + (its start's offset) elements.
+    bool shift = false;
     uint32_t grid = 0;
     const float *x = nullptr;
     float *out = nullptr;         // sums / maxima (softmax statistics: m)
@@ -234,6 +241,8 @@ struct TransposePlan {
     int aligned = 0;
     int sm = 1, sn = 1;           // staged sub-tile extents (powers of two, sm * sn <= sub)
     int sub = kTrSubElems;        // the kernel instance's largest sub-tile: kTrSubElems or twice that
+    bool pairs = false;           // vertical pairs of sub-tiles on one XCD (one matrix, y rows off the
+                                  // 128-byte line grid): per_b is then the divisor ceil(subs_m / 2)
     int log_g = 0;                // batches per work item: 2^log_g (whole matrices in one sub-tile)
     // Few channels with a packed side (transpose_packed): 1 = y rows of exactly M < kTrSub floats
     // (NCHW -> NHWC), 2 = x rows of exactly N < kTrSub floats (NHWC -> NCHW); 0 = neither.

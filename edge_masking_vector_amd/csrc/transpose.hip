@@ -61,8 +61,18 @@ static_assert(sizeof(TrArgs) <= 128, "transpose arguments outgrew one scalar loa
 // own rows allow (a 9163 x 1051 transpose with 16-byte x rows and 4-byte y rows took 42 us with
 // 4-byte chunks on both sides).
 // SUB: the largest sub-tile (elements) the instance stages.
-template <bool VX, bool VY, bool ALIGNED, int BS, bool WIDE, bool PACK, int SUB = kSubElems>
+// PAIRS (one matrix, y rows off the 128-byte line grid): the sub-tiles above and below each other
+// share the lines at the ends of their y-row pieces.  A line that two workgroups write in parts
+// reaches memory as two partial writes unless both parts meet in one L2 first, and HBM3E has no
+// write mask: a partial write costs the controller a read-modify-write (written bytes rise only
+// 11-13%, but 4096 x 4096 with y stride 4100 took 55.7 against 24.4 us).  So sub-tiles go in
+// vertical pairs (pm even, pm + 1) to workgroups b and b + 8, which the dispatcher sends to the
+// same XCD at about the same time: work item w is pair 8 (w / 16) + (w mod 8), half (w mod 16) / 8,
+// pairs numbered pm / 2 fastest (per_b / c_pb hold the pair rows, ceil(subs_m / 2)).  Work items
+// past the last pair do nothing.
+template <bool VX, bool VY, bool ALIGNED, int BS, bool WIDE, bool PACK, int SUB = kSubElems, bool PAIRS = false>
 __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
+    static_assert(!PAIRS || (!WIDE && !PACK), "pair order is for one matrix of 32-bit work counts");
     static_assert(!ALIGNED || (VX && VY), "the promise implies 16-byte rows on both sides");
     constexpr int LOG_WX = VX ? 2 : 0, LOG_WY = VY ? 2 : 0;
     constexpr int WX = 1 << LOG_WX, WY = 1 << LOG_WY;
@@ -89,7 +99,16 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
         // order they would all write y at one column offset, rows SN * ldy apart, and crowd the
         // same HBM channels).  For each pm, q runs over every sub-tile column once.
         uint64_t b, pm, pn;
-        if constexpr (!WIDE) {  // the work count fits 32 bits: multiply-high divisions
+        bool skip = false;
+        if constexpr (PAIRS) {
+            const uint32_t w32 = static_cast<uint32_t>(w);
+            const uint32_t pair = (w32 >> 4) * 8 + (w32 & 7u), half = (w32 >> 3) & 1u;
+            const uint32_t q = fast_div(pair, a.c_pb, a.per_b);  // per_b: pair rows
+            b = 0;
+            pm = 2 * (pair - q * a.per_b) + half;
+            pn = q;
+            skip = pm >= a.subs_m || pn >= a.subs_n;
+        } else if constexpr (!WIDE) {  // the work count fits 32 bits: multiply-high divisions
             const uint32_t w32 = static_cast<uint32_t>(w);
             const uint32_t b32 = fast_div(w32, a.c_pb, a.per_b);
             const uint32_t rest = w32 - b32 * a.per_b;
@@ -105,9 +124,10 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
             pm = rest % a.subs_m;
             pn = (rest / a.subs_m + pm) % a.subs_n;
         }
+        // (a skipped pair-order item still takes part in the barriers below: uniform, no loads)
         const int64_t row0 = int64_t(pm) * sm;     // x rows = y columns
         const int64_t col0 = int64_t(pn) * sn;     // x columns = y rows
-        const int64_t rows_live = a.M - row0, cols_live = a.N - col0;
+        const int64_t rows_live = skip ? 0 : a.M - row0, cols_live = skip ? 0 : a.N - col0;
         // Chunk e of the work item belongs to batch b0 + (e >> lt) (PACK; else b) and is chunk
         // e & (2^lt - 1) of that batch's sub-tile (lt: ltx for reads, lty for writes).
         const int64_t b0 = PACK ? int64_t(b) << a.log_g : int64_t(b);
@@ -396,6 +416,16 @@ hipError_t launch_packed(const tmp::TransposePlan &p, hipStream_t stream) {
 
 template <bool WIDE, bool PACK>
 const void *pick(const tmp::TransposePlan &p) {
+    if constexpr (!PACK && !WIDE) {
+        if (p.pairs) {  // y rows off the line grid, one matrix: 64 x 32 sub-tiles in vertical pairs
+            constexpr int S2 = 2 * kSubElems;
+            if (p.vx)
+                return p.vy ? reinterpret_cast<const void *>(&transpose_tiles<true, true, false, kTrBlock, false, false, S2, true>)
+                            : reinterpret_cast<const void *>(&transpose_tiles<true, false, false, kTrBlock, false, false, S2, true>);
+            return p.vy ? reinterpret_cast<const void *>(&transpose_tiles<false, true, false, kTrBlock, false, false, S2, true>)
+                        : reinterpret_cast<const void *>(&transpose_tiles<false, false, false, kTrBlock, false, false, S2, true>);
+        }
+    }
     if (!PACK && !p.vy && p.sub == 2 * kSubElems)  // y rows off the 16-byte grid: 64 x 32 sub-tiles
         return p.vx ? reinterpret_cast<const void *>(&transpose_tiles<true, false, false, kTrBlock, WIDE, false, 2 * kSubElems>)
                     : reinterpret_cast<const void *>(&transpose_tiles<false, false, false, kTrBlock, WIDE, false, 2 * kSubElems>);

@@ -238,13 +238,40 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
     CHECK(!p.wide, "%s small job planned as wide", tag);
     CHECK(p.subs_m == uint32_t((M + p.sm - 1) / p.sm) && p.subs_n == uint32_t((N + p.sn - 1) / p.sn),
           "%s sub-tile counts", tag);
-    CHECK((p.log_g > 0 || p.nwork == uint64_t(B) * p.subs_m * p.subs_n) && p.grid >= 1 && p.grid <= p.nwork,
+    CHECK((p.log_g > 0 || p.pairs || p.nwork == uint64_t(B) * p.subs_m * p.subs_n) && p.grid >= 1 &&
+              p.grid <= p.nwork,
           "%s work", tag);
     // the instance's capacity: kTrSubElems, or twice that for the 64 x 32 sub-tiles of views whose
-    // y rows are off the 16-byte grid
-    CHECK(p.sub == tmp::kTrSubElems || (p.sub == 2 * tmp::kTrSubElems && !p.vy && p.log_g == 0 && p.packed == 0 &&
-                                        p.sm == 2 * tmp::kTrSub && p.sn == tmp::kTrSub),
+    // y rows are off the 16-byte grid (or, in pair order, off the 128-byte line grid)
+    CHECK(p.sub == tmp::kTrSubElems || (p.sub == 2 * tmp::kTrSubElems && (!p.vy || p.pairs) && p.log_g == 0 &&
+                                        p.packed == 0 && p.sm == 2 * tmp::kTrSub && p.sn == tmp::kTrSub),
           "%s instance of %d elements", tag, p.sub);
+    if (p.pairs) {
+        // pair order: item w -> pair 8 (w / 16) + w mod 8, half (w / 8) mod 2; pm = 2 (pair mod
+        // pair_rows) + half, pn = pair / pair_rows; items past the grid of sub-tiles do nothing;
+        // every sub-tile is visited exactly once, and the grid keeps items w, w + 8 on one XCD
+        CHECK(B == 1 && !p.wide && p.log_g == 0 && p.packed == 0 && p.nwork % 16 == 0 && p.grid % 16 == 0,
+              "%s pair plan", tag);
+        const uint32_t pair_rows = (p.subs_m + 1) / 2;
+        CHECK(p.per_b.d == pair_rows, "%s pair divisor", tag);
+        std::vector<uint8_t> seen(size_t(p.subs_m) * p.subs_n, 0);
+        for (uint64_t w = 0; w < p.nwork; ++w) {
+            const uint32_t w32 = uint32_t(w);
+            const uint32_t pair = (w32 >> 4) * 8 + (w32 & 7u), half = (w32 >> 3) & 1u;
+            const uint32_t q = umulhi_div(pair, p.per_b);
+            const uint32_t pm = 2 * (pair - q * p.per_b.d) + half, pn = q;
+            CHECK(q == pair / pair_rows, "%s pair division", tag);
+            if (pm < p.subs_m && pn < p.subs_n)
+                ++seen[size_t(pn) * p.subs_m + pm];
+        }
+        for (size_t k = 0; k < seen.size(); ++k)
+            if (seen[k] != 1) {
+                CHECK(false, "%s pair-order sub-tile %zu visited %d times", tag, k, int(seen[k]));
+                break;
+            }
+        ++g_checked;
+        return;
+    }
     CHECK((p.sm & (p.sm - 1)) == 0 && (p.sn & (p.sn - 1)) == 0 && int64_t(p.sm) * p.sn <= p.sub,
           "%s sub-tile %dx%d above %d elements", tag, p.sm, p.sn, p.sub);
     // the staged sub-tile (rows of stride SN + 1 floats) fits the instance's LDS of 2 * sub floats
@@ -256,8 +283,9 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
         CHECK(p.sm <= std::max<int64_t>(p.vy ? 4 : 1, p2(M)) && p.sn <= std::max<int64_t>(p.vx ? 4 : 1, p2(N)),
               "%s sub-tile %dx%d wider than the view", tag, p.sm, p.sn);
         if (M >= tmp::kTrSub && N >= tmp::kTrSub) {
-            // 32 x 32, or 64 x 32 for large views whose y rows are off the 16-byte grid
-            const bool tall = !p.vy && M >= 2 * tmp::kTrSub && M * N >= (int64_t{1} << 22);
+            // 32 x 32, or 64 x 32 for large views whose y rows are off the 16-byte grid (or, one
+            // matrix, off the line grid)
+            const bool tall = (!p.vy || p.pairs) && M >= 2 * tmp::kTrSub && M * N >= (int64_t{1} << 22);
             CHECK(tall ? (p.sm == 2 * tmp::kTrSub && p.sn == tmp::kTrSub && p.sub == 2 * tmp::kTrSubElems)
                        : (p.sm == tmp::kTrSub && p.sn == tmp::kTrSub),
                   "%s wide view on %dx%d sub-tiles", tag, p.sm, p.sn);
@@ -444,7 +472,8 @@ static void check_reductions() {
                                         break;
                                     }
                             } else {
-                                CHECK(p.bc == p.lpr * (p.vec ? 4 : 1) * p.per_tile, "rows bc %d", p.bc);
+                                CHECK(p.bc == p.lpr * (p.vec || p.shift ? 4 : 1) * p.per_tile, "rows bc %d", p.bc);
+                                CHECK(!p.shift || (!p.vec && N > tmp::kRowShiftMinN), "rows shift N=%ld", long(N));
                                 CHECK(p.per_tile >= 1 && p.per_tile <= 4, "rows per_tile %d", p.per_tile);
                             }
                             CHECK(p.nfull * p.bc + p.rem == N && p.rem >= 0 && p.rem < p.bc,

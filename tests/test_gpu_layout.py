@@ -211,9 +211,19 @@ def test_transpose_empty(dev):
     (1707, 7425, 7428, 1707, 0, 0),     # both strides padded, y off the grid
     (4099, 4099, 4099, 4099, 1, 1),     # neither side on the grid, bases 4 bytes off
     (2051, 1030, 1031, 2053, 0, 3),     # ragged sub-tiles at both edges
+    (4096, 4096, 4096, 4100, 0, 0),     # 16-byte y rows off the 128-byte line grid
+    (4103, 2049, 2052, 4108, 4, 0),     # the same with ragged edges (an odd number of sub-tile rows)
 ])
 def test_transpose_y_rows_off_the_grid(dev, M, N, ldx, ldy, xoff, yoff):
     """Large views whose y rows are not 16-byte aligned take 64 x 32 sub-tiles staged in a
-    2048-element instance: bit for bit, padding and guard bands untouched, ragged edges masked."""
+    2048-element instance, and one matrix whose y rows miss the 128-byte line grid takes them in
+    vertical pairs: bit for bit, padding and guard bands untouched, ragged edges masked."""
     note("transpose off-grid %dx%d ldx %d ldy %d" % (M, N, ldx, ldy))
     check_transpose(dev, 1, M, N, ldx, ldy, 0, 0, 1, 1, 0, xoff=xoff, yoff=yoff, seed=M + N)
+
+
+def test_transpose_batched_off_the_line_grid(dev):
+    """Several matrices whose y rows miss the line grid keep the plain sub-tile order."""
+    B, M, N, ldx, ldy = 3, 1030, 2051, 2052, 1034
+    note("transpose batched off-grid")
+    check_transpose(dev, B, M, N, ldx, ldy, M * ldx + 8, N * ldy + 4, 1, 1, 0, seed=77)
