@@ -34,6 +34,7 @@ struct RowArgs {
     int64_t rem;        // live columns of the remainder tile (0 = no remainder tile)
     int64_t bc;         // column tile width
     int per_tile;       // chunks per lane per column tile
+    int log_bc;         // log2(bc) (bc = LPR * W * per_tile, a power of two)
     uint32_t ngroups;   // row groups of kBlock / LPR rows
     uint64_t nf_c;      // multiply-high divisor of nfull (0: nfull too large, 64-bit modulo)
     uint32_t nf_d;
@@ -93,6 +94,41 @@ __device__ __forceinline__ auto load_fill(const float *p, int64_t live) {
     }
 }
 
+// SHIFT walks (rows off the 16-byte grid): the row is read from the 16-byte boundary `head`
+// elements before its start, and the first `head` elements of its first chunk (not the row's)
+// take the fill.
+template <class Op>
+__device__ __forceinline__ f4 head_fill(f4 v, int head) {
+    v.x = head > 0 ? Op::kFill : v.x;
+    v.y = head > 1 ? Op::kFill : v.y;
+    v.z = head > 2 ? Op::kFill : v.z;
+    return v;
+}
+template <class Op>
+__device__ __forceinline__ float head_fill(float v, int head) { return v; }
+
+// The row a lane walks: its start, its length and its split into whole tiles plus a remainder.
+// SHIFT: from the 16-byte boundary at or before the row's start, with head masked elements in
+// front (head = (start address / 4) mod 4), so that every chunk is a 16-byte vector; the split is
+// then that of N + head elements.
+struct RowSpan {
+    const float *xr;
+    int64_t N, nfull, rem;
+    int head;
+};
+template <bool SHIFT>
+__device__ __forceinline__ RowSpan row_span(const float *xr, int64_t N, int64_t nfull, int64_t rem, int log_bc) {
+    RowSpan s{xr, N, nfull, rem, 0};
+    if constexpr (SHIFT) {
+        s.head = int((reinterpret_cast<uintptr_t>(xr) >> 2) & 3);
+        s.xr = xr - s.head;
+        s.N = N + s.head;
+        s.nfull = s.N >> log_bc;
+        s.rem = s.N - (s.nfull << log_bc);
+    }
+    return s;
+}
+
 // First whole tile of row group grp in the rotated walk: 7 * grp mod nfull, by multiply-high
 // division (exact: fast_mod(grp) * 7 stays below 2^32 for the divisors the host passes).  A 64-bit
 // modulo costs about a hundred scalar instructions, paid by every row group before its first
@@ -135,8 +171,11 @@ __device__ __forceinline__ float row_combine(float v, float *wv) {
 // DEEP (4-byte chunks, at least 32 whole chunks per lane; chosen on the host): whole chunks go 32
 // at a time while 32 remain, the bytes per lane in flight of the 16-byte path.  A separate instance,
 // so that short walks keep the registers (and waves per SIMD) of the 8-deep loop.
-template <class Op, int LPR, bool VEC, bool PRE, bool DEEP>
+// SHIFT (rows off the 16-byte grid, with VEC): see row_span; no rotation (the row pitch is not a
+// multiple of 16 bytes, let alone of 4 KiB).
+template <class Op, int LPR, bool VEC, bool PRE, bool DEEP, bool SHIFT = false>
 __global__ __launch_bounds__(block_threads<LPR>()) void row_reduce(RowArgs a) {
+    static_assert(!SHIFT || (VEC && !DEEP), "a shifted walk reads 16-byte chunks");
     using T = typename std::conditional<VEC, f4, float>::type;
     constexpr int W = VEC ? 4 : 1;
     constexpr int kRows = block_threads<LPR>() / LPR;  // rows per workgroup
@@ -148,7 +187,8 @@ __global__ __launch_bounds__(block_threads<LPR>()) void row_reduce(RowArgs a) {
     for (uint32_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
         const int64_t row = int64_t(grp) * kRows + t / LPR;
         const int64_t rr = row < a.M ? row : a.M - 1;
-        const float *xr = a.x + rr * a.ld;
+        const RowSpan sp = row_span<SHIFT>(a.x + rr * a.ld, a.N, a.nfull, a.rem, a.log_bc);
+        const float *xr = sp.xr;
         const float *p = xr + g * W;
 
         T acc[kAcc];
@@ -159,13 +199,15 @@ __global__ __launch_bounds__(block_threads<LPR>()) void row_reduce(RowArgs a) {
         // The remainder tile (columns kt .. N-1) is loaded first, so that its latency overlaps the
         // whole tiles instead of adding one more round trip after them (8.1 -> 7.6 us on the
         // 8192 x 1000 masked row max); it is still combined last.
-        const int64_t kt = a.nfull * a.bc;
+        const int64_t kt = sp.nfull * a.bc;
         T rv[PRE ? kRemPrefetch : 1];
         if constexpr (PRE) {
 #pragma unroll
             for (int f = 0; f < kRemPrefetch; ++f) {
                 const int64_t c = int64_t(f) * kStep + g * W;  // tile-local column of the chunk
-                rv[f] = f < a.per_tile ? load_fill<Op, VEC>(xr + kt + c, a.N - kt - c) : T(Op::kFill);
+                rv[f] = f < a.per_tile ? load_fill<Op, VEC>(xr + kt + c, sp.N - kt - c) : T(Op::kFill);
+                if (SHIFT && kt + c == 0)
+                    rv[f] = head_fill<Op>(rv[f], sp.head);
             }
         }
 
@@ -173,8 +215,8 @@ __global__ __launch_bounds__(block_threads<LPR>()) void row_reduce(RowArgs a) {
         // workgroup starts at a different whole tile (7 * group mod nfull) and wraps around: when the
         // row pitch is a multiple of 4 KiB, workgroups that all walked the tiles in the same order
         // would hit the same HBM channels at the same time.
-        const int64_t main_chunks = a.nfull * a.per_tile;
-        const int64_t start = first_tile(grp, a) * a.per_tile;
+        const int64_t main_chunks = sp.nfull * a.per_tile;
+        const int64_t start = SHIFT ? 0 : first_tile(grp, a) * a.per_tile;
         // Chunk c feeds accumulator c mod kAcc in the same order at either depth: the same bits.
         int64_t k = 0;
         if constexpr (DEEP) {
@@ -203,6 +245,10 @@ __global__ __launch_bounds__(block_threads<LPR>()) void row_reduce(RowArgs a) {
                     idx -= main_chunks;
                 v[u] = (k + u < main_chunks) ? load_whole<VEC, LPR>(p + idx * kStep) : T(Op::kFill);
             }
+            if constexpr (SHIFT) {
+                if (k == 0 && g == 0)
+                    v[0] = head_fill<Op>(v[0], sp.head);  // the chunk at the row's 16-byte boundary
+            }
 #pragma unroll
             for (int u = 0; u < kLoads; ++u)
                 acc[u % kAcc] = combine<Op>(acc[u % kAcc], v[u]);
@@ -215,10 +261,13 @@ __global__ __launch_bounds__(block_threads<LPR>()) void row_reduce(RowArgs a) {
             for (int f = 0; f < kRemPrefetch; ++f)
                 if (f < a.per_tile)
                     acc[0] = combine<Op>(acc[0], rv[f]);
-        } else if (a.rem > 0) {
+        } else if (sp.rem > 0) {
             for (int f = 0; f < a.per_tile; ++f) {
                 const int64_t c = int64_t(f) * kStep + g * W;  // tile-local column of the chunk
-                acc[0] = combine<Op>(acc[0], load_fill<Op, VEC>(xr + kt + c, a.N - kt - c));
+                T v = load_fill<Op, VEC>(xr + kt + c, sp.N - kt - c);
+                if (SHIFT && kt + c == 0)
+                    v = head_fill<Op>(v, sp.head);
+                acc[0] = combine<Op>(acc[0], v);
             }
         }
 
@@ -370,8 +419,19 @@ __global__ __launch_bounds__(kBlock) void row_once(OnceArgs a) {
     }
 }
 
-template <int LPR, bool VEC, bool PRE>
+// Sum of exp(s - b) over elements lo .. hi - 1 of a chunk (positions, not values, decide: a score
+// may equal the fill).
+__device__ __forceinline__ float sum_exp_range(f4 v, float b, int64_t lo, int64_t hi) {
+    return ((lo <= 0 && 0 < hi ? exp_f32(v.x - b) : 0.0f) + (lo <= 1 && 1 < hi ? exp_f32(v.y - b) : 0.0f)) +
+           ((lo <= 2 && 2 < hi ? exp_f32(v.z - b) : 0.0f) + (lo <= 3 && 3 < hi ? exp_f32(v.w - b) : 0.0f));
+}
+__device__ __forceinline__ float sum_exp_range(float v, float b, int64_t lo, int64_t hi) {
+    return lo <= 0 && 0 < hi ? exp_f32(v - b) : 0.0f;
+}
+
+template <int LPR, bool VEC, bool PRE, bool SHIFT = false>
 __global__ __launch_bounds__(block_threads<LPR>()) void row_softmax(RowArgs a) {
+    static_assert(!SHIFT || VEC, "a shifted walk reads 16-byte chunks");
     using T = typename std::conditional<VEC, f4, float>::type;
     constexpr int W = VEC ? 4 : 1;
     constexpr int kRows = block_threads<LPR>() / LPR;
@@ -383,25 +443,28 @@ __global__ __launch_bounds__(block_threads<LPR>()) void row_softmax(RowArgs a) {
     for (uint32_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
         const int64_t row = int64_t(grp) * kRows + t / LPR;
         const int64_t rr = row < a.M ? row : a.M - 1;
-        const float *xr = a.x + rr * a.ld;
+        const RowSpan sp = row_span<SHIFT>(a.x + rr * a.ld, a.N, a.nfull, a.rem, a.log_bc);
+        const float *xr = sp.xr;
         const float *p = xr + g * W;
         float m = kMaxFill, l = 0.0f;
 
         // The remainder tile's chunks are loaded ahead of the whole tiles (as in row_reduce) and
         // folded in after them.
-        const int64_t kt = a.nfull * a.bc;
+        const int64_t kt = sp.nfull * a.bc;
         T rv[PRE ? kRemPrefetch : 1];
         if constexpr (PRE) {
 #pragma unroll
             for (int f = 0; f < kRemPrefetch; ++f) {
                 const int64_t c = int64_t(f) * kStep + g * W;
-                rv[f] = f < a.per_tile ? load_fill<MaxOp, VEC>(xr + kt + c, a.N - kt - c) : T(kMaxFill);
+                rv[f] = f < a.per_tile ? load_fill<MaxOp, VEC>(xr + kt + c, sp.N - kt - c) : T(kMaxFill);
+                if (SHIFT && kt + c == 0)
+                    rv[f] = head_fill<MaxOp>(rv[f], sp.head);
             }
         }
 
         // Whole tiles, in the rotated order of row_reduce; no masks.
-        const int64_t main_chunks = a.nfull * a.per_tile;
-        const int64_t start = first_tile(grp, a) * a.per_tile;
+        const int64_t main_chunks = sp.nfull * a.per_tile;
+        const int64_t start = SHIFT ? 0 : first_tile(grp, a) * a.per_tile;
         for (int64_t k = 0; k < main_chunks; k += kLoads) {
             T v[kLoads];
 #pragma unroll
@@ -411,15 +474,22 @@ __global__ __launch_bounds__(block_threads<LPR>()) void row_softmax(RowArgs a) {
                     idx -= main_chunks;
                 v[u] = (k + u < main_chunks) ? load_whole<VEC, LPR>(p + idx * kStep) : T(kMaxFill);
             }
+            if constexpr (SHIFT) {
+                if (k == 0 && g == 0)
+                    v[0] = head_fill<MaxOp>(v[0], sp.head);  // its exp underflows to 0 below
+            }
             float b = m;
 #pragma unroll
             for (int u = 0; u < kLoads; ++u)
                 b = __builtin_fmaxf(b, chunk_max(v[u]));  // padding is the fill: never above a score
             float acc = 0.0f;
 #pragma unroll
-            for (int u = 0; u < kLoads; ++u)
-                if (k + u < main_chunks)
+            for (int u = 0; u < kLoads; ++u) {
+                if (SHIFT && u == 0 && k == 0 && g == 0)
+                    acc += main_chunks > 0 ? sum_exp_range(v[0], b, sp.head, 4) : 0.0f;  // not the masked head
+                else if (k + u < main_chunks)
                     acc += sum_exp(v[u], b);
+            }
             l = l * exp_f32(m - b) + acc;
             m = b;
         }
@@ -428,21 +498,27 @@ __global__ __launch_bounds__(block_threads<LPR>()) void row_softmax(RowArgs a) {
         if constexpr (PRE) {
 #pragma unroll
             for (int f = 0; f < kRemPrefetch; ++f) {
-                const int64_t live = a.N - kt - (int64_t(f) * kStep + g * W);
+                const int64_t c = int64_t(f) * kStep + g * W;
+                const int64_t live = sp.N - kt - c;
                 if (f < a.per_tile && live > 0) {
                     const float b = __builtin_fmaxf(m, chunk_max(rv[f]));
-                    l = l * exp_f32(m - b) + sum_exp_live(rv[f], b, live);
+                    const float add = SHIFT && kt + c == 0 ? sum_exp_range(rv[f], b, sp.head, live)
+                                                           : sum_exp_live(rv[f], b, live);
+                    l = l * exp_f32(m - b) + add;
                     m = b;
                 }
             }
-        } else if (a.rem > 0) {
+        } else if (sp.rem > 0) {
             for (int f = 0; f < a.per_tile; ++f) {
                 const int64_t c = int64_t(f) * kStep + g * W;
-                const int64_t live = a.N - kt - c;
+                const int64_t live = sp.N - kt - c;
                 if (live > 0) {
-                    const T v = load_fill<MaxOp, VEC>(xr + kt + c, live);
+                    T v = load_fill<MaxOp, VEC>(xr + kt + c, live);
+                    const int64_t lo = SHIFT && kt + c == 0 ? sp.head : 0;  // masked head: not counted
+                    if (lo > 0)
+                        v = head_fill<MaxOp>(v, sp.head);
                     const float b = __builtin_fmaxf(m, chunk_max(v));
-                    l = l * exp_f32(m - b) + sum_exp_live(v, b, live);
+                    l = l * exp_f32(m - b) + (lo > 0 ? sum_exp_range(v, b, lo, live) : sum_exp_live(v, b, live));
                     m = b;
                 }
             }
@@ -618,42 +694,44 @@ hipError_t launch_split(const tmp::RowPlan &p, hipStream_t stream) {
 }
 
 template <int LPR, bool PRE>
-const void *pick_softmax_vec(bool vec) {
-    return vec ? reinterpret_cast<const void *>(&row_softmax<LPR, true, PRE>)
-               : reinterpret_cast<const void *>(&row_softmax<LPR, false, PRE>);
+const void *pick_softmax_vec(const tmp::RowPlan &p) {
+    if (p.shift)
+        return reinterpret_cast<const void *>(&row_softmax<LPR, true, PRE, true>);
+    return p.vec ? reinterpret_cast<const void *>(&row_softmax<LPR, true, PRE>)
+                 : reinterpret_cast<const void *>(&row_softmax<LPR, false, PRE>);
 }
 
 template <bool PRE>
 const void *pick_softmax(const tmp::RowPlan &p) {
     switch (p.lpr) {
-    case 1: return pick_softmax_vec<1, PRE>(p.vec);
-    case 2: return pick_softmax_vec<2, PRE>(p.vec);
-    case 4: return pick_softmax_vec<4, PRE>(p.vec);
-    case 8: return pick_softmax_vec<8, PRE>(p.vec);
-    case 16: return pick_softmax_vec<16, PRE>(p.vec);
-    case 32: return pick_softmax_vec<32, PRE>(p.vec);
-    case 64: return pick_softmax_vec<64, PRE>(p.vec);
-    case 128: return pick_softmax_vec<128, PRE>(p.vec);
-    case 256: return pick_softmax_vec<256, PRE>(p.vec);
-    case 512: return pick_softmax_vec<512, PRE>(p.vec);
-    default: return pick_softmax_vec<1024, PRE>(p.vec);
+    case 1: return pick_softmax_vec<1, PRE>(p);
+    case 2: return pick_softmax_vec<2, PRE>(p);
+    case 4: return pick_softmax_vec<4, PRE>(p);
+    case 8: return pick_softmax_vec<8, PRE>(p);
+    case 16: return pick_softmax_vec<16, PRE>(p);
+    case 32: return pick_softmax_vec<32, PRE>(p);
+    case 64: return pick_softmax_vec<64, PRE>(p);
+    case 128: return pick_softmax_vec<128, PRE>(p);
+    case 256: return pick_softmax_vec<256, PRE>(p);
+    case 512: return pick_softmax_vec<512, PRE>(p);
+    default: return pick_softmax_vec<1024, PRE>(p);
     }
 }
 
-template <class Op, bool VEC, bool PRE, bool DEEP>
+template <class Op, bool VEC, bool PRE, bool DEEP, bool SHIFT = false>
 const void *pick_lpr(int lpr) {
     switch (lpr) {
-    case 1: return reinterpret_cast<const void *>(&row_reduce<Op, 1, VEC, PRE, DEEP>);
-    case 2: return reinterpret_cast<const void *>(&row_reduce<Op, 2, VEC, PRE, DEEP>);
-    case 4: return reinterpret_cast<const void *>(&row_reduce<Op, 4, VEC, PRE, DEEP>);
-    case 8: return reinterpret_cast<const void *>(&row_reduce<Op, 8, VEC, PRE, DEEP>);
-    case 16: return reinterpret_cast<const void *>(&row_reduce<Op, 16, VEC, PRE, DEEP>);
-    case 32: return reinterpret_cast<const void *>(&row_reduce<Op, 32, VEC, PRE, DEEP>);
-    case 64: return reinterpret_cast<const void *>(&row_reduce<Op, 64, VEC, PRE, DEEP>);
-    case 128: return reinterpret_cast<const void *>(&row_reduce<Op, 128, VEC, PRE, DEEP>);
-    case 256: return reinterpret_cast<const void *>(&row_reduce<Op, 256, VEC, PRE, DEEP>);
-    case 512: return reinterpret_cast<const void *>(&row_reduce<Op, 512, VEC, PRE, DEEP>);
-    default: return reinterpret_cast<const void *>(&row_reduce<Op, 1024, VEC, PRE, DEEP>);
+    case 1: return reinterpret_cast<const void *>(&row_reduce<Op, 1, VEC, PRE, DEEP, SHIFT>);
+    case 2: return reinterpret_cast<const void *>(&row_reduce<Op, 2, VEC, PRE, DEEP, SHIFT>);
+    case 4: return reinterpret_cast<const void *>(&row_reduce<Op, 4, VEC, PRE, DEEP, SHIFT>);
+    case 8: return reinterpret_cast<const void *>(&row_reduce<Op, 8, VEC, PRE, DEEP, SHIFT>);
+    case 16: return reinterpret_cast<const void *>(&row_reduce<Op, 16, VEC, PRE, DEEP, SHIFT>);
+    case 32: return reinterpret_cast<const void *>(&row_reduce<Op, 32, VEC, PRE, DEEP, SHIFT>);
+    case 64: return reinterpret_cast<const void *>(&row_reduce<Op, 64, VEC, PRE, DEEP, SHIFT>);
+    case 128: return reinterpret_cast<const void *>(&row_reduce<Op, 128, VEC, PRE, DEEP, SHIFT>);
+    case 256: return reinterpret_cast<const void *>(&row_reduce<Op, 256, VEC, PRE, DEEP, SHIFT>);
+    case 512: return reinterpret_cast<const void *>(&row_reduce<Op, 512, VEC, PRE, DEEP, SHIFT>);
+    default: return reinterpret_cast<const void *>(&row_reduce<Op, 1024, VEC, PRE, DEEP, SHIFT>);
     }
 }
 
@@ -662,6 +740,8 @@ const void *pick_vec(const tmp::RowPlan &p) {
     // 4-byte walks of at least 32 whole chunks per lane: 2048 x 8191 row sums 18.3 -> 14.9 us, 16
     // x 1000003 130 -> 110 us.  (One instance for every length had cost short walks up to 17%:
     // 8192 x 1000 at stride 1001 7.9 -> 9.3 us.)
+    if (p.shift)
+        return pick_lpr<Op, true, PRE, false, true>(p.lpr);
     if (p.vec)
         return pick_lpr<Op, true, PRE, false>(p.lpr);
     return p.nfull * p.per_tile >= 4 * kLoads ? pick_lpr<Op, false, PRE, true>(p.lpr)
@@ -728,6 +808,7 @@ hipError_t launch_rows(const tmp::RowPlan &p, hipStream_t stream) {
     a.rem = p.rem;
     a.bc = p.bc;
     a.per_tile = p.per_tile;
+    a.log_bc = tmp::ilog2(p.bc);
     const int64_t rows_per_wg = p.block / p.lpr;
     a.ngroups = static_cast<uint32_t>((p.M + rows_per_wg - 1) / rows_per_wg);
     // 7 * (grp mod nfull) < 2^32 keeps the two-step multiply-high modulo exact

@@ -127,6 +127,7 @@ def test_row_walk_split_is_the_remainder_rule():
         for N in (1, 5, 16, 63, 64, 100, 1000, 4096, 70000):
             for ld in (N + (-N) % 4, N + 1 if N % 4 == 0 else N):
                 W = 4 if M <= 1 or ld % 4 == 0 else 1  # 16-byte chunks when every row starts on 16 bytes
+                shifted = W == 1 and N > 2048  # long rows off the grid: 16-byte chunks from the boundary
                 for BC in (1, 4, 16, 64, 256, 1024):
                     st, bc, nf, rem, lanes = tm.tm_row_walk(M, N, ld, 1, BC, 0, LINE)
                     assert st == tm.TM_OK
@@ -137,12 +138,13 @@ def test_row_walk_split_is_the_remainder_rule():
                         # one batch: at least 16 lanes cover the row, and the tile is the caller's
                         assert lanes >= 16 and lanes * K >= chunks and bc == max(BC, W), (M, N, ld, BC)
                         continue
-                    assert bc % (lanes * W) == 0 and 1 <= bc // (lanes * W) <= 4, (M, N, ld, BC, bc, lanes)
+                    Wt = 4 if shifted else W
+                    assert bc % (lanes * Wt) == 0 and 1 <= bc // (lanes * Wt) <= 4, (M, N, ld, BC, bc, lanes)
                     if bc == BC:
                         continue
                     # the caller's tile was not taken: it was not whole chunks, would leave fewer
                     # than half the lanes, or would need more than 4 chunks per lane
-                    assert BC % W or BC // W < lanes // 2 or BC // W > 4 * lanes, (M, N, ld, BC, bc, lanes)
+                    assert BC % Wt or BC // Wt < lanes // 2 or BC // Wt > 4 * lanes, (M, N, ld, BC, bc, lanes)
 
 
 def test_row_walk_errors():

@@ -467,3 +467,35 @@ def test_softmax_stats_empty_rows(dev):
     assert st == tm.TM_OK
     torch.cuda.synchronize()
     assert (bits(Mo.payload()) == 0xF149F2CA).all() and (bits(Lo.payload()) == 0).all()
+
+
+@pytest.mark.parametrize("M,N,ld,off", [
+    (133, 64954, 64986, 0),   # row stride = 2 mod 4: rows start 0 or 8 bytes past a 16-byte boundary
+    (1000, 3001, 3003, 0),    # stride = 3 mod 4: all four offsets
+    (257, 8191, 8193, 1),     # stride = 1 mod 4, base 4 bytes off
+    (64, 100003, 100005, 3),  # few long rows (several waves per row), base 12 bytes off
+    (4000, 2049, 2049, 2),    # just past the length where the shifted walk starts
+])
+def test_rows_off_the_grid_shifted_walk(dev, M, N, ld, off):
+    """Long rows that do not start on 16-byte boundaries are read in 16-byte chunks from the
+    boundary before each row, the elements before the row masked (0 for sums, the -1e30 fill for
+    maxima): sums within 1e-5 of sum |x|, maxima and softmax m bit for bit, l within 1e-5, and
+    the padding (+1e30) between rows never read into a result."""
+    note("shifted rows %dx%d ld %d off %d" % (M, N, ld, off))
+    xh = inputs.uniform(M + N + off, M * N, -10.0, -1.0)
+    X, host = device_matrix(xh, M, N, ld, dev, off)
+    ref = oracle.rowsum_f64(host, ld, M, N)
+    absref = oracle.rowsum_f64(np.abs(host), ld, M, N)
+    st, O = gpu_rowsum(X, ld, M, N, 1, 64, 0, dev)
+    assert st == tm.TM_OK
+    torch.cuda.synchronize()
+    assert_sums(O.payload().cpu().numpy(), ref, absref)
+    assert O.guards_intact()
+    st, O = gpu_rowmax(X, ld, M, N, 1, 64, 0, dev)
+    assert st == tm.TM_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(O.payload()), bits(oracle.rowmax(host, ld, M, N)))
+    st, Mo, Lo = gpu_softmax(X, ld, M, N, 1, 64, 0, dev)
+    assert st == tm.TM_OK
+    torch.cuda.synchronize()
+    check_softmax(Mo, Lo, host, ld, M, N)
