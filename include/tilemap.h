@@ -321,7 +321,12 @@ int tm_pad_extents(int64_t M, int64_t N, int TM, int TN, int64_t *Mp, int64_t *N
  * time per launch in *us_best.  If table != NULL it receives 9 x 11 floats, row i for TM = 2^i and
  * column j for TN = 2^j: the candidate's mean microseconds per launch, or -1 where it was not run.
  * The caller's buffers are used as they are: buffers that fit in the 256 MiB Infinity Cache time
- * cache bandwidth, not HBM.  Synchronizes `stream`; y holds the op's result afterwards.  x and y
+ * cache bandwidth, not HBM.  In this library the tile states the promise (and, on the ragged path,
+ * which elements are masked) but does not shape the work: the scheduler cuts every call into the
+ * same work items whatever tile keeps the promise, so the candidates' times differ by launch noise
+ * and the "fastest" is the fastest of this run, not a better tile.  The sweep is kept as the check
+ * that no tile is a trap (each candidate's time is in `table`).  Synchronizes `stream`; y holds the
+ * op's result afterwards.  x and y
  * must not overlap.  Errors: those of the op's own call for the shared arguments; TM_E_INVAL for
  * an unknown op, reps < 1, a NULL event or result pointer, or x == y; TM_E_ALIGN when no tile keeps
  * the promise; TM_E_HIP if a launch or event call fails. */
