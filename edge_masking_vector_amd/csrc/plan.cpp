@@ -926,12 +926,20 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
             plan->packed = 0;  // nothing to gain, or work ids beyond 32 bits
     }
     if (plan->pairs) {
-        // work items: 16 per 8 pairs (pair p -> items 16 (p / 8) + p mod 8 and that + 8)
-        const int64_t pair_rows = ceil_div(subs_m, 2);
-        const int64_t items = ceil_div(pair_rows * subs_n, 8) * 16;
+        // Groups of G vertically adjacent sub-tiles on one XCD; more of a y row's shared lines meet
+        // in one L2 the larger G is.  Against pairs, in the kernel over 1 GiB of rotating buffers:
+        // with 16-byte x rows G = 8 took 4096 x 4096 at y stride 4100 from 33.9 to 30.3 us, stride
+        // 4098 38.2 -> 35.1, 4097 38.6 -> 35.5, 5450 x 2568 37.5 -> 36.9, 57348 x 252 40.8 -> 39.4
+        // (1707 x 7425: 37.3 -> 37.8); with x rows off the 16-byte grid G = 4 (4096 x 4096 at
+        // strides 4097: 42.7 -> 42.8, 4099 x 4099: 48.7 -> 48.4; G = 8 and 16 lost 2-12% there).
+        // Work items: 8 G per 8 groups (group r -> items 8 G (r / 8) + r mod 8 + 8 k, member k < G).
+        plan->log_grp = vx ? 3 : 2;
+        const int64_t G = int64_t{1} << plan->log_grp;
+        const int64_t grp_rows = ceil_div(subs_m, G);
+        const int64_t items = ceil_div(grp_rows * subs_n, 8) * 8 * G;
         if (items <= UINT32_MAX && plan->packed == 0 && plan->log_g == 0) {
             plan->nwork = static_cast<uint64_t>(items);
-            plan->per_b = make_div32(static_cast<uint32_t>(pair_rows));
+            plan->per_b = make_div32(static_cast<uint32_t>(grp_rows));
         } else {
             plan->pairs = false;
         }

@@ -244,6 +244,7 @@ struct TransposePlan {
     bool pairs = false;           // vertical pairs of sub-tiles on one XCD (one matrix, y rows off the
                                   // 128-byte line grid): per_b is then the divisor ceil(subs_m / 2)
     int log_g = 0;                // batches per work item: 2^log_g (whole matrices in one sub-tile)
+    int log_grp = 1;              // pairs: 2^log_grp vertically adjacent sub-tiles on one XCD
     // Few channels with a packed side (transpose_packed): 1 = y rows of exactly M < kTrSub floats
     // (NCHW -> NHWC), 2 = x rows of exactly N < kTrSub floats (NHWC -> NCHW); 0 = neither.
     int packed = 0;

@@ -66,10 +66,37 @@ static_assert(sizeof(TrArgs) <= 128, "transpose arguments outgrew one scalar loa
 // reaches memory as two partial writes unless both parts meet in one L2 first, and HBM3E has no
 // write mask: a partial write costs the controller a read-modify-write (written bytes rise only
 // 11-13%, but 4096 x 4096 with y stride 4100 took 55.7 against 24.4 us).  So sub-tiles go in
-// vertical pairs (pm even, pm + 1) to workgroups b and b + 8, which the dispatcher sends to the
-// same XCD at about the same time: work item w is pair 8 (w / 16) + (w mod 8), half (w mod 16) / 8,
-// pairs numbered pm / 2 fastest (per_b / c_pb hold the pair rows, ceil(subs_m / 2)).  Work items
-// past the last pair do nothing.
+// vertical groups of G = 2^log_g (pm = G r .. G r + G - 1; here log_g counts sub-tiles, not
+// batches) to workgroups b, b + 8, ..., b + 8 (G - 1), which the dispatcher sends to the same XCD
+// one after another: work item w is group 8 (w / 8G) + (w mod 8), member (w / 8) mod G, groups
+// numbered r fastest (per_b / c_pb hold the group rows, ceil(subs_m / G)).  Work items past the
+// last group do nothing.
+// Work item w -> (batch b, sub-tile row pm, sub-tile column pn) for work counts below 2^32: the
+// group order of PAIRS, else the diagonal order (multiply-high divisions).  skip: an item past
+// the last group (PAIRS only) has no sub-tile.
+template <bool PAIRS>
+__device__ __forceinline__ void decode32(const TrArgs &a, uint32_t w32, uint32_t &b, uint32_t &pm, uint32_t &pn,
+                                         bool &skip) {
+    if constexpr (PAIRS) {
+        const uint32_t grp = (w32 >> (3 + a.log_g)) * 8 + (w32 & 7u);
+        const uint32_t member = (w32 >> 3) & ((1u << a.log_g) - 1u);
+        const uint32_t q = fast_div(grp, a.c_pb, a.per_b);  // per_b: group rows
+        b = 0;
+        pm = ((grp - q * a.per_b) << a.log_g) + member;    // < subs_m + 2^log_g <= 2^32
+        pn = q;
+        skip = pm >= a.subs_m || pn >= a.subs_n;
+    } else {
+        const uint32_t b32 = fast_div(w32, a.c_pb, a.per_b);
+        const uint32_t rest = w32 - b32 * a.per_b;
+        const uint32_t q = fast_div(rest, a.c_m, a.subs_m);
+        const uint32_t pm32 = rest - q * a.subs_m;
+        b = b32;
+        pm = pm32;
+        pn = fast_mod(q + pm32, a.c_n, a.subs_n);  // q + pm32 < subs_n + subs_m < 2^32
+        skip = false;
+    }
+}
+
 template <bool VX, bool VY, bool ALIGNED, int BS, bool WIDE, bool PACK, int SUB = kSubElems, bool PAIRS = false>
 __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
     static_assert(!PAIRS || (!WIDE && !PACK), "pair order is for one matrix of 32-bit work counts");
@@ -100,23 +127,12 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
         // same HBM channels).  For each pm, q runs over every sub-tile column once.
         uint64_t b, pm, pn;
         bool skip = false;
-        if constexpr (PAIRS) {
-            const uint32_t w32 = static_cast<uint32_t>(w);
-            const uint32_t pair = (w32 >> 4) * 8 + (w32 & 7u), half = (w32 >> 3) & 1u;
-            const uint32_t q = fast_div(pair, a.c_pb, a.per_b);  // per_b: pair rows
-            b = 0;
-            pm = 2 * (pair - q * a.per_b) + half;
-            pn = q;
-            skip = pm >= a.subs_m || pn >= a.subs_n;
-        } else if constexpr (!WIDE) {  // the work count fits 32 bits: multiply-high divisions
-            const uint32_t w32 = static_cast<uint32_t>(w);
-            const uint32_t b32 = fast_div(w32, a.c_pb, a.per_b);
-            const uint32_t rest = w32 - b32 * a.per_b;
-            const uint32_t q = fast_div(rest, a.c_m, a.subs_m);
-            const uint32_t pm32 = rest - q * a.subs_m;
+        if constexpr (!WIDE) {  // the work count fits 32 bits
+            uint32_t b32, pm32, pn32;
+            decode32<PAIRS>(a, static_cast<uint32_t>(w), b32, pm32, pn32, skip);
             b = b32;
             pm = pm32;
-            pn = fast_mod(q + pm32, a.c_n, a.subs_n);  // q + pm32 < subs_n + subs_m < 2^32
+            pn = pn32;
         } else {
             const uint64_t per_b = uint64_t(a.subs_m) * a.subs_n;
             b = w / per_b;
@@ -417,7 +433,7 @@ hipError_t launch_packed(const tmp::TransposePlan &p, hipStream_t stream) {
 template <bool WIDE, bool PACK>
 const void *pick(const tmp::TransposePlan &p) {
     if constexpr (!PACK && !WIDE) {
-        if (p.pairs) {  // y rows off the line grid, one matrix: 64 x 32 sub-tiles in vertical pairs
+        if (p.pairs) {  // y rows off the line grid, one matrix: 64 x 32 sub-tiles in groups on one XCD
             constexpr int S2 = 2 * kSubElems;
             if (p.vx)
                 return p.vy ? reinterpret_cast<const void *>(&transpose_tiles<true, true, false, kTrBlock, false, false, S2, true>)
@@ -462,7 +478,7 @@ hipError_t launch_transpose(const tmp::TransposePlan &p, hipStream_t stream) {
     a.c_m = p.by_m.c;
     a.c_n = p.by_n.c;
     a.nwork = p.nwork;
-    a.log_g = p.log_g;
+    a.log_g = p.pairs ? p.log_grp : p.log_g;
     a.B = p.B;
     const void *fn = p.log_g > 0 ? (p.wide ? pick<true, true>(p) : pick<false, true>(p))
                                  : (p.wide ? pick<true, false>(p) : pick<false, false>(p));

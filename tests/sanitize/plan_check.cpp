@@ -247,26 +247,29 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
                                         p.packed == 0 && p.sm == 2 * tmp::kTrSub && p.sn == tmp::kTrSub),
           "%s instance of %d elements", tag, p.sub);
     if (p.pairs) {
-        // pair order: item w -> pair 8 (w / 16) + w mod 8, half (w / 8) mod 2; pm = 2 (pair mod
-        // pair_rows) + half, pn = pair / pair_rows; items past the grid of sub-tiles do nothing;
-        // every sub-tile is visited exactly once, and the grid keeps items w, w + 8 on one XCD
-        CHECK(B == 1 && !p.wide && p.log_g == 0 && p.packed == 0 && p.nwork % 16 == 0 && p.grid % 16 == 0,
-              "%s pair plan", tag);
-        const uint32_t pair_rows = (p.subs_m + 1) / 2;
-        CHECK(p.per_b.d == pair_rows, "%s pair divisor", tag);
+        // group order (G = 2^log_grp vertically adjacent sub-tiles): item w -> group 8 (w / 8G) +
+        // w mod 8, member (w / 8) mod G; pm = G (group mod group_rows) + member, pn = group /
+        // group_rows; items past the grid of sub-tiles do nothing; every sub-tile is visited
+        // exactly once, and the grid keeps items w, w + 8, ..., w + 8 (G - 1) on one XCD
+        const uint32_t G = 1u << p.log_grp;
+        CHECK(B == 1 && !p.wide && p.log_g == 0 && p.packed == 0 && p.log_grp >= 1 && p.log_grp <= 4 &&
+                  p.nwork % (8 * G) == 0 && p.grid % (8 * G) == 0,
+              "%s group plan", tag);
+        const uint32_t grp_rows = (p.subs_m + G - 1) / G;
+        CHECK(p.per_b.d == grp_rows, "%s group divisor", tag);
         std::vector<uint8_t> seen(size_t(p.subs_m) * p.subs_n, 0);
         for (uint64_t w = 0; w < p.nwork; ++w) {
             const uint32_t w32 = uint32_t(w);
-            const uint32_t pair = (w32 >> 4) * 8 + (w32 & 7u), half = (w32 >> 3) & 1u;
-            const uint32_t q = umulhi_div(pair, p.per_b);
-            const uint32_t pm = 2 * (pair - q * p.per_b.d) + half, pn = q;
-            CHECK(q == pair / pair_rows, "%s pair division", tag);
+            const uint32_t grp = (w32 >> (3 + p.log_grp)) * 8 + (w32 & 7u), member = (w32 >> 3) & (G - 1);
+            const uint32_t q = umulhi_div(grp, p.per_b);
+            const uint64_t pm = uint64_t(grp - q * p.per_b.d) * G + member, pn = q;
+            CHECK(q == grp / grp_rows, "%s group division", tag);
             if (pm < p.subs_m && pn < p.subs_n)
                 ++seen[size_t(pn) * p.subs_m + pm];
         }
         for (size_t k = 0; k < seen.size(); ++k)
             if (seen[k] != 1) {
-                CHECK(false, "%s pair-order sub-tile %zu visited %d times", tag, k, int(seen[k]));
+                CHECK(false, "%s group-order sub-tile %zu visited %d times", tag, k, int(seen[k]));
                 break;
             }
         ++g_checked;
