@@ -100,6 +100,7 @@ __device__ __forceinline__ void decode32(const TrArgs &a, uint32_t w32, uint32_t
 template <bool VX, bool VY, bool ALIGNED, int BS, bool WIDE, bool PACK, int SUB = kSubElems, bool PAIRS = false>
 __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
     static_assert(!PAIRS || (!WIDE && !PACK), "pair order is for one matrix of 32-bit work counts");
+    static_assert(!PAIRS || !ALIGNED, "items past the last group rely on the masks to touch nothing");
     static_assert(!ALIGNED || (VX && VY), "the promise implies 16-byte rows on both sides");
     constexpr int LOG_WX = VX ? 2 : 0, LOG_WY = VY ? 2 : 0;
     constexpr int WX = 1 << LOG_WX, WY = 1 << LOG_WY;
