@@ -378,27 +378,33 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
               "y = fmaf(x, 0.75, -0.25), 64x64 tiles; rows contiguous (row stride N), so the view is "
               "planned as one flat row whose only ragged edge is its end")
         del xs, ys
-    # the same ragged map over padded rows, where the 2-D tile plan runs and its edge tiles (the
-    # bottom 4 rows, the right 40 columns) take the masked body: rows off the 16-byte grid (row
-    # stride 1001: 4-byte chunks) and on it (row stride 1004: 16-byte chunks, 64 x 40 right-edge
-    # tiles); then a scale-sized ragged view, 4100 x 4100 at row stride 4104 under 32 x 128
-    for (M, N, ld, TM, TN, var, name, what) in (
-            (4100, 1000, 1001, 64, 64, tm.TM_VAR_AUTO, "affine_4100x1000_ld1001_ragged_2d",
-             "4-byte chunks (rows off the 16-byte grid)"),
-            (4100, 1000, 1004, 64, 64, tm.TM_VAR_VEC4, "affine_4100x1000_ld1004_ragged_2d",
-             "16-byte chunks, 64x40 right-edge tiles"),
-            (4100, 4100, 4104, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ld4104_ragged_2d",
-             "16-byte chunks, 32x128 tiles: 4-row bottom and 4-column right edge tiles")):
-        xh = inputs.matrix(inputs.ragged_input(M, N, seed=12), M, N, ld)
+    # the same ragged map over padded rows.  With one row stride in both tensors (and less than a
+    # line of padding) the view is one span of 1 KiB items on y's 1 KiB grid whose columns past N
+    # are masked: rows off the 16-byte grid (row stride 1001), on it (1004), and a scale-sized
+    # view (4100 x 4100 at row stride 4104).  With different strides in x and y the 2-D tile plan
+    # runs, and its edge tiles (the bottom 4 rows, the right 40 or 4 columns) take the masked body.
+    for (M, N, ldx, ldy, TM, TN, var, name, what) in (
+            (4100, 1000, 1001, 1001, 64, 64, tm.TM_VAR_AUTO, "affine_4100x1000_ld1001_ragged_2d",
+             "one span of 1 KiB items, columns past N masked (rows off the 16-byte grid)"),
+            (4100, 1000, 1004, 1004, 64, 64, tm.TM_VAR_VEC4, "affine_4100x1000_ld1004_ragged_2d",
+             "one span of 1 KiB items, columns past N masked"),
+            (4100, 4100, 4104, 4104, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ld4104_ragged_2d",
+             "one span of 1 KiB items, columns past N masked"),
+            (4100, 1000, 1004, 1008, 64, 64, tm.TM_VAR_VEC4, "affine_4100x1000_ldx1004_ldy1008_ragged_tiles",
+             "the 2-D tile plan: 16-byte chunks, 4-row bottom and 64x40 right-edge tiles masked"),
+            (4100, 4100, 4104, 4108, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ldx4104_ldy4108_ragged_tiles",
+             "the 2-D tile plan: 16-byte chunks, 32x128 tiles, 4-row bottom and 4-column right edge "
+             "tiles masked")):
+        xh = inputs.matrix(inputs.ragged_input(M, N, seed=12), M, N, ldx)
         nb = 2 * M * N * 4
-        R = sets_for(2 * M * ld * 4)
+        R = sets_for(M * ldx * 4 + M * ldy * 4)
         xs = rotated(torch, xh, R, dev)
-        ys = [torch.zeros_like(x) for x in xs]
+        ys = [torch.zeros(M * ldy, device=dev) for _ in range(R)]
         timed(name, nb, R,
-              lambda i, M=M, N=N, ld=ld, TM=TM, TN=TN, var=var: ok(tm.tm_map_affine(
-                  xs[i], ld, ys[i], ld, M, N, 0.75, -0.25, TM, TN, 0, var, stream)),
-              "ragged path, row stride %d (padded rows: the 2-D tile plan, edge tiles masked), %s; "
-              "bytes count the %dx%d elements only" % (ld, what, M, N))
+              lambda i, M=M, N=N, ldx=ldx, ldy=ldy, TM=TM, TN=TN, var=var: ok(tm.tm_map_affine(
+                  xs[i], ldx, ys[i], ldy, M, N, 0.75, -0.25, TM, TN, 0, var, stream)),
+              "ragged path, %dx%d tiles, row strides %d / %d (padded rows): %s; bytes count the %dx%d "
+              "elements only" % (TM, TN, ldx, ldy, what, M, N))
         del xs, ys
 
     # row and column sums of 4096 x 4096 U[0,1)

@@ -468,7 +468,7 @@ const void *pick(const tmp::MapPlan &p) {
 }  // namespace
 
 hipError_t launch_map(const tmp::MapPlan &p, hipStream_t stream) {
-    if (p.flat)
+    if (p.flat || p.rows)
         return launch_map_flat(p, stream);
     MapArgs a;
     a.x = p.x;

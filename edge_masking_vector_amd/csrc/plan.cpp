@@ -233,6 +233,42 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
         }
     }
 
+    // Padded rows (row stride ld > N, the same in both tensors, less than one 128-byte line of
+    // padding between rows, both bases the same distance past a 16-byte boundary): on the ragged
+    // path the span from y[0] to the last element is cut into 1 KiB items on y's 1 KiB grid, and
+    // each item moves 16-byte chunks with the columns past N masked (mapflat.hip, map_rows).
+    // Work items then never share a line, where 2-D tiles over rows off the line grid shared the
+    // lines at both ends of every row piece with the neighbouring items: a line written in parts
+    // by two XCDs reaches HBM3E as partial writes, which the controller turns into
+    // read-modify-writes.  Only the lines that hold padding are written in part here.
+    if (!aligned && M > 1 && ldx == ldy && ldx > N && ldx - N < kLineBytes / 4 && N >= kRowsSpanMinN &&
+        op != kChannel && (access == kVec4 || access == kScalar) &&
+        (reinterpret_cast<uintptr_t>(x) - reinterpret_cast<uintptr_t>(y)) % 16 == 0) {
+        const int64_t head = static_cast<int64_t>((reinterpret_cast<uintptr_t>(y) / 4) % 256);
+        const int64_t span = (M - 1) * ldx + N;
+        if (head + span + 256 <= INT32_MAX && ldx <= UINT32_MAX) {  // span indexes are 32-bit
+            const int64_t nwork = ceil_div(head + span, 256);
+            plan->launch = true;
+            plan->op = op;
+            plan->access = access;
+            plan->rows = true;
+            plan->head = static_cast<uint32_t>(head);
+            plan->span = static_cast<uint32_t>(span);
+            plan->ld_div = make_div32(static_cast<uint32_t>(ldx));
+            plan->nwork = static_cast<uint32_t>(nwork);
+            plan->grid = cap_grid(nwork);
+            plan->x = x;
+            plan->y = y;
+            plan->ldx = ldx;
+            plan->ldy = ldy;
+            plan->M = M;
+            plan->N = N;
+            plan->alpha = alpha;
+            plan->beta = beta;
+            return TM_OK;
+        }
+    }
+
     // Columns are scheduled in tiles at most one row segment wide: a wider tile (TN = 512, 1024)
     // is cut into row-segment columns.  The caller's tile only states the promise (already
     // checked) and, on the ragged path, which chunks take the masked body; neither changes a

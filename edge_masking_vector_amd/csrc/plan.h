@@ -25,6 +25,8 @@ constexpr int kRowSegmentBytes = 512;  // map work items: bytes of each row they
 constexpr int kStreamSegmentBytes = 1024;  // ... or one row segment of this many bytes, moved
                                            // with device-scope streaming buffer accesses
 constexpr int64_t kChanFlatMax = 65535;  // channel op: flat views up to this many channels
+constexpr int64_t kRowsSpanMinN = 64;      // padded rows in one span: rows of at least this many
+                                           // floats and less than a line of padding between them
                                          // (C * C < 2^32 for the device's 32-bit modulo)
 constexpr int kTrSub = 32;          // transpose: staged sub-tile edge (one 128-byte line of f32) ...
 constexpr int kTrSubElems = kTrSub * kTrSub;  // ... and elements; a narrow tensor's sub-tile is
@@ -127,6 +129,14 @@ struct MapPlan {
     bool flat = false;            // one contiguous row in 1 KiB stream items, no channel op: the
                                   // kernel of mapflat.hip (item w = elements [256 w, 256 w + 256))
     uint32_t flat_last = 0;       // flat: elements of the last item inside the row (1 .. 256)
+    // Padded rows in one span (mapflat.hip, map_rows): the view's rows lie ld apart in both
+    // tensors; the span y[0 .. (M - 1) ld + N) is cut into 1 KiB items on y's 1 KiB grid, item 0
+    // starting `head` floats before y[0].  Element f of the span is (row f / ld, column f % ld),
+    // live when the column is below N.
+    bool rows = false;
+    uint32_t head = 0;            // rows: floats from the first item's start to y[0] (0 .. 255)
+    uint32_t span = 0;            // rows: (M - 1) * ld + N
+    Div32 ld_div;                 // rows: divisor ld
     uint32_t group = 1;           // G
     uint32_t groups_n = 0;        // ceil(tiles_n / G)
     uint32_t tiles_n = 0;         // tiles along N

@@ -24,7 +24,7 @@
 
 #include "../../edge_masking_vector_amd/csrc/plan.h"
 
-static long g_checked = 0, g_failed = 0, g_flat = 0;
+static long g_checked = 0, g_failed = 0, g_flat = 0, g_rows = 0;
 
 #define CHECK(cond, ...)                                   \
     do {                                                   \
@@ -98,10 +98,75 @@ static void replay_flat(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld,
     ++g_flat;
 }
 
+// Padded rows in one span (mapflat.hip, map_rows): item w, lane t moves the 16-byte chunk of span
+// elements q .. q + 3, q = 256 w + 4 t - head; element f is row f / ld, column f % ld, live when the
+// column is below N.  Every load (clamped to the chunks holding the span's first and last
+// elements) must be a 16-byte aligned block of x that holds an element of the span; every live
+// element must be stored exactly once and nothing else at all; whole-chunk stores must be aligned
+// blocks inside the item's 1 KiB block of y.
+static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, const char *tag) {
+    CHECK(!p.aligned && M > 1 && p.ldx == ld && p.ldy == ld && ld > N && ld - N < 32 && N >= tmp::kRowsSpanMinN &&
+              p.op != tmp::kChannel && (p.access == tmp::kVec4 || p.access == tmp::kScalar),
+          "%s span plan outside its case", tag);
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(p.x), ya = reinterpret_cast<uintptr_t>(p.y);
+    const int64_t span = (M - 1) * ld + N;
+    CHECK(p.span == uint64_t(span) && p.head == (ya / 4) % 256 && (xa - ya) % 16 == 0 && p.ld_div.d == ld,
+          "%s span geometry", tag);
+    CHECK(p.nwork == uint64_t((p.head + span + 255) / 256) && p.grid >= 1 && p.grid <= p.nwork, "%s span items", tag);
+    const int32_t q_first = -int32_t(p.head & 3u);
+    const int32_t q_last = int32_t(span - 1) - int32_t((span - 1 + p.head) & 3u);
+    std::vector<uint8_t> hits(size_t(span), 0);
+    bool bad_load = false, bad_store = false;
+    for (uint32_t w = 0; w < p.nwork; ++w)
+        for (int t = 0; t < 64; ++t) {
+            const int32_t q = int32_t(w * 256u + 4u * t) - int32_t(p.head);
+            const int32_t qc = q < q_first ? q_first : (q > q_last ? q_last : q);
+            // aligned, and holding an element of the span
+            if ((xa + 4 * int64_t(qc)) % 16 != 0 || qc + 3 < 0 || qc >= span)
+                bad_load = true;
+            const uint32_t c = q > 0 ? umulhi_mod(uint32_t(q), p.ld_div) : 0u;
+            if (q > 0 && c != uint32_t(q % ld))
+                bad_load = true;
+            if (q >= 0 && int64_t(q) + 3 < span && c + 3 < N) {
+                const uintptr_t blk = ya + 4 * (int64_t(w) * 256 - p.head);
+                if (blk % 1024 != 0 || (ya + 4 * int64_t(q)) != blk + 16 * uintptr_t(t))
+                    bad_store = true;
+                for (int i = 0; i < 4; ++i)
+                    ++hits[size_t(q + i)];
+            } else {
+                for (int i = 0; i < 4; ++i) {
+                    const int32_t f = q + i;
+                    uint32_t col = q >= 0 ? c + i : uint32_t(f);
+                    col = col >= ld ? col - uint32_t(ld) : col;
+                    if (f >= 0 && f < span && col < N) {
+                        if (col != uint32_t(f % ld))
+                            bad_store = true;
+                        ++hits[size_t(f)];
+                    }
+                }
+            }
+        }
+    CHECK(!bad_load, "%s span: a load off the view's 16-byte blocks (or a wrong column)", tag);
+    CHECK(!bad_store, "%s span: a misplaced store", tag);
+    for (int64_t f = 0; f < span; ++f) {
+        const bool live = f % ld < N;
+        if (hits[size_t(f)] != (live ? 1 : 0)) {
+            CHECK(false, "%s span element %ld (live %d) stored %d times", tag, long(f), int(live), int(hits[size_t(f)]));
+            break;
+        }
+    }
+    ++g_checked;
+    ++g_rows;
+}
+
 static void replay_map(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, uintptr_t xbase,
                        const char *tag) {
     if (p.flat) {
         replay_flat(p, M, N, ld, tag);
+        return;
+    }
+    if (p.rows) {
+        replay_rows(p, M, N, ld, tag);
         return;
     }
     const int W = p.access == tmp::kScalar || p.access == tmp::kScalar1 ? 1 : 4;
@@ -669,6 +734,8 @@ int main() {
     check_transposes();
     check_reductions();
     check_split_rows();
-    std::printf("plan_check: %ld plans checked (%ld flat), %ld failures\n", g_checked, g_flat, g_failed);
+    CHECK(g_rows > 0, "no padded-row span plan was replayed");
+    std::printf("plan_check: %ld plans checked (%ld flat, %ld span), %ld failures\n", g_checked, g_flat, g_rows,
+                g_failed);
     return g_failed == 0 ? 0 : 1;
 }

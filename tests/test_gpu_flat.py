@@ -158,3 +158,64 @@ def test_rowmax_walk_reported_and_exact(dev, BC, ld):
     wm, wl = oracle.softmax_stats(sh, ld, M, N)
     assert np.array_equal(bits(m), bits(wm))
     assert np.allclose(l.cpu().numpy(), wl, rtol=1e-5, atol=0)
+
+
+# ---- padded rows in one span (mapflat.hip, map_rows) -------------------------------------------
+def _check_strided(dev, op, M, N, ldx, ldy, xoff, yoff, variant, seed, alpha=0.75, beta=-0.25):
+    nx, ny = (M - 1) * ldx + N, (M - 1) * ldy + N
+    xh = inputs.uniform(seed, nx, -8.0, 8.0)
+    X = Guarded(nx, dev, offset=xoff, guard=LINE_GUARD_FLOATS)
+    X.upload(xh)
+    Y = Guarded(ny, dev, offset=yoff, guard=LINE_GUARD_FLOATS)
+    s = torch.cuda.current_stream()
+    if op == "affine":
+        st = tm.tm_map_affine(X.ptr, ldx, Y.ptr, ldy, M, N, alpha, beta, 64, 64, 0, variant, s)
+    elif op == "scale":
+        st = tm.tm_scale2d(X.ptr, ldx, Y.ptr, ldy, M, N, alpha, 64, 64, 0, variant, s)
+    else:
+        st = tm.tm_copy2d(X.ptr, ldx, Y.ptr, ldy, M, N, 64, 64, 0, variant, s)
+    assert st == tm.TM_OK, tm.tm_status_string(st)
+    torch.cuda.synchronize()
+    want = sentinel_host(Y.buf.numel())
+    region = want[Y.off:Y.off + ny].copy()   # the padding between rows keeps its sentinels
+    if op == "affine":
+        oracle.map_affine(xh, ldx, region, ldy, M, N, alpha, beta)
+    elif op == "scale":
+        oracle.scale2d(xh, ldx, region, ldy, M, N, alpha)
+    else:
+        oracle.copy2d(xh, ldx, region, ldy, M, N)
+    want[Y.off:Y.off + ny] = region
+    assert np.array_equal(bits(Y.host()), bits(want)), (op, M, N, ldx, ldy, xoff, yoff, variant)
+    assert X.guards_intact()
+
+
+@pytest.mark.parametrize("op,M,N,ld,off,variant", [
+    ("affine", 3, 64, 65, 0, tm.TM_VAR_AUTO),         # the smallest rows taken, one float of padding
+    ("scale", 7, 299, 320, 1, tm.TM_VAR_AUTO),        # the span starts 1 float past a line
+    ("copy", 100, 1000, 1001, 3, tm.TM_VAR_AUTO),     # rows off the 16-byte grid
+    ("affine", 100, 1000, 1004, 0, tm.TM_VAR_VEC4),   # 16-byte rows, a chunk of padding per row
+    ("affine", 50, 4100, 4104, 2, tm.TM_VAR_AUTO),    # bases 8 bytes off the 16-byte grid
+    ("scale", 1000, 257, 288, 5, tm.TM_VAR_AUTO),     # 31 floats of padding, ragged row ends
+    ("copy", 513, 777, 808, 64, tm.TM_VAR_AUTO),      # the span starts mid 1 KiB block
+    ("affine", 4100, 1000, 1001, 0, tm.TM_VAR_AUTO),  # the padded 4100 x 1000 workload
+])
+def test_padded_rows_one_span(dev, op, M, N, ld, off, variant):
+    """Rows with less than a line of padding and one stride in both tensors are moved as one span
+    of 1 KiB items on y's 1 KiB grid, 16-byte chunks whose columns past N are masked ([SLICING]
+    "Masking": nothing past the view's edge is stored): bit for bit, the padding between rows and
+    the guard bands untouched."""
+    note("span %s %dx%d ld %d off %d variant %d" % (op, M, N, ld, off, variant))
+    _check_strided(dev, op, M, N, ld, ld, off, off, variant, seed=M + N + ld)
+
+
+@pytest.mark.parametrize("M,N,ldx,ldy,xoff,yoff", [
+    (100, 1000, 1001, 1001, 1, 0),    # bases at different distances past a 16-byte boundary
+    (100, 1000, 1004, 1008, 0, 0),    # different strides: the 2-D tile plan
+    (100, 60, 61, 61, 0, 0),          # rows narrower than the span's minimum
+    (100, 1000, 1040, 1040, 0, 0),    # a line or more of padding
+])
+def test_padded_rows_outside_the_span(dev, M, N, ldx, ldy, xoff, yoff):
+    """Padded views the span does not take (different strides or base offsets, narrow rows, wide
+    padding) keep the 2-D tile plan: the same results bit for bit."""
+    note("no span %dx%d ldx %d ldy %d" % (M, N, ldx, ldy))
+    _check_strided(dev, "affine", M, N, ldx, ldy, xoff, yoff, tm.TM_VAR_AUTO, seed=7 * M + N)
