@@ -914,19 +914,28 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     // When y's rows are off the 128-byte line grid (16-byte rows or not), the lines at the ends of
     // each y-row piece are shared with the sub-tiles above and below, and a line written in parts
     // by two XCDs reaches HBM as partial writes (read-modify-write in the controller: 4096 x 4096
-    // with y stride 4100 took 55.7 against 24.4 us with stride 4096).  One matrix then takes the
-    // 64 x 32 sub-tiles in vertical pairs on one XCD (transpose.hip, PAIRS).
+    // with y stride 4100 took 55.7 against 24.4 us with stride 4096).  One matrix then writes
+    // line-aligned windows of its y rows instead of sub-tiles (transpose.hip, transpose_skew):
+    // 64 elements of 32 y rows per work item, each window starting on a line, from a staged band
+    // of 96 x rows.  Against 64 x 32 sub-tiles in vertical groups on one XCD (one process, 1 GiB of
+    // rotating buffers): 4096 x 4096 at y stride 4100 30.3 -> 26.9 us, 4098 35.2 -> 27.3, 4097
+    // 35.2 -> 27.6, both strides 4097 43.4 -> 32.5 (4-byte x reads), 5450 x 2568 36.9 -> 25.8,
+    // 57348 x 252 39.4 -> 26.8, 1707 x 7425 37.9 -> 26.2, 4099 x 4099 48.2 -> 32.3.
     const bool y_lines = aligned_to(y, kLineBytes) && (N <= 1 || ldy % (kLineBytes / 4) == 0);
     const bool large = !aligned && M >= 2 * kTrSub && N >= kTrSub && M * N >= (int64_t{1} << 22);
-    if (large && (!vy || (B == 1 && !y_lines))) {
+    const bool skew = large && B == 1 && !y_lines;
+    if (large && (!vy || skew)) {
         plan->sm = 2 * kTrSub;
         plan->sn = kTrSub;
         plan->sub = 2 * kTrSubElems;
-        plan->pairs = B == 1 && !y_lines;
+        plan->skew = skew;
     }
     plan->vx = vx;
     plan->vy = vy;
-    const int64_t subs_m = ceil_div(M, plan->sm), subs_n = ceil_div(N, plan->sn);
+    // skew: item rows of 64 windows each, one more when the windows' shift (up to 31 floats) can
+    // leave the last rows of y uncovered
+    const int64_t subs_m = skew ? ceil_div(M + kTrSub - 1, plan->sm) : ceil_div(M, plan->sm);
+    const int64_t subs_n = ceil_div(N, plan->sn);
     if (subs_m > INT32_MAX || subs_n > INT32_MAX)
         return TM_E_UNSUPPORTED;
     plan->subs_m = static_cast<uint32_t>(subs_m);
@@ -961,27 +970,22 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
         if (plan->packed != 0 && ((!plan->pvec && !plan->flat16) || plan->nwork > UINT32_MAX))
             plan->packed = 0;  // nothing to gain, or work ids beyond 32 bits
     }
-    if (plan->pairs) {
-        // Groups of G vertically adjacent sub-tiles on one XCD; more of a y row's shared lines meet
-        // in one L2 the larger G is.  Against pairs, in the kernel over 1 GiB of rotating buffers:
-        // with 16-byte x rows G = 8 took 4096 x 4096 at y stride 4100 from 33.9 to 30.3 us, stride
-        // 4098 38.2 -> 35.1, 4097 38.6 -> 35.5, 5450 x 2568 37.5 -> 36.9, 57348 x 252 40.8 -> 39.4
-        // (1707 x 7425: 37.3 -> 37.8); with x rows off the 16-byte grid G = 4 (4096 x 4096 at
-        // strides 4097: 42.7 -> 42.8, 4099 x 4099: 48.7 -> 48.4; G = 8 and 16 lost 2-12% there).
-        // Work items: 8 G per 8 groups (group r -> items 8 G (r / 8) + r mod 8 + 8 k, member k < G).
+    if (plan->skew) {
+        // Groups of G vertically adjacent items on one XCD: the upper neighbour's band rows are
+        // still in that L2.  G = 4, 8 and 16 measured within 2-4% of each other; 8 with 16-byte x
+        // rows, 4 with 4-byte ones.  Work items: 8 G per 8 groups (group r -> items 8 G (r / 8) +
+        // r mod 8 + 8 k, member k < G).
         plan->log_grp = vx ? 3 : 2;
         const int64_t G = int64_t{1} << plan->log_grp;
         const int64_t grp_rows = ceil_div(subs_m, G);
         const int64_t items = ceil_div(grp_rows * subs_n, 8) * 8 * G;
-        if (items <= UINT32_MAX && plan->packed == 0 && plan->log_g == 0) {
-            plan->nwork = static_cast<uint64_t>(items);
-            plan->per_b = make_div32(static_cast<uint32_t>(grp_rows));
-        } else {
-            plan->pairs = false;
-        }
+        if (items > UINT32_MAX)
+            return TM_E_UNSUPPORTED;  // work ids are 32-bit in this order
+        plan->nwork = static_cast<uint64_t>(items);
+        plan->per_b = make_div32(static_cast<uint32_t>(grp_rows));
     }
     plan->wide = plan->nwork > UINT32_MAX;
-    if (!plan->wide && !plan->pairs)
+    if (!plan->wide && !plan->skew)
         plan->per_b = make_div32(static_cast<uint32_t>(subs_m * subs_n));
     if (!plan->wide) {
         plan->by_m = make_div32(plan->subs_m);

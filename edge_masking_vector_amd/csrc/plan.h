@@ -251,10 +251,11 @@ struct TransposePlan {
     int aligned = 0;
     int sm = 1, sn = 1;           // staged sub-tile extents (powers of two, sm * sn <= sub)
     int sub = kTrSubElems;        // the kernel instance's largest sub-tile: kTrSubElems or twice that
-    bool pairs = false;           // vertical pairs of sub-tiles on one XCD (one matrix, y rows off the
-                                  // 128-byte line grid): per_b is then the divisor ceil(subs_m / 2)
+    bool skew = false;            // one matrix, y rows off the 128-byte line grid: line-aligned y
+                                  // windows (transpose_skew); subs_m = ceil((M + 31) / 64) item rows
+                                  // in groups of 2^log_grp on one XCD, per_b the divisor of the group rows
     int log_g = 0;                // batches per work item: 2^log_g (whole matrices in one sub-tile)
-    int log_grp = 1;              // pairs: 2^log_grp vertically adjacent sub-tiles on one XCD
+    int log_grp = 0;              // skew: 2^log_grp vertically adjacent items on one XCD
     // Few channels with a packed side (transpose_packed): 1 = y rows of exactly M < kTrSub floats
     // (NCHW -> NHWC), 2 = x rows of exactly N < kTrSub floats (NHWC -> NCHW); 0 = neither.
     int packed = 0;

@@ -61,23 +61,18 @@ static_assert(sizeof(TrArgs) <= 128, "transpose arguments outgrew one scalar loa
 // own rows allow (a 9163 x 1051 transpose with 16-byte x rows and 4-byte y rows took 42 us with
 // 4-byte chunks on both sides).
 // SUB: the largest sub-tile (elements) the instance stages.
-// PAIRS (one matrix, y rows off the 128-byte line grid): the sub-tiles above and below each other
-// share the lines at the ends of their y-row pieces.  A line that two workgroups write in parts
-// reaches memory as two partial writes unless both parts meet in one L2 first, and HBM3E has no
-// write mask: a partial write costs the controller a read-modify-write (written bytes rise only
-// 11-13%, but 4096 x 4096 with y stride 4100 took 55.7 against 24.4 us).  So sub-tiles go in
-// vertical groups of G = 2^log_g (pm = G r .. G r + G - 1; here log_g counts sub-tiles, not
-// batches) to workgroups b, b + 8, ..., b + 8 (G - 1), which the dispatcher sends to the same XCD
-// one after another: work item w is group 8 (w / 8G) + (w mod 8), member (w / 8) mod G, groups
-// numbered r fastest (per_b / c_pb hold the group rows, ceil(subs_m / G)).  Work items past the
-// last group do nothing.
-// Work item w -> (batch b, sub-tile row pm, sub-tile column pn) for work counts below 2^32: the
-// group order of PAIRS, else the diagonal order (multiply-high divisions).  skip: an item past
-// the last group (PAIRS only) has no sub-tile.
-template <bool PAIRS>
+//
+// Work item w -> (batch b, sub-tile row pm, sub-tile column pn) for work counts below 2^32.
+// GROUPS (one matrix): vertical groups of G = 2^log_g items (pm = G r .. G r + G - 1; here log_g
+// counts items, not batches) go to workgroups b, b + 8, ..., b + 8 (G - 1), which the dispatcher
+// sends to the same XCD one after another: item w is group 8 (w / 8G) + (w mod 8), member
+// (w / 8) mod G, groups numbered r fastest (per_b / c_pb hold the group rows, ceil(subs_m / G));
+// an item past the last group has none (skip).  Otherwise the diagonal order, by multiply-high
+// divisions.
+template <bool GROUPS>
 __device__ __forceinline__ void decode32(const TrArgs &a, uint32_t w32, uint32_t &b, uint32_t &pm, uint32_t &pn,
                                          bool &skip) {
-    if constexpr (PAIRS) {
+    if constexpr (GROUPS) {
         const uint32_t grp = (w32 >> (3 + a.log_g)) * 8 + (w32 & 7u);
         const uint32_t member = (w32 >> 3) & ((1u << a.log_g) - 1u);
         const uint32_t q = fast_div(grp, a.c_pb, a.per_b);  // per_b: group rows
@@ -97,10 +92,8 @@ __device__ __forceinline__ void decode32(const TrArgs &a, uint32_t w32, uint32_t
     }
 }
 
-template <bool VX, bool VY, bool ALIGNED, int BS, bool WIDE, bool PACK, int SUB = kSubElems, bool PAIRS = false>
+template <bool VX, bool VY, bool ALIGNED, int BS, bool WIDE, bool PACK, int SUB = kSubElems>
 __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
-    static_assert(!PAIRS || (!WIDE && !PACK), "pair order is for one matrix of 32-bit work counts");
-    static_assert(!PAIRS || !ALIGNED, "items past the last group rely on the masks to touch nothing");
     static_assert(!ALIGNED || (VX && VY), "the promise implies 16-byte rows on both sides");
     constexpr int LOG_WX = VX ? 2 : 0, LOG_WY = VY ? 2 : 0;
     constexpr int WX = 1 << LOG_WX, WY = 1 << LOG_WY;
@@ -130,7 +123,7 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
         bool skip = false;
         if constexpr (!WIDE) {  // the work count fits 32 bits
             uint32_t b32, pm32, pn32;
-            decode32<PAIRS>(a, static_cast<uint32_t>(w), b32, pm32, pn32, skip);
+            decode32<false>(a, static_cast<uint32_t>(w), b32, pm32, pn32, skip);
             b = b32;
             pm = pm32;
             pn = pn32;
@@ -230,6 +223,103 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
             break;  // uniform; no barrier after the last sub-tile (it would hold the workgroup
                     // until its stores complete)
         __syncthreads();  // the next sub-tile reuses the LDS tile
+    } while (true);
+}
+
+// ---- y rows off the line grid: line-aligned y windows -------------------------------------------
+// One matrix whose y rows miss the 128-byte line grid.  With sub-tiles, the sub-tiles above and
+// below each other share the lines at the ends of their y-row pieces, and a line that two
+// workgroups write in parts reaches memory as two partial writes unless both parts meet in one
+// L2 first; HBM3E has no write mask, so each costs the controller a read-modify-write (written
+// bytes rose only 11-13%, but 4096 x 4096 with y stride 4100 took 55.7 against 24.4 us).
+// Here work item (pm, pn) writes, in each y row
+// j of its 32 (x columns col0 + j), the 64 elements that start at the line boundary at or before
+// y column row0 = 64 pm: a window [row0 - s_j, row0 - s_j + 64), s_j = the offset of y[col0 + j]
+// [row0] inside its line (0 .. 31 floats).  The windows of pm and pm + 1 meet exactly, so every
+// line of y is written by one work item (only a line that holds a row's end and the next row's
+// start has two writers), and no line is written in parts from two XCDs, which HBM3E would
+// serve as read-modify-writes.  A window starts on a line, so its chunks are 16-byte aligned
+// whatever the row stride: y is written in 16-byte stores.  The windows of one item reach x rows
+// row0 - 31 .. row0 + 63, so the item stages the band of x rows row0 - 32 .. row0 + 63 (the
+// top 32 are also its upper neighbour's, which the group order runs on the same XCD just before:
+// plain loads, so they are still in that L2).  ceil((M + 31) / 64) items along M cover every row.
+// Loads are clamped into the view (row to 0 .. M - 1, chunk to the one holding the last live
+// column); what a clamped load stages is never stored.  VX: x rows on the 16-byte grid.
+template <bool VX>
+__global__ __launch_bounds__(kTrBlock) void transpose_skew(TrArgs a) {
+    constexpr int SM = 2 * tmp::kTrSub, SN = tmp::kTrSub, BAND = SM + SN, PAD = SN + 1;
+    constexpr int WX = VX ? 4 : 1;
+    constexpr int NXC = BAND * SN / WX;                 // read chunks of the band
+    constexpr int KX = NXC / kTrBlock;                  // 3 (16-byte) or 12 (4-byte) per thread
+    constexpr int KY = SN * (SM / 4) / kTrBlock;        // 2 16-byte write chunks per thread
+    static_assert(NXC % kTrBlock == 0 && SN * (SM / 4) % kTrBlock == 0, "chunks divide the workgroup");
+    __shared__ float tile[BAND * PAD];
+    const int t = threadIdx.x;
+    uint64_t w = blockIdx.x;
+    do {
+        uint32_t b, pm, pn;
+        bool skip;
+        decode32<true>(a, static_cast<uint32_t>(w), b, pm, pn, skip);
+        const int64_t row0 = int64_t(pm) * SM, col0 = int64_t(pn) * SN;
+        const int cols_live = skip ? 0 : static_cast<int>(a.N - col0 < SN ? a.N - col0 : SN);
+        if (cols_live > 0) {  // uniform
+            // band row r is x row row0 - SN + r; loads from clamped rows and chunks
+            float v[KX][WX];
+            const int clast = (cols_live - 1) / WX;
+#pragma unroll
+            for (int k = 0; k < KX; ++k) {
+                const int e = t + k * kTrBlock;
+                const int r = e / (SN / WX), c = e - r * (SN / WX);
+                int64_t xr = row0 - SN + r;
+                xr = xr < 0 ? 0 : (xr >= a.M ? a.M - 1 : xr);
+                const float *p = a.x + xr * a.ldx + col0 + (c < clast ? c : clast) * WX;
+                if constexpr (VX) {
+                    const f4 q = ld16(p);
+                    v[k][0] = q.x, v[k][1] = q.y, v[k][2] = q.z, v[k][3] = q.w;
+                } else {
+                    v[k][0] = *p;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < KX; ++k) {
+                const int e = t + k * kTrBlock;
+                const int r = e / (SN / WX), c = e - r * (SN / WX);
+#pragma unroll
+                for (int i = 0; i < WX; ++i)
+                    tile[r * PAD + c * WX + i] = v[k][i];
+            }
+        }
+        __syncthreads();
+        if (cols_live > 0) {
+#pragma unroll
+            for (int k = 0; k < KY; ++k) {
+                const int e = t + k * kTrBlock;
+                const int j = e >> 4, c = e & 15;  // y row j, chunk c of its 64-element window
+                if (j < cols_live) {
+                    float *yr = a.y + (col0 + j) * a.ldy;
+                    const int sft = static_cast<int>((reinterpret_cast<uintptr_t>(yr + row0) >> 2) & 31u);
+                    const int64_t i0 = row0 - sft + 4 * c;  // y column (x row) of the chunk's first element
+                    const int br = SN - sft + 4 * c;        // its band row
+                    f4 u;
+                    u.x = tile[(br + 0) * PAD + j];
+                    u.y = tile[(br + 1) * PAD + j];
+                    u.z = tile[(br + 2) * PAD + j];
+                    u.w = tile[(br + 3) * PAD + j];
+                    if (i0 >= 0 && i0 + 4 <= a.M) {
+                        st16_nt(yr + i0, u);
+                    } else {
+                        if (i0 + 0 >= 0 && i0 + 0 < a.M) st4_nt(yr + i0 + 0, u.x);
+                        if (i0 + 1 >= 0 && i0 + 1 < a.M) st4_nt(yr + i0 + 1, u.y);
+                        if (i0 + 2 >= 0 && i0 + 2 < a.M) st4_nt(yr + i0 + 2, u.z);
+                        if (i0 + 3 >= 0 && i0 + 3 < a.M) st4_nt(yr + i0 + 3, u.w);
+                    }
+                }
+            }
+        }
+        w += gridDim.x;
+        if (w >= a.nwork)
+            break;  // uniform
+        __syncthreads();  // the next item reuses the LDS band
     } while (true);
 }
 
@@ -434,14 +524,9 @@ hipError_t launch_packed(const tmp::TransposePlan &p, hipStream_t stream) {
 template <bool WIDE, bool PACK>
 const void *pick(const tmp::TransposePlan &p) {
     if constexpr (!PACK && !WIDE) {
-        if (p.pairs) {  // y rows off the line grid, one matrix: 64 x 32 sub-tiles in groups on one XCD
-            constexpr int S2 = 2 * kSubElems;
-            if (p.vx)
-                return p.vy ? reinterpret_cast<const void *>(&transpose_tiles<true, true, false, kTrBlock, false, false, S2, true>)
-                            : reinterpret_cast<const void *>(&transpose_tiles<true, false, false, kTrBlock, false, false, S2, true>);
-            return p.vy ? reinterpret_cast<const void *>(&transpose_tiles<false, true, false, kTrBlock, false, false, S2, true>)
-                        : reinterpret_cast<const void *>(&transpose_tiles<false, false, false, kTrBlock, false, false, S2, true>);
-        }
+        if (p.skew)  // y rows off the line grid, one matrix: line-aligned y windows
+            return p.vx ? reinterpret_cast<const void *>(&transpose_skew<true>)
+                        : reinterpret_cast<const void *>(&transpose_skew<false>);
     }
     if (!PACK && !p.vy && p.sub == 2 * kSubElems)  // y rows off the 16-byte grid: 64 x 32 sub-tiles
         return p.vx ? reinterpret_cast<const void *>(&transpose_tiles<true, false, false, kTrBlock, WIDE, false, 2 * kSubElems>)
@@ -479,7 +564,7 @@ hipError_t launch_transpose(const tmp::TransposePlan &p, hipStream_t stream) {
     a.c_m = p.by_m.c;
     a.c_n = p.by_n.c;
     a.nwork = p.nwork;
-    a.log_g = p.pairs ? p.log_grp : p.log_g;
+    a.log_g = p.skew ? p.log_grp : p.log_g;
     a.B = p.B;
     const void *fn = p.log_g > 0 ? (p.wide ? pick<true, true>(p) : pick<false, true>(p))
                                  : (p.wide ? pick<true, false>(p) : pick<false, false>(p));

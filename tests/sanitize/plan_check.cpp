@@ -24,7 +24,7 @@
 
 #include "../../edge_masking_vector_amd/csrc/plan.h"
 
-static long g_checked = 0, g_failed = 0, g_flat = 0, g_rows = 0;
+static long g_checked = 0, g_failed = 0, g_flat = 0, g_rows = 0, g_skew = 0;
 
 #define CHECK(cond, ...)                                   \
     do {                                                   \
@@ -301,40 +301,70 @@ static void check_maps() {
 // ---- transpose --------------------------------------------------------------------------------
 static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, int64_t N, const char *tag) {
     CHECK(!p.wide, "%s small job planned as wide", tag);
-    CHECK(p.subs_m == uint32_t((M + p.sm - 1) / p.sm) && p.subs_n == uint32_t((N + p.sn - 1) / p.sn),
+    CHECK(p.subs_m == uint32_t((M + (p.skew ? tmp::kTrSub - 1 : 0) + p.sm - 1) / p.sm) &&
+              p.subs_n == uint32_t((N + p.sn - 1) / p.sn),
           "%s sub-tile counts", tag);
-    CHECK((p.log_g > 0 || p.pairs || p.nwork == uint64_t(B) * p.subs_m * p.subs_n) && p.grid >= 1 &&
+    CHECK((p.log_g > 0 || p.skew || p.nwork == uint64_t(B) * p.subs_m * p.subs_n) && p.grid >= 1 &&
               p.grid <= p.nwork,
           "%s work", tag);
     // the instance's capacity: kTrSubElems, or twice that for the 64 x 32 sub-tiles of views whose
-    // y rows are off the 16-byte grid (or, in pair order, off the 128-byte line grid)
-    CHECK(p.sub == tmp::kTrSubElems || (p.sub == 2 * tmp::kTrSubElems && (!p.vy || p.pairs) && p.log_g == 0 &&
+    // y rows are off the 16-byte grid (and for the line-aligned windows of one matrix)
+    CHECK(p.sub == tmp::kTrSubElems || (p.sub == 2 * tmp::kTrSubElems && (!p.vy || p.skew) && p.log_g == 0 &&
                                         p.packed == 0 && p.sm == 2 * tmp::kTrSub && p.sn == tmp::kTrSub),
           "%s instance of %d elements", tag, p.sub);
-    if (p.pairs) {
-        // group order (G = 2^log_grp vertically adjacent sub-tiles): item w -> group 8 (w / 8G) +
-        // w mod 8, member (w / 8) mod G; pm = G (group mod group_rows) + member, pn = group /
-        // group_rows; items past the grid of sub-tiles do nothing; every sub-tile is visited
-        // exactly once, and the grid keeps items w, w + 8, ..., w + 8 (G - 1) on one XCD
+    if (p.skew) {
+        // transpose_skew: group order (G = 2^log_grp vertically adjacent items): item w -> group
+        // 8 (w / 8G) + w mod 8, member (w / 8) mod G; pm = G (group mod group_rows) + member, pn =
+        // group / group_rows; items past subs_m x subs_n do nothing.  Item (pm, pn) writes, in y row
+        // 32 pn + j (j < 32), the 64 elements from the line boundary at or before y column 64 pm,
+        // those inside [0, M); it reads band rows 64 pm - 32 .. 64 pm + 63 of
+        // x clamped into [0, M).  Every element of y must be written exactly once, by the item whose
+        // band holds its x row, and 16-byte stores must be aligned.
         const uint32_t G = 1u << p.log_grp;
         CHECK(B == 1 && !p.wide && p.log_g == 0 && p.packed == 0 && p.log_grp >= 1 && p.log_grp <= 4 &&
-                  p.nwork % (8 * G) == 0 && p.grid % (8 * G) == 0,
-              "%s group plan", tag);
+                  p.nwork % (8 * G) == 0 && p.grid % (8 * G) == 0 && p.sm == 64 && p.sn == 32,
+              "%s skew plan", tag);
         const uint32_t grp_rows = (p.subs_m + G - 1) / G;
         CHECK(p.per_b.d == grp_rows, "%s group divisor", tag);
-        std::vector<uint8_t> seen(size_t(p.subs_m) * p.subs_n, 0);
+        const uintptr_t ya = reinterpret_cast<uintptr_t>(p.y);
+        std::vector<uint8_t> hits(size_t(N) * M, 0);
+        bool bad = false;
         for (uint64_t w = 0; w < p.nwork; ++w) {
             const uint32_t w32 = uint32_t(w);
             const uint32_t grp = (w32 >> (3 + p.log_grp)) * 8 + (w32 & 7u), member = (w32 >> 3) & (G - 1);
             const uint32_t q = umulhi_div(grp, p.per_b);
             const uint64_t pm = uint64_t(grp - q * p.per_b.d) * G + member, pn = q;
             CHECK(q == grp / grp_rows, "%s group division", tag);
-            if (pm < p.subs_m && pn < p.subs_n)
-                ++seen[size_t(pn) * p.subs_m + pm];
+            if (pm >= p.subs_m || pn >= p.subs_n)
+                continue;
+            const int64_t row0 = int64_t(pm) * 64, col0 = int64_t(pn) * 32;
+            const int cols_live = int(std::min<int64_t>(N - col0, 32));
+            for (int j = 0; j < cols_live; ++j) {
+                const uintptr_t yr = ya + 4 * uintptr_t((col0 + j) * p.ldy);
+                const int sft = int(((yr + 4 * uintptr_t(row0)) >> 2) & 31u);
+                for (int c = 0; c < 16; ++c) {
+                    const int64_t i0 = row0 - sft + 4 * c;
+                    const int br = 32 - sft + 4 * c;
+                    if (br < 0 || br + 3 >= 96)
+                        bad = true;  // outside the staged band
+                    if (i0 >= 0 && i0 + 4 <= M && (yr + 4 * uintptr_t(i0)) % 16 != 0)
+                        bad = true;  // a misaligned 16-byte store
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t i = i0 + e;
+                        if (i >= 0 && i < M) {
+                            if (i - (row0 - 32) != br + e)
+                                bad = true;  // the band row is not this x row
+                            ++hits[size_t(col0 + j) * M + i];
+                        }
+                    }
+                }
+            }
         }
-        for (size_t k = 0; k < seen.size(); ++k)
-            if (seen[k] != 1) {
-                CHECK(false, "%s group-order sub-tile %zu visited %d times", tag, k, int(seen[k]));
+        CHECK(!bad, "%s skew: a window outside the band or a misaligned store", tag);
+        ++g_skew;
+        for (size_t k = 0; k < hits.size(); ++k)
+            if (hits[k] != 1) {
+                CHECK(false, "%s skew: y element %zu written %d times", tag, k, int(hits[k]));
                 break;
             }
         ++g_checked;
@@ -353,7 +383,7 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
         if (M >= tmp::kTrSub && N >= tmp::kTrSub) {
             // 32 x 32, or 64 x 32 for large views whose y rows are off the 16-byte grid (or, one
             // matrix, off the line grid)
-            const bool tall = (!p.vy || p.pairs) && M >= 2 * tmp::kTrSub && M * N >= (int64_t{1} << 22);
+            const bool tall = (!p.vy || p.skew) && M >= 2 * tmp::kTrSub && M * N >= (int64_t{1} << 22);
             CHECK(tall ? (p.sm == 2 * tmp::kTrSub && p.sn == tmp::kTrSub && p.sub == 2 * tmp::kTrSubElems)
                        : (p.sm == tmp::kTrSub && p.sn == tmp::kTrSub),
                   "%s wide view on %dx%d sub-tiles", tag, p.sm, p.sn);
@@ -427,6 +457,27 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
         }
     }
     ++g_checked;
+}
+
+// Views whose y rows miss the line grid, with bases at several offsets: the line-aligned windows.
+static void check_skew_transposes() {
+    struct S { int64_t M, N, ldx, ldy; };
+    const S cases[] = {{4096, 4096, 4096, 4100}, {4099, 4099, 4099, 4099}, {5450, 2568, 2568, 5450},
+                       {2049, 2050, 2051, 2049}, {8191, 513, 515, 8191}, {4103, 2049, 2052, 4108}};
+    for (const S &c : cases)
+        for (uintptr_t xoff : {uintptr_t{0}, uintptr_t{4}})
+            for (uintptr_t yoff : {uintptr_t{0}, uintptr_t{12}, uintptr_t{68}}) {
+                tmp::TransposePlan p;
+                const int st = tmp::plan_transpose(fake(0x1000000 + xoff), c.ldx, 0,
+                                                   const_cast<float *>(fake(0x40000000 + yoff)), c.ldy, 0, 1, c.M,
+                                                   c.N, 1, 1, 0, &p);
+                char tag[128];
+                std::snprintf(tag, sizeof tag, "skew transpose %ldx%ld ldx=%ld ldy=%ld xoff=%lu yoff=%lu", long(c.M),
+                              long(c.N), long(c.ldx), long(c.ldy), (unsigned long)xoff, (unsigned long)yoff);
+                CHECK(st == TM_OK && p.launch && p.skew, "%s not planned as line-aligned windows", tag);
+                if (st == TM_OK && p.launch)
+                    replay_transpose(p, 1, c.M, c.N, tag);
+            }
 }
 
 static void check_transposes() {
@@ -734,7 +785,9 @@ int main() {
     check_transposes();
     check_reductions();
     check_split_rows();
+    check_skew_transposes();
     CHECK(g_rows > 0, "no padded-row span plan was replayed");
+    CHECK(g_skew >= 36, "only %ld line-aligned window plans replayed", g_skew);
     std::printf("plan_check: %ld plans checked (%ld flat, %ld span), %ld failures\n", g_checked, g_flat, g_rows,
                 g_failed);
     return g_failed == 0 ? 0 : 1;

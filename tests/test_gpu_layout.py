@@ -213,17 +213,20 @@ def test_transpose_empty(dev):
     (2051, 1030, 1031, 2053, 0, 3),     # ragged sub-tiles at both edges
     (4096, 4096, 4096, 4100, 0, 0),     # 16-byte y rows off the 128-byte line grid
     (4103, 2049, 2052, 4108, 4, 0),     # the same with ragged edges (an odd number of sub-tile rows)
+    (4146, 1100, 1100, 4150, 0, 3),     # windows shifted by up to 31 floats past the last 64-row band
+    (4160, 1057, 1061, 4163, 2, 17),    # y base 17 floats past a line, ragged columns, odd strides
 ])
 def test_transpose_y_rows_off_the_grid(dev, M, N, ldx, ldy, xoff, yoff):
-    """Large views whose y rows are not 16-byte aligned take 64 x 32 sub-tiles staged in a
-    2048-element instance, and one matrix whose y rows miss the 128-byte line grid takes them in
-    vertical pairs: bit for bit, padding and guard bands untouched, ragged edges masked."""
+    """One large matrix whose y rows miss the 128-byte line grid is written in line-aligned
+    windows of its y rows (each work item: 64 elements of 32 y rows from a band of 96 x rows):
+    bit for bit, padding and guard bands untouched, the windows' ends at each y row's start and
+    end masked."""
     note("transpose off-grid %dx%d ldx %d ldy %d" % (M, N, ldx, ldy))
     check_transpose(dev, 1, M, N, ldx, ldy, 0, 0, 1, 1, 0, xoff=xoff, yoff=yoff, seed=M + N)
 
 
 def test_transpose_batched_off_the_line_grid(dev):
-    """Several matrices whose y rows miss the line grid keep the plain sub-tile order."""
+    """Several matrices whose y rows miss the line grid take 64 x 32 sub-tiles in the plain order."""
     B, M, N, ldx, ldy = 3, 1030, 2051, 2052, 1034
     note("transpose batched off-grid")
     check_transpose(dev, B, M, N, ldx, ldy, M * ldx + 8, N * ldy + 4, 1, 1, 0, seed=77)
