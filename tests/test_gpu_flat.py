@@ -219,3 +219,22 @@ def test_padded_rows_outside_the_span(dev, M, N, ldx, ldy, xoff, yoff):
     padding) keep the 2-D tile plan: the same results bit for bit."""
     note("no span %dx%d ldx %d ldy %d" % (M, N, ldx, ldy))
     _check_strided(dev, "affine", M, N, ldx, ldy, xoff, yoff, tm.TM_VAR_AUTO, seed=7 * M + N)
+
+
+@pytest.mark.parametrize("ld,off", [(1003, 0), (1001, 1)])
+def test_padded_rows_in_place(dev, ld, off):
+    """x == y over padded rows (the span plan): every live element mapped once, the padding between
+    rows untouched, as the oracle's out-of-place result."""
+    M, N = 777, 1000
+    n = (M - 1) * ld + N
+    xh = inputs.uniform(41 + ld, n, -8.0, 8.0)
+    X = Guarded(n, dev, offset=off, guard=LINE_GUARD_FLOATS)
+    X.upload(xh)
+    note("span in place %dx%d ld %d off %d" % (M, N, ld, off))
+    assert tm.tm_map_affine(X.ptr, ld, X.ptr, ld, M, N, 0.75, -0.25, 64, 64, 0, tm.TM_VAR_AUTO) == tm.TM_OK
+    torch.cuda.synchronize()
+    want = sentinel_host(X.buf.numel())
+    region = xh.copy()   # the padding keeps the input's values
+    oracle.map_affine(xh, ld, region, ld, M, N, 0.75, -0.25)
+    want[X.off:X.off + n] = region
+    assert np.array_equal(bits(X.host()), bits(want))
