@@ -372,3 +372,71 @@ def test_fuzz_transposes(dev):
         assert np.array_equal(bits(Y.host()), bits(want)), "case %d" % case
         assert X.guards_intact()
     assert ok >= 140
+
+
+def test_fuzz_padded_spans(dev):
+    """Padded rows with one stride in both tensors and less than a line of padding (the span plan
+    of 1 KiB items on y's 1 KiB grid when the bases sit the same distance past a 16-byte boundary,
+    the 2-D tile plan otherwise): random shapes, paddings, offsets, ops and variants, bit for bit,
+    the padding between rows untouched."""
+    rng = random.Random(4242)
+    for case in range(120):
+        op = rng.choice(["affine", "scale", "copy"])
+        variant = rng.choice([tm.TM_VAR_AUTO, tm.TM_VAR_AUTO, tm.TM_VAR_VEC4, tm.TM_VAR_SCALAR])
+        M, N = rng.randint(2, 300), rng.randint(64, 1100)
+        ld = N + rng.randint(1, 31)
+        offx = rng.choice([0, 1, 2, 3, 5, 64, 100])
+        offy = offx if rng.random() < 0.8 else rng.choice([0, 1, 2, 3])
+        note("fuzz span %d: %s M=%d N=%d ld=%d offs=%d,%d variant=%d" % (case, op, M, N, ld, offx, offy, variant))
+        n = (M - 1) * ld + N
+        xh = inputs.uniform(7000 + case, n, -8.0, 8.0)
+        X = Guarded(n, dev, offx, LINE_GUARD_FLOATS)
+        X.upload(xh)
+        Y = Guarded(n, dev, offy, LINE_GUARD_FLOATS)
+        if op == "affine":
+            st = tm.tm_map_affine(X.ptr, ld, Y.ptr, ld, M, N, 0.75, -0.25, 64, 64, 0, variant)
+        elif op == "scale":
+            st = tm.tm_scale2d(X.ptr, ld, Y.ptr, ld, M, N, 1.5, 64, 64, 0, variant)
+        else:
+            st = tm.tm_copy2d(X.ptr, ld, Y.ptr, ld, M, N, 64, 64, 0, variant)
+        vec_ok = rows16(X.ptr, M, ld) and rows16(Y.ptr, M, ld)
+        assert st == (tm.TM_OK if variant != tm.TM_VAR_VEC4 or vec_ok else tm.TM_E_ALIGN), tm.tm_status_string(st)
+        torch.cuda.synchronize()
+        want = sentinel_host(Y.buf.numel())
+        if st == tm.TM_OK:
+            region = want[Y.off:Y.off + n].copy()
+            if op == "affine":
+                oracle.map_affine(xh, ld, region, ld, M, N, 0.75, -0.25)
+            elif op == "scale":
+                oracle.scale2d(xh, ld, region, ld, M, N, 1.5)
+            else:
+                oracle.copy2d(xh, ld, region, ld, M, N)
+            want[Y.off:Y.off + n] = region
+        assert np.array_equal(bits(Y.host()), bits(want)), "case %d" % case
+        assert X.guards_intact()
+
+
+def test_fuzz_line_windows(dev):
+    """One large matrix whose y rows miss the 128-byte line grid (line-aligned y windows from a band
+    of x rows): random shapes of 4-7M elements, strides and base offsets, bit for bit."""
+    rng = random.Random(777)
+    for case in range(10):
+        N = rng.randint(40, 3000)
+        M = max(64, (rng.randint(4_200_000, 7_000_000) // N))
+        ldx = N + rng.choice([0, 1, 3, 4, 7, 32])
+        ldy = M + rng.choice([1, 2, 3, 4, 5, 17, 33])
+        offx, offy = rng.choice([0, 1, 4]), rng.choice([0, 1, 2, 3, 9])
+        note("fuzz line windows %d: M=%d N=%d ld=%d,%d offs=%d,%d" % (case, M, N, ldx, ldy, offx, offy))
+        nx, ny = (M - 1) * ldx + N, (N - 1) * ldy + M
+        xh = inputs.uniform(8000 + case, nx, -4.0, 4.0)
+        X = Guarded(nx, dev, offx)
+        X.upload(xh)
+        Y = Guarded(ny, dev, offy)
+        assert tm.tm_transpose(X.ptr, ldx, 0, Y.ptr, ldy, 0, 1, M, N, 1, 1, 0) == tm.TM_OK
+        torch.cuda.synchronize()
+        want = sentinel_host(Y.buf.numel())
+        region = want[Y.off:Y.off + Y.n].copy()
+        oracle.transpose(xh, ldx, 0, region, ldy, 0, 1, M, N)
+        want[Y.off:Y.off + Y.n] = region
+        assert np.array_equal(bits(Y.host()), bits(want)), "case %d" % case
+        assert X.guards_intact()
