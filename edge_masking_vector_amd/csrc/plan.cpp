@@ -459,7 +459,7 @@ struct RowWalk {
     int once_k = 0;     // chunks per lane of a one-batch row
 };
 
-static RowWalk row_walk(int64_t M, int64_t N, bool vec, int TC) {
+static RowWalk row_walk(int64_t M, int64_t N, bool vec, int TC, bool once_ok = true) {
     const int W = vec ? 4 : 1;
     const int64_t chunks = ceil_div(N, W);  // chunks per row
     RowWalk rw;
@@ -473,7 +473,7 @@ static RowWalk row_walk(int64_t M, int64_t N, bool vec, int TC) {
     // lanes' reach with too few rows to fill the GPU keep the multi-wave walk.
     const int K = vec ? kRowOnceK : kRowOnceKScalar;
     const bool few_long = chunks > int64_t{K} * 32 && M < kRowWideWaves;
-    if (chunks > int64_t{K} * kRowOnceMinLanes / 2 && chunks <= int64_t{K} * 64 && !few_long) {
+    if (once_ok && chunks > int64_t{K} * kRowOnceMinLanes / 2 && chunks <= int64_t{K} * 64 && !few_long) {
         rw.once = true;
         rw.once_k = K;
         rw.lpr = std::max(kRowOnceMinLanes, 1 << ilog2(ceil_div(chunks, K)));
@@ -601,7 +601,10 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
     // row does not touch), its first one to three elements masked, the walk laid out for N + 3
     // elements.  133 x 64954 at row stride 64986 read as 4-byte chunks streamed 2.8 TB/s.
     const bool shift = !vec && N > kRowShiftMinN;
-    const RowWalk rw = shift ? row_walk(M, N + 3, true, TC) : row_walk(M, N, vec, TC);
+    // (The one-batch kernel has no shifted form: such rows keep the batched walk.  One wave per
+    // 4096-float row with all 16 of its lanes' chunks in flight took the 4096 x 4096 row sums from
+    // 12.0 to 12.6 us, so rows past 512 16-byte chunks keep the batched walk too.)
+    const RowWalk rw = shift ? row_walk(M, N + 3, true, TC, false) : row_walk(M, N, vec, TC);
     const int lpr = rw.lpr;
     plan->launch = true;
     plan->op = op;
@@ -647,7 +650,7 @@ int row_walk_query(int64_t M, int64_t N, int64_t ld, int TR, int TC, int aligned
     if (aligned && !promise_holds(M, N, ld, 0, TR, TC, x, nullptr))
         return TM_E_ALIGN;
     const bool vec = rows16(x, M, ld);
-    const RowWalk rw = !vec && N > kRowShiftMinN ? row_walk(M, N + 3, true, TC) : row_walk(M, N, vec, TC);
+    const RowWalk rw = !vec && N > kRowShiftMinN ? row_walk(M, N + 3, true, TC, false) : row_walk(M, N, vec, TC);
     *lanes = rw.lpr;
     *bc = rw.bc;
     return split(N, *bc, nfull, rem);

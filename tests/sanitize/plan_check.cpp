@@ -553,8 +553,8 @@ static void check_reductions() {
         for (int64_t N : Ns)
             for (int TR : {1, 4, 16, 256})
                 for (int TC : {1, 4, 64, 256, 1024})
-                    for (int aligned = 0; aligned <= 1; ++aligned) {
-                        const int64_t ld = (N + 3) / 4 * 4;
+                    for (int aligned = 0; aligned <= 1; ++aligned)
+                      for (int64_t ld : {(N + 3) / 4 * 4, N % 4 == 0 ? N + 1 : N}) {  // rows on / off the 16-byte grid
                         for (int op : {int(tmp::kRowSum), int(tmp::kRowMax), int(tmp::kRowSoftmax)}) {
                             tmp::RowPlan p;
                             float *o = const_cast<float *>(fake(0x200000));
@@ -565,6 +565,7 @@ static void check_reductions() {
                             CHECK(p.lpr >= 1 && p.lpr <= tmp::kRowMaxLanes && (p.lpr & (p.lpr - 1)) == 0,
                                   "rows lpr %d", p.lpr);
                             CHECK(p.block == (p.lpr > 64 ? p.lpr : tmp::kBlock), "rows block %d", p.block);
+                            CHECK(!(p.once && p.shift), "rows: a shifted walk planned as one batch (N=%ld)", long(N));
                             if (p.once) {
                                 // one batch (row_once): lane g of a row takes chunks g + k * lpr for
                                 // k < once_k; chunks below whole = nfull * bc / W load unmasked and

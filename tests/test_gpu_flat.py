@@ -238,3 +238,28 @@ def test_padded_rows_in_place(dev, ld, off):
     oracle.map_affine(xh, ld, region, ld, M, N, 0.75, -0.25)
     want[X.off:X.off + n] = region
     assert np.array_equal(bits(X.host()), bits(want))
+
+
+@pytest.mark.parametrize("M,N,ldx,ldy,TM,TN,variant", [
+    (4100, 1000, 1001, 1001, 64, 64, tm.TM_VAR_AUTO),     # the bench's padded maps: one span
+    (4100, 1000, 1004, 1004, 64, 64, tm.TM_VAR_VEC4),
+    (4100, 4100, 4104, 4104, 32, 128, tm.TM_VAR_VEC4),
+    (4100, 1000, 1004, 1008, 64, 64, tm.TM_VAR_VEC4),     # ... and the 2-D tile plan
+    (4100, 4100, 4104, 4108, 32, 128, tm.TM_VAR_VEC4),
+])
+def test_bench_padded_maps_full_size(dev, M, N, ldx, ldy, TM, TN, variant):
+    """The padded-row maps the benchmark times, at their full sizes and in the same calls (ragged
+    path, the same tiles and variants), bit for bit against the oracle, padding untouched."""
+    note("bench padded map %dx%d ld %d/%d" % (M, N, ldx, ldy))
+    nx, ny = (M - 1) * ldx + N, (M - 1) * ldy + N
+    xh = inputs.matrix(inputs.ragged_input(M, N, seed=12), M, N, ldx)[:nx].copy()
+    X = Guarded(nx, dev, guard=LINE_GUARD_FLOATS)
+    X.upload(xh)
+    Y = Guarded(ny, dev, guard=LINE_GUARD_FLOATS)
+    assert tm.tm_map_affine(X.ptr, ldx, Y.ptr, ldy, M, N, 0.75, -0.25, TM, TN, 0, variant) == tm.TM_OK
+    torch.cuda.synchronize()
+    want = sentinel_host(Y.buf.numel())
+    region = want[Y.off:Y.off + ny].copy()
+    oracle.map_affine(xh, ldx, region, ldy, M, N, 0.75, -0.25)
+    want[Y.off:Y.off + ny] = region
+    assert np.array_equal(bits(Y.host()), bits(want))
