@@ -233,16 +233,20 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
         }
     }
 
-    // Padded rows (row stride ld > N, the same in both tensors, less than one 128-byte line of
-    // padding between rows, both bases the same distance past a 16-byte boundary): on the ragged
-    // path the span from y[0] to the last element is cut into 1 KiB items on y's 1 KiB grid, and
-    // each item moves 16-byte chunks with the columns past N masked (mapflat.hip, map_rows).
-    // Work items then never share a line, where 2-D tiles over rows off the line grid shared the
-    // lines at both ends of every row piece with the neighbouring items: a line written in parts
-    // by two XCDs reaches HBM3E as partial writes, which the controller turns into
-    // read-modify-writes.  Only the lines that hold padding are written in part here.
-    if (!aligned && M > 1 && ldx == ldy && ldx > N && ldx - N < kLineBytes / 4 && N >= kRowsSpanMinN &&
-        op != kChannel && (access == kVec4 || access == kScalar) &&
+    // Padded rows (row stride ld > N, the same in both tensors, both bases the same distance past a
+    // 16-byte boundary, padding under one 128-byte line or at most an eighth of the row): on the
+    // ragged path the span from y[0] to the last element is cut into 1 KiB items on y's 1 KiB grid,
+    // and each item moves 16-byte chunks with the columns past N masked (mapflat.hip, map_rows);
+    // the channel op takes each element's column as its channel.  Work items then never share a
+    // line, where 2-D tiles over rows off the line grid shared the lines at both ends of every row
+    // piece with the neighbouring items: a line written in parts by two XCDs reaches HBM3E as
+    // partial writes, which the controller turns into read-modify-writes.  Only the lines that
+    // hold padding are written in part here.  4100 x 4100 at row stride 4104: the map 33.6 ->
+    // 21.6 us; at stride 4140 (40 floats of padding) the map 33.4 us and the bias add 54.3 us
+    // under 2-D tiles.
+    const int64_t pad = ldx - N;
+    if (!aligned && M > 1 && ldx == ldy && pad > 0 && (pad < kLineBytes / 4 || pad * 8 <= N) &&
+        N >= kRowsSpanMinN && (access == kVec4 || access == kScalar) &&
         (reinterpret_cast<uintptr_t>(x) - reinterpret_cast<uintptr_t>(y)) % 16 == 0) {
         const int64_t head = static_cast<int64_t>((reinterpret_cast<uintptr_t>(y) / 4) % 256);
         const int64_t span = (M - 1) * ldx + N;
@@ -265,6 +269,12 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
             plan->N = N;
             plan->alpha = alpha;
             plan->beta = beta;
+            plan->scale = scale;
+            plan->bias = bias;
+            // a whole chunk's channels start on a column divisible by 4 when every chunk of the
+            // span does (16-byte rows of y); then both vectors load as 16-byte chunks if aligned
+            plan->cvec16 = op == kChannel && aligned_to(bias, 16) && aligned_to(scale, 16) && aligned_to(y, 16) &&
+                           ldx % 4 == 0;
             return TM_OK;
         }
     }

@@ -100,19 +100,23 @@ static void replay_flat(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld,
 
 // Padded rows in one span (mapflat.hip, map_rows): item w, lane t moves the 16-byte chunk of span
 // elements q .. q + 3, q = 256 w + 4 t - head; element f is row f / ld, column f % ld, live when the
-// column is below N.  Every load (clamped to the chunks holding the span's first and last
-// elements) must be a 16-byte aligned block of x that holds an element of the span; every live
+// column is below N.  A chunk wholly inside the padding loads the row's last live chunk; loads are
+// clamped to the chunks holding the span's first and last elements.  Every load must be a 16-byte
+// aligned block of x holding a live element (so no line of padding alone is fetched); every live
 // element must be stored exactly once and nothing else at all; whole-chunk stores must be aligned
-// blocks inside the item's 1 KiB block of y.
+// blocks inside the item's 1 KiB block of y, and for the channel op a whole chunk's channels are
+// its columns c .. c + 3 (16-byte vector loads only when c is divisible by 4).
 static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, const char *tag) {
-    CHECK(!p.aligned && M > 1 && p.ldx == ld && p.ldy == ld && ld > N && ld - N < 32 && N >= tmp::kRowsSpanMinN &&
-              p.op != tmp::kChannel && (p.access == tmp::kVec4 || p.access == tmp::kScalar),
+    const int64_t pad = ld - N;
+    CHECK(!p.aligned && M > 1 && p.ldx == ld && p.ldy == ld && pad > 0 && (pad < 32 || pad * 8 <= N) &&
+              N >= tmp::kRowsSpanMinN && (p.access == tmp::kVec4 || p.access == tmp::kScalar),
           "%s span plan outside its case", tag);
     const uintptr_t xa = reinterpret_cast<uintptr_t>(p.x), ya = reinterpret_cast<uintptr_t>(p.y);
     const int64_t span = (M - 1) * ld + N;
     CHECK(p.span == uint64_t(span) && p.head == (ya / 4) % 256 && (xa - ya) % 16 == 0 && p.ld_div.d == ld,
           "%s span geometry", tag);
     CHECK(p.nwork == uint64_t((p.head + span + 255) / 256) && p.grid >= 1 && p.grid <= p.nwork, "%s span items", tag);
+    CHECK(!p.cvec16 || (p.op == tmp::kChannel && ya % 16 == 0 && ld % 4 == 0), "%s span channel vectors", tag);
     const int32_t q_first = -int32_t(p.head & 3u);
     const int32_t q_last = int32_t(span - 1) - int32_t((span - 1 + p.head) & 3u);
     std::vector<uint8_t> hits(size_t(span), 0);
@@ -120,17 +124,29 @@ static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld,
     for (uint32_t w = 0; w < p.nwork; ++w)
         for (int t = 0; t < 64; ++t) {
             const int32_t q = int32_t(w * 256u + 4u * t) - int32_t(p.head);
-            const int32_t qc = q < q_first ? q_first : (q > q_last ? q_last : q);
-            // aligned, and holding an element of the span
-            if ((xa + 4 * int64_t(qc)) % 16 != 0 || qc + 3 < 0 || qc >= span)
-                bad_load = true;
             const uint32_t c = q > 0 ? umulhi_mod(uint32_t(q), p.ld_div) : 0u;
             if (q > 0 && c != uint32_t(q % ld))
+                bad_load = true;
+            int32_t qa = q;
+            if (q >= 0 && c >= N && c + 3 < ld) {
+                const int32_t last = q - int32_t(c) + int32_t(N) - 1;
+                qa = last - int32_t((uint32_t(last) + p.head) & 3u);
+            }
+            qa = qa < q_first ? q_first : (qa > q_last ? q_last : qa);
+            // aligned, and holding a live element of the span
+            bool live_in_load = false;
+            for (int e = 0; e < 4; ++e) {
+                const int64_t f = int64_t(qa) + e;
+                live_in_load = live_in_load || (f >= 0 && f < span && f % ld < N);
+            }
+            if ((xa + 4 * int64_t(qa)) % 16 != 0 || !live_in_load)
                 bad_load = true;
             if (q >= 0 && int64_t(q) + 3 < span && c + 3 < N) {
                 const uintptr_t blk = ya + 4 * (int64_t(w) * 256 - p.head);
                 if (blk % 1024 != 0 || (ya + 4 * int64_t(q)) != blk + 16 * uintptr_t(t))
                     bad_store = true;
+                if (p.cvec16 && c % 4 != 0)
+                    bad_store = true;  // a 16-byte channel-vector load off its grid
                 for (int i = 0; i < 4; ++i)
                     ++hits[size_t(q + i)];
             } else {
@@ -146,7 +162,7 @@ static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld,
                 }
             }
         }
-    CHECK(!bad_load, "%s span: a load off the view's 16-byte blocks (or a wrong column)", tag);
+    CHECK(!bad_load, "%s span: a load off the view's live 16-byte blocks (or a wrong column)", tag);
     CHECK(!bad_store, "%s span: a misplaced store", tag);
     for (int64_t f = 0; f < span; ++f) {
         const bool live = f % ld < N;
@@ -272,7 +288,7 @@ static void check_maps() {
     const uintptr_t bases[] = {0x100000, 0x100004, 0x100010};  // line-aligned, 4-byte, 16-byte
     for (int64_t M : Ms)
         for (int64_t N : Ns) {
-            const int64_t lds[] = {N, N + 3, (N + 3) / 4 * 4, (N + 31) / 32 * 32};
+            const int64_t lds[] = {N, N + 3, (N + 3) / 4 * 4, (N + 31) / 32 * 32, N + 40, N + N / 8, N + N / 8 + 1};
             for (int64_t ld : lds)
                 for (int TM : TMs)
                     for (int TN : TNs)

@@ -263,3 +263,47 @@ def test_bench_padded_maps_full_size(dev, M, N, ldx, ldy, TM, TN, variant):
     oracle.map_affine(xh, ldx, region, ldy, M, N, 0.75, -0.25)
     want[Y.off:Y.off + ny] = region
     assert np.array_equal(bits(Y.host()), bits(want))
+
+
+@pytest.mark.parametrize("M,N,ld,off,boff,with_scale", [
+    (300, 1000, 1004, 0, 0, False),   # 16-byte rows, bias as 16-byte vectors
+    (300, 1000, 1004, 0, 1, True),    # vectors off their 16-byte grid: gathered one by one
+    (257, 777, 800, 3, 0, True),      # rows off the 16-byte grid
+    (100, 4100, 4140, 0, 0, False),   # 40 floats of padding: chunks wholly inside it load live data
+    (64, 2000, 2250, 1, 2, True),     # padding of an eighth of the row
+])
+def test_padded_rows_channel_span(dev, M, N, ld, off, boff, with_scale):
+    """The per-channel op over padded rows in one span: element (i, j) takes channel j, bit for
+    bit against the oracle (one fmaf, scale 1 when absent), the padding untouched."""
+    note("span channel %dx%d ld %d off %d boff %d scale %d" % (M, N, ld, off, boff, with_scale))
+    n = (M - 1) * ld + N
+    xh = inputs.uniform(61 + ld, n, -8.0, 8.0)
+    bh = inputs.uniform(62 + ld, N, -1.0, 1.0)
+    sh = inputs.uniform(63 + ld, N, 0.5, 1.5) if with_scale else None
+    X = Guarded(n, dev, offset=off, guard=LINE_GUARD_FLOATS)
+    X.upload(xh)
+    Y = Guarded(n, dev, offset=off, guard=LINE_GUARD_FLOATS)
+    B = Guarded(N, dev, offset=boff)
+    B.upload(bh)
+    S = None
+    if with_scale:
+        S = Guarded(N, dev, offset=boff)
+        S.upload(sh)
+    st = tm.tm_channel_affine(X.ptr, ld, S.ptr if S is not None else None, B.ptr, Y.ptr, ld, M, N, 64, 64, 0,
+                              tm.TM_VAR_AUTO)
+    assert st == tm.TM_OK, tm.tm_status_string(st)
+    torch.cuda.synchronize()
+    want = sentinel_host(Y.buf.numel())
+    region = want[Y.off:Y.off + n].copy()
+    oracle.channel_affine(xh, ld, sh, bh, region, ld, M, N)
+    want[Y.off:Y.off + n] = region
+    assert np.array_equal(bits(Y.host()), bits(want))
+    assert X.guards_intact() and B.guards_intact()
+
+
+@pytest.mark.parametrize("M,N,ld,off", [(100, 4100, 4140, 0), (300, 1000, 1125, 2), (41, 561, 593, 1)])
+def test_padded_rows_wide_padding(dev, M, N, ld, off):
+    """Padding of a line or more (at most an eighth of the row) is still one span; chunks wholly
+    inside it load the row's last live chunk and store nothing."""
+    note("span wide padding %dx%d ld %d off %d" % (M, N, ld, off))
+    _check_strided(dev, "affine", M, N, ld, ld, off, off, tm.TM_VAR_AUTO, seed=M * 7 + ld)

@@ -375,16 +375,17 @@ def test_fuzz_transposes(dev):
 
 
 def test_fuzz_padded_spans(dev):
-    """Padded rows with one stride in both tensors and less than a line of padding (the span plan
-    of 1 KiB items on y's 1 KiB grid when the bases sit the same distance past a 16-byte boundary,
-    the 2-D tile plan otherwise): random shapes, paddings, offsets, ops and variants, bit for bit,
-    the padding between rows untouched."""
+    """Padded rows with one stride in both tensors (the span plan of 1 KiB items on y's 1 KiB grid
+    when the bases sit the same distance past a 16-byte boundary and the padding is under a line
+    or at most an eighth of the row, the 2-D tile plan otherwise): random shapes, paddings,
+    offsets, ops (the channel op too) and variants, bit for bit, the padding between rows
+    untouched."""
     rng = random.Random(4242)
-    for case in range(120):
-        op = rng.choice(["affine", "scale", "copy"])
+    for case in range(150):
+        op = rng.choice(["affine", "scale", "copy", "channel", "channel_scale"])
         variant = rng.choice([tm.TM_VAR_AUTO, tm.TM_VAR_AUTO, tm.TM_VAR_VEC4, tm.TM_VAR_SCALAR])
         M, N = rng.randint(2, 300), rng.randint(64, 1100)
-        ld = N + rng.randint(1, 31)
+        ld = N + (rng.randint(1, 31) if rng.random() < 0.7 else rng.randint(32, max(32, N // 8 + 3)))
         offx = rng.choice([0, 1, 2, 3, 5, 64, 100])
         offy = offx if rng.random() < 0.8 else rng.choice([0, 1, 2, 3])
         note("fuzz span %d: %s M=%d N=%d ld=%d offs=%d,%d variant=%d" % (case, op, M, N, ld, offx, offy, variant))
@@ -393,7 +394,18 @@ def test_fuzz_padded_spans(dev):
         X = Guarded(n, dev, offx, LINE_GUARD_FLOATS)
         X.upload(xh)
         Y = Guarded(n, dev, offy, LINE_GUARD_FLOATS)
-        if op == "affine":
+        sh = None
+        if op.startswith("channel"):
+            bh = inputs.uniform(7500 + case, N, -1.0, 1.0)
+            Bv = Guarded(N, dev, rng.choice([0, 1, 4]))
+            Bv.upload(bh)
+            if op == "channel_scale":
+                sh = inputs.uniform(7700 + case, N, 0.5, 1.5)
+                Sv = Guarded(N, dev, rng.choice([0, 4]))
+                Sv.upload(sh)
+            st = tm.tm_channel_affine(X.ptr, ld, Sv.ptr if sh is not None else None, Bv.ptr, Y.ptr, ld, M, N,
+                                      64, 64, 0, variant)
+        elif op == "affine":
             st = tm.tm_map_affine(X.ptr, ld, Y.ptr, ld, M, N, 0.75, -0.25, 64, 64, 0, variant)
         elif op == "scale":
             st = tm.tm_scale2d(X.ptr, ld, Y.ptr, ld, M, N, 1.5, 64, 64, 0, variant)
@@ -409,8 +421,10 @@ def test_fuzz_padded_spans(dev):
                 oracle.map_affine(xh, ld, region, ld, M, N, 0.75, -0.25)
             elif op == "scale":
                 oracle.scale2d(xh, ld, region, ld, M, N, 1.5)
-            else:
+            elif op == "copy":
                 oracle.copy2d(xh, ld, region, ld, M, N)
+            else:
+                oracle.channel_affine(xh, ld, sh, bh, region, ld, M, N)
             want[Y.off:Y.off + n] = region
         assert np.array_equal(bits(Y.host()), bits(want)), "case %d" % case
         assert X.guards_intact()
