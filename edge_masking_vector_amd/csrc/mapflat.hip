@@ -133,53 +133,75 @@ __global__ __launch_bounds__(flat_threads<MODE>()) void map_flat(const float *__
 // distance past a 16-byte boundary, so the chunk is aligned on both sides).  A chunk whose four
 // elements are live is stored whole through a buffer resource spanning the block; at a row's end
 // or the span's ends the live elements are stored one by one.  Every load holds a live element:
-// loads are clamped to the chunks that hold y[0] and the span's last element, and a chunk wholly
-// inside the padding between two rows loads the row's last live chunk instead (already read by
-// another lane), so no line of padding alone is fetched.  Columns come from a multiply-high
+// loads are clamped to the chunks that hold y[0] and the span's last element, and with a line or
+// more of padding (WIDE) a chunk wholly inside the padding between two rows loads the row's last
+// live chunk instead (already read by another lane), so no line of padding alone is fetched.
+// (Under a line of padding every line holds live elements, and the load is issued before the
+// column is known.)  Columns come from a multiply-high
 // remainder by ld (rows of at least 64 floats: at most one row boundary per chunk).
 // The channel op (OP = kChannel) takes element (row, column c)'s channel c: y = fmaf(x, scale[c],
 // bias[c]), scale 1 when absent; a whole chunk's four channels are one 16-byte load of each vector
 // when cvec16 (both vectors 16-byte aligned and every chunk starting on a column divisible by 4).
-template <int OP>
-__global__ __launch_bounds__(64) void map_rows(const float *__restrict__ x, float *__restrict__ y, float alpha,
-                                               float beta, uint32_t nwork, uint32_t head, uint32_t span,
-                                               uint32_t ld, uint32_t N, uint64_t c_ld,
-                                               const float *__restrict__ scale, const float *__restrict__ bias,
-                                               uint32_t cvec16) {
+template <int OP, bool WIDE>
+__device__ __forceinline__ void rows_body(const float *__restrict__ x, float *__restrict__ y, float alpha, float beta,
+                                          uint32_t nwork, uint32_t head, uint32_t span, uint32_t ld, uint32_t N,
+                                          uint64_t c_ld, const float *__restrict__ scale,
+                                          const float *__restrict__ bias, uint32_t cvec16) {
     const int t = threadIdx.x;
     const int32_t q_first = -int32_t(head & 3u);                         // the chunk holding y[0]
     const int32_t q_last = int32_t(span - 1) - int32_t((span - 1 + head) & 3u);  // ... the last element
     for (uint32_t w = blockIdx.x; w < nwork; w += gridDim.x) {
         const int32_t q = int32_t(w * 256u + 4u * t) - int32_t(head);
-        const uint32_t c = q > 0 ? fast_mod(uint32_t(q), c_ld, ld) : 0u;  // column of element q (q >= 0)
         int32_t qa = q;
-        if (q >= 0 && c >= N && c + 3 < ld) {  // padding only: the row's last live chunk
-            const int32_t last = q - int32_t(c) + int32_t(N) - 1;
-            qa = last - int32_t((uint32_t(last) + head) & 3u);
+        f4 xv;
+        if constexpr (!WIDE) {
+            qa = qa < q_first ? q_first : (qa > q_last ? q_last : qa);
+            xv = ld16_nt(x + qa);
         }
-        qa = qa < q_first ? q_first : (qa > q_last ? q_last : qa);
-        const f4 xv = ld16_nt(x + qa);
-        const __amdgpu_buffer_rsrc_t ry = segment_rsrc(y + (int64_t(w) * 256 - head), kItemFloats * 4);
-        if (q >= 0 && uint32_t(q) + 3 < span && c + 3 < N) {
-            f4 v;
-            if constexpr (OP == tmp::kChannel) {
-                f4 sv = f4(1.0f), bv;
-                if (cvec16) {
-                    bv = ld16(bias + c);
-                    if (scale)
-                        sv = ld16(scale + c);
-                } else {
-                    bv = f4{bias[c], bias[c + 1], bias[c + 2], bias[c + 3]};
-                    if (scale)
-                        sv = f4{scale[c], scale[c + 1], scale[c + 2], scale[c + 3]};
-                }
-                v.x = __builtin_fmaf(xv.x, sv.x, bv.x);
-                v.y = __builtin_fmaf(xv.y, sv.y, bv.y);
-                v.z = __builtin_fmaf(xv.z, sv.z, bv.z);
-                v.w = __builtin_fmaf(xv.w, sv.w, bv.w);
-            } else {
-                v = op4<OP>(xv, alpha, beta);
+        const uint32_t c = q > 0 ? fast_mod(uint32_t(q), c_ld, ld) : 0u;  // column of element q (q >= 0)
+        if constexpr (WIDE) {
+            if (q >= 0 && c >= N && c + 3 < ld) {  // padding only: the row's last live chunk
+                const int32_t last = q - int32_t(c) + int32_t(N) - 1;
+                qa = last - int32_t((uint32_t(last) + head) & 3u);
             }
+            qa = qa < q_first ? q_first : (qa > q_last ? q_last : qa);
+            xv = ld16_nt(x + qa);
+        }
+        const __amdgpu_buffer_rsrc_t ry = segment_rsrc(y + (int64_t(w) * 256 - head), kItemFloats * 4);
+        const bool whole = q >= 0 && uint32_t(q) + 3 < span && c + 3 < N;
+        uint32_t col[4];  // the chunk's columns (q < 0: f < 4, row 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t ci = q >= 0 ? c + i : uint32_t(q + i);
+            col[i] = ci >= ld ? ci - ld : ci;
+        }
+        // The result of every lane is computed before the stores, whole or not: with the
+        // arithmetic inside the masked branch, each lane there waited for its first element's
+        // store before the next (the 4100 x 1000 map at row stride 1001: 8.1 against 7.5 us).
+        f4 v;
+        if constexpr (OP == tmp::kChannel) {
+            f4 sv = f4(1.0f), bv;
+            if (cvec16 && whole) {
+                bv = ld16(bias + c);
+                if (scale)
+                    sv = ld16(scale + c);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t cc = col[i] < N ? col[i] : N - 1;  // a dead element reads a live channel
+                    bv[i] = bias[cc];
+                    if (scale)
+                        sv[i] = scale[cc];
+                }
+            }
+            v.x = __builtin_fmaf(xv.x, sv.x, bv.x);
+            v.y = __builtin_fmaf(xv.y, sv.y, bv.y);
+            v.z = __builtin_fmaf(xv.z, sv.z, bv.z);
+            v.w = __builtin_fmaf(xv.w, sv.w, bv.w);
+        } else {
+            v = op4<OP>(xv, alpha, beta);
+        }
+        if (whole) {
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), ry, t * 16, 0, kFlatStorePolicy);
         } else {
             // the same buffer and policy as the whole chunks, which write the rest of these lines
@@ -188,20 +210,36 @@ __global__ __launch_bounds__(64) void map_rows(const float *__restrict__ x, floa
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int32_t f = q + i;
-                uint32_t col = q >= 0 ? c + i : uint32_t(f);  // q < 0: f < 4, row 0
-                col = col >= ld ? col - ld : col;
-                const float e = xv[i];  // (a bit cast of the vector element itself stored element 0)
-                if (f >= 0 && uint32_t(f) < span && col < N) {
-                    float r;
-                    if constexpr (OP == tmp::kChannel)
-                        r = __builtin_fmaf(e, scale ? scale[col] : 1.0f, bias[col]);
-                    else
-                        r = op1<OP>(e, alpha, beta);
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(r), ry, (t * 4 + i) * 4, 0, kFlatStorePolicy);
-                }
+                const float e = v[i];  // (a bit cast of the vector element itself stored element 0)
+                if (f >= 0 && uint32_t(f) < span && col[i] < N)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), ry, (t * 4 + i) * 4, 0, kFlatStorePolicy);
             }
         }
     }
+}
+
+// The maps take ten arguments (the channel vectors would add three to every dispatch's argument
+// block: 1-1.5% on these kernels); the channel op has a kernel of its own.
+template <int OP, bool WIDE>
+__global__ __launch_bounds__(64) void map_rows(const float *__restrict__ x, float *__restrict__ y, float alpha,
+                                               float beta, uint32_t nwork, uint32_t head, uint32_t span,
+                                               uint32_t ld, uint32_t N, uint64_t c_ld) {
+    rows_body<OP, WIDE>(x, y, alpha, beta, nwork, head, span, ld, N, c_ld, nullptr, nullptr, 0u);
+}
+
+template <bool WIDE>
+__global__ __launch_bounds__(64) void map_rows_channel(const float *__restrict__ x, float *__restrict__ y,
+                                                       uint32_t nwork, uint32_t head, uint32_t span, uint32_t ld,
+                                                       uint32_t N, uint64_t c_ld, const float *__restrict__ scale,
+                                                       const float *__restrict__ bias, uint32_t cvec16) {
+    rows_body<tmp::kChannel, WIDE>(x, y, 0.0f, 0.0f, nwork, head, span, ld, N, c_ld, scale, bias, cvec16);
+}
+
+template <bool WIDE>
+const void *pick_rows(int op) {
+    return op == tmp::kAffine  ? reinterpret_cast<const void *>(&map_rows<tmp::kAffine, WIDE>)
+           : op == tmp::kScale ? reinterpret_cast<const void *>(&map_rows<tmp::kScale, WIDE>)
+                               : reinterpret_cast<const void *>(&map_rows<tmp::kCopy, WIDE>);
 }
 
 template <int OP>
@@ -222,13 +260,17 @@ hipError_t launch_map_flat(const tmp::MapPlan &p, hipStream_t stream) {
     if (p.rows) {
         uint32_t nwork = p.nwork, head = p.head, span = p.span, ld = p.ld_div.d, N = static_cast<uint32_t>(p.N);
         uint64_t c_ld = p.ld_div.c;
-        const float *scale = p.scale, *bias = p.bias;
-        uint32_t cvec16 = p.cvec16 ? 1u : 0u;
-        void *args[] = {&x, &y, &alpha, &beta, &nwork, &head, &span, &ld, &N, &c_ld, &scale, &bias, &cvec16};
-        const void *fn = p.op == tmp::kAffine  ? reinterpret_cast<const void *>(&map_rows<tmp::kAffine>)
-                         : p.op == tmp::kScale ? reinterpret_cast<const void *>(&map_rows<tmp::kScale>)
-                         : p.op == tmp::kCopy  ? reinterpret_cast<const void *>(&map_rows<tmp::kCopy>)
-                                               : reinterpret_cast<const void *>(&map_rows<tmp::kChannel>);
+        const bool wide = p.ldx - p.N >= 32;
+        if (p.op == tmp::kChannel) {
+            const float *scale = p.scale, *bias = p.bias;
+            uint32_t cvec16 = p.cvec16 ? 1u : 0u;
+            void *cargs[] = {&x, &y, &nwork, &head, &span, &ld, &N, &c_ld, &scale, &bias, &cvec16};
+            const void *cfn = wide ? reinterpret_cast<const void *>(&map_rows_channel<true>)
+                                   : reinterpret_cast<const void *>(&map_rows_channel<false>);
+            return hipLaunchKernel(cfn, dim3(p.grid), dim3(64), cargs, 0, stream);
+        }
+        void *args[] = {&x, &y, &alpha, &beta, &nwork, &head, &span, &ld, &N, &c_ld};
+        const void *fn = wide ? pick_rows<true>(p.op) : pick_rows<false>(p.op);
         return hipLaunchKernel(fn, dim3(p.grid), dim3(64), args, 0, stream);
     }
     uint32_t nwhole = p.flat_last == 256 ? p.nwork : p.nwork - 1;

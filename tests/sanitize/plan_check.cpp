@@ -100,9 +100,10 @@ static void replay_flat(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld,
 
 // Padded rows in one span (mapflat.hip, map_rows): item w, lane t moves the 16-byte chunk of span
 // elements q .. q + 3, q = 256 w + 4 t - head; element f is row f / ld, column f % ld, live when the
-// column is below N.  A chunk wholly inside the padding loads the row's last live chunk; loads are
-// clamped to the chunks holding the span's first and last elements.  Every load must be a 16-byte
-// aligned block of x holding a live element (so no line of padding alone is fetched); every live
+// column is below N.  With a line or more of padding a chunk wholly inside it loads the row's last
+// live chunk; loads are clamped to the chunks holding the span's first and last elements.  Every
+// load must be a 16-byte aligned block of x inside a 128-byte line that holds a live element (so
+// no line of padding alone is fetched, and no load leaves the view's lines); every live
 // element must be stored exactly once and nothing else at all; whole-chunk stores must be aligned
 // blocks inside the item's 1 KiB block of y, and for the channel op a whole chunk's channels are
 // its columns c .. c + 3 (16-byte vector loads only when c is divisible by 4).
@@ -128,15 +129,16 @@ static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld,
             if (q > 0 && c != uint32_t(q % ld))
                 bad_load = true;
             int32_t qa = q;
-            if (q >= 0 && c >= N && c + 3 < ld) {
+            if (pad >= 32 && q >= 0 && c >= N && c + 3 < ld) {
                 const int32_t last = q - int32_t(c) + int32_t(N) - 1;
                 qa = last - int32_t((uint32_t(last) + p.head) & 3u);
             }
             qa = qa < q_first ? q_first : (qa > q_last ? q_last : qa);
-            // aligned, and holding a live element of the span
+            // aligned, and inside a line of x that holds a live element of the span
             bool live_in_load = false;
-            for (int e = 0; e < 4; ++e) {
-                const int64_t f = int64_t(qa) + e;
+            const uintptr_t line = (xa + 4 * int64_t(qa)) / 128 * 128;
+            for (int e = 0; e < 32; ++e) {
+                const int64_t f = (int64_t(line) - int64_t(xa)) / 4 + e;
                 live_in_load = live_in_load || (f >= 0 && f < span && f % ld < N);
             }
             if ((xa + 4 * int64_t(qa)) % 16 != 0 || !live_in_load)
