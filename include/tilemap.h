@@ -104,9 +104,10 @@ typedef enum {
 
 /* ---- element-wise maps over tiles --------------------------------------------------------------
  * x: input, M x N, row stride ldx.  y: output, M x N, row stride ldy.  TM, TN: tile.  aligned: 0|1.
- * variant: tm_variant.  The tile is what the alignment promise is made for and, on the ragged
- * path, what decides which chunks take the masked code; how the work is cut into workgroups is
- * the library's choice and never changes a result. */
+ * variant: tm_variant.  The tile is what the alignment promise is made for.  How the work is cut
+ * into workgroups, and which chunks take the masked code on the ragged path (the view's own edges:
+ * nothing outside the M x N view is stored, and padding between rows is never written), is the
+ * library's choice and never changes a result. */
 
 /* y[i,j] = fmaf(x[i,j], alpha, beta): one correctly rounded multiply-add per element
  * ([P35] "The exercise": out = a*2 + 1; generalised to alpha, beta). */
