@@ -1,4 +1,4 @@
-"""Reductions and the transpose on a tensor of more than 2**31 elements (64-bit addressing):
+"""Reductions, the transpose and a padded-row map on a tensor of more than 2**31 elements (64-bit addressing):
 65792 x 32768 f32 (8.6 GB), built on the device by tiling one seeded block of 64 rows, so that
 any row is known on the host.  Sampled rows (including those around element 2**31 and the last
 ones) are checked against the oracle; column sums against the oracle's sums of the block times
@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from edge_masking_vector_amd import inputs
-from gpu_helpers import bits, sum_tol
+from gpu_helpers import SENTINEL, bits, sum_tol
 
 pytestmark = pytest.mark.gpu
 tm = pytest.importorskip("edge_masking_vector_amd.tilemap")
@@ -116,5 +116,29 @@ def test_transpose_beyond_2g(big):
         got = y[j].cpu().numpy()                 # y row j = x column j
         want = np.tile(B[:, j], M // BLK)
         assert np.array_equal(bits(got), bits(want)), j
+    del y
+    torch.cuda.empty_cache()
+
+
+def test_padded_map_near_and_beyond_2g(big):
+    """The affine map over the big tensor read as padded rows (N - 5 of every N floats): with
+    64000 rows the view is one span of just under 2**31 floats (32-bit span indexes near their
+    limit), with every row it is more, and the 2-D tile plan takes it.  Sampled rows bit for bit
+    against the oracle, the 5 padding floats of each and the rows past the view untouched."""
+    dev, x, blk = big
+    Np = N - 5
+    y = torch.empty(M, N, dtype=torch.float32, device=dev)
+    for Mr in (64000, M):
+        y.fill_(float(SENTINEL))
+        note("padded map %dx%d at stride %d" % (Mr, Np, N))
+        assert tm.tm_map_affine(x, N, y, N, Mr, Np, 0.75, -0.25, 64, 64, 0, tm.TM_VAR_AUTO) == tm.TM_OK
+        torch.cuda.synchronize()
+        for r in sorted(set(ROWS + (Mr - 1, min(Mr, M - 1)))):
+            got = y[r].cpu().numpy()
+            want = np.full(N, SENTINEL, np.float32)
+            if r < Mr:
+                row = block_row(blk, r)
+                oracle.map_affine(row, N, want, N, 1, Np, 0.75, -0.25)
+            assert np.array_equal(bits(got), bits(want)), (Mr, r)
     del y
     torch.cuda.empty_cache()
