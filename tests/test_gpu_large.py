@@ -142,3 +142,24 @@ def test_padded_map_near_and_beyond_2g(big):
             assert np.array_equal(bits(got), bits(want)), (Mr, r)
     del y
     torch.cuda.empty_cache()
+
+
+def test_transpose_off_the_line_grid_beyond_2g(big):
+    """The transpose of the big tensor into y rows of stride M + 3 (off the 128-byte line grid):
+    line-aligned y windows with 64-bit addresses; sampled y rows bit for bit, their 3 padding
+    floats untouched."""
+    dev, x, blk = big
+    ldy = M + 3
+    note("transpose %dx%d to y stride %d" % (M, N, ldy))
+    y = torch.empty(N * ldy, dtype=torch.float32, device=dev)
+    y.fill_(float(SENTINEL))
+    assert tm.tm_transpose(x, N, 0, y, ldy, 0, 1, M, N, 1, 1, 0) == tm.TM_OK
+    torch.cuda.synchronize()
+    B = blk.reshape(BLK, N)
+    for j in (0, 1, 31, 32, 16383, 16384, N - 1):
+        got = y[j * ldy:(j + 1) * ldy].cpu().numpy() if j < N - 1 else y[j * ldy:].cpu().numpy()
+        want = np.full(got.size, SENTINEL, np.float32)
+        want[:M] = np.tile(B[:, j], M // BLK)
+        assert np.array_equal(bits(got), bits(want)), j
+    del y
+    torch.cuda.empty_cache()
