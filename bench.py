@@ -378,11 +378,12 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
               "y = fmaf(x, 0.75, -0.25), 64x64 tiles; rows contiguous (row stride N), so the view is "
               "planned as one flat row whose only ragged edge is its end")
         del xs, ys
-    # the same ragged map over padded rows.  With one row stride in both tensors (and less than a
-    # line of padding) the view is one span of 1 KiB items on y's 1 KiB grid whose columns past N
-    # are masked: rows off the 16-byte grid (row stride 1001), on it (1004), and a scale-sized
-    # view (4100 x 4100 at row stride 4104).  With different strides in x and y the 2-D tile plan
-    # runs, and its edge tiles (the bottom 4 rows, the right 40 or 4 columns) take the masked body.
+    # the same ragged map over padded rows.  With padding under a line or at most an eighth of a
+    # row the view is one span of 1 KiB items on y's 1 KiB grid whose columns past N are masked:
+    # rows off the 16-byte grid (row stride 1001), on it (1004), a scale-sized view (4100 x 4100
+    # at row stride 4104), and strides that differ between x and y (rows of 1024 floats or more).
+    # With different strides over narrower rows, or wider padding of y, the 2-D tile plan runs,
+    # and its edge tiles (the bottom 4 rows, the right 40 or 4 columns) take the masked body.
     for (M, N, ldx, ldy, TM, TN, var, name, what) in (
             (4100, 1000, 1001, 1001, 64, 64, tm.TM_VAR_AUTO, "affine_4100x1000_ld1001_ragged_2d",
              "one span of 1 KiB items, columns past N masked (rows off the 16-byte grid)"),
@@ -390,11 +391,14 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
              "one span of 1 KiB items, columns past N masked"),
             (4100, 4100, 4104, 4104, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ld4104_ragged_2d",
              "one span of 1 KiB items, columns past N masked"),
+            (4100, 4100, 4104, 4108, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ldx4104_ldy4108_ragged_2d",
+             "one span over y, x's rows 4 floats shorter"),
             (4100, 1000, 1004, 1008, 64, 64, tm.TM_VAR_VEC4, "affine_4100x1000_ldx1004_ldy1008_ragged_tiles",
-             "the 2-D tile plan: 16-byte chunks, 4-row bottom and 64x40 right-edge tiles masked"),
-            (4100, 4100, 4104, 4108, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ldx4104_ldy4108_ragged_tiles",
-             "the 2-D tile plan: 16-byte chunks, 32x128 tiles, 4-row bottom and 4-column right edge "
-             "tiles masked")):
+             "the 2-D tile plan (different strides, rows under 1024 floats): 16-byte chunks, 4-row "
+             "bottom and 64x40 right-edge tiles masked"),
+            (4100, 4100, 4104, 4700, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ldx4104_ldy4700_ragged_tiles",
+             "the 2-D tile plan (y padding over an eighth of the row): 16-byte chunks, 32x128 tiles, "
+             "4-row bottom and 4-column right edge tiles masked")):
         xh = inputs.matrix(inputs.ragged_input(M, N, seed=12), M, N, ldx)
         nb = 2 * M * N * 4
         R = sets_for(M * ldx * 4 + M * ldy * 4)

@@ -142,30 +142,57 @@ __global__ __launch_bounds__(flat_threads<MODE>()) void map_flat(const float *__
 // The channel op (OP = kChannel) takes element (row, column c)'s channel c: y = fmaf(x, scale[c],
 // bias[c]), scale 1 when absent; a whole chunk's four channels are one 16-byte load of each vector
 // when cvec16 (both vectors 16-byte aligned and every chunk starting on a column divisible by 4).
-template <int OP, bool WIDE>
+template <int OP, bool WIDE, bool DIFF>
 __device__ __forceinline__ void rows_body(const float *__restrict__ x, float *__restrict__ y, float alpha, float beta,
                                           uint32_t nwork, uint32_t head, uint32_t span, uint32_t ld, uint32_t N,
                                           uint64_t c_ld, const float *__restrict__ scale,
-                                          const float *__restrict__ bias, uint32_t cvec16) {
+                                          const float *__restrict__ bias, uint32_t cvec16, int32_t dld,
+                                          int32_t x_last) {
     const int t = threadIdx.x;
     const int32_t q_first = -int32_t(head & 3u);                         // the chunk holding y[0]
     const int32_t q_last = int32_t(span - 1) - int32_t((span - 1 + head) & 3u);  // ... the last element
     for (uint32_t w = blockIdx.x; w < nwork; w += gridDim.x) {
         const int32_t q = int32_t(w * 256u + 4u * t) - int32_t(head);
-        int32_t qa = q;
-        f4 xv;
-        if constexpr (!WIDE) {
-            qa = qa < q_first ? q_first : (qa > q_last ? q_last : qa);
-            xv = ld16_nt(x + qa);
+        f4 xv, xn;  // x's chunk for the span elements q .. q + 3; (DIFF) the next row's part
+        if constexpr (!WIDE && !DIFF) {
+            xv = ld16_nt(x + (q < q_first ? q_first : (q > q_last ? q_last : q)));
         }
-        const uint32_t c = q > 0 ? fast_mod(uint32_t(q), c_ld, ld) : 0u;  // column of element q (q >= 0)
-        if constexpr (WIDE) {
-            if (q >= 0 && c >= N && c + 3 < ld) {  // padding only: the row's last live chunk
+        uint32_t r = 0, c = 0;  // row and column of element q (q >= 0)
+        if (q > 0) {
+            if constexpr (DIFF) {
+                r = fast_div(uint32_t(q), c_ld, ld);
+                c = uint32_t(q) - r * ld;
+            } else {
+                c = fast_mod(uint32_t(q), c_ld, ld);
+            }
+        }
+        if constexpr (WIDE || DIFF) {
+            // x index of the chunk: the span's own index shifted by dld per row (DIFF); a chunk
+            // wholly inside y's padding loads the row's last live chunk; the span's ends clamp
+            int32_t qa = q;
+            if (q >= 0 && c >= N && c + 3 < ld) {
                 const int32_t last = q - int32_t(c) + int32_t(N) - 1;
                 qa = last - int32_t((uint32_t(last) + head) & 3u);
             }
-            qa = qa < q_first ? q_first : (qa > q_last ? q_last : qa);
-            xv = ld16_nt(x + qa);
+            int32_t xa = DIFF ? qa + int32_t(r) * dld : qa;
+            xa = q < q_first ? q_first : (q > q_last ? (DIFF ? x_last : q_last) : xa);
+            if constexpr (DIFF) {
+                // elements past the row's end belong to the next row, dld further on in x; when
+                // none of the chunk's elements is live in its own row, both loads take the next
+                // row's chunk (x's padding past the row may hold no live element in its line)
+                const bool cross = q >= 0 && c + 3 >= ld && int64_t(q) - c + ld < int64_t(span);
+                const int32_t xb = cross ? xa + dld : xa;
+                if (cross && c >= N)
+                    xa = xb;
+                xv = ld16_nt(x + xa);
+                // the second load only in waves where a chunk crosses a row's end (a wave-uniform
+                // test; chunks cross row ends only when y's rows start off the 16-byte grid)
+                xn = xv;
+                if (__builtin_amdgcn_ballot_w64(cross) != 0)
+                    xn = ld16_nt(x + xb);
+            } else {
+                xv = ld16_nt(x + xa);
+            }
         }
         const __amdgpu_buffer_rsrc_t ry = segment_rsrc(y + (int64_t(w) * 256 - head), kItemFloats * 4);
         const bool whole = q >= 0 && uint32_t(q) + 3 < span && c + 3 < N;
@@ -173,6 +200,10 @@ __device__ __forceinline__ void rows_body(const float *__restrict__ x, float *__
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t ci = q >= 0 ? c + i : uint32_t(q + i);
+            if constexpr (DIFF) {
+                if (q >= 0 && ci >= ld)
+                    xv[i] = xn[i];
+            }
             col[i] = ci >= ld ? ci - ld : ci;
         }
         // The result of every lane is computed before the stores, whole or not: with the
@@ -218,21 +249,33 @@ __device__ __forceinline__ void rows_body(const float *__restrict__ x, float *__
     }
 }
 
-// The maps take ten arguments (the channel vectors would add three to every dispatch's argument
-// block: 1-1.5% on these kernels); the channel op has a kernel of its own.
+// The maps over one stride take ten arguments (the channel vectors and the second stride would
+// add to every dispatch's argument block: three more cost these kernels 1-1.5%); the channel op
+// and different strides have kernels of their own.
 template <int OP, bool WIDE>
 __global__ __launch_bounds__(64) void map_rows(const float *__restrict__ x, float *__restrict__ y, float alpha,
                                                float beta, uint32_t nwork, uint32_t head, uint32_t span,
                                                uint32_t ld, uint32_t N, uint64_t c_ld) {
-    rows_body<OP, WIDE>(x, y, alpha, beta, nwork, head, span, ld, N, c_ld, nullptr, nullptr, 0u);
+    rows_body<OP, WIDE, false>(x, y, alpha, beta, nwork, head, span, ld, N, c_ld, nullptr, nullptr, 0u, 0, 0);
 }
 
-template <bool WIDE>
+// Different strides (dld = ldx - ldy, a multiple of 4; x_last: x's index of the span's last chunk).
+template <int OP>
+__global__ __launch_bounds__(64) void map_rows_diff(const float *__restrict__ x, float *__restrict__ y, float alpha,
+                                                    float beta, uint32_t nwork, uint32_t head, uint32_t span,
+                                                    uint32_t ld, uint32_t N, uint64_t c_ld, int32_t dld,
+                                                    int32_t x_last) {
+    rows_body<OP, true, true>(x, y, alpha, beta, nwork, head, span, ld, N, c_ld, nullptr, nullptr, 0u, dld, x_last);
+}
+
+template <bool WIDE, bool DIFF>
 __global__ __launch_bounds__(64) void map_rows_channel(const float *__restrict__ x, float *__restrict__ y,
                                                        uint32_t nwork, uint32_t head, uint32_t span, uint32_t ld,
                                                        uint32_t N, uint64_t c_ld, const float *__restrict__ scale,
-                                                       const float *__restrict__ bias, uint32_t cvec16) {
-    rows_body<tmp::kChannel, WIDE>(x, y, 0.0f, 0.0f, nwork, head, span, ld, N, c_ld, scale, bias, cvec16);
+                                                       const float *__restrict__ bias, uint32_t cvec16, int32_t dld,
+                                                       int32_t x_last) {
+    rows_body<tmp::kChannel, WIDE, DIFF>(x, y, 0.0f, 0.0f, nwork, head, span, ld, N, c_ld, scale, bias, cvec16, dld,
+                                        x_last);
 }
 
 template <bool WIDE>
@@ -260,14 +303,24 @@ hipError_t launch_map_flat(const tmp::MapPlan &p, hipStream_t stream) {
     if (p.rows) {
         uint32_t nwork = p.nwork, head = p.head, span = p.span, ld = p.ld_div.d, N = static_cast<uint32_t>(p.N);
         uint64_t c_ld = p.ld_div.c;
-        const bool wide = p.ldx - p.N >= 32;
+        int32_t dld = static_cast<int32_t>(p.ldx - p.ldy), x_last = p.x_last;
+        const bool diff = dld != 0;
+        const bool wide = p.ldy - p.N >= 32;
         if (p.op == tmp::kChannel) {
             const float *scale = p.scale, *bias = p.bias;
             uint32_t cvec16 = p.cvec16 ? 1u : 0u;
-            void *cargs[] = {&x, &y, &nwork, &head, &span, &ld, &N, &c_ld, &scale, &bias, &cvec16};
-            const void *cfn = wide ? reinterpret_cast<const void *>(&map_rows_channel<true>)
-                                   : reinterpret_cast<const void *>(&map_rows_channel<false>);
+            void *cargs[] = {&x, &y, &nwork, &head, &span, &ld, &N, &c_ld, &scale, &bias, &cvec16, &dld, &x_last};
+            const void *cfn = diff   ? reinterpret_cast<const void *>(&map_rows_channel<true, true>)
+                              : wide ? reinterpret_cast<const void *>(&map_rows_channel<true, false>)
+                                     : reinterpret_cast<const void *>(&map_rows_channel<false, false>);
             return hipLaunchKernel(cfn, dim3(p.grid), dim3(64), cargs, 0, stream);
+        }
+        if (diff) {
+            void *dargs[] = {&x, &y, &alpha, &beta, &nwork, &head, &span, &ld, &N, &c_ld, &dld, &x_last};
+            const void *dfn = p.op == tmp::kAffine  ? reinterpret_cast<const void *>(&map_rows_diff<tmp::kAffine>)
+                              : p.op == tmp::kScale ? reinterpret_cast<const void *>(&map_rows_diff<tmp::kScale>)
+                                                    : reinterpret_cast<const void *>(&map_rows_diff<tmp::kCopy>);
+            return hipLaunchKernel(dfn, dim3(p.grid), dim3(64), dargs, 0, stream);
         }
         void *args[] = {&x, &y, &alpha, &beta, &nwork, &head, &span, &ld, &N, &c_ld};
         const void *fn = wide ? pick_rows<true>(p.op) : pick_rows<false>(p.op);

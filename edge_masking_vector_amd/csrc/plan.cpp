@@ -244,21 +244,37 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     // hold padding are written in part here.  4100 x 4100 at row stride 4104: the map 33.6 ->
     // 21.6 us; at stride 4140 (40 floats of padding) the map 33.4 us and the bias add 54.3 us
     // under 2-D tiles.
-    const int64_t pad = ldx - N;
-    if (!aligned && M > 1 && ldx == ldy && pad > 0 && (pad < kLineBytes / 4 || pad * 8 <= N) &&
-        N >= kRowsSpanMinN && (access == kVec4 || access == kScalar) &&
+    // Different row strides take the same span over y (DIFF in mapflat.hip) when they differ by a
+    // multiple of 4 floats: the chunk of span element q, row r, then sits r (ldx - ldy) floats
+    // further on in x, still 16-byte aligned; a chunk that crosses a row's end takes the next
+    // row's elements from a second load.  y may then also be contiguous (x padded).
+    // (Rows of both tensors on the 128-byte line grid keep the 2-D plan, whose work items are then
+    // whole lines already, when the strides differ.)  x's rows drift against y's 1 KiB grid, so
+    // an item's 1 KiB of x mostly spans nine lines, one of them fetched by two XCDs (11% more
+    // reads); under 1024 floats a row the span then measured slower than the 2-D plan: 4100 x
+    // 1000 at strides 1004 / 1008 8.1 us as a span, 7.8 under 2-D tiles, 16400 x 1000 24.8
+    // against 23.6; 4100 x 4100 at 4104 / 4108 23.5 against 33.5, 2733 x 1500 at 1504 / 1508
+    // 8.1 against 8.4.
+    const int64_t pad = ldy - N;
+    const bool both_lines = aligned_to(x, kLineBytes) && aligned_to(y, kLineBytes) && ldx % (kLineBytes / 4) == 0 &&
+                            ldy % (kLineBytes / 4) == 0;
+    if (!aligned && M > 1 && pad >= 0 && (ldx != ldy ? !both_lines && N >= kRowsDiffMinN : pad > 0) && (ldx - ldy) % 4 == 0 &&
+        (pad < kLineBytes / 4 || pad * 8 <= N) && N >= kRowsSpanMinN && (access == kVec4 || access == kScalar) &&
         (reinterpret_cast<uintptr_t>(x) - reinterpret_cast<uintptr_t>(y)) % 16 == 0) {
         const int64_t head = static_cast<int64_t>((reinterpret_cast<uintptr_t>(y) / 4) % 256);
-        const int64_t span = (M - 1) * ldx + N;
-        if (head + span + 256 <= INT32_MAX && ldx <= UINT32_MAX) {  // span indexes are 32-bit
+        const int64_t span = (M - 1) * ldy + N;
+        const int64_t xspan = (M - 1) * ldx + N;
+        if (head + span + 256 <= INT32_MAX && xspan + 256 <= INT32_MAX && ldy <= UINT32_MAX) {  // 32-bit indexes
             const int64_t nwork = ceil_div(head + span, 256);
+            const int64_t q_last = (span - 1) - ((span - 1 + head) & 3);
             plan->launch = true;
             plan->op = op;
             plan->access = access;
             plan->rows = true;
             plan->head = static_cast<uint32_t>(head);
             plan->span = static_cast<uint32_t>(span);
-            plan->ld_div = make_div32(static_cast<uint32_t>(ldx));
+            plan->ld_div = make_div32(static_cast<uint32_t>(ldy));
+            plan->x_last = static_cast<int32_t>(q_last + (M - 1) * (ldx - ldy));
             plan->nwork = static_cast<uint32_t>(nwork);
             plan->grid = cap_grid(nwork);
             plan->x = x;
@@ -274,7 +290,7 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
             // a whole chunk's channels start on a column divisible by 4 when every chunk of the
             // span does (16-byte rows of y); then both vectors load as 16-byte chunks if aligned
             plan->cvec16 = op == kChannel && aligned_to(bias, 16) && aligned_to(scale, 16) && aligned_to(y, 16) &&
-                           ldx % 4 == 0;
+                           ldy % 4 == 0;
             return TM_OK;
         }
     }

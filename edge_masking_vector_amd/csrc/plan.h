@@ -27,6 +27,8 @@ constexpr int kStreamSegmentBytes = 1024;  // ... or one row segment of this man
 constexpr int64_t kChanFlatMax = 65535;  // channel op: flat views up to this many channels
 constexpr int64_t kRowsSpanMinN = 64;      // padded rows in one span: rows of at least this many
                                            // floats and less than a line of padding between them
+constexpr int64_t kRowsDiffMinN = 1024;    // ... and of at least this many when x's and y's row
+                                           // strides differ
                                          // (C * C < 2^32 for the device's 32-bit modulo)
 constexpr int kTrSub = 32;          // transpose: staged sub-tile edge (one 128-byte line of f32) ...
 constexpr int kTrSubElems = kTrSub * kTrSub;  // ... and elements; a narrow tensor's sub-tile is
@@ -136,7 +138,8 @@ struct MapPlan {
     bool rows = false;
     uint32_t head = 0;            // rows: floats from the first item's start to y[0] (0 .. 255)
     uint32_t span = 0;            // rows: (M - 1) * ld + N
-    Div32 ld_div;                 // rows: divisor ld
+    Div32 ld_div;                 // rows: divisor ld (y's row stride)
+    int32_t x_last = 0;           // rows: x's index of the chunk that holds the span's last element
     uint32_t group = 1;           // G
     uint32_t groups_n = 0;        // ceil(tiles_n / G)
     uint32_t tiles_n = 0;         // tiles along N

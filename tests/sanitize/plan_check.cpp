@@ -107,10 +107,12 @@ static void replay_flat(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld,
 // element must be stored exactly once and nothing else at all; whole-chunk stores must be aligned
 // blocks inside the item's 1 KiB block of y, and for the channel op a whole chunk's channels are
 // its columns c .. c + 3 (16-byte vector loads only when c is divisible by 4).
-static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, const char *tag) {
-    const int64_t pad = ld - N;
-    CHECK(!p.aligned && M > 1 && p.ldx == ld && p.ldy == ld && pad > 0 && (pad < 32 || pad * 8 <= N) &&
-              N >= tmp::kRowsSpanMinN && (p.access == tmp::kVec4 || p.access == tmp::kScalar),
+static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ldx_, int64_t ldy_, const char *tag) {
+    const int64_t ldx = ldx_, ldy = ldy_, ld = ldy, pad = ldy - N, dld = ldx - ldy;
+    const bool diff = dld != 0;
+    CHECK(!p.aligned && M > 1 && p.ldx == ldx && p.ldy == ldy && pad >= 0 && (diff || pad > 0) && dld % 4 == 0 &&
+              (pad < 32 || pad * 8 <= N) && N >= tmp::kRowsSpanMinN &&
+              (p.access == tmp::kVec4 || p.access == tmp::kScalar),
           "%s span plan outside its case", tag);
     const uintptr_t xa = reinterpret_cast<uintptr_t>(p.x), ya = reinterpret_cast<uintptr_t>(p.y);
     const int64_t span = (M - 1) * ld + N;
@@ -120,52 +122,80 @@ static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld,
     CHECK(!p.cvec16 || (p.op == tmp::kChannel && ya % 16 == 0 && ld % 4 == 0), "%s span channel vectors", tag);
     const int32_t q_first = -int32_t(p.head & 3u);
     const int32_t q_last = int32_t(span - 1) - int32_t((span - 1 + p.head) & 3u);
+    CHECK(p.x_last == int32_t(q_last + (M - 1) * dld), "%s span x_last", tag);
+    const bool wide = pad >= 32 || diff;  // the kernels that redirect chunks wholly inside the padding
     std::vector<uint8_t> hits(size_t(span), 0);
-    bool bad_load = false, bad_store = false;
+    bool bad_load = false, bad_store = false, bad_source = false;
+    // a 16-byte block of x at float index xi: aligned, and inside a line that holds a live element
+    auto live_line = [&](int64_t xi) {
+        if ((xa + 4 * xi) % 16 != 0)
+            return false;
+        const int64_t line = int64_t((xa + 4 * xi) / 128 * 128);
+        for (int e = 0; e < 32; ++e) {
+            const int64_t g = (line - int64_t(xa)) / 4 + e;  // x float index
+            if (g >= 0 && g < (M - 1) * ldx + N && g % ldx < N)
+                return true;
+        }
+        return false;
+    };
     for (uint32_t w = 0; w < p.nwork; ++w)
         for (int t = 0; t < 64; ++t) {
             const int32_t q = int32_t(w * 256u + 4u * t) - int32_t(p.head);
-            const uint32_t c = q > 0 ? umulhi_mod(uint32_t(q), p.ld_div) : 0u;
-            if (q > 0 && c != uint32_t(q % ld))
-                bad_load = true;
-            int32_t qa = q;
-            if (pad >= 32 && q >= 0 && c >= N && c + 3 < ld) {
-                const int32_t last = q - int32_t(c) + int32_t(N) - 1;
-                qa = last - int32_t((uint32_t(last) + p.head) & 3u);
+            uint32_t r = 0, c = 0;
+            if (q > 0) {
+                r = uint32_t(q / ld);
+                c = uint32_t(q % ld);
+                if (!diff && umulhi_mod(uint32_t(q), p.ld_div) != c)
+                    bad_load = true;
+                if (diff && umulhi_div(uint32_t(q), p.ld_div) != r)
+                    bad_load = true;
             }
-            qa = qa < q_first ? q_first : (qa > q_last ? q_last : qa);
-            // aligned, and inside a line of x that holds a live element of the span
-            bool live_in_load = false;
-            const uintptr_t line = (xa + 4 * int64_t(qa)) / 128 * 128;
-            for (int e = 0; e < 32; ++e) {
-                const int64_t f = (int64_t(line) - int64_t(xa)) / 4 + e;
-                live_in_load = live_in_load || (f >= 0 && f < span && f % ld < N);
+            int64_t xa0 = q < q_first ? q_first : (q > q_last ? q_last : q), xb0 = xa0;
+            if (wide) {
+                int32_t qa = q;
+                if (q >= 0 && c >= N && c + 3 < ld) {
+                    const int32_t last = q - int32_t(c) + int32_t(N) - 1;
+                    qa = last - int32_t((uint32_t(last) + p.head) & 3u);
+                }
+                xa0 = diff ? int64_t(qa) + int64_t(r) * dld : qa;
+                xa0 = q < q_first ? q_first : (q > q_last ? (diff ? p.x_last : q_last) : xa0);
+                xb0 = xa0;
+                if (diff) {
+                    const bool cross = q >= 0 && c + 3 >= ld && int64_t(q) - c + ld < span;
+                    xb0 = cross ? xa0 + dld : xa0;
+                    if (cross && c >= N)
+                        xa0 = xb0;  // no element of the chunk is live in its own row
+                }
             }
-            if ((xa + 4 * int64_t(qa)) % 16 != 0 || !live_in_load)
+            if (!live_line(xa0) || (diff && !live_line(xb0)))
                 bad_load = true;
-            if (q >= 0 && int64_t(q) + 3 < span && c + 3 < N) {
+            const bool whole = q >= 0 && int64_t(q) + 3 < span && c + 3 < N;
+            if (whole) {
                 const uintptr_t blk = ya + 4 * (int64_t(w) * 256 - p.head);
                 if (blk % 1024 != 0 || (ya + 4 * int64_t(q)) != blk + 16 * uintptr_t(t))
                     bad_store = true;
                 if (p.cvec16 && c % 4 != 0)
                     bad_store = true;  // a 16-byte channel-vector load off its grid
-                for (int i = 0; i < 4; ++i)
-                    ++hits[size_t(q + i)];
-            } else {
-                for (int i = 0; i < 4; ++i) {
-                    const int32_t f = q + i;
-                    uint32_t col = q >= 0 ? c + i : uint32_t(f);
-                    col = col >= ld ? col - uint32_t(ld) : col;
-                    if (f >= 0 && f < span && col < N) {
-                        if (col != uint32_t(f % ld))
-                            bad_store = true;
-                        ++hits[size_t(f)];
-                    }
+            }
+            for (int i = 0; i < 4; ++i) {
+                const int32_t f = q + i;
+                const uint32_t ci = q >= 0 ? c + i : uint32_t(f);
+                const bool next = q >= 0 && ci >= ld;
+                const uint32_t col = next ? ci - uint32_t(ld) : ci;
+                if (f >= 0 && f < span && col < N) {
+                    if (col != uint32_t(f % ld))
+                        bad_store = true;
+                    // the x element this output takes: row f / ldy, same column
+                    const int64_t src = (next && diff ? xb0 : xa0) + i;
+                    if (src != int64_t(f / ld) * ldx + col)
+                        bad_source = true;
+                    ++hits[size_t(f)];
                 }
             }
         }
-    CHECK(!bad_load, "%s span: a load off the view's live 16-byte blocks (or a wrong column)", tag);
+    CHECK(!bad_load, "%s span: a load off x's live lines (or a wrong row or column)", tag);
     CHECK(!bad_store, "%s span: a misplaced store", tag);
+    CHECK(!bad_source, "%s span: an output element taken from the wrong x element", tag);
     for (int64_t f = 0; f < span; ++f) {
         const bool live = f % ld < N;
         if (hits[size_t(f)] != (live ? 1 : 0)) {
@@ -184,7 +214,7 @@ static void replay_map(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, 
         return;
     }
     if (p.rows) {
-        replay_rows(p, M, N, ld, tag);
+        replay_rows(p, M, N, p.ldx, p.ldy, tag);
         return;
     }
     const int W = p.access == tmp::kScalar || p.access == tmp::kScalar1 ? 1 : 4;
@@ -280,6 +310,38 @@ static void replay_map(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, 
         }
     }
     ++g_checked;
+}
+
+// Different row strides in x and y (the span's DIFF form when they differ by a multiple of 4 and
+// the bases sit the same distance past a 16-byte boundary; the 2-D plan otherwise).
+static void check_maps_diff() {
+    long spans = 0;
+    for (int64_t M : {int64_t{2}, int64_t{3}, int64_t{17}, int64_t{100}})
+        for (int64_t N : {int64_t{1000}, int64_t{1024}, int64_t{1029}, int64_t{2000}})
+            for (int dx : {0, 1, 4, 8, 40, 200})
+                for (int dy : {0, 3, 4, 8, 31, 40})
+                    for (uintptr_t xoff : {uintptr_t{0}, uintptr_t{4}, uintptr_t{12}})
+                        for (uintptr_t yoff : {uintptr_t{0}, uintptr_t{4}})
+                            for (int op : {int(tmp::kAffine), int(tmp::kChannel)})
+                                for (int variant : {TM_VAR_AUTO, TM_VAR_VEC4}) {
+                                    const int64_t ldx = N + dx, ldy = N + dy;
+                                    if (ldx == ldy)
+                                        continue;
+                                    tmp::MapPlan p;
+                                    const uintptr_t xb = 0x100000 + xoff, yb = 0x40000000 + yoff;
+                                    const int st = tmp::plan_map(op, fake(xb), ldx, const_cast<float *>(fake(yb)), ldy, M, N,
+                                                                 1.5f, 0.f, 64, 64, 0, variant, &p, nullptr, fake(0x200000));
+                                    if (st != TM_OK || !p.launch)
+                                        continue;
+                                    char tag[160];
+                                    std::snprintf(tag, sizeof tag, "map diff M=%ld N=%ld ldx=%ld ldy=%ld offs=%lu,%lu op=%d var=%d",
+                                                  long(M), long(N), long(ldx), long(ldy), (unsigned long)xoff,
+                                                  (unsigned long)yoff, op, variant);
+                                    CHECK(!p.rows || N >= tmp::kRowsDiffMinN, "%s: a span under the width minimum", tag);
+                                    spans += p.rows;
+                                    replay_map(p, M, N, ldy, xb, tag);
+                                }
+    CHECK(spans >= 500, "only %ld different-stride span plans", spans);
 }
 
 static void check_maps() {
@@ -801,6 +863,7 @@ static void check_extremes() {
 int main() {
     check_extremes();
     check_maps();
+    check_maps_diff();
     check_transposes();
     check_reductions();
     check_split_rows();

@@ -210,7 +210,7 @@ def test_padded_rows_one_span(dev, op, M, N, ld, off, variant):
 
 @pytest.mark.parametrize("M,N,ldx,ldy,xoff,yoff", [
     (100, 1000, 1001, 1001, 1, 0),    # bases at different distances past a 16-byte boundary
-    (100, 1000, 1004, 1008, 0, 0),    # different strides: the 2-D tile plan
+    (100, 1000, 1004, 1008, 0, 0),    # different strides over rows under 1024 floats
     (100, 60, 61, 61, 0, 0),          # rows narrower than the span's minimum
     (100, 1000, 1040, 1040, 0, 0),    # a line or more of padding
 ])
@@ -244,8 +244,9 @@ def test_padded_rows_in_place(dev, ld, off):
     (4100, 1000, 1001, 1001, 64, 64, tm.TM_VAR_AUTO),     # the bench's padded maps: one span
     (4100, 1000, 1004, 1004, 64, 64, tm.TM_VAR_VEC4),
     (4100, 4100, 4104, 4104, 32, 128, tm.TM_VAR_VEC4),
-    (4100, 1000, 1004, 1008, 64, 64, tm.TM_VAR_VEC4),     # ... and the 2-D tile plan
-    (4100, 4100, 4104, 4108, 32, 128, tm.TM_VAR_VEC4),
+    (4100, 4100, 4104, 4108, 32, 128, tm.TM_VAR_VEC4),    # one span over y, different strides
+    (4100, 1000, 1004, 1008, 64, 64, tm.TM_VAR_VEC4),     # the 2-D tile plan
+    (4100, 4100, 4104, 4700, 32, 128, tm.TM_VAR_VEC4),
 ])
 def test_bench_padded_maps_full_size(dev, M, N, ldx, ldy, TM, TN, variant):
     """The padded-row maps the benchmark times, at their full sizes and in the same calls (ragged
@@ -307,3 +308,46 @@ def test_padded_rows_wide_padding(dev, M, N, ld, off):
     inside it load the row's last live chunk and store nothing."""
     note("span wide padding %dx%d ld %d off %d" % (M, N, ld, off))
     _check_strided(dev, "affine", M, N, ld, ld, off, off, tm.TM_VAR_AUTO, seed=M * 7 + ld)
+
+
+@pytest.mark.parametrize("op,M,N,ldx,ldy,off", [
+    ("affine", 300, 1100, 1104, 1108, 0),   # x rows 4 floats shorter than y's
+    ("affine", 300, 1100, 1108, 1104, 0),   # ... and longer
+    ("copy", 300, 1024, 1024, 1028, 0),     # x contiguous, y padded
+    ("scale", 300, 1100, 1140, 1100, 2),    # x padded by 40, y contiguous
+    ("affine", 257, 1777, 2801, 1781, 3),   # x padding far wider than y's
+    ("affine", 64, 4100, 4104, 4108, 0),
+    ("affine", 300, 1100, 1101, 1104, 1),   # strides 3 apart: the 2-D tile plan
+    ("affine", 300, 1000, 1004, 1008, 0),   # rows under 1024 floats: the 2-D tile plan
+])
+def test_padded_rows_different_strides(dev, op, M, N, ldx, ldy, off):
+    """Rows of 1024 floats or more with different strides in x and y (a multiple of 4 floats
+    apart) as one span over y: the chunk of a row sits (ldx - ldy) floats further on in x per row,
+    and a chunk that crosses a row's end takes the next row's elements from a second load; bit for
+    bit, the padding of y untouched."""
+    note("span %s %dx%d ldx %d ldy %d off %d" % (op, M, N, ldx, ldy, off))
+    _check_strided(dev, op, M, N, ldx, ldy, off, off, tm.TM_VAR_AUTO, seed=M + 3 * ldx + ldy)
+
+
+def test_padded_rows_different_strides_channel(dev):
+    """The per-channel op over different strides in one span."""
+    M, N, ldx, ldy = 300, 1100, 1112, 1104
+    n_x, n_y = (M - 1) * ldx + N, (M - 1) * ldy + N
+    xh = inputs.uniform(71, n_x, -8.0, 8.0)
+    bh = inputs.uniform(72, N, -1.0, 1.0)
+    sh = inputs.uniform(73, N, 0.5, 1.5)
+    X = Guarded(n_x, dev, guard=LINE_GUARD_FLOATS)
+    X.upload(xh)
+    Y = Guarded(n_y, dev, guard=LINE_GUARD_FLOATS)
+    B = Guarded(N, dev)
+    B.upload(bh)
+    S = Guarded(N, dev)
+    S.upload(sh)
+    note("span channel %dx%d ldx %d ldy %d" % (M, N, ldx, ldy))
+    assert tm.tm_channel_affine(X.ptr, ldx, S.ptr, B.ptr, Y.ptr, ldy, M, N, 64, 64, 0, tm.TM_VAR_AUTO) == tm.TM_OK
+    torch.cuda.synchronize()
+    want = sentinel_host(Y.buf.numel())
+    region = want[Y.off:Y.off + n_y].copy()
+    oracle.channel_affine(xh, ldx, sh, bh, region, ldy, M, N)
+    want[Y.off:Y.off + n_y] = region
+    assert np.array_equal(bits(Y.host()), bits(want))

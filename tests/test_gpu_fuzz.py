@@ -375,23 +375,28 @@ def test_fuzz_transposes(dev):
 
 
 def test_fuzz_padded_spans(dev):
-    """Padded rows with one stride in both tensors (the span plan of 1 KiB items on y's 1 KiB grid
-    when the bases sit the same distance past a 16-byte boundary and the padding is under a line
-    or at most an eighth of the row, the 2-D tile plan otherwise): random shapes, paddings,
-    offsets, ops (the channel op too) and variants, bit for bit, the padding between rows
-    untouched."""
+    """Padded rows (the span plan of 1 KiB items on y's 1 KiB grid when the bases sit the same
+    distance past a 16-byte boundary, y's padding is under a line or at most an eighth of the row
+    and x's stride is the same or, over rows of 1024 floats or more, a multiple of 4 floats away;
+    the 2-D tile plan otherwise): random shapes, paddings, strides, offsets, ops (the channel op
+    too) and variants, bit for bit, the padding between rows untouched."""
     rng = random.Random(4242)
     for case in range(150):
         op = rng.choice(["affine", "scale", "copy", "channel", "channel_scale"])
         variant = rng.choice([tm.TM_VAR_AUTO, tm.TM_VAR_AUTO, tm.TM_VAR_VEC4, tm.TM_VAR_SCALAR])
-        M, N = rng.randint(2, 300), rng.randint(64, 1100)
+        # x's stride: mostly the same, else (over rows of 1024 floats or more) a multiple of 4
+        # floats away, or not
+        diff = rng.random() >= 0.6
+        M, N = rng.randint(2, 300), (rng.randint(1024, 2600) if diff else rng.randint(64, 1100))
         ld = N + (rng.randint(1, 31) if rng.random() < 0.7 else rng.randint(32, max(32, N // 8 + 3)))
+        ldx = max(N, ld + rng.choice([-8, -4, 4, 8, 12, 40, 3, -1])) if diff else ld
         offx = rng.choice([0, 1, 2, 3, 5, 64, 100])
         offy = offx if rng.random() < 0.8 else rng.choice([0, 1, 2, 3])
-        note("fuzz span %d: %s M=%d N=%d ld=%d offs=%d,%d variant=%d" % (case, op, M, N, ld, offx, offy, variant))
+        note("fuzz span %d: %s M=%d N=%d ldx=%d ld=%d offs=%d,%d variant=%d" % (case, op, M, N, ldx, ld, offx, offy, variant))
         n = (M - 1) * ld + N
-        xh = inputs.uniform(7000 + case, n, -8.0, 8.0)
-        X = Guarded(n, dev, offx, LINE_GUARD_FLOATS)
+        nx = (M - 1) * ldx + N
+        xh = inputs.uniform(7000 + case, nx, -8.0, 8.0)
+        X = Guarded(nx, dev, offx, LINE_GUARD_FLOATS)
         X.upload(xh)
         Y = Guarded(n, dev, offy, LINE_GUARD_FLOATS)
         sh = None
@@ -403,28 +408,28 @@ def test_fuzz_padded_spans(dev):
                 sh = inputs.uniform(7700 + case, N, 0.5, 1.5)
                 Sv = Guarded(N, dev, rng.choice([0, 4]))
                 Sv.upload(sh)
-            st = tm.tm_channel_affine(X.ptr, ld, Sv.ptr if sh is not None else None, Bv.ptr, Y.ptr, ld, M, N,
+            st = tm.tm_channel_affine(X.ptr, ldx, Sv.ptr if sh is not None else None, Bv.ptr, Y.ptr, ld, M, N,
                                       64, 64, 0, variant)
         elif op == "affine":
-            st = tm.tm_map_affine(X.ptr, ld, Y.ptr, ld, M, N, 0.75, -0.25, 64, 64, 0, variant)
+            st = tm.tm_map_affine(X.ptr, ldx, Y.ptr, ld, M, N, 0.75, -0.25, 64, 64, 0, variant)
         elif op == "scale":
-            st = tm.tm_scale2d(X.ptr, ld, Y.ptr, ld, M, N, 1.5, 64, 64, 0, variant)
+            st = tm.tm_scale2d(X.ptr, ldx, Y.ptr, ld, M, N, 1.5, 64, 64, 0, variant)
         else:
-            st = tm.tm_copy2d(X.ptr, ld, Y.ptr, ld, M, N, 64, 64, 0, variant)
-        vec_ok = rows16(X.ptr, M, ld) and rows16(Y.ptr, M, ld)
+            st = tm.tm_copy2d(X.ptr, ldx, Y.ptr, ld, M, N, 64, 64, 0, variant)
+        vec_ok = rows16(X.ptr, M, ldx) and rows16(Y.ptr, M, ld)
         assert st == (tm.TM_OK if variant != tm.TM_VAR_VEC4 or vec_ok else tm.TM_E_ALIGN), tm.tm_status_string(st)
         torch.cuda.synchronize()
         want = sentinel_host(Y.buf.numel())
         if st == tm.TM_OK:
             region = want[Y.off:Y.off + n].copy()
             if op == "affine":
-                oracle.map_affine(xh, ld, region, ld, M, N, 0.75, -0.25)
+                oracle.map_affine(xh, ldx, region, ld, M, N, 0.75, -0.25)
             elif op == "scale":
-                oracle.scale2d(xh, ld, region, ld, M, N, 1.5)
+                oracle.scale2d(xh, ldx, region, ld, M, N, 1.5)
             elif op == "copy":
-                oracle.copy2d(xh, ld, region, ld, M, N)
+                oracle.copy2d(xh, ldx, region, ld, M, N)
             else:
-                oracle.channel_affine(xh, ld, sh, bh, region, ld, M, N)
+                oracle.channel_affine(xh, ldx, sh, bh, region, ld, M, N)
             want[Y.off:Y.off + n] = region
         assert np.array_equal(bits(Y.host()), bits(want)), "case %d" % case
         assert X.guards_intact()
