@@ -279,7 +279,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     only if `sweep`)."""
     out = {}
 
-    def timed(name, nbytes, n_sets, launch, note):
+    def timed(name, nbytes, n_sets, launch, note, plan=None):
         """W warm-ups, then K launches timed as one region (mean_us), then path_batches batches of
         BATCH_LAUNCHES launches that carry on the rotation through the buffer sets.  The headline
         (us, gbs, frac) is the median over the batches, which does not depend on --steps: with
@@ -289,6 +289,8 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
             launch(i % n_sets)
         mean = Timer(torch, stream).run(lambda i: launch(i % n_sets), K) / K
         rec = {"bytes": nbytes, "note": note, "mean_us": round(mean * 1e6, 3)}
+        if plan is not None:
+            rec["plan"] = plan
         head, how = mean, "mean of %d launches" % K
         if path_batches > 0:
             batch = []
@@ -309,6 +311,17 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     def ok(st):
         if st != tm.TM_OK:
             raise tm.TilemapError(st)
+
+    walk_names = {tm.TM_MAP_FLAT: "flat", tm.TM_MAP_SPAN: "span", tm.TM_MAP_TILES: "tiles"}
+
+    def map_plan(expect, x, ldx, y, ldy, M, N, TM, TN, aligned, var):
+        """The plan the map call will run (tm_map_walk), checked against the path's label."""
+        st, walk, items = tm.tm_map_walk(0, x, ldx, y, ldy, M, N, TM, TN, aligned, var)
+        ok(st)
+        if walk_names.get(walk) != expect:
+            raise RuntimeError("map %dx%d strides %d / %d runs the %s plan, labelled %s"
+                               % (M, N, ldx, ldy, walk_names.get(walk), expect))
+        return {"walk": expect, "items": items}
 
     # ceiling probe: the aligned copy and the runtime's device-to-device copy of 8192 x 8192 f32
     # (256 MiB read + 256 MiB written per launch, twice the Infinity Cache)
@@ -376,29 +389,34 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
               lambda i, M=M, N=N, aligned=aligned, var=var: ok(tm.tm_map_affine(
                   xs[i], N, ys[i], N, M, N, 0.75, -0.25, 64, 64, aligned, var, stream)),
               "y = fmaf(x, 0.75, -0.25), 64x64 tiles; rows contiguous (row stride N), so the view is "
-              "planned as one flat row whose only ragged edge is its end")
+              "planned as one flat row whose only ragged edge is its end",
+              plan=map_plan("flat", xs[0], N, ys[0], N, M, N, 64, 64, aligned, var))
         del xs, ys
-    # the same ragged map over padded rows.  With padding under a line or at most an eighth of a
-    # row the view is one span of 1 KiB items on y's 1 KiB grid whose columns past N are masked:
-    # rows off the 16-byte grid (row stride 1001), on it (1004), a scale-sized view (4100 x 4100
-    # at row stride 4104), and strides that differ between x and y (rows of 1024 floats or more).
-    # With different strides over narrower rows, or wider padding of y, the 2-D tile plan runs,
-    # and its edge tiles (the bottom 4 rows, the right 40 or 4 columns) take the masked body.
-    for (M, N, ldx, ldy, TM, TN, var, name, what) in (
-            (4100, 1000, 1001, 1001, 64, 64, tm.TM_VAR_AUTO, "affine_4100x1000_ld1001_ragged_2d",
+    # the same ragged map over padded rows.  The view is one span of 1 KiB items on y's 1 KiB grid
+    # whose columns past N are masked when the padding is under a line or at most an eighth of the
+    # row, or (rows off the line grid) wider: rows off the 16-byte grid (row stride 1001), on it
+    # (1004), a scale-sized view (4100 x 4100 at row stride 4104), strides that differ between x
+    # and y, and 600 floats of padding (waves wholly inside it exit at once).  Different strides
+    # over rows under 1024 floats, and wide padding between rows on the line grid, keep the 2-D
+    # tile plan, whose edge tiles (the bottom 4 rows, the right 40 or 4 columns) take the masked
+    # body.
+    for (M, N, ldx, ldy, TM, TN, var, name, expect, what) in (
+            (4100, 1000, 1001, 1001, 64, 64, tm.TM_VAR_AUTO, "affine_4100x1000_ld1001_ragged_2d", "span",
              "one span of 1 KiB items, columns past N masked (rows off the 16-byte grid)"),
-            (4100, 1000, 1004, 1004, 64, 64, tm.TM_VAR_VEC4, "affine_4100x1000_ld1004_ragged_2d",
+            (4100, 1000, 1004, 1004, 64, 64, tm.TM_VAR_VEC4, "affine_4100x1000_ld1004_ragged_2d", "span",
              "one span of 1 KiB items, columns past N masked"),
-            (4100, 4100, 4104, 4104, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ld4104_ragged_2d",
+            (4100, 4100, 4104, 4104, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ld4104_ragged_2d", "span",
              "one span of 1 KiB items, columns past N masked"),
-            (4100, 4100, 4104, 4108, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ldx4104_ldy4108_ragged_2d",
+            (4100, 4100, 4104, 4108, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ldx4104_ldy4108_ragged_2d", "span",
              "one span over y, x's rows 4 floats shorter"),
-            (4100, 1000, 1004, 1008, 64, 64, tm.TM_VAR_VEC4, "affine_4100x1000_ldx1004_ldy1008_ragged_tiles",
+            (4100, 4100, 4700, 4700, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ld4700_ragged_2d", "span",
+             "one span, 600 floats of padding between rows (waves wholly inside it exit at once)"),
+            (4100, 1000, 1004, 1008, 64, 64, tm.TM_VAR_VEC4, "affine_4100x1000_ldx1004_ldy1008_ragged_tiles", "tiles",
              "the 2-D tile plan (different strides, rows under 1024 floats): 16-byte chunks, 4-row "
              "bottom and 64x40 right-edge tiles masked"),
-            (4100, 4100, 4104, 4700, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ldx4104_ldy4700_ragged_tiles",
-             "the 2-D tile plan (y padding over an eighth of the row): 16-byte chunks, 32x128 tiles, "
-             "4-row bottom and 4-column right edge tiles masked")):
+            (4100, 4100, 5120, 5120, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ld5120_ragged_tiles", "tiles",
+             "the 2-D tile plan (rows on the 128-byte line grid, 1020 floats of padding): 16-byte "
+             "chunks, 32x128 tiles, 4-row bottom and 4-column right edge tiles masked")):
         xh = inputs.matrix(inputs.ragged_input(M, N, seed=12), M, N, ldx)
         nb = 2 * M * N * 4
         R = sets_for(M * ldx * 4 + M * ldy * 4)
@@ -408,7 +426,8 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
               lambda i, M=M, N=N, ldx=ldx, ldy=ldy, TM=TM, TN=TN, var=var: ok(tm.tm_map_affine(
                   xs[i], ldx, ys[i], ldy, M, N, 0.75, -0.25, TM, TN, 0, var, stream)),
               "ragged path, %dx%d tiles, row strides %d / %d (padded rows): %s; bytes count the %dx%d "
-              "elements only" % (TM, TN, ldx, ldy, what, M, N))
+              "elements only" % (TM, TN, ldx, ldy, what, M, N),
+              plan=map_plan(expect, xs[0], ldx, ys[0], ldy, M, N, TM, TN, 0, var))
         del xs, ys
 
     # row and column sums of 4096 x 4096 U[0,1)

@@ -148,6 +148,26 @@ TM_API int tm_row_walk(int64_t M, int64_t N, int64_t ld, int BR, int BC, int ali
     return tmp::row_walk_query(M, N, ld, BR, BC, aligned, x, bc, nfull, rem, lanes);
 }
 
+TM_API int tm_map_walk(int op, const void *x, int64_t ldx, const void *y, int64_t ldy, int64_t M, int64_t N,
+                       int TM, int TN, int aligned, int variant, const void *bias, int *walk, int64_t *items) {
+    if (op < tmp::kAffine || op > tmp::kChannel || walk == nullptr || items == nullptr)
+        return TM_E_INVAL;
+    tmp::MapPlan plan;
+    const float *xf = static_cast<const float *>(x);
+    float *yf = static_cast<float *>(const_cast<void *>(y));
+    const int st = tmp::plan_map(op, xf, ldx, yf, ldy, M, N, 1.0f, 0.0f, TM, TN, aligned, variant, &plan, nullptr,
+                                 op == tmp::kChannel ? static_cast<const float *>(bias) : nullptr);
+    if (st != TM_OK)
+        return st;
+    // (the channel op over contiguous rows is one flat row too, its channel the flat column mod C)
+    *walk = !plan.launch                    ? TM_MAP_NONE
+            : plan.flat || plan.chan_n != 0 ? TM_MAP_FLAT
+            : plan.rows                     ? TM_MAP_SPAN
+                                            : TM_MAP_TILES;
+    *items = plan.launch ? int64_t(plan.nwork) : 0;
+    return TM_OK;
+}
+
 TM_API int tm_plan_tiles(int64_t M, int64_t N, int TM, int TN, int64_t *tiles_m, int64_t *tiles_n,
                          int64_t *whole) {
     return tmp::plan_tiles(M, N, TM, TN, tiles_m, tiles_n, whole);

@@ -167,6 +167,11 @@ __device__ __forceinline__ void rows_body(const float *__restrict__ x, float *__
             }
         }
         if constexpr (WIDE || DIFF) {
+            // a wave whose chunks all lie in the padding between two rows (or past the span's
+            // ends) neither loads nor stores
+            const bool some_live = q + 3 >= 0 && q < int32_t(span) && (q < 0 || c < N || c + 3 >= ld);
+            if (__builtin_amdgcn_ballot_w64(some_live) == 0)
+                continue;
             // x index of the chunk: the span's own index shifted by dld per row (DIFF); a chunk
             // wholly inside y's padding loads the row's last live chunk; the span's ends clamp
             int32_t qa = q;

@@ -234,9 +234,10 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     }
 
     // Padded rows (row stride ld > N, the same in both tensors, both bases the same distance past a
-    // 16-byte boundary, padding under one 128-byte line or at most an eighth of the row): on the
-    // ragged path the span from y[0] to the last element is cut into 1 KiB items on y's 1 KiB grid,
-    // and each item moves 16-byte chunks with the columns past N masked (mapflat.hip, map_rows);
+    // 16-byte boundary, padding under one 128-byte line or at most an eighth of the row, or wider
+    // as below): on the ragged path the span from y[0] to the last element is cut into 1 KiB items
+    // on y's 1 KiB grid, and each item moves 16-byte chunks with the columns past N masked
+    // (mapflat.hip, map_rows);
     // the channel op takes each element's column as its channel.  Work items then never share a
     // line, where 2-D tiles over rows off the line grid shared the lines at both ends of every row
     // piece with the neighbouring items: a line written in parts by two XCDs reaches HBM3E as
@@ -256,10 +257,23 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     // against 23.6; 4100 x 4100 at 4104 / 4108 23.5 against 33.5, 2733 x 1500 at 1504 / 1508
     // 8.1 against 8.4.
     const int64_t pad = ldy - N;
-    const bool both_lines = aligned_to(x, kLineBytes) && aligned_to(y, kLineBytes) && ldx % (kLineBytes / 4) == 0 &&
-                            ldy % (kLineBytes / 4) == 0;
+    const bool y_lines = aligned_to(y, kLineBytes) && ldy % (kLineBytes / 4) == 0;
+    const bool both_lines = y_lines && aligned_to(x, kLineBytes) && ldx % (kLineBytes / 4) == 0;
+    // Padding: under a line, or at most an eighth of the row; wider padding when y's rows miss the
+    // line grid, where the 2-D plan's row pieces share lines between items (a wave wholly inside
+    // the padding exits at once, so what wider padding costs is those waves' dispatch): a quarter
+    // of the row for 16-byte rows of 2048 floats or more, and for rows off the 16-byte grid (which
+    // the 2-D plan moves in 4-byte chunks) a quarter, or half from 2048 floats on.  Span against
+    // 2-D tiles, HIP events over 1 GiB of rotating buffers: 4100 x 4100 at stride 4700 24.6 against
+    // 33.8 us, 2048 x 4100 at 6150 14.2 against 24.5, 4096 x 2500 at 3750 16.8 against 23.4,
+    // 8192 x 1000 at 1201 13.8 against 15.8; past those limits the span lost or tied: 8192 x 2048
+    // at 3000 26.2 against 24.0, 4096 x 2048 at 2900 14.4 against 13.6, 32768 x 250 at 375 18.4
+    // against 16.5, 8192 x 1000 at 1501 16.4 against 16.2.
+    const bool y16 = aligned_to(y, 16) && ldy % 4 == 0;
+    const bool pad_ok = pad < kLineBytes / 4 || pad * 8 <= N ||
+                        (!y_lines && (pad * 4 <= N ? N >= kRowsWideMinN || !y16 : !y16 && N >= kRowsWideMinN && pad * 2 <= N));
     if (!aligned && M > 1 && pad >= 0 && (ldx != ldy ? !both_lines && N >= kRowsDiffMinN : pad > 0) && (ldx - ldy) % 4 == 0 &&
-        (pad < kLineBytes / 4 || pad * 8 <= N) && N >= kRowsSpanMinN && (access == kVec4 || access == kScalar) &&
+        pad_ok && N >= kRowsSpanMinN && (access == kVec4 || access == kScalar) &&
         (reinterpret_cast<uintptr_t>(x) - reinterpret_cast<uintptr_t>(y)) % 16 == 0) {
         const int64_t head = static_cast<int64_t>((reinterpret_cast<uintptr_t>(y) / 4) % 256);
         const int64_t span = (M - 1) * ldy + N;

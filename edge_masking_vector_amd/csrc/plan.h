@@ -29,6 +29,9 @@ constexpr int64_t kRowsSpanMinN = 64;      // padded rows in one span: rows of a
                                            // floats and less than a line of padding between them
 constexpr int64_t kRowsDiffMinN = 1024;    // ... and of at least this many when x's and y's row
                                            // strides differ
+constexpr int64_t kRowsWideMinN = 2048;    // ... and padding past an eighth of the row off the line
+                                           // grid: a quarter from this many floats on (16-byte
+                                           // rows), half (rows off the 16-byte grid)
                                          // (C * C < 2^32 for the device's 32-bit modulo)
 constexpr int kTrSub = 32;          // transpose: staged sub-tile edge (one 128-byte line of f32) ...
 constexpr int kTrSubElems = kTrSub * kTrSub;  // ... and elements; a narrow tensor's sub-tile is

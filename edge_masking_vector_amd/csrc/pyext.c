@@ -2,7 +2,7 @@
  * taking device addresses as Python ints (None for NULL), sizes as ints, scalars as floats and the
  * stream as an int (a hipStream_t; 0 is the null stream).  Argument conversion only: each function
  * converts its arguments and calls the C ABI once.  Calls that write through host pointers
- * (tm_split, tm_plan_tiles, tm_row_walk, tm_pad_extents, tm_autotune_map) return a tuple that starts with the
+ * (tm_split, tm_plan_tiles, tm_map_walk, tm_row_walk, tm_pad_extents, tm_autotune_map) return a tuple that starts with the
  * status instead.  A wrong argument count or type raises TypeError / OverflowError before any call.
  *
  * METH_FASTCALL keeps a call near half a microsecond; through ctypes the same call took several,
@@ -303,6 +303,19 @@ static PyObject *py_row_walk(ARGS) {
     return Py_BuildValue("(iLLLi)", st, (long long)bc, (long long)nfull, (long long)rem, lanes);
 }
 
+static PyObject *py_map_walk(ARGS) {
+    int64_t ldx, ldy, M, N, items = -1;
+    int op, TM, TN, al, var, walk = -1;
+    void *x, *y, *bias;
+    (void)self;
+    OK(want(n, 12, "tm_map_walk"));
+    OK(as_int(a[0], &op) && as_ptr(a[1], &x) && as_i64(a[2], &ldx) && as_ptr(a[3], &y) && as_i64(a[4], &ldy) &&
+       as_i64(a[5], &M) && as_i64(a[6], &N) && as_int(a[7], &TM) && as_int(a[8], &TN) && as_int(a[9], &al) &&
+       as_int(a[10], &var) && as_ptr(a[11], &bias));
+    const int st = tm_map_walk(op, x, ldx, y, ldy, M, N, TM, TN, al, var, bias, &walk, &items);
+    return Py_BuildValue("(iiL)", st, walk, (long long)items);
+}
+
 static PyObject *py_plan_tiles(ARGS) {
     int64_t M, N, tm_ = -1, tn_ = -1, whole = -1;
     int TM, TN;
@@ -395,6 +408,7 @@ static PyMethodDef methods[] = {
     FAST("tm_check_promise", py_check_promise),
     FAST("tm_split", py_split),
     FAST("tm_plan_tiles", py_plan_tiles),
+    FAST("tm_map_walk", py_map_walk),
     FAST("tm_colsum_noalloc", py_colsum_noalloc),
     FAST("tm_row_walk", py_row_walk),
     FAST("tm_pad_extents", py_pad_extents),

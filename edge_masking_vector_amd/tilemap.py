@@ -34,6 +34,11 @@ TM_COL_NAIVE = 0
 TM_COL_LDS = 1
 TM_COL_NAIVE_XCD = 2
 
+TM_MAP_NONE = 0
+TM_MAP_FLAT = 1
+TM_MAP_SPAN = 2
+TM_MAP_TILES = 3
+
 if not os.path.exists(LIB_PATH):
     raise ImportError("libtilemap.so is not built (expected at %s); run "
                       "`python -c 'import __graft_entry__ as g; g.build()'` first" % LIB_PATH)
@@ -168,6 +173,13 @@ def tm_row_walk(M, N, ld, BR, BC, aligned, x):
     """Returns (status, bc, nfull, rem, lanes): the column walk of the one-pass row reductions.
     x is a tensor or an address (inspected, never dereferenced)."""
     return _ext.tm_row_walk(M, N, ld, BR, BC, aligned, _ptr(x))
+
+
+def tm_map_walk(op, x, ldx, y, ldy, M, N, TM, TN, aligned, variant=TM_VAR_AUTO, bias=None):
+    """Returns (status, walk, items): the plan an element-wise map would run (op 0 affine, 1 scale,
+    2 copy, 3 channel with the vector bias).  x, y, bias: tensors or addresses (inspected, never
+    dereferenced)."""
+    return _ext.tm_map_walk(op, _ptr(x), ldx, _ptr(y), ldy, M, N, TM, TN, aligned, variant, _ptr(bias))
 
 
 def tm_pad_extents(M, N, TM, TN):

@@ -102,6 +102,17 @@ typedef enum {
                             strided walk's modest cost.  Same results as TM_COL_NAIVE. */
 } tm_colwalk;
 
+/* How the element-wise maps cut a call into work (reported by tm_map_walk). */
+typedef enum {
+    TM_MAP_NONE = 0,  /* nothing to launch (M or N is 0) */
+    TM_MAP_FLAT = 1,  /* the view's rows are contiguous in both tensors: one flat row of 1 KiB work
+                         items, only its end ragged */
+    TM_MAP_SPAN = 2,  /* padded rows as one span of 1 KiB items on y's 1 KiB grid, the columns past
+                         N masked per 16-byte chunk ([SLICING] "Masking"); x's row stride may differ
+                         from y's by a multiple of 4 floats */
+    TM_MAP_TILES = 3  /* the 2-D tile schedule: whole tiles unmasked, edge tiles masked */
+} tm_mapwalk;
+
 /* ---- element-wise maps over tiles --------------------------------------------------------------
  * x: input, M x N, row stride ldx.  y: output, M x N, row stride ldy.  TM, TN: tile.  aligned: 0|1.
  * variant: tm_variant.  The tile is what the alignment promise is made for.  How the work is cut
@@ -294,6 +305,17 @@ int tm_split(int64_t K, int64_t T, int64_t *nfull, int64_t *rem);
  * TM_E_INVAL if an output pointer is NULL. */
 int tm_row_walk(int64_t M, int64_t N, int64_t ld, int BR, int BC, int aligned, const void *x,
                 int64_t *bc, int64_t *nfull, int64_t *rem, int *lanes);
+
+/* The plan an element-wise map would run ([SLICING] "Masking": which elements are masked follows
+ * from it).  op: 0 = tm_map_affine, 1 = tm_scale2d, 2 = tm_copy2d, 3 = tm_channel_affine with the
+ * channel vector `bias` and no scale (bias is ignored for ops 0-2); the other arguments as for
+ * that call.  Writes *walk (tm_mapwalk) and *items, the work items of the launch (one per
+ * workgroup, before the grid is capped; 0 with TM_MAP_NONE).  Pointers are only inspected, never
+ * dereferenced.  Returns what the call would return before launching (TM_E_INVAL, TM_E_ALIGN,
+ * TM_E_UNSUPPORTED, and TM_E_INVAL for an op out of range or a NULL output pointer); the outputs
+ * are written only on TM_OK. */
+int tm_map_walk(int op, const void *x, int64_t ldx, const void *y, int64_t ldy, int64_t M, int64_t N,
+                int TM, int TN, int aligned, int variant, const void *bias, int *walk, int64_t *items);
 
 /* Tile scheduler counts ([SLICING] "Masking"): *tiles_m = ceil(M / TM), *tiles_n = ceil(N / TN) and
  * *whole = the number of tiles lying entirely inside the M x N tensor; the other tiles are edge

@@ -24,7 +24,7 @@
 
 #include "../../edge_masking_vector_amd/csrc/plan.h"
 
-static long g_checked = 0, g_failed = 0, g_flat = 0, g_rows = 0, g_skew = 0;
+static long g_checked = 0, g_failed = 0, g_flat = 0, g_rows = 0, g_skew = 0, g_dead_items = 0;
 
 #define CHECK(cond, ...)                                   \
     do {                                                   \
@@ -110,11 +110,16 @@ static void replay_flat(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld,
 static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ldx_, int64_t ldy_, const char *tag) {
     const int64_t ldx = ldx_, ldy = ldy_, ld = ldy, pad = ldy - N, dld = ldx - ldy;
     const bool diff = dld != 0;
-    CHECK(!p.aligned && M > 1 && p.ldx == ldx && p.ldy == ldy && pad >= 0 && (diff || pad > 0) && dld % 4 == 0 &&
-              (pad < 32 || pad * 8 <= N) && N >= tmp::kRowsSpanMinN &&
-              (p.access == tmp::kVec4 || p.access == tmp::kScalar),
-          "%s span plan outside its case", tag);
     const uintptr_t xa = reinterpret_cast<uintptr_t>(p.x), ya = reinterpret_cast<uintptr_t>(p.y);
+    // padding: under a line, an eighth of the row, or (y's rows off the line grid) a quarter of
+    // rows of 2048 floats or more on the 16-byte grid, a quarter or (2048 floats or more) half off it
+    const bool y_lines = ya % 128 == 0 && ldy % 32 == 0, y16 = ya % 16 == 0 && ldy % 4 == 0;
+    const bool wide_ok = !y_lines && (y16 ? N >= tmp::kRowsWideMinN && pad * 4 <= N
+                                          : pad * 4 <= N || (N >= tmp::kRowsWideMinN && pad * 2 <= N));
+    CHECK(!p.aligned && M > 1 && p.ldx == ldx && p.ldy == ldy && pad >= 0 && (diff || pad > 0) && dld % 4 == 0 &&
+              (pad < 32 || pad * 8 <= N || wide_ok) && N >= tmp::kRowsSpanMinN &&
+              (!diff || N >= tmp::kRowsDiffMinN) && (p.access == tmp::kVec4 || p.access == tmp::kScalar),
+          "%s span plan outside its case", tag);
     const int64_t span = (M - 1) * ld + N;
     CHECK(p.span == uint64_t(span) && p.head == (ya / 4) % 256 && (xa - ya) % 16 == 0 && p.ld_div.d == ld,
           "%s span geometry", tag);
@@ -138,7 +143,20 @@ static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ldx
         }
         return false;
     };
-    for (uint32_t w = 0; w < p.nwork; ++w)
+    for (uint32_t w = 0; w < p.nwork; ++w) {
+        if (wide) {
+            // the wave exits when none of its chunks holds an element of a row or the next
+            bool some = false;
+            for (int t = 0; t < 64; ++t) {
+                const int32_t q = int32_t(w * 256u + 4u * t) - int32_t(p.head);
+                const uint32_t c = q > 0 ? uint32_t(q % ld) : 0u;
+                some = some || (q + 3 >= 0 && q < span && (q < 0 || c < N || c + 3 >= ld));
+            }
+            if (!some) {
+                ++g_dead_items;
+                continue;
+            }
+        }
         for (int t = 0; t < 64; ++t) {
             const int32_t q = int32_t(w * 256u + 4u * t) - int32_t(p.head);
             uint32_t r = 0, c = 0;
@@ -193,6 +211,7 @@ static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ldx
                 }
             }
         }
+    }
     CHECK(!bad_load, "%s span: a load off x's live lines (or a wrong row or column)", tag);
     CHECK(!bad_store, "%s span: a misplaced store", tag);
     CHECK(!bad_source, "%s span: an output element taken from the wrong x element", tag);
@@ -342,6 +361,34 @@ static void check_maps_diff() {
                                     replay_map(p, M, N, ldy, xb, tag);
                                 }
     CHECK(spans >= 500, "only %ld different-stride span plans", spans);
+}
+
+// Wide padding off the line grid: spans whose items lie wholly inside the padding (the waves that
+// exit at once), rows on and off the 16-byte grid, on both sides of each width and padding limit.
+static void check_maps_wide() {
+    long spans = 0, tiles = 0;
+    for (int64_t M : {int64_t{2}, int64_t{3}, int64_t{9}})
+        for (int64_t N : {int64_t{1000}, int64_t{2047}, int64_t{2048}, int64_t{2500}, int64_t{4100}})
+            for (int64_t pad : {N / 8 + 4, N / 4, N / 4 + 1, N / 4 + 2, N / 2 - 1, N / 2, N / 2 + 1, N / 2 + 3})
+                for (int dx : {0, 4, -4})
+                    for (uintptr_t off : {uintptr_t{0}, uintptr_t{4}, uintptr_t{8}, uintptr_t{64}})
+                        for (int op : {int(tmp::kAffine), int(tmp::kChannel)}) {
+                            const int64_t ldy = N + pad, ldx = std::max(N, ldy + dx);
+                            tmp::MapPlan p;
+                            const uintptr_t xb = 0x100000 + off, yb = 0x40000000 + off;
+                            const int st = tmp::plan_map(op, fake(xb), ldx, const_cast<float *>(fake(yb)), ldy, M, N, 1.5f,
+                                                         0.f, 64, 64, 0, TM_VAR_AUTO, &p, nullptr, fake(0x200000));
+                            if (st != TM_OK || !p.launch)
+                                continue;
+                            char tag[160];
+                            std::snprintf(tag, sizeof tag, "map wide M=%ld N=%ld ldx=%ld ldy=%ld off=%lu op=%d", long(M),
+                                          long(N), long(ldx), long(ldy), (unsigned long)off, op);
+                            spans += p.rows;
+                            tiles += !p.rows && !p.flat;
+                            replay_map(p, M, N, ldy, xb, tag);
+                        }
+    CHECK(spans >= 200 && tiles >= 200, "wide padding: %ld span and %ld tile plans", spans, tiles);
+    CHECK(g_dead_items > 0, "no span wave wholly inside the padding was replayed");
 }
 
 static void check_maps() {
@@ -864,6 +911,7 @@ int main() {
     check_extremes();
     check_maps();
     check_maps_diff();
+    check_maps_wide();
     check_transposes();
     check_reductions();
     check_split_rows();

@@ -157,6 +157,75 @@ def test_row_walk_errors():
     assert tm.tm_row_walk(0, 10, 10, 1, 64, 0, None)[0] == tm.TM_OK
 
 
+# ---- the maps' plan (tm_map_walk) ----------------------------------------------------------------
+
+X0, Y0 = LINE, LINE + (1 << 30)   # two line-aligned bases (inspected only)
+
+
+def walk(M, N, ldx, ldy, xoff=0, yoff=0, var=None, op=0, bias=None, aligned=0, TM=64, TN=64):
+    var = tm.TM_VAR_AUTO if var is None else var
+    st, w, items = tm.tm_map_walk(op, X0 + 4 * xoff, ldx, Y0 + 4 * yoff, ldy, M, N, TM, TN, aligned, var, bias)
+    assert st == tm.TM_OK, (M, N, ldx, ldy, xoff, yoff, st)
+    return w, items
+
+
+def test_map_walk_bench_views():
+    """The plans the benchmark's map paths are labelled with."""
+    SPAN, TILES, FLAT = tm.TM_MAP_SPAN, tm.TM_MAP_TILES, tm.TM_MAP_FLAT
+    assert walk(4100, 1000, 1000, 1000) == (FLAT, -(-4100 * 1000 // 256))   # one flat row of 1 KiB items
+    assert walk(4096, 4096, 4096, 4096, var=tm.TM_VAR_VEC4, aligned=1, TM=32, TN=128) == (FLAT, 65536)
+    for (M, N, ldx, ldy) in ((4100, 1000, 1001, 1001), (4100, 1000, 1004, 1004), (4100, 4100, 4104, 4104),
+                             (4100, 4100, 4104, 4108), (4100, 4100, 4700, 4700)):
+        # one span of 1 KiB items on y's 1 KiB grid from y[0] (line-aligned: head 0)
+        assert walk(M, N, ldx, ldy) == (SPAN, -(-((M - 1) * ldy + N) // 256)), (M, N, ldx, ldy)
+    assert walk(4100, 1000, 1004, 1008)[0] == TILES   # different strides, rows under 1024 floats
+    assert walk(4100, 4100, 5120, 5120)[0] == TILES   # wide padding, rows on the line grid
+    # the span's first item starts on y's 1 KiB grid: y 100 floats past it adds 100 to the span
+    assert walk(4100, 1000, 1001, 1001, 100, 100) == (SPAN, -(-(100 + 4099 * 1001 + 1000) // 256))
+
+
+def test_map_walk_span_limits():
+    """Where the span stops and the 2-D tiles take over: one stride (or strides a multiple of 4
+    floats apart over rows of 1024 floats or more), both bases the same distance past a 16-byte
+    boundary, rows of 64 floats or more, and padding under a line, at most an eighth of the row,
+    or -- y's rows off the line grid -- a quarter of 16-byte rows of 2048 floats or more, a
+    quarter of rows off the 16-byte grid, or half of them from 2048 floats on."""
+    SPAN, TILES = tm.TM_MAP_SPAN, tm.TM_MAP_TILES
+    assert walk(100, 1000, 1031, 1031)[0] == SPAN     # under a line
+    assert walk(100, 1000, 1125, 1125)[0] == SPAN     # an eighth
+    assert walk(100, 1000, 1128, 1128)[0] == TILES    # past it, 16-byte rows under 2048 floats
+    assert walk(100, 2048, 2556, 2556)[0] == SPAN     # a quarter of 16-byte rows of 2048 floats
+    assert walk(100, 2048, 2564, 2564)[0] == TILES    # past it
+    assert walk(100, 2044, 2552, 2552)[0] == TILES    # a quarter, rows under 2048 floats
+    assert walk(100, 2048, 2560, 2560)[0] == TILES    # rows on the line grid: an eighth at most
+    assert walk(100, 2048, 2304, 2304, 32, 32)[0] == SPAN
+    assert walk(100, 2048, 2560, 2560, 4, 4)[0] == SPAN   # the same stride, bases off the line grid
+    assert walk(100, 1000, 1249, 1249)[0] == SPAN     # a quarter of rows off the 16-byte grid
+    assert walk(100, 1000, 1251, 1251)[0] == TILES
+    assert walk(100, 2048, 3071, 3071)[0] == SPAN     # half of them from 2048 floats on
+    assert walk(100, 2048, 3073, 3073)[0] == TILES
+    assert walk(100, 2048, 3072, 3072, 2, 2)[0] == SPAN    # 16-byte stride, base off the 16-byte grid
+    assert walk(100, 2047, 3071, 3071)[0] == TILES    # half, rows under 2048 floats
+    assert walk(100, 1100, 1104, 1108)[0] == SPAN     # different strides, 1024 floats or more
+    assert walk(100, 1023, 1027, 1031)[0] == TILES
+    assert walk(100, 1100, 1101, 1104)[0] == TILES    # strides not a multiple of 4 floats apart
+    assert walk(100, 1024, 1024, 1024 + 128, 0, 0)[0] == TILES   # both on the line grid, strides differ
+    assert walk(100, 1000, 1001, 1001, 1, 0)[0] == TILES   # bases at different 16-byte offsets
+    assert walk(100, 63, 64, 64)[0] == TILES          # rows under 64 floats
+    assert walk(100, 1000, 1004, 1004, var=tm.TM_VAR_VEC4_UNDERSTATED)[0] == TILES
+    assert walk(1, 1000, 1004, 1004)[0] == tm.TM_MAP_FLAT   # one row is a flat row
+    assert walk(0, 1000, 1004, 1004) == (tm.TM_MAP_NONE, 0)
+
+
+def test_map_walk_channel_and_errors():
+    assert walk(300, 1000, 1004, 1004, op=3, bias=LINE + (2 << 30))[0] == tm.TM_MAP_SPAN
+    assert walk(300, 1000, 1000, 1000, op=3, bias=LINE + (2 << 30))[0] == tm.TM_MAP_FLAT
+    assert tm.tm_map_walk(3, X0, 1004, Y0, 1004, 300, 1000, 64, 64, 0, 0, None)[0] == tm.TM_E_INVAL  # no bias
+    assert tm.tm_map_walk(4, X0, 1004, Y0, 1004, 300, 1000, 64, 64, 0, 0)[0] == tm.TM_E_INVAL
+    assert tm.tm_map_walk(0, X0, 1004, Y0, 1004, 4100, 1000, 64, 64, 1, 0)[0] == tm.TM_E_ALIGN
+    assert tm.tm_map_walk(0, X0, 999, Y0, 1004, 4, 1000, 64, 64, 0, 0)[0] == tm.TM_E_INVAL   # ldx < N
+
+
 # ---- tile scheduler counts ---------------------------------------------------------------------
 
 def test_plan_tiles_workload_shapes():

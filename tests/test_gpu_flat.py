@@ -212,11 +212,13 @@ def test_padded_rows_one_span(dev, op, M, N, ld, off, variant):
     (100, 1000, 1001, 1001, 1, 0),    # bases at different distances past a 16-byte boundary
     (100, 1000, 1004, 1008, 0, 0),    # different strides over rows under 1024 floats
     (100, 60, 61, 61, 0, 0),          # rows narrower than the span's minimum
-    (100, 1000, 1040, 1040, 0, 0),    # a line or more of padding
+    (100, 1000, 1500, 1500, 0, 0),    # half a row of padding, 16-byte rows under 2048 floats
+    (50, 2048, 3072, 3072, 0, 0),     # wide padding between rows on the line grid
 ])
 def test_padded_rows_outside_the_span(dev, M, N, ldx, ldy, xoff, yoff):
     """Padded views the span does not take (different strides or base offsets, narrow rows, wide
-    padding) keep the 2-D tile plan: the same results bit for bit."""
+    padding on the 16-byte grid or on the line grid) keep the 2-D tile plan: the same results bit
+    for bit."""
     note("no span %dx%d ldx %d ldy %d" % (M, N, ldx, ldy))
     _check_strided(dev, "affine", M, N, ldx, ldy, xoff, yoff, tm.TM_VAR_AUTO, seed=7 * M + N)
 
@@ -240,23 +242,29 @@ def test_padded_rows_in_place(dev, ld, off):
     assert np.array_equal(bits(X.host()), bits(want))
 
 
-@pytest.mark.parametrize("M,N,ldx,ldy,TM,TN,variant", [
-    (4100, 1000, 1001, 1001, 64, 64, tm.TM_VAR_AUTO),     # the bench's padded maps: one span
-    (4100, 1000, 1004, 1004, 64, 64, tm.TM_VAR_VEC4),
-    (4100, 4100, 4104, 4104, 32, 128, tm.TM_VAR_VEC4),
-    (4100, 4100, 4104, 4108, 32, 128, tm.TM_VAR_VEC4),    # one span over y, different strides
-    (4100, 1000, 1004, 1008, 64, 64, tm.TM_VAR_VEC4),     # the 2-D tile plan
-    (4100, 4100, 4104, 4700, 32, 128, tm.TM_VAR_VEC4),
+SPAN, TILES = tm.TM_MAP_SPAN, tm.TM_MAP_TILES
+
+
+@pytest.mark.parametrize("M,N,ldx,ldy,TM,TN,variant,walk", [
+    (4100, 1000, 1001, 1001, 64, 64, tm.TM_VAR_AUTO, SPAN),     # the bench's padded maps
+    (4100, 1000, 1004, 1004, 64, 64, tm.TM_VAR_VEC4, SPAN),
+    (4100, 4100, 4104, 4104, 32, 128, tm.TM_VAR_VEC4, SPAN),
+    (4100, 4100, 4104, 4108, 32, 128, tm.TM_VAR_VEC4, SPAN),    # different strides
+    (4100, 4100, 4700, 4700, 32, 128, tm.TM_VAR_VEC4, SPAN),    # 600 floats of padding
+    (4100, 1000, 1004, 1008, 64, 64, tm.TM_VAR_VEC4, TILES),
+    (4100, 4100, 5120, 5120, 32, 128, tm.TM_VAR_VEC4, TILES),
 ])
-def test_bench_padded_maps_full_size(dev, M, N, ldx, ldy, TM, TN, variant):
+def test_bench_padded_maps_full_size(dev, M, N, ldx, ldy, TM, TN, variant, walk):
     """The padded-row maps the benchmark times, at their full sizes and in the same calls (ragged
-    path, the same tiles and variants), bit for bit against the oracle, padding untouched."""
+    path, the same tiles and variants), bit for bit against the oracle, padding untouched, and on
+    the plan the benchmark labels them with (tm_map_walk)."""
     note("bench padded map %dx%d ld %d/%d" % (M, N, ldx, ldy))
     nx, ny = (M - 1) * ldx + N, (M - 1) * ldy + N
     xh = inputs.matrix(inputs.ragged_input(M, N, seed=12), M, N, ldx)[:nx].copy()
     X = Guarded(nx, dev, guard=LINE_GUARD_FLOATS)
     X.upload(xh)
     Y = Guarded(ny, dev, guard=LINE_GUARD_FLOATS)
+    assert tm.tm_map_walk(0, X.ptr, ldx, Y.ptr, ldy, M, N, TM, TN, 0, variant)[:2] == (tm.TM_OK, walk)
     assert tm.tm_map_affine(X.ptr, ldx, Y.ptr, ldy, M, N, 0.75, -0.25, TM, TN, 0, variant) == tm.TM_OK
     torch.cuda.synchronize()
     want = sentinel_host(Y.buf.numel())
@@ -302,10 +310,17 @@ def test_padded_rows_channel_span(dev, M, N, ld, off, boff, with_scale):
     assert X.guards_intact() and B.guards_intact()
 
 
-@pytest.mark.parametrize("M,N,ld,off", [(100, 4100, 4140, 0), (300, 1000, 1125, 2), (41, 561, 593, 1)])
+@pytest.mark.parametrize("M,N,ld,off", [
+    (100, 4100, 4140, 0), (300, 1000, 1125, 2), (41, 561, 593, 1),   # up to an eighth of the row
+    (64, 4100, 4700, 0),     # a quarter of 16-byte rows of 2048 floats or more
+    (100, 1000, 1201, 0),    # a quarter of rows off the 16-byte grid
+    (40, 2500, 3750, 1),     # half of rows off the 16-byte grid, 2048 floats or more
+    (16, 2048, 3072, 2),     # ... rows on the 16-byte grid, base off it
+])
 def test_padded_rows_wide_padding(dev, M, N, ld, off):
-    """Padding of a line or more (at most an eighth of the row) is still one span; chunks wholly
-    inside it load the row's last live chunk and store nothing."""
+    """Padding of a line or more is still one span (up to an eighth of the row, or wider off the
+    line grid); chunks wholly inside it load the row's last live chunk and store nothing, and
+    waves wholly inside it exit at once."""
     note("span wide padding %dx%d ld %d off %d" % (M, N, ld, off))
     _check_strided(dev, "affine", M, N, ld, ld, off, off, tm.TM_VAR_AUTO, seed=M * 7 + ld)
 
@@ -317,6 +332,7 @@ def test_padded_rows_wide_padding(dev, M, N, ld, off):
     ("scale", 300, 1100, 1140, 1100, 2),    # x padded by 40, y contiguous
     ("affine", 257, 1777, 2801, 1781, 3),   # x padding far wider than y's
     ("affine", 64, 4100, 4104, 4108, 0),
+    ("scale", 64, 4100, 4104, 4700, 0),     # y padded by 600 floats
     ("affine", 300, 1100, 1101, 1104, 1),   # strides 3 apart: the 2-D tile plan
     ("affine", 300, 1000, 1004, 1008, 0),   # rows under 1024 floats: the 2-D tile plan
 ])

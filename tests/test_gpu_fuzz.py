@@ -376,8 +376,9 @@ def test_fuzz_transposes(dev):
 
 def test_fuzz_padded_spans(dev):
     """Padded rows (the span plan of 1 KiB items on y's 1 KiB grid when the bases sit the same
-    distance past a 16-byte boundary, y's padding is under a line or at most an eighth of the row
-    and x's stride is the same or, over rows of 1024 floats or more, a multiple of 4 floats away;
+    distance past a 16-byte boundary, y's padding is under a line, at most an eighth of the row or
+    (rows off the line grid) up to half of it, and x's stride is the same or, over rows of 1024
+    floats or more, a multiple of 4 floats away;
     the 2-D tile plan otherwise): random shapes, paddings, strides, offsets, ops (the channel op
     too) and variants, bit for bit, the padding between rows untouched."""
     rng = random.Random(4242)
@@ -387,8 +388,11 @@ def test_fuzz_padded_spans(dev):
         # x's stride: mostly the same, else (over rows of 1024 floats or more) a multiple of 4
         # floats away, or not
         diff = rng.random() >= 0.6
-        M, N = rng.randint(2, 300), (rng.randint(1024, 2600) if diff else rng.randint(64, 1100))
-        ld = N + (rng.randint(1, 31) if rng.random() < 0.7 else rng.randint(32, max(32, N // 8 + 3)))
+        M = rng.randint(2, 300)
+        N = rng.randint(1024, 2600) if diff else (rng.randint(64, 1100) if rng.random() < 0.7 else rng.randint(1024, 4200))
+        u = rng.random()   # y's padding: under a line, up to an eighth of the row, or wider
+        ld = N + (rng.randint(1, 31) if u < 0.55 else rng.randint(32, max(32, N // 8 + 3)) if u < 0.8
+                  else rng.randint(N // 8, N // 2 + 3))
         ldx = max(N, ld + rng.choice([-8, -4, 4, 8, 12, 40, 3, -1])) if diff else ld
         offx = rng.choice([0, 1, 2, 3, 5, 64, 100])
         offy = offx if rng.random() < 0.8 else rng.choice([0, 1, 2, 3])
