@@ -411,16 +411,21 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
              "one span over y, x's rows 4 floats shorter"),
             (4100, 4100, 4700, 4700, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ld4700_ragged_2d", "span",
              "one span, 600 floats of padding between rows (waves wholly inside it exit at once)"),
+            (4100, 4100, 4104, 4104, 32, 128, tm.TM_VAR_AUTO, "scale_4100x4100_ld4104_xoff1_ragged_2d", "span",
+             "one span over y, x's view one float past y's 16-byte phase: x's chunks are 4-byte "
+             "aligned 16-byte loads"),
             (4100, 1000, 1004, 1008, 64, 64, tm.TM_VAR_VEC4, "affine_4100x1000_ldx1004_ldy1008_ragged_tiles", "tiles",
              "the 2-D tile plan (different strides, rows under 1024 floats): 16-byte chunks, 4-row "
              "bottom and 64x40 right-edge tiles masked"),
             (4100, 4100, 5120, 5120, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ld5120_ragged_tiles", "tiles",
              "the 2-D tile plan (rows on the 128-byte line grid, 1020 floats of padding): 16-byte "
              "chunks, 32x128 tiles, 4-row bottom and 4-column right edge tiles masked")):
+        xoff = 1 if "xoff1" in name else 0   # x's view this many floats into its buffer
         xh = inputs.matrix(inputs.ragged_input(M, N, seed=12), M, N, ldx)
+        xh = np.concatenate([np.zeros(xoff, np.float32), xh])
         nb = 2 * M * N * 4
         R = sets_for(M * ldx * 4 + M * ldy * 4)
-        xs = rotated(torch, xh, R, dev)
+        xs = [x[xoff:] for x in rotated(torch, xh, R, dev)]
         ys = [torch.zeros(M * ldy, device=dev) for _ in range(R)]
         timed(name, nb, R,
               lambda i, M=M, N=N, ldx=ldx, ldy=ldy, TM=TM, TN=TN, var=var: ok(tm.tm_map_affine(

@@ -27,6 +27,13 @@ __device__ __forceinline__ void st16_nt(float *p, f4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<f4 *>(p));
 }
 __device__ __forceinline__ float ld4_nt(const float *p) { return __builtin_nontemporal_load(p); }
+
+// 16-byte load from a 4-byte aligned address (one global_load_dwordx4: the HSA ABI runs the GPU in
+// its unaligned access mode, so a vector access need only be aligned to its element).
+typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ f4 ld16u_nt(const float *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f4u *>(p));
+}
 __device__ __forceinline__ void st4_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
 
 // One contiguous block of `bytes` bytes addressed through a buffer resource (raw buffer: stride 0,

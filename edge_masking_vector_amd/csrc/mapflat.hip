@@ -142,7 +142,7 @@ __global__ __launch_bounds__(flat_threads<MODE>()) void map_flat(const float *__
 // The channel op (OP = kChannel) takes element (row, column c)'s channel c: y = fmaf(x, scale[c],
 // bias[c]), scale 1 when absent; a whole chunk's four channels are one 16-byte load of each vector
 // when cvec16 (both vectors 16-byte aligned and every chunk starting on a column divisible by 4).
-template <int OP, bool WIDE, bool DIFF>
+template <int OP, bool WIDE, bool DIFF, bool SHIFT = false>
 __device__ __forceinline__ void rows_body(const float *__restrict__ x, float *__restrict__ y, float alpha, float beta,
                                           uint32_t nwork, uint32_t head, uint32_t span, uint32_t ld, uint32_t N,
                                           uint64_t c_ld, const float *__restrict__ scale,
@@ -180,8 +180,34 @@ __device__ __forceinline__ void rows_body(const float *__restrict__ x, float *__
                 qa = last - int32_t((uint32_t(last) + head) & 3u);
             }
             int32_t xa = DIFF ? qa + int32_t(r) * dld : qa;
-            xa = q < q_first ? q_first : (q > q_last ? (DIFF ? x_last : q_last) : xa);
-            if constexpr (DIFF) {
+            if constexpr (!SHIFT)
+                xa = q < q_first ? q_first : (q > q_last ? (DIFF ? x_last : q_last) : xa);
+            if constexpr (SHIFT) {
+                // x at another 4-byte phase than y: x's chunk is the 16 bytes from x + xa, 4-byte
+                // aligned.  The span's two end chunks (some element outside the span) load their
+                // live elements one by one, so that no load leaves the view.
+                const bool cross = q >= 0 && c + 3 >= ld && int64_t(q) - c + ld < int64_t(span);
+                const int32_t xb = cross ? xa + dld : xa;
+                if (cross && c >= N)
+                    xa = xb;
+                if (q >= 0 && q + 3 < int32_t(span)) {
+                    xv = ld16u_nt(x + xa);
+                    xn = xv;
+                    if (dld != 0 && __builtin_amdgcn_ballot_w64(cross) != 0)
+                        xn = ld16u_nt(x + xb);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int32_t f = q + i;
+                        const uint32_t ci = q >= 0 ? c + i : uint32_t(f);
+                        const bool nxt = q >= 0 && ci >= ld;
+                        const uint32_t cl = nxt ? ci - ld : ci;
+                        const int32_t row = int32_t(r) + (nxt ? 1 : 0);
+                        xv[i] = f >= 0 && f < int32_t(span) && cl < N ? x[f + row * dld] : 0.0f;
+                    }
+                    xn = xv;
+                }
+            } else if constexpr (DIFF) {
                 // elements past the row's end belong to the next row, dld further on in x; when
                 // none of the chunk's elements is live in its own row, both loads take the next
                 // row's chunk (x's padding past the row may hold no live element in its line)
@@ -264,6 +290,48 @@ __global__ __launch_bounds__(64) void map_rows(const float *__restrict__ x, floa
     rows_body<OP, WIDE, false>(x, y, alpha, beta, nwork, head, span, ld, N, c_ld, nullptr, nullptr, 0u, 0, 0);
 }
 
+// One contiguous row (contiguous rows folded into one) that the flat kernel cannot take: x at
+// another 4-byte phase than y, or a base off the 128-byte line grid.  Items on y's 1 KiB grid
+// (item 0 starting `head` floats before y[0]); lane t moves the 16 bytes of y from element
+// q = 256 w + 4 t - head, x's as one 4-byte aligned 16-byte load.  The row's two end chunks
+// (some element outside it) move their elements one by one, so that no access leaves the row.
+template <int OP>
+__global__ __launch_bounds__(64) void map_flat_shift(const float *__restrict__ x, float *__restrict__ y, float alpha,
+                                                     float beta, uint32_t nwork, uint32_t head, uint32_t n) {
+    const int t = threadIdx.x;
+    for (uint32_t w = blockIdx.x; w < nwork; w += gridDim.x) {
+        const int32_t q = int32_t(w * 256u + 4u * t) - int32_t(head);
+        const __amdgpu_buffer_rsrc_t ry = segment_rsrc(y + (int64_t(w) * 256 - head), kItemFloats * 4);
+        if (q >= 0 && q + 4 <= int32_t(n)) {
+            const f4 v = op4<OP>(ld16u_nt(x + q), alpha, beta);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), ry, t * 16, 0, kFlatStorePolicy);
+        } else {
+            f4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int32_t f = q + i;
+                v[i] = f >= 0 && f < int32_t(n) ? op1<OP>(x[f], alpha, beta) : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int32_t f = q + i;
+                const float e = v[i];
+                if (f >= 0 && f < int32_t(n))
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), ry, (t * 4 + i) * 4, 0, kFlatStorePolicy);
+            }
+        }
+    }
+}
+
+// x at another 4-byte phase than y (bases not a multiple of 16 bytes apart, or strides not a
+// multiple of 4 floats apart; dld = ldx - ldy, 0 for one stride): 4-byte aligned 16-byte loads.
+template <int OP>
+__global__ __launch_bounds__(64) void map_rows_shift(const float *__restrict__ x, float *__restrict__ y, float alpha,
+                                                     float beta, uint32_t nwork, uint32_t head, uint32_t span,
+                                                     uint32_t ld, uint32_t N, uint64_t c_ld, int32_t dld) {
+    rows_body<OP, true, true, true>(x, y, alpha, beta, nwork, head, span, ld, N, c_ld, nullptr, nullptr, 0u, dld, 0);
+}
+
 // Different strides (dld = ldx - ldy, a multiple of 4; x_last: x's index of the span's last chunk).
 template <int OP>
 __global__ __launch_bounds__(64) void map_rows_diff(const float *__restrict__ x, float *__restrict__ y, float alpha,
@@ -273,14 +341,14 @@ __global__ __launch_bounds__(64) void map_rows_diff(const float *__restrict__ x,
     rows_body<OP, true, true>(x, y, alpha, beta, nwork, head, span, ld, N, c_ld, nullptr, nullptr, 0u, dld, x_last);
 }
 
-template <bool WIDE, bool DIFF>
+template <bool WIDE, bool DIFF, bool SHIFT>
 __global__ __launch_bounds__(64) void map_rows_channel(const float *__restrict__ x, float *__restrict__ y,
                                                        uint32_t nwork, uint32_t head, uint32_t span, uint32_t ld,
                                                        uint32_t N, uint64_t c_ld, const float *__restrict__ scale,
                                                        const float *__restrict__ bias, uint32_t cvec16, int32_t dld,
                                                        int32_t x_last) {
-    rows_body<tmp::kChannel, WIDE, DIFF>(x, y, 0.0f, 0.0f, nwork, head, span, ld, N, c_ld, scale, bias, cvec16, dld,
-                                        x_last);
+    rows_body<tmp::kChannel, WIDE, DIFF, SHIFT>(x, y, 0.0f, 0.0f, nwork, head, span, ld, N, c_ld, scale, bias, cvec16,
+                                               dld, x_last);
 }
 
 template <bool WIDE>
@@ -315,10 +383,25 @@ hipError_t launch_map_flat(const tmp::MapPlan &p, hipStream_t stream) {
             const float *scale = p.scale, *bias = p.bias;
             uint32_t cvec16 = p.cvec16 ? 1u : 0u;
             void *cargs[] = {&x, &y, &nwork, &head, &span, &ld, &N, &c_ld, &scale, &bias, &cvec16, &dld, &x_last};
-            const void *cfn = diff   ? reinterpret_cast<const void *>(&map_rows_channel<true, true>)
-                              : wide ? reinterpret_cast<const void *>(&map_rows_channel<true, false>)
-                                     : reinterpret_cast<const void *>(&map_rows_channel<false, false>);
+            const void *cfn = p.shift ? reinterpret_cast<const void *>(&map_rows_channel<true, true, true>)
+                              : diff  ? reinterpret_cast<const void *>(&map_rows_channel<true, true, false>)
+                              : wide  ? reinterpret_cast<const void *>(&map_rows_channel<true, false, false>)
+                                      : reinterpret_cast<const void *>(&map_rows_channel<false, false, false>);
             return hipLaunchKernel(cfn, dim3(p.grid), dim3(64), cargs, 0, stream);
+        }
+        if (p.M == 1) {
+            void *fargs[] = {&x, &y, &alpha, &beta, &nwork, &head, &span};
+            const void *ffn = p.op == tmp::kAffine  ? reinterpret_cast<const void *>(&map_flat_shift<tmp::kAffine>)
+                              : p.op == tmp::kScale ? reinterpret_cast<const void *>(&map_flat_shift<tmp::kScale>)
+                                                    : reinterpret_cast<const void *>(&map_flat_shift<tmp::kCopy>);
+            return hipLaunchKernel(ffn, dim3(p.grid), dim3(64), fargs, 0, stream);
+        }
+        if (p.shift) {
+            void *sargs[] = {&x, &y, &alpha, &beta, &nwork, &head, &span, &ld, &N, &c_ld, &dld};
+            const void *sfn = p.op == tmp::kAffine  ? reinterpret_cast<const void *>(&map_rows_shift<tmp::kAffine>)
+                              : p.op == tmp::kScale ? reinterpret_cast<const void *>(&map_rows_shift<tmp::kScale>)
+                                                    : reinterpret_cast<const void *>(&map_rows_shift<tmp::kCopy>);
+            return hipLaunchKernel(sfn, dim3(p.grid), dim3(64), sargs, 0, stream);
         }
         if (diff) {
             void *dargs[] = {&x, &y, &alpha, &beta, &nwork, &head, &span, &ld, &N, &c_ld, &dld, &x_last};

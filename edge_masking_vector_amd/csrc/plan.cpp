@@ -272,9 +272,18 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     const bool y16 = aligned_to(y, 16) && ldy % 4 == 0;
     const bool pad_ok = pad < kLineBytes / 4 || pad * 8 <= N ||
                         (!y_lines && (pad * 4 <= N ? N >= kRowsWideMinN || !y16 : !y16 && N >= kRowsWideMinN && pad * 2 <= N));
-    if (!aligned && M > 1 && pad >= 0 && (ldx != ldy ? !both_lines && N >= kRowsDiffMinN : pad > 0) && (ldx - ldy) % 4 == 0 &&
-        pad_ok && N >= kRowsSpanMinN && (access == kVec4 || access == kScalar) &&
-        (reinterpret_cast<uintptr_t>(x) - reinterpret_cast<uintptr_t>(y)) % 16 == 0) {
+    // x at another 4-byte phase than y's grid (bases not a multiple of 16 bytes apart, or strides
+    // not a multiple of 4 floats apart): the same span over y, x's chunks moved as 4-byte aligned
+    // 16-byte loads (SHIFT in mapflat.hip).  One flat row (contiguous rows, folded into one above)
+    // takes the span too when the flat kernel cannot: x at another phase, or a base off the
+    // 128-byte line grid (not the channel op, whose flat view finds channels by remainder).
+    const bool shift = (reinterpret_cast<uintptr_t>(x) - reinterpret_cast<uintptr_t>(y)) % 16 != 0 ||
+                       (M > 1 && (ldx - ldy) % 4 != 0);
+    const bool padded = M > 1 && pad >= 0 && (ldx != ldy ? !both_lines && N >= kRowsDiffMinN : pad > 0) && pad_ok;
+    const bool flat_row = M == 1 && op != kChannel && (shift || !aligned_to(x, kLineBytes) || !aligned_to(y, kLineBytes));
+    if (!aligned && (padded || flat_row) && N >= kRowsSpanMinN && (access == kVec4 || access == kScalar)) {
+        if (M == 1)
+            ldx = ldy = N;  // one row: the strides play no part
         const int64_t head = static_cast<int64_t>((reinterpret_cast<uintptr_t>(y) / 4) % 256);
         const int64_t span = (M - 1) * ldy + N;
         const int64_t xspan = (M - 1) * ldx + N;
@@ -289,6 +298,7 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
             plan->span = static_cast<uint32_t>(span);
             plan->ld_div = make_div32(static_cast<uint32_t>(ldy));
             plan->x_last = static_cast<int32_t>(q_last + (M - 1) * (ldx - ldy));
+            plan->shift = shift;
             plan->nwork = static_cast<uint32_t>(nwork);
             plan->grid = cap_grid(nwork);
             plan->x = x;

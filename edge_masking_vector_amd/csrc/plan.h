@@ -143,6 +143,7 @@ struct MapPlan {
     uint32_t span = 0;            // rows: (M - 1) * ld + N
     Div32 ld_div;                 // rows: divisor ld (y's row stride)
     int32_t x_last = 0;           // rows: x's index of the chunk that holds the span's last element
+    bool shift = false;           // rows: x at another 4-byte phase than y (4-byte aligned 16-byte loads)
     uint32_t group = 1;           // G
     uint32_t groups_n = 0;        // ceil(tiles_n / G)
     uint32_t tiles_n = 0;         // tiles along N

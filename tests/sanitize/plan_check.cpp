@@ -116,19 +116,25 @@ static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ldx
     const bool y_lines = ya % 128 == 0 && ldy % 32 == 0, y16 = ya % 16 == 0 && ldy % 4 == 0;
     const bool wide_ok = !y_lines && (y16 ? N >= tmp::kRowsWideMinN && pad * 4 <= N
                                           : pad * 4 <= N || (N >= tmp::kRowsWideMinN && pad * 2 <= N));
-    CHECK(!p.aligned && M > 1 && p.ldx == ldx && p.ldy == ldy && pad >= 0 && (diff || pad > 0) && dld % 4 == 0 &&
-              (pad < 32 || pad * 8 <= N || wide_ok) && N >= tmp::kRowsSpanMinN &&
-              (!diff || N >= tmp::kRowsDiffMinN) && (p.access == tmp::kVec4 || p.access == tmp::kScalar),
+    // x at another 4-byte phase than y: bases not a multiple of 16 bytes apart, or strides not a
+    // multiple of 4 floats apart (then x's chunks are 4-byte aligned 16-byte loads)
+    const bool shift = (xa - ya) % 16 != 0 || dld % 4 != 0;
+    const bool one_row = M == 1 && ldx == N && ldy == N && p.op != tmp::kChannel &&
+                         (shift || xa % 128 != 0 || ya % 128 != 0);
+    const bool padded = M > 1 && pad >= 0 && (diff || pad > 0) && (pad < 32 || pad * 8 <= N || wide_ok) &&
+                        (!diff || N >= tmp::kRowsDiffMinN);
+    CHECK(!p.aligned && p.ldx == ldx && p.ldy == ldy && (padded || one_row) && N >= tmp::kRowsSpanMinN &&
+              p.shift == shift && (p.access == tmp::kVec4 || p.access == tmp::kScalar),
           "%s span plan outside its case", tag);
-    const int64_t span = (M - 1) * ld + N;
-    CHECK(p.span == uint64_t(span) && p.head == (ya / 4) % 256 && (xa - ya) % 16 == 0 && p.ld_div.d == ld,
-          "%s span geometry", tag);
+    const int64_t span = (M - 1) * ld + N, xspan = (M - 1) * ldx + N;
+    CHECK(p.span == uint64_t(span) && p.head == (ya / 4) % 256 && p.ld_div.d == ld, "%s span geometry", tag);
     CHECK(p.nwork == uint64_t((p.head + span + 255) / 256) && p.grid >= 1 && p.grid <= p.nwork, "%s span items", tag);
     CHECK(!p.cvec16 || (p.op == tmp::kChannel && ya % 16 == 0 && ld % 4 == 0), "%s span channel vectors", tag);
     const int32_t q_first = -int32_t(p.head & 3u);
     const int32_t q_last = int32_t(span - 1) - int32_t((span - 1 + p.head) & 3u);
     CHECK(p.x_last == int32_t(q_last + (M - 1) * dld), "%s span x_last", tag);
-    const bool wide = pad >= 32 || diff;  // the kernels that redirect chunks wholly inside the padding
+    const bool wide = pad >= 32 || diff || shift;  // the kernels that redirect chunks wholly inside the padding
+    auto in_x = [&](int64_t xi) { return xi >= 0 && xi < xspan; };
     std::vector<uint8_t> hits(size_t(span), 0);
     bool bad_load = false, bad_store = false, bad_source = false;
     // a 16-byte block of x at float index xi: aligned, and inside a line that holds a live element
@@ -163,9 +169,9 @@ static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ldx
             if (q > 0) {
                 r = uint32_t(q / ld);
                 c = uint32_t(q % ld);
-                if (!diff && umulhi_mod(uint32_t(q), p.ld_div) != c)
+                if (!diff && !shift && umulhi_mod(uint32_t(q), p.ld_div) != c)
                     bad_load = true;
-                if (diff && umulhi_div(uint32_t(q), p.ld_div) != r)
+                if ((diff || shift) && umulhi_div(uint32_t(q), p.ld_div) != r)
                     bad_load = true;
             }
             int64_t xa0 = q < q_first ? q_first : (q > q_last ? q_last : q), xb0 = xa0;
@@ -176,17 +182,27 @@ static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ldx
                     qa = last - int32_t((uint32_t(last) + p.head) & 3u);
                 }
                 xa0 = diff ? int64_t(qa) + int64_t(r) * dld : qa;
-                xa0 = q < q_first ? q_first : (q > q_last ? (diff ? p.x_last : q_last) : xa0);
+                if (!shift)
+                    xa0 = q < q_first ? q_first : (q > q_last ? (diff ? p.x_last : q_last) : xa0);
                 xb0 = xa0;
-                if (diff) {
+                if (diff || shift) {
                     const bool cross = q >= 0 && c + 3 >= ld && int64_t(q) - c + ld < span;
                     xb0 = cross ? xa0 + dld : xa0;
                     if (cross && c >= N)
                         xa0 = xb0;  // no element of the chunk is live in its own row
                 }
             }
-            if (!live_line(xa0) || (diff && !live_line(xb0)))
+            // the span's end chunks of a shifted plan load their live elements one by one
+            const bool edge = shift && !(q >= 0 && int64_t(q) + 3 < span);
+            if (shift) {
+                // every float of every 16-byte load inside x's view
+                if (!edge)
+                    for (int k = 0; k < 4; ++k)
+                        if (!in_x(xa0 + k) || !in_x(xb0 + k))
+                            bad_load = true;
+            } else if (!live_line(xa0) || (diff && !live_line(xb0))) {
                 bad_load = true;
+            }
             const bool whole = q >= 0 && int64_t(q) + 3 < span && c + 3 < N;
             if (whole) {
                 const uintptr_t blk = ya + 4 * (int64_t(w) * 256 - p.head);
@@ -204,8 +220,9 @@ static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ldx
                     if (col != uint32_t(f % ld))
                         bad_store = true;
                     // the x element this output takes: row f / ldy, same column
-                    const int64_t src = (next && diff ? xb0 : xa0) + i;
-                    if (src != int64_t(f / ld) * ldx + col)
+                    const int64_t row = q >= 0 ? int64_t(r) + (next ? 1 : 0) : 0;
+                    const int64_t src = edge ? f + row * dld : (next && diff ? xb0 : xa0) + i;
+                    if (src != int64_t(f / ld) * ldx + col || !in_x(src))
                         bad_source = true;
                     ++hits[size_t(f)];
                 }
@@ -233,7 +250,7 @@ static void replay_map(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ld, 
         return;
     }
     if (p.rows) {
-        replay_rows(p, M, N, p.ldx, p.ldy, tag);
+        replay_rows(p, p.M, p.N, p.ldx, p.ldy, tag);  // the plan's view (contiguous rows: one row)
         return;
     }
     const int W = p.access == tmp::kScalar || p.access == tmp::kScalar1 ? 1 : 4;

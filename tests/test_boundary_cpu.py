@@ -185,11 +185,12 @@ def test_map_walk_bench_views():
 
 
 def test_map_walk_span_limits():
-    """Where the span stops and the 2-D tiles take over: one stride (or strides a multiple of 4
-    floats apart over rows of 1024 floats or more), both bases the same distance past a 16-byte
-    boundary, rows of 64 floats or more, and padding under a line, at most an eighth of the row,
-    or -- y's rows off the line grid -- a quarter of 16-byte rows of 2048 floats or more, a
-    quarter of rows off the 16-byte grid, or half of them from 2048 floats on."""
+    """Where the span stops and the 2-D tiles take over: one stride (or different strides over
+    rows of 1024 floats or more, unless both tensors' rows lie on the line grid), rows of 64
+    floats or more, and padding under a line, at most an eighth of the row, or -- y's rows off
+    the line grid -- a quarter of 16-byte rows of 2048 floats or more, a quarter of rows off the
+    16-byte grid, or half of them from 2048 floats on; x at any 4-byte phase.  Contiguous rows
+    are one row: the flat kernel's when both bases lie on the line grid at one phase, else a span."""
     SPAN, TILES = tm.TM_MAP_SPAN, tm.TM_MAP_TILES
     assert walk(100, 1000, 1031, 1031)[0] == SPAN     # under a line
     assert walk(100, 1000, 1125, 1125)[0] == SPAN     # an eighth
@@ -208,12 +209,17 @@ def test_map_walk_span_limits():
     assert walk(100, 2047, 3071, 3071)[0] == TILES    # half, rows under 2048 floats
     assert walk(100, 1100, 1104, 1108)[0] == SPAN     # different strides, 1024 floats or more
     assert walk(100, 1023, 1027, 1031)[0] == TILES
-    assert walk(100, 1100, 1101, 1104)[0] == TILES    # strides not a multiple of 4 floats apart
+    assert walk(100, 1100, 1101, 1104)[0] == SPAN     # strides 3 apart: x's chunks 4-byte aligned
     assert walk(100, 1024, 1024, 1024 + 128, 0, 0)[0] == TILES   # both on the line grid, strides differ
-    assert walk(100, 1000, 1001, 1001, 1, 0)[0] == TILES   # bases at different 16-byte offsets
+    assert walk(100, 1000, 1001, 1001, 1, 0)[0] == SPAN    # bases at different 16-byte phases
+    assert walk(100, 1000, 1000, 1000, 1, 0) == (SPAN, -(-100000 // 256))   # contiguous: one row
+    assert walk(100, 1000, 1000, 1000, 4, 4)[0] == SPAN    # one phase, bases off the line grid
+    assert walk(100, 1000, 1000, 1000, 32, 32)[0] == tm.TM_MAP_FLAT   # ... on it: the flat kernel
+    assert walk(1, 100, 100, 100, 1, 0)[0] == SPAN     # one row at another phase
+    assert walk(1, 63, 63, 63, 1, 0)[0] == TILES       # ... under 64 floats
     assert walk(100, 63, 64, 64)[0] == TILES          # rows under 64 floats
     assert walk(100, 1000, 1004, 1004, var=tm.TM_VAR_VEC4_UNDERSTATED)[0] == TILES
-    assert walk(1, 1000, 1004, 1004)[0] == tm.TM_MAP_FLAT   # one row is a flat row
+    assert walk(1, 1000, 1004, 1004)[0] == tm.TM_MAP_FLAT   # one row on the line grid is a flat row
     assert walk(0, 1000, 1004, 1004) == (tm.TM_MAP_NONE, 0)
 
 

@@ -161,13 +161,15 @@ def test_rowmax_walk_reported_and_exact(dev, BC, ld):
 
 
 # ---- padded rows in one span (mapflat.hip, map_rows) -------------------------------------------
-def _check_strided(dev, op, M, N, ldx, ldy, xoff, yoff, variant, seed, alpha=0.75, beta=-0.25):
+def _check_strided(dev, op, M, N, ldx, ldy, xoff, yoff, variant, seed, alpha=0.75, beta=-0.25, walk=None):
     nx, ny = (M - 1) * ldx + N, (M - 1) * ldy + N
     xh = inputs.uniform(seed, nx, -8.0, 8.0)
     X = Guarded(nx, dev, offset=xoff, guard=LINE_GUARD_FLOATS)
     X.upload(xh)
     Y = Guarded(ny, dev, offset=yoff, guard=LINE_GUARD_FLOATS)
     s = torch.cuda.current_stream()
+    if walk is not None:
+        assert tm.tm_map_walk(0, X.ptr, ldx, Y.ptr, ldy, M, N, 64, 64, 0, variant)[:2] == (tm.TM_OK, walk)
     if op == "affine":
         st = tm.tm_map_affine(X.ptr, ldx, Y.ptr, ldy, M, N, alpha, beta, 64, 64, 0, variant, s)
     elif op == "scale":
@@ -209,7 +211,6 @@ def test_padded_rows_one_span(dev, op, M, N, ld, off, variant):
 
 
 @pytest.mark.parametrize("M,N,ldx,ldy,xoff,yoff", [
-    (100, 1000, 1001, 1001, 1, 0),    # bases at different distances past a 16-byte boundary
     (100, 1000, 1004, 1008, 0, 0),    # different strides over rows under 1024 floats
     (100, 60, 61, 61, 0, 0),          # rows narrower than the span's minimum
     (100, 1000, 1500, 1500, 0, 0),    # half a row of padding, 16-byte rows under 2048 floats
@@ -245,23 +246,24 @@ def test_padded_rows_in_place(dev, ld, off):
 SPAN, TILES = tm.TM_MAP_SPAN, tm.TM_MAP_TILES
 
 
-@pytest.mark.parametrize("M,N,ldx,ldy,TM,TN,variant,walk", [
-    (4100, 1000, 1001, 1001, 64, 64, tm.TM_VAR_AUTO, SPAN),     # the bench's padded maps
-    (4100, 1000, 1004, 1004, 64, 64, tm.TM_VAR_VEC4, SPAN),
-    (4100, 4100, 4104, 4104, 32, 128, tm.TM_VAR_VEC4, SPAN),
-    (4100, 4100, 4104, 4108, 32, 128, tm.TM_VAR_VEC4, SPAN),    # different strides
-    (4100, 4100, 4700, 4700, 32, 128, tm.TM_VAR_VEC4, SPAN),    # 600 floats of padding
-    (4100, 1000, 1004, 1008, 64, 64, tm.TM_VAR_VEC4, TILES),
-    (4100, 4100, 5120, 5120, 32, 128, tm.TM_VAR_VEC4, TILES),
+@pytest.mark.parametrize("M,N,ldx,ldy,TM,TN,variant,walk,xoff", [
+    (4100, 1000, 1001, 1001, 64, 64, tm.TM_VAR_AUTO, SPAN, 0),     # the bench's padded maps
+    (4100, 1000, 1004, 1004, 64, 64, tm.TM_VAR_VEC4, SPAN, 0),
+    (4100, 4100, 4104, 4104, 32, 128, tm.TM_VAR_VEC4, SPAN, 0),
+    (4100, 4100, 4104, 4108, 32, 128, tm.TM_VAR_VEC4, SPAN, 0),    # different strides
+    (4100, 4100, 4700, 4700, 32, 128, tm.TM_VAR_VEC4, SPAN, 0),    # 600 floats of padding
+    (4100, 4100, 4104, 4104, 32, 128, tm.TM_VAR_AUTO, SPAN, 1),    # x one float past y's 16-byte phase
+    (4100, 1000, 1004, 1008, 64, 64, tm.TM_VAR_VEC4, TILES, 0),
+    (4100, 4100, 5120, 5120, 32, 128, tm.TM_VAR_VEC4, TILES, 0),
 ])
-def test_bench_padded_maps_full_size(dev, M, N, ldx, ldy, TM, TN, variant, walk):
+def test_bench_padded_maps_full_size(dev, M, N, ldx, ldy, TM, TN, variant, walk, xoff):
     """The padded-row maps the benchmark times, at their full sizes and in the same calls (ragged
     path, the same tiles and variants), bit for bit against the oracle, padding untouched, and on
     the plan the benchmark labels them with (tm_map_walk)."""
-    note("bench padded map %dx%d ld %d/%d" % (M, N, ldx, ldy))
+    note("bench padded map %dx%d ld %d/%d x offset %d" % (M, N, ldx, ldy, xoff))
     nx, ny = (M - 1) * ldx + N, (M - 1) * ldy + N
     xh = inputs.matrix(inputs.ragged_input(M, N, seed=12), M, N, ldx)[:nx].copy()
-    X = Guarded(nx, dev, guard=LINE_GUARD_FLOATS)
+    X = Guarded(nx, dev, offset=xoff, guard=LINE_GUARD_FLOATS)
     X.upload(xh)
     Y = Guarded(ny, dev, guard=LINE_GUARD_FLOATS)
     assert tm.tm_map_walk(0, X.ptr, ldx, Y.ptr, ldy, M, N, TM, TN, 0, variant)[:2] == (tm.TM_OK, walk)
@@ -333,7 +335,7 @@ def test_padded_rows_wide_padding(dev, M, N, ld, off):
     ("affine", 257, 1777, 2801, 1781, 3),   # x padding far wider than y's
     ("affine", 64, 4100, 4104, 4108, 0),
     ("scale", 64, 4100, 4104, 4700, 0),     # y padded by 600 floats
-    ("affine", 300, 1100, 1101, 1104, 1),   # strides 3 apart: the 2-D tile plan
+    ("affine", 300, 1100, 1101, 1104, 1),   # strides 3 apart: x's chunks 4-byte aligned
     ("affine", 300, 1000, 1004, 1008, 0),   # rows under 1024 floats: the 2-D tile plan
 ])
 def test_padded_rows_different_strides(dev, op, M, N, ldx, ldy, off):
@@ -343,6 +345,58 @@ def test_padded_rows_different_strides(dev, op, M, N, ldx, ldy, off):
     bit, the padding of y untouched."""
     note("span %s %dx%d ldx %d ldy %d off %d" % (op, M, N, ldx, ldy, off))
     _check_strided(dev, op, M, N, ldx, ldy, off, off, tm.TM_VAR_AUTO, seed=M + 3 * ldx + ldy)
+
+
+@pytest.mark.parametrize("op,M,N,ldx,ldy,xoff,yoff", [
+    ("affine", 300, 1000, 1004, 1004, 1, 0),    # one stride, x one float past y's 16-byte phase
+    ("scale", 300, 1000, 1001, 1001, 2, 1),     # rows off the 16-byte grid too
+    ("copy", 257, 777, 800, 800, 3, 0),
+    ("affine", 100, 4100, 4104, 4104, 1, 0),
+    ("affine", 64, 4100, 4700, 4700, 2, 0),     # wide padding
+    ("affine", 50, 2048, 3071, 3071, 1, 3),     # half a row of padding off the 16-byte grid
+    ("affine", 300, 1100, 1107, 1104, 1, 2),    # strides 3 apart and bases at other phases
+    ("copy", 64, 2048, 2049, 2048, 0, 0),       # y contiguous, x rows one float longer
+    ("scale", 64, 2048, 2049, 2053, 3, 0),      # x rows shorter than y's
+    ("affine", 100, 1000, 1000, 1000, 1, 0),    # contiguous rows: one row, x at another phase
+    ("scale", 4096, 64, 64, 64, 2, 0),
+    ("copy", 1, 100003, 100003, 100003, 3, 1),
+    ("affine", 100, 1000, 1000, 1000, 4, 4),    # one phase, bases off the 128-byte line grid
+    ("scale", 1, 65536, 65536, 65536, 8, 8),
+    ("affine", 3, 64, 64, 64, 1, 0),            # a row of 192 floats: every chunk at an end
+])
+def test_shifted_phase_spans(dev, op, M, N, ldx, ldy, xoff, yoff):
+    """x at another 4-byte phase than y's 1 KiB grid (bases not a multiple of 16 bytes apart,
+    strides not a multiple of 4 floats apart), and contiguous views whose bases miss the 128-byte
+    line grid: one span over y, x's chunks loaded as 4-byte aligned 16-byte vectors and the
+    span's end chunks element by element; bit for bit, padding and guards untouched."""
+    note("shifted span %s %dx%d ldx %d ldy %d offs %d,%d" % (op, M, N, ldx, ldy, xoff, yoff))
+    _check_strided(dev, op, M, N, ldx, ldy, xoff, yoff, tm.TM_VAR_AUTO, seed=M + 5 * N + ldx + xoff,
+                   walk=tm.TM_MAP_SPAN)
+
+
+def test_shifted_phase_channel(dev):
+    """The per-channel op over padded rows with x one float past y's phase."""
+    M, N, ld = 300, 1000, 1004
+    n = (M - 1) * ld + N
+    xh = inputs.uniform(81, n, -8.0, 8.0)
+    bh = inputs.uniform(82, N, -1.0, 1.0)
+    sh = inputs.uniform(83, N, 0.5, 1.5)
+    X = Guarded(n, dev, offset=1, guard=LINE_GUARD_FLOATS)
+    X.upload(xh)
+    Y = Guarded(n, dev, guard=LINE_GUARD_FLOATS)
+    B = Guarded(N, dev)
+    B.upload(bh)
+    S = Guarded(N, dev)
+    S.upload(sh)
+    assert tm.tm_map_walk(3, X.ptr, ld, Y.ptr, ld, M, N, 64, 64, 0, 0, B.ptr)[:2] == (tm.TM_OK, tm.TM_MAP_SPAN)
+    st = tm.tm_channel_affine(X.ptr, ld, S.ptr, B.ptr, Y.ptr, ld, M, N, 64, 64, 0, tm.TM_VAR_AUTO)
+    assert st == tm.TM_OK, tm.tm_status_string(st)
+    torch.cuda.synchronize()
+    want = sentinel_host(Y.buf.numel())
+    region = want[Y.off:Y.off + n].copy()
+    oracle.channel_affine(xh, ld, sh, bh, region, ld, M, N)
+    want[Y.off:Y.off + n] = region
+    assert np.array_equal(bits(Y.host()), bits(want))
 
 
 def test_padded_rows_different_strides_channel(dev):

@@ -375,10 +375,9 @@ def test_fuzz_transposes(dev):
 
 
 def test_fuzz_padded_spans(dev):
-    """Padded rows (the span plan of 1 KiB items on y's 1 KiB grid when the bases sit the same
-    distance past a 16-byte boundary, y's padding is under a line, at most an eighth of the row or
-    (rows off the line grid) up to half of it, and x's stride is the same or, over rows of 1024
-    floats or more, a multiple of 4 floats away;
+    """Padded rows (the span plan of 1 KiB items on y's 1 KiB grid when y's padding is under a
+    line, at most an eighth of the row or (rows off the line grid) up to half of it, and x's
+    stride is the same or, over rows of 1024 floats or more, another; x at any 4-byte phase;
     the 2-D tile plan otherwise): random shapes, paddings, strides, offsets, ops (the channel op
     too) and variants, bit for bit, the padding between rows untouched."""
     rng = random.Random(4242)
