@@ -187,10 +187,12 @@ __global__ __launch_bounds__(kBlock) void col_lds(ColArgs a) {
 // ws[slab * N + column] (the workspace is 16-byte aligned and N % 4 == 0).  The loads carry no
 // control flow: a row past M re-reads row M - 1 and a chunk past N re-reads the row's last chunk,
 // and both are then replaced by 0 ([SLICING] "Masking": out-of-range elements read as 0).
-// WHOLE: the host found whole slabs and strips, so there is nothing to replace.
+// WHOLE: the host found whole slabs and strips, so there is nothing to replace.  U: rows off the
+// 16-byte grid (N a whole number of strips): chunks are 16-byte loads from 4-byte aligned
+// addresses, which the GPU's unaligned access mode executes as one load.
 constexpr int kStripBatch = 16;
 
-template <bool WHOLE>
+template <bool WHOLE, bool U>
 __global__ __launch_bounds__(kBlock) void col_strip(ColArgs a) {
     const int t = threadIdx.x;
     const uint32_t strip = blockIdx.x % a.strips, slab = blockIdx.x / a.strips;
@@ -206,7 +208,8 @@ __global__ __launch_bounds__(kBlock) void col_strip(ColArgs a) {
 #pragma unroll
         for (int u = 0; u < kStripBatch; ++u) {
             const int64_t row = row0 + r0 + u;
-            v[u] = ld16_nt(p + (WHOLE || row < a.M ? row : a.M - 1) * a.ld);
+            const float *pr = p + (WHOLE || row < a.M ? row : a.M - 1) * a.ld;
+            v[u] = U ? ld16u_nt(pr) : ld16_nt(pr);
         }
 #pragma unroll
         for (int u = 0; u < kStripBatch; ++u) {
@@ -223,7 +226,8 @@ __global__ __launch_bounds__(kBlock) void col_strip(ColArgs a) {
 // Pass 2 after the strip walk: workgroup b takes 16-byte column chunks 64 b .. 64 b + 63; wave w of
 // its kFold waves adds slabs [w S / kFold, (w + 1) S / kFold) of its lane's chunk in order, 16
 // coalesced loads in flight (consecutive lanes on consecutive chunks), and the waves' sums meet
-// in LDS in wave order.  Fixed order throughout: the result is deterministic.
+// in LDS in wave order.  Fixed order throughout: the result is deterministic.  out need only be
+// 4-byte aligned: its 16-byte stores go to 4-byte aligned addresses.
 constexpr int kFold = 4;  // waves per workgroup
 
 __global__ __launch_bounds__(kFold * 64) void colsum_fold16(const float *ws, float *out, int64_t N,
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(kFold * 64) void colsum_fold16(const float *ws, flo
 #pragma unroll
         for (int k = 1; k < kFold; ++k)
             total += wsum[k][lane];
-        *reinterpret_cast<f4 *>(out + ch * 4) = total;
+        *reinterpret_cast<f4u *>(out + ch * 4) = total;
     }
 }
 
@@ -407,8 +411,10 @@ hipError_t launch_cols(const tmp::ColPlan &p, hipStream_t stream) {
         a.strips = p.strips;
         a.slabs = p.slabs;
         void *args[] = {&a};
-        const void *fn = p.whole ? reinterpret_cast<const void *>(&col_strip<true>)
-                                 : reinterpret_cast<const void *>(&col_strip<false>);
+        const void *fn = p.vec ? (p.whole ? reinterpret_cast<const void *>(&col_strip<true, false>)
+                                          : reinterpret_cast<const void *>(&col_strip<false, false>))
+                               : (p.whole ? reinterpret_cast<const void *>(&col_strip<true, true>)
+                                          : reinterpret_cast<const void *>(&col_strip<false, true>));
         hipError_t err = hipLaunchKernel(fn, dim3(p.slabs * p.strips), dim3(kBlock), args, 0, stream);
         if (err != hipSuccess)
             return err;

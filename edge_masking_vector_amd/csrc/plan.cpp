@@ -771,8 +771,8 @@ size_t colsum_ws_bytes(int64_t M, int64_t N, int TM, int TN, int walk) {
     if (col_direct(M, N, walk))
         return 0;  // one pass, no partials
     int64_t slabs = ceil_div(M, int64_t{1} << slab_log(M, N, TM, walk));
-    // A wide matrix takes the strip kernel when its rows and the workspace allow 16-byte chunks,
-    // and the LDS-staged kernel otherwise: room for the larger of the two.
+    // A wide matrix takes the strip kernel when the workspace is 16-byte aligned (and the rows
+    // allow it), and the LDS-staged kernel otherwise: room for the larger of the two.
     if (const int ls = strip_slab_log(M, N, walk))
         slabs = std::max(slabs, ceil_div(M, int64_t{1} << ls));
     if (slabs > INT64_MAX / 4 / N)
@@ -834,11 +834,18 @@ int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int 
     // partial has to meet another thread's.  On 4096 x 4096 (1 GiB of rotating inputs) pass 1
     // took 12.2 us against 13.8 us for the LDS-staged kernel's 128 x 128 tiles, whose 1024
     // workgroups all issue their loads in one round and then fold through LDS together.
+    // Rows off the 16-byte grid take the same walk with 4-byte aligned 16-byte loads (vec =
+    // false: col_strip<..., U>) when N is a whole number of strips: 4096 x 4096 at row stride 4097
+    // 17.9 -> 15.6 us against the LDS-staged kernel's 4-byte loads, with the base one float off
+    // 19.2 -> 15.7, 8192 x 2048 at 2049 17.9 -> 16.3.  With a part-filled last strip the LDS-staged
+    // kernel was faster (4096 x 3100 at 3101 15.0 against 16.7 us, 4096 x 4352 at 4353 19.0
+    // against 20.1, 4096 x 4100 at 4103 19.0 against 20.3).
     const int lstrip = strip_slab_log(M, N, walk);
-    if (lstrip > 0 && rows16(x, M, ld) && aligned_to(ws, 16)) {
+    const bool x16 = rows16(x, M, ld);
+    if (lstrip > 0 && aligned_to(ws, 16) && (x16 || N % kColRowStrip == 0)) {
         const int64_t sslabs = ceil_div(M, int64_t{1} << lstrip);
         plan->strip = true;
-        plan->vec = true;
+        plan->vec = x16;
         plan->log_tm = lstrip;
         plan->slabs = static_cast<uint32_t>(sslabs);
         plan->tw = kColRowStrip;

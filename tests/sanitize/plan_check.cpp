@@ -767,9 +767,12 @@ static void check_reductions() {
                             if (c.strip) {
                                 // strip walk: workgroup (slab, strip), thread t of 256 owns column chunk
                                 // strip * 256 + t; its partial lands at ws[slab * N + 4 * chunk]; every
-                                // (slab, column) partial is written exactly once, rows read stay < M
+                                // (slab, column) partial is written exactly once, rows read stay < M;
+                                // rows off the 16-byte grid only with whole strips (no partial chunk)
                                 const int64_t ts = int64_t{1} << c.log_tm, nch = N / 4;
-                                CHECK(walk == TM_COL_LDS && c.vec && N % 4 == 0 && ts >= tmp::kColRowSlab &&
+                                const bool x16 = M <= 1 || ld % 4 == 0;  // the fake base is 16-byte aligned
+                                CHECK(walk == TM_COL_LDS && c.vec == x16 && N % 4 == 0 &&
+                                          (x16 || N % tmp::kColRowStrip == 0) && ts >= tmp::kColRowSlab &&
                                           c.slabs == uint32_t((M + ts - 1) / ts) &&
                                           uint64_t(c.strips) * tmp::kColRowStrip >= uint64_t(N) &&
                                           uint64_t(c.slabs) * uint64_t(N) * 4 <= wsb,

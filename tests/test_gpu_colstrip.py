@@ -76,3 +76,42 @@ def test_strip_workspace_query_covers_both_kernels(dev):
     for M, N in ((4096, 4096), (7000, 3000), (16384, 1024)):
         wsb = tm.tm_colsum_workspace_bytes(M, N, 1, 4, tm.TM_COL_LDS)
         assert wsb >= -(-M // 64) * N * 4 or wsb >= 256 * N * 4
+
+
+@pytest.mark.parametrize("M,N,ld,xoff", [
+    (4096, 4096, 4097, 0),    # rows off the 16-byte grid, whole strips: the strip walk
+    (4096, 4096, 4096, 1),    # the base one float off it
+    (1000, 3072, 3072, 3),    # ragged slabs
+    (64, 1024, 1027, 0),      # one slab
+    (2048, 2051, 2051, 0),    # a part-filled last strip: the LDS-staged walk
+    (3000, 1025, 1030, 3),
+    (700, 5002, 5002, 2),
+])
+def test_strip_walk_unaligned_rows(dev, M, N, ld, xoff):
+    """Rows off the 16-byte grid: with whole strips, the strip walk with 4-byte aligned 16-byte
+    loads; otherwise the LDS-staged walk.  The padding between rows and the floats past the view
+    hold NaN, so a sum that took any of them would be NaN; within the bound on U[0,1) data and
+    bit-exact on integers."""
+    note("strip colsum unaligned %dx%d ld %d off %d" % (M, N, ld, xoff))
+    n = (M - 1) * ld + N
+    for data in ("uniform", "integers"):
+        vals = (inputs.uniform(M + N + xoff, M * N, 0.0, 1.0) if data == "uniform"
+                else inputs.integers(M + 3 * N, M * N, 0, 16).astype(np.float32))
+        xh = inputs.matrix(vals, M, N, ld, pad=np.nan)[:n]
+        buf = np.concatenate([np.zeros(xoff, np.float32), xh, np.full(64, np.nan, np.float32)])
+        x = torch.from_numpy(buf).to(dev)
+        wsb = tm.tm_colsum_workspace_bytes(M, N, 1, 4, tm.TM_COL_LDS)
+        ws = torch.empty(wsb // 4 + 8, device=dev)
+        out = Guarded(N, dev)
+        st = tm.tm_colsum(x.data_ptr() + 4 * xoff, ld, out.ptr, M, N, 1, 4, 0, tm.TM_COL_LDS, ws, wsb,
+                          torch.cuda.current_stream())
+        assert st == tm.TM_OK, tm.tm_status_string(st)
+        torch.cuda.synchronize()
+        assert out.guards_intact()
+        got = out.payload().cpu().numpy().astype(np.float64)
+        want = oracle.colsum_f64(xh, ld, M, N)
+        assert np.all(np.isfinite(got)), data
+        if data == "integers":
+            assert np.array_equal(got, want)
+        else:
+            assert np.all(np.abs(got - want) <= sum_tol(want))
