@@ -34,6 +34,7 @@ typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
 __device__ __forceinline__ f4 ld16u_nt(const float *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const f4u *>(p));
 }
+__device__ __forceinline__ f4 ld16u(const float *p) { return *reinterpret_cast<const f4u *>(p); }
 __device__ __forceinline__ void st4_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
 
 // One contiguous block of `bytes` bytes addressed through a buffer resource (raw buffer: stride 0,

@@ -923,13 +923,20 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     // 16-byte chunks: x rows read along N, y rows written along M, every row on a 16-byte boundary
     // in every batch.  Whether they are used depends on the data only (a chunk that straddles the
     // edge of a ragged view moves element by element); the promise also covers the tile.
-    const bool vx = rows16(x, M, ldx) && (B <= 1 || bsx % 4 == 0);
+    const bool vx16 = rows16(x, M, ldx) && (B <= 1 || bsx % 4 == 0);
     const bool vy = rows16(y, N, ldy) && (B <= 1 || bsy % 4 == 0);
-    const bool vec = vx && vy;
+    const bool vec = vx16 && vy;
     if (aligned && !(M % TM == 0 && N % TN == 0 && TM % 4 == 0 && TN % 4 == 0 && vec))
         return TM_E_ALIGN;
     if (!work)
         return TM_OK;
+    const bool y_lines = aligned_to(y, kLineBytes) && (N <= 1 || ldy % (kLineBytes / 4) == 0);
+    const bool large = !aligned && M >= 2 * kTrSub && N >= kTrSub && M * N >= (int64_t{1} << 22);
+    const bool skew = large && B == 1 && !y_lines;
+    // x's reads move in 16-byte chunks also off the 16-byte grid, as 4-byte aligned 16-byte loads,
+    // when its rows hold a whole sub-tile row (the line windows clamp their last chunk to the one
+    // holding the row's last column, so there N % 4 == 0 as well).
+    const bool vx = vx16 || (N >= kTrSub && (!skew || N % 4 == 0));
     plan->launch = true;
     plan->vec = vec;
     plan->aligned = aligned;
@@ -981,9 +988,6 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     // rotating buffers): 4096 x 4096 at y stride 4100 30.3 -> 26.9 us, 4098 35.2 -> 27.3, 4097
     // 35.2 -> 27.6, both strides 4097 43.4 -> 32.5 (4-byte x reads), 5450 x 2568 36.9 -> 25.8,
     // 57348 x 252 39.4 -> 26.8, 1707 x 7425 37.9 -> 26.2, 4099 x 4099 48.2 -> 32.3.
-    const bool y_lines = aligned_to(y, kLineBytes) && (N <= 1 || ldy % (kLineBytes / 4) == 0);
-    const bool large = !aligned && M >= 2 * kTrSub && N >= kTrSub && M * N >= (int64_t{1} << 22);
-    const bool skew = large && B == 1 && !y_lines;
     if (large && (!vy || skew)) {
         plan->sm = 2 * kTrSub;
         plan->sn = kTrSub;

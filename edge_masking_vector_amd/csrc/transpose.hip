@@ -59,7 +59,9 @@ static_assert(sizeof(TrArgs) <= 128, "transpose arguments outgrew one scalar loa
 // staged in its own LDS region (a 256-thread workgroup per 4 x 4 matrix left 240 threads idle).
 // VX / VY: x's rows (the reads) / y's rows (the writes) move in 16-byte chunks, each side as its
 // own rows allow (a 9163 x 1051 transpose with 16-byte x rows and 4-byte y rows took 42 us with
-// 4-byte chunks on both sides).
+// 4-byte chunks on both sides).  The reads need no 16-byte grid: off it they are 16-byte loads from
+// 4-byte aligned addresses (the GPU's unaligned access mode), and a chunk that crosses the view's
+// edge moves element by element.
 // SUB: the largest sub-tile (elements) the instance stages.
 //
 // Work item w -> (batch b, sub-tile row pm, sub-tile column pn) for work counts below 2^32.
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
             if (e < nx && (!PACK || bb < a.B)) {
                 if (ALIGNED || (r < rows_live && c + WX <= cols_live)) {
                     if constexpr (VX) {
-                        const f4 q = ld16_nt(p);
+                        const f4 q = ld16u_nt(p);  // x's rows may be off the 16-byte grid
                         v[k][0] = q.x, v[k][1] = q.y, v[k][2] = q.z, v[k][3] = q.w;
                     } else {
                         v[k][0] = ld4_nt(p);
@@ -244,7 +246,8 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
 // top 32 are also its upper neighbour's, which the group order runs on the same XCD just before:
 // plain loads, so they are still in that L2).  ceil((M + 31) / 64) items along M cover every row.
 // Loads are clamped into the view (row to 0 .. M - 1, chunk to the one holding the last live
-// column); what a clamped load stages is never stored.  VX: x rows on the 16-byte grid.
+// column); what a clamped load stages is never stored.  VX: x read in 16-byte chunks: rows on the
+// 16-byte grid, or off it with N % 4 == 0 (the clamped chunk then ends at the row's last column).
 template <bool VX>
 __global__ __launch_bounds__(kTrBlock) void transpose_skew(TrArgs a) {
     constexpr int SM = 2 * tmp::kTrSub, SN = tmp::kTrSub, BAND = SM + SN, PAD = SN + 1;
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(kTrBlock) void transpose_skew(TrArgs a) {
                 xr = xr < 0 ? 0 : (xr >= a.M ? a.M - 1 : xr);
                 const float *p = a.x + xr * a.ldx + col0 + (c < clast ? c : clast) * WX;
                 if constexpr (VX) {
-                    const f4 q = ld16(p);
+                    const f4 q = ld16u(p);  // x's rows may be off the 16-byte grid (then N % 4 == 0)
                     v[k][0] = q.x, v[k][1] = q.y, v[k][2] = q.z, v[k][3] = q.w;
                 } else {
                     v[k][0] = *p;

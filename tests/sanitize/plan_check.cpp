@@ -470,6 +470,14 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
               "%s skew plan", tag);
         const uint32_t grp_rows = (p.subs_m + G - 1) / G;
         CHECK(p.per_b.d == grp_rows, "%s group divisor", tag);
+        {
+            // 16-byte x reads clamp to the chunk holding the row's last column: off the 16-byte
+            // grid that chunk must end there (N % 4 == 0), or it would read past the view
+            const uintptr_t xa = reinterpret_cast<uintptr_t>(p.x);
+            const bool x16 = xa % 16 == 0 && (M <= 1 || p.ldx % 4 == 0);
+            CHECK(!p.vx || x16 || N % 4 == 0, "%s skew: 16-byte reads past the row's end", tag);
+            CHECK(p.vx == (x16 || N % 4 == 0), "%s skew: x chunk width", tag);
+        }
         const uintptr_t ya = reinterpret_cast<uintptr_t>(p.y);
         std::vector<uint8_t> hits(size_t(N) * M, 0);
         bool bad = false;
@@ -535,7 +543,13 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
     }
     if (p.aligned)
         CHECK(M % p.sm == 0 && N % p.sn == 0, "%s promised sub-tiles are not whole", tag);
-    CHECK(p.vec == (p.vx && p.vy), "%s vec flag", tag);
+    CHECK(!p.vec || (p.vx && p.vy), "%s vec flag", tag);
+    {
+        // x read in 16-byte chunks: rows on the 16-byte grid, or rows of a whole sub-tile row
+        const uintptr_t xa = reinterpret_cast<uintptr_t>(p.x);
+        const bool x16 = xa % 16 == 0 && (M <= 1 || p.ldx % 4 == 0) && (B <= 1 || p.bsx % 4 == 0);
+        CHECK(p.vx == (x16 || N >= tmp::kTrSub), "%s x chunk width", tag);
+    }
     if (p.vx)
         CHECK(p.sn >= 4, "%s 16-byte reads need sub-tile rows of 4+", tag);
     if (p.vy)
