@@ -1,7 +1,10 @@
 // mapflat.hip -- the element-wise maps over one contiguous row, cut into 1 KiB work items: the
 // case the tile scheduler reaches for every view whose rows are contiguous in both tensors (row
 // stride N: the M x N elements are one row of M*N) and whose bases sit on 128-byte lines, with the
-// affine map, the scale or the copy moved in 16-byte chunks or in 4-byte elements.
+// affine map, the scale or the copy moved in 16-byte chunks or in 4-byte elements (map_flat).
+// Also here: padded rows as one span of 1 KiB items on y's 1 KiB grid, columns past N masked per
+// chunk (map_rows, map_rows_diff, map_rows_shift, map_rows_channel), and one contiguous row that
+// map_flat cannot take, x at another 4-byte phase or a base off the line grid (map_flat_shift).
 //
 // Sources (web pages): Phobos docs "@aligned" ("A minimal kernel": the scale; "What it changes":
 // no masks, 16-byte rows); Phobos docs "Slicing, bounds and masking" ("Masking": elements past the
@@ -126,19 +129,23 @@ __global__ __launch_bounds__(flat_threads<MODE>()) void map_flat(const float *__
     }
 }
 
-// Padded rows in one span.  Element f of the span (f = 0 at y[0], x[0]) is row f / ld, column
-// f % ld, and live when that column is below N (the padding between rows is never stored).  Item
-// w is the 1 KiB block of y's 1 KiB grid that starts 256 w - head floats from y[0]; lane t moves
-// the 16-byte chunk of span elements q .. q + 3, q = 256 w + 4 t - head (x and y are the same
-// distance past a 16-byte boundary, so the chunk is aligned on both sides).  A chunk whose four
-// elements are live is stored whole through a buffer resource spanning the block; at a row's end
-// or the span's ends the live elements are stored one by one.  Every load holds a live element:
-// loads are clamped to the chunks that hold y[0] and the span's last element, and with a line or
-// more of padding (WIDE) a chunk wholly inside the padding between two rows loads the row's last
-// live chunk instead (already read by another lane), so no line of padding alone is fetched.
-// (Under a line of padding every line holds live elements, and the load is issued before the
-// column is known.)  Columns come from a multiply-high
-// remainder by ld (rows of at least 64 floats: at most one row boundary per chunk).
+// Padded rows in one span.  Element f of the span (f = 0 at y[0]) is row f / ld, column f % ld
+// (ld: y's row stride), and live when that column is below N (the padding between rows is never
+// stored).  Item w is the 1 KiB block of y's 1 KiB grid that starts 256 w - head floats from
+// y[0]; lane t moves the 16-byte chunk of span elements q .. q + 3, q = 256 w + 4 t - head.  x's
+// chunk for it starts at x index q + r dld (r: q's row; dld = ldx - ldy, 0 for one stride): on the
+// 16-byte grid when x and y share their 16-byte phase, else (SHIFT) a 16-byte load from a 4-byte
+// aligned address.  A chunk whose four elements are live is stored whole through a buffer
+// resource spanning the block; at a row's end or the span's ends the live elements are stored one
+// by one.  Every load holds a live element: loads are clamped to the chunks that hold y[0] and the
+// span's last element (SHIFT: those two chunks load their live elements one by one), and with a
+// line or more of padding (WIDE) a chunk wholly inside the padding between two rows loads the
+// row's last live chunk instead (already read by another lane), so no line of padding alone is
+// fetched, and a wave wholly inside the padding exits.  (Under a line of padding every line holds
+// live elements, and the load is issued before the column is known.)  With different strides
+// (DIFF) a chunk that crosses a row's end takes the next row's elements from a second load.
+// Columns (and rows) come from a multiply-high division by ld (rows of at least 64 floats: at
+// most one row boundary per chunk).
 // The channel op (OP = kChannel) takes element (row, column c)'s channel c: y = fmaf(x, scale[c],
 // bias[c]), scale 1 when absent; a whole chunk's four channels are one 16-byte load of each vector
 // when cvec16 (both vectors 16-byte aligned and every chunk starting on a column divisible by 4).
