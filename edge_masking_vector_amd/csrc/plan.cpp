@@ -934,9 +934,8 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     const bool large = !aligned && M >= 2 * kTrSub && N >= kTrSub && M * N >= (int64_t{1} << 22);
     const bool skew = large && B == 1 && !y_lines;
     // x's reads move in 16-byte chunks also off the 16-byte grid, as 4-byte aligned 16-byte loads,
-    // when its rows hold a whole sub-tile row (the line windows clamp their last chunk to the one
-    // holding the row's last column, so there N % 4 == 0 as well).
-    const bool vx = vx16 || (N >= kTrSub && (!skew || N % 4 == 0));
+    // when its rows hold a whole sub-tile row.
+    const bool vx = vx16 || N >= kTrSub;
     plan->launch = true;
     plan->vec = vec;
     plan->aligned = aligned;
@@ -1037,8 +1036,10 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     if (plan->skew) {
         // Groups of G vertically adjacent items on one XCD: the upper neighbour's band rows are
         // still in that L2.  G = 4, 8 and 16 measured within 2-4% of each other; 8 with 16-byte x
-        // rows, 4 with 4-byte ones.  Work items: 8 G per 8 groups (group r -> items 8 G (r / 8) +
-        // r mod 8 + 8 k, member k < G).
+        // reads, 4 with 4-byte ones.  (With 16-byte reads off the 16-byte grid, G = 8 against 4:
+        // 17827 x 767 26.3 against 27.9 us, 5450 x 2568 with x stride 2569 26.9 against 28.1,
+        // 9163 x 1051 19.7 against 20.2, 4096 x 4096 with both strides 4097 31.2-32.3 either way.)
+        // Work items: 8 G per 8 groups (group r -> items 8 G (r / 8) + r mod 8 + 8 k, member k < G).
         plan->log_grp = vx ? 3 : 2;
         const int64_t G = int64_t{1} << plan->log_grp;
         const int64_t grp_rows = ceil_div(subs_m, G);

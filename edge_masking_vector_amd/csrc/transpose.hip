@@ -246,8 +246,9 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
 // top 32 are also its upper neighbour's, which the group order runs on the same XCD just before:
 // plain loads, so they are still in that L2).  ceil((M + 31) / 64) items along M cover every row.
 // Loads are clamped into the view (row to 0 .. M - 1, chunk to the one holding the last live
-// column); what a clamped load stages is never stored.  VX: x read in 16-byte chunks: rows on the
-// 16-byte grid, or off it with N % 4 == 0 (the clamped chunk then ends at the row's last column).
+// column); what a clamped load stages is never stored.  VX: x read in 16-byte chunks (16-byte
+// loads from 4-byte aligned addresses when x's rows are off the 16-byte grid); the chunks at or
+// past the one holding a row's last live column read the 16 bytes that end at that column.
 template <bool VX>
 __global__ __launch_bounds__(kTrBlock) void transpose_skew(TrArgs a) {
     constexpr int SM = 2 * tmp::kTrSub, SN = tmp::kTrSub, BAND = SM + SN, PAD = SN + 1;
@@ -266,30 +267,36 @@ __global__ __launch_bounds__(kTrBlock) void transpose_skew(TrArgs a) {
         const int64_t row0 = int64_t(pm) * SM, col0 = int64_t(pn) * SN;
         const int cols_live = skip ? 0 : static_cast<int>(a.N - col0 < SN ? a.N - col0 : SN);
         if (cols_live > 0) {  // uniform
-            // band row r is x row row0 - SN + r; loads from clamped rows and chunks
+            // band row r is x row row0 - SN + r; loads from clamped rows and chunks.  With 16-byte
+            // reads a chunk at or past the one holding the last live column reads the 16 bytes
+            // that end at that column (from a 4-byte aligned address: x's rows need no 16-byte
+            // grid) and stages them there; threads that clamp alike stage the same values.
             float v[KX][WX];
             const int clast = (cols_live - 1) / WX;
+            const int cend = cols_live - WX;  // 16-byte reads: the clamped chunk's first column
 #pragma unroll
             for (int k = 0; k < KX; ++k) {
                 const int e = t + k * kTrBlock;
                 const int r = e / (SN / WX), c = e - r * (SN / WX);
                 int64_t xr = row0 - SN + r;
                 xr = xr < 0 ? 0 : (xr >= a.M ? a.M - 1 : xr);
-                const float *p = a.x + xr * a.ldx + col0 + (c < clast ? c : clast) * WX;
                 if constexpr (VX) {
-                    const f4 q = ld16u(p);  // x's rows may be off the 16-byte grid (then N % 4 == 0)
+                    const int cs = c < clast ? c * WX : cend;  // cend >= -3: col0 >= 32 when below 4
+                    const f4 q = ld16u(a.x + xr * a.ldx + col0 + cs);
                     v[k][0] = q.x, v[k][1] = q.y, v[k][2] = q.z, v[k][3] = q.w;
                 } else {
-                    v[k][0] = *p;
+                    v[k][0] = a.x[xr * a.ldx + col0 + (c < clast ? c : clast)];
                 }
             }
 #pragma unroll
             for (int k = 0; k < KX; ++k) {
                 const int e = t + k * kTrBlock;
                 const int r = e / (SN / WX), c = e - r * (SN / WX);
+                const int cs = VX && c >= clast ? cend : c * WX;
 #pragma unroll
                 for (int i = 0; i < WX; ++i)
-                    tile[r * PAD + c * WX + i] = v[k][i];
+                    if (!VX || cs + i >= 0)
+                        tile[r * PAD + cs + i] = v[k][i];
             }
         }
         __syncthreads();

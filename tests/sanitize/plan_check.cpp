@@ -471,12 +471,30 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
         const uint32_t grp_rows = (p.subs_m + G - 1) / G;
         CHECK(p.per_b.d == grp_rows, "%s group divisor", tag);
         {
-            // 16-byte x reads clamp to the chunk holding the row's last column: off the 16-byte
-            // grid that chunk must end there (N % 4 == 0), or it would read past the view
-            const uintptr_t xa = reinterpret_cast<uintptr_t>(p.x);
-            const bool x16 = xa % 16 == 0 && (M <= 1 || p.ldx % 4 == 0);
-            CHECK(!p.vx || x16 || N % 4 == 0, "%s skew: 16-byte reads past the row's end", tag);
-            CHECK(p.vx == (x16 || N % 4 == 0), "%s skew: x chunk width", tag);
+            // 16-byte x reads: chunk c of a band row reads columns col0 + 4c .. + 3, and the chunks
+            // at or past the one holding the last live column read the 16 bytes that end at it;
+            // every read lies inside the row, and every live column is staged by its own chunk or
+            // by the clamped one
+            CHECK(p.vx && N >= tmp::kTrSub, "%s skew: x chunk width", tag);
+            bool bad_read = false;
+            for (uint32_t pn = 0; pn < p.subs_n; ++pn) {
+                const int64_t col0 = int64_t(pn) * 32;
+                const int cols_live = int(std::min<int64_t>(N - col0, 32));
+                const int clast = (cols_live - 1) / 4, cend = cols_live - 4;
+                std::vector<int> staged(32, 0);
+                for (int c = 0; c < 8; ++c) {
+                    const int cs = c < clast ? 4 * c : cend;
+                    if (col0 + cs < 0 || col0 + cs + 4 > N)
+                        bad_read = true;
+                    for (int i = 0; i < 4; ++i)
+                        if (cs + i >= 0 && cs + i < 32)
+                            ++staged[size_t(cs + i)];
+                }
+                for (int j = 0; j < cols_live; ++j)
+                    if (staged[size_t(j)] == 0)
+                        bad_read = true;
+            }
+            CHECK(!bad_read, "%s skew: a 16-byte read outside its row, or a live column not staged", tag);
         }
         const uintptr_t ya = reinterpret_cast<uintptr_t>(p.y);
         std::vector<uint8_t> hits(size_t(N) * M, 0);
