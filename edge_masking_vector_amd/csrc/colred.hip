@@ -98,7 +98,7 @@ template <bool VEC>
 __device__ __forceinline__ auto chunk_or_zero(const float *p, int64_t live) {
     if constexpr (VEC) {
         if (live >= 4)
-            return ld16_nt(p);
+            return ld16u_nt(p);  // rows may be off the 16-byte grid
         f4 r = f4(0.0f);
         if (live > 0)
             r.x = p[0];
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kBlock) void col_lds(ColArgs a) {
                 v[u] = T(0.0f);
                 if (rr < rows) {
                     if constexpr (ALIGNED)
-                        v[u] = ld16_nt(p + rr * a.ld);
+                        v[u] = ld16u_nt(p + rr * a.ld);
                     else
                         v[u] = chunk_or_zero<VEC>(p + rr * a.ld, live);
                 }

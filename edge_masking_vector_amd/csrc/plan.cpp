@@ -813,7 +813,9 @@ int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int 
         plan->direct = true;
         plan->finish = true;  // a call with work (callers launch when finish is set)
         plan->walk = walk;
-        plan->vec = rows16(x, M, ld);
+        // 16-byte chunks, from 4-byte aligned addresses when the rows are off the 16-byte grid:
+        // 16 x 2^20 at row stride 2^20 + 1 14.6 against 17.7 us with 4-byte chunks
+        plan->vec = true;
         plan->out16 = aligned_to(out, 16);
         plan->x = x;
         plan->out = out;
@@ -861,6 +863,10 @@ int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int 
     }
     if (walk == TM_COL_LDS) {
         // Like the slabs, the strips are the walk's own: the caller's tile states the promise.
+        // (16-byte chunks from 4-byte aligned addresses for rows off the 16-byte grid measured
+        // slower here over narrow rows -- fewer lanes per row: 43690 x 96 at row stride 128 with
+        // the base 3 floats off 13.0 against 11.7 us, 1677721 x 10 at 13 24.6 against 20.9 -- so
+        // such rows keep 4-byte chunks.)
         plan->vec = rows16(x, M, ld);
         const int W = plan->vec ? 4 : 1;
         plan->tw = std::max(W, N >= kColStrip ? kColStrip : 1 << ilog2(N));

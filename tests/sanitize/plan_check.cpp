@@ -794,7 +794,7 @@ static void check_reductions() {
                             CHECK(c.direct == (N > 0 && tmp::col_direct(M, N, walk)), "cols direct M=%ld N=%ld", long(M),
                                   long(N));
                             if (c.direct)
-                                CHECK(!c.launch && wsb == 0 && c.vec == (M <= 1 || ld % 4 == 0) && c.out16,
+                                CHECK(!c.launch && wsb == 0 && c.vec && c.out16,
                                       "cols direct plan M=%ld N=%ld", long(M), long(N));
                             if (c.strip) {
                                 // strip walk: workgroup (slab, strip), thread t of 256 owns column chunk

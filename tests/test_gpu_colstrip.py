@@ -115,3 +115,38 @@ def test_strip_walk_unaligned_rows(dev, M, N, ld, xoff):
             assert np.array_equal(got, want)
         else:
             assert np.all(np.abs(got - want) <= sum_tol(want))
+
+
+@pytest.mark.parametrize("M,N,ld,xoff", [
+    (16, 1 << 20, (1 << 20) + 1, 0),   # rows off the 16-byte grid
+    (64, 262147, 262147, 1),           # N % 4 == 3, the base one float off
+    (1, 1001, 1001, 3),                # one row
+    (7, 5003, 5010, 2),
+])
+def test_direct_walk_unaligned_rows(dev, M, N, ld, xoff):
+    """Few rows take the one-pass walk (no workspace), whose 16-byte column chunks are loads from
+    4-byte aligned addresses when the rows are off the 16-byte grid and whose last chunk of a row
+    moves element by element.  NaN in the padding and past the view must reach no sum; within the
+    bound on U[0,1) data, bit-exact on integers."""
+    note("direct colsum unaligned %dx%d ld %d off %d" % (M, N, ld, xoff))
+    assert tm.tm_colsum_workspace_bytes(M, N, 1, 4, tm.TM_COL_LDS) == 0   # the one-pass walk
+    n = (M - 1) * ld + N
+    for data in ("uniform", "integers"):
+        vals = (inputs.uniform(M + N + xoff, M * N, 0.0, 1.0) if data == "uniform"
+                else inputs.integers(M + 3 * N, M * N, 0, 16).astype(np.float32))
+        xh = inputs.matrix(vals, M, N, ld, pad=np.nan)[:n]
+        buf = np.concatenate([np.zeros(xoff, np.float32), xh, np.full(64, np.nan, np.float32)])
+        x = torch.from_numpy(buf).to(dev)
+        out = Guarded(N, dev)
+        st = tm.tm_colsum(x.data_ptr() + 4 * xoff, ld, out.ptr, M, N, 1, 4, 0, tm.TM_COL_LDS, None, 0,
+                          torch.cuda.current_stream())
+        assert st == tm.TM_OK, tm.tm_status_string(st)
+        torch.cuda.synchronize()
+        assert out.guards_intact()
+        got = out.payload().cpu().numpy().astype(np.float64)
+        want = oracle.colsum_f64(xh, ld, M, N)
+        assert np.all(np.isfinite(got)), data
+        if data == "integers":
+            assert np.array_equal(got, want)
+        else:
+            assert np.all(np.abs(got - want) <= sum_tol(want))
