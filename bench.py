@@ -445,7 +445,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
     # row, or (rows off the line grid) wider: rows off the 16-byte grid (row stride 1001), on it
     # (1004), a scale-sized view (4100 x 4100 at row stride 4104), strides that differ between x
     # and y, and 600 floats of padding (waves wholly inside it exit at once).  Different strides
-    # over rows under 1024 floats, and wide padding between rows on the line grid, keep the 2-D
+    # over 16-byte rows under 1024 floats, and wide padding between rows on the line grid, keep the 2-D
     # tile plan, whose edge tiles (the bottom 4 rows, the right 40 or 4 columns) take the masked
     # body.
     for (M, N, ldx, ldy, TM, TN, var, name, expect, what) in (
@@ -463,7 +463,7 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
              "one span over y, x's view one float past y's 16-byte phase: x's chunks are 4-byte "
              "aligned 16-byte loads"),
             (4100, 1000, 1004, 1008, 64, 64, tm.TM_VAR_VEC4, "affine_4100x1000_ldx1004_ldy1008_ragged_tiles", "tiles",
-             "the 2-D tile plan (different strides, rows under 1024 floats): 16-byte chunks, 4-row "
+             "the 2-D tile plan (different strides, 16-byte rows under 1024 floats): 16-byte chunks, 4-row "
              "bottom and 64x40 right-edge tiles masked"),
             (4100, 4100, 5120, 5120, 32, 128, tm.TM_VAR_VEC4, "scale_4100x4100_ld5120_ragged_tiles", "tiles",
              "the 2-D tile plan (rows on the 128-byte line grid, 1020 floats of padding): 16-byte "

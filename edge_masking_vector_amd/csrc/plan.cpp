@@ -252,10 +252,14 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     // (Rows of both tensors on the 128-byte line grid keep the 2-D plan, whose work items are then
     // whole lines already, when the strides differ.)  x's rows drift against y's 1 KiB grid, so
     // an item's 1 KiB of x mostly spans nine lines, one of them fetched by two XCDs (11% more
-    // reads); under 1024 floats a row the span then measured slower than the 2-D plan: 4100 x
-    // 1000 at strides 1004 / 1008 8.1 us as a span, 7.8 under 2-D tiles, 16400 x 1000 24.8
-    // against 23.6; 4100 x 4100 at 4104 / 4108 23.5 against 33.5, 2733 x 1500 at 1504 / 1508
-    // 8.1 against 8.4.
+    // reads); under 1024 floats a row the span then measured slower than the 2-D plan on 16-byte
+    // rows: 4100 x 1000 at strides 1004 / 1008 8.1 us as a span, 7.8 under 2-D tiles, 16400 x
+    // 1000 24.8 against 23.6; 4100 x 4100 at 4104 / 4108 23.5 against 33.5, 2733 x 1500 at 1504 /
+    // 1508 8.1 against 8.4.  Rows off the 16-byte grid (where the 2-D plan moves 4-byte chunks)
+    // take the span at any width: 62137 x 135 at 138 / 135 18.1 against 24.3 us, 7781 x 539 at
+    // 539 / 607 10.5 against 12.9, 4100 x 1000 at 1001 / 1004 8.7 against 9.5, 16400 x 250 at
+    // 251 / 256 9.0 against 9.5; it lost on 32768 x 100 at 101 / 103 (9.8 against 9.1) and
+    // 8192 x 500 at 503 / 500 (9.7 against 9.1).
     const int64_t pad = ldy - N;
     const bool y_lines = aligned_to(y, kLineBytes) && ldy % (kLineBytes / 4) == 0;
     const bool both_lines = y_lines && aligned_to(x, kLineBytes) && ldx % (kLineBytes / 4) == 0;
@@ -279,7 +283,7 @@ int plan_map(int op, const float *x, int64_t ldx, float *y, int64_t ldy, int64_t
     // 128-byte line grid (not the channel op, whose flat view finds channels by remainder).
     const bool shift = (reinterpret_cast<uintptr_t>(x) - reinterpret_cast<uintptr_t>(y)) % 16 != 0 ||
                        (M > 1 && (ldx - ldy) % 4 != 0);
-    const bool padded = M > 1 && pad >= 0 && (ldx != ldy ? !both_lines && N >= kRowsDiffMinN : pad > 0) && pad_ok;
+    const bool padded = M > 1 && pad >= 0 && (ldx != ldy ? !both_lines && (N >= kRowsDiffMinN || access != kVec4) : pad > 0) && pad_ok;
     const bool flat_row = M == 1 && op != kChannel && (shift || !aligned_to(x, kLineBytes) || !aligned_to(y, kLineBytes));
     if (!aligned && (padded || flat_row) && N >= kRowsSpanMinN && (access == kVec4 || access == kScalar)) {
         if (M == 1)

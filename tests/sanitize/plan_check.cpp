@@ -122,7 +122,7 @@ static void replay_rows(const tmp::MapPlan &p, int64_t M, int64_t N, int64_t ldx
     const bool one_row = M == 1 && ldx == N && ldy == N && p.op != tmp::kChannel &&
                          (shift || xa % 128 != 0 || ya % 128 != 0);
     const bool padded = M > 1 && pad >= 0 && (diff || pad > 0) && (pad < 32 || pad * 8 <= N || wide_ok) &&
-                        (!diff || N >= tmp::kRowsDiffMinN);
+                        (!diff || N >= tmp::kRowsDiffMinN || p.access != tmp::kVec4);
     CHECK(!p.aligned && p.ldx == ldx && p.ldy == ldy && (padded || one_row) && N >= tmp::kRowsSpanMinN &&
               p.shift == shift && (p.access == tmp::kVec4 || p.access == tmp::kScalar),
           "%s span plan outside its case", tag);
@@ -373,7 +373,8 @@ static void check_maps_diff() {
                                     std::snprintf(tag, sizeof tag, "map diff M=%ld N=%ld ldx=%ld ldy=%ld offs=%lu,%lu op=%d var=%d",
                                                   long(M), long(N), long(ldx), long(ldy), (unsigned long)xoff,
                                                   (unsigned long)yoff, op, variant);
-                                    CHECK(!p.rows || N >= tmp::kRowsDiffMinN, "%s: a span under the width minimum", tag);
+                                    CHECK(!p.rows || N >= tmp::kRowsDiffMinN || p.access != tmp::kVec4,
+                                          "%s: a span of 16-byte rows under the width minimum", tag);
                                     spans += p.rows;
                                     replay_map(p, M, N, ldy, xb, tag);
                                 }

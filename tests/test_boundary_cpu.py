@@ -186,7 +186,8 @@ def test_map_walk_bench_views():
 
 def test_map_walk_span_limits():
     """Where the span stops and the 2-D tiles take over: one stride (or different strides over
-    rows of 1024 floats or more, unless both tensors' rows lie on the line grid), rows of 64
+    rows of 1024 floats or more, or off the 16-byte grid, unless both tensors' rows lie on the
+    line grid), rows of 64
     floats or more, and padding under a line, at most an eighth of the row, or -- y's rows off
     the line grid -- a quarter of 16-byte rows of 2048 floats or more, a quarter of rows off the
     16-byte grid, or half of them from 2048 floats on; x at any 4-byte phase.  Contiguous rows
@@ -208,7 +209,8 @@ def test_map_walk_span_limits():
     assert walk(100, 2048, 3072, 3072, 2, 2)[0] == SPAN    # 16-byte stride, base off the 16-byte grid
     assert walk(100, 2047, 3071, 3071)[0] == TILES    # half, rows under 2048 floats
     assert walk(100, 1100, 1104, 1108)[0] == SPAN     # different strides, 1024 floats or more
-    assert walk(100, 1023, 1027, 1031)[0] == TILES
+    assert walk(100, 1000, 1004, 1008)[0] == TILES    # ... on the 16-byte grid under 1024 floats
+    assert walk(100, 1000, 1003, 1007)[0] == SPAN     # ... off it, at any width
     assert walk(100, 1100, 1101, 1104)[0] == SPAN     # strides 3 apart: x's chunks 4-byte aligned
     assert walk(100, 1024, 1024, 1024 + 128, 0, 0)[0] == TILES   # both on the line grid, strides differ
     assert walk(100, 1000, 1001, 1001, 1, 0)[0] == SPAN    # bases at different 16-byte phases

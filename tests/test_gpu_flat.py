@@ -211,7 +211,7 @@ def test_padded_rows_one_span(dev, op, M, N, ld, off, variant):
 
 
 @pytest.mark.parametrize("M,N,ldx,ldy,xoff,yoff", [
-    (100, 1000, 1004, 1008, 0, 0),    # different strides over rows under 1024 floats
+    (100, 1000, 1004, 1008, 0, 0),    # different strides over 16-byte rows under 1024 floats
     (100, 60, 61, 61, 0, 0),          # rows narrower than the span's minimum
     (100, 1000, 1500, 1500, 0, 0),    # half a row of padding, 16-byte rows under 2048 floats
     (50, 2048, 3072, 3072, 0, 0),     # wide padding between rows on the line grid
@@ -336,7 +336,9 @@ def test_padded_rows_wide_padding(dev, M, N, ld, off):
     ("affine", 64, 4100, 4104, 4108, 0),
     ("scale", 64, 4100, 4104, 4700, 0),     # y padded by 600 floats
     ("affine", 300, 1100, 1101, 1104, 1),   # strides 3 apart: x's chunks 4-byte aligned
-    ("affine", 300, 1000, 1004, 1008, 0),   # rows under 1024 floats: the 2-D tile plan
+    ("affine", 300, 1000, 1004, 1008, 0),   # 16-byte rows under 1024 floats: the 2-D tile plan
+    ("affine", 300, 1000, 1003, 1007, 0),   # ... rows off the 16-byte grid: the span at any width
+    ("copy", 500, 135, 138, 135, 1),        # narrow rows, y contiguous
 ])
 def test_padded_rows_different_strides(dev, op, M, N, ldx, ldy, off):
     """Rows of 1024 floats or more with different strides in x and y (a multiple of 4 floats
