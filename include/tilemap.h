@@ -109,7 +109,8 @@ typedef enum {
                          items, only its end ragged */
     TM_MAP_SPAN = 2,  /* padded rows as one span of 1 KiB items on y's 1 KiB grid, the columns past
                          N masked per 16-byte chunk ([SLICING] "Masking"); x's row stride may differ
-                         from y's by a multiple of 4 floats */
+                         from y's, and x may start at another 4-byte phase than y (also: one
+                         contiguous row that the flat plan cannot take) */
     TM_MAP_TILES = 3  /* the 2-D tile schedule: whole tiles unmasked, edge tiles masked */
 } tm_mapwalk;
 
@@ -169,9 +170,12 @@ int tm_rowsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t N,
  * a slab is TM rows for the naive walks and 256 rows for the LDS walk (taller, doubling, while
  * there would be more than 4096 slabs; shorter, halving, while there would be fewer than 1024
  * slabs x column strips of up to 128 columns, down to 32 rows, or 4096 / strip width rows for
- * narrower strips); 0 when the LDS walk takes its one-pass form (at most 64
- * rows, or at most 256 rows of at least 262144 columns: each thread adds one 16-byte column chunk
- * down all M rows and writes the sums, so there are no partials). */
+ * narrower strips).  Wide matrices (N >= 1024, N % 4 == 0) may take the LDS walk's strip form, with
+ * slabs of 64 rows (doubling while there would be more than 256) by 1024-column strips, when that
+ * makes at least 256 workgroups; the size then covers the larger of the two slab counts, since the
+ * workspace's alignment (16 bytes for the strip form) is not known here.  0 when the LDS walk takes
+ * its one-pass form (at most 64 rows, or at most 256 rows of at least 262144 columns: each thread
+ * adds one 16-byte column chunk down all M rows and writes the sums, so there are no partials). */
 size_t tm_colsum_workspace_bytes(int64_t M, int64_t N, int TM, int TN, int walk);
 
 /* out[j] = sum over i < M of x[i,j] for j < N (out: N floats, contiguous).  Two passes: pass 1 writes
