@@ -384,11 +384,11 @@ def test_fuzz_padded_spans(dev):
     for case in range(150):
         op = rng.choice(["affine", "scale", "copy", "channel", "channel_scale"])
         variant = rng.choice([tm.TM_VAR_AUTO, tm.TM_VAR_AUTO, tm.TM_VAR_VEC4, tm.TM_VAR_SCALAR])
-        # x's stride: mostly the same, else (over rows of 1024 floats or more) a multiple of 4
-        # floats away, or not
+        # x's stride: mostly the same, else a multiple of 4 floats away, or not (the span over
+        # 16-byte rows from 1024 floats on, over rows off the 16-byte grid at any width)
         diff = rng.random() >= 0.6
         M = rng.randint(2, 300)
-        N = rng.randint(1024, 2600) if diff else (rng.randint(64, 1100) if rng.random() < 0.7 else rng.randint(1024, 4200))
+        N = rng.randint(64, 2600) if diff else (rng.randint(64, 1100) if rng.random() < 0.7 else rng.randint(1024, 4200))
         u = rng.random()   # y's padding: under a line, up to an eighth of the row, or wider
         ld = N + (rng.randint(1, 31) if u < 0.55 else rng.randint(32, max(32, N // 8 + 3)) if u < 0.8
                   else rng.randint(N // 8, N // 2 + 3))
