@@ -1043,6 +1043,59 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
         if (plan->packed != 0 && ((!plan->pvec && !plan->flat16) || plan->nwork > UINT32_MAX))
             plan->packed = 0;  // nothing to gain, or work ids beyond 32 bits
     }
+    // 32 to kTrPackBigC channels whose packed rows (C floats) miss the 128-byte line grid: the
+    // sub-tiles would write those rows in pieces that share lines with their neighbours (read-
+    // modify-writes in HBM3E).  The packed kernel with larger items instead writes each item's
+    // S positions x C channels as one block whose ends lie on lines (S a multiple of 32), S the
+    // largest power of two with S C <= kTrPackBigElems; both sides in 16-byte chunks.  Against the
+    // sub-tiles, NCHW -> NHWC / NHWC -> NCHW (one process, 1 GiB of rotating buffers): (32, 65,
+    // 56, 56) 19.0 -> 12.6 / 16.2 -> 12.6 us, (64, 33, 56, 56) 21.0 -> 12.5 / 17.6 -> 12.8,
+    // (16, 100, 56, 56) 13.6 -> 10.4 / 12.2 -> 9.8, (8, 127, 64, 64) 12.0 -> 8.8, one 100 x 262144
+    // matrix 72.7 -> 40.1.  Items of up to 8192 elements took (32, 65, 56, 56) to 15.4 us, of
+    // 16384 (two workgroups' LDS per CU) to 23.0.
+    if (plan->packed == 0 && plan->log_g == 0 && !aligned) {
+        const bool bs16y = B <= 1 || bsy % 4 == 0, bs16x = B <= 1 || bsx % 4 == 0;
+        const int64_t line = kLineBytes / 4;
+        int mode = 0;
+        int64_t C = 0, P = 0;
+        if (M >= kTrSub && M <= kTrPackBigC && ldy == M && N >= 2 * kTrSub && rows16(x, M, ldx) && bs16x &&
+            aligned_to(y, 16) && bs16y && !(M % line == 0 && aligned_to(y, kLineBytes) && (B <= 1 || bsy % line == 0))) {
+            mode = 1;
+            C = M;
+            P = N;
+        } else if (N >= kTrSub && N <= kTrPackBigC && ldx == N && M >= 2 * kTrSub && rows16(y, N, ldy) && bs16y &&
+                   aligned_to(x, 16) && bs16x && !(N % line == 0 && aligned_to(x, kLineBytes) && (B <= 1 || bsx % line == 0))) {
+            mode = 2;
+            C = N;
+            P = M;
+        }
+        if (mode != 0) {
+            int64_t S = kTrPackBigElems;
+            while (S * C > kTrPackBigElems)
+                S /= 2;
+            const int64_t subs = ceil_div(P, S);
+            if (B * subs <= UINT32_MAX && subs <= UINT32_MAX) {
+                plan->packed = mode;
+                plan->pbig = true;
+                plan->pvec = true;
+                plan->flat16 = true;
+                plan->skew = false;
+                plan->sub = kTrSubElems;
+                if (mode == 1) {
+                    plan->sm = static_cast<int>(C);
+                    plan->sn = static_cast<int>(S);
+                    plan->subs_m = 1;
+                    plan->subs_n = static_cast<uint32_t>(subs);
+                } else {
+                    plan->sn = static_cast<int>(C);
+                    plan->sm = static_cast<int>(S);
+                    plan->subs_n = 1;
+                    plan->subs_m = static_cast<uint32_t>(subs);
+                }
+                plan->nwork = static_cast<uint64_t>(B * subs);
+            }
+        }
+    }
     if (plan->skew) {
         // Groups of G vertically adjacent items on one XCD: the upper neighbour's band rows are
         // still in that L2.  G = 4, 8 and 16 measured within 2-4% of each other; 8 with 16-byte x

@@ -34,6 +34,8 @@ constexpr int64_t kRowsWideMinN = 2048;    // ... and padding past an eighth of 
                                            // rows), half (rows off the 16-byte grid)
                                          // (C * C < 2^32 for the device's 32-bit modulo)
 constexpr int kTrSub = 32;          // transpose: staged sub-tile edge (one 128-byte line of f32) ...
+constexpr int kTrPackBigC = 128;        // transpose: packed side of up to this many channels ...
+constexpr int kTrPackBigElems = 4096;  // ... in work items of up to this many elements
 constexpr int kTrSubElems = kTrSub * kTrSub;  // ... and elements; a narrow tensor's sub-tile is
                                               // narrower and longer (up to kTrSubElems long)
 // Row reductions: rows of at most kTinyRowChunks 16-byte chunks are walked as one tile with
@@ -268,6 +270,8 @@ struct TransposePlan {
     int packed = 0;
     bool pvec = false;            // packed kernel: the strided side moves 16-byte chunks
     bool flat16 = false;          // packed kernel: the packed block starts on 16-byte boundaries
+    bool pbig = false;            // packed kernel: 32 to kTrPackBigC channels, items of up to
+                                  // kTrPackBigElems elements
     uint32_t subs_m = 0, subs_n = 0;
     uint64_t nwork = 0;
     bool wide = false;            // nwork >= 2^32: 64-bit work-item arithmetic

@@ -355,12 +355,19 @@ struct PackedArgs {
     int flat16;           // the packed block starts on 16-byte boundaries
 };
 
-template <int MODE, bool V>
+// CAP: the largest work item (elements): kSubElems for fewer than 32 channels, tmp::kTrPackBigElems
+// for 32 to tmp::kTrPackBigC (16-byte strided rows only; items of 32 positions or more, so that
+// each item's packed block starts and ends on a 128-byte line), whose LDS holds C rows of S + 1.
+template <int CAP>
+constexpr int packed_stage() { return CAP == kSubElems ? kStage : CAP + 2 * tmp::kTrPackBigC; }
+
+template <int MODE, bool V, int CAP = kSubElems>
 __global__ __launch_bounds__(kTrBlock) void transpose_packed(PackedArgs a) {
+    static_assert(CAP == kSubElems || V, "large work items move the strided side in 16-byte chunks");
     constexpr int W = V ? 4 : 1;                       // strided side: elements per chunk
-    constexpr int KS = kSubElems / W / kTrBlock;       // strided chunks per thread (at most)
-    constexpr int KF = kSubElems / 4 / kTrBlock;       // packed 16-byte chunks per thread (at most)
-    __shared__ float tile[kStage];
+    constexpr int KS = CAP / W / kTrBlock;             // strided chunks per thread (at most)
+    constexpr int KF = CAP / 4 / kTrBlock;             // packed 16-byte chunks per thread (at most)
+    __shared__ float tile[packed_stage<CAP>()];
     const int t = threadIdx.x;
     const int S = 1 << a.log_s, pad = S + 1;
     const int lcs = a.log_s - (V ? 2 : 0);             // log2 of the strided chunks per channel row
@@ -524,10 +531,12 @@ hipError_t launch_packed(const tmp::TransposePlan &p, hipStream_t stream) {
     a.log_s = tmp::ilog2(m0 ? p.sn : p.sm);
     a.flat16 = p.flat16 ? 1 : 0;
     void *args[] = {&a};
-    const void *fn = m0 ? (p.pvec ? reinterpret_cast<const void *>(&transpose_packed<0, true>)
-                                  : reinterpret_cast<const void *>(&transpose_packed<0, false>))
-                        : (p.pvec ? reinterpret_cast<const void *>(&transpose_packed<1, true>)
-                                  : reinterpret_cast<const void *>(&transpose_packed<1, false>));
+    const void *fn = p.pbig ? (m0 ? reinterpret_cast<const void *>(&transpose_packed<0, true, tmp::kTrPackBigElems>)
+                                  : reinterpret_cast<const void *>(&transpose_packed<1, true, tmp::kTrPackBigElems>))
+                     : m0 ? (p.pvec ? reinterpret_cast<const void *>(&transpose_packed<0, true>)
+                                    : reinterpret_cast<const void *>(&transpose_packed<0, false>))
+                          : (p.pvec ? reinterpret_cast<const void *>(&transpose_packed<1, true>)
+                                    : reinterpret_cast<const void *>(&transpose_packed<1, false>));
     return hipLaunchKernel(fn, dim3(p.grid), dim3(kTrBlock), args, 0, stream);
 }
 

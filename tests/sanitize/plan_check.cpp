@@ -24,7 +24,7 @@
 
 #include "../../edge_masking_vector_amd/csrc/plan.h"
 
-static long g_checked = 0, g_failed = 0, g_flat = 0, g_rows = 0, g_skew = 0, g_dead_items = 0;
+static long g_checked = 0, g_failed = 0, g_flat = 0, g_rows = 0, g_skew = 0, g_dead_items = 0, g_pbig = 0;
 
 #define CHECK(cond, ...)                                   \
     do {                                                   \
@@ -541,6 +541,27 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
         ++g_checked;
         return;
     }
+    if (p.pbig) {
+        // packed side of 32 to kTrPackBigC channels: items of S positions x C channels, S the
+        // largest power of two with S C <= kTrPackBigElems, at least 32 (so each item's packed
+        // block ends on a 128-byte line); 16-byte chunks on both sides; the LDS holds C rows of S + 1
+        const bool m0 = p.packed == 1;
+        const int64_t C = m0 ? M : N, S = m0 ? p.sn : p.sm, P = m0 ? N : M;
+        CHECK((p.packed == 1 || p.packed == 2) && !p.aligned && !p.skew && p.log_g == 0 && p.pvec && p.flat16,
+              "%s large packed mode", tag);
+        CHECK(C >= tmp::kTrSub && C <= tmp::kTrPackBigC && (m0 ? p.ldy == M : p.ldx == N) && P >= 2 * tmp::kTrSub,
+              "%s large packed shape", tag);
+        CHECK((S & (S - 1)) == 0 && S >= 32 && S * C <= tmp::kTrPackBigElems && 2 * S * C > tmp::kTrPackBigElems &&
+                  C * (S + 1) <= tmp::kTrPackBigElems + 2 * tmp::kTrPackBigC && (S * C * 4) % 128 == 0,
+              "%s large packed item of %ld x %ld", tag, long(S), long(C));
+        const uint32_t subs = uint32_t((P + S - 1) / S);
+        CHECK((m0 ? (p.subs_m == 1 && p.subs_n == subs) : (p.subs_n == 1 && p.subs_m == subs)) &&
+                  p.nwork == uint64_t(B) * subs,
+              "%s large packed work", tag);
+        ++g_checked;
+        ++g_pbig;
+        return;
+    }
     CHECK((p.sm & (p.sm - 1)) == 0 && (p.sn & (p.sn - 1)) == 0 && int64_t(p.sm) * p.sn <= p.sub,
           "%s sub-tile %dx%d above %d elements", tag, p.sm, p.sn, p.sub);
     // the staged sub-tile (rows of stride SN + 1 floats) fits the instance's LDS of 2 * sub floats
@@ -654,6 +675,30 @@ static void check_skew_transposes() {
                 CHECK(st == TM_OK && p.launch && p.skew, "%s not planned as line-aligned windows", tag);
                 if (st == TM_OK && p.launch)
                     replay_transpose(p, 1, c.M, c.N, tag);
+            }
+}
+
+// NCHW <-> NHWC with 32 to 128 channels: the packed kernel's large items when the packed rows miss
+// the line grid, the sub-tiles when they lie on it (64 channels on a line-aligned base).
+static void check_packed_big() {
+    struct S { int64_t B, C, P; };
+    const S cases[] = {{32, 65, 3136}, {4, 33, 100}, {2, 128, 4100}, {1, 100, 5000}, {3, 127, 64}, {8, 64, 3136},
+                       {2, 32, 1000}};
+    for (const S &c : cases)
+        for (int rev = 0; rev <= 1; ++rev)
+            for (uintptr_t off : {uintptr_t{0}, uintptr_t{16}, uintptr_t{4}}) {
+                const int64_t M = rev ? c.P : c.C, N = rev ? c.C : c.P;
+                tmp::TransposePlan p;
+                const int st = tmp::plan_transpose(fake(0x100000 + off), N, M * N, const_cast<float *>(fake(0x40000000 + off)),
+                                                   M, M * N, c.B, M, N, 1, 1, 0, &p);
+                if (st != TM_OK)
+                    continue;
+                char tag[160];
+                std::snprintf(tag, sizeof tag, "packed B=%ld C=%ld P=%ld rev=%d off=%lu", long(c.B), long(c.C),
+                              long(c.P), rev, (unsigned long)off);
+                const bool lines = c.C % 32 == 0 && off == 0;   // packed rows on the line grid
+                CHECK(p.pbig == (!lines && off % 16 == 0 && c.P >= 64), "%s: large packed items %d", tag, int(p.pbig));
+                replay_transpose(p, c.B, M, N, tag);
             }
 }
 
@@ -969,6 +1014,8 @@ int main() {
     check_reductions();
     check_split_rows();
     check_skew_transposes();
+    check_packed_big();
+    CHECK(g_pbig >= 20, "only %ld large packed plans replayed", g_pbig);
     CHECK(g_rows > 0, "no padded-row span plan was replayed");
     CHECK(g_skew >= 36, "only %ld line-aligned window plans replayed", g_skew);
     std::printf("plan_check: %ld plans checked (%ld flat, %ld span), %ld failures\n", g_checked, g_flat, g_rows,

@@ -103,6 +103,24 @@ def test_nchw_nhwc_few_channels(dev, C):
         check_transpose(dev, B, HW, C, C, HW, HW * C, C * HW, 64, 4, 1, seed=C + 300)
 
 
+@pytest.mark.parametrize("B,C,HW,off", [
+    (32, 65, 56 * 56, 0),    # odd channel counts: the packed rows miss the line grid
+    (16, 100, 56 * 56, 0),   # 16-byte packed rows that miss the line grid
+    (4, 33, 100, 4),         # a ragged last item (100 positions in items of 128), base 16 bytes off
+    (2, 128, 4100, 0),       # the largest channel count, items of 64 positions
+    (3, 127, 64, 0),         # one item per batch
+    (8, 64, 3136, 0),        # packed rows on the line grid: the sub-tiles
+])
+def test_nchw_nhwc_channels_32_to_128(dev, B, C, HW, off):
+    """32 to 128 channels whose packed rows (C floats) miss the 128-byte line grid take the packed
+    kernel with large items (S positions x C channels per item, each item's packed block one run
+    of 16-byte chunks that ends on a line): both directions bit for bit against the oracle, the
+    guard bands untouched."""
+    note("channels 32-128: B=%d C=%d HW=%d off=%d" % (B, C, HW, off))
+    check_transpose(dev, B, C, HW, HW, C, C * HW, HW * C, 1, 64, 0, xoff=off, yoff=off, seed=C + HW)
+    check_transpose(dev, B, HW, C, C, HW, HW * C, C * HW, 64, 1, 0, xoff=off, yoff=off, seed=C + HW + 1)
+
+
 def test_transpose_narrow_edges(dev):
     """Single rows and columns, narrow and ragged both ways, odd strides, misaligned bases."""
     for (M, N, ldx, ldy, xoff, yoff) in ((1, 5000, 5000, 1, 0, 0), (5000, 1, 1, 5000, 0, 0),
