@@ -940,9 +940,12 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
         return TM_E_ALIGN;
     if (!work)
         return TM_OK;
-    const bool y_lines = aligned_to(y, kLineBytes) && (N <= 1 || ldy % (kLineBytes / 4) == 0);
+    const bool y_lines = aligned_to(y, kLineBytes) && (N <= 1 || ldy % (kLineBytes / 4) == 0) &&
+                         (B <= 1 || bsy % (kLineBytes / 4) == 0);
     const bool large = !aligned && M >= 2 * kTrSub && N >= kTrSub && M * N >= (int64_t{1} << 22);
-    const bool skew = large && B == 1 && !y_lines;
+    // (batches: the line windows of every batch, numbered as one matrix of B x subs_n strips)
+    const bool skew = !aligned && M >= 2 * kTrSub && N >= kTrSub &&
+                      M * N >= ceil_div(int64_t{1} << 22, std::max<int64_t>(B, 1)) && !y_lines;
     // x's reads move in 16-byte chunks also off the 16-byte grid, as 4-byte aligned 16-byte loads,
     // when its rows hold a whole sub-tile row.
     const bool vx = vx16 || N >= kTrSub;
@@ -997,7 +1000,7 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     // rotating buffers): 4096 x 4096 at y stride 4100 30.3 -> 26.9 us, 4098 35.2 -> 27.3, 4097
     // 35.2 -> 27.6, both strides 4097 43.4 -> 32.5 (4-byte x reads), 5450 x 2568 36.9 -> 25.8,
     // 57348 x 252 39.4 -> 26.8, 1707 x 7425 37.9 -> 26.2, 4099 x 4099 48.2 -> 32.3.
-    if (large && (!vy || skew)) {
+    if ((large && !vy) || skew) {
         plan->sm = 2 * kTrSub;
         plan->sn = kTrSub;
         plan->sub = 2 * kTrSubElems;
@@ -1104,9 +1107,17 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
         // 9163 x 1051 19.7 against 20.2, 4096 x 4096 with both strides 4097 31.2-32.3 either way.)
         // Work items: 8 G per 8 groups (group r -> items 8 G (r / 8) + r mod 8 + 8 k, member k < G).
         plan->log_grp = vx ? 3 : 2;
+        // few item rows (short y rows, as in batches): smaller groups, so that at most a quarter of
+        // the group slots lie past the last item row (9 item rows in groups of 8 left 7 of 16 idle)
+        while (plan->log_grp > 0 &&
+               4 * (ceil_div(subs_m, int64_t{1} << plan->log_grp) * (int64_t{1} << plan->log_grp) - subs_m) >
+                   ceil_div(subs_m, int64_t{1} << plan->log_grp) * (int64_t{1} << plan->log_grp))
+            --plan->log_grp;
         const int64_t G = int64_t{1} << plan->log_grp;
         const int64_t grp_rows = ceil_div(subs_m, G);
-        const int64_t items = ceil_div(grp_rows * subs_n, 8) * 8 * G;
+        if (B > INT32_MAX || grp_rows * subs_n > UINT32_MAX / B)
+            return TM_E_UNSUPPORTED;  // group ids are 32-bit
+        const int64_t items = ceil_div(grp_rows * subs_n * B, 8) * 8 * G;
         if (items > UINT32_MAX)
             return TM_E_UNSUPPORTED;  // work ids are 32-bit in this order
         plan->nwork = static_cast<uint64_t>(items);

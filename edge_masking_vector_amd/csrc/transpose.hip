@@ -75,13 +75,15 @@ template <bool GROUPS>
 __device__ __forceinline__ void decode32(const TrArgs &a, uint32_t w32, uint32_t &b, uint32_t &pm, uint32_t &pn,
                                          bool &skip) {
     if constexpr (GROUPS) {
+        // groups are numbered by group row fastest, then by column strip over all batches (batch
+        // q / subs_n, strip q mod subs_n)
         const uint32_t grp = (w32 >> (3 + a.log_g)) * 8 + (w32 & 7u);
         const uint32_t member = (w32 >> 3) & ((1u << a.log_g) - 1u);
         const uint32_t q = fast_div(grp, a.c_pb, a.per_b);  // per_b: group rows
-        b = 0;
+        b = fast_div(q, a.c_n, a.subs_n);
         pm = ((grp - q * a.per_b) << a.log_g) + member;    // < subs_m + 2^log_g <= 2^32
-        pn = q;
-        skip = pm >= a.subs_m || pn >= a.subs_n;
+        pn = q - b * a.subs_n;
+        skip = pm >= a.subs_m || int64_t(b) >= a.B;
     } else {
         const uint32_t b32 = fast_div(w32, a.c_pb, a.per_b);
         const uint32_t rest = w32 - b32 * a.per_b;
@@ -229,8 +231,10 @@ __global__ __launch_bounds__(BS) void transpose_tiles(TrArgs a) {
 }
 
 // ---- y rows off the line grid: line-aligned y windows -------------------------------------------
-// One matrix whose y rows miss the 128-byte line grid.  With sub-tiles, the sub-tiles above and
-// below each other share the lines at the ends of their y-row pieces, and a line that two
+// Matrices whose y rows miss the 128-byte line grid (a batch's windows are numbered with its
+// column strips: strip q of B x subs_n is strip q mod subs_n of batch q / subs_n).  With
+// sub-tiles, the sub-tiles above and below each other share the lines at the ends of their y-row
+// pieces, and a line that two
 // workgroups write in parts reaches memory as two partial writes unless both parts meet in one
 // L2 first; HBM3E has no write mask, so each costs the controller a read-modify-write (written
 // bytes rose only 11-13%, but 4096 x 4096 with y stride 4100 took 55.7 against 24.4 us).
@@ -282,10 +286,10 @@ __global__ __launch_bounds__(kTrBlock) void transpose_skew(TrArgs a) {
                 xr = xr < 0 ? 0 : (xr >= a.M ? a.M - 1 : xr);
                 if constexpr (VX) {
                     const int cs = c < clast ? c * WX : cend;  // cend >= -3: col0 >= 32 when below 4
-                    const f4 q = ld16u(a.x + xr * a.ldx + col0 + cs);
+                    const f4 q = ld16u(a.x + int64_t(b) * a.bsx + xr * a.ldx + col0 + cs);
                     v[k][0] = q.x, v[k][1] = q.y, v[k][2] = q.z, v[k][3] = q.w;
                 } else {
-                    v[k][0] = a.x[xr * a.ldx + col0 + (c < clast ? c : clast)];
+                    v[k][0] = a.x[int64_t(b) * a.bsx + xr * a.ldx + col0 + (c < clast ? c : clast)];
                 }
             }
 #pragma unroll
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(kTrBlock) void transpose_skew(TrArgs a) {
                 const int e = t + k * kTrBlock;
                 const int j = e >> 4, c = e & 15;  // y row j, chunk c of its 64-element window
                 if (j < cols_live) {
-                    float *yr = a.y + (col0 + j) * a.ldy;
+                    float *yr = a.y + int64_t(b) * a.bsy + (col0 + j) * a.ldy;
                     const int sft = static_cast<int>((reinterpret_cast<uintptr_t>(yr + row0) >> 2) & 31u);
                     const int64_t i0 = row0 - sft + 4 * c;  // y column (x row) of the chunk's first element
                     const int br = SN - sft + 4 * c;        // its band row
@@ -543,7 +547,7 @@ hipError_t launch_packed(const tmp::TransposePlan &p, hipStream_t stream) {
 template <bool WIDE, bool PACK>
 const void *pick(const tmp::TransposePlan &p) {
     if constexpr (!PACK && !WIDE) {
-        if (p.skew)  // y rows off the line grid, one matrix: line-aligned y windows
+        if (p.skew)  // y rows off the line grid: line-aligned y windows
             return p.vx ? reinterpret_cast<const void *>(&transpose_skew<true>)
                         : reinterpret_cast<const void *>(&transpose_skew<false>);
     }

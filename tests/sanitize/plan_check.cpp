@@ -466,7 +466,7 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
         // x clamped into [0, M).  Every element of y must be written exactly once, by the item whose
         // band holds its x row, and 16-byte stores must be aligned.
         const uint32_t G = 1u << p.log_grp;
-        CHECK(B == 1 && !p.wide && p.log_g == 0 && p.packed == 0 && p.log_grp >= 1 && p.log_grp <= 4 &&
+        CHECK(B >= 1 && !p.wide && p.log_g == 0 && p.packed == 0 && p.log_grp >= 0 && p.log_grp <= 4 &&
                   p.nwork % (8 * G) == 0 && p.grid % (8 * G) == 0 && p.sm == 64 && p.sn == 32,
               "%s skew plan", tag);
         const uint32_t grp_rows = (p.subs_m + G - 1) / G;
@@ -498,20 +498,23 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
             CHECK(!bad_read, "%s skew: a 16-byte read outside its row, or a live column not staged", tag);
         }
         const uintptr_t ya = reinterpret_cast<uintptr_t>(p.y);
-        std::vector<uint8_t> hits(size_t(N) * M, 0);
+        std::vector<uint8_t> hits(size_t(B) * size_t(N) * M, 0);
         bool bad = false;
+        CHECK(p.nwork >= uint64_t(grp_rows) * p.subs_n * uint64_t(B) * G, "%s skew: too few items", tag);
         for (uint64_t w = 0; w < p.nwork; ++w) {
             const uint32_t w32 = uint32_t(w);
             const uint32_t grp = (w32 >> (3 + p.log_grp)) * 8 + (w32 & 7u), member = (w32 >> 3) & (G - 1);
             const uint32_t q = umulhi_div(grp, p.per_b);
-            const uint64_t pm = uint64_t(grp - q * p.per_b.d) * G + member, pn = q;
-            CHECK(q == grp / grp_rows, "%s group division", tag);
-            if (pm >= p.subs_m || pn >= p.subs_n)
+            // the group's column strip runs over all batches: batch q / subs_n, strip q mod subs_n
+            const uint32_t b = umulhi_div(q, p.by_n);
+            const uint64_t pm = uint64_t(grp - q * p.per_b.d) * G + member, pn = q - b * p.subs_n;
+            CHECK(q == grp / grp_rows && b == q / p.subs_n, "%s group division", tag);
+            if (pm >= p.subs_m || int64_t(b) >= B)
                 continue;
             const int64_t row0 = int64_t(pm) * 64, col0 = int64_t(pn) * 32;
             const int cols_live = int(std::min<int64_t>(N - col0, 32));
             for (int j = 0; j < cols_live; ++j) {
-                const uintptr_t yr = ya + 4 * uintptr_t((col0 + j) * p.ldy);
+                const uintptr_t yr = ya + 4 * uintptr_t(int64_t(b) * p.bsy + (col0 + j) * p.ldy);
                 const int sft = int(((yr + 4 * uintptr_t(row0)) >> 2) & 31u);
                 for (int c = 0; c < 16; ++c) {
                     const int64_t i0 = row0 - sft + 4 * c;
@@ -525,7 +528,7 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
                         if (i >= 0 && i < M) {
                             if (i - (row0 - 32) != br + e)
                                 bad = true;  // the band row is not this x row
-                            ++hits[size_t(col0 + j) * M + i];
+                            ++hits[(size_t(b) * size_t(N) + size_t(col0 + j)) * M + i];
                         }
                     }
                 }
@@ -676,6 +679,24 @@ static void check_skew_transposes() {
                 if (st == TM_OK && p.launch)
                     replay_transpose(p, 1, c.M, c.N, tag);
             }
+    // batches: y rows off the line grid in some batch (the row stride, the batch stride or the base)
+    struct SB { int64_t B, M, N, ldx, ldy, bsx, bsy; };
+    const SB bcases[] = {{8, 200, 4096, 4096, 200, 200 * 4096, 4096 * 200},    // NCHW -> NHWC, 200 channels
+                         {3, 300, 5000, 5001, 300, 300 * 5001, 5000 * 300 + 7},  // padded batch stride
+                         {4, 4096, 256, 256, 4096, 4096 * 256, 256 * 4096 + 4},  // rows on lines, batches not
+                         {2, 129, 20000, 20000, 129, 129 * 20000, 20000 * 129}};
+    for (const SB &c : bcases)
+        for (uintptr_t yoff : {uintptr_t{0}, uintptr_t{16}}) {
+            tmp::TransposePlan p;
+            const int st = tmp::plan_transpose(fake(0x1000000), c.ldx, c.bsx, const_cast<float *>(fake(0x40000000 + yoff)),
+                                               c.ldy, c.bsy, c.B, c.M, c.N, 1, 1, 0, &p);
+            char tag[160];
+            std::snprintf(tag, sizeof tag, "batched skew transpose B=%ld %ldx%ld ldy=%ld bsy=%ld yoff=%lu", long(c.B),
+                          long(c.M), long(c.N), long(c.ldy), long(c.bsy), (unsigned long)yoff);
+            CHECK(st == TM_OK && p.launch && p.skew, "%s not planned as line-aligned windows", tag);
+            if (st == TM_OK && p.launch)
+                replay_transpose(p, c.B, c.M, c.N, tag);
+        }
 }
 
 // NCHW <-> NHWC with 32 to 128 channels: the packed kernel's large items when the packed rows miss

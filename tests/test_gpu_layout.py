@@ -243,8 +243,16 @@ def test_transpose_y_rows_off_the_grid(dev, M, N, ldx, ldy, xoff, yoff):
     check_transpose(dev, 1, M, N, ldx, ldy, 0, 0, 1, 1, 0, xoff=xoff, yoff=yoff, seed=M + N)
 
 
-def test_transpose_batched_off_the_line_grid(dev):
-    """Several matrices whose y rows miss the line grid take 64 x 32 sub-tiles in the plain order."""
-    B, M, N, ldx, ldy = 3, 1030, 2051, 2052, 1034
-    note("transpose batched off-grid")
-    check_transpose(dev, B, M, N, ldx, ldy, M * ldx + 8, N * ldy + 4, 1, 1, 0, seed=77)
+@pytest.mark.parametrize("B,M,N,ldx,ldy,bsx,bsy,yoff", [
+    (3, 1030, 2051, 2052, 1034, 1030 * 2052 + 8, 2051 * 1034 + 4, 0),   # padded batch strides
+    (8, 200, 4096, 4096, 200, 200 * 4096, 4096 * 200, 0),               # NCHW -> NHWC, 200 channels
+    (4, 4096, 256, 256, 4096, 4096 * 256, 256 * 4096 + 4, 0),           # rows on lines, batches not
+    (2, 129, 20000, 20000, 129, 129 * 20000, 20000 * 129, 3),           # base off the 16-byte grid
+    (2, 100, 1000, 1001, 100, 100 * 1001, 1000 * 100, 0),               # below the size for windows
+])
+def test_transpose_batched_off_the_line_grid(dev, B, M, N, ldx, ldy, bsx, bsy, yoff):
+    """Batches whose y rows miss the line grid in some batch (row stride, batch stride or base)
+    take the line-aligned y windows, numbered over every batch's column strips (small views keep
+    the sub-tiles): bit for bit against the oracle, the guard bands untouched."""
+    note("transpose batched off-grid B=%d %dx%d ldy %d bsy %d yoff %d" % (B, M, N, ldy, bsy, yoff))
+    check_transpose(dev, B, M, N, ldx, ldy, bsx, bsy, 1, 1, 0, yoff=yoff, seed=77 + B + M)
