@@ -944,7 +944,7 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
                          (B <= 1 || bsy % (kLineBytes / 4) == 0);
     const bool large = !aligned && M >= 2 * kTrSub && N >= kTrSub && M * N >= (int64_t{1} << 22);
     // (batches: the line windows of every batch, numbered as one matrix of B x subs_n strips)
-    const bool skew = !aligned && M >= 2 * kTrSub && N >= kTrSub &&
+    const bool skew = !aligned && M >= 2 * kTrSub && N >= kTrWindowMinN &&
                       M * N >= ceil_div(int64_t{1} << 22, std::max<int64_t>(B, 1)) && !y_lines;
     // x's reads move in 16-byte chunks also off the 16-byte grid, as 4-byte aligned 16-byte loads,
     // when its rows hold a whole sub-tile row.
@@ -1032,7 +1032,7 @@ int plan_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t l
     // side of a work item is one contiguous block, moved in 16-byte chunks by transpose_packed.
     // (32, 3, 224, 224) NCHW -> NHWC and back: 13.9 -> 8.9 us; 1 to 31 channels gain 1.25-1.7x
     // (in one process, over 1 GiB of rotating buffers, outputs compared bit for bit).
-    if (!vec && plan->log_g == 0 && !(M < kTrSub && N < kTrSub)) {
+    if (!vec && !plan->skew && plan->log_g == 0 && !(M < kTrSub && N < kTrSub)) {
         const bool bs16y = B <= 1 || bsy % 4 == 0, bs16x = B <= 1 || bsx % 4 == 0;
         if (M < kTrSub && ldy == M && subs_m == 1) {
             plan->packed = 1;

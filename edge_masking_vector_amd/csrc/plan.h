@@ -34,6 +34,9 @@ constexpr int64_t kRowsWideMinN = 2048;    // ... and padding past an eighth of 
                                            // rows), half (rows off the 16-byte grid)
                                          // (C * C < 2^32 for the device's 32-bit modulo)
 constexpr int kTrSub = 32;          // transpose: staged sub-tile edge (one 128-byte line of f32) ...
+constexpr int64_t kTrWindowMinN = 12;  // transpose: line windows of y rows off the line grid need
+                                       // x rows of at least this many floats (fewer: each window
+                                       // item writes too short a stretch of y rows to pay)
 constexpr int kTrPackBigC = 128;        // transpose: packed side of up to this many channels ...
 constexpr int kTrPackBigElems = 4096;  // ... in work items of up to this many elements
 constexpr int kTrSubElems = kTrSub * kTrSub;  // ... and elements; a narrow tensor's sub-tile is

@@ -476,14 +476,16 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
             // at or past the one holding the last live column read the 16 bytes that end at it;
             // every read lies inside the row, and every live column is staged by its own chunk or
             // by the clamped one
-            CHECK(p.vx && N >= tmp::kTrSub, "%s skew: x chunk width", tag);
+            const uintptr_t xa = reinterpret_cast<uintptr_t>(p.x);
+            const bool x16 = xa % 16 == 0 && (M <= 1 || p.ldx % 4 == 0) && (B <= 1 || p.bsx % 4 == 0);
+            CHECK(p.vx == (x16 || N >= tmp::kTrSub) && N >= tmp::kTrWindowMinN, "%s skew: x chunk width", tag);
             bool bad_read = false;
             for (uint32_t pn = 0; pn < p.subs_n; ++pn) {
                 const int64_t col0 = int64_t(pn) * 32;
                 const int cols_live = int(std::min<int64_t>(N - col0, 32));
                 const int clast = (cols_live - 1) / 4, cend = cols_live - 4;
                 std::vector<int> staged(32, 0);
-                for (int c = 0; c < 8; ++c) {
+                for (int c = 0; c < 8 && p.vx; ++c) {
                     const int cs = c < clast ? 4 * c : cend;
                     if (col0 + cs < 0 || col0 + cs + 4 > N)
                         bad_read = true;
@@ -491,7 +493,7 @@ static void replay_transpose(const tmp::TransposePlan &p, int64_t B, int64_t M, 
                         if (cs + i >= 0 && cs + i < 32)
                             ++staged[size_t(cs + i)];
                 }
-                for (int j = 0; j < cols_live; ++j)
+                for (int j = 0; j < cols_live && p.vx; ++j)
                     if (staged[size_t(j)] == 0)
                         bad_read = true;
             }
@@ -684,7 +686,11 @@ static void check_skew_transposes() {
     const SB bcases[] = {{8, 200, 4096, 4096, 200, 200 * 4096, 4096 * 200},    // NCHW -> NHWC, 200 channels
                          {3, 300, 5000, 5001, 300, 300 * 5001, 5000 * 300 + 7},  // padded batch stride
                          {4, 4096, 256, 256, 4096, 4096 * 256, 256 * 4096 + 4},  // rows on lines, batches not
-                         {2, 129, 20000, 20000, 129, 129 * 20000, 20000 * 129}};
+                         {2, 129, 20000, 20000, 129, 129 * 20000, 20000 * 129},
+                         {1, 1198372, 28, 68, 1198373, 0, 0},          // few columns, long y rows off the grid
+                         {1, 1398101, 24, 24, 1398102, 0, 0},
+                         {1, 900000, 12, 13, 900001, 0, 0},
+                         {1, 330000, 13, 13, 330004, 0, 0}};
     for (const SB &c : bcases)
         for (uintptr_t yoff : {uintptr_t{0}, uintptr_t{16}}) {
             tmp::TransposePlan p;

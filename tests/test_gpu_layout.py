@@ -249,10 +249,15 @@ def test_transpose_y_rows_off_the_grid(dev, M, N, ldx, ldy, xoff, yoff):
     (4, 4096, 256, 256, 4096, 4096 * 256, 256 * 4096 + 4, 0),           # rows on lines, batches not
     (2, 129, 20000, 20000, 129, 129 * 20000, 20000 * 129, 3),           # base off the 16-byte grid
     (2, 100, 1000, 1001, 100, 100 * 1001, 1000 * 100, 0),               # below the size for windows
+    (1, 1198372 // 4, 28, 68, 1198373 // 4 + 1, 0, 0, 0),                # few columns, long y rows
+    (1, 700000, 12, 13, 700001, 0, 0, 1),
+    (1, 700000, 9, 9, 700001, 0, 0, 0),                                  # too few columns for windows
+    (1, 1398101 // 2, 24, 24, 1398102 // 2, 0, 0, 1),                    # x rows of exactly 24 floats
 ])
 def test_transpose_batched_off_the_line_grid(dev, B, M, N, ldx, ldy, bsx, bsy, yoff):
     """Batches whose y rows miss the line grid in some batch (row stride, batch stride or base)
     take the line-aligned y windows, numbered over every batch's column strips (small views keep
-    the sub-tiles): bit for bit against the oracle, the guard bands untouched."""
+    the sub-tiles), as do views of 12 to 31 columns whose long y rows miss it: bit for bit against
+    the oracle, the guard bands untouched."""
     note("transpose batched off-grid B=%d %dx%d ldy %d bsy %d yoff %d" % (B, M, N, ldy, bsy, yoff))
     check_transpose(dev, B, M, N, ldx, ldy, bsx, bsy, 1, 1, 0, yoff=yoff, seed=77 + B + M)
