@@ -8,9 +8,10 @@
 // out-of-range elements read as 0).
 //
 // Both walks cut the rows into slabs and write one partial per (slab, column) into the caller's
-// workspace ws[slab * N + column]; colsum_finish then adds each column's partials in a fixed order
-// (a group of lanes per column, each taking every FL-th slab, then a lane tree).  Nothing uses
-// atomics, so results are deterministic.
+// workspace, column by column: ws[column * slabs + slab]; colsum_finish then adds each column's
+// partials in a fixed order (a group of lanes per column, each taking every FL-th slab, then a
+// lane tree), so the lanes of a column read consecutive floats.  Nothing uses atomics, so results
+// are deterministic.
 //
 // Naive walk: slabs of the caller's TM rows; one workgroup per (slab, column), column fastest;
 // lane t reads row slab*TM + t of that column.  The lane-varying term of the address is row * ld: every lane touches its own
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(kBlock) void col_naive(ColArgs a) {
             float s = wave_sum[0];
             for (int i = 1; i < nwaves; ++i)
                 s += wave_sum[i];
-            a.ws[int64_t(slab) * a.N + c] = s;
+            a.ws[c * int64_t(a.slabs) + int64_t(slab)] = s;
         }
         if (w + gridDim.x < nwork)
             __syncthreads();  // the next work item reuses wave_sum (uniform test)
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(kBlock) void col_lds(ColArgs a) {
             for (int k = 0; k < RP; ++k)
                 colsum += part[k * TW + cl];
             if (col0 + cl < a.N)
-                a.ws[int64_t(slab) * a.N + col0 + cl] = colsum;
+                a.ws[(col0 + cl) * int64_t(a.slabs) + int64_t(slab)] = colsum;
         }
         if (w + gridDim.x < nwork)
             __syncthreads();  // the next work item reuses the LDS partials (uniform test)
@@ -313,16 +314,20 @@ __global__ __launch_bounds__(kBlock) void col_direct(ColArgs a) {
 
 // ---- pass 2: fixed-order sum of the slab partials ---------------------------------------------
 
-constexpr int kFinishBatch = 16;   // partials loaded at once per lane, then added in slab order
+constexpr int kFinishBatch = tmp::kFinishBatchSlabs;  // partials loaded at once per lane, then added in slab order
 constexpr int kFinishBlock = 256;  // threads per workgroup: kFinishBlock / FL columns
 
 // FL lanes per column: lane f adds slabs f, f + FL, f + 2 FL, ... in order (batches of
-// kFinishBatch loads in flight), then the FL lane values meet in a fixed DPP tree.  Columns past N
+// kFinishBatch loads in flight), then the FL lane values meet in a fixed DPP tree; past 64 lanes
+// (2 or 4 waves per column) the waves' sums then meet in LDS in wave order.  Columns past N
 // re-read column N - 1 so that every lane takes part in the tree; they are not stored.
 template <int FL>
 __global__ __launch_bounds__(kFinishBlock) void colsum_finish(const float *ws, float *out, int64_t N,
                                                             uint32_t slabs) {
+    static_assert(FL <= kFinishBlock && kFinishBlock % FL == 0, "whole columns per workgroup");
     constexpr int kCols = kFinishBlock / FL;  // columns per workgroup and step
+    constexpr int kWaves = FL > 64 ? FL / 64 : 1;  // waves per column
+    __shared__ float wave_sum[kFinishBlock / 64];
     const int f = threadIdx.x % FL;
     for (int64_t j0 = int64_t(blockIdx.x) * kCols; j0 < N; j0 += int64_t(gridDim.x) * kCols) {
         const int64_t j = j0 + threadIdx.x / FL;
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(kFinishBlock) void colsum_finish(const float *ws, f
 #pragma unroll
             for (int u = 0; u < kFinishBatch; ++u) {
                 const uint32_t s = s0 + uint32_t(u) * FL;
-                v[u] = s < slabs ? ws[int64_t(s) * N + jc] : 0.0f;
+                v[u] = s < slabs ? ws[jc * int64_t(slabs) + int64_t(s)] : 0.0f;
             }
             float blk = 0.0f;
 #pragma unroll
@@ -341,9 +346,25 @@ __global__ __launch_bounds__(kFinishBlock) void colsum_finish(const float *ws, f
                 blk += v[u];
             total += blk;
         }
-        total = group_reduce<SumOp, FL>(total);
-        if (f == 0 && j < N)
-            out[j] = total;
+        if constexpr (kWaves == 1) {
+            total = group_reduce<SumOp, FL>(total);
+            if (f == 0 && j < N)
+                out[j] = total;
+        } else {
+            total = group_reduce<SumOp, 64>(total);
+            if (threadIdx.x % 64 == 0)
+                wave_sum[threadIdx.x / 64] = total;
+            __syncthreads();
+            if (f == 0) {
+                float s = wave_sum[threadIdx.x / 64];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w)
+                    s += wave_sum[threadIdx.x / 64 + w];
+                if (j < N)
+                    out[j] = s;
+            }
+            __syncthreads();  // the next step reuses wave_sum (j0 is uniform over the workgroup)
+        }
     }
 }
 
@@ -355,7 +376,9 @@ const void *pick_finish(int fl) {
     case 8: return reinterpret_cast<const void *>(&colsum_finish<8>);
     case 16: return reinterpret_cast<const void *>(&colsum_finish<16>);
     case 32: return reinterpret_cast<const void *>(&colsum_finish<32>);
-    default: return reinterpret_cast<const void *>(&colsum_finish<64>);
+    case 64: return reinterpret_cast<const void *>(&colsum_finish<64>);
+    case 128: return reinterpret_cast<const void *>(&colsum_finish<128>);
+    default: return reinterpret_cast<const void *>(&colsum_finish<256>);
     }
 }
 

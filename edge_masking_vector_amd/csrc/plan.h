@@ -92,8 +92,12 @@ constexpr int kColRowStrip = 1024;
 constexpr int kColRowSlab = 64;
 constexpr int64_t kColRowMaxSlabs = 256;
 constexpr int64_t kColRowMinWork = 256;
-// Column-sum pass 2: lanes per column chosen so that about this many threads run.
+// Column-sum pass 2: lanes per column chosen so that about this many threads run (one wave per
+// column at most), or up to kFinishMaxLanes lanes (whole waves) while each lane would add more
+// than kFinishBatchSlabs partials, the partials one lane loads at once.
 constexpr int kFinishThreads = 16384;
+constexpr int kFinishMaxLanes = 256;
+constexpr int kFinishBatchSlabs = 16;
 // The LDS walk goes direct (one thread per 16-byte column chunk down all rows, one pass) for at
 // most kColDirectRows rows, or at most kColDirectRowsWide rows of at least kColDirectMinN columns.
 constexpr int64_t kColDirectRows = 64;
@@ -238,7 +242,7 @@ struct ColPlan {
     // LDS walk over wide matrices (col_strip + colsum_fold16): a workgroup per (slab, strip of
     // kColRowStrip columns), each thread one 16-byte column chunk; partials as 16-byte vectors.
     bool strip = false;
-    int fl = 1;                   // pass 2: lanes per column (power of two <= 64)
+    int fl = 1;                   // pass 2: lanes per column (power of two <= kFinishMaxLanes)
     int naive_block = 64;         // threads per workgroup (naive walk)
     uint32_t slabs = 0;           // ceil(M / rows per slab): partials per column
     uint32_t strips = 0;          // column strips (LDS walk) or columns (naive walk)

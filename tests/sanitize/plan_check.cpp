@@ -911,7 +911,9 @@ static void check_reductions() {
                                 } else {
                                     CHECK(ts == TR, "cols slab rows");
                                 }
-                                CHECK(c.fl >= 1 && c.fl <= 64 && (c.fl & (c.fl - 1)) == 0, "cols fl %d", c.fl);
+                                CHECK(c.fl >= 1 && c.fl <= tmp::kFinishMaxLanes && (c.fl & (c.fl - 1)) == 0 &&
+                                          (c.fl <= 64 || int64_t(c.fl / 2) * tmp::kFinishBatchSlabs < int64_t(c.slabs)),
+                                      "cols fl %d", c.fl);
                                 if (walk == TM_COL_LDS) {
                                     CHECK(c.tw >= 1 && c.tw <= tmp::kColStrip && uint64_t(c.strips) * c.tw >= uint64_t(N),
                                           "cols strips");

@@ -114,6 +114,25 @@ def test_sums_long_rows_and_tall_columns(dev):
         assert O.guards_intact() and W.guards_intact()
 
 
+@pytest.mark.parametrize("N", [37, 200])
+def test_colsum_second_pass_over_two_waves_per_column(dev, N):
+    """300007 rows make 1172 slab partials per column: the second pass gives each column two waves
+    (128 lanes, whose sums meet in LDS), two columns per workgroup, the last one past N when N is
+    odd.  Both walks, within 1e-5 of the fp64 sums."""
+    M = 300007
+    xh = inputs.uniform(93 + N, M * N, -1.0, 1.0)
+    X, host = device_matrix(xh, M, N, N, dev)
+    ref = oracle.colsum_f64(host, N, M, N)
+    absref = oracle.colsum_f64(np.abs(host), N, M, N)
+    for walk, TM, TN in ((tm.TM_COL_LDS, 256, 64), (tm.TM_COL_NAIVE, 256, 1)):
+        note("colsum two waves per column %dx%d walk=%d tile=%dx%d" % (M, N, walk, TM, TN))
+        st, O, W = gpu_colsum(X, N, M, N, TM, TN, 0, walk, dev)
+        assert st == tm.TM_OK
+        torch.cuda.synchronize()
+        assert_sums(O.payload().cpu().numpy(), ref, absref)
+        assert O.guards_intact() and W.guards_intact()
+
+
 @pytest.mark.parametrize("M", [1, 7, 300, 700, 1500])
 def test_row_reductions_multiwave_rows(dev, M):
     """Few long rows get a workgroup of several waves per row, combined across the waves through
