@@ -500,9 +500,15 @@ def run_paths(torch, tm, inputs, dev, stream, K, W, sweep_out=None, sweep=True, 
                                ("colsum_lds_4096", tm.TM_COL_LDS, 256, 64)):
         wsb = tm.tm_colsum_workspace_bytes(M, N, TM, TN, walk)
         wss = [torch.zeros(wsb // 4, device=dev) for _ in range(R)]
-        slabs = wsb // (4 * N)
-        geometry = ("the naive walk: %d-row slabs of one column per workgroup" % TM if walk != tm.TM_COL_LDS
-                    else "the LDS walk's own %d-row slabs by 128-column strips" % (M // slabs))
+        st, form, srows, scols, slabs, strips = tm.tm_col_walk(xs[0], N, outs[0], M, N, TM, TN,
+                                                               walk == tm.TM_COL_LDS and 1 or 0, walk,
+                                                               wss[0], wsb)
+        ok(st)
+        geometry = ("the naive walk: %d-row slabs of one column per workgroup" % srows
+                    if walk != tm.TM_COL_LDS else
+                    "the LDS walk's own %d-row slabs by %d-column strips (%d x %d workgroups%s)"
+                    % (srows, scols, slabs, strips,
+                       ", one 16-byte column chunk per thread" if form == tm.TM_COLFORM_STRIPS else ""))
         timed(name, nb, R,
               lambda i, walk=walk, TM=TM, TN=TN, wsb=wsb, wss=wss: ok(tm.tm_colsum(
                   xs[i], N, outs[i], M, N, TM, TN, walk == tm.TM_COL_LDS and 1 or 0, walk, wss[i], wsb,

@@ -125,6 +125,35 @@ TM_API int tm_colsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t
     return launched(tmk::launch_cols(plan, static_cast<hipStream_t>(stream)));
 }
 
+TM_API int tm_col_walk(const void *x, int64_t ldx, const void *out, int64_t M, int64_t N, int TM, int TN,
+                       int aligned, int walk, const void *ws, size_t ws_bytes, int *form, int64_t *slab_rows,
+                       int64_t *strip_cols, int64_t *slabs, int64_t *strips) {
+    if (form == nullptr || slab_rows == nullptr || strip_cols == nullptr || slabs == nullptr || strips == nullptr)
+        return TM_E_INVAL;
+    tmp::ColPlan plan;
+    const int st = tmp::plan_cols(static_cast<const float *>(x), ldx, static_cast<float *>(const_cast<void *>(out)),
+                                  M, N, TM, TN, aligned, walk, const_cast<void *>(ws), ws_bytes, &plan);
+    if (st != TM_OK)
+        return st;
+    if (!plan.finish) {
+        *form = TM_COLFORM_NONE;
+        *slab_rows = *strip_cols = *slabs = *strips = 0;
+    } else if (plan.direct) {
+        *form = TM_COLFORM_ONE_PASS;
+        *slab_rows = M;
+        *strip_cols = plan.vec ? 4 : 1;
+        *slabs = 1;
+        *strips = (N + *strip_cols - 1) / *strip_cols;
+    } else {
+        *form = plan.strip ? TM_COLFORM_STRIPS : TM_COLFORM_TILES;
+        *slab_rows = plan.launch ? int64_t{1} << plan.log_tm : 0;
+        *strip_cols = plan.walk == TM_COL_LDS ? plan.tw : 1;
+        *slabs = plan.launch ? int64_t(plan.slabs) : 0;
+        *strips = int64_t(plan.strips);
+    }
+    return TM_OK;
+}
+
 TM_API int tm_transpose(const float *x, int64_t ldx, int64_t bsx, float *y, int64_t ldy, int64_t bsy,
                         int64_t B, int64_t M, int64_t N, int TM, int TN, int aligned, void *stream) {
     tmp::TransposePlan plan;

@@ -2,8 +2,9 @@
  * taking device addresses as Python ints (None for NULL), sizes as ints, scalars as floats and the
  * stream as an int (a hipStream_t; 0 is the null stream).  Argument conversion only: each function
  * converts its arguments and calls the C ABI once.  Calls that write through host pointers
- * (tm_split, tm_plan_tiles, tm_map_walk, tm_row_walk, tm_pad_extents, tm_autotune_map) return a tuple that starts with the
- * status instead.  A wrong argument count or type raises TypeError / OverflowError before any call.
+ * (tm_split, tm_plan_tiles, tm_map_walk, tm_row_walk, tm_col_walk, tm_pad_extents, tm_autotune_map)
+ * return a tuple that starts with the status instead.  A wrong argument count or type raises
+ * TypeError / OverflowError before any call.
  *
  * METH_FASTCALL keeps a call near half a microsecond; through ctypes the same call took several,
  * more than a 1M-element map takes on the GPU. */
@@ -316,6 +317,22 @@ static PyObject *py_map_walk(ARGS) {
     return Py_BuildValue("(iiL)", st, walk, (long long)items);
 }
 
+static PyObject *py_col_walk(ARGS) {
+    int64_t ldx, M, N, slab_rows = -1, strip_cols = -1, slabs = -1, strips = -1;
+    int TM, TN, al, walk, form = -1;
+    void *x, *out, *ws;
+    size_t wsb;
+    (void)self;
+    OK(want(n, 11, "tm_col_walk"));
+    OK(as_ptr(a[0], &x) && as_i64(a[1], &ldx) && as_ptr(a[2], &out) && as_i64(a[3], &M) && as_i64(a[4], &N) &&
+       as_int(a[5], &TM) && as_int(a[6], &TN) && as_int(a[7], &al) && as_int(a[8], &walk) && as_ptr(a[9], &ws) &&
+       as_size(a[10], &wsb));
+    const int st = tm_col_walk(x, ldx, out, M, N, TM, TN, al, walk, ws, wsb, &form, &slab_rows, &strip_cols, &slabs,
+                               &strips);
+    return Py_BuildValue("(iiLLLL)", st, form, (long long)slab_rows, (long long)strip_cols, (long long)slabs,
+                         (long long)strips);
+}
+
 static PyObject *py_plan_tiles(ARGS) {
     int64_t M, N, tm_ = -1, tn_ = -1, whole = -1;
     int TM, TN;
@@ -411,6 +428,7 @@ static PyMethodDef methods[] = {
     FAST("tm_map_walk", py_map_walk),
     FAST("tm_colsum_noalloc", py_colsum_noalloc),
     FAST("tm_row_walk", py_row_walk),
+    FAST("tm_col_walk", py_col_walk),
     FAST("tm_pad_extents", py_pad_extents),
     FAST("tm_autotune_map", py_autotune_map),
     FAST("tm_status_string", py_status_string),

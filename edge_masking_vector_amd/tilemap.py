@@ -39,6 +39,11 @@ TM_MAP_FLAT = 1
 TM_MAP_SPAN = 2
 TM_MAP_TILES = 3
 
+TM_COLFORM_NONE = 0
+TM_COLFORM_ONE_PASS = 1
+TM_COLFORM_TILES = 2
+TM_COLFORM_STRIPS = 3
+
 if not os.path.exists(LIB_PATH):
     raise ImportError("libtilemap.so is not built (expected at %s); run "
                       "`python -c 'import __graft_entry__ as g; g.build()'` first" % LIB_PATH)
@@ -180,6 +185,12 @@ def tm_map_walk(op, x, ldx, y, ldy, M, N, TM, TN, aligned, variant=TM_VAR_AUTO, 
     2 copy, 3 channel with the vector bias).  x, y, bias: tensors or addresses (inspected, never
     dereferenced)."""
     return _ext.tm_map_walk(op, _ptr(x), ldx, _ptr(y), ldy, M, N, TM, TN, aligned, variant, _ptr(bias))
+
+
+def tm_col_walk(x, ldx, out, M, N, TM, TN, aligned, walk, ws=None, ws_bytes=0):
+    """Returns (status, form, slab_rows, strip_cols, slabs, strips): the plan tm_colsum would run
+    (form: TM_COLFORM_*).  x, out, ws: tensors or addresses (inspected, never dereferenced)."""
+    return _ext.tm_col_walk(_ptr(x), ldx, _ptr(out), M, N, TM, TN, aligned, walk, _ptr(ws), ws_bytes)
 
 
 def tm_pad_extents(M, N, TM, TN):

@@ -114,6 +114,19 @@ typedef enum {
     TM_MAP_TILES = 3  /* the 2-D tile schedule: whole tiles unmasked, edge tiles masked */
 } tm_mapwalk;
 
+/* How tm_colsum cuts a call into work (reported by tm_col_walk). */
+typedef enum {
+    TM_COLFORM_NONE = 0,      /* nothing to launch (N is 0) */
+    TM_COLFORM_ONE_PASS = 1,  /* the LDS walk over few rows: each thread adds one chunk of columns
+                                 down all M rows and writes the sums; no partials */
+    TM_COLFORM_TILES = 2,     /* two passes: one workgroup per (row slab, column strip) writes a
+                                 partial per column, then a fixed-order sum of each column's
+                                 partials (the naive walks: strips of one column) */
+    TM_COLFORM_STRIPS = 3     /* two passes, the LDS walk over wide matrices: one workgroup per
+                                 (row slab, strip of 1024 columns), one 16-byte column chunk per
+                                 thread, then the same fixed-order sum */
+} tm_colform;
+
 /* ---- element-wise maps over tiles --------------------------------------------------------------
  * x: input, M x N, row stride ldx.  y: output, M x N, row stride ldy.  TM, TN: tile.  aligned: 0|1.
  * variant: tm_variant.  The tile is what the alignment promise is made for.  How the work is cut
@@ -320,6 +333,21 @@ int tm_row_walk(int64_t M, int64_t N, int64_t ld, int BR, int BC, int aligned, c
  * are written only on TM_OK. */
 int tm_map_walk(int op, const void *x, int64_t ldx, const void *y, int64_t ldy, int64_t M, int64_t N,
                 int TM, int TN, int aligned, int variant, const void *bias, int *walk, int64_t *items);
+
+/* The plan tm_colsum would run for these arguments, as a pure host function ([LAYOUT] "What it
+ * actually costs": the column walk; "Seeing it in a real kernel": the staged walk): *form
+ * (tm_colform), *slab_rows (rows each work item adds down its columns: M for the one-pass form),
+ * *strip_cols (columns per work item: 1 for the naive walks, the chunk width of a thread for the
+ * one-pass form), *slabs and *strips (work items down and across; *slabs is the number of
+ * partials per column of the two-pass forms, 0 when M is 0).  x, out and ws are only inspected,
+ * never dereferenced (the strip form needs a 16-byte aligned ws).  Returns what tm_colsum would
+ * return before launching (TM_E_INVAL, TM_E_ALIGN, TM_E_UNSUPPORTED, TM_E_WORKSPACE), or
+ * TM_E_INVAL if an output pointer is NULL; the outputs are written only on TM_OK.  4096 x 4096
+ * with the LDS walk and a 16-byte aligned workspace: TM_COLFORM_STRIPS, 64-row slabs by
+ * 1024-column strips, 64 x 4. */
+int tm_col_walk(const void *x, int64_t ldx, const void *out, int64_t M, int64_t N, int TM, int TN,
+                int aligned, int walk, const void *ws, size_t ws_bytes, int *form, int64_t *slab_rows,
+                int64_t *strip_cols, int64_t *slabs, int64_t *strips);
 
 /* Tile scheduler counts ([SLICING] "Masking"): *tiles_m = ceil(M / TM), *tiles_n = ceil(N / TN) and
  * *whole = the number of tiles lying entirely inside the M x N tensor; the other tiles are edge

@@ -157,6 +157,66 @@ def test_row_walk_errors():
     assert tm.tm_row_walk(0, 10, 10, 1, 64, 0, None)[0] == tm.TM_OK
 
 
+# ---- the column sums' plan (tm_col_walk) ---------------------------------------------------------
+def test_col_walk_reports_the_walks_the_column_sums_run():
+    """teenygrad 'What it actually costs' walks 4096 x 4096 column by column (the naive walk: one
+    column per workgroup, slabs of the caller's TM rows) and 'Seeing it in a real kernel' stages the
+    reads so that they stay coalesced (the LDS walk, whose slabs and strips are its own)."""
+    M = N = 4096
+    wsb = tm.tm_colsum_workspace_bytes(M, N, 256, 64, tm.TM_COL_LDS)
+    # wide matrix, 16-byte aligned workspace: the strip form, 64-row slabs by 1024-column strips
+    assert tm.tm_col_walk(LINE, N, LINE, M, N, 256, 64, 1, tm.TM_COL_LDS, LINE, wsb) == \
+        (tm.TM_OK, tm.TM_COLFORM_STRIPS, 64, 1024, 64, 4)
+    # a workspace off the 16-byte grid: the LDS-staged slabs by 128-column strips instead
+    st, form, srows, scols, slabs, strips = tm.tm_col_walk(LINE, N, LINE, M, N, 256, 64, 1, tm.TM_COL_LDS,
+                                                           LINE + 4, wsb)
+    assert (st, form, scols, strips) == (tm.TM_OK, tm.TM_COLFORM_TILES, 128, 32)
+    assert slabs * srows >= M > (slabs - 1) * srows and slabs * N * 4 <= wsb
+    # the naive walks: the caller's TM rows per slab, one column per workgroup
+    for walk in (tm.TM_COL_NAIVE, tm.TM_COL_NAIVE_XCD):
+        wsn = tm.tm_colsum_workspace_bytes(M, N, 256, 1, walk)
+        assert tm.tm_col_walk(LINE, N, LINE, M, N, 256, 1, 0, walk, LINE, wsn) == \
+            (tm.TM_OK, tm.TM_COLFORM_TILES, 256, 1, 16, N)
+        assert wsn == 16 * N * 4
+    # few rows: one pass, 16-byte column chunks down all rows, no workspace
+    assert tm.tm_colsum_workspace_bytes(16, 1 << 20, 16, 64, tm.TM_COL_LDS) == 0
+    assert tm.tm_col_walk(LINE, 1 << 20, LINE, 16, 1 << 20, 16, 64, 1, tm.TM_COL_LDS, None, 0) == \
+        (tm.TM_OK, tm.TM_COLFORM_ONE_PASS, 16, 4, 1, 1 << 18)
+    # nothing to launch without columns; only the zero-writing pass without rows
+    assert tm.tm_col_walk(LINE, 10, LINE, 10, 0, 1, 1, 0, tm.TM_COL_LDS, None, 0)[:2] == (tm.TM_OK, tm.TM_COLFORM_NONE)
+    assert tm.tm_col_walk(None, 10, LINE, 0, 10, 1, 1, 0, tm.TM_COL_LDS, None, 0)[:2] == (tm.TM_OK, tm.TM_COLFORM_TILES)
+
+
+def test_col_walk_partials_fit_the_workspace():
+    """Every two-pass plan's partials (slabs per column x N floats) fit the size
+    tm_colsum_workspace_bytes reports, for any workspace alignment."""
+    for M in (1, 63, 64, 300, 4096, 70000):
+        for N in (1, 5, 127, 1024, 3000, 4096):
+            for walk, TM, TN in ((tm.TM_COL_LDS, 64, 64), (tm.TM_COL_NAIVE, 256, 1), (tm.TM_COL_NAIVE_XCD, 64, 1)):
+                wsb = tm.tm_colsum_workspace_bytes(M, N, TM, TN, walk)
+                for ws in (LINE, LINE + 4):
+                    st, form, srows, scols, slabs, strips = tm.tm_col_walk(LINE, N, LINE, M, N, TM, TN, 0, walk,
+                                                                           ws if wsb else None, wsb)
+                    assert st == tm.TM_OK, (M, N, walk, ws)
+                    if form == tm.TM_COLFORM_ONE_PASS:
+                        assert wsb == 0 and srows == M
+                        continue
+                    assert form in (tm.TM_COLFORM_TILES, tm.TM_COLFORM_STRIPS)
+                    assert slabs * N * 4 <= wsb, (M, N, walk, ws, slabs, wsb)
+                    assert slabs * srows >= M > (slabs - 1) * srows and strips * scols >= N > (strips - 1) * scols
+                    assert form != tm.TM_COLFORM_STRIPS or (ws % 16 == 0 and scols == 1024)
+
+
+@no_gpu
+def test_col_walk_errors():
+    wsb = tm.tm_colsum_workspace_bytes(100, 100, 64, 64, tm.TM_COL_LDS)
+    assert tm.tm_col_walk(A16, 100, B16, 100, 100, 64, 64, 0, 7, A16, wsb)[0] == tm.TM_E_INVAL       # walk
+    assert tm.tm_col_walk(A16, 100, B16, 100, 100, 64, 64, 1, tm.TM_COL_LDS, A16, wsb)[0] == tm.TM_E_ALIGN
+    assert tm.tm_col_walk(A16, 100, B16, 100, 100, 64, 64, 0, tm.TM_COL_LDS, A16, wsb - 4)[0] == tm.TM_E_WORKSPACE
+    assert tm.tm_col_walk(A16, 100, None, 100, 100, 64, 64, 0, tm.TM_COL_LDS, A16, wsb)[0] == tm.TM_E_INVAL
+    assert tm.tm_col_walk(A16, 99, B16, 100, 100, 64, 64, 0, tm.TM_COL_LDS, A16, wsb)[0] == tm.TM_E_INVAL  # ld < N
+
+
 # ---- the maps' plan (tm_map_walk) ----------------------------------------------------------------
 
 X0, Y0 = LINE, LINE + (1 << 30)   # two line-aligned bases (inspected only)
