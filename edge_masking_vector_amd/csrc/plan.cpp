@@ -525,9 +525,14 @@ static RowWalk row_walk(int64_t M, int64_t N, bool vec, int TC, bool once_ok = t
     // walk below, on 8192 x 1000 masked maxima (1 GiB of rotating inputs, one process): 6.6-6.8 us
     // with 16, 32 or 64 lanes per row against 7.3-7.4 us.  Rows of more than half the batch's
     // lanes' reach with too few rows to fill the GPU keep the multi-wave walk.
+    // 16-byte rows of up to kRowOnceMaxLanes * K chunks take 128 or 256 lanes per row, one row
+    // per workgroup (4096 x 4096 sums, probe kernels of this shape, 1 GiB of rotating inputs: 128
+    // or 256 lanes with 8 or 4 chunks each 11.2-11.3 us, where the batched walk below took 11.9;
+    // one wave per row with 16 chunks per lane 12.5).
     const int K = vec ? kRowOnceK : kRowOnceKScalar;
     const bool few_long = chunks > int64_t{K} * 32 && M < kRowWideWaves;
-    if (once_ok && chunks > int64_t{K} * kRowOnceMinLanes / 2 && chunks <= int64_t{K} * 64 && !few_long) {
+    const int max_lanes = vec ? kRowOnceMaxLanes : 64;
+    if (once_ok && chunks > int64_t{K} * kRowOnceMinLanes / 2 && chunks <= int64_t{K} * max_lanes && !few_long) {
         rw.once = true;
         rw.once_k = K;
         rw.lpr = std::max(kRowOnceMinLanes, 1 << ilog2(ceil_div(chunks, K)));
@@ -655,9 +660,7 @@ int plan_rows(int op, const float *x, int64_t ld, float *out, int64_t M, int64_t
     // row does not touch), its first one to three elements masked, the walk laid out for N + 3
     // elements.  133 x 64954 at row stride 64986 read as 4-byte chunks streamed 2.8 TB/s.
     const bool shift = !vec && N > kRowShiftMinN;
-    // (The one-batch kernel has no shifted form: such rows keep the batched walk.  One wave per
-    // 4096-float row with all 16 of its lanes' chunks in flight took the 4096 x 4096 row sums from
-    // 12.0 to 12.6 us, so rows past 512 16-byte chunks keep the batched walk too.)
+    // (The one-batch kernel has no shifted form: such rows keep the batched walk.)
     const RowWalk rw = shift ? row_walk(M, N + 3, true, TC, false) : row_walk(M, N, vec, TC);
     const int lpr = rw.lpr;
     plan->launch = true;

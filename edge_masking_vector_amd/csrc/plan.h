@@ -64,6 +64,9 @@ constexpr int64_t kRowTileMaxChunks = 4;
 constexpr int kRowOnceK = 8;
 constexpr int kRowOnceKScalar = 16;
 constexpr int kRowOnceMinLanes = 16;
+// 16-byte rows take up to this many lanes per row in one batch (past 64: one row per workgroup of
+// that many threads, its waves combined through LDS); 4-byte rows at most one wave.
+constexpr int kRowOnceMaxLanes = 256;
 // Rows off the 16-byte grid of more than this many elements are read as 16-byte chunks from the
 // 16-byte boundary at or before each row's start.
 constexpr int64_t kRowShiftMinN = 2048;

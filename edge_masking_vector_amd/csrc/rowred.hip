@@ -312,9 +312,10 @@ __device__ __forceinline__ float sum_exp_live(f4 v, float b, int64_t live) {
 }
 
 // ---- rows read in one batch ---------------------------------------------------------------------
-// Rows of a few hundred chunks: LPR lanes per row (16, 32 or 64; kBlock / LPR rows per workgroup)
-// and K chunks per lane cover the row, lane g taking chunks g, g + LPR, ..., so a row costs one
-// memory round trip.  The loads carry no control flow: every one is issued before any wait (a
+// Rows of a few hundred to a few thousand chunks: LPR lanes per row (16 to 64: kBlock / LPR rows per
+// workgroup; 128 or 256: one row per workgroup of LPR threads, whose waves then meet in LDS in
+// order) and K chunks per lane cover the row, lane g taking chunks g, g + LPR, ..., so a row costs
+// one memory round trip.  The loads carry no control flow: every one is issued before any wait (a
 // branch around each load had the compiler wait for each before the next, 8 round trips instead
 // of 1: 7.9 against 6.9 us on 8192 x 1000).  A slot past the row loads the row's last chunk again
 // and is then replaced by the fill.  The caller's column tile decides the masks ([SLICING] "Loops
@@ -336,14 +337,15 @@ struct OnceArgs {
 
 // OPK: tmp::kRowSum, kRowMax or kRowSoftmax.
 template <int OPK, int LPR, int K, bool VEC, bool PART>
-__global__ __launch_bounds__(kBlock) void row_once(OnceArgs a) {
+__global__ __launch_bounds__(block_threads<LPR>()) void row_once(OnceArgs a) {
     using T = typename std::conditional<VEC, f4, float>::type;
     using Op = typename std::conditional<OPK == tmp::kRowSum, SumOp, MaxOp>::type;
     constexpr int W = VEC ? 4 : 1;
     static_assert(VEC || !PART, "4-byte chunks never straddle the row's end");
+    __shared__ float wv[LPR > 64 ? LPR / 64 : 1];  // LPR > 64: the row's wave values
     const int t = threadIdx.x;
     const int g = t % LPR;
-    const int64_t row = int64_t(blockIdx.x) * (kBlock / LPR) + t / LPR;
+    const int64_t row = int64_t(blockIdx.x) * (block_threads<LPR>() / LPR) + t / LPR;
     const int64_t rr = row < a.M ? row : a.M - 1;  // rows past M re-read row M-1, never stored
     const float *xr = a.x + rr * a.ld;
 
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(kBlock) void row_once(OnceArgs a) {
 #pragma unroll
             for (int i = 0; i + st < K; i += 2 * st)
                 v[i] = combine<Op>(v[i], v[i + st]);
-        const float r = group_reduce<Op, LPR>(lanes<Op>(v[0]));
+        const float r = row_combine<Op, LPR>(lanes<Op>(v[0]), wv);
         if (g == 0 && row < a.M)
             a.out[row] = r;
     } else {
@@ -415,8 +417,8 @@ __global__ __launch_bounds__(kBlock) void row_once(OnceArgs a) {
                 l += live(c, 0) ? exp_f32(v[k] - m) : 0.0f;
             }
         }
-        const float gm = group_reduce<MaxOp, LPR>(m);
-        const float gl = group_reduce<SumOp, LPR>(l * exp_f32(m - gm));
+        const float gm = row_combine<MaxOp, LPR>(m, wv);
+        const float gl = row_combine<SumOp, LPR>(l * exp_f32(m - gm), wv);
         if (g == 0 && row < a.M) {
             a.out[row] = gm;
             a.out2[row] = gl;
@@ -765,8 +767,13 @@ const void *pick_once_lpr(int lpr) {
     switch (lpr) {
     case 16: return reinterpret_cast<const void *>(&row_once<OPK, 16, K, VEC, PART>);
     case 32: return reinterpret_cast<const void *>(&row_once<OPK, 32, K, VEC, PART>);
-    default: return reinterpret_cast<const void *>(&row_once<OPK, 64, K, VEC, PART>);
+    case 64: return reinterpret_cast<const void *>(&row_once<OPK, 64, K, VEC, PART>);
+    default: break;
     }
+    if constexpr (VEC)  // 4-byte rows are planned with at most 64 lanes
+        return lpr == 128 ? reinterpret_cast<const void *>(&row_once<OPK, 128, K, VEC, PART>)
+                          : reinterpret_cast<const void *>(&row_once<OPK, 256, K, VEC, PART>);
+    return nullptr;
 }
 
 template <int OPK>
@@ -791,8 +798,10 @@ hipError_t launch_once(const tmp::RowPlan &p, hipStream_t stream) {
     const void *fn = p.op == tmp::kRowMax       ? pick_once<tmp::kRowMax>(p)
                      : p.op == tmp::kRowSoftmax ? pick_once<tmp::kRowSoftmax>(p)
                                                 : pick_once<tmp::kRowSum>(p);
+    if (fn == nullptr)
+        return hipErrorInvalidConfiguration;
     void *args[] = {&a};
-    return hipLaunchKernel(fn, dim3(p.grid), dim3(kBlock), args, 0, stream);
+    return hipLaunchKernel(fn, dim3(p.grid), dim3(p.block), args, 0, stream);
 }
 
 }  // namespace

@@ -821,7 +821,8 @@ static void check_reductions() {
                                 // must lie inside the row; every chunk of the row is taken once
                                 const int W = p.vec ? 4 : 1;
                                 const int64_t chunks = (N + W - 1) / W;
-                                CHECK(p.bc == std::max(TC, W) && p.lpr >= tmp::kRowOnceMinLanes && p.lpr <= 64 &&
+                                CHECK(p.bc == std::max(TC, W) && p.lpr >= tmp::kRowOnceMinLanes &&
+                                          p.lpr <= (p.vec ? tmp::kRowOnceMaxLanes : 64) &&
                                           int64_t(p.lpr) * p.once_k >= chunks,
                                       "rows once bc %d lpr %d k %d N %ld", p.bc, p.lpr, p.once_k, long(N));
                                 const int64_t whole = p.nfull * (p.bc / W);

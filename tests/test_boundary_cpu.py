@@ -134,8 +134,9 @@ def test_row_walk_split_is_the_remainder_rule():
                     assert (nf, rem) == oracle.split(N, bc), (M, N, ld, BC)
                     chunks = -(-N // W)
                     K = 8 if W == 4 else 16
-                    if 8 * K < chunks <= 64 * K and not (chunks > 32 * K and M < 2048):
-                        # one batch: at least 16 lanes cover the row, and the tile is the caller's
+                    if 8 * K < chunks <= (256 if W == 4 else 64) * K and not (chunks > 32 * K and M < 2048):
+                        # one batch: at least 16 lanes cover the row (up to 256 lanes for 16-byte
+                        # chunks, 64 for 4-byte ones), and the tile is the caller's
                         assert lanes >= 16 and lanes * K >= chunks and bc == max(BC, W), (M, N, ld, BC)
                         continue
                     Wt = 4 if shifted else W
