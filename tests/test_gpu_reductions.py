@@ -518,3 +518,37 @@ def test_rows_off_the_grid_shifted_walk(dev, M, N, ld, off):
     assert st == tm.TM_OK
     torch.cuda.synchronize()
     check_softmax(Mo, Lo, host, ld, M, N)
+
+
+@pytest.mark.parametrize("N", [2052, 3001, 4093, 4096, 8189, 8192])
+def test_rows_in_one_batch_over_several_waves(dev, N):
+    """Rows of 513 to 2048 16-byte chunks are read in one batch by 128 or 256 lanes per row, one
+    row per workgroup, the row's waves combined in LDS in order.  Ragged N (the last chunk read
+    through a buffer resource that ends at the row's end), rows off a multiple of the workgroup's
+    rows (M = 2049), a padded stride, the caller's 64- and 1024-column tiles (whole tiles plus one
+    masked remainder, [SLICING] "Reductions over a ragged tile"); sums within 1e-5 of fp64, maxima
+    and softmax m bit-exact, l within 1e-5."""
+    for M, ld in ((2048, 4 * ((N + 3) // 4)), (2049, 4 * ((N + 3) // 4) + 4)):
+        xh = inputs.uniform(7 * N + M, M * N, -10.0, -1.0)
+        X, host = device_matrix(xh, M, N, ld, dev)
+        ref = oracle.rowsum_f64(host, ld, M, N)
+        absref = oracle.rowsum_f64(np.abs(host), ld, M, N)
+        mref = oracle.rowmax(host, ld, M, N)
+        for BC in (64, 1024):
+            st, bc, nfull, rem, lanes = tm.tm_row_walk(M, N, ld, 1, BC, 0, X.ptr)
+            assert st == tm.TM_OK and lanes in (128, 256) and (bc, nfull, rem) == (BC, *oracle.split(N, BC))
+            note("one-batch rows %dx%d ld=%d BC=%d lanes=%d" % (M, N, ld, BC, lanes))
+            st, O = gpu_rowsum(X, ld, M, N, 1, BC, 0, dev)
+            assert st == tm.TM_OK
+            torch.cuda.synchronize()
+            assert_sums(O.payload().cpu().numpy(), ref, absref)
+            assert O.guards_intact()
+            st, O = gpu_rowmax(X, ld, M, N, 1, BC, 0, dev)
+            assert st == tm.TM_OK
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(O.payload()), bits(mref))
+            assert O.guards_intact()
+            st, Mo, Lo = gpu_softmax(X, ld, M, N, 1, BC, 0, dev)
+            assert st == tm.TM_OK
+            torch.cuda.synchronize()
+            check_softmax(Mo, Lo, host, ld, M, N)
