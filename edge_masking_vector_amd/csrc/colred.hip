@@ -181,30 +181,36 @@ __global__ __launch_bounds__(kBlock) void col_lds(ColArgs a) {
 }
 
 // ---- strip walk (wide matrices) -------------------------------------------------------------------
-// A workgroup takes (slab, strip): tm rows by tmp::kColRowStrip columns, strip fastest, so the
-// workgroups running together read whole rows.  Thread t owns 16-byte column chunk t of the strip
-// and adds the slab's rows down it, 16 loads in flight into 4 accumulators, folded in a fixed order;
-// its four column sums are the slab's partial for those columns, stored as one 16-byte vector at
-// ws[slab * N + column] (the workspace is 16-byte aligned and N % 4 == 0).  The loads carry no
-// control flow: a row past M re-reads row M - 1 and a chunk past N re-reads the row's last chunk,
-// and both are then replaced by 0 ([SLICING] "Masking": out-of-range elements read as 0).
-// WHOLE: the host found whole slabs and strips, so there is nothing to replace.  U: rows off the
-// 16-byte grid (N a whole number of strips): chunks are 16-byte loads from 4-byte aligned
-// addresses, which the GPU's unaligned access mode executes as one load.
-constexpr int kStripBatch = 16;
+// A workgroup takes (slab, strip): tm rows by tmp::kColStripCols columns, strip fastest, so the
+// workgroups running together read whole rows.  Lane t of each of its kColStripGroups waves owns
+// 16-byte column chunk t of the strip; wave q adds rows [q tm / G, (q + 1) tm / G) of the slab
+// down it, kStripBatch loads in flight into 4 accumulators folded in a fixed order, and the waves'
+// sums meet in LDS in wave order: the slab's partial for the lane's four columns, stored as one
+// 16-byte vector at ws[slab * N + column] (the workspace is 16-byte aligned and N % 4 == 0).  The
+// loads carry no control flow: a row past M re-reads row M - 1 and a chunk past N re-reads the
+// row's last chunk, and both are then replaced by 0 ([SLICING] "Masking": out-of-range elements
+// read as 0).  WHOLE: the host found whole slabs and strips, so there is nothing to replace.  U:
+// rows off the 16-byte grid (N a whole number of strips): chunks are 16-byte loads from 4-byte
+// aligned addresses, which the GPU's unaligned access mode executes as one load.
+constexpr int kStripBatch = 8;
+constexpr int kStripGroups = tmp::kColStripGroups;
+constexpr int kStripThreads = 64 * kStripGroups;
+static_assert(tmp::kColStripCols == 64 * 4, "a strip is one 16-byte chunk per lane of a wave");
+static_assert(tmp::kColRowSlab % (kStripGroups * kStripBatch) == 0, "whole batches per row group");
 
 template <bool WHOLE, bool U>
-__global__ __launch_bounds__(kBlock) void col_strip(ColArgs a) {
-    const int t = threadIdx.x;
+__global__ __launch_bounds__(kStripThreads) void col_strip(ColArgs a) {
+    __shared__ f4 part[kStripGroups][64];
+    const int t = threadIdx.x % 64, q = threadIdx.x / 64;
     const uint32_t strip = blockIdx.x % a.strips, slab = blockIdx.x / a.strips;
     const int64_t nch = a.N / 4;                          // 16-byte chunks per row
-    const int64_t ch = int64_t(strip) * kBlock + t;       // this thread's column chunk
+    const int64_t ch = int64_t(strip) * 64 + t;           // this lane's column chunk
     const int64_t chc = ch < nch ? ch : nch - 1;
-    const int64_t tm = int64_t(1) << a.log_tm;
-    const int64_t row0 = int64_t(slab) * tm;
+    const int64_t rg = (int64_t(1) << a.log_tm) / kStripGroups;  // rows per wave (tm >= 64)
+    const int64_t row0 = (int64_t(slab) << a.log_tm) + q * rg;
     const float *p = a.x + chc * 4;
     f4 acc[4] = {f4(0.0f), f4(0.0f), f4(0.0f), f4(0.0f)};
-    for (int64_t r0 = 0; r0 < tm; r0 += kStripBatch) {
+    for (int64_t r0 = 0; r0 < rg; r0 += kStripBatch) {
         f4 v[kStripBatch];
 #pragma unroll
         for (int u = 0; u < kStripBatch; ++u) {
@@ -219,9 +225,15 @@ __global__ __launch_bounds__(kBlock) void col_strip(ColArgs a) {
             acc[u % 4] += v[u];
         }
     }
-    const f4 s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    if (WHOLE || ch < nch)
+    part[q][t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    __syncthreads();
+    if (q == 0 && (WHOLE || ch < nch)) {
+        f4 s = part[0][t];
+#pragma unroll
+        for (int k = 1; k < kStripGroups; ++k)
+            s += part[k][t];
         *reinterpret_cast<f4 *>(a.ws + int64_t(slab) * a.N + ch * 4) = s;
+    }
 }
 
 // Pass 2 after the strip walk: workgroup b takes 16-byte column chunks 64 b .. 64 b + 63; wave w of
@@ -230,6 +242,7 @@ __global__ __launch_bounds__(kBlock) void col_strip(ColArgs a) {
 // in LDS in wave order.  Fixed order throughout: the result is deterministic.  out need only be
 // 4-byte aligned: its 16-byte stores go to 4-byte aligned addresses.
 constexpr int kFold = 4;  // waves per workgroup
+constexpr int kFoldBatch = 16;  // partials in flight per lane
 
 __global__ __launch_bounds__(kFold * 64) void colsum_fold16(const float *ws, float *out, int64_t N,
                                                               uint32_t slabs) {
@@ -242,15 +255,15 @@ __global__ __launch_bounds__(kFold * 64) void colsum_fold16(const float *ws, flo
     const uint32_t s_end = uint32_t(uint64_t(slabs) * (w + 1) / kFold);
     const f4 *p = reinterpret_cast<const f4 *>(ws) + chc;
     f4 acc = f4(0.0f);
-    for (uint32_t s0 = s_begin; s0 < s_end; s0 += kStripBatch) {
-        f4 v[kStripBatch];
+    for (uint32_t s0 = s_begin; s0 < s_end; s0 += kFoldBatch) {
+        f4 v[kFoldBatch];
 #pragma unroll
-        for (int u = 0; u < kStripBatch; ++u) {
+        for (int u = 0; u < kFoldBatch; ++u) {
             const uint32_t s = s0 + u < s_end ? s0 + u : s_end - 1;
             v[u] = p[int64_t(s) * nch];
         }
 #pragma unroll
-        for (int u = 0; u < kStripBatch; ++u)
+        for (int u = 0; u < kFoldBatch; ++u)
             acc += s0 + u < s_end ? v[u] : f4(0.0f);
     }
     wsum[w][lane] = acc;
@@ -438,7 +451,7 @@ hipError_t launch_cols(const tmp::ColPlan &p, hipStream_t stream) {
                                           : reinterpret_cast<const void *>(&col_strip<false, false>))
                                : (p.whole ? reinterpret_cast<const void *>(&col_strip<true, true>)
                                           : reinterpret_cast<const void *>(&col_strip<false, true>));
-        hipError_t err = hipLaunchKernel(fn, dim3(p.slabs * p.strips), dim3(kBlock), args, 0, stream);
+        hipError_t err = hipLaunchKernel(fn, dim3(p.slabs * p.strips), dim3(kStripThreads), args, 0, stream);
         if (err != hipSuccess)
             return err;
         const float *ws = p.ws;

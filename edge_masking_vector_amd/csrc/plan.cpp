@@ -837,12 +837,15 @@ int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int 
     plan->walk = walk;
     plan->log_tm = log_ts;
     plan->slabs = static_cast<uint32_t>(slabs);
-    // Wide matrices with 16-byte rows and a 16-byte aligned workspace: the strip kernel.  Each
-    // thread owns one 16-byte column chunk of a kColRowStrip-column strip and adds kColRowSlab
-    // rows down it, 16 loads in flight; each row of a strip is one 4 KiB run of memory, and no
-    // partial has to meet another thread's.  On 4096 x 4096 (1 GiB of rotating inputs) pass 1
-    // took 12.2 us against 13.8 us for the LDS-staged kernel's 128 x 128 tiles, whose 1024
-    // workgroups all issue their loads in one round and then fold through LDS together.
+    // Wide matrices (at least kColRowStrip columns) with 16-byte rows and a 16-byte aligned
+    // workspace: the strip kernel.  A workgroup takes one slab of a kColStripCols-column strip:
+    // lane t of each of its kColStripGroups waves owns 16-byte column chunk t of the strip (each
+    // row of the strip one 1 KiB run of memory), wave q adds its eighth of the slab's rows, 8
+    // loads in flight, and the waves' sums meet in LDS in order.  On 4096 x 4096 (1 GiB of
+    // rotating inputs) both passes took 14.3 us against 16.1 us when each thread of 256 walked
+    // all 64 rows of a 1024-column strip 16 loads at a time (pass 1 alone 11.8 against 12.3 us;
+    // the second launch then also started sooner), and 13.8 us was the LDS-staged kernel's
+    // 128 x 128 tiles' pass 1 alone.
     // Rows off the 16-byte grid take the same walk with 4-byte aligned 16-byte loads (vec =
     // false: col_strip<..., U>) when N is a whole number of strips: 4096 x 4096 at row stride 4097
     // 17.9 -> 15.6 us against the LDS-staged kernel's 4-byte loads, with the base one float off
@@ -851,15 +854,18 @@ int plan_cols(const float *x, int64_t ld, float *out, int64_t M, int64_t N, int 
     // against 20.1, 4096 x 4100 at 4103 19.0 against 20.3).
     const int lstrip = strip_slab_log(M, N, walk);
     const bool x16 = rows16(x, M, ld);
-    if (lstrip > 0 && aligned_to(ws, 16) && (x16 || N % kColRowStrip == 0)) {
-        const int64_t sslabs = ceil_div(M, int64_t{1} << lstrip);
+    const int64_t sslabs = lstrip > 0 ? ceil_div(M, int64_t{1} << lstrip) : 0;
+    // (the grid's thread count, slabs x strips x workgroup threads, must fit 32 bits)
+    const bool strip_grid = uint64_t(sslabs) * uint64_t(ceil_div(N, kColStripCols)) * (64u * kColStripGroups) <
+                            (uint64_t{1} << 32);
+    if (lstrip > 0 && strip_grid && aligned_to(ws, 16) && (x16 || N % kColRowStrip == 0)) {
         plan->strip = true;
         plan->vec = x16;
         plan->log_tm = lstrip;
         plan->slabs = static_cast<uint32_t>(sslabs);
-        plan->tw = kColRowStrip;
-        plan->strips = static_cast<uint32_t>(ceil_div(N, kColRowStrip));
-        plan->whole = M % (int64_t{1} << lstrip) == 0 && N % kColRowStrip == 0;
+        plan->tw = kColStripCols;
+        plan->strips = static_cast<uint32_t>(ceil_div(N, kColStripCols));
+        plan->whole = M % (int64_t{1} << lstrip) == 0 && N % kColStripCols == 0;
         plan->x = x;
         plan->out = out;
         plan->ws = static_cast<float *>(ws);

@@ -93,6 +93,11 @@ constexpr int64_t kColTargetWork = 1024;  // LDS walk: fewer (slab, strip) workg
 // kColRowMaxSlabs), when that makes at least kColRowMinWork workgroups.
 constexpr int kColRowStrip = 1024;
 constexpr int kColRowSlab = 64;
+// The strip kernel itself: a workgroup of kColStripGroups x 64 threads takes a strip of
+// kColStripCols columns (one 16-byte chunk per lane of a wave) of one slab, its row groups each
+// adding an eighth of the slab's rows, folded through LDS.
+constexpr int kColStripCols = 256;
+constexpr int kColStripGroups = 8;
 constexpr int64_t kColRowMaxSlabs = 256;
 constexpr int64_t kColRowMinWork = 256;
 // Column-sum pass 2: lanes per column chosen so that about this many threads run (one wave per
@@ -243,7 +248,8 @@ struct ColPlan {
     bool direct = false;          // LDS walk over few rows or many columns: one pass, no partials
     bool out16 = false;           // direct walk: out is 16-byte aligned
     // LDS walk over wide matrices (col_strip + colsum_fold16): a workgroup per (slab, strip of
-    // kColRowStrip columns), each thread one 16-byte column chunk; partials as 16-byte vectors.
+    // kColStripCols columns), each lane one 16-byte column chunk, kColStripGroups row groups;
+    // partials as 16-byte vectors.
     bool strip = false;
     int fl = 1;                   // pass 2: lanes per column (power of two <= kFinishMaxLanes)
     int naive_block = 64;         // threads per workgroup (naive walk)

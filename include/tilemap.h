@@ -123,8 +123,9 @@ typedef enum {
                                  partial per column, then a fixed-order sum of each column's
                                  partials (the naive walks: strips of one column) */
     TM_COLFORM_STRIPS = 3     /* two passes, the LDS walk over wide matrices: one workgroup per
-                                 (row slab, strip of 1024 columns), one 16-byte column chunk per
-                                 thread, then the same fixed-order sum */
+                                 (row slab, strip of 256 columns), one 16-byte column chunk per
+                                 lane of each of its 8 waves, which add an eighth of the slab's
+                                 rows each, then the same fixed-order sum */
 } tm_colform;
 
 /* ---- element-wise maps over tiles --------------------------------------------------------------
@@ -184,7 +185,7 @@ int tm_rowsum(const float *x, int64_t ldx, float *out, int64_t M, int64_t N,
  * there would be more than 4096 slabs; shorter, halving, while there would be fewer than 1024
  * slabs x column strips of up to 128 columns, down to 32 rows, or 4096 / strip width rows for
  * narrower strips).  Wide matrices (N >= 1024, N % 4 == 0) may take the LDS walk's strip form, with
- * slabs of 64 rows (doubling while there would be more than 256) by 1024-column strips, when that
+ * slabs of 64 rows (doubling while there would be more than 256) by 256-column strips, when that
  * makes at least 256 workgroups; the size then covers the larger of the two slab counts, since the
  * workspace's alignment (16 bytes for the strip form) is not known here.  0 when the LDS walk takes
  * its one-pass form (at most 64 rows, or at most 256 rows of at least 262144 columns: each thread
@@ -344,7 +345,7 @@ int tm_map_walk(int op, const void *x, int64_t ldx, const void *y, int64_t ldy, 
  * return before launching (TM_E_INVAL, TM_E_ALIGN, TM_E_UNSUPPORTED, TM_E_WORKSPACE), or
  * TM_E_INVAL if an output pointer is NULL; the outputs are written only on TM_OK.  4096 x 4096
  * with the LDS walk and a 16-byte aligned workspace: TM_COLFORM_STRIPS, 64-row slabs by
- * 1024-column strips, 64 x 4. */
+ * 256-column strips, 64 x 16. */
 int tm_col_walk(const void *x, int64_t ldx, const void *out, int64_t M, int64_t N, int TM, int TN,
                 int aligned, int walk, const void *ws, size_t ws_bytes, int *form, int64_t *slab_rows,
                 int64_t *strip_cols, int64_t *slabs, int64_t *strips);

@@ -871,8 +871,8 @@ static void check_reductions() {
                                 CHECK(!c.launch && wsb == 0 && c.vec && c.out16,
                                       "cols direct plan M=%ld N=%ld", long(M), long(N));
                             if (c.strip) {
-                                // strip walk: workgroup (slab, strip), thread t of 256 owns column chunk
-                                // strip * 256 + t; its partial lands at ws[slab * N + 4 * chunk]; every
+                                // strip walk: workgroup (slab, strip), lane t of each wave owns column
+                                // chunk strip * 64 + t; its partial lands at ws[slab * N + 4 * chunk]; every
                                 // (slab, column) partial is written exactly once, rows read stay < M;
                                 // rows off the 16-byte grid only with whole strips (no partial chunk)
                                 const int64_t ts = int64_t{1} << c.log_tm, nch = N / 4;
@@ -880,15 +880,17 @@ static void check_reductions() {
                                 CHECK(walk == TM_COL_LDS && c.vec == x16 && N % 4 == 0 &&
                                           (x16 || N % tmp::kColRowStrip == 0) && ts >= tmp::kColRowSlab &&
                                           c.slabs == uint32_t((M + ts - 1) / ts) &&
-                                          uint64_t(c.strips) * tmp::kColRowStrip >= uint64_t(N) &&
+                                          uint64_t(c.strips) * tmp::kColStripCols >= uint64_t(N) &&
+                                          uint64_t(c.slabs) * c.strips * 64 * tmp::kColStripGroups < (uint64_t{1} << 32) &&
+                                          ts % (tmp::kColStripGroups * 8) == 0 &&
                                           uint64_t(c.slabs) * uint64_t(N) * 4 <= wsb,
                                       "cols strip plan M=%ld N=%ld", long(M), long(N));
-                                CHECK(!c.whole || (M % ts == 0 && N % tmp::kColRowStrip == 0), "cols strip whole");
+                                CHECK(!c.whole || (M % ts == 0 && N % tmp::kColStripCols == 0), "cols strip whole");
                                 std::vector<uint8_t> hit(size_t(c.slabs) * size_t(nch), 0);
                                 for (uint32_t b = 0; b < c.slabs * c.strips; ++b) {
                                     const uint32_t strip = b % c.strips, slab = b / c.strips;
-                                    for (int t = 0; t < tmp::kBlock; ++t) {
-                                        const int64_t ch = int64_t(strip) * tmp::kBlock + t;
+                                    for (int t = 0; t < 64; ++t) {
+                                        const int64_t ch = int64_t(strip) * 64 + t;
                                         if (ch < nch)
                                             ++hit[size_t(slab) * size_t(nch) + size_t(ch)];
                                     }

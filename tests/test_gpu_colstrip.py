@@ -1,5 +1,6 @@
 """GPU parity of the LDS walk's kernel for wide matrices (a workgroup per slab of rows and strip of
-1024 columns, each thread one 16-byte column chunk; then a fold of the slab partials), against the
+256 columns, each lane of its 8 waves one 16-byte column chunk over an eighth of the slab's rows;
+then a fold of the slab partials), against the
 fp64 oracle: the column-sum workload, matrices ragged in rows and columns, integer data (every
 partial sum exact, so the result is exact too), and the same call with a workspace off the
 16-byte grid, which takes the LDS-staged kernel instead and must agree within the bound.
@@ -46,9 +47,10 @@ def _colsum(dev, xh, M, N, ld, TM, TN, aligned, ws_offset=0):
 
 @pytest.mark.parametrize("M,N,ld,TM,TN,aligned", [
     (4096, 4096, 4096, 256, 64, 1),     # the column-sum workload
-    (7000, 3000, 3000, 1, 4, 0),        # ragged rows (7000 = 109 slabs of 64 + 24) and strips (2 x 1024 + 952)
-    (16384, 1024, 1028, 64, 256, 0),    # padded rows, one strip
+    (7000, 3000, 3000, 1, 4, 0),        # ragged rows (7000 = 109 slabs of 64 + 24) and strips (11 x 256 + 184)
+    (16384, 1024, 1028, 64, 256, 0),    # padded rows, four strips
     (2048, 8192, 8192, 64, 1024, 1),    # short and wide
+    (20000, 4096, 4096, 1, 4, 0),       # tall: 157 slabs of 128 rows (16 per wave, 2 batches), the last of 32
 ])
 def test_strip_walk_against_oracle(dev, M, N, ld, TM, TN, aligned):
     note("strip colsum %dx%d ld %d" % (M, N, ld))
